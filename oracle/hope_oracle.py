@@ -1,0 +1,295 @@
+"""fp64 CPU oracle for the four-direction Hope memory scan.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  The product path (the
+HIP library and its Python binding) never calls it, and it shares no code with
+that path: the two meet only in the seeded inputs of ``workloads``.
+
+The oracle is the method written out plainly, token by token, in float64,
+following the pages' order and notation.  Sources (cited by page title and
+section / equation):
+
+  [VH]  "VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"
+  [NLz] "Nested Learning: the 'illusion' of deep learning architectures and
+         multi-timescale memory" (Chinese reading notes on Nested Learning)
+  [VM]  "VMamba: Visual State Space Model" (explainer page)
+  [NL]  "Nested Learning: The Illusion of Deep Learning Architectures", part 12
+
+What is computed, per image b, head h and selected route r:
+  * the route order p_r(t) ([VM] "Four orders give each position several views
+    of the image"; [VH] Sec. 2.3, Eq. 24);
+  * chunks aligned with rows / columns ([VH] Sec. 2.3, Eq. 25);
+  * per chunk, quantities generated from the memories frozen at the chunk start
+    ([VH] Sec. 2.1.3, Eq. 15-16; [NLz] Sec. 2.10 on the chunk-start index);
+  * the executed step of the stability-matched control ([VH] Sec. 2.2,
+    Definition 1, Eq. 19-20, with the finite-precision safeguards of App. B.3);
+  * the self-referential retained-DGD update of every memory, token by token
+    ([VH] Sec. 2.1.2, Eq. 13, with the chunked signal of Eq. 16);
+  * the readout y_t = M^m_b q_t and the restore-and-sum merge ([VH] Eq. 16 and
+    Eq. 26 with unit scales; [VM] "Cross-merge restores positions before adding").
+
+Readings where the pages leave a step open:
+  * six memories: VisionHOPE's five plus the query memory M_q that the Nested
+    Learning update set (Eq. 96) contains; q_t = n(M_q,b x_t) and every memory
+    follows the same update;
+  * q is normalised like k: q = q_raw / sqrt(|q_raw|^2 + 1e-6);
+  * gate maps: eta = eta_scale * sigmoid(s) (default) or eta_scale * softplus(s)
+    ([VH] App. C.1, Eq. 53); alpha = sigmoid(s + alpha_bias);
+  * the inward factor (1 - 1e-3) multiplies eta_inj before the soft cap; the
+    spectral limit is multiplied by (1 - 1e-6), its |k|^2 floored at 1e-20 and
+    the result moved one ulp toward zero in the working precision;
+  * eta_bar = 0 when eta = 0 or eta_inj = 0 (the cap's 0/0 limit).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MEMORIES = ("mem", "k", "v", "q", "eta", "alpha")
+ROUTES = (0, 1, 2, 3)            # ->, <-, down, up
+INJ_INWARD = 1.0 - 1e-3
+SPEC_INWARD = 1.0 - 1e-6
+KAPPA_FLOOR = 1e-20
+NORM_EPS = 1e-6
+
+
+# --------------------------------------------------------------------------
+# Route orders: [VM] "Four orders give each position several views of the
+# image" and [VH] Sec. 2.3 Eq. 24.  Row-major flattening, the flattening of the
+# spatial transpose, and the full reversal of each.
+# --------------------------------------------------------------------------
+def route_order(H: int, W: int, r: int) -> np.ndarray:
+    """p_r(t): flat pixel index (h * W + w) visited at sequence step t."""
+    grid = np.arange(H * W, dtype=np.int64).reshape(H, W)
+    if r == 0:
+        return grid.reshape(-1)
+    if r == 1:
+        return grid.reshape(-1)[::-1].copy()
+    if r == 2:
+        return grid.T.reshape(-1)
+    if r == 3:
+        return grid.T.reshape(-1)[::-1].copy()
+    raise ValueError("route index must be 0..3")
+
+
+def route_chunk(H: int, W: int, r: int, chunk: int) -> int:
+    """Chunk length of route r: [VH] Sec. 2.3 Eq. 25 when chunk == 0."""
+    if chunk > 0:
+        return chunk
+    return W if r in (0, 1) else H
+
+
+def cross_scan(x: np.ndarray, r: int) -> np.ndarray:
+    """Serialise x[B, H, W, D] along route r -> [B, N, D]."""
+    B, H, W, D = x.shape
+    return x.reshape(B, H * W, D)[:, route_order(H, W, r), :]
+
+
+def cross_merge(routes: dict, H: int, W: int) -> np.ndarray:
+    """Restore each route's [B, N, D] output to the grid and add, per pixel,
+    in the fixed order ->, <-, down, up ([VH] Eq. 26 with lambda_r = 1)."""
+    first = next(iter(routes.values()))
+    B, N, D = first.shape
+    out = np.zeros((B, N, D), dtype=np.float64)
+    for r in ROUTES:
+        if r not in routes:
+            continue
+        order = route_order(H, W, r)
+        y = routes[r]
+        for t in range(N):
+            out[:, order[t], :] += y[:, t, :]
+    return out.reshape(B, H, W, D)
+
+
+# --------------------------------------------------------------------------
+# Gate maps: [VH] App. C.1 Eq. 53 (softplus form) and the sigmoid form of the
+# synthetic workloads.
+# --------------------------------------------------------------------------
+def sigmoid(s):
+    return 1.0 / (1.0 + np.exp(-s))
+
+
+def phi_eta(s, eta_map: str = "sigmoid", eta_scale: float = 1.0):
+    if eta_map == "sigmoid":
+        return eta_scale * sigmoid(s)
+    if eta_map == "softplus":
+        return eta_scale * np.logaddexp(0.0, s)
+    raise ValueError(eta_map)
+
+
+def phi_alpha(s, alpha_bias: float = 4.0):
+    return sigmoid(s + alpha_bias)
+
+
+def stabilized_normalize(z: np.ndarray, eps: float = NORM_EPS) -> np.ndarray:
+    """z / sqrt(|z|^2 + eps) along the last axis ([VH] App. C.1, key normalisation)."""
+    return z / np.sqrt(np.sum(z * z, axis=-1, keepdims=True) + eps)
+
+
+# --------------------------------------------------------------------------
+# Stability-matched step-size control: [VH] Sec. 2.2 Definition 1, Eq. 19-20,
+# and the finite-precision safeguards of App. B.3.
+# --------------------------------------------------------------------------
+def soft_injection_cap(eta, alpha, delta, eps: float = NORM_EPS, inward: float = INJ_INWARD):
+    """Eq. 19: returns (eta_bar, eta_inj) for one token or a batch of tokens."""
+    eta = np.asarray(eta, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    r = np.sqrt(np.sum(delta * delta, axis=-1) + eps * eps) + eps
+    eta_inj = inward * (1.0 - alpha) / r
+    ok = (eta != 0.0) & (eta_inj != 0.0)
+    safe_inj = np.where(ok, eta_inj, 1.0)
+    eta_bar = np.where(ok, safe_inj * -np.expm1(-eta / safe_inj), 0.0)
+    return eta_bar, eta_inj
+
+
+def spectral_limit(alpha, k, inward: float = SPEC_INWARD, floor: float = KAPPA_FLOOR,
+                   dtype=np.float64):
+    """Eq. 20 with the App. B.3 safeguards, rounded one ulp toward zero in ``dtype``."""
+    kappa = np.maximum(np.sum(k * k, axis=-1), floor)
+    lim = (inward * 2.0 * np.asarray(alpha, dtype=np.float64) / kappa).astype(dtype)
+    return np.nextafter(lim, dtype(0)).astype(np.float64)
+
+
+def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS):
+    """eta_tilde = min(eta_bar, eta_spec) ([VH] Eq. 20)."""
+    eta_bar, _ = soft_injection_cap(eta, alpha, delta, eps)
+    return np.minimum(eta_bar, spectral_limit(alpha, k))
+
+
+# --------------------------------------------------------------------------
+# One retained-DGD write: [VH] Sec. 2.1.1 Eq. 7 / Sec. 2.1.2 Eq. 13.
+#   M <- M (alpha I - eta k k^T) - eta g k^T
+# M is [n, rows, d] (a 1 x d row memory has rows = 1); k is [n, d]; g is
+# [n, rows]; alpha, eta are [n].
+# --------------------------------------------------------------------------
+def retained_dgd(M, k, g, eta, alpha):
+    n, d = k.shape
+    eye = np.broadcast_to(np.eye(d), (n, d, d))
+    A = alpha[:, None, None] * eye - eta[:, None, None] * (k[:, :, None] * k[:, None, :])
+    return M @ A - eta[:, None, None] * (g[:, :, None] * k[:, None, :])
+
+
+def _matvec(M, x):
+    """[n, rows, d] @ [n, d] -> [n, rows]."""
+    return (M @ x[:, :, None])[:, :, 0]
+
+
+# --------------------------------------------------------------------------
+# One SRNL chain (one head of one route, possibly many chains in a batch):
+# [VH] Sec. 2.1.3 Eq. 15-16 for generation from the chunk-start state,
+# Eq. 19-20 for the step, Eq. 13 for the token-order update of each memory.
+# --------------------------------------------------------------------------
+def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid",
+               eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
+               control: bool = True, log: list | None = None):
+    """Run chains over ordered tokens.
+
+    xs    : [n, N, d] tokens in route order
+    state : dict name -> [n, rows, d] initial memories (rows = d, or 1 for eta/alpha)
+    chunk : chunk length C >= 1
+    control=False executes the raw step eta (the uncontrolled recurrence of
+    [VH] Eq. 17), used only to show that the checks can fail.
+    Returns (ys [n, N, d], final state dict).
+    """
+    xs = np.asarray(xs, dtype=np.float64)
+    n, N, d = xs.shape
+    M = {m: np.array(state[m], dtype=np.float64, copy=True) for m in MEMORIES}
+    ys = np.zeros((n, N, d), dtype=np.float64)
+    for s in range(0, N, chunk):
+        Mb = {m: M[m].copy() for m in MEMORIES}          # boundary states M_b
+        for t in range(s, min(s + chunk, N)):
+            x = xs[:, t, :]
+            k = stabilized_normalize(_matvec(Mb["k"], x), eps)
+            v = _matvec(Mb["v"], x)
+            q = stabilized_normalize(_matvec(Mb["q"], x), eps)
+            eta = phi_eta(_matvec(Mb["eta"], x)[:, 0], eta_map, eta_scale)
+            alpha = phi_alpha(_matvec(Mb["alpha"], x)[:, 0], alpha_bias)
+            ys[:, t, :] = _matvec(Mb["mem"], q)               # y_t = M^m_b q_t
+            delta = k - v
+            step = executed_step(eta, alpha, k, delta, eps) if control else eta
+            if log is not None:
+                log.append({"t": t, "eta": eta, "alpha": alpha, "step": step, "k": k,
+                            "delta": delta})
+            for m in MEMORIES:
+                vhat = _matvec(Mb[m], v)                      # self-generated target, Eq. 16
+                g = _matvec(Mb[m], k) - vhat                  # output-space signal, Eq. 16
+                M[m] = retained_dgd(M[m], k, g, step, alpha)  # Eq. 13
+    return ys, M
+
+
+def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk: int = 0,
+           eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
+           eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None):
+    """The whole operator: serialise, run every (image, head, route) chain, merge.
+
+    x    : [B, H, W, D] (any float dtype; widened to fp64)
+    init : [4, n_heads, S] (or [B, 4, n_heads, S] with init_per_image), S = 4d^2 + 2d,
+           per (route, head) the flat concatenation M_mem, M_k, M_v, M_q (row-major
+           d x d), m_eta, m_alpha.
+    heads / images restrict the computation to a subset (sampled checks); the
+    returned arrays then cover only those.
+    Returns (out [b, H, W, D_sel] fp64, final [b, 4, h, S] fp64, NaN for
+    unselected routes).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    B, H, W, D = x.shape
+    d = D // n_heads
+    heads = list(range(n_heads)) if heads is None else list(heads)
+    images = list(range(B)) if images is None else list(images)
+    xb = x[images]
+    nb = len(images)
+    S = 4 * d * d + 2 * d
+    init = np.asarray(init, dtype=np.float64)
+    out = np.zeros((nb, H, W, len(heads) * d), dtype=np.float64)
+    final = np.full((nb, 4, len(heads), S), np.nan, dtype=np.float64)
+    for hi, h in enumerate(heads):
+        routes = {}
+        for r in ROUTES:
+            if not (dirs >> r) & 1:
+                continue
+            xs = cross_scan(xb[..., h * d:(h + 1) * d], r)
+            flat = init[images, r, h] if init_per_image else np.broadcast_to(init[r, h], (nb, S))
+            st = unflatten_state(flat, d)
+            C = route_chunk(H, W, r, chunk)
+            ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps)
+            routes[r] = ys
+            final[:, r, hi, :] = flatten_state(fin)
+        if routes:
+            out[..., hi * d:(hi + 1) * d] = cross_merge(routes, H, W)
+    return out, final
+
+
+def unflatten_state(flat: np.ndarray, d: int) -> dict:
+    flat = np.asarray(flat, dtype=np.float64)
+    dd = d * d
+    st = {}
+    for i, m in enumerate(("mem", "k", "v", "q")):
+        st[m] = flat[..., i * dd:(i + 1) * dd].reshape(flat.shape[:-1] + (d, d)).copy()
+    st["eta"] = flat[..., 4 * dd:4 * dd + d].reshape(flat.shape[:-1] + (1, d)).copy()
+    st["alpha"] = flat[..., 4 * dd + d:].reshape(flat.shape[:-1] + (1, d)).copy()
+    return st
+
+
+def flatten_state(st: dict) -> np.ndarray:
+    lead = st["k"].shape[:-2]
+    parts = [st[m].reshape(lead + (-1,)) for m in MEMORIES]
+    return np.concatenate(parts, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Second form of the same chunk: the shared right-multiplicative gain of
+# [VH] App. B.4 Prop. 2, Eq. 46 (G_b = I, G_t = G_{t-1} A_t + B_t with
+# A_t = alpha_t I - eta_t k k^T and B_t = -eta_t delta k^T, Eq. 21).
+# Used by the tests to check the literal per-memory loop, not by scan2d.
+# --------------------------------------------------------------------------
+def chunk_gain(k, delta, step, alpha):
+    """k, delta: [n, C, d]; step, alpha: [n, C] -> list of G_t, t = b..b+C ([n, d, d])."""
+    n, C, d = k.shape
+    G = np.broadcast_to(np.eye(d), (n, d, d)).copy()
+    out = [G.copy()]
+    for t in range(C):
+        kt = k[:, t]
+        A = alpha[:, t, None, None] * np.eye(d) - step[:, t, None, None] * (kt[:, :, None] * kt[:, None, :])
+        Bm = -step[:, t, None, None] * (delta[:, t, :, None] * kt[:, None, :])
+        G = G @ A + Bm
+        out.append(G.copy())
+    return out
