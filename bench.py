@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark of the four-direction Hope memory scan on one MI355X.
+
+One step = one hope_scan2d_forward call over the whole batch of the stage-3
+workload (B=128, 14x14 map, D=384 as 6 heads of 64, row/column chunks of 14,
+bf16 inputs, fp32 state), inputs already resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--no-cpu-baseline]
+
+Roofline of the scan kernel: algorithmic work per (token, head, route), in
+multiply-accumulates, is 4d^2 + 2d for the projections and the readout (bf16
+inputs, MFMA class, 2.5 PFLOP/s) plus the cheapest exact fp32 chunk form for the
+gain and the carry, min(F1, F2, F3) (fp32 class, 157.3 TFLOP/s):
+  F1 = 3d^2 + (4d^3 + 2d^2)/C,  F2 = Cd + C^2/6 + d^2 + (4d^3 + 2d^2)/C,
+  F3 = Cd + C^2/6 + 8d^2 + 4d.
+The roofline time is the sum of each class's flops over its peak; "peak" in the
+JSON is the total flop count over that time (the blend of the two peaks), so
+frac = roofline time / measured kernel time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_FP32 = 157.3e12    # fp32 matrix / vector, FLOP/s
+PEAK_HBM = 8.0e12       # bytes/s
+METRIC = wl_metric = "scan tokens/s (positions×dirs) for 4-dir Hope memory scan; % MFMA/HBM peak"
+
+
+def work_per_token(d: int, C: int) -> tuple[float, float]:
+    """(bf16-class MACs, fp32-class MACs) per (token, head, route)."""
+    bf16 = 4 * d * d + 2 * d
+    f1 = 3 * d * d + (4 * d ** 3 + 2 * d * d) / C
+    f2 = C * d + C * C / 6 + d * d + (4 * d ** 3 + 2 * d * d) / C
+    f3 = C * d + C * C / 6 + 8 * d * d + 4 * d
+    return float(bf16), float(min(f1, f2, f3))
+
+
+def roofline_numbers(w: wl.Workload, n_dirs: int = 4) -> dict:
+    d = w.d
+    C = w.W  # square maps: row and column chunks are equal
+    bf16, fp32 = work_per_token(d, C)
+    units = w.scan_tokens(n_dirs) * w.n_heads
+    f_bf16 = 2 * bf16 * units
+    f_fp32 = 2 * fp32 * units
+    t_compute = f_bf16 / PEAK_BF16 + f_fp32 / PEAK_FP32
+    x_bytes = w.B * w.H * w.W * w.D * (2 if w.dtype == "bf16" else 4)
+    out_bytes = w.B * w.H * w.W * w.D * 4
+    init_bytes = 4 * w.n_heads * w.state_size * 4
+    hbm = x_bytes + out_bytes + init_bytes
+    return {"flops": f_bf16 + f_fp32, "flops_bf16": f_bf16, "flops_fp32": f_fp32,
+            "t_compute": t_compute, "hbm_bytes": hbm, "t_hbm": hbm / PEAK_HBM}
+
+
+def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 12.0) -> dict:
+    """Time the fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        images = [0]
+        t0 = time.perf_counter()
+        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images)
+        t1 = time.perf_counter() - t0
+        n_img = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
+        images = list(range(n_img))
+        t0 = time.perf_counter()
+        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images)
+        dt = time.perf_counter() - t0
+    toks = n_img * w.H * w.W * 4
+    return {"value": toks / dt, "unit": "scan tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_img} of {w.B} images, all {w.n_heads} heads and 4 routes "
+                      f"({toks} scan tokens) in {dt:.1f} s, fp64 numpy, 1 BLAS thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every (image, head, route) chain of this scan is "
+              "independent, so more GPUs would only split the batch; run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from self_modifying_memory_amd.scan2d import alloc_workspace, hope_scan2d_forward
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    w = wl.WORKLOADS[args.workload]
+    inp = wl.draw_workload(w, live=True)
+    dev = torch.device("cuda:0")
+    if w.dtype == "bf16":
+        x_host = torch.from_numpy(inp["x_bits"].view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        x_host = torch.from_numpy(inp["x"].copy())
+    init = torch.from_numpy(inp["init"].copy()).to(dev)
+    sets = []
+    for _ in range(max(1, args.sets)):
+        x = x_host.to(dev)
+        sets.append((x, torch.empty(x.shape, dtype=torch.float32, device=dev),
+                     alloc_workspace(x, w.n_heads, 15, w.chunk)))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x, out, ws = sets[i % len(sets)]
+        hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    k_avg = float(np.mean(kernel_ms)) * 1e-3
+
+    tokens = w.scan_tokens(4)
+    roof = roofline_numbers(w)
+    achieved = roof["flops"] / k_avg
+    peak = roof["flops"] / roof["t_compute"]
+    rec = {
+        "metric": METRIC,
+        "value": tokens * args.steps / wall,
+        "unit": "scan tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
+                   "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
+                   "state_dtype": "f32"},
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel_ms": k_avg * 1e3, "kernel_ms_p10_p90": [
+                         float(np.percentile(kernel_ms, 10)), float(np.percentile(kernel_ms, 90))],
+                     "hbm_frac": roof["hbm_bytes"] / k_avg / PEAK_HBM},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,169 @@
+/*
+ * hope_scan2d.h -- C ABI of the four-direction Hope memory scan on MI355X (gfx950).
+ *
+ * The operation (page titles cited, then section / equation):
+ *   "VisionHOPE: Visual Backbones as Self-Modifying Learning Systems" (VisionHOPE)
+ *     Sec. 2.3 Eq. 24-26: serialise the feature map along four routes
+ *       (row-major, its reversal, column-major, its reversal), run one
+ *       self-referential memory per route and head, restore and sum;
+ *     Sec. 2.3 Eq. 25: chunks span one row (row routes) or one column
+ *       (column routes);
+ *     Sec. 2.1.3 Eq. 15-16: per chunk, k, v, q, eta, alpha and the readout
+ *       y = M_mem q are generated from the memories frozen at the chunk start;
+ *     Sec. 2.2 Definition 1, Eq. 19-20 and App. B.3: the executed step
+ *       (soft injection cap, spectral clamp, finite-precision safeguards);
+ *     Sec. 2.1.2 Eq. 13 / App. B.4 Eq. 45-46: every memory is updated by the
+ *       same right-multiplicative gain of the chunk.
+ *   "Nested Learning: The Illusion of Deep Learning Architectures" part 12,
+ *     Eq. 94-96: the update set {k, v, q, eta, alpha, memory}; this library
+ *     keeps q as a sixth coupled memory M_q, q = n(M_q x).
+ *   "VMamba: Visual State Space Model" (explainer): the exact scan orders and
+ *     the restore-then-sum merge (no averaging).
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after a call returns and never allocates device memory.
+ *   - Every call only enqueues work on the given stream (0 = default stream) and
+ *     returns; results are ready when the stream is synchronised.
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has written nothing.
+ *   - Feature maps are channels-last and contiguous: x[B][H][W][D], the flat
+ *     pixel index is h * W + w.  Heads are contiguous channel slices of width
+ *     d = D / n_heads; d must be 16, 32 or 64.
+ *   - Route index r: 0 = row-major forward, 1 = its full reversal, 2 = column-major
+ *     forward (flatten of the spatial transpose), 3 = its full reversal.
+ *   - Per (route, head) state: S(d) = 4 d^2 + 2 d floats, the concatenation of
+ *     M_mem, M_k, M_v, M_q (each d x d, row-major, applied as M @ x), m_eta and
+ *     m_alpha (each 1 x d).
+ *   - Thread safety: reentrant; no mutable global state.
+ */
+#ifndef HOPE_SCAN2D_H
+#define HOPE_SCAN2D_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HOPE_OK = 0,
+  HOPE_ERR_INVALID_ARG = -1,  /* malformed shape, null or misaligned pointer, aliasing, bad flag */
+  HOPE_ERR_UNSUPPORTED = -2,  /* well-formed but not implemented (head dimension not 16/32/64) */
+  HOPE_ERR_WORKSPACE = -3,    /* workspace missing or smaller than hope_scan2d_workspace_size() */
+  HOPE_ERR_HIP = -4           /* a HIP launch failed; hope_last_hip_error() tells which */
+} hope_status_t;
+
+typedef enum { HOPE_F32 = 0, HOPE_BF16 = 1 } hope_dtype_t;
+
+enum {
+  HOPE_DIR_ROW_FWD = 1u, /* route 0 */
+  HOPE_DIR_ROW_REV = 2u, /* route 1 */
+  HOPE_DIR_COL_FWD = 4u, /* route 2 */
+  HOPE_DIR_COL_REV = 8u, /* route 3 */
+  HOPE_DIR_ALL = 15u
+};
+
+typedef enum {
+  HOPE_ETA_SIGMOID = 0,  /* eta = eta_scale * sigmoid(s)  (synthetic workloads: eta_scale = 1) */
+  HOPE_ETA_SOFTPLUS = 1  /* eta = eta_scale * softplus(s) (VisionHOPE App. C.1 Eq. 53, gamma = 0.025) */
+} hope_eta_map_t;
+
+/* A feature map.  data: device pointer to x[B][H][W][D], 16-byte aligned;
+ * dtype: hope_dtype_t (F32 or BF16). */
+typedef struct {
+  const void* data;
+  int32_t dtype;
+  int32_t B, H, W, D, n_heads;
+} hope_fmap_t;
+
+/* Options of hope_scan2d_forward.  Start from hope_scan2d_default_opts(). */
+typedef struct {
+  hipStream_t stream;        /* stream to enqueue on; 0 = default stream */
+  float* final_memories;     /* NULL, or device [B][4][n_heads][S(d)] fp32: state after the
+                                last chunk of every (image, route, head); rows of unselected
+                                routes are left untouched */
+  void* workspace;           /* device scratch of at least workspace_bytes, 256-byte aligned */
+  size_t workspace_bytes;
+  int32_t eta_map;           /* hope_eta_map_t; default HOPE_ETA_SIGMOID */
+  float eta_scale;           /* default 1.0 */
+  float alpha_bias;          /* alpha = sigmoid(s + alpha_bias); default 4.0 */
+  float eps;                 /* stabiliser of the key / query normalisation (App. C.1) and the
+                                epsilon of the soft injection cap (Eq. 19); default 1e-6 */
+  int32_t init_per_image;    /* 0: init is [4][n_heads][S]; 1: [B][4][n_heads][S] (resume) */
+  int32_t reserved;          /* must be 0 */
+} hope_scan2d_opts_t;
+
+/* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */
+void hope_scan2d_default_opts(hope_scan2d_opts_t* opts);
+
+/*
+ * hope_scan2d_forward -- the four-direction scan (VisionHOPE Sec. 2.3 Eq. 24-26
+ * with unit direction scales; recurrence of Sec. 2.1.3 Eq. 15-16 with the
+ * executed step of Sec. 2.2 Eq. 19-20 and the shared gain of App. B.4 Eq. 46).
+ *
+ *   x              feature map (see hope_fmap_t).
+ *   init_memories  device fp32, [4][n_heads][S(d)] (or [B][4][n_heads][S(d)] when
+ *                  opts->init_per_image): the initial state of every route and head;
+ *                  rows of unselected routes are not read.
+ *   dirs           bit set of routes (HOPE_DIR_*), 1..15.  Unselected routes add
+ *                  nothing to out.
+ *   chunk          chunk length; 0 = aligned (W on row routes, H on column routes,
+ *                  Eq. 25).  A chunk length that does not divide H*W leaves a
+ *                  shorter last chunk.
+ *   out            device fp32 [B][H][W][D], 16-byte aligned, overwritten with the
+ *                  sum over selected routes of each route's readout restored to its
+ *                  pixel, added in the fixed order route 0, 1, 2, 3.
+ *   opts           NULL = defaults.  With two or more routes selected a workspace
+ *                  is required (hope_scan2d_workspace_size).
+ * Errors: HOPE_ERR_INVALID_ARG for null / misaligned pointers, non-positive sizes,
+ * D not divisible by n_heads, dirs outside 1..15, chunk < 0, dtype not F32/BF16,
+ * out overlapping x, init_memories, final_memories or the workspace;
+ * HOPE_ERR_UNSUPPORTED for d not in {16, 32, 64}; HOPE_ERR_WORKSPACE when the
+ * workspace is missing or too small; HOPE_ERR_HIP when a launch fails.
+ * Results are deterministic: the same inputs give bit-identical outputs.
+ */
+hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
+                                  uint32_t dirs, int32_t chunk, float* out,
+                                  const hope_scan2d_opts_t* opts);
+
+/* Bytes of workspace hope_scan2d_forward needs for this call (0 when one route is
+ * selected); 0 also for arguments that hope_scan2d_forward would reject. */
+size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                  const hope_scan2d_opts_t* opts);
+
+/* Static, human-readable name of a status code. */
+const char* hope_status_string(hope_status_t status);
+
+/* The hipError_t behind the last HOPE_ERR_HIP returned on this thread (0 if none). */
+int hope_last_hip_error(void);
+
+/*
+ * Test and measurement exports of the two permutations on their own.
+ *
+ * hope_debug_cross_scan -- routes[slot][b][t][c] = x[b][p_r(t)][c] for every
+ * selected route r, slots numbered in increasing r ("VMamba: Visual State Space
+ * Model", the four scan orders; VisionHOPE Eq. 24).  routes has the dtype of x and
+ * popcount(dirs) * B * H * W * D elements; it must not overlap x.  Bit-exact copy.
+ */
+hope_status_t hope_debug_cross_scan(const hope_fmap_t* x, uint32_t dirs, void* routes,
+                                    hipStream_t stream);
+
+/*
+ * hope_debug_cross_merge -- out[b][p][c] = sum over selected routes, in increasing r,
+ * of routes[slot][b][t][c] at p = p_r(t) (the restore-then-sum merge of VisionHOPE
+ * Eq. 26 with unit scales).  routes: dtype F32 or BF16 (widened to fp32 before the
+ * adds), popcount(dirs) * B * H * W * D elements; out: fp32 [B][H][W][D], not
+ * overlapping routes.
+ */
+hope_status_t hope_debug_cross_merge(const void* routes, int32_t dtype, int32_t B, int32_t H,
+                                     int32_t W, int32_t D, uint32_t dirs, float* out,
+                                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HOPE_SCAN2D_H */

@@ -1,0 +1,229 @@
+// Host side of the C ABI declared in include/hope_scan2d.h: argument validation
+// (all of it before anything is enqueued), workspace accounting and kernel dispatch.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/hope_scan2d.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + bytes};
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int popcount4(uint32_t dirs) {
+  int n = 0;
+  for (int r = 0; r < 4; ++r) n += (dirs >> r) & 1u;
+  return n;
+}
+
+int slots_of(uint32_t dirs, int* route_of_slot) {
+  int n = 0;
+  for (int r = 0; r < 4; ++r)
+    if ((dirs >> r) & 1u) route_of_slot[n++] = r;
+  return n;
+}
+
+// Workspace layout: [B*nh int32 arrival counters, padded to 256 bytes]
+//                   [(n_sel-1) fp32 planes of one map each, each padded to 256 bytes].
+int64_t plane_stride_elems(int64_t n_elem) { return (n_elem + 63) / 64 * 64; }
+size_t counter_bytes(const hope_fmap_t* x) {
+  return ((size_t)x->B * x->n_heads * sizeof(int) + 255) / 256 * 256;
+}
+
+hope_status_t check_fmap(const hope_fmap_t* x) {
+  if (!x || !x->data) return HOPE_ERR_INVALID_ARG;
+  if (x->dtype != HOPE_F32 && x->dtype != HOPE_BF16) return HOPE_ERR_INVALID_ARG;
+  if (x->B <= 0 || x->H <= 0 || x->W <= 0 || x->D <= 0 || x->n_heads <= 0)
+    return HOPE_ERR_INVALID_ARG;
+  if (x->D % x->n_heads) return HOPE_ERR_INVALID_ARG;
+  if ((int64_t)x->H * x->W > INT32_MAX) return HOPE_ERR_INVALID_ARG;
+  if ((int64_t)x->B * x->H * x->W > INT64_MAX / 8 / x->D) return HOPE_ERR_INVALID_ARG;
+  if (!aligned(x->data, 16)) return HOPE_ERR_INVALID_ARG;
+  return HOPE_OK;
+}
+
+hope_status_t check_opts(const hope_scan2d_opts_t* o) {
+  if (o->eta_map != HOPE_ETA_SIGMOID && o->eta_map != HOPE_ETA_SOFTPLUS)
+    return HOPE_ERR_INVALID_ARG;
+  if (!isfinite(o->eta_scale) || o->eta_scale < 0.f) return HOPE_ERR_INVALID_ARG;
+  if (!isfinite(o->alpha_bias)) return HOPE_ERR_INVALID_ARG;
+  if (!isfinite(o->eps) || o->eps < 0.f) return HOPE_ERR_INVALID_ARG;
+  if (o->init_per_image != 0 && o->init_per_image != 1) return HOPE_ERR_INVALID_ARG;
+  if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->final_memories && !aligned(o->final_memories, 16)) return HOPE_ERR_INVALID_ARG;
+  if (o->workspace && !aligned(o->workspace, 256)) return HOPE_ERR_INVALID_ARG;
+  return HOPE_OK;
+}
+
+size_t workspace_bytes_for(const hope_fmap_t* x, uint32_t dirs) {
+  const int n_sel = popcount4(dirs);
+  if (n_sel <= 1) return 0;
+  const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
+  return counter_bytes(x) + (size_t)(n_sel - 1) * (size_t)plane_stride_elems(n_elem) * sizeof(float);
+}
+
+hope_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return HOPE_OK;
+  g_last_hip_error = (int)e;
+  return HOPE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+void hope_scan2d_default_opts(hope_scan2d_opts_t* opts) {
+  if (!opts) return;
+  memset(opts, 0, sizeof(*opts));
+  opts->eta_map = HOPE_ETA_SIGMOID;
+  opts->eta_scale = 1.0f;
+  opts->alpha_bias = 4.0f;
+  opts->eps = 1e-6f;
+}
+
+size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                  const hope_scan2d_opts_t* opts) {
+  (void)opts;
+  if (check_fmap(x) != HOPE_OK || dirs == 0 || dirs > 15 || chunk < 0) return 0;
+  return workspace_bytes_for(x, dirs);
+}
+
+hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
+                                  uint32_t dirs, int32_t chunk, float* out,
+                                  const hope_scan2d_opts_t* opts) {
+  hope_scan2d_opts_t o;
+  if (opts) {
+    o = *opts;
+  } else {
+    hope_scan2d_default_opts(&o);
+  }
+  hope_status_t st = check_fmap(x);
+  if (st != HOPE_OK) return st;
+  if ((st = check_opts(&o)) != HOPE_OK) return st;
+  if (!init_memories || !out) return HOPE_ERR_INVALID_ARG;
+  if (!aligned(init_memories, 16) || !aligned(out, 16)) return HOPE_ERR_INVALID_ARG;
+  if (dirs == 0 || dirs > 15 || chunk < 0) return HOPE_ERR_INVALID_ARG;
+
+  const int d = x->D / x->n_heads;
+  const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
+  const size_t x_bytes = (size_t)n_elem * (x->dtype == HOPE_BF16 ? 2 : 4);
+  const size_t out_bytes = (size_t)n_elem * sizeof(float);
+  const size_t state_floats = (size_t)4 * d * d + 2 * (size_t)d;
+  const size_t init_bytes =
+      (o.init_per_image ? (size_t)x->B : 1) * 4 * (size_t)x->n_heads * state_floats * sizeof(float);
+  const size_t final_bytes = (size_t)x->B * 4 * x->n_heads * state_floats * sizeof(float);
+  const size_t ws_need = workspace_bytes_for(x, dirs);
+
+  const Range r_out = range_of(out, out_bytes);
+  if (overlaps(r_out, range_of(x->data, x_bytes))) return HOPE_ERR_INVALID_ARG;
+  if (overlaps(r_out, range_of(init_memories, init_bytes))) return HOPE_ERR_INVALID_ARG;
+  if (o.final_memories) {
+    const Range r_fin = range_of(o.final_memories, final_bytes);
+    if (overlaps(r_out, r_fin) || overlaps(r_fin, range_of(x->data, x_bytes)) ||
+        overlaps(r_fin, range_of(init_memories, init_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+  }
+  if (o.workspace && o.workspace_bytes) {
+    const Range r_ws = range_of(o.workspace, o.workspace_bytes);
+    if (overlaps(r_out, r_ws) || overlaps(r_ws, range_of(x->data, x_bytes)) ||
+        overlaps(r_ws, range_of(init_memories, init_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+    if (o.final_memories && overlaps(r_ws, range_of(o.final_memories, final_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+  }
+  if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
+  if (ws_need > 0 && (!o.workspace || o.workspace_bytes < ws_need)) return HOPE_ERR_WORKSPACE;
+
+  hope::ChainParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x->data;
+  p.init = init_memories;
+  p.out = out;
+  if (ws_need > 0) {
+    p.counters = static_cast<int*>(o.workspace);
+    p.planes = reinterpret_cast<float*>(static_cast<char*>(o.workspace) + counter_bytes(x));
+  }
+  p.final_mem = o.final_memories;
+  p.plane_stride = plane_stride_elems(n_elem);
+  p.x_bf16 = x->dtype == HOPE_BF16;
+  p.B = x->B;
+  p.H = x->H;
+  p.W = x->W;
+  p.D = x->D;
+  p.nh = x->n_heads;
+  p.n_sel = slots_of(dirs, p.route_of_slot);
+  p.chunk = chunk;
+  p.init_per_image = o.init_per_image;
+  p.eta_map = o.eta_map;
+  p.eta_scale = o.eta_scale;
+  p.alpha_bias = o.alpha_bias;
+  p.eps = o.eps;
+  if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
+
+  hipStream_t s = o.stream;
+  if (p.n_sel > 1) {
+    st = hip_status(hope::launch_zero_ints(p.counters, (int64_t)x->B * x->n_heads, s));
+    if (st != HOPE_OK) return st;
+  }
+  return hip_status(hope::launch_chain(p, d, s));
+}
+
+const char* hope_status_string(hope_status_t status) {
+  switch (status) {
+    case HOPE_OK: return "HOPE_OK";
+    case HOPE_ERR_INVALID_ARG: return "HOPE_ERR_INVALID_ARG";
+    case HOPE_ERR_UNSUPPORTED: return "HOPE_ERR_UNSUPPORTED";
+    case HOPE_ERR_WORKSPACE: return "HOPE_ERR_WORKSPACE";
+    case HOPE_ERR_HIP: return "HOPE_ERR_HIP";
+  }
+  return "HOPE_ERR_UNKNOWN";
+}
+
+int hope_last_hip_error(void) { return g_last_hip_error; }
+
+hope_status_t hope_debug_cross_scan(const hope_fmap_t* x, uint32_t dirs, void* routes,
+                                    hipStream_t stream) {
+  hope_status_t st = check_fmap(x);
+  if (st != HOPE_OK) return st;
+  if (!routes || !aligned(routes, 16) || dirs == 0 || dirs > 15) return HOPE_ERR_INVALID_ARG;
+  int route_of_slot[4];
+  const int n_sel = slots_of(dirs, route_of_slot);
+  const int eb = x->dtype == HOPE_BF16 ? 2 : 4;
+  const size_t n_elem = (size_t)x->B * x->H * x->W * x->D;
+  if (overlaps(range_of(routes, n_elem * n_sel * eb), range_of(x->data, n_elem * eb)))
+    return HOPE_ERR_INVALID_ARG;
+  return hip_status(hope::launch_cross_scan(x->data, eb, x->B, x->H, x->W, x->D, route_of_slot,
+                                            n_sel, routes, stream));
+}
+
+hope_status_t hope_debug_cross_merge(const void* routes, int32_t dtype, int32_t B, int32_t H,
+                                     int32_t W, int32_t D, uint32_t dirs, float* out,
+                                     hipStream_t stream) {
+  if (!routes || !out || !aligned(routes, 16) || !aligned(out, 16)) return HOPE_ERR_INVALID_ARG;
+  if (dtype != HOPE_F32 && dtype != HOPE_BF16) return HOPE_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || W <= 0 || D <= 0 || dirs == 0 || dirs > 15) return HOPE_ERR_INVALID_ARG;
+  if ((int64_t)H * W > INT32_MAX) return HOPE_ERR_INVALID_ARG;
+  int route_of_slot[4];
+  const int n_sel = slots_of(dirs, route_of_slot);
+  const int eb = dtype == HOPE_BF16 ? 2 : 4;
+  const size_t n_elem = (size_t)B * H * W * D;
+  if (overlaps(range_of(routes, n_elem * n_sel * eb), range_of(out, n_elem * sizeof(float))))
+    return HOPE_ERR_INVALID_ARG;
+  return hip_status(hope::launch_cross_merge(routes, dtype == HOPE_BF16, B, H, W, D, route_of_slot,
+                                             n_sel, out, stream));
+}
+
+}  // extern "C"

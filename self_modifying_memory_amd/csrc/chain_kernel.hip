@@ -1,0 +1,264 @@
+// Fused chunked recurrence of one (image, head, route) chain per workgroup, gfx950.
+//
+// Method ("VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"):
+//   Sec. 2.3 Eq. 24-25   route order and row/column-aligned chunks;
+//   Sec. 2.1.3 Eq. 15-16 k, v, q, eta, alpha and y = M_mem q from the chunk-start state;
+//   Sec. 2.2 Eq. 19-20   executed step (soft injection cap, spectral clamp) with the
+//                        App. B.3 inward factors, |k|^2 floor and one-ulp rounding;
+//   App. B.4 Eq. 46      one gain G per chunk, G_t = alpha_t G_{t-1} - step_t (G_{t-1} k_t
+//                        + delta_t) k_t^T, shared by all six memories: S_end = S_b G_C.
+//
+// Layout: the fp32 state (4d+2 rows of d: M_mem, M_k, M_v, M_q, m_eta, m_alpha) stays
+// in LDS for the whole sequence; tokens are processed in blocks of kTB; each thread
+// keeps a strip of one row of G in registers.
+#include "kernels.h"
+
+namespace hope {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTB = 16;  // tokens per LDS block
+
+__device__ __forceinline__ int route_pixel(int r, int t, int H, int W, int N) {
+  if (r & 1) t = N - 1 - t;          // routes 1 and 3 are full reversals
+  if (r < 2) return t;               // row-major
+  return (t % H) * W + (t / H);      // column-major: flatten of the spatial transpose
+}
+
+__device__ __forceinline__ float load_x(const void* x, int bf16, int64_t idx) {
+  if (bf16) {
+    uint32_t b = static_cast<const uint16_t*>(x)[idx];
+    return __uint_as_float(b << 16);
+  }
+  return static_cast<const float*>(x)[idx];
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
+  constexpr int R = 4 * D + 2;        // state rows
+  constexpr int SP = D + 1;           // padded LDS row stride of state / tokens / gain
+  constexpr int NP = 3 * D + 2;       // projected rows: k, v, q, s_eta, s_alpha
+  constexpr int PS = NP + 1;          // padded per-token stride of the projections
+  constexpr int TPR = kThreads / D;   // threads per gain row
+  constexpr int CPT = D / TPR;        // gain columns per thread
+  constexpr int NG = kThreads / D;    // row groups of the state update
+
+  __shared__ float S[R * SP];
+  __shared__ float X[kTB * SP];
+  __shared__ float P[kTB * PS];
+  __shared__ float Gl[D * SP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nh = p.nh;
+  const int h = blockIdx.x % nh;
+  const int b = (blockIdx.x / nh) % p.B;
+  const int slot = blockIdx.x / (nh * p.B);
+  const int r = p.route_of_slot[slot];
+  const int H = p.H, W = p.W, N = H * W, Dt = p.D;
+  const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
+  const int64_t SS = 4 * D * D + 2 * D;
+
+  float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
+  const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h
+                                                 : (int64_t)r * nh + h) * SS;
+  for (int e = tid; e < R * D; e += kThreads) S[(e / D) * SP + e % D] = init[e];
+
+  const int grow = tid / TPR;         // gain row owned by this thread
+  const int gcol0 = (tid % TPR) * CPT;
+  const float eps = p.eps;
+  __syncthreads();
+
+  for (int s0 = 0; s0 < N; s0 += C) {
+    const int s1 = min(s0 + C, N);
+    float g[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) g[c] = (gcol0 + c == grow) ? 1.f : 0.f;
+
+    for (int tb = s0; tb < s1; tb += kTB) {
+      const int nt = min(kTB, s1 - tb);
+      // gather the block's tokens in route order
+      for (int e = tid; e < nt * D; e += kThreads) {
+        const int t = e / D, i = e % D;
+        const int pix = route_pixel(r, tb + t, H, W, N);
+        X[t * SP + i] = load_x(p.x, p.x_bf16, ((int64_t)b * N + pix) * Dt + (int64_t)h * D + i);
+      }
+      __syncthreads();
+      // projections from the chunk-start memories (Eq. 15): rows D.. of the state
+      for (int e = tid; e < nt * NP; e += kThreads) {
+        const int t = e % nt, j = e / nt;
+        const float* srow = &S[(D + j) * SP];
+        const float* xrow = &X[t * SP];
+        float acc = 0.f;
+#pragma unroll 16
+        for (int i = 0; i < D; ++i) acc = fmaf(srow[i], xrow[i], acc);
+        P[t * PS + j] = acc;
+      }
+      __syncthreads();
+      // gates and executed step (Eq. 19-20), one wave per token
+      for (int t = wave; t < nt; t += kThreads / 64) {
+        float* pt = &P[t * PS];
+        const float kr = lane < D ? pt[lane] : 0.f;
+        const float vr = lane < D ? pt[D + lane] : 0.f;
+        const float qr = lane < D ? pt[2 * D + lane] : 0.f;
+        const float s_eta = pt[3 * D];
+        const float s_alpha = pt[3 * D + 1];
+        const float k = kr / sqrtf(wave_sum(kr * kr) + 1e-6f);
+        const float q = qr / sqrtf(wave_sum(qr * qr) + 1e-6f);
+        const float dl = k - vr;
+        const float dd = wave_sum(dl * dl);
+        const float kk = wave_sum(k * k);
+        float eta;
+        if (p.eta_map == 0) {
+          eta = p.eta_scale / (1.f + expf(-s_eta));
+        } else {
+          eta = p.eta_scale * (fmaxf(s_eta, 0.f) + log1pf(expf(-fabsf(s_eta))));
+        }
+        const float z = s_alpha + p.alpha_bias;
+        const float alpha = 1.f / (1.f + expf(-z));
+        const float one_minus_alpha = 1.f / (1.f + expf(z));
+        const float rr = sqrtf(dd + eps * eps) + eps;
+        const float inj = (1.f - 1e-3f) * one_minus_alpha / rr;
+        const float bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta / inj);
+        float spec = (1.f - 1e-6f) * 2.f * alpha / fmaxf(kk, 1e-20f);
+        if (spec > 0.f) spec = __uint_as_float(__float_as_uint(spec) - 1u);  // one ulp toward 0
+        const float step = fminf(bar, spec);
+        if (lane < D) {
+          pt[lane] = k;
+          pt[D + lane] = dl;
+          pt[2 * D + lane] = q;
+        }
+        if (lane == 0) {
+          pt[3 * D] = step;
+          pt[3 * D + 1] = alpha;
+        }
+      }
+      __syncthreads();
+      // readout y_t = M_mem,b q_t (Eq. 16), written at the token's pixel
+      for (int e = tid; e < nt * D; e += kThreads) {
+        const int t = e / D, i = e % D;
+        const float* mrow = &S[i * SP];
+        const float* qv = &P[t * PS + 2 * D];
+        float acc = 0.f;
+#pragma unroll 16
+        for (int j = 0; j < D; ++j) acc = fmaf(mrow[j], qv[j], acc);
+        const int pix = route_pixel(r, tb + t, H, W, N);
+        dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + i] = acc;
+      }
+      // shared gain, token by token (Eq. 46)
+      for (int t = 0; t < nt; ++t) {
+        const float* pt = &P[t * PS];
+        float w = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) w = fmaf(g[c], pt[gcol0 + c], w);
+#pragma unroll
+        for (int off = TPR / 2; off >= 1; off >>= 1) w += __shfl_xor(w, off, 64);
+        const float step = pt[3 * D], alpha = pt[3 * D + 1];
+        const float u = -step * (w + pt[D + grow]);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) g[c] = fmaf(alpha, g[c], u * pt[gcol0 + c]);
+      }
+      __syncthreads();
+    }
+    // carry: S <- S_b G_C for all six memories at once
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) Gl[grow * SP + gcol0 + c] = g[c];
+    __syncthreads();
+    {
+      // rows are independent, so the product runs in passes of kRB rows per
+      // thread; a barrier separates each pass's reads from its in-place writes
+      constexpr int kRB = 8;
+      const int col = tid % D, grp = tid / D;
+      float gc[D];
+#pragma unroll
+      for (int j = 0; j < D; ++j) gc[j] = Gl[j * SP + col];
+#pragma unroll 1
+      for (int r0 = 0; r0 < R; r0 += kRB * NG) {
+        float acc[kRB];
+#pragma unroll
+        for (int k = 0; k < kRB; ++k) {
+          const int row = r0 + grp + k * NG;
+          float a = 0.f;
+          if (row < R) {
+            const float* srow = &S[row * SP];
+#pragma unroll
+            for (int j = 0; j < D; ++j) a = fmaf(srow[j], gc[j], a);
+          }
+          acc[k] = a;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kRB; ++k) {
+          const int row = r0 + grp + k * NG;
+          if (row < R) S[row * SP + col] = acc[k];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (p.final_mem) {
+    float* fin = p.final_mem + (((int64_t)b * 4 + r) * nh + h) * SS;
+    for (int e = tid; e < R * D; e += kThreads) fin[e] = S[(e / D) * SP + e % D];
+  }
+
+  // Restore-and-sum (Eq. 26, unit scales): slot 0 wrote into out, the other slots into
+  // workspace planes.  The last chain of this (image, head) to arrive adds the planes
+  // into out in slot order, so the sum is deterministic whoever arrives last.  No
+  // workgroup ever waits on another.
+  if (p.n_sel > 1) {
+    __shared__ int is_last;
+    __threadfence();                       // release this chain's readouts (agent scope)
+    __syncthreads();
+    if (tid == 0) {
+      const int prev = atomicAdd(&p.counters[(int64_t)b * nh + h], 1);
+      is_last = prev == p.n_sel - 1;
+    }
+    __syncthreads();
+    if (is_last) {
+      __threadfence();                     // acquire the other chains' readouts
+      for (int64_t e = tid; e < (int64_t)N * D; e += kThreads) {
+        const int64_t idx = ((int64_t)b * N + e / D) * Dt + (int64_t)h * D + e % D;
+        float a = p.out[idx];
+        for (int k = 0; k < p.n_sel - 1; ++k) a += p.planes[k * p.plane_stride + idx];
+        p.out[idx] = a;
+      }
+    }
+  }
+}
+
+__global__ void zero_ints_kernel(int* p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
+  dim3 grid((unsigned)blocks), block(kThreads);
+  switch (d) {
+    case 16: hipLaunchKernelGGL(chain_kernel<16>, grid, block, 0, stream, p); break;
+    case 32: hipLaunchKernelGGL(chain_kernel<32>, grid, block, 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(chain_kernel<64>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t stream) {
+  int64_t g = (n + 255) / 256;
+  if (g > 1024) g = 1024;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)g), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace hope

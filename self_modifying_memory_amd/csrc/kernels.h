@@ -1,0 +1,42 @@
+// Internal launch interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hope {
+
+// One (image, head, route) recurrence per workgroup.
+struct ChainParams {
+  const void* x;          // [B][H][W][D], fp32 or bf16
+  const float* init;      // [4][nh][S] or [B][4][nh][S]
+  float* out;             // [B][H][W][D] fp32: plane of slot 0
+  float* planes;          // slots 1..n_sel-1: planes + (slot-1)*plane_stride
+  int* counters;          // [B*nh] arrival counters of the route chains (zeroed per call)
+  float* final_mem;       // [B][4][nh][S] or nullptr
+  int64_t plane_stride;   // elements between consecutive workspace planes
+  int x_bf16;
+  int B, H, W, D, nh;
+  int n_sel;              // number of selected routes
+  int route_of_slot[4];   // route index of each slot, increasing
+  int chunk;              // 0 = aligned
+  int init_per_image;
+  int eta_map;            // 0 sigmoid, 1 softplus
+  float eta_scale, alpha_bias, eps;
+};
+
+hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
+
+// Zero n ints (the arrival counters) with a kernel, so the call stays capturable.
+hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t stream);
+
+// Bit-exact permutation of x into route order: routes[slot][b][t][c] = x[b][p_r(t)][c].
+hipError_t launch_cross_scan(const void* x, int elem_bytes, int B, int H, int W, int D,
+                             const int* route_of_slot, int n_sel, void* routes, hipStream_t stream);
+
+// out[b][p][c] = sum over slots (increasing route) of routes[slot][b][p_r^-1(p)][c].
+hipError_t launch_cross_merge(const void* routes, int bf16, int B, int H, int W, int D,
+                              const int* route_of_slot, int n_sel, float* out, hipStream_t stream);
+
+}  // namespace hope

@@ -1,0 +1,127 @@
+// Route permutations and the fixed-order route sum, gfx950.
+//
+// Orders: "VMamba: Visual State Space Model" (explainer), the four scan orders:
+// row-major, the flatten of the spatial transpose, and the full reversal of each;
+// "VisionHOPE: Visual Backbones as Self-Modifying Learning Systems" Sec. 2.3 Eq. 24.
+// Merge: restore each route to its pixel, then add (VisionHOPE Eq. 26, unit scales).
+// All kernels are HBM-bound streaming kernels: consecutive threads touch
+// consecutive channels of one pixel, so every wave reads/writes contiguous runs.
+#include "kernels.h"
+
+namespace hope {
+namespace {
+
+struct Routes4 {
+  int r[4];
+};
+
+__device__ __forceinline__ int64_t route_pixel64(int r, int64_t t, int H, int W, int64_t N) {
+  if (r & 1) t = N - 1 - t;
+  if (r < 2) return t;
+  return (t % H) * W + (t / H);
+}
+
+// inverse: sequence index of pixel p on route r
+__device__ __forceinline__ int64_t route_step64(int r, int64_t p, int H, int W, int64_t N) {
+  int64_t t = p;
+  if (r >= 2) {
+    const int64_t hh = p / W, ww = p % W;
+    t = ww * H + hh;
+  }
+  if (r & 1) t = N - 1 - t;
+  return t;
+}
+
+template <typename T>
+__global__ void cross_scan_kernel(const T* __restrict__ x, int B, int H, int W, int D, Routes4 rs,
+                                  int n_sel, T* __restrict__ routes) {
+  const int64_t N = (int64_t)H * W;
+  const int64_t per_route = (int64_t)B * N * D;
+  const int64_t total = per_route * n_sel;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(e / per_route);
+    int64_t rem = e - slot * per_route;
+    const int c = (int)(rem % D);
+    rem /= D;
+    const int64_t t = rem % N;
+    const int64_t b = rem / N;
+    const int64_t p = route_pixel64(rs.r[slot], t, H, W, N);
+    routes[e] = x[(b * N + p) * D + c];
+  }
+}
+
+template <bool BF16>
+__global__ void cross_merge_kernel(const void* __restrict__ routes, int B, int H, int W, int D,
+                                   Routes4 rs, int n_sel, float* __restrict__ out) {
+  const int64_t N = (int64_t)H * W;
+  const int64_t per_route = (int64_t)B * N * D;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < per_route;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e % D);
+    const int64_t rem = e / D;
+    const int64_t p = rem % N;
+    const int64_t b = rem / N;
+    float acc = 0.f;
+    for (int s = 0; s < n_sel; ++s) {
+      const int64_t t = route_step64(rs.r[s], p, H, W, N);
+      const int64_t idx = s * per_route + (b * N + t) * D + c;
+      float v;
+      if (BF16) {
+        v = __uint_as_float((uint32_t)static_cast<const uint16_t*>(routes)[idx] << 16);
+      } else {
+        v = static_cast<const float*>(routes)[idx];
+      }
+      acc = s == 0 ? v : acc + v;
+    }
+    out[e] = acc;
+  }
+}
+
+unsigned grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  const int64_t cap = 256 * 64;  // enough waves to saturate HBM; grid-stride beyond
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_cross_scan(const void* x, int elem_bytes, int B, int H, int W, int D,
+                             const int* route_of_slot, int n_sel, void* routes,
+                             hipStream_t stream) {
+  Routes4 rs{{0, 0, 0, 0}};
+  for (int i = 0; i < n_sel; ++i) rs.r[i] = route_of_slot[i];
+  const int64_t total = (int64_t)n_sel * B * H * W * D;
+  const dim3 grid(grid_for(total, 256)), block(256);
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(cross_scan_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), B, H, W, D, rs, n_sel,
+                       static_cast<uint16_t*>(routes));
+  } else {
+    hipLaunchKernelGGL(cross_scan_kernel<uint32_t>, grid, block, 0, stream,
+                       static_cast<const uint32_t*>(x), B, H, W, D, rs, n_sel,
+                       static_cast<uint32_t*>(routes));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cross_merge(const void* routes, int bf16, int B, int H, int W, int D,
+                              const int* route_of_slot, int n_sel, float* out,
+                              hipStream_t stream) {
+  Routes4 rs{{0, 0, 0, 0}};
+  for (int i = 0; i < n_sel; ++i) rs.r[i] = route_of_slot[i];
+  const int64_t total = (int64_t)B * H * W * D;
+  const dim3 grid(grid_for(total, 256)), block(256);
+  if (bf16) {
+    hipLaunchKernelGGL(cross_merge_kernel<true>, grid, block, 0, stream, routes, B, H, W, D, rs,
+                       n_sel, out);
+  } else {
+    hipLaunchKernelGGL(cross_merge_kernel<false>, grid, block, 0, stream, routes, B, H, W, D, rs,
+                       n_sel, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hope

@@ -1,0 +1,156 @@
+"""Python binding of the C ABI over torch device tensors.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+libhopescan.so.  torch supplies device memory and the stream.  Function names
+follow include/hope_scan2d.h.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native as N
+
+_ETA_MAPS = {"sigmoid": N.HOPE_ETA_SIGMOID, "softplus": N.HOPE_ETA_SOFTPLUS}
+
+
+class HopeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = N.load_library()
+        name = lib.hope_status_string(status).decode()
+        extra = f" (hipError {lib.hope_last_hip_error()})" if status == N.HOPE_ERR_HIP else ""
+        super().__init__(f"{where}: {name}{extra}")
+        self.status = status
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return N.HOPE_F32
+    if t.dtype == torch.bfloat16:
+        return N.HOPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _require_device(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def make_fmap(x: torch.Tensor, n_heads: int) -> N.hope_fmap_t:
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, W, D]")
+    B, H, W, D = x.shape
+    return N.hope_fmap_t(x.data_ptr(), _dtype_code(x), B, H, W, D, n_heads)
+
+
+def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
+              alpha_bias: float = 4.0, eps: float = 1e-6, init_per_image: bool = False,
+              final_memories: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> N.hope_scan2d_opts_t:
+    lib = N.load_library()
+    o = N.hope_scan2d_opts_t()
+    lib.hope_scan2d_default_opts(ctypes.byref(o))
+    o.stream = _stream_handle(stream)
+    o.eta_map = _ETA_MAPS[eta_map]
+    o.eta_scale = eta_scale
+    o.alpha_bias = alpha_bias
+    o.eps = eps
+    o.init_per_image = int(bool(init_per_image))
+    if final_memories is not None:
+        _require_device(final_memories, "final_memories")
+        if final_memories.dtype != torch.float32:
+            raise TypeError("final_memories must be float32")
+        o.final_memories = final_memories.data_ptr()
+    if workspace is not None:
+        _require_device(workspace, "workspace")
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    return o
+
+
+def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0) -> int:
+    lib = N.load_library()
+    fm = make_fmap(x, n_heads)
+    return int(lib.hope_scan2d_workspace_size(ctypes.byref(fm), dirs, chunk, None))
+
+
+def alloc_workspace(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0) -> torch.Tensor | None:
+    """A workspace of the size the library asks for (None when none is needed)."""
+    nbytes = hope_scan2d_workspace_size(x, n_heads, dirs, chunk)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+
+
+def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: int, dirs: int = 15,
+                        chunk: int = 0, out: torch.Tensor | None = None, *, stream=None,
+                        eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
+                        eps: float = 1e-6, init_per_image: bool = False,
+                        final_memories: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32).
+
+    init_memories: float32 [4, n_heads, 4d^2+2d] (or [B, 4, n_heads, ...] with
+    init_per_image).  A workspace is allocated through torch when none is given.
+    """
+    lib = N.load_library()
+    _require_device(x, "x")
+    _require_device(init_memories, "init_memories")
+    if init_memories.dtype != torch.float32:
+        raise TypeError("init_memories must be float32")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _require_device(out, "out")
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must be float32 with the shape of x")
+    if workspace is None:
+        workspace = alloc_workspace(x, n_heads, dirs, chunk)
+    fm = make_fmap(x, n_heads)
+    opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
+                     workspace)
+    st = lib.hope_scan2d_forward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
+                                 out.data_ptr(), ctypes.byref(opts))
+    if st != N.HOPE_OK:
+        raise HopeError(st, "hope_scan2d_forward")
+    return out
+
+
+def hope_debug_cross_scan(x: torch.Tensor, dirs: int = 15, routes: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """routes[slot, b, t, c] = x[b, p_r(t), c] for the selected routes (bit-exact)."""
+    lib = N.load_library()
+    _require_device(x, "x")
+    B, H, W, D = x.shape
+    n_sel = bin(dirs & 15).count("1")
+    if routes is None:
+        routes = torch.empty((max(n_sel, 1), B, H * W, D), dtype=x.dtype, device=x.device)
+    _require_device(routes, "routes")
+    fm = make_fmap(x, 1)
+    st = lib.hope_debug_cross_scan(ctypes.byref(fm), dirs, routes.data_ptr(), _stream_handle(stream))
+    if st != N.HOPE_OK:
+        raise HopeError(st, "hope_debug_cross_scan")
+    return routes
+
+
+def hope_debug_cross_merge(routes: torch.Tensor, H: int, W: int, dirs: int = 15,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out[b, p, c] = sum over selected routes of routes[slot, b, p_r^-1(p), c] (fp32)."""
+    lib = N.load_library()
+    _require_device(routes, "routes")
+    _, B, Nn, D = routes.shape
+    if out is None:
+        out = torch.empty((B, H, W, D), dtype=torch.float32, device=routes.device)
+    _require_device(out, "out")
+    st = lib.hope_debug_cross_merge(routes.data_ptr(), _dtype_code(routes), B, H, W, D, dirs,
+                                    out.data_ptr(), _stream_handle(stream))
+    if st != N.HOPE_OK:
+        raise HopeError(st, "hope_debug_cross_merge")
+    return out

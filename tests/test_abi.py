@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol,
+its structs have the C layout, and every validation error returns before anything
+is enqueued.  No test here launches a kernel; the device pointers passed to the
+rejected calls are never dereferenced (validation is pure pointer arithmetic).
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from self_modifying_memory_amd import _native as N
+
+FAKE = 1 << 40          # 256-byte aligned address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return N.load_library()
+
+
+def fmap(B=2, H=4, W=5, D=32, nh=1, dtype=N.HOPE_F32, data=FAKE):
+    return N.hope_fmap_t(data, dtype, B, H, W, D, nh)
+
+
+def opts(lib, **kw):
+    o = N.hope_scan2d_opts_t()
+    lib.hope_scan2d_default_opts(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def call(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, out=FAKE + (2 << 30), o=None):
+    return lib.hope_scan2d_forward(ctypes.byref(x), init, dirs, chunk, out,
+                                   ctypes.byref(o) if o is not None else None)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = N.header_functions()
+    assert "hope_scan2d_forward" in names and len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_c():
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "hope_scan2d.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
+         offsetof(hope_fmap_t, dtype), offsetof(hope_fmap_t, n_heads),
+         offsetof(hope_scan2d_opts_t, final_memories), offsetof(hope_scan2d_opts_t, workspace_bytes),
+         offsetof(hope_scan2d_opts_t, eta_map), offsetof(hope_scan2d_opts_t, eta_scale),
+         offsetof(hope_scan2d_opts_t, eps), offsetof(hope_scan2d_opts_t, init_per_image),
+         offsetof(hope_scan2d_opts_t, reserved));
+  return 0;
+}
+"""
+    tmp = os.path.join(os.environ.get("TMPDIR", "/tmp"), f"hope_abi_{os.getpid()}")
+    os.makedirs(tmp, exist_ok=True)
+    with open(os.path.join(tmp, "abi.c"), "w") as f:
+        f.write(src)
+    exe = os.path.join(tmp, "abi")
+    inc = os.path.dirname(N.HEADER_PATH)
+    res = subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include",
+                          os.path.join(tmp, "abi.c"), "-o", exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    F, O = N.hope_fmap_t, N.hope_scan2d_opts_t
+    want = [ctypes.sizeof(F), ctypes.sizeof(O), F.dtype.offset, F.n_heads.offset,
+            O.final_memories.offset, O.workspace_bytes.offset, O.eta_map.offset, O.eta_scale.offset,
+            O.eps.offset, O.init_per_image.offset, O.reserved.offset]
+    assert vals == want
+
+
+def test_default_opts_and_status_strings(lib):
+    o = opts(lib)
+    assert (o.eta_map, o.eta_scale, o.alpha_bias, o.init_per_image) == (0, 1.0, 4.0, 0)
+    assert abs(o.eps - 1e-6) < 1e-12 and o.final_memories is None and o.workspace is None
+    for code, name in [(0, b"HOPE_OK"), (-1, b"HOPE_ERR_INVALID_ARG"), (-2, b"HOPE_ERR_UNSUPPORTED"),
+                       (-3, b"HOPE_ERR_WORKSPACE"), (-4, b"HOPE_ERR_HIP")]:
+        assert lib.hope_status_string(code) == name
+    assert lib.hope_last_hip_error() == 0
+
+
+def test_workspace_size(lib):
+    x = fmap(B=2, H=4, W=5, D=32)
+    n = 2 * 4 * 5 * 32
+    plane = (n + 63) // 64 * 64 * 4
+    cnt = 256
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, None) == cnt + 3 * plane
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 5, 0, None) == cnt + plane
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 4, 0, None) == 0
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(fmap(B=0)), 15, 0, None) == 0
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 0, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), N.HOPE_ERR_INVALID_ARG),
+    (dict(H=-1), N.HOPE_ERR_INVALID_ARG),
+    (dict(W=0), N.HOPE_ERR_INVALID_ARG),
+    (dict(D=33), N.HOPE_ERR_INVALID_ARG),            # not a multiple of n_heads (33 % 2)
+    (dict(dtype=7), N.HOPE_ERR_INVALID_ARG),
+    (dict(data=0), N.HOPE_ERR_INVALID_ARG),
+    (dict(data=FAKE + 8), N.HOPE_ERR_INVALID_ARG),    # misaligned
+    (dict(D=16, nh=2), N.HOPE_ERR_UNSUPPORTED),       # d = 8
+    (dict(D=96, nh=1), N.HOPE_ERR_UNSUPPORTED),       # d = 96
+])
+def test_shape_errors(lib, kw, code):
+    base = dict(B=2, H=4, W=5, D=32, nh=2)
+    base.update(kw)
+    x = fmap(**base)
+    assert call(lib, x, o=opts(lib)) == code
+
+
+def test_argument_errors(lib):
+    x = fmap()
+    o = opts(lib)
+    assert call(lib, x, dirs=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, dirs=16, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, chunk=-1, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, init=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, out=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, out=FAKE + (2 << 30) + 4, o=o) == N.HOPE_ERR_INVALID_ARG
+    # out overlapping x / init
+    assert call(lib, x, out=FAKE + 256, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, out=FAKE + (1 << 30), o=o) == N.HOPE_ERR_INVALID_ARG
+    for k, v in [("eta_map", 2), ("eta_scale", -1.0), ("eta_scale", float("nan")),
+                 ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("reserved", 1)]:
+        assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k
+    # final memories overlapping out, misaligned workspace
+    assert call(lib, x, o=opts(lib, final_memories=FAKE + (2 << 30))) == N.HOPE_ERR_INVALID_ARG
+    assert call(lib, x, o=opts(lib, workspace=FAKE + (3 << 30) + 16,
+                               workspace_bytes=1 << 20)) == N.HOPE_ERR_INVALID_ARG
+
+
+def test_workspace_errors(lib):
+    x = fmap()
+    need = lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, None)
+    assert call(lib, x, o=opts(lib)) == N.HOPE_ERR_WORKSPACE
+    assert call(lib, x, o=None) == N.HOPE_ERR_WORKSPACE
+    small = opts(lib, workspace=FAKE + (3 << 30), workspace_bytes=need - 4)
+    assert call(lib, x, o=small) == N.HOPE_ERR_WORKSPACE
+    overlap = opts(lib, workspace=FAKE + (2 << 30), workspace_bytes=need)
+    assert call(lib, x, o=overlap) == N.HOPE_ERR_INVALID_ARG
+
+
+def test_debug_export_errors(lib):
+    x = fmap()
+    assert lib.hope_debug_cross_scan(ctypes.byref(x), 0, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_debug_cross_scan(ctypes.byref(x), 15, FAKE + 64, None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_debug_cross_scan(ctypes.byref(fmap(B=0)), 15, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_debug_cross_merge(FAKE, 3, 2, 4, 5, 32, 15, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_debug_cross_merge(FAKE, 0, 2, 4, 5, 32, 15, FAKE + 64, None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_debug_cross_merge(FAKE, 0, 2, 0, 5, 32, 15, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG

@@ -1,0 +1,114 @@
+"""GPU parity of hope_scan2d_forward (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on the whole map; they span several token blocks,
+ragged chunks, rectangles, every head dimension, route subsets and both gate
+maps.  The full-size workloads run on the GPU at their real shape and launch
+configuration and are compared on sampled (image, head) slices, which the oracle
+computes exactly (all four routes of the slice).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from _parity import TOL, check_final, check_out, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # B, H, W, D, nh, dtype, dirs, chunk, live, extra
+    (1, 8, 8, 16, 1, "f32", 15, 0, False, {}),          # tiny workload as written: out == 0
+    (1, 8, 8, 16, 1, "f32", 15, 0, True, {}),
+    (2, 5, 7, 64, 2, "bf16", 15, 0, True, {}),          # rectangle, d = 32, two heads
+    (1, 6, 9, 64, 1, "f32", 15, 4, True, {}),           # d = 64, chunk 4 does not divide 54
+    (2, 3, 20, 48, 3, "f32", 15, 0, True, {}),          # d = 16, row chunks of 20 (> one block)
+    (1, 17, 3, 32, 1, "bf16", 5, 0, True, {}),          # routes -> and down only
+    (2, 4, 6, 32, 1, "f32", 2, 0, True, {}),            # a single route: no workspace
+    (1, 4, 5, 32, 1, "f32", 15, 1, True, {}),           # chunk 1: token-wise recurrence
+    (1, 4, 5, 32, 1, "f32", 15, 50, True, {}),          # one chunk longer than the map
+    (1, 1, 13, 16, 1, "f32", 15, 0, True, {}),          # one row
+    (1, 11, 1, 16, 1, "f32", 15, 0, True, {}),          # one column
+    (2, 6, 6, 64, 2, "f32", 15, 0, True,
+     dict(eta_map="softplus", eta_scale=0.025, alpha_bias=math.log(9.0))),  # VisionHOPE gates
+    (1, 5, 5, 16, 1, "f32", 15, 0, True, dict(eta_scale=50.0, alpha_bias=-3.0)),  # clamps active
+    (1, 40, 3, 32, 1, "f32", 12, 0, True, {}),          # column chunks of 40 tokens
+]
+
+
+def _case_id(c):
+    B, H, W, D, nh, dt, dirs, chunk, live, extra = c
+    return f"B{B}_{H}x{W}_D{D}h{nh}_{dt}_dirs{dirs}_c{chunk}_{'live' if live else 'lit'}" + \
+        ("_" + "_".join(f"{k}{v:g}" if isinstance(v, float) else f"{k}{v}" for k, v in extra.items())
+         if extra else "")
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_case_id(c) for c in SMALL])
+def test_small_maps_match_oracle(case):
+    B, H, W, D, nh, dt, dirs, chunk, live, extra = case
+    print("case", _case_id(case), flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=B * 1000 + H * 37 + W, dtype=dt, live=live)
+    out, fin = run_gpu(inp, nh, dt, dirs, chunk, **extra)
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], nh, dirs=dirs, chunk=chunk, **extra)
+    tol = TOL[dt]
+    e_out = check_out(out, ref_out, nh, tol)
+    e_fin = check_final(fin, ref_fin, D // nh, dirs, tol)
+    if not live:
+        assert np.all(out == 0.0)
+    for r in range(4):                              # unselected routes leave final untouched
+        if not (dirs >> r) & 1:
+            assert np.all(np.isnan(fin[:, r]))
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+def test_resume_from_final_state_on_gpu():
+    # The final state of rows [0, k) resumes rows [k, H) of the row-major route.
+    B, H, W, D = 2, 7, 5, 32
+    inp = wl.draw(B, H, W, D, 1, seed=77, live=True)
+    full, fin_full = run_gpu(inp, 1, "f32", dirs=1)
+    k = 3
+    a = {"x": np.ascontiguousarray(inp["x"][:, :k]), "init": inp["init"]}
+    out_a, fin_a = run_gpu(a, 1, "f32", dirs=1)
+    init_b = np.zeros((B, 4, 1, inp["init"].shape[-1]), dtype=np.float32)
+    init_b[:, 0] = fin_a[:, 0]
+    bpart = {"x": np.ascontiguousarray(inp["x"][:, k:]), "init": init_b}
+    out_b, fin_b = run_gpu(bpart, 1, "f32", dirs=1, init_per_image=True)
+    np.testing.assert_allclose(np.concatenate([out_a, out_b], 1), full, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(fin_b[:, 0], fin_full[:, 0], rtol=1e-5, atol=1e-6)
+
+
+def test_deterministic_bitwise():
+    w = wl.WORKLOADS[2].with_batch(8)
+    inp = wl.draw_workload(w, live=True)
+    o1, f1 = run_gpu(inp, w.n_heads, w.dtype)
+    o2, f2 = run_gpu(inp, w.n_heads, w.dtype)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+# Full-size workloads: the GPU runs the whole map; the oracle checks sampled slices.
+SAMPLES = {1: ([0, 15], [0, 2]), 2: ([0, 63], [1, 5]), 3: ([0, 127], [0, 5]), 4: ([1], [2])}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_full_size_workloads_sampled(idx):
+    w = wl.WORKLOADS[idx]
+    images, heads = SAMPLES[idx]
+    print(f"workload {w.name}: images {images} heads {heads}", flush=True)
+    inp = wl.draw_workload(w, live=True)
+    out, fin = run_gpu(inp, w.n_heads, w.dtype)
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, heads=heads, images=images)
+    e_out = check_out(out, ref_out, w.n_heads, TOL[w.dtype], heads=heads, images=images)
+    e_fin = check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=heads, images=images)
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+def test_full_size_literal_workload_reads_zero():
+    # The workload as written (M_mem = 0) reads exactly zero everywhere (Eq. 46 fixed point).
+    w = wl.WORKLOADS[3]
+    inp = wl.draw_workload(w, live=False)
+    out, fin = run_gpu(inp, w.n_heads, w.dtype)
+    assert np.all(out == 0.0)
+    assert np.all(fin[..., : w.d * w.d] == 0.0)
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, heads=[3], images=[64])
+    check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=[3], images=[64])
