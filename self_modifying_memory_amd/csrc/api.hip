@@ -178,6 +178,7 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
     st = hip_status(hope::launch_zero_ints(p.counters, (int64_t)x->B * x->n_heads, s));
     if (st != HOPE_OK) return st;
   }
+  if (hope::mfma_path_supported(p, d)) return hip_status(hope::launch_chain_mfma(p, d, s));
   return hip_status(hope::launch_chain(p, d, s));
 }
 

@@ -11,6 +11,7 @@
 // Layout: the fp32 state (4d+2 rows of d: M_mem, M_k, M_v, M_q, m_eta, m_alpha) stays
 // in LDS for the whole sequence; tokens are processed in blocks of kTB; each thread
 // keeps a strip of one row of G in registers.
+#include "device_common.h"
 #include "kernels.h"
 
 namespace hope {
@@ -19,24 +20,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTB = 16;  // tokens per LDS block
 
-__device__ __forceinline__ int route_pixel(int r, int t, int H, int W, int N) {
-  if (r & 1) t = N - 1 - t;          // routes 1 and 3 are full reversals
-  if (r < 2) return t;               // row-major
-  return (t % H) * W + (t / H);      // column-major: flatten of the spatial transpose
-}
-
 __device__ __forceinline__ float load_x(const void* x, int bf16, int64_t idx) {
   if (bf16) {
     uint32_t b = static_cast<const uint16_t*>(x)[idx];
     return __uint_as_float(b << 16);
   }
   return static_cast<const float*>(x)[idx];
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
 }
 
 template <int D>
@@ -73,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
 
   const int grow = tid / TPR;         // gain row owned by this thread
   const int gcol0 = (tid % TPR) * CPT;
-  const float eps = p.eps;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps};
   __syncthreads();
 
   for (int s0 = 0; s0 < N; s0 += C) {
@@ -108,28 +97,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         const float kr = lane < D ? pt[lane] : 0.f;
         const float vr = lane < D ? pt[D + lane] : 0.f;
         const float qr = lane < D ? pt[2 * D + lane] : 0.f;
-        const float s_eta = pt[3 * D];
-        const float s_alpha = pt[3 * D + 1];
-        const float k = kr / sqrtf(wave_sum(kr * kr) + 1e-6f);
-        const float q = qr / sqrtf(wave_sum(qr * qr) + 1e-6f);
-        const float dl = k - vr;
-        const float dd = wave_sum(dl * dl);
-        const float kk = wave_sum(k * k);
-        float eta;
-        if (p.eta_map == 0) {
-          eta = p.eta_scale / (1.f + expf(-s_eta));
-        } else {
-          eta = p.eta_scale * (fmaxf(s_eta, 0.f) + log1pf(expf(-fabsf(s_eta))));
-        }
-        const float z = s_alpha + p.alpha_bias;
-        const float alpha = 1.f / (1.f + expf(-z));
-        const float one_minus_alpha = 1.f / (1.f + expf(z));
-        const float rr = sqrtf(dd + eps * eps) + eps;
-        const float inj = (1.f - 1e-3f) * one_minus_alpha / rr;
-        const float bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta / inj);
-        float spec = (1.f - 1e-6f) * 2.f * alpha / fmaxf(kk, 1e-20f);
-        if (spec > 0.f) spec = __uint_as_float(__float_as_uint(spec) - 1u);  // one ulp toward 0
-        const float step = fminf(bar, spec);
+        const TokenGates tg = token_gates(kr, vr, qr, pt[3 * D], pt[3 * D + 1], gp);
+        const float k = tg.k, q = tg.q, dl = tg.delta, step = tg.step, alpha = tg.alpha;
         if (lane < D) {
           pt[lane] = k;
           pt[D + lane] = dl;

@@ -1,0 +1,505 @@
+// Chunked recurrence on MFMA: one (image, head, route) chain per workgroup of four
+// waves, for bf16 feature maps and head dimension 32 or 64 (gfx950).
+//
+// Method ("VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"):
+//   Sec. 2.1.3 Eq. 15-16  projections k, v, q, eta, alpha and the readout M_mem q are
+//                         generated from the chunk-start state S_b;
+//   Sec. 2.2 Eq. 19-20    executed step per token (shared helper token_gates);
+//   App. B.4 Eq. 46-47    all six memories follow one gain: S_end = S_b G_C with
+//                         G_t = alpha_t G_{t-1} + u_t k_t^T,  u_t = -step_t (G_{t-1} k_t + delta_t).
+//
+// The gain is applied in a compact (WY-like) form over blocks of up to 16 tokens.
+// Starting a block from gain G_s, with P(a, b) = prod_{a <= s < b} alpha_s:
+//   u_t = -step_t (P(0,t) G_s k_t + delta_t) - step_t sum_{j<t} P(j+1,t) (k_j . k_t) u_j
+//   G_end = P(0,n) G_s + sum_j P(j+1,n) u_j k_j^T =: c G_s + Ub^T K.
+// The state is then carried as S_b G = c (S_b G_s) + (S_b Ub^T) K, so the block costs two
+// thin products with S_b instead of a d x d x (4d+2) product per chunk.
+//
+// Precision: the state, the gain and every accumulation are fp32.  Each dense
+// contraction runs on bf16 MFMA with fp32 operands split as x = hi + lo (hi = bf16(x),
+// lo = bf16(x - hi), |x - hi - lo| <= 2^-17 |x|) and three products hi*hi + hi*lo + lo*hi;
+// the bf16 input tokens are exact, so the projections need two.
+//
+// Layout: the state stays in registers in the B-operand layout of a 16x16 MFMA tile:
+// lane l of the wave that owns state-row tile m holds, for column tile n,
+// S[16 m + (l & 15)][16 n + 4 (l >> 4) + i], i < 4.  Every product below is arranged
+// so that its output lands in that same layout (or in the operand layout of the next
+// product), so the state never goes through LDS.  A 32-deep k-step pairs column tiles
+// (2s, 2s+1); the A operands read their k values in the same pairing.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hope {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSB = 16;  // tokens per block = MFMA tile height
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+// c += a b with a, b given as hi/lo pairs (the lo*lo term is below fp32 resolution)
+__device__ __forceinline__ f32x4 mma32x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  c = mma32(al, bh, c);
+  c = mma32(ah, bl, c);
+  return mma32(ah, bh, c);
+}
+__device__ __forceinline__ f32x4 mma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 c) {
+  c = mma16(al, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(ah, bh, c);
+}
+
+__device__ __forceinline__ void split8(const f32x4 v0, const f32x4 v1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h0 = (__bf16)v0[e], h1 = (__bf16)v1[e];
+    hi[e] = h0;
+    hi[e + 4] = h1;
+    lo[e] = (__bf16)(v0[e] - (float)h0);
+    lo[e + 4] = (__bf16)(v1[e] - (float)h1);
+  }
+}
+__device__ __forceinline__ void split4(const f32x4 v, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = (__bf16)v[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(v[e] - (float)h);
+  }
+}
+
+// A-operand k values of step s for a token-major fp32 row: cols 32s+4g.. and 32s+16+4g..
+__device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f32x4& v0, f32x4& v1) {
+  v0 = *reinterpret_cast<const f32x4*>(row + 32 * s + 4 * g);
+  v1 = *reinterpret_cast<const f32x4*>(row + 32 * s + 16 + 4 * g);
+}
+
+template <int D, bool MULTI>
+__global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
+  constexpr int NT = D / 16;                       // column tiles of the state
+  constexpr int KS = D / 32;                       // 32-deep k-steps over the head dimension
+  constexpr int R = 4 * D + 2;                     // state rows: M_mem, M_k, M_v, M_q, m_eta, m_alpha
+  constexpr int MT = (R + 15) / 16;                // state-row tiles
+  constexpr int MTW = (MT + kWaves - 1) / kWaves;  // tiles per wave (round robin)
+  constexpr int LD = D + 4;                        // fp32 stride of token-major tiles
+  constexpr int XLD = D + 8;                       // bf16 stride of the token block
+  constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
+  constexpr int TLD = kSB + 4;
+
+  __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
+  __shared__ __attribute__((aligned(16))) float Ks[kSB * LD];
+  __shared__ __attribute__((aligned(16))) float Dls[kSB * LD];
+  __shared__ __attribute__((aligned(16))) float Qs[kSB * LD];
+  __shared__ __attribute__((aligned(16))) float Ubs[kSB * LD];
+  __shared__ __attribute__((aligned(16))) float GKs[MULTI ? kSB * LD : 4];
+  __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
+  __shared__ __attribute__((aligned(16))) float coef[kSB * TLD];  // coef[t][j], j < t
+  __shared__ __attribute__((aligned(16))) float alph[kSB];
+  __shared__ __attribute__((aligned(16))) float stp[kSB];
+  __shared__ float bco[kSB + 1];
+  __shared__ int is_last;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const int nh = p.nh;
+  const int h = blockIdx.x % nh;
+  const int b = (blockIdx.x / nh) % p.B;
+  const int slot = blockIdx.x / (nh * p.B);
+  const int r = p.route_of_slot[slot];
+  const int H = p.H, W = p.W, N = H * W, Dt = p.D;
+  const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
+  const int64_t SS = 4 * D * D + 2 * D;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps};
+  const unsigned short* xg = static_cast<const unsigned short*>(p.x);
+  float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
+
+  // ---- state in registers --------------------------------------------------------
+  f32x4 S[MTW][NT];
+  f32x4 Acc[MULTI ? MTW : 1][MULTI ? NT : 1];
+  {
+    const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h
+                                                   : (int64_t)r * nh + h) * SS;
+#pragma unroll
+    for (int mi = 0; mi < MTW; ++mi) {
+      const int row = (w + kWaves * mi) * 16 + c16;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row < R) v = *reinterpret_cast<const f32x4*>(init + row * D + n * 16 + 4 * g);
+        S[mi][n] = v;
+      }
+    }
+  }
+
+  // Tokens of the next block are loaded one block ahead into registers (8 channels
+  // per thread), so the HBM latency of the gather stays off the per-block critical path.
+  constexpr int kLoaders = kSB * (D / 8);
+  const int ld_t = threadIdx.x / (D / 8), ld_c8 = threadIdx.x % (D / 8);
+  auto fetch = [&](int tb, int nt) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (threadIdx.x < kLoaders && ld_t < nt) {
+      const int pix = route_pixel(r, tb + ld_t, H, W, N);
+      v = *reinterpret_cast<const u32x4*>(xg + ((int64_t)b * N + pix) * Dt + (int64_t)h * D + ld_c8 * 8);
+    }
+    return v;
+  };
+  u32x4 pf = fetch(0, min(kSB, min(C, N)));
+
+  // bf16 hi/lo split of the chunk-start state, shared by the projections, the readout
+  // and the carry of every block of the chunk (S_b is constant over the chunk)
+  bf16x8 Sh[MTW][KS], Sl[MTW][KS];
+
+  for (int s0 = 0; s0 < N; s0 += C) {
+    const int s1 = min(s0 + C, N);
+#pragma unroll
+    for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
+    if (MULTI) {
+#pragma unroll
+      for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) Acc[MULTI ? mi : 0][MULTI ? n : 0] = S[mi][n];
+    }
+    for (int tb = s0; tb < s1; tb += kSB) {
+      const int nt = min(kSB, s1 - tb);
+      const bool first = tb == s0;
+      const bool last_block = tb + kSB >= s1;
+
+      // P1: the prefetched block goes to LDS (zero past nt); the next block is requested
+      if (threadIdx.x < kLoaders) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
+      {
+        const int tn = last_block ? s1 : tb + kSB;
+        if (tn < N) {
+          const int cend = min((tn / C + 1) * C, N);
+          pf = fetch(tn, min(kSB, cend - tn));
+        }
+      }
+      lds_barrier();
+
+      // P2: projections P[t][row] = x_t . S_b[row] for the k, v, q, eta, alpha rows
+      {
+        bf16x8 xa[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const unsigned short* xr = Xs + c16 * XLD + 32 * s + 4 * g;
+          const u32x2 lo4 = *reinterpret_cast<const u32x2*>(xr);
+          const u32x2 hi4 = *reinterpret_cast<const u32x2*>(xr + 16);
+          const u32x4 both = {lo4[0], lo4[1], hi4[0], hi4[1]};
+          xa[s] = __builtin_bit_cast(bf16x8, both);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MTW; ++mi) {
+          const int m = w + kWaves * mi;
+          if (m < NT || m >= MT) continue;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            acc = mma32(xa[s], Sl[mi][s], acc);
+            acc = mma32(xa[s], Sh[mi][s], acc);
+          }
+          const int row = m * 16 + c16;
+          if (row < R) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pj[(4 * g + i) * PLD + row - D] = acc[i];
+          }
+        }
+      }
+      lds_barrier();
+
+      // P3: normalisation, gates and executed step; 16 lanes per token (one DPP row),
+      // each lane holding CPL consecutive components.  Padding tokens get no key, no
+      // write and unit retention.
+      {
+        constexpr int CPL = D / 16;
+        const int t = 4 * w + g;
+        const float* pt = Pj + t * PLD + c16 * CPL;
+        float kr[CPL], vr[CPL], qr[CPL];
+        float kk = 0.f, qq = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          kr[e] = pt[e];
+          vr[e] = pt[D + e];
+          qr[e] = pt[2 * D + e];
+          kk += kr[e] * kr[e];
+          qq += qr[e] * qr[e];
+        }
+        const float kinv = rsqrtf(row16_sum(kk) + gp.eps);
+        const float qinv = rsqrtf(row16_sum(qq) + gp.eps);
+        float kn[CPL], dl[CPL], qn[CPL];
+        float kk2 = 0.f, dd = 0.f;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          kn[e] = kr[e] * kinv;
+          qn[e] = qr[e] * qinv;
+          dl[e] = kn[e] - vr[e];
+          kk2 += kn[e] * kn[e];
+          dd += dl[e] * dl[e];
+        }
+        float alpha;
+        const float step = executed_step(row16_sum(kk2), row16_sum(dd), Pj[t * PLD + 3 * D],
+                                         Pj[t * PLD + 3 * D + 1], gp, &alpha);
+        const bool live = t < nt;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          Ks[t * LD + c16 * CPL + e] = live ? kn[e] : 0.f;
+          Dls[t * LD + c16 * CPL + e] = live ? dl[e] : 0.f;
+          Qs[t * LD + c16 * CPL + e] = live ? qn[e] : 0.f;
+        }
+        if (c16 == 0) {
+          alph[t] = live ? alpha : 1.f;
+          stp[t] = live ? step : 0.f;
+        }
+      }
+      lds_barrier();
+
+      // P4a: readout y_t = M_mem,b q_t on the waves that own M_mem tiles
+#pragma unroll
+      for (int mi = 0; mi < MTW; ++mi) {
+        const int m = w + kWaves * mi;
+        if (m >= NT) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f32x4 q0, q1;
+          load_row_pair(Qs + c16 * LD, s, g, q0, q1);
+          bf16x8 ah, al;
+          split8(q0, q1, ah, al);
+          acc = mma32x3(ah, al, Sh[mi][s], Sl[mi][s], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * g + i;
+          if (t < nt) {
+            const int pix = route_pixel(r, tb + t, H, W, N);
+            dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+          }
+        }
+      }
+      // P4b: solve coefficients, one DPP row of 16 lanes per token t = 4w + g, lane j:
+      //   coef[t][j] = step_t P(j+1, t) (k_t . k_j) for j < t (exact fp32 dot products);
+      //   P(j+1, t) is the suffix product over the row of x_j = (j + 1 < t ? alpha_{j+1} : 1).
+      {
+        const int t = 4 * w + g, j = c16;
+        const float* kt = Ks + t * LD;
+        const float* kj = Ks + j * LD;
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; e += 8) {
+          const f32x4 a0 = *reinterpret_cast<const f32x4*>(kt + e);
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(kj + e);
+          const f32x4 a1 = *reinterpret_cast<const f32x4*>(kt + e + 4);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(kj + e + 4);
+          d0 += a0[0] * b0[0] + a0[1] * b0[1] + a0[2] * b0[2] + a0[3] * b0[3];
+          d1 += a1[0] * b1[0] + a1[1] * b1[1] + a1[2] * b1[2] + a1[3] * b1[3];
+        }
+        const float ptj = row16_suffix_prod(j + 1 < t ? alph[j + 1] : 1.f);
+        coef[t * TLD + j] = j < t ? stp[t] * ptj * (d0 + d1) : 0.f;
+      }
+      if (MULTI && !first && w < NT) {
+        // GK[t][i] = (G_s k_t)_i for column tile w of G's rows
+        const int n = w;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f32x4 k0, k1, g0, g1;
+          load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+          load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
+          bf16x8 kh, kl, gh, gl;
+          split8(k0, k1, kh, kl);
+          split8(g0, g1, gh, gl);
+          acc = mma32x3(kh, kl, gh, gl, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) GKs[(4 * g + i) * LD + n * 16 + c16] = acc[i];
+      }
+      lds_barrier();
+
+      // P5: triangular solve for u_t, token by token (wave 0, lane = component):
+      //   u_t = rhs_t - sum_{j<t} coef[t][j] u_j,  rhs_t = -step_t (P(0, t) (G_s k_t) + delta_t).
+      // Block products P(0, t) and P(t+1, 16) are uniform register products; each token's
+      // sum uses four partial sums so the chain through u stays short.
+      if (w == 0) {
+        const int i = lane & (D - 1);
+        float al[kSB], st[kSB];
+#pragma unroll
+        for (int q = 0; q < kSB; q += 4) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(alph + q);
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(stp + q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            al[q + e] = a4[e];
+            st[q + e] = s4[e];
+          }
+        }
+        float ur[kSB];
+        float pre = 1.f;  // P(0, t)
+#pragma unroll
+        for (int t = 0; t < kSB; ++t) {
+          const float gk = (MULTI && !first) ? GKs[t * LD + i] : Ks[t * LD + i];
+          ur[t] = -st[t] * (pre * gk + Dls[t * LD + i]);
+          pre *= al[t];
+        }
+#pragma unroll
+        for (int t = 1; t < kSB; ++t) {
+          const float* crow = coef + t * TLD;
+          float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < t; ++j) a[j & 3] = fmaf(crow[j], ur[j], a[j & 3]);
+          ur[t] -= (a[0] + a[1]) + (a[2] + a[3]);
+          if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the load hoisting
+        }
+        float suf = 1.f;  // P(t+1, 16)
+#pragma unroll
+        for (int t = kSB - 1; t >= 0; --t) {
+          if (lane < D) Ubs[t * LD + i] = suf * ur[t];
+          suf *= al[t];
+        }
+        if (lane == 0) bco[kSB] = pre;  // P(0, 16): retention of the whole block
+      }
+      lds_barrier();
+
+      // P6: carry.  Z^T = Ub S_b^T (per state-row tile), then
+      //     (S_b G)_new = c (S_b G) + Z K, evaluated transposed so it lands in place.
+      {
+        const float cc = bco[kSB];
+        bf16x8 uh[KS], ul[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f32x4 u0, u1;
+          load_row_pair(Ubs + c16 * LD, s, g, u0, u1);
+          split8(u0, u1, uh[s], ul[s]);
+        }
+        bf16x4 kah[NT], kal[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 kv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = Ks[(4 * g + e) * LD + n * 16 + c16];
+          split4(kv, kah[n], kal[n]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MTW; ++mi) {
+          const int m = w + kWaves * mi;
+          if (m >= MT) continue;
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
+          bf16x4 zh, zl;
+          split4(z, zh, zl);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            f32x4 acc = MULTI ? Acc[MULTI ? mi : 0][MULTI ? n : 0] : S[mi][n];
+            acc *= cc;
+            acc = mma16x3(kah[n], kal[n], zh, zl, acc);
+            if (MULTI) {
+              Acc[MULTI ? mi : 0][MULTI ? n : 0] = acc;
+            } else {
+              S[mi][n] = acc;
+            }
+          }
+        }
+        // gain of the chunk so far, needed by the next block of the same chunk
+        if (MULTI && !last_block) {
+          for (int tile = w; tile < NT * NT; tile += kWaves) {
+            const int ti = tile / NT, tn = tile % NT;
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int gi = ti * 16 + 4 * g + e, gn = tn * 16 + c16;
+              acc[e] = first ? (gi == gn ? cc : 0.f) : cc * Gs[gi * LD + gn];
+            }
+            f32x4 uv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uv[e] = Ubs[(4 * g + e) * LD + ti * 16 + c16];
+            bf16x4 ah, al;
+            split4(uv, ah, al);
+            acc = mma16x3(ah, al, kah[tn], kal[tn], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gs[(ti * 16 + 4 * g + e) * LD + tn * 16 + c16] = acc[e];
+          }
+        }
+      }
+    }
+    if (MULTI) {
+#pragma unroll
+      for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[mi][n] = Acc[MULTI ? mi : 0][MULTI ? n : 0];
+    }
+  }
+
+  if (p.final_mem) {
+    float* fin = p.final_mem + (((int64_t)b * 4 + r) * nh + h) * SS;
+#pragma unroll
+    for (int mi = 0; mi < MTW; ++mi) {
+      const int row = (w + kWaves * mi) * 16 + c16;
+      if (row >= R) continue;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        *reinterpret_cast<f32x4*>(fin + row * D + n * 16 + 4 * g) = S[mi][n];
+    }
+  }
+
+  // Restore-and-sum of the routes, as in the fp32 kernel: the last chain of this
+  // (image, head) to finish adds the workspace planes into out in slot order.
+  if (p.n_sel > 1) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = atomicAdd(&p.counters[(int64_t)b * nh + h], 1) == p.n_sel - 1;
+    __syncthreads();
+    if (is_last) {
+      __threadfence();
+      for (int64_t e = threadIdx.x; e < (int64_t)N * D; e += kThreads) {
+        const int64_t idx = ((int64_t)b * N + e / D) * Dt + (int64_t)h * D + e % D;
+        float a = p.out[idx];
+        for (int k = 0; k < p.n_sel - 1; ++k) a += p.planes[k * p.plane_stride + idx];
+        p.out[idx] = a;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool mfma_path_supported(const ChainParams& p, int d) {
+  if (!p.x_bf16) return false;
+  if (d == 32) return true;
+  if (d != 64) return false;
+  for (int s = 0; s < p.n_sel; ++s) {
+    const int r = p.route_of_slot[s];
+    const int C = p.chunk > 0 ? p.chunk : (r < 2 ? p.W : p.H);
+    if (C > kSB) return false;  // the d = 64 variant keeps one state copy: one block per chunk
+  }
+  return true;
+}
+
+hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
+  dim3 grid((unsigned)blocks), block(kThreads);
+  if (d == 32) {
+    hipLaunchKernelGGL((chain_mfma_kernel<32, true>), grid, block, 0, stream, p);
+  } else if (d == 64) {
+    hipLaunchKernelGGL((chain_mfma_kernel<64, false>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hope

@@ -1,0 +1,110 @@
+// Device helpers shared by the chain kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hope {
+
+// Flat pixel visited at step t of route r ("VMamba: Visual State Space Model",
+// the four scan orders; VisionHOPE Sec. 2.3 Eq. 24).
+__device__ __forceinline__ int route_pixel(int r, int t, int H, int W, int N) {
+  if (r & 1) t = N - 1 - t;          // routes 1 and 3 are full reversals
+  if (r < 2) return t;               // row-major
+  return (t % H) * W + (t / H);      // column-major: flatten of the spatial transpose
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+struct GateParams {
+  int eta_map;   // 0 sigmoid, 1 softplus
+  float eta_scale, alpha_bias, eps;
+};
+
+struct TokenGates {
+  float k, q, delta;  // this lane's component (0 for lanes >= d)
+  float alpha, step;  // per token (same in every lane)
+};
+
+// Executed step from the token's norms ("VisionHOPE: Visual Backbones as Self-Modifying
+// Learning Systems", Sec. 2.2 Definition 1, Eq. 19-20 with the App. B.3 safeguards):
+//   r = sqrt(|delta|^2 + eps^2) + eps,  eta_inj = (1 - 1e-3)(1 - alpha) / r,
+//   eta_bar = eta_inj (1 - exp(-eta / eta_inj)),
+//   eta_spec = (1 - 1e-6) 2 alpha / max(|k|^2, 1e-20), one ulp toward zero,
+//   step = min(eta_bar, eta_spec);
+// gate maps of App. C.1 Eq. 53 (eta_scale * sigmoid or softplus; alpha = sigmoid(s + bias)).
+// 1 - alpha is evaluated as sigmoid(-z) to keep its relative accuracy near alpha = 1.
+// Reciprocals and exponentials use the hardware approximations (about 1 ulp); 1 - e^-x
+// keeps expm1 for its accuracy at small x.
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, float s_alpha,
+                                               const GateParams& g, float* alpha_out) {
+  float eta;
+  if (g.eta_map == 0) {
+    eta = g.eta_scale * fast_rcp(1.f + fast_exp(-s_eta));
+  } else {
+    eta = g.eta_scale * (fmaxf(s_eta, 0.f) + log1pf(fast_exp(-fabsf(s_eta))));
+  }
+  const float z = s_alpha + g.alpha_bias;
+  const float alpha = fast_rcp(1.f + fast_exp(-z));
+  const float one_minus_alpha = fast_rcp(1.f + fast_exp(z));
+  const float rr = sqrtf(dd + g.eps * g.eps) + g.eps;
+  const float inj = (1.f - 1e-3f) * one_minus_alpha * fast_rcp(rr);
+  const float bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta * fast_rcp(inj));
+  float spec = (1.f - 1e-6f) * 2.f * alpha * fast_rcp(fmaxf(kk, 1e-20f));
+  if (spec > 0.f) spec = __uint_as_float(__float_as_uint(spec) - 1u);  // one ulp toward 0
+  *alpha_out = alpha;
+  return fminf(bar, spec);
+}
+
+// One token on one wave, lane i holding component i of the raw projections: the
+// stabilised normalisation of k (App. C.1; q the same way), delta = k - v, and the step.
+__device__ __forceinline__ TokenGates token_gates(float kr, float vr, float qr, float s_eta,
+                                                  float s_alpha, const GateParams& g) {
+  TokenGates o;
+  o.k = kr / sqrtf(wave_sum(kr * kr) + g.eps);
+  o.q = qr / sqrtf(wave_sum(qr * qr) + g.eps);
+  o.delta = o.k - vr;
+  const float dd = wave_sum(o.delta * o.delta);
+  const float kk = wave_sum(o.k * o.k);
+  o.step = executed_step(kk, dd, s_eta, s_alpha, g, &o.alpha);
+  return o;
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_move<0x128>(v);  // row_ror:8
+  v += dpp_move<0x124>(v);  // row_ror:4
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  return v;
+}
+
+// Product over lanes j..15 of a DPP row (suffix product); lanes past the row end count as 1.
+__device__ __forceinline__ float row16_suffix_prod(float v) {
+  const int one = __builtin_bit_cast(int, 1.f);
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x101, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x102, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x108, 0xF, 0xF, false));
+  return v;
+}
+
+// Workgroup barrier that orders LDS only: global loads in flight (prefetches) and global
+// stores (readouts) stay outstanding across it, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace hope

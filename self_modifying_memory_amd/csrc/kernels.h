@@ -26,7 +26,12 @@ struct ChainParams {
   float eta_scale, alpha_bias, eps;
 };
 
+// fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
+
+// MFMA kernel for bf16 maps (d = 32, or d = 64 with every chunk <= 16 tokens).
+bool mfma_path_supported(const ChainParams& p, int d);
+hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream);
 
 // Zero n ints (the arrival counters) with a kernel, so the call stays capturable.
 hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t stream);
