@@ -39,8 +39,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kSB = 16;  // tokens per block = MFMA tile height
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -87,8 +85,13 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
   v1 = *reinterpret_cast<const f32x4*>(row + 32 * s + 16 + 4 * g);
 }
 
-template <int D, bool MULTI>
-__global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
+// NW waves per chain: 4 for d = 32, 8 for d = 64 (at most three state-row tiles per wave,
+// so two waves fit on a SIMD).  Gates use waves 0-3 (16 lanes per token); with eight
+// waves the solve coefficients run on waves 4-7 while waves 0-3 read out.
+template <int D, bool MULTI, int NW>
+__global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
+  constexpr int kWaves = NW;
+  constexpr int kThreads = 64 * NW;
   constexpr int NT = D / 16;                       // column tiles of the state
   constexpr int KS = D / 32;                       // 32-deep k-steps over the head dimension
   constexpr int R = 4 * D + 2;                     // state rows: M_mem, M_k, M_v, M_q, m_eta, m_alpha
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
   // Tokens of the next block are loaded one block ahead into registers (8 channels
   // per thread), so the HBM latency of the gather stays off the per-block critical path.
   constexpr int kLoaders = kSB * (D / 8);
+  static_assert(kLoaders <= kThreads, "one 16-byte load per loader thread");
   const int ld_t = threadIdx.x / (D / 8), ld_c8 = threadIdx.x % (D / 8);
   auto fetch = [&](int tb, int nt) {
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -177,6 +181,13 @@ __global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
         for (int n = 0; n < NT; ++n) Acc[MULTI ? mi : 0][MULTI ? n : 0] = S[mi][n];
     }
     for (int tb = s0; tb < s1; tb += kSB) {
+      // lane indices re-derived through an opaque copy each block: the address
+      // arithmetic built on them is then recomputed per block instead of being hoisted
+      // out of the loop and held in registers across every phase
+      int lid = threadIdx.x;
+      asm volatile("" : "+v"(lid));
+      const int lane = lid & 63;
+      const int c16 = lid & 15, g = (lid >> 4) & 3;
       const int nt = min(kSB, s1 - tb);
       const bool first = tb == s0;
       const bool last_block = tb + kSB >= s1;
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
       // P3: normalisation, gates and executed step; 16 lanes per token (one DPP row),
       // each lane holding CPL consecutive components.  Padding tokens get no key, no
       // write and unit retention.
-      {
+      if (w < 4) {
         constexpr int CPL = D / 16;
         const int t = 4 * w + g;
         const float* pt = Pj + t * PLD + c16 * CPL;
@@ -291,11 +302,11 @@ __global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
           }
         }
       }
-      // P4b: solve coefficients, one DPP row of 16 lanes per token t = 4w + g, lane j:
+      // P4b: solve coefficients, one DPP row of 16 lanes per token t = 4(w mod 4) + g, lane j:
       //   coef[t][j] = step_t P(j+1, t) (k_t . k_j) for j < t (exact fp32 dot products);
       //   P(j+1, t) is the suffix product over the row of x_j = (j + 1 < t ? alpha_{j+1} : 1).
-      {
-        const int t = 4 * w + g, j = c16;
+      if (NW == 4 || w >= 4) {
+        const int t = 4 * (w & 3) + g, j = c16;
         const float* kt = Ks + t * LD;
         const float* kj = Ks + j * LD;
         float d0 = 0.f, d1 = 0.f;
@@ -393,20 +404,26 @@ __global__ __launch_bounds__(kThreads) void chain_mfma_kernel(ChainParams p) {
           for (int e = 0; e < 4; ++e) kv[e] = Ks[(4 * g + e) * LD + n * 16 + c16];
           split4(kv, kah[n], kal[n]);
         }
+        // all Z tiles first, so the state split dies before the updates start
+        bf16x4 zh[MTW], zl[MTW];
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
-          const int m = w + kWaves * mi;
-          if (m >= MT) continue;
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          if (w + kWaves * mi < MT) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
-          bf16x4 zh, zl;
-          split4(z, zh, zl);
+            for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
+          }
+          split4(z, zh[mi], zl[mi]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < MTW; ++mi) {
+          if (w + kWaves * mi >= MT) continue;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             f32x4 acc = MULTI ? Acc[MULTI ? mi : 0][MULTI ? n : 0] : S[mi][n];
             acc *= cc;
-            acc = mma16x3(kah[n], kal[n], zh, zl, acc);
+            acc = mma16x3(kah[n], kal[n], zh[mi], zl[mi], acc);
             if (MULTI) {
               Acc[MULTI ? mi : 0][MULTI ? n : 0] = acc;
             } else {
@@ -491,11 +508,11 @@ bool mfma_path_supported(const ChainParams& p, int d) {
 
 hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
-  dim3 grid((unsigned)blocks), block(kThreads);
+  dim3 grid((unsigned)blocks);
   if (d == 32) {
-    hipLaunchKernelGGL((chain_mfma_kernel<32, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4>), grid, dim3(256), 0, stream, p);
   } else if (d == 64) {
-    hipLaunchKernelGGL((chain_mfma_kernel<64, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8>), grid, dim3(512), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
