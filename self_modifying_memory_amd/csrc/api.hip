@@ -36,12 +36,8 @@ int slots_of(uint32_t dirs, int* route_of_slot) {
   return n;
 }
 
-// Workspace layout: [B*nh int32 arrival counters, padded to 256 bytes]
-//                   [(n_sel-1) fp32 planes of one map each, each padded to 256 bytes].
+// Workspace layout: (n_sel-1) fp32 route planes of one map each, each padded to 256 bytes.
 int64_t plane_stride_elems(int64_t n_elem) { return (n_elem + 63) / 64 * 64; }
-size_t counter_bytes(const hope_fmap_t* x) {
-  return ((size_t)x->B * x->n_heads * sizeof(int) + 255) / 256 * 256;
-}
 
 hope_status_t check_fmap(const hope_fmap_t* x) {
   if (!x || !x->data) return HOPE_ERR_INVALID_ARG;
@@ -72,7 +68,7 @@ size_t workspace_bytes_for(const hope_fmap_t* x, uint32_t dirs) {
   const int n_sel = popcount4(dirs);
   if (n_sel <= 1) return 0;
   const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
-  return counter_bytes(x) + (size_t)(n_sel - 1) * (size_t)plane_stride_elems(n_elem) * sizeof(float);
+  return (size_t)(n_sel - 1) * (size_t)plane_stride_elems(n_elem) * sizeof(float);
 }
 
 hope_status_t hip_status(hipError_t e) {
@@ -152,10 +148,7 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   p.x = x->data;
   p.init = init_memories;
   p.out = out;
-  if (ws_need > 0) {
-    p.counters = static_cast<int*>(o.workspace);
-    p.planes = reinterpret_cast<float*>(static_cast<char*>(o.workspace) + counter_bytes(x));
-  }
+  if (ws_need > 0) p.planes = static_cast<float*>(o.workspace);
   p.final_mem = o.final_memories;
   p.plane_stride = plane_stride_elems(n_elem);
   p.x_bf16 = x->dtype == HOPE_BF16;
@@ -174,12 +167,10 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;
-  if (p.n_sel > 1) {
-    st = hip_status(hope::launch_zero_ints(p.counters, (int64_t)x->B * x->n_heads, s));
-    if (st != HOPE_OK) return st;
-  }
-  if (hope::mfma_path_supported(p, d)) return hip_status(hope::launch_chain_mfma(p, d, s));
-  return hip_status(hope::launch_chain(p, d, s));
+  st = hip_status(hope::mfma_path_supported(p, d) ? hope::launch_chain_mfma(p, d, s)
+                                                  : hope::launch_chain(p, d, s));
+  if (st != HOPE_OK || p.n_sel == 1) return st;
+  return hip_status(hope::launch_plane_sum(out, p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
 }
 
 const char* hope_status_string(hope_status_t status) {

@@ -178,35 +178,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
     for (int e = tid; e < R * D; e += kThreads) fin[e] = S[(e / D) * SP + e % D];
   }
 
-  // Restore-and-sum (Eq. 26, unit scales): slot 0 wrote into out, the other slots into
-  // workspace planes.  The last chain of this (image, head) to arrive adds the planes
-  // into out in slot order, so the sum is deterministic whoever arrives last.  No
-  // workgroup ever waits on another.
-  if (p.n_sel > 1) {
-    __shared__ int is_last;
-    __threadfence();                       // release this chain's readouts (agent scope)
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&p.counters[(int64_t)b * nh + h], 1);
-      is_last = prev == p.n_sel - 1;
-    }
-    __syncthreads();
-    if (is_last) {
-      __threadfence();                     // acquire the other chains' readouts
-      for (int64_t e = tid; e < (int64_t)N * D; e += kThreads) {
-        const int64_t idx = ((int64_t)b * N + e / D) * Dt + (int64_t)h * D + e % D;
-        float a = p.out[idx];
-        for (int k = 0; k < p.n_sel - 1; ++k) a += p.planes[k * p.plane_stride + idx];
-        p.out[idx] = a;
-      }
-    }
-  }
-}
-
-__global__ void zero_ints_kernel(int* p, int64_t n) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x)
-    p[e] = 0;
 }
 
 }  // namespace
@@ -220,13 +191,6 @@ hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream) {
     case 64: hipLaunchKernelGGL(chain_kernel<64>, grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t stream) {
-  int64_t g = (n + 255) / 256;
-  if (g > 1024) g = 1024;
-  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)g), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

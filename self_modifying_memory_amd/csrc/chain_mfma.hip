@@ -60,6 +60,18 @@ __device__ __forceinline__ f32x4 mma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4
   return mma16(ah, bh, c);
 }
 
+__device__ __forceinline__ void split4(const f32x4 v, bf16x4& hi, bf16x4& lo);
+
+// X Y for 16x16 fp32 matrices in the accumulator layout: a_t holds X^T (A operand),
+// b holds Y (B operand); hi/lo split, three products
+__device__ __forceinline__ f32x4 mm16(const f32x4 a_t, const f32x4 b) {
+  bf16x4 ah, al, bh, bl;
+  split4(a_t, ah, al);
+  split4(b, bh, bl);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return mma16x3(ah, al, bh, bl, z);
+}
+
 __device__ __forceinline__ void split8(const f32x4 v0, const f32x4 v1, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -100,21 +112,25 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   constexpr int LD = D + 4;                        // fp32 stride of token-major tiles
   constexpr int XLD = D + 8;                       // bf16 stride of the token block
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
-  constexpr int TLD = kSB + 4;
+  constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
 
   __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
   __shared__ __attribute__((aligned(16))) float Ks[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Dls[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Qs[kSB * LD];
-  __shared__ __attribute__((aligned(16))) float Ubs[kSB * LD];
-  __shared__ __attribute__((aligned(16))) float GKs[MULTI ? kSB * LD : 4];
+  __shared__ __attribute__((aligned(16))) float Ubs[MULTI ? kSB * LD : 4];
+  // MFMA-ready bf16 hi/lo copies: Ub rows (A operand of S_b Ub^T) and K transposed
+  // (A operand of the carry), written once by their producers instead of re-split per wave
+  __shared__ __attribute__((aligned(16))) unsigned short UbH[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short UbL[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short KtH[D * KTLD];
+  __shared__ __attribute__((aligned(16))) unsigned short KtL[D * KTLD];
+  __shared__ int pixs[kSB];
   __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
-  __shared__ __attribute__((aligned(16))) float coef[kSB * TLD];  // coef[t][j], j < t
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
-  __shared__ float bco[kSB + 1];
-  __shared__ int is_last;
+  __shared__ float cprev[NT * kSB], bco[NT * (kSB + 1)];  // one copy per solve wave
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -129,6 +145,11 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   const int64_t SS = 4 * D * D + 2 * D;
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps};
   const unsigned short* xg = static_cast<const unsigned short*>(p.x);
+  const float inv_h = 1.f / (float)H;
+  const bool fast_pix = N < (1 << 22);
+  auto pixel = [&](int t) {
+    return fast_pix ? route_pixel_fast(r, t, H, W, N, inv_h) : route_pixel(r, t, H, W, N);
+  };
   float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
 
   // ---- state in registers --------------------------------------------------------
@@ -149,20 +170,44 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
     }
   }
 
-  // Tokens of the next block are loaded one block ahead into registers (8 channels
-  // per thread), so the HBM latency of the gather stays off the per-block critical path.
+  // Tokens are gathered one block ahead: block k+1's 16-byte loads (8 channels per loader
+  // thread) are in flight while block k computes, and are staged into LDS at its end.
   constexpr int kLoaders = kSB * (D / 8);
   static_assert(kLoaders <= kThreads, "one 16-byte load per loader thread");
+  // solve waves: the last NSW waves, none of which owns an M_mem (readout) tile; each
+  // repeats the short 16x16 inverse and then handles its own column tiles of U
+  constexpr int NSW = NT;
+  constexpr int SW0 = kWaves - NSW;
+  static_assert(SW0 >= NT, "solve waves must not own readout tiles");
   const int ld_t = threadIdx.x / (D / 8), ld_c8 = threadIdx.x % (D / 8);
   auto fetch = [&](int tb, int nt) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (threadIdx.x < kLoaders && ld_t < nt) {
-      const int pix = route_pixel(r, tb + ld_t, H, W, N);
+      const int pix = pixel(tb + ld_t);
       v = *reinterpret_cast<const u32x4*>(xg + ((int64_t)b * N + pix) * Dt + (int64_t)h * D + ld_c8 * 8);
     }
     return v;
   };
-  u32x4 pf = fetch(0, min(kSB, min(C, N)));
+  // start and length of the block after the one starting at tb (length 0 past the end)
+  auto next_block = [&](int tb, int& tn, int& ntn) {
+    const int cend = min((tb / C + 1) * C, N);
+    tn = tb + kSB < cend ? tb + kSB : cend;
+    ntn = tn < N ? min(kSB, min((tn / C + 1) * C, N) - tn) : 0;
+  };
+  auto stage_block = [&](const u32x4& v, int tb, int nt) {
+    if (threadIdx.x < kLoaders) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
+    if (threadIdx.x < kSB)
+      pixs[threadIdx.x] = (int)threadIdx.x < nt ? pixel(tb + threadIdx.x) : 0;
+  };
+  u32x4 pf;
+  {
+    const int nt0 = min(kSB, min(C, N));
+    stage_block(fetch(0, nt0), 0, nt0);
+    int tn, ntn;
+    next_block(0, tn, ntn);
+    pf = fetch(tn, ntn);
+  }
+  lds_barrier();
 
   // bf16 hi/lo split of the chunk-start state, shared by the projections, the readout
   // and the carry of every block of the chunk (S_b is constant over the chunk)
@@ -192,18 +237,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       const bool first = tb == s0;
       const bool last_block = tb + kSB >= s1;
 
-      // P1: the prefetched block goes to LDS (zero past nt); the next block is requested
-      if (threadIdx.x < kLoaders) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
-      {
-        const int tn = last_block ? s1 : tb + kSB;
-        if (tn < N) {
-          const int cend = min((tn / C + 1) * C, N);
-          pf = fetch(tn, min(kSB, cend - tn));
-        }
-      }
-      lds_barrier();
-
-      // P2: projections P[t][row] = x_t . S_b[row] for the k, v, q, eta, alpha rows
+      // A: projections P[t][row] = x_t . S_b[row] for the k, v, q, eta, alpha rows
       {
         bf16x8 xa[KS];
 #pragma unroll
@@ -233,7 +267,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       }
       lds_barrier();
 
-      // P3: normalisation, gates and executed step; 16 lanes per token (one DPP row),
+      // B: normalisation, gates and executed step; 16 lanes per token (one DPP row),
       // each lane holding CPL consecutive components.  Padding tokens get no key, no
       // write and unit retention.
       if (w < 4) {
@@ -268,9 +302,13 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         const bool live = t < nt;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-          Ks[t * LD + c16 * CPL + e] = live ? kn[e] : 0.f;
+          const float kv = live ? kn[e] : 0.f;
+          Ks[t * LD + c16 * CPL + e] = kv;
           Dls[t * LD + c16 * CPL + e] = live ? dl[e] : 0.f;
           Qs[t * LD + c16 * CPL + e] = live ? qn[e] : 0.f;
+          const __bf16 kh = (__bf16)kv;
+          KtH[(c16 * CPL + e) * KTLD + t] = __builtin_bit_cast(unsigned short, kh);
+          KtL[(c16 * CPL + e) * KTLD + t] = __builtin_bit_cast(unsigned short, (__bf16)(kv - (float)kh));
         }
         if (c16 == 0) {
           alph[t] = live ? alpha : 1.f;
@@ -279,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       }
       lds_barrier();
 
-      // P4a: readout y_t = M_mem,b q_t on the waves that own M_mem tiles
+      // C1: readout y_t = M_mem,b q_t on the waves that own M_mem tiles
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi) {
         const int m = w + kWaves * mi;
@@ -296,113 +334,130 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 4 * g + i;
-          if (t < nt) {
-            const int pix = route_pixel(r, tb + t, H, W, N);
-            dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+          if (t < nt) dst[((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+        }
+      }
+      // C2: the block's write vectors, on the solve wave, all in registers.
+      //   (I + L) U = RHS,  L[t][j] = step_t P(j+1,t) (k_t . k_j) for j < t,
+      //   RHS[t] = -step_t (P(0,t) G_s k_t + delta_t),  Ub[t] = P(t+1,16) U[t].
+      // L is strictly lower triangular (nilpotent), so (I + L)^-1 =
+      // (I - L)(I + L^2)(I + L^4)(I + L^8): six dependent 16x16 products instead of a
+      // 16-step substitution.  Matrices are held in the MFMA accumulator layout (lane
+      // (g, c16), register i = entry [4g+i][c16]) together with their transposes, which
+      // is exactly the A / B operand layout of the next product.
+      if (w >= SW0) {
+        const int wi = w - SW0;  // this solve wave's column tile of U
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        // retention products over DPP rows (they need only alpha, so they overlap the
+        // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for L^T (prefix
+        // over c), and the block products P(0, t), P(t+1, 16)
+        const float a_self = alph[c16];
+        const float a_next = alph[min(c16 + 1, kSB - 1)], a_prev = alph[max(c16 - 1, 0)];
+        const float st_c = stp[c16];
+        float pj[4], pc[4], st_r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * g + i;
+          st_r[i] = stp[rr];
+          pj[i] = row16_suffix_prod(c16 + 1 < rr ? a_next : 1.f);
+          pc[i] = row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f);
+        }
+        {
+          const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
+          const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
+          if (lane < kSB) {
+            cprev[wi * kSB + lane] = pre;
+            bco[wi * (kSB + 1) + lane] = suf;
+            if (lane == kSB - 1) bco[wi * (kSB + 1) + kSB] = pre * a_self;
           }
         }
-      }
-      // P4b: solve coefficients, one DPP row of 16 lanes per token t = 4(w mod 4) + g, lane j:
-      //   coef[t][j] = step_t P(j+1, t) (k_t . k_j) for j < t (exact fp32 dot products);
-      //   P(j+1, t) is the suffix product over the row of x_j = (j + 1 < t ? alpha_{j+1} : 1).
-      if (NW == 4 || w >= 4) {
-        const int t = 4 * (w & 3) + g, j = c16;
-        const float* kt = Ks + t * LD;
-        const float* kj = Ks + j * LD;
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < D; e += 8) {
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(kt + e);
-          const f32x4 b0 = *reinterpret_cast<const f32x4*>(kj + e);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(kt + e + 4);
-          const f32x4 b1 = *reinterpret_cast<const f32x4*>(kj + e + 4);
-          d0 += a0[0] * b0[0] + a0[1] * b0[1] + a0[2] * b0[2] + a0[3] * b0[3];
-          d1 += a1[0] * b1[0] + a1[1] * b1[1] + a1[2] * b1[2] + a1[3] * b1[3];
-        }
-        const float ptj = row16_suffix_prod(j + 1 < t ? alph[j + 1] : 1.f);
-        coef[t * TLD + j] = j < t ? stp[t] * ptj * (d0 + d1) : 0.f;
-      }
-      if (MULTI && !first && w < NT) {
-        // GK[t][i] = (G_s k_t)_i for column tile w of G's rows
-        const int n = w;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // token Gram matrix, gr[i] = k_{4g+i} . k_{c16}
+        f32x4 gr = zero4;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          f32x4 k0, k1, g0, g1;
+          f32x4 k0, k1;
           load_row_pair(Ks + c16 * LD, s, g, k0, k1);
-          load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
-          bf16x8 kh, kl, gh, gl;
+          bf16x8 kh, kl;
           split8(k0, k1, kh, kl);
-          split8(g0, g1, gh, gl);
-          acc = mma32x3(kh, kl, gh, gl, acc);
+          gr = mma32x3(kh, kl, kh, kl, gr);
         }
+        f32x4 L1, L1T, eye;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) GKs[(4 * g + i) * LD + n * 16 + c16] = acc[i];
-      }
-      lds_barrier();
-
-      // P5: triangular solve for u_t, token by token (wave 0, lane = component):
-      //   u_t = rhs_t - sum_{j<t} coef[t][j] u_j,  rhs_t = -step_t (P(0, t) (G_s k_t) + delta_t).
-      // Block products P(0, t) and P(t+1, 16) are uniform register products; each token's
-      // sum uses four partial sums so the chain through u stays short.
-      if (w == 0) {
-        const int i = lane & (D - 1);
-        float al[kSB], st[kSB];
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * g + i;
+          L1[i] = c16 < rr ? st_r[i] * pj[i] * gr[i] : 0.f;
+          L1T[i] = rr < c16 ? st_c * pc[i] * gr[i] : 0.f;
+          eye[i] = rr == c16 ? 1.f : 0.f;
+        }
+        const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
+        const f32x4 E = eye - L1T + L2T - mm16(L2, L1T);       // (I + L2^T)(I - L^T)
+        const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
+        const f32x4 L8 = mm16(L4T, L4);
+        const f32x4 FT = eye + L4 + L8 + mm16(L4T, L8);        // ((I + L8^T)(I + L4^T))^T
+        const f32x4 TiT = mm16(FT, E);                         // ((I + L)^-1)^T
+        bf16x4 th, tl;
+        split4(TiT, th, tl);
+        // right-hand sides of this wave's column tile(s), already in the B-operand layout
+        for (int n = wi; n < NT; n += NSW) {
+          f32x4 gk;
+          if (MULTI && !first) {  // G_s k_t for this column tile (G_s is the chunk gain so far)
+            gk = zero4;
 #pragma unroll
-        for (int q = 0; q < kSB; q += 4) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4*>(alph + q);
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(stp + q);
+            for (int s = 0; s < KS; ++s) {
+              f32x4 k0, k1, g0, g1;
+              load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+              load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
+              bf16x8 kh, kl, gh, gl;
+              split8(k0, k1, kh, kl);
+              split8(g0, g1, gh, gl);
+              gk = mma32x3(kh, kl, gh, gl, gk);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n * 16 + c16];
+          }
+          f32x4 rhs;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            al[q + e] = a4[e];
-            st[q + e] = s4[e];
+            const int j = 4 * g + e;
+            rhs[e] = -stp[j] * (cprev[wi * kSB + j] * gk[e] + Dls[j * LD + n * 16 + c16]);
+          }
+          bf16x4 rh, rl;
+          split4(rhs, rh, rl);
+          const f32x4 u = mma16x3(th, tl, rh, rl, zero4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i, col = n * 16 + c16;
+            const float ub = bco[wi * (kSB + 1) + t] * u[i];
+            if (MULTI) Ubs[t * LD + col] = ub;
+            const __bf16 uh = (__bf16)ub;
+            UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
+            UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
           }
         }
-        float ur[kSB];
-        float pre = 1.f;  // P(0, t)
-#pragma unroll
-        for (int t = 0; t < kSB; ++t) {
-          const float gk = (MULTI && !first) ? GKs[t * LD + i] : Ks[t * LD + i];
-          ur[t] = -st[t] * (pre * gk + Dls[t * LD + i]);
-          pre *= al[t];
-        }
-#pragma unroll
-        for (int t = 1; t < kSB; ++t) {
-          const float* crow = coef + t * TLD;
-          float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < t; ++j) a[j & 3] = fmaf(crow[j], ur[j], a[j & 3]);
-          ur[t] -= (a[0] + a[1]) + (a[2] + a[3]);
-          if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the load hoisting
-        }
-        float suf = 1.f;  // P(t+1, 16)
-#pragma unroll
-        for (int t = kSB - 1; t >= 0; --t) {
-          if (lane < D) Ubs[t * LD + i] = suf * ur[t];
-          suf *= al[t];
-        }
-        if (lane == 0) bco[kSB] = pre;  // P(0, 16): retention of the whole block
       }
       lds_barrier();
 
-      // P6: carry.  Z^T = Ub S_b^T (per state-row tile), then
+      // D: carry.  Z^T = Ub S_b^T (per state-row tile), then
       //     (S_b G)_new = c (S_b G) + Z K, evaluated transposed so it lands in place.
       {
-        const float cc = bco[kSB];
+        const float cc = bco[kSB];  // copy of the first solve wave
         bf16x8 uh[KS], ul[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          f32x4 u0, u1;
-          load_row_pair(Ubs + c16 * LD, s, g, u0, u1);
-          split8(u0, u1, uh[s], ul[s]);
+          const unsigned short* hr = UbH + c16 * XLD + 32 * s + 4 * g;
+          const unsigned short* lr = UbL + c16 * XLD + 32 * s + 4 * g;
+          const u32x2 h0 = *reinterpret_cast<const u32x2*>(hr), h1 = *reinterpret_cast<const u32x2*>(hr + 16);
+          const u32x2 l0 = *reinterpret_cast<const u32x2*>(lr), l1 = *reinterpret_cast<const u32x2*>(lr + 16);
+          const u32x4 hv = {h0[0], h0[1], h1[0], h1[1]}, lv = {l0[0], l0[1], l1[0], l1[1]};
+          uh[s] = __builtin_bit_cast(bf16x8, hv);
+          ul[s] = __builtin_bit_cast(bf16x8, lv);
         }
         bf16x4 kah[NT], kal[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          f32x4 kv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kv[e] = Ks[(4 * g + e) * LD + n * 16 + c16];
-          split4(kv, kah[n], kal[n]);
+          kah[n] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtH + (n * 16 + c16) * KTLD + 4 * g));
+          kal[n] = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (n * 16 + c16) * KTLD + 4 * g));
         }
         // all Z tiles first, so the state split dies before the updates start
         bf16x4 zh[MTW], zl[MTW];
@@ -452,6 +507,19 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           }
         }
       }
+      // stage the next block (X was last read in A, the pixel table in C) and request
+      // the one after it
+      {
+        int tn, ntn;
+        next_block(tb, tn, ntn);
+        if (ntn > 0) {
+          stage_block(pf, tn, ntn);
+          int tn2, ntn2;
+          next_block(tn, tn2, ntn2);
+          pf = fetch(tn2, ntn2);
+        }
+      }
+      lds_barrier();
     }
     if (MULTI) {
 #pragma unroll
@@ -473,23 +541,6 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
     }
   }
 
-  // Restore-and-sum of the routes, as in the fp32 kernel: the last chain of this
-  // (image, head) to finish adds the workspace planes into out in slot order.
-  if (p.n_sel > 1) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = atomicAdd(&p.counters[(int64_t)b * nh + h], 1) == p.n_sel - 1;
-    __syncthreads();
-    if (is_last) {
-      __threadfence();
-      for (int64_t e = threadIdx.x; e < (int64_t)N * D; e += kThreads) {
-        const int64_t idx = ((int64_t)b * N + e / D) * Dt + (int64_t)h * D + e % D;
-        float a = p.out[idx];
-        for (int k = 0; k < p.n_sel - 1; ++k) a += p.planes[k * p.plane_stride + idx];
-        p.out[idx] = a;
-      }
-    }
-  }
 }
 
 }  // namespace

@@ -14,6 +14,23 @@ __device__ __forceinline__ int route_pixel(int r, int t, int H, int W, int N) {
   return (t % H) * W + (t / H);      // column-major: flatten of the spatial transpose
 }
 
+// Same map without an integer division: t / H through a float reciprocal and one
+// correction step, exact for t < 2^22 (callers check N).
+__device__ __forceinline__ int route_pixel_fast(int r, int t, int H, int W, int N, float inv_h) {
+  if (r & 1) t = N - 1 - t;
+  if (r < 2) return t;
+  int q = (int)((float)t * inv_h);
+  int rem = t - q * H;
+  if (rem < 0) {
+    q -= 1;
+    rem += H;
+  } else if (rem >= H) {
+    q += 1;
+    rem -= H;
+  }
+  return rem * W + q;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -37,7 +54,8 @@ struct TokenGates {
 //   eta_spec = (1 - 1e-6) 2 alpha / max(|k|^2, 1e-20), one ulp toward zero,
 //   step = min(eta_bar, eta_spec);
 // gate maps of App. C.1 Eq. 53 (eta_scale * sigmoid or softplus; alpha = sigmoid(s + bias)).
-// 1 - alpha is evaluated as sigmoid(-z) to keep its relative accuracy near alpha = 1.
+// 1 - alpha is evaluated as e^-z sigmoid(z) = sigmoid(-z) to keep its relative accuracy
+// near alpha = 1.
 // Reciprocals and exponentials use the hardware approximations (about 1 ulp); 1 - e^-x
 // keeps expm1 for its accuracy at small x.
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -52,8 +70,9 @@ __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, 
     eta = g.eta_scale * (fmaxf(s_eta, 0.f) + log1pf(fast_exp(-fabsf(s_eta))));
   }
   const float z = s_alpha + g.alpha_bias;
-  const float alpha = fast_rcp(1.f + fast_exp(-z));
-  const float one_minus_alpha = fast_rcp(1.f + fast_exp(z));
+  const float ez = fast_exp(-z);
+  const float alpha = fast_rcp(1.f + ez);
+  const float one_minus_alpha = ez * alpha;  // sigmoid(-z), accurate near alpha = 1
   const float rr = sqrtf(dd + g.eps * g.eps) + g.eps;
   const float inj = (1.f - 1e-3f) * one_minus_alpha * fast_rcp(rr);
   const float bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta * fast_rcp(inj));
@@ -98,6 +117,16 @@ __device__ __forceinline__ float row16_suffix_prod(float v) {
   v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x102, 0xF, 0xF, false));
   v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false));
   v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x108, 0xF, 0xF, false));
+  return v;
+}
+
+// Product over lanes 0..j of a DPP row (prefix product); lanes before the row start count as 1.
+__device__ __forceinline__ float row16_prefix_prod(float v) {
+  const int one = __builtin_bit_cast(int, 1.f);
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, false));
+  v *= __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, false));
   return v;
 }
 

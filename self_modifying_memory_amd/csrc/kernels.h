@@ -13,7 +13,6 @@ struct ChainParams {
   const float* init;      // [4][nh][S] or [B][4][nh][S]
   float* out;             // [B][H][W][D] fp32: plane of slot 0
   float* planes;          // slots 1..n_sel-1: planes + (slot-1)*plane_stride
-  int* counters;          // [B*nh] arrival counters of the route chains (zeroed per call)
   float* final_mem;       // [B][4][nh][S] or nullptr
   int64_t plane_stride;   // elements between consecutive workspace planes
   int x_bf16;
@@ -33,8 +32,9 @@ hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
 bool mfma_path_supported(const ChainParams& p, int d);
 hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream);
 
-// Zero n ints (the arrival counters) with a kernel, so the call stays capturable.
-hipError_t launch_zero_ints(int* p, int64_t n, hipStream_t stream);
+// out[i] += planes[0][i] + ... + planes[n-1][i], left to right, fp32 (route sum).
+hipError_t launch_plane_sum(float* out, const float* planes, int64_t plane_stride, int n_planes,
+                            int64_t n_elem, hipStream_t stream);
 
 // Bit-exact permutation of x into route order: routes[slot][b][t][c] = x[b][p_r(t)][c].
 hipError_t launch_cross_scan(const void* x, int elem_bytes, int B, int H, int W, int D,

@@ -78,6 +78,35 @@ __global__ void cross_merge_kernel(const void* __restrict__ routes, int B, int H
   }
 }
 
+// Restore-and-sum of the routes (VisionHOPE Eq. 26 with unit scales): slot 0 is already
+// in out, slots 1.. are workspace planes of the same layout; added in slot order so the
+// result is bit-for-bit reproducible.
+__global__ void plane_sum_vec4(float4* __restrict__ out, const float4* __restrict__ planes,
+                               int64_t stride4, int n_planes, int64_t n4) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = out[e];
+    for (int k = 0; k < n_planes; ++k) {
+      const float4 v = planes[k * stride4 + e];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    out[e] = a;
+  }
+}
+
+__global__ void plane_sum_scalar(float* __restrict__ out, const float* __restrict__ planes,
+                                 int64_t stride, int n_planes, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float a = out[e];
+    for (int k = 0; k < n_planes; ++k) a += planes[k * stride + e];
+    out[e] = a;
+  }
+}
+
 unsigned grid_for(int64_t n, int block) {
   int64_t g = (n + block - 1) / block;
   const int64_t cap = 256 * 64;  // enough waves to saturate HBM; grid-stride beyond
@@ -87,6 +116,21 @@ unsigned grid_for(int64_t n, int block) {
 }
 
 }  // namespace
+
+hipError_t launch_plane_sum(float* out, const float* planes, int64_t plane_stride, int n_planes,
+                            int64_t n_elem, hipStream_t stream) {
+  if (n_planes <= 0 || n_elem <= 0) return hipSuccess;
+  if (n_elem % 4 == 0 && plane_stride % 4 == 0) {
+    const int64_t n4 = n_elem / 4;
+    hipLaunchKernelGGL(plane_sum_vec4, dim3(grid_for(n4, 256)), dim3(256), 0, stream,
+                       reinterpret_cast<float4*>(out), reinterpret_cast<const float4*>(planes),
+                       plane_stride / 4, n_planes, n4);
+  } else {
+    hipLaunchKernelGGL(plane_sum_scalar, dim3(grid_for(n_elem, 256)), dim3(256), 0, stream, out,
+                       planes, plane_stride, n_planes, n_elem);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_cross_scan(const void* x, int elem_bytes, int B, int H, int W, int D,
                              const int* route_of_slot, int n_sel, void* routes,

@@ -93,7 +93,7 @@ def test_workspace_size(lib):
     x = fmap(B=2, H=4, W=5, D=32)
     n = 2 * 4 * 5 * 32
     plane = (n + 63) // 64 * 64 * 4
-    cnt = 256
+    cnt = 0  # no counters: the route sum is a separate streaming pass
     assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, None) == cnt + 3 * plane
     assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 5, 0, None) == cnt + plane
     assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 4, 0, None) == 0
