@@ -48,7 +48,10 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
                                                    __builtin_bit_cast(short4v, b), c, 0, 0, 0);
 }
-// c += a b with a, b given as hi/lo pairs (the lo*lo term is below fp32 resolution)
+// c += a b with a, b given as hi/lo pairs (the lo*lo term is below fp32 resolution).
+// An accumulation chain never mixes the 16x16x32 and 16x16x16 shapes: a 16x16x16 that
+// takes a just-issued 16x16x32 result as its accumulator was seen to read the accumulator
+// from before that product (no wait states are inserted between the two shapes).
 __device__ __forceinline__ f32x4 mma32x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
   c = mma32(al, bh, c);
   c = mma32(ah, bl, c);
@@ -106,9 +109,10 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   constexpr int kThreads = 64 * NW;
   constexpr int NT = D / 16;                       // column tiles of the state
   constexpr int KS = D / 32;                       // 32-deep k-steps over the head dimension
-  constexpr int R = 4 * D + 2;                     // state rows: M_mem, M_k, M_v, M_q, m_eta, m_alpha
-  constexpr int MT = (R + 15) / 16;                // state-row tiles
-  constexpr int MTW = (MT + kWaves - 1) / kWaves;  // tiles per wave (round robin)
+  constexpr int MT = 4 * D / 16;                   // register tiles: rows of M_mem, M_k, M_v, M_q
+  constexpr int MTW = MT / kWaves;                 // tiles per wave (round robin)
+  static_assert(MT % kWaves == 0, "every wave holds the same number of state-row tiles");
+  constexpr int TR = 4 * D;                        // first tail row: m_eta, then m_alpha
   constexpr int LD = D + 4;                        // fp32 stride of token-major tiles
   constexpr int XLD = D + 8;                       // bf16 stride of the token block
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
@@ -131,6 +135,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
   __shared__ float cprev[NT * kSB], bco[NT * (kSB + 1)];  // one copy per solve wave
+  // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
+  // number of register tiles: Tb[cur] is the chunk-start copy, Tb[cur ^ 1] the update
+  __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,13 +169,17 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
     for (int mi = 0; mi < MTW; ++mi) {
       const int row = (w + kWaves * mi) * 16 + c16;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (row < R) v = *reinterpret_cast<const f32x4*>(init + row * D + n * 16 + 4 * g);
-        S[mi][n] = v;
-      }
+      for (int n = 0; n < NT; ++n) S[mi][n] = *reinterpret_cast<const f32x4*>(init + row * D + n * 16 + 4 * g);
     }
+    for (int i = threadIdx.x; i < 2 * D; i += kThreads) Tb[0][i] = init[TR * D + i];
   }
+  int cur = 0;  // which Tb copy holds the chunk-start gate rows
+  // B-operand values of the gate rows for column tile n (rows past the two are zero)
+  auto tail_tile = [&](const float* t, int n, int c, int gg) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(t + (c & 1) * D + n * 16 + 4 * gg);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    return c < 2 ? v : z;
+  };
 
   // Tokens are gathered one block ahead: block k+1's 16-byte loads (8 channels per loader
   // thread) are in flight while block k computes, and are staged into LDS at its end.
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           const int m = w + kWaves * mi;
-          if (m < NT || m >= MT) continue;
+          if (m < NT) continue;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -259,9 +270,21 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
             acc = mma32(xa[s], Sh[mi][s], acc);
           }
           const int row = m * 16 + c16;
-          if (row < R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Pj[(4 * g + i) * PLD + row - D] = acc[i];
+          for (int i = 0; i < 4; ++i) Pj[(4 * g + i) * PLD + row - D] = acc[i];
+        }
+        if (w == 0) {  // the gate rows: scores s_eta, s_alpha of every token
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            bf16x8 th, tl;
+            split8(tail_tile(Tb[cur], 2 * s, c16, g), tail_tile(Tb[cur], 2 * s + 1, c16, g), th, tl);
+            acc = mma32(xa[s], tl, acc);
+            acc = mma32(xa[s], th, acc);
+          }
+          if (c16 < 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pj[(4 * g + i) * PLD + 3 * D + c16] = acc[i];
           }
         }
       }
@@ -389,6 +412,33 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           L1T[i] = rr < c16 ? st_c * pc[i] * gr[i] : 0.f;
           eye[i] = rr == c16 ? 1.f : 0.f;
         }
+        // right-hand-side inputs of this wave's column tile, loaded before the inverse so
+        // their latency overlaps it (RHS[j][col] = -step_j (P(0,j) (G_s k_j)[col] + delta_j[col]))
+        const int n_own = wi;  // NSW == NT: exactly one column tile per solve wave
+        f32x4 gk, dj, sj, cj;
+        if (MULTI && !first) {  // G_s k_t for this column tile (G_s is the chunk gain so far)
+          gk = zero4;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            f32x4 k0, k1, g0, g1;
+            load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+            load_row_pair(Gs + (n_own * 16 + c16) * LD, s, g, g0, g1);
+            bf16x8 kh, kl, gh, gl;
+            split8(k0, k1, kh, kl);
+            split8(g0, g1, gh, gl);
+            gk = mma32x3(kh, kl, gh, gl, gk);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n_own * 16 + c16];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * g + e;
+          dj[e] = Dls[j * LD + n_own * 16 + c16];
+          sj[e] = stp[j];
+          cj[e] = cprev[wi * kSB + j];
+        }
         const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
         const f32x4 E = eye - L1T + L2T - mm16(L2, L1T);       // (I + L2^T)(I - L^T)
         const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
@@ -397,37 +447,17 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         const f32x4 TiT = mm16(FT, E);                         // ((I + L)^-1)^T
         bf16x4 th, tl;
         split4(TiT, th, tl);
-        // right-hand sides of this wave's column tile(s), already in the B-operand layout
-        for (int n = wi; n < NT; n += NSW) {
-          f32x4 gk;
-          if (MULTI && !first) {  // G_s k_t for this column tile (G_s is the chunk gain so far)
-            gk = zero4;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              f32x4 k0, k1, g0, g1;
-              load_row_pair(Ks + c16 * LD, s, g, k0, k1);
-              load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
-              bf16x8 kh, kl, gh, gl;
-              split8(k0, k1, kh, kl);
-              split8(g0, g1, gh, gl);
-              gk = mma32x3(kh, kl, gh, gl, gk);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n * 16 + c16];
-          }
+        // U = (I + L)^-1 RHS for this wave's column tile, then Ub = P(t+1,16) U
+        {
           f32x4 rhs;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 4 * g + e;
-            rhs[e] = -stp[j] * (cprev[wi * kSB + j] * gk[e] + Dls[j * LD + n * 16 + c16]);
-          }
+          for (int e = 0; e < 4; ++e) rhs[e] = -sj[e] * (cj[e] * gk[e] + dj[e]);
           bf16x4 rh, rl;
           split4(rhs, rh, rl);
           const f32x4 u = mma16x3(th, tl, rh, rl, zero4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int t = 4 * g + i, col = n * 16 + c16;
+            const int t = 4 * g + i, col = n_own * 16 + c16;
             const float ub = bco[wi * (kSB + 1) + t] * u[i];
             if (MULTI) Ubs[t * LD + col] = ub;
             const __bf16 uh = (__bf16)ub;
@@ -464,16 +494,25 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          if (w + kWaves * mi < MT) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
-          }
+          for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
           split4(z, zh[mi], zl[mi]);
+        }
+        // gate rows: every readout wave forms their Z tile and updates column tile w
+        bf16x4 tzh, tzl;
+        if (w < NT) {
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            bf16x8 th, tl;
+            split8(tail_tile(Tb[cur], 2 * s, c16, g), tail_tile(Tb[cur], 2 * s + 1, c16, g), th, tl);
+            z = mma32x3(uh[s], ul[s], th, tl, z);
+          }
+          split4(z, tzh, tzl);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
-          if (w + kWaves * mi >= MT) continue;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             f32x4 acc = MULTI ? Acc[MULTI ? mi : 0][MULTI ? n : 0] : S[mi][n];
@@ -485,6 +524,16 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
               S[mi][n] = acc;
             }
           }
+        }
+        if (w < NT) {
+          f32x4 acc = tail_tile(first ? Tb[cur] : Tb[cur ^ 1], w, c16, g);
+          acc *= cc;
+          // K operand of column tile w, read again (an index into kah by wave id would not
+          // stay in registers)
+          const bf16x4 kh = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtH + (w * 16 + c16) * KTLD + 4 * g));
+          const bf16x4 kl = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (w * 16 + c16) * KTLD + 4 * g));
+          acc = mma16x3(kh, kl, tzh, tzl, acc);
+          if (c16 < 2) *reinterpret_cast<f32x4*>(Tb[cur ^ 1] + c16 * D + w * 16 + 4 * g) = acc;
         }
         // gain of the chunk so far, needed by the next block of the same chunk
         if (MULTI && !last_block) {
@@ -527,6 +576,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) S[mi][n] = Acc[MULTI ? mi : 0][MULTI ? n : 0];
     }
+    cur ^= 1;
   }
 
   if (p.final_mem) {
@@ -534,11 +584,11 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
     for (int mi = 0; mi < MTW; ++mi) {
       const int row = (w + kWaves * mi) * 16 + c16;
-      if (row >= R) continue;
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         *reinterpret_cast<f32x4*>(fin + row * D + n * 16 + 4 * g) = S[mi][n];
     }
+    for (int i = threadIdx.x; i < 2 * D; i += kThreads) fin[TR * D + i] = Tb[cur][i];
   }
 
 }
