@@ -103,7 +103,7 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // NW waves per chain: 4 for d = 32, 8 for d = 64 (at most three state-row tiles per wave,
 // so two waves fit on a SIMD).  Gates use waves 0-3 (16 lanes per token); with eight
 // waves the solve coefficients run on waves 4-7 while waves 0-3 read out.
-template <int D, bool MULTI, int NW>
+template <int D, bool MULTI, int NW, bool KEEP_SPLIT>
 __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
@@ -222,14 +222,30 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 
   // bf16 hi/lo split of the chunk-start state, shared by the projections, the readout
   // and the carry of every block of the chunk (S_b is constant over the chunk)
-  bf16x8 Sh[MTW][KS], Sl[MTW][KS];
+  // KEEP_SPLIT holds it across the chunk; otherwise each phase splits its own tiles
+  // again (fewer live registers, more VALU work)
+  bf16x8 Sh[KEEP_SPLIT ? MTW : 1][KEEP_SPLIT ? KS : 1], Sl[KEEP_SPLIT ? MTW : 1][KEEP_SPLIT ? KS : 1];
+  auto state_split = [&](int mi, int s, bf16x8& hi, bf16x8& lo) {
+    if (KEEP_SPLIT) {
+      hi = Sh[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0];
+      lo = Sl[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0];
+    } else {
+      // opaque copies: the compiler would otherwise share one split between the phases
+      // and keep it live across all of them
+      f32x4 a = S[mi][2 * s], c = S[mi][2 * s + 1];
+      asm volatile("" : "+v"(a), "+v"(c));
+      split8(a, c, hi, lo);
+    }
+  };
 
   for (int s0 = 0; s0 < N; s0 += C) {
     const int s1 = min(s0 + C, N);
 #pragma unroll
     for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
+      for (int s = 0; s < KS; ++s)
+        if (KEEP_SPLIT) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0],
+                               Sl[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0]);
     if (MULTI) {
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
@@ -266,8 +282,10 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            acc = mma32(xa[s], Sl[mi][s], acc);
-            acc = mma32(xa[s], Sh[mi][s], acc);
+            bf16x8 sh, sl;
+            state_split(mi, s, sh, sl);
+            acc = mma32(xa[s], sl, acc);
+            acc = mma32(xa[s], sh, acc);
           }
           const int row = m * 16 + c16;
 #pragma unroll
@@ -352,7 +370,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           load_row_pair(Qs + c16 * LD, s, g, q0, q1);
           bf16x8 ah, al;
           split8(q0, q1, ah, al);
-          acc = mma32x3(ah, al, Sh[mi][s], Sl[mi][s], acc);
+          bf16x8 sh, sl;
+          state_split(mi, s, sh, sl);
+          acc = mma32x3(ah, al, sh, sl, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -404,18 +424,23 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           split8(k0, k1, kh, kl);
           gr = mma32x3(kh, kl, kh, kl, gr);
         }
-        f32x4 L1, L1T, eye;
+        f32x4 L1, L1T;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g + i;
           L1[i] = c16 < rr ? st_r[i] * pj[i] * gr[i] : 0.f;
           L1T[i] = rr < c16 ? st_c * pc[i] * gr[i] : 0.f;
-          eye[i] = rr == c16 ? 1.f : 0.f;
         }
+        // X + I for a matrix in the accumulator layout
+        auto plus_eye = [&](f32x4 x) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] += (4 * g + i == c16) ? 1.f : 0.f;
+          return x;
+        };
         // right-hand-side inputs of this wave's column tile, loaded before the inverse so
         // their latency overlaps it (RHS[j][col] = -step_j (P(0,j) (G_s k_j)[col] + delta_j[col]))
         const int n_own = wi;  // NSW == NT: exactly one column tile per solve wave
-        f32x4 gk, dj, sj, cj;
+        f32x4 gk;
         if (MULTI && !first) {  // G_s k_t for this column tile (G_s is the chunk gain so far)
           gk = zero4;
 #pragma unroll
@@ -432,26 +457,22 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n_own * 16 + c16];
         }
+        f32x4 rhs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * g + e;
-          dj[e] = Dls[j * LD + n_own * 16 + c16];
-          sj[e] = stp[j];
-          cj[e] = cprev[wi * kSB + j];
+          rhs[e] = -stp[j] * (cprev[wi * kSB + j] * gk[e] + Dls[j * LD + n_own * 16 + c16]);
         }
         const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
-        const f32x4 E = eye - L1T + L2T - mm16(L2, L1T);       // (I + L2^T)(I - L^T)
+        const f32x4 E = plus_eye(L2T - L1T - mm16(L2, L1T));  // (I + L2^T)(I - L^T)
         const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
         const f32x4 L8 = mm16(L4T, L4);
-        const f32x4 FT = eye + L4 + L8 + mm16(L4T, L8);        // ((I + L8^T)(I + L4^T))^T
+        const f32x4 FT = plus_eye(L4 + L8 + mm16(L4T, L8));   // ((I + L8^T)(I + L4^T))^T
         const f32x4 TiT = mm16(FT, E);                         // ((I + L)^-1)^T
         bf16x4 th, tl;
         split4(TiT, th, tl);
         // U = (I + L)^-1 RHS for this wave's column tile, then Ub = P(t+1,16) U
         {
-          f32x4 rhs;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rhs[e] = -sj[e] * (cj[e] * gk[e] + dj[e]);
           bf16x4 rh, rl;
           split4(rhs, rh, rl);
           const f32x4 u = mma16x3(th, tl, rh, rl, zero4);
@@ -495,7 +516,11 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         for (int mi = 0; mi < MTW; ++mi) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) z = mma32x3(uh[s], ul[s], Sh[mi][s], Sl[mi][s], z);
+          for (int s = 0; s < KS; ++s) {
+            bf16x8 sh, sl;
+            state_split(mi, s, sh, sl);
+            z = mma32x3(uh[s], ul[s], sh, sl, z);
+          }
           split4(z, zh[mi], zl[mi]);
         }
         // gate rows: every readout wave forms their Z tile and updates column tile w
@@ -595,6 +620,13 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 
 }  // namespace
 
+#ifndef KEEP32
+#define KEEP32 true
+#endif
+#ifndef KEEP64
+#define KEEP64 false
+#endif
+
 bool mfma_path_supported(const ChainParams& p, int d) {
   if (!p.x_bf16) return false;
   if (d == 32) return true;
@@ -611,9 +643,9 @@ hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
   dim3 grid((unsigned)blocks);
   if (d == 32) {
-    hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32>), grid, dim3(256), 0, stream, p);
   } else if (d == 64) {
-    hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64>), grid, dim3(512), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
