@@ -65,33 +65,46 @@ __device__ __forceinline__ f32x4 mma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4
 
 __device__ __forceinline__ void split4(const f32x4 v, bf16x4& hi, bf16x4& lo);
 
-// X Y for 16x16 fp32 matrices in the accumulator layout: a_t holds X^T (A operand),
-// b holds Y (B operand); hi/lo split, three products
+// X Y for 16x16 fp32 matrices in the accumulator layout (lane (g, c), register i holds
+// entry [4g + i][c]): a_t holds X^T, b holds Y.  Register i of both then carries the
+// summation index 4g + i in the k slot of a 16x16x4 fp32 product, so four of them give
+// the exact fp32 product with no operand splitting (VALU-free).
 __device__ __forceinline__ f32x4 mm16(const f32x4 a_t, const f32x4 b) {
-  bf16x4 ah, al, bh, bl;
-  split4(a_t, ah, al);
-  split4(b, bh, bl);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  return mma16x3(ah, al, bh, bl, z);
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a_t[i], b[i], c, 0, 0, 0);
+  return c;
 }
 
+// hi = bf16(x) (round to nearest even), lo = bf16(x - hi), for a pair of floats: one
+// packed conversion for hi, its two halves widened back by a shift and a mask, two
+// subtractions and one packed conversion for lo (three VALU operations per element)
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const f32x2v x = {x0, x1};
+  const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2v));
+  const f32x2v r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+  hi = h;
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(r, bf16x2v));
+}
 __device__ __forceinline__ void split8(const f32x4 v0, const f32x4 v1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 h0 = (__bf16)v0[e], h1 = (__bf16)v1[e];
-    hi[e] = h0;
-    hi[e + 4] = h1;
-    lo[e] = (__bf16)(v0[e] - (float)h0);
-    lo[e + 4] = (__bf16)(v1[e] - (float)h1);
-  }
+  unsigned h0, h1, h2, h3, l0, l1, l2, l3;
+  split_pair(v0[0], v0[1], h0, l0);
+  split_pair(v0[2], v0[3], h1, l1);
+  split_pair(v1[0], v1[1], h2, l2);
+  split_pair(v1[2], v1[3], h3, l3);
+  const u32x4 h = {h0, h1, h2, h3}, l = {l0, l1, l2, l3};
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 __device__ __forceinline__ void split4(const f32x4 v, bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 h = (__bf16)v[e];
-    hi[e] = h;
-    lo[e] = (__bf16)(v[e] - (float)h);
-  }
+  unsigned h0, h1, l0, l1;
+  split_pair(v[0], v[1], h0, l0);
+  split_pair(v[2], v[3], h1, l1);
+  const u32x2 h = {h0, h1}, l = {l0, l1};
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // A-operand k values of step s for a token-major fp32 row: cols 32s+4g.. and 32s+16+4g..
@@ -183,17 +196,22 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 
   // Tokens are gathered one block ahead: block k+1's 16-byte loads (8 channels per loader
   // thread) are in flight while block k computes, and are staged into LDS at its end.
+  // The loaders are the last threads, on solve waves, which issue no global stores: a
+  // wave's wait for its load then never includes the acknowledgements of readout stores.
   constexpr int kLoaders = kSB * (D / 8);
+  constexpr int kLoad0 = kThreads - kLoaders;
   static_assert(kLoaders <= kThreads, "one 16-byte load per loader thread");
   // solve waves: the last NSW waves, none of which owns an M_mem (readout) tile; each
   // repeats the short 16x16 inverse and then handles its own column tiles of U
   constexpr int NSW = NT;
   constexpr int SW0 = kWaves - NSW;
   static_assert(SW0 >= NT, "solve waves must not own readout tiles");
-  const int ld_t = threadIdx.x / (D / 8), ld_c8 = threadIdx.x % (D / 8);
+  static_assert(kLoad0 >= SW0 * 64, "loader threads sit on solve waves");
+  const int ld_i = (int)threadIdx.x - kLoad0;
+  const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
   auto fetch = [&](int tb, int nt) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (threadIdx.x < kLoaders && ld_t < nt) {
+    if (ld_i >= 0 && ld_t < nt) {
       const int pix = pixel(tb + ld_t);
       v = *reinterpret_cast<const u32x4*>(xg + ((int64_t)b * N + pix) * Dt + (int64_t)h * D + ld_c8 * 8);
     }
@@ -206,7 +224,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
     ntn = tn < N ? min(kSB, min((tn / C + 1) * C, N) - tn) : 0;
   };
   auto stage_block = [&](const u32x4& v, int tb, int nt) {
-    if (threadIdx.x < kLoaders) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
+    if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
     if (threadIdx.x < kSB)
       pixs[threadIdx.x] = (int)threadIdx.x < nt ? pixel(tb + threadIdx.x) : 0;
   };
@@ -469,13 +487,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         const f32x4 L8 = mm16(L4T, L4);
         const f32x4 FT = plus_eye(L4 + L8 + mm16(L4T, L8));   // ((I + L8^T)(I + L4^T))^T
         const f32x4 TiT = mm16(FT, E);                         // ((I + L)^-1)^T
-        bf16x4 th, tl;
-        split4(TiT, th, tl);
         // U = (I + L)^-1 RHS for this wave's column tile, then Ub = P(t+1,16) U
         {
-          bf16x4 rh, rl;
-          split4(rhs, rh, rl);
-          const f32x4 u = mma16x3(th, tl, rh, rl, zero4);
+          const f32x4 u = mm16(TiT, rhs);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i, col = n_own * 16 + c16;
