@@ -147,7 +147,8 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
-  __shared__ float cprev[NT * kSB], bco[NT * (kSB + 1)];  // one copy per solve wave
+  __shared__ float cprev[kSB], bco[kSB + 1];  // block retention products
+  __shared__ __attribute__((aligned(16))) float Tis[64 * 4];  // block inverse (transposed)
   // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
   // number of register tiles: Tb[cur] is the chunk-start copy, Tb[cur ^ 1] the update
   __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           if (t < nt) dst[((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
         }
       }
-      // C2: the block's write vectors, on the solve wave, all in registers.
+      // C2: the block's write vectors.
       //   (I + L) U = RHS,  L[t][j] = step_t P(j+1,t) (k_t . k_j) for j < t,
       //   RHS[t] = -step_t (P(0,t) G_s k_t + delta_t),  Ub[t] = P(t+1,16) U[t].
       // L is strictly lower triangular (nilpotent), so (I + L)^-1 =
@@ -406,8 +407,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       // 16-step substitution.  Matrices are held in the MFMA accumulator layout (lane
       // (g, c16), register i = entry [4g+i][c16]) together with their transposes, which
       // is exactly the A / B operand layout of the next product.
-      if (w >= SW0) {
-        const int wi = w - SW0;  // this solve wave's column tile of U
+      // The inverse is formed once, by the first solve wave, and published through LDS;
+      // every solve wave then applies it to its own column tile of RHS.
+      if (w == SW0) {
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         // retention products over DPP rows (they need only alpha, so they overlap the
         // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for L^T (prefix
@@ -427,9 +429,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
           const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
           if (lane < kSB) {
-            cprev[wi * kSB + lane] = pre;
-            bco[wi * (kSB + 1) + lane] = suf;
-            if (lane == kSB - 1) bco[wi * (kSB + 1) + kSB] = pre * a_self;
+            cprev[lane] = pre;
+            bco[lane] = suf;
+            if (lane == kSB - 1) bco[kSB] = pre * a_self;
           }
         }
         // token Gram matrix, gr[i] = k_{4g+i} . k_{c16}
@@ -455,12 +457,20 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           for (int i = 0; i < 4; ++i) x[i] += (4 * g + i == c16) ? 1.f : 0.f;
           return x;
         };
-        // right-hand-side inputs of this wave's column tile, loaded before the inverse so
-        // their latency overlaps it (RHS[j][col] = -step_j (P(0,j) (G_s k_j)[col] + delta_j[col]))
-        const int n_own = wi;  // NSW == NT: exactly one column tile per solve wave
-        f32x4 gk;
-        if (MULTI && !first) {  // G_s k_t for this column tile (G_s is the chunk gain so far)
-          gk = zero4;
+        const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
+        const f32x4 E = plus_eye(L2T - L1T - mm16(L2, L1T));  // (I + L2^T)(I - L^T)
+        const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
+        const f32x4 L8 = mm16(L4T, L4);
+        const f32x4 FT = plus_eye(L4 + L8 + mm16(L4T, L8));   // ((I + L8^T)(I + L4^T))^T
+        *reinterpret_cast<f32x4*>(Tis + 4 * lane) = mm16(FT, E);  // ((I + L)^-1)^T
+      }
+      // right-hand-side inputs of each solve wave's column tile (NSW == NT: one each):
+      // G_s k_t (the chunk gain so far applied to the keys) and delta_t
+      f32x4 gk, dl;
+      if (w >= SW0) {
+        const int n_own = w - SW0;
+        if (MULTI && !first) {
+          gk = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             f32x4 k0, k1, g0, g1;
@@ -475,30 +485,29 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n_own * 16 + c16];
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dl[e] = Dls[(4 * g + e) * LD + n_own * 16 + c16];
+      }
+      lds_barrier();
+      // U = (I + L)^-1 RHS for each column tile, then Ub = P(t+1,16) U
+      if (w >= SW0) {
+        const int n_own = w - SW0;
+        const f32x4 TiT = *reinterpret_cast<const f32x4*>(Tis + 4 * lane);
         f32x4 rhs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * g + e;
-          rhs[e] = -stp[j] * (cprev[wi * kSB + j] * gk[e] + Dls[j * LD + n_own * 16 + c16]);
+          rhs[e] = -stp[j] * (cprev[j] * gk[e] + dl[e]);
         }
-        const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
-        const f32x4 E = plus_eye(L2T - L1T - mm16(L2, L1T));  // (I + L2^T)(I - L^T)
-        const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
-        const f32x4 L8 = mm16(L4T, L4);
-        const f32x4 FT = plus_eye(L4 + L8 + mm16(L4T, L8));   // ((I + L8^T)(I + L4^T))^T
-        const f32x4 TiT = mm16(FT, E);                         // ((I + L)^-1)^T
-        // U = (I + L)^-1 RHS for this wave's column tile, then Ub = P(t+1,16) U
-        {
-          const f32x4 u = mm16(TiT, rhs);
+        const f32x4 u = mm16(TiT, rhs);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 4 * g + i, col = n_own * 16 + c16;
-            const float ub = bco[wi * (kSB + 1) + t] * u[i];
-            if (MULTI) Ubs[t * LD + col] = ub;
-            const __bf16 uh = (__bf16)ub;
-            UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
-            UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * g + i, col = n_own * 16 + c16;
+          const float ub = bco[t] * u[i];
+          if (MULTI) Ubs[t * LD + col] = ub;
+          const __bf16 uh = (__bf16)ub;
+          UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
+          UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
         }
       }
       lds_barrier();
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       // D: carry.  Z^T = Ub S_b^T (per state-row tile), then
       //     (S_b G)_new = c (S_b G) + Z K, evaluated transposed so it lands in place.
       {
-        const float cc = bco[kSB];  // copy of the first solve wave
+        const float cc = bco[kSB];
         bf16x8 uh[KS], ul[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
