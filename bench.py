@@ -6,6 +6,15 @@ workload (B=128, 14x14 map, D=384 as 6 heads of 64, row/column chunks of 14,
 bf16 inputs, fp32 state), inputs already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--no-cpu-baseline]
+                  [--copy-probe-mib N]
+
+The roofline object is that of the scan kernel: its time per launch comes from HIP
+events the library records around that kernel alone (the route sum that follows it
+is excluded), on the stream the call is enqueued on.  "traffic" is the scan kernel's
+HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counter runs, scaled by
+what the same counters read for a plain device copy of known size (--copy-probe-mib
+runs one after the timed steps); it is read from the committed record under
+profiles/ and reported only while the kernel sources hash to the recorded value.
 
 Roofline of the scan kernel: algorithmic work per (token, head, route), in
 multiply-accumulates, is 4d^2 + 2d for the projections and the readout (bf16
@@ -36,6 +45,8 @@ import workloads as wl  # noqa: E402
 PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
 PEAK_FP32 = 157.3e12    # fp32 matrix / vector, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_traffic.json")
+KERNEL_SOURCES = ["chain_mfma.hip", "device_common.h", "kernels.h"]
 METRIC = wl_metric = "scan tokens/s (positions×dirs) for 4-dir Hope memory scan; % MFMA/HBM peak"
 
 
@@ -62,6 +73,28 @@ def roofline_numbers(w: wl.Workload, n_dirs: int = 4) -> dict:
     hbm = x_bytes + out_bytes + init_bytes
     return {"flops": f_bf16 + f_fp32, "flops_bf16": f_bf16, "flops_fp32": f_fp32,
             "t_compute": t_compute, "hbm_bytes": hbm, "t_hbm": hbm / PEAK_HBM}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "self_modifying_memory_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(w: wl.Workload):
+    """HBM bytes per scan launch from the counter record, or None when the record is
+    missing, is for another workload, or predates the current kernel sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != w.name or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 12.0) -> dict:
@@ -92,6 +125,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every (image, head, route) chain of this scan is "
@@ -119,10 +154,17 @@ def main() -> int:
         sets.append((x, torch.empty(x.shape, dtype=torch.float32, device=dev),
                      alloc_workspace(x, w.n_heads, 15, w.chunk)))
     stream = torch.cuda.current_stream()
+    # events around the scan kernel alone, recorded by the library on this stream
+    scan_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for a, b in scan_ev:
+        a.record(stream)
+        b.record(stream)
 
-    def step(i):
+    def step(i, ev=None):
         x, out, ws = sets[i % len(sets)]
-        hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream)
+        hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream,
+                            scan_events=ev)
 
     for i in range(args.warmup):
         step(i)
@@ -133,12 +175,19 @@ def main() -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        step(i)
+        step(i, scan_ev[i])
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_ms = [a.elapsed_time(b) for a, b in scan_ev]
     k_avg = float(np.mean(kernel_ms)) * 1e-3
+    if args.copy_probe_mib > 0:  # a plain copy of known size for the HBM counter scale
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     tokens = w.scan_tokens(4)
     roof = roofline_numbers(w)
@@ -161,9 +210,12 @@ def main() -> int:
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
                    "state_dtype": "f32"},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "kernel_ms": k_avg * 1e3, "kernel_ms_p10_p90": [
-                         float(np.percentile(kernel_ms, 10)), float(np.percentile(kernel_ms, 90))],
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": recorded_traffic(w),
+                     "kernel": "chain_mfma_kernel", "kernel_ms": k_avg * 1e3,
+                     "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)),
+                                           float(np.percentile(kernel_ms, 90))],
+                     "call_ms": float(np.mean(call_ms)),
+                     "hbm_algorithmic_bytes": roof["hbm_bytes"],
                      "hbm_frac": roof["hbm_bytes"] / k_avg / PEAK_HBM},
     }
     if not args.no_cpu_baseline:

@@ -94,6 +94,10 @@ typedef struct {
                                 epsilon of the soft injection cap (Eq. 19); default 1e-6 */
   int32_t init_per_image;    /* 0: init is [4][n_heads][S]; 1: [B][4][n_heads][S] (resume) */
   int32_t reserved;          /* must be 0 */
+  hipEvent_t scan_begin;     /* NULL, or an event recorded on the stream just before the scan
+                                kernel is enqueued (profiling) */
+  hipEvent_t scan_end;       /* NULL, or an event recorded just after it, before the route sum;
+                                the pair times the scan kernel alone.  Both or neither. */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

@@ -59,6 +59,7 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if (!isfinite(o->eps) || o->eps < 0.f) return HOPE_ERR_INVALID_ARG;
   if (o->init_per_image != 0 && o->init_per_image != 1) return HOPE_ERR_INVALID_ARG;
   if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
+  if ((o->scan_begin == nullptr) != (o->scan_end == nullptr)) return HOPE_ERR_INVALID_ARG;
   if (o->final_memories && !aligned(o->final_memories, 16)) return HOPE_ERR_INVALID_ARG;
   if (o->workspace && !aligned(o->workspace, 256)) return HOPE_ERR_INVALID_ARG;
   return HOPE_OK;
@@ -167,8 +168,10 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;
+  if (o.scan_begin && (st = hip_status(hipEventRecord(o.scan_begin, s))) != HOPE_OK) return st;
   st = hip_status(hope::mfma_path_supported(p, d) ? hope::launch_chain_mfma(p, d, s)
                                                   : hope::launch_chain(p, d, s));
+  if (st == HOPE_OK && o.scan_end) st = hip_status(hipEventRecord(o.scan_end, s));
   if (st != HOPE_OK || p.n_sel == 1) return st;
   return hip_status(hope::launch_plane_sum(out, p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
 }

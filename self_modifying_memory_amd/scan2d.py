@@ -95,11 +95,14 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
                         eps: float = 1e-6, init_per_image: bool = False,
                         final_memories: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+                        workspace: torch.Tensor | None = None,
+                        scan_events: tuple | None = None) -> torch.Tensor:
     """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32).
 
     init_memories: float32 [4, n_heads, 4d^2+2d] (or [B, 4, n_heads, ...] with
     init_per_image).  A workspace is allocated through torch when none is given.
+    scan_events: optional (begin, end) torch.cuda.Event pair that the library records
+    around the scan kernel alone (already recorded once, so that they exist).
     """
     lib = N.load_library()
     _require_device(x, "x")
@@ -116,6 +119,11 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     fm = make_fmap(x, n_heads)
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
                      workspace)
+    if scan_events is not None:
+        begin, end = scan_events
+        if not begin.cuda_event or not end.cuda_event:
+            raise ValueError("scan_events must have been recorded once before use")
+        opts.scan_begin, opts.scan_end = begin.cuda_event, end.cuda_event
     st = lib.hope_scan2d_forward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
                                  out.data_ptr(), ctypes.byref(opts))
     if st != N.HOPE_OK:
