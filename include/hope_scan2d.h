@@ -93,7 +93,8 @@ typedef struct {
   float eps;                 /* stabiliser of the key / query normalisation (App. C.1) and the
                                 epsilon of the soft injection cap (Eq. 19); default 1e-6 */
   int32_t init_per_image;    /* 0: init is [4][n_heads][S]; 1: [B][4][n_heads][S] (resume) */
-  int32_t reserved;          /* must be 0 */
+  int32_t out_dtype;         /* hope_dtype_t of out: HOPE_F32 (default) or HOPE_BF16; a bf16
+                                out holds the fp32 route sum rounded once to nearest even */
   hipEvent_t scan_begin;     /* NULL, or an event recorded on the stream just before the scan
                                 kernel is enqueued (profiling) */
   hipEvent_t scan_end;       /* NULL, or an event recorded just after it, before the route sum;
@@ -117,24 +118,28 @@ void hope_scan2d_default_opts(hope_scan2d_opts_t* opts);
  *   chunk          chunk length; 0 = aligned (W on row routes, H on column routes,
  *                  Eq. 25).  A chunk length that does not divide H*W leaves a
  *                  shorter last chunk.
- *   out            device fp32 [B][H][W][D], 16-byte aligned, overwritten with the
- *                  sum over selected routes of each route's readout restored to its
- *                  pixel, added in the fixed order route 0, 1, 2, 3.
- *   opts           NULL = defaults.  With two or more routes selected a workspace
- *                  is required (hope_scan2d_workspace_size).
+ *   out            device [B][H][W][D] of opts->out_dtype (fp32 by default, or bf16),
+ *                  16-byte aligned, overwritten with the sum over selected routes of
+ *                  each route's readout restored to its pixel, added in fp32 in the
+ *                  fixed order route 0, 1, 2, 3 (then rounded once for a bf16 out).
+ *   opts           NULL = defaults.  With two or more routes selected, or a bf16 out,
+ *                  a workspace is required (hope_scan2d_workspace_size).
  * Errors: HOPE_ERR_INVALID_ARG for null / misaligned pointers, non-positive sizes,
- * D not divisible by n_heads, dirs outside 1..15, chunk < 0, dtype not F32/BF16,
+ * D not divisible by n_heads, dirs outside 1..15, chunk < 0, dtype or out_dtype not
+ * F32/BF16,
  * out overlapping x, init_memories, final_memories or the workspace;
  * HOPE_ERR_UNSUPPORTED for d not in {16, 32, 64}; HOPE_ERR_WORKSPACE when the
  * workspace is missing or too small; HOPE_ERR_HIP when a launch fails.
  * Results are deterministic: the same inputs give bit-identical outputs.
  */
 hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
-                                  uint32_t dirs, int32_t chunk, float* out,
+                                  uint32_t dirs, int32_t chunk, void* out,
                                   const hope_scan2d_opts_t* opts);
 
-/* Bytes of workspace hope_scan2d_forward needs for this call (0 when one route is
- * selected); 0 also for arguments that hope_scan2d_forward would reject. */
+/* Bytes of workspace hope_scan2d_forward needs for this call with these options (NULL =
+ * defaults): one fp32 plane of the map per selected route beyond the first, or per
+ * selected route for a bf16 out; 0 when none is needed, and 0 for arguments that
+ * hope_scan2d_forward would reject. */
 size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                   const hope_scan2d_opts_t* opts);
 

@@ -37,7 +37,7 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("eta_map", ctypes.c_int32), ("eta_scale", ctypes.c_float),
                 ("alpha_bias", ctypes.c_float), ("eps", ctypes.c_float),
-                ("init_per_image", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("init_per_image", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("scan_begin", ctypes.c_void_p), ("scan_end", ctypes.c_void_p)]
 
 

@@ -36,7 +36,9 @@ int slots_of(uint32_t dirs, int* route_of_slot) {
   return n;
 }
 
-// Workspace layout: (n_sel-1) fp32 route planes of one map each, each padded to 256 bytes.
+// Workspace layout: fp32 route planes of one map each, each padded to 256 bytes: one per
+// selected route beyond the first (route 0 writes an fp32 out directly), or one per
+// selected route when out is bf16 (the route sum then rounds once, in its own pass).
 int64_t plane_stride_elems(int64_t n_elem) { return (n_elem + 63) / 64 * 64; }
 
 hope_status_t check_fmap(const hope_fmap_t* x) {
@@ -58,18 +60,23 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if (!isfinite(o->alpha_bias)) return HOPE_ERR_INVALID_ARG;
   if (!isfinite(o->eps) || o->eps < 0.f) return HOPE_ERR_INVALID_ARG;
   if (o->init_per_image != 0 && o->init_per_image != 1) return HOPE_ERR_INVALID_ARG;
-  if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->out_dtype != HOPE_F32 && o->out_dtype != HOPE_BF16) return HOPE_ERR_INVALID_ARG;
   if ((o->scan_begin == nullptr) != (o->scan_end == nullptr)) return HOPE_ERR_INVALID_ARG;
   if (o->final_memories && !aligned(o->final_memories, 16)) return HOPE_ERR_INVALID_ARG;
   if (o->workspace && !aligned(o->workspace, 256)) return HOPE_ERR_INVALID_ARG;
   return HOPE_OK;
 }
 
-size_t workspace_bytes_for(const hope_fmap_t* x, uint32_t dirs) {
+int planes_for(uint32_t dirs, int32_t out_dtype) {
   const int n_sel = popcount4(dirs);
-  if (n_sel <= 1) return 0;
+  return out_dtype == HOPE_BF16 ? n_sel : n_sel - 1;
+}
+
+size_t workspace_bytes_for(const hope_fmap_t* x, uint32_t dirs, int32_t out_dtype) {
+  const int n_planes = planes_for(dirs, out_dtype);
+  if (n_planes <= 0) return 0;
   const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
-  return (size_t)(n_sel - 1) * (size_t)plane_stride_elems(n_elem) * sizeof(float);
+  return (size_t)n_planes * (size_t)plane_stride_elems(n_elem) * sizeof(float);
 }
 
 hope_status_t hip_status(hipError_t e) {
@@ -93,13 +100,14 @@ void hope_scan2d_default_opts(hope_scan2d_opts_t* opts) {
 
 size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                   const hope_scan2d_opts_t* opts) {
-  (void)opts;
   if (check_fmap(x) != HOPE_OK || dirs == 0 || dirs > 15 || chunk < 0) return 0;
-  return workspace_bytes_for(x, dirs);
+  const int32_t out_dtype = opts ? opts->out_dtype : HOPE_F32;
+  if (out_dtype != HOPE_F32 && out_dtype != HOPE_BF16) return 0;
+  return workspace_bytes_for(x, dirs, out_dtype);
 }
 
 hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
-                                  uint32_t dirs, int32_t chunk, float* out,
+                                  uint32_t dirs, int32_t chunk, void* out,
                                   const hope_scan2d_opts_t* opts) {
   hope_scan2d_opts_t o;
   if (opts) {
@@ -117,12 +125,13 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   const int d = x->D / x->n_heads;
   const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
   const size_t x_bytes = (size_t)n_elem * (x->dtype == HOPE_BF16 ? 2 : 4);
-  const size_t out_bytes = (size_t)n_elem * sizeof(float);
+  const bool out_bf16 = o.out_dtype == HOPE_BF16;
+  const size_t out_bytes = (size_t)n_elem * (out_bf16 ? 2 : 4);
   const size_t state_floats = (size_t)4 * d * d + 2 * (size_t)d;
   const size_t init_bytes =
       (o.init_per_image ? (size_t)x->B : 1) * 4 * (size_t)x->n_heads * state_floats * sizeof(float);
   const size_t final_bytes = (size_t)x->B * 4 * x->n_heads * state_floats * sizeof(float);
-  const size_t ws_need = workspace_bytes_for(x, dirs);
+  const size_t ws_need = workspace_bytes_for(x, dirs, o.out_dtype);
 
   const Range r_out = range_of(out, out_bytes);
   if (overlaps(r_out, range_of(x->data, x_bytes))) return HOPE_ERR_INVALID_ARG;
@@ -148,10 +157,15 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   memset(&p, 0, sizeof(p));
   p.x = x->data;
   p.init = init_memories;
-  p.out = out;
-  if (ws_need > 0) p.planes = static_cast<float*>(o.workspace);
-  p.final_mem = o.final_memories;
   p.plane_stride = plane_stride_elems(n_elem);
+  if (out_bf16) {  // every route writes an fp32 plane; the route sum rounds once
+    p.out = static_cast<float*>(o.workspace);
+    p.planes = p.out + p.plane_stride;
+  } else {
+    p.out = static_cast<float*>(out);
+    if (ws_need > 0) p.planes = static_cast<float*>(o.workspace);
+  }
+  p.final_mem = o.final_memories;
   p.x_bf16 = x->dtype == HOPE_BF16;
   p.B = x->B;
   p.H = x->H;
@@ -172,8 +186,13 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   st = hip_status(hope::mfma_path_supported(p, d) ? hope::launch_chain_mfma(p, d, s)
                                                   : hope::launch_chain(p, d, s));
   if (st == HOPE_OK && o.scan_end) st = hip_status(hipEventRecord(o.scan_end, s));
-  if (st != HOPE_OK || p.n_sel == 1) return st;
-  return hip_status(hope::launch_plane_sum(out, p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
+  if (st != HOPE_OK) return st;
+  if (out_bf16)
+    return hip_status(hope::launch_plane_sum_bf16(static_cast<unsigned short*>(out), p.out,
+                                                  p.plane_stride, p.n_sel, n_elem, s));
+  if (p.n_sel == 1) return st;
+  return hip_status(
+      hope::launch_plane_sum(static_cast<float*>(out), p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
 }
 
 const char* hope_status_string(hope_status_t status) {

@@ -33,6 +33,9 @@ bool mfma_path_supported(const ChainParams& p, int d);
 hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream);
 
 // out[i] += planes[0][i] + ... + planes[n-1][i], left to right, fp32 (route sum).
+// out = bf16(planes[0] + planes[1] + ...) in that order, rounded once to nearest even
+hipError_t launch_plane_sum_bf16(unsigned short* out, const float* planes, int64_t plane_stride,
+                                 int n_planes, int64_t n_elem, hipStream_t stream);
 hipError_t launch_plane_sum(float* out, const float* planes, int64_t plane_stride, int n_planes,
                             int64_t n_elem, hipStream_t stream);
 

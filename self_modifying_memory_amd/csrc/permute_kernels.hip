@@ -107,6 +107,37 @@ __global__ void plane_sum_scalar(float* __restrict__ out, const float* __restric
   }
 }
 
+// bf16 out: the fp32 sum of the route planes in slot order, rounded once
+__global__ void plane_sum_bf16_vec4(uint2* __restrict__ out, const float4* __restrict__ planes,
+                                    int64_t stride4, int n_planes, int64_t n4) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n4;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = planes[e];
+    for (int k = 1; k < n_planes; ++k) {
+      const float4 v = planes[k * stride4 + e];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+    }
+    const __bf16 b0 = (__bf16)a.x, b1 = (__bf16)a.y, b2 = (__bf16)a.z, b3 = (__bf16)a.w;
+    uint2 o;
+    o.x = (unsigned)__builtin_bit_cast(unsigned short, b0) | ((unsigned)__builtin_bit_cast(unsigned short, b1) << 16);
+    o.y = (unsigned)__builtin_bit_cast(unsigned short, b2) | ((unsigned)__builtin_bit_cast(unsigned short, b3) << 16);
+    out[e] = o;
+  }
+}
+
+__global__ void plane_sum_bf16_scalar(unsigned short* __restrict__ out, const float* __restrict__ planes,
+                                      int64_t stride, int n_planes, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float a = planes[e];
+    for (int k = 1; k < n_planes; ++k) a += planes[k * stride + e];
+    out[e] = __builtin_bit_cast(unsigned short, (__bf16)a);
+  }
+}
+
 unsigned grid_for(int64_t n, int block) {
   int64_t g = (n + block - 1) / block;
   const int64_t cap = 256 * 64;  // enough waves to saturate HBM; grid-stride beyond
@@ -128,6 +159,21 @@ hipError_t launch_plane_sum(float* out, const float* planes, int64_t plane_strid
   } else {
     hipLaunchKernelGGL(plane_sum_scalar, dim3(grid_for(n_elem, 256)), dim3(256), 0, stream, out,
                        planes, plane_stride, n_planes, n_elem);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_plane_sum_bf16(unsigned short* out, const float* planes, int64_t plane_stride,
+                                 int n_planes, int64_t n_elem, hipStream_t stream) {
+  if (n_planes <= 0 || n_elem <= 0) return hipSuccess;
+  if (n_elem % 4 == 0 && plane_stride % 4 == 0) {
+    const int64_t n4 = n_elem / 4;
+    hipLaunchKernelGGL(plane_sum_bf16_vec4, dim3(grid_for(n4, 256)), dim3(256), 0, stream,
+                       reinterpret_cast<uint2*>(out), reinterpret_cast<const float4*>(planes),
+                       plane_stride / 4, n_planes, n4);
+  } else {
+    hipLaunchKernelGGL(plane_sum_bf16_scalar, dim3(grid_for(n_elem, 256)), dim3(256), 0, stream,
+                       out, planes, plane_stride, n_planes, n_elem);
   }
   return hipGetLastError();
 }

@@ -54,7 +54,8 @@ def make_fmap(x: torch.Tensor, n_heads: int) -> N.hope_fmap_t:
 def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
               alpha_bias: float = 4.0, eps: float = 1e-6, init_per_image: bool = False,
               final_memories: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None) -> N.hope_scan2d_opts_t:
+              workspace: torch.Tensor | None = None,
+              out_dtype: torch.dtype = torch.float32) -> N.hope_scan2d_opts_t:
     lib = N.load_library()
     o = N.hope_scan2d_opts_t()
     lib.hope_scan2d_default_opts(ctypes.byref(o))
@@ -64,6 +65,7 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
     o.alpha_bias = alpha_bias
     o.eps = eps
     o.init_per_image = int(bool(init_per_image))
+    o.out_dtype = N.HOPE_BF16 if out_dtype == torch.bfloat16 else N.HOPE_F32
     if final_memories is not None:
         _require_device(final_memories, "final_memories")
         if final_memories.dtype != torch.float32:
@@ -76,15 +78,20 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
     return o
 
 
-def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0) -> int:
+def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
+                               out_dtype: torch.dtype = torch.float32) -> int:
     lib = N.load_library()
     fm = make_fmap(x, n_heads)
-    return int(lib.hope_scan2d_workspace_size(ctypes.byref(fm), dirs, chunk, None))
+    o = N.hope_scan2d_opts_t()
+    lib.hope_scan2d_default_opts(ctypes.byref(o))
+    o.out_dtype = N.HOPE_BF16 if out_dtype == torch.bfloat16 else N.HOPE_F32
+    return int(lib.hope_scan2d_workspace_size(ctypes.byref(fm), dirs, chunk, ctypes.byref(o)))
 
 
-def alloc_workspace(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0) -> torch.Tensor | None:
+def alloc_workspace(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor | None:
     """A workspace of the size the library asks for (None when none is needed)."""
-    nbytes = hope_scan2d_workspace_size(x, n_heads, dirs, chunk)
+    nbytes = hope_scan2d_workspace_size(x, n_heads, dirs, chunk, out_dtype)
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
@@ -97,7 +104,8 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         final_memories: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None,
                         scan_events: tuple | None = None) -> torch.Tensor:
-    """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32).
+    """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32, or bfloat16
+    when a bfloat16 ``out`` is passed: the fp32 route sum rounded once).
 
     init_memories: float32 [4, n_heads, 4d^2+2d] (or [B, 4, n_heads, ...] with
     init_per_image).  A workspace is allocated through torch when none is given.
@@ -112,13 +120,13 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     _require_device(out, "out")
-    if out.dtype != torch.float32 or tuple(out.shape) != tuple(x.shape):
-        raise ValueError("out must be float32 with the shape of x")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must be float32 or bfloat16 with the shape of x")
     if workspace is None:
-        workspace = alloc_workspace(x, n_heads, dirs, chunk)
+        workspace = alloc_workspace(x, n_heads, dirs, chunk, out.dtype)
     fm = make_fmap(x, n_heads)
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
-                     workspace)
+                     workspace, out.dtype)
     if scan_events is not None:
         begin, end = scan_events
         if not begin.cuda_event or not end.cuda_event:

@@ -58,7 +58,7 @@ int main(void) {
          offsetof(hope_scan2d_opts_t, final_memories), offsetof(hope_scan2d_opts_t, workspace_bytes),
          offsetof(hope_scan2d_opts_t, eta_map), offsetof(hope_scan2d_opts_t, eta_scale),
          offsetof(hope_scan2d_opts_t, eps), offsetof(hope_scan2d_opts_t, init_per_image),
-         offsetof(hope_scan2d_opts_t, reserved), offsetof(hope_scan2d_opts_t, scan_begin),
+         offsetof(hope_scan2d_opts_t, out_dtype), offsetof(hope_scan2d_opts_t, scan_begin),
          offsetof(hope_scan2d_opts_t, scan_end));
   return 0;
 }
@@ -76,7 +76,7 @@ int main(void) {
     F, O = N.hope_fmap_t, N.hope_scan2d_opts_t
     want = [ctypes.sizeof(F), ctypes.sizeof(O), F.dtype.offset, F.n_heads.offset,
             O.final_memories.offset, O.workspace_bytes.offset, O.eta_map.offset, O.eta_scale.offset,
-            O.eps.offset, O.init_per_image.offset, O.reserved.offset, O.scan_begin.offset,
+            O.eps.offset, O.init_per_image.offset, O.out_dtype.offset, O.scan_begin.offset,
             O.scan_end.offset]
     assert vals == want
 
@@ -135,7 +135,7 @@ def test_argument_errors(lib):
     assert call(lib, x, out=FAKE + 256, o=o) == N.HOPE_ERR_INVALID_ARG
     assert call(lib, x, out=FAKE + (1 << 30), o=o) == N.HOPE_ERR_INVALID_ARG
     for k, v in [("eta_map", 2), ("eta_scale", -1.0), ("eta_scale", float("nan")),
-                 ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("reserved", 1),
+                 ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("out_dtype", 2),
                  ("scan_begin", FAKE), ("scan_end", FAKE)]:  # the event pair is both or neither
         assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k
     # final memories overlapping out, misaligned workspace
@@ -153,6 +153,18 @@ def test_workspace_errors(lib):
     assert call(lib, x, o=small) == N.HOPE_ERR_WORKSPACE
     overlap = opts(lib, workspace=FAKE + (2 << 30), workspace_bytes=need)
     assert call(lib, x, o=overlap) == N.HOPE_ERR_INVALID_ARG
+
+
+def test_workspace_size_counts_route_planes(lib):
+    x = fmap(B=2, H=4, W=5, D=32)
+    plane = 2 * 4 * 5 * 32 * 4  # one fp32 map, already a multiple of 256 bytes
+    bf = opts(lib, out_dtype=N.HOPE_BF16)
+    for dirs, n_sel in [(1, 1), (5, 2), (15, 4)]:
+        assert lib.hope_scan2d_workspace_size(ctypes.byref(x), dirs, 0, None) == (n_sel - 1) * plane
+        assert lib.hope_scan2d_workspace_size(ctypes.byref(x), dirs, 0, ctypes.byref(bf)) == n_sel * plane
+    # a single route with a bf16 out still needs its fp32 plane
+    assert call(lib, x, dirs=1, o=bf) == N.HOPE_ERR_WORKSPACE
+    assert lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, ctypes.byref(opts(lib, out_dtype=5))) == 0
 
 
 def test_debug_export_errors(lib):

@@ -123,3 +123,46 @@ def test_full_size_literal_workload_reads_zero():
     assert np.all(fin[..., : w.d * w.d] == 0.0)
     ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, heads=[3], images=[64])
     check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=[3], images=[64])
+
+
+BF16_OUT = [
+    # B, H, W, D, nh, dtype, dirs, chunk
+    (2, 5, 7, 64, 2, "bf16", 15, 0),    # MFMA kernel, four routes
+    (1, 6, 9, 64, 1, "f32", 15, 4),     # fp32 kernel, ragged chunks
+    (2, 7, 7, 64, 2, "bf16", 8, 0),     # one route: its own fp32 plane, then rounded
+]
+
+
+@pytest.mark.parametrize("case", BF16_OUT, ids=[f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}h{c[4]}_{c[5]}_dirs{c[6]}"
+                                                  for c in BF16_OUT])
+def test_bf16_out_is_the_fp32_sum_rounded_once(case):
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    from _parity import to_device
+    B, H, W, D, nh, dt, dirs, chunk = case
+    print("case", case, flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=5000 + H * 37 + W, dtype=dt, live=True)
+    x, init = to_device(inp, dt)
+    o32 = hope_scan2d_forward(x, init, nh, dirs, chunk)
+    o16 = hope_scan2d_forward(x, init, nh, dirs, chunk,
+                              out=torch.empty(x.shape, dtype=torch.bfloat16, device=x.device))
+    torch.cuda.synchronize()
+    # the same fp32 sum, added in the same route order, rounded once to nearest even
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    ref, _ = oracle.scan2d(inp["x"], inp["init"], nh, dirs=dirs, chunk=chunk)
+    e = check_out(o16.float().cpu().numpy(), ref, nh, TOL[dt] + 2.0 ** -8)
+    print(f"  rel_inf out(bf16) {e:.2e}", flush=True)
+
+
+def test_hires_long_memory_stress_sampled():
+    # The high-resolution map with alpha-bias 8 (alpha ~ 0.9997): state carried across
+    # 128 chunks of 128 tokens with almost no decay, checked on one (image, head) slice.
+    w = wl.WORKLOADS[4]
+    print(f"workload {w.name} alpha_bias 8: image 0 head 1", flush=True)
+    inp = wl.draw_workload(w, live=True)
+    out, fin = run_gpu(inp, w.n_heads, w.dtype, alpha_bias=8.0)
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, heads=[1], images=[0],
+                                     alpha_bias=8.0)
+    e_out = check_out(out, ref_out, w.n_heads, TOL[w.dtype], heads=[1], images=[0])
+    e_fin = check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=[1], images=[0])
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
