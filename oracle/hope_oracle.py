@@ -180,7 +180,7 @@ def _matvec(M, x):
 # --------------------------------------------------------------------------
 def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid",
                eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
-               control: bool = True, log: list | None = None):
+               control: bool = True, log: list | None = None, readout: str = "boundary"):
     """Run chains over ordered tokens.
 
     xs    : [n, N, d] tokens in route order
@@ -188,8 +188,15 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
     chunk : chunk length C >= 1
     control=False executes the raw step eta (the uncontrolled recurrence of
     [VH] Eq. 17), used only to show that the checks can fail.
+    readout="boundary" reads y_t = M^m_b q_t with the memory frozen at the chunk
+    start ([VH] Eq. 16); "running" reads y_t = M^m_{t-1} q_t, the memory as updated
+    by the chunk's earlier tokens ([NL] Eq. 94, y_t = M_memory,t-1 q_t, applied inside
+    the chunk; the projections still come from the chunk-start memories).  Both
+    agree when every chunk is one token.
     Returns (ys [n, N, d], final state dict).
     """
+    if readout not in ("boundary", "running"):
+        raise ValueError("readout must be 'boundary' or 'running'")
     xs = np.asarray(xs, dtype=np.float64)
     n, N, d = xs.shape
     M = {m: np.array(state[m], dtype=np.float64, copy=True) for m in MEMORIES}
@@ -203,7 +210,9 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
             q = stabilized_normalize(_matvec(Mb["q"], x), eps)
             eta = phi_eta(_matvec(Mb["eta"], x)[:, 0], eta_map, eta_scale)
             alpha = phi_alpha(_matvec(Mb["alpha"], x)[:, 0], alpha_bias)
-            ys[:, t, :] = _matvec(Mb["mem"], q)               # y_t = M^m_b q_t
+            # y_t = M^m_b q_t (boundary) or M^m_{t-1} q_t (running: M is not yet
+            # updated with token t here)
+            ys[:, t, :] = _matvec(Mb["mem"] if readout == "boundary" else M["mem"], q)
             delta = k - v
             step = executed_step(eta, alpha, k, delta, eps) if control else eta
             if log is not None:
@@ -218,7 +227,8 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
 
 def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk: int = 0,
            eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
-           eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None):
+           eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None,
+           readout: str = "boundary"):
     """The whole operator: serialise, run every (image, head, route) chain, merge.
 
     x    : [B, H, W, D] (any float dtype; widened to fp64)
@@ -250,7 +260,7 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
             flat = init[images, r, h] if init_per_image else np.broadcast_to(init[r, h], (nb, S))
             st = unflatten_state(flat, d)
             C = route_chunk(H, W, r, chunk)
-            ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps)
+            ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout)
             routes[r] = ys
             final[:, r, hi, :] = flatten_state(fin)
         if routes:

@@ -32,7 +32,7 @@ def _normalize(z):
     return [v / n for v in z]
 
 
-def mp_chain(xs, st, C, eta_scale, alpha_bias):
+def mp_chain(xs, st, C, eta_scale, alpha_bias, running=False):
     N, d = len(xs), len(xs[0])
     M = {m: [row[:] for row in st[m]] for m in NAMES}
     ys = []
@@ -46,7 +46,7 @@ def mp_chain(xs, st, C, eta_scale, alpha_bias):
             q = _normalize(_mv(Mb["q"], x))
             eta = eta_scale / (1 + mp.exp(-_mv(Mb["eta"], x)[0]))
             alpha = 1 / (1 + mp.exp(-(_mv(Mb["alpha"], x)[0] + alpha_bias)))
-            ys.append(_mv(Mb["mem"], q))
+            ys.append(_mv(M["mem"] if running else Mb["mem"], q))
             delta = [k[i] - v[i] for i in range(d)]
             r = mp.sqrt(mp.fsum(z * z for z in delta) + eps * eps) + eps
             inj = (1 - mp.mpf("1e-3")) * (1 - alpha) / r
@@ -69,9 +69,10 @@ def mp_chain(xs, st, C, eta_scale, alpha_bias):
     return ys, M
 
 
+@pytest.mark.parametrize("readout", ["boundary", "running"])
 @pytest.mark.parametrize("d", [1, 2, 4])
 @pytest.mark.parametrize("C", [1, 2, 4, 0])
-def test_oracle_matches_50_digit_evaluation_on_4x4(d, C):
+def test_oracle_matches_50_digit_evaluation_on_4x4(d, C, readout):
     rng = np.random.Generator(np.random.PCG64(100 + d * 10 + C))
     H = W = 4
     B = 1
@@ -80,7 +81,7 @@ def test_oracle_matches_50_digit_evaluation_on_4x4(d, C):
     init = rng.standard_normal((4, 1, S)) * np.sqrt(1.0 / d)
     eta_scale, alpha_bias = 2.0, 1.5
     out, fin = oracle.scan2d(x, init, 1, dirs=15, chunk=C, eta_scale=eta_scale,
-                             alpha_bias=alpha_bias)
+                             alpha_bias=alpha_bias, readout=readout)
     want_out = [[[mp.mpf(0)] * d for _ in range(W)] for _ in range(H)]
     for r in range(4):
         order = oracle.route_order(H, W, r)
@@ -88,7 +89,8 @@ def test_oracle_matches_50_digit_evaluation_on_4x4(d, C):
         st0 = oracle.unflatten_state(init[r, 0], d)
         st = {m: _mpmat(st0[m]) for m in NAMES}
         Cr = C if C > 0 else (W if r < 2 else H)
-        ys, M = mp_chain(xs, st, Cr, mp.mpf(eta_scale), mp.mpf(alpha_bias))
+        ys, M = mp_chain(xs, st, Cr, mp.mpf(eta_scale), mp.mpf(alpha_bias),
+                         running=readout == "running")
         for t, p in enumerate(order):
             for i in range(d):
                 want_out[p // W][p % W][i] += ys[t][i]

@@ -432,3 +432,56 @@ def test_partial_last_chunk_matches_tokenwise_at_chunk_one():
     ya, fa = oracle.srnl_chain(xs[:, :6], st, 3, eta_scale=2.0)
     yb, fb = oracle.srnl_chain(xs[:, 6:], fa, 3, eta_scale=2.0)
     np.testing.assert_allclose(np.concatenate([ya, yb], 1), ys3, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Running-state readout: [NL] Eq. 94 reads y_t = M_memory,t-1 q_t; inside a chunk of
+# [VH] Sec. 2.1.3 the memory after the chunk's earlier tokens is M^m_b G_{t-1}
+# ([VH] App. B.4 Prop. 2), while q_t still comes from the chunk-start M_q.
+# --------------------------------------------------------------------------
+def test_running_readout_equals_gain_form():
+    rng = _rng(31)
+    d, C, n = 5, 9, 3
+    st = _state(rng, d, n)
+    xs = rng.standard_normal((n, C, d)) * 1.3
+    log = []
+    ys, _ = oracle.srnl_chain(xs, st, C, eta_scale=2.5, log=log, readout="running")
+    k = np.stack([e["k"] for e in log], 1)
+    delta = np.stack([e["delta"] for e in log], 1)
+    step = np.stack([e["step"] for e in log], 1)
+    alpha = np.stack([e["alpha"] for e in log], 1)
+    gains = oracle.chunk_gain(k, delta, step, alpha)  # gains[t]: after t tokens
+    for t in range(C):
+        q = np.einsum("nij,nj->ni", st["q"], xs[:, t])
+        q = q / np.sqrt(np.sum(q * q, -1, keepdims=True) + 1e-6)
+        want = np.einsum("nij,njk,nk->ni", st["mem"], gains[t], q)
+        np.testing.assert_allclose(ys[:, t], want, rtol=1e-11, atol=1e-13)
+
+
+def test_running_readout_is_boundary_readout_at_chunk_one():
+    rng = _rng(32)
+    st = _state(rng, 4, 2)
+    xs = rng.standard_normal((2, 10, 4))
+    yb, fb = oracle.srnl_chain(xs, st, 1, eta_scale=2.0, readout="boundary")
+    yr, fr = oracle.srnl_chain(xs, st, 1, eta_scale=2.0, readout="running")
+    assert np.array_equal(yb, yr)
+    for m in oracle.MEMORIES:
+        assert np.array_equal(fb[m], fr[m])  # the readout never feeds the state
+
+
+def test_running_readout_zero_step_is_decayed_boundary_readout():
+    # eta = 0: M^m_{t-1} = (prod of the chunk's earlier alphas) M^m_b, so the running
+    # readout is the boundary readout scaled by that in-chunk product.
+    rng = _rng(33)
+    d, N, C, n = 4, 10, 4, 2
+    st = _state(rng, d, n)
+    xs = rng.standard_normal((n, N, d))
+    log = []
+    yr, _ = oracle.srnl_chain(xs, st, C, eta_scale=0.0, alpha_bias=1.0, log=log, readout="running")
+    yb, _ = oracle.srnl_chain(xs, st, C, eta_scale=0.0, alpha_bias=1.0, readout="boundary")
+    alpha = np.stack([e["alpha"] for e in log], 1)
+    for s in range(0, N, C):
+        prod = np.ones(n)
+        for t in range(s, min(s + C, N)):
+            np.testing.assert_allclose(yr[:, t], prod[:, None] * yb[:, t], rtol=1e-12)
+            prod = prod * alpha[:, t]
