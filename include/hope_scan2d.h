@@ -79,6 +79,16 @@ typedef struct {
   int32_t B, H, W, D, n_heads;
 } hope_fmap_t;
 
+/* Which memory the readout y_t = M_mem q_t uses inside a chunk.
+ *   BOUNDARY: the memory frozen at the chunk start, M_mem,b ("VisionHOPE: Visual
+ *             Backbones as Self-Modifying Learning Systems", Sec. 2.1.3 Eq. 16).
+ *   RUNNING:  the memory after the chunk's earlier tokens, M_mem,b G_{t-1} ("Nested
+ *             Learning: The Illusion of Deep Learning Architectures", Eq. 94, which reads
+ *             M_memory,t-1; the gain G of VisionHOPE App. B.4 Prop. 2).  q_t and every
+ *             other projection still come from the chunk-start memories.  Equal to
+ *             BOUNDARY when every chunk is one token. */
+typedef enum { HOPE_READOUT_BOUNDARY = 0, HOPE_READOUT_RUNNING = 1 } hope_readout_t;
+
 /* Options of hope_scan2d_forward.  Start from hope_scan2d_default_opts(). */
 typedef struct {
   hipStream_t stream;        /* stream to enqueue on; 0 = default stream */
@@ -99,6 +109,8 @@ typedef struct {
                                 kernel is enqueued (profiling) */
   hipEvent_t scan_end;       /* NULL, or an event recorded just after it, before the route sum;
                                 the pair times the scan kernel alone.  Both or neither. */
+  int32_t readout;           /* hope_readout_t; default HOPE_READOUT_BOUNDARY */
+  int32_t reserved;          /* must be 0 */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

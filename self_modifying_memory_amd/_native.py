@@ -23,6 +23,8 @@ HOPE_F32 = 0
 HOPE_BF16 = 1
 HOPE_ETA_SIGMOID = 0
 HOPE_ETA_SOFTPLUS = 1
+HOPE_READOUT_BOUNDARY = 0
+HOPE_READOUT_RUNNING = 1
 HOPE_DIR_ALL = 15
 
 
@@ -38,7 +40,8 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("eta_map", ctypes.c_int32), ("eta_scale", ctypes.c_float),
                 ("alpha_bias", ctypes.c_float), ("eps", ctypes.c_float),
                 ("init_per_image", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("scan_begin", ctypes.c_void_p), ("scan_end", ctypes.c_void_p)]
+                ("scan_begin", ctypes.c_void_p), ("scan_end", ctypes.c_void_p),
+                ("readout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None

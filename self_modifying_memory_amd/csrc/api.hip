@@ -62,6 +62,9 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if (o->init_per_image != 0 && o->init_per_image != 1) return HOPE_ERR_INVALID_ARG;
   if (o->out_dtype != HOPE_F32 && o->out_dtype != HOPE_BF16) return HOPE_ERR_INVALID_ARG;
   if ((o->scan_begin == nullptr) != (o->scan_end == nullptr)) return HOPE_ERR_INVALID_ARG;
+  if (o->readout != HOPE_READOUT_BOUNDARY && o->readout != HOPE_READOUT_RUNNING)
+    return HOPE_ERR_INVALID_ARG;
+  if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
   if (o->final_memories && !aligned(o->final_memories, 16)) return HOPE_ERR_INVALID_ARG;
   if (o->workspace && !aligned(o->workspace, 256)) return HOPE_ERR_INVALID_ARG;
   return HOPE_OK;
@@ -179,6 +182,7 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   p.eta_scale = o.eta_scale;
   p.alpha_bias = o.alpha_bias;
   p.eps = o.eps;
+  p.readout = o.readout;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;

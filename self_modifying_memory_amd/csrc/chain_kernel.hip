@@ -3,6 +3,8 @@
 // Method ("VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"):
 //   Sec. 2.3 Eq. 24-25   route order and row/column-aligned chunks;
 //   Sec. 2.1.3 Eq. 15-16 k, v, q, eta, alpha and y = M_mem q from the chunk-start state;
+//                        or the running readout y_t = M_mem,b G_{t-1} q_t ("Nested
+//                        Learning", Eq. 94 applied inside the chunk);
 //   Sec. 2.2 Eq. 19-20   executed step (soft injection cap, spectral clamp) with the
 //                        App. B.3 inward factors, |k|^2 floor and one-ulp rounding;
 //   App. B.4 Eq. 46      one gain G per chunk, G_t = alpha_t G_{t-1} - step_t (G_{t-1} k_t
@@ -42,6 +44,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   __shared__ float X[kTB * SP];
   __shared__ float P[kTB * PS];
   __shared__ float Gl[D * SP];
+  __shared__ float Wq[kTB * SP];  // running readout: w_t = G_{t-1} q_t per token
+  const bool running = p.readout != 0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,31 +114,47 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         }
       }
       __syncthreads();
-      // readout y_t = M_mem,b q_t (Eq. 16), written at the token's pixel
-      for (int e = tid; e < nt * D; e += kThreads) {
-        const int t = e / D, i = e % D;
-        const float* mrow = &S[i * SP];
-        const float* qv = &P[t * PS + 2 * D];
-        float acc = 0.f;
+      // readout y_t = M_mem,b v_t with v_t = q_t (Eq. 16, boundary) or v_t = G_{t-1} q_t
+      // (running: M_mem,b G_{t-1} is the memory after the chunk's earlier tokens),
+      // written at the token's pixel
+      auto readout = [&](const float* vbase, int vstride) {
+        for (int e = tid; e < nt * D; e += kThreads) {
+          const int t = e / D, i = e % D;
+          const float* mrow = &S[i * SP];
+          const float* qv = vbase + t * vstride;
+          float acc = 0.f;
 #pragma unroll 16
-        for (int j = 0; j < D; ++j) acc = fmaf(mrow[j], qv[j], acc);
-        const int pix = route_pixel(r, tb + t, H, W, N);
-        dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + i] = acc;
-      }
+          for (int j = 0; j < D; ++j) acc = fmaf(mrow[j], qv[j], acc);
+          const int pix = route_pixel(r, tb + t, H, W, N);
+          dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + i] = acc;
+        }
+      };
+      if (!running) readout(&P[2 * D], PS);
       // shared gain, token by token (Eq. 46)
       for (int t = 0; t < nt; ++t) {
         const float* pt = &P[t * PS];
-        float w = 0.f;
+        float w = 0.f, wq = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) w = fmaf(g[c], pt[gcol0 + c], w);
+        for (int c = 0; c < CPT; ++c) {
+          w = fmaf(g[c], pt[gcol0 + c], w);
+          if (running) wq = fmaf(g[c], pt[2 * D + gcol0 + c], wq);
+        }
 #pragma unroll
-        for (int off = TPR / 2; off >= 1; off >>= 1) w += __shfl_xor(w, off, 64);
+        for (int off = TPR / 2; off >= 1; off >>= 1) {
+          w += __shfl_xor(w, off, 64);
+          if (running) wq += __shfl_xor(wq, off, 64);
+        }
+        if (running && tid % TPR == 0) Wq[t * SP + grow] = wq;
         const float step = pt[3 * D], alpha = pt[3 * D + 1];
         const float u = -step * (w + pt[D + grow]);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) g[c] = fmaf(alpha, g[c], u * pt[gcol0 + c]);
       }
       __syncthreads();
+      if (running) {
+        readout(Wq, SP);
+        __syncthreads();
+      }
     }
     // carry: S <- S_b G_C for all six memories at once
 #pragma unroll

@@ -116,7 +116,7 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // NW waves per chain: 4 for d = 32, 8 for d = 64 (at most three state-row tiles per wave,
 // so two waves fit on a SIMD).  Gates use waves 0-3 (16 lanes per token); with eight
 // waves the solve coefficients run on waves 4-7 while waves 0-3 read out.
-template <int D, bool MULTI, int NW, bool KEEP_SPLIT>
+template <int D, bool MULTI, int NW, bool KEEP_SPLIT, bool RUN>
 __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
@@ -149,6 +149,10 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   __shared__ __attribute__((aligned(16))) float stp[kSB];
   __shared__ float cprev[kSB], bco[kSB + 1];  // block retention products
   __shared__ __attribute__((aligned(16))) float Tis[64 * 4];  // block inverse (transposed)
+  // running readout: the masked token matrix A^T and the unscaled write vectors U
+  __shared__ __attribute__((aligned(16))) float Ais[RUN ? 64 * 4 : 4];
+  __shared__ __attribute__((aligned(16))) unsigned short UuH[RUN ? kSB * XLD : 4];
+  __shared__ __attribute__((aligned(16))) unsigned short UuL[RUN ? kSB * XLD : 4];
   // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
   // number of register tiles: Tb[cur] is the chunk-start copy, Tb[cur ^ 1] the update
   __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
@@ -377,7 +381,11 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       }
       lds_barrier();
 
-      // C1: readout y_t = M_mem,b q_t on the waves that own M_mem tiles
+      // C1: readout y_t = M_mem,b q_t on the waves that own M_mem tiles.  The running
+      // readout keeps R = Q (M_mem,b G_s)^T (G_s: the chunk gain before this block) and the
+      // token pixels in registers and completes y in D, once the block's U is known.
+      f32x4 rq = {0.f, 0.f, 0.f, 0.f};
+      int rpix[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi) {
         const int m = w + kWaves * mi;
@@ -390,13 +398,23 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           bf16x8 ah, al;
           split8(q0, q1, ah, al);
           bf16x8 sh, sl;
-          state_split(mi, s, sh, sl);
+          if (RUN && MULTI) {  // the running state of the chunk so far
+            split8(Acc[MULTI ? mi : 0][MULTI ? 2 * s : 0], Acc[MULTI ? mi : 0][MULTI ? 2 * s + 1 : 0], sh, sl);
+          } else {
+            state_split(mi, s, sh, sl);
+          }
           acc = mma32x3(ah, al, sh, sl, acc);
         }
+        if (RUN) {
+          rq = acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * g + i;
-          if (t < nt) dst[((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+          for (int i = 0; i < 4; ++i) rpix[i] = pixs[4 * g + i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            if (t < nt) dst[((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+          }
         }
       }
       // C2: the block's write vectors.
@@ -434,8 +452,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
             if (lane == kSB - 1) bco[kSB] = pre * a_self;
           }
         }
-        // token Gram matrix, gr[i] = k_{4g+i} . k_{c16}
-        f32x4 gr = zero4;
+        // token Gram matrix, gr[i] = k_{4g+i} . k_{c16} (and, for the running readout,
+        // aq[i] = k_{4g+i} . q_{c16})
+        f32x4 gr = zero4, aq = zero4;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           f32x4 k0, k1;
@@ -443,6 +462,20 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           bf16x8 kh, kl;
           split8(k0, k1, kh, kl);
           gr = mma32x3(kh, kl, kh, kl, gr);
+          if (RUN) {
+            f32x4 q0, q1;
+            load_row_pair(Qs + c16 * LD, s, g, q0, q1);
+            bf16x8 qh, ql;
+            split8(q0, q1, qh, ql);
+            aq = mma32x3(kh, kl, qh, ql, aq);
+          }
+        }
+        if (RUN) {
+          // A^T[j][t] = P(j+1, t) (k_j . q_t) for j < t, in the accumulator layout
+          f32x4 at;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) at[i] = 4 * g + i < c16 ? pc[i] * aq[i] : 0.f;
+          *reinterpret_cast<f32x4*>(Ais + 4 * lane) = at;
         }
         f32x4 L1, L1T;
 #pragma unroll
@@ -508,6 +541,11 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           const __bf16 uh = (__bf16)ub;
           UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
           UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
+          if (RUN) {
+            const __bf16 vh = (__bf16)u[i];
+            UuH[t * XLD + col] = __builtin_bit_cast(unsigned short, vh);
+            UuL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(u[i] - (float)vh));
+          }
         }
       }
       lds_barrier();
@@ -535,6 +573,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         }
         // all Z tiles first, so the state split dies before the updates start
         bf16x4 zh[MTW], zl[MTW];
+        f32x4 zu = {0.f, 0.f, 0.f, 0.f};  // running readout: (M_mem,b u_t) for this tile
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -543,8 +582,27 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
             bf16x8 sh, sl;
             state_split(mi, s, sh, sl);
             z = mma32x3(uh[s], ul[s], sh, sl, z);
+            if (RUN && mi == 0 && w < NT) {
+              const unsigned short* hr = UuH + c16 * XLD + 32 * s + 4 * g;
+              const unsigned short* lr = UuL + c16 * XLD + 32 * s + 4 * g;
+              const u32x2 h0 = *reinterpret_cast<const u32x2*>(hr), h1 = *reinterpret_cast<const u32x2*>(hr + 16);
+              const u32x2 l0 = *reinterpret_cast<const u32x2*>(lr), l1 = *reinterpret_cast<const u32x2*>(lr + 16);
+              const u32x4 hv = {h0[0], h0[1], h1[0], h1[1]}, lv = {l0[0], l0[1], l1[0], l1[1]};
+              zu = mma32x3(__builtin_bit_cast(bf16x8, hv), __builtin_bit_cast(bf16x8, lv), sh, sl, zu);
+            }
           }
           split4(z, zh[mi], zl[mi]);
+        }
+        if (RUN && w < NT) {
+          // y_t = P(0,t) (M_mem,b G_s q_t) + sum_{j<t} P(j+1,t) (k_j . q_t) (M_mem,b u_j)
+          const f32x4 at = *reinterpret_cast<const f32x4*>(Ais + 4 * lane);
+          const f32x4 y = mm16(at, zu);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            if (t < nt)
+              dst[((int64_t)b * N + rpix[i]) * Dt + (int64_t)h * D + w * 16 + c16] = cprev[t] * rq[i] + y[i];
+          }
         }
         // gate rows: every readout wave forms their Z tile and updates column tile w
         bf16x4 tzh, tzl;
@@ -666,9 +724,15 @@ hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
   dim3 grid((unsigned)blocks);
   if (d == 32) {
-    hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32>), grid, dim3(256), 0, stream, p);
+    if (p.readout)
+      hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32, false>), grid, dim3(256), 0, stream, p);
   } else if (d == 64) {
-    hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64>), grid, dim3(512), 0, stream, p);
+    if (p.readout)
+      hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64, false>), grid, dim3(512), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

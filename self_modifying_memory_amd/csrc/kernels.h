@@ -23,6 +23,8 @@ struct ChainParams {
   int init_per_image;
   int eta_map;            // 0 sigmoid, 1 softplus
   float eta_scale, alpha_bias, eps;
+  int readout;            // 0 boundary (chunk-start memory), 1 running (memory after the
+                          // chunk's earlier tokens)
 };
 
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
@@ -32,10 +34,10 @@ hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
 bool mfma_path_supported(const ChainParams& p, int d);
 hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream);
 
-// out[i] += planes[0][i] + ... + planes[n-1][i], left to right, fp32 (route sum).
 // out = bf16(planes[0] + planes[1] + ...) in that order, rounded once to nearest even
 hipError_t launch_plane_sum_bf16(unsigned short* out, const float* planes, int64_t plane_stride,
                                  int n_planes, int64_t n_elem, hipStream_t stream);
+// out[i] += planes[0][i] + ... + planes[n-1][i], left to right, fp32 (route sum).
 hipError_t launch_plane_sum(float* out, const float* planes, int64_t plane_stride, int n_planes,
                             int64_t n_elem, hipStream_t stream);
 

@@ -13,6 +13,7 @@ import torch
 from . import _native as N
 
 _ETA_MAPS = {"sigmoid": N.HOPE_ETA_SIGMOID, "softplus": N.HOPE_ETA_SOFTPLUS}
+_READOUTS = {"boundary": N.HOPE_READOUT_BOUNDARY, "running": N.HOPE_READOUT_RUNNING}
 
 
 class HopeError(RuntimeError):
@@ -55,7 +56,8 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
               alpha_bias: float = 4.0, eps: float = 1e-6, init_per_image: bool = False,
               final_memories: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None,
-              out_dtype: torch.dtype = torch.float32) -> N.hope_scan2d_opts_t:
+              out_dtype: torch.dtype = torch.float32,
+              readout: str = "boundary") -> N.hope_scan2d_opts_t:
     lib = N.load_library()
     o = N.hope_scan2d_opts_t()
     lib.hope_scan2d_default_opts(ctypes.byref(o))
@@ -66,6 +68,7 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
     o.eps = eps
     o.init_per_image = int(bool(init_per_image))
     o.out_dtype = N.HOPE_BF16 if out_dtype == torch.bfloat16 else N.HOPE_F32
+    o.readout = _READOUTS[readout]
     if final_memories is not None:
         _require_device(final_memories, "final_memories")
         if final_memories.dtype != torch.float32:
@@ -103,12 +106,15 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         eps: float = 1e-6, init_per_image: bool = False,
                         final_memories: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None,
-                        scan_events: tuple | None = None) -> torch.Tensor:
+                        scan_events: tuple | None = None,
+                        readout: str = "boundary") -> torch.Tensor:
     """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32, or bfloat16
     when a bfloat16 ``out`` is passed: the fp32 route sum rounded once).
 
     init_memories: float32 [4, n_heads, 4d^2+2d] (or [B, 4, n_heads, ...] with
     init_per_image).  A workspace is allocated through torch when none is given.
+    readout: "boundary" (memory frozen at the chunk start) or "running" (memory after
+    the chunk's earlier tokens).
     scan_events: optional (begin, end) torch.cuda.Event pair that the library records
     around the scan kernel alone (already recorded once, so that they exist).
     """
@@ -126,7 +132,7 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
         workspace = alloc_workspace(x, n_heads, dirs, chunk, out.dtype)
     fm = make_fmap(x, n_heads)
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
-                     workspace, out.dtype)
+                     workspace, out.dtype, readout)
     if scan_events is not None:
         begin, end = scan_events
         if not begin.cuda_event or not end.cuda_event:

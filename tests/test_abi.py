@@ -53,13 +53,14 @@ def test_struct_layout_matches_c():
 #include <stddef.h>
 #include "hope_scan2d.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
          offsetof(hope_fmap_t, dtype), offsetof(hope_fmap_t, n_heads),
          offsetof(hope_scan2d_opts_t, final_memories), offsetof(hope_scan2d_opts_t, workspace_bytes),
          offsetof(hope_scan2d_opts_t, eta_map), offsetof(hope_scan2d_opts_t, eta_scale),
          offsetof(hope_scan2d_opts_t, eps), offsetof(hope_scan2d_opts_t, init_per_image),
          offsetof(hope_scan2d_opts_t, out_dtype), offsetof(hope_scan2d_opts_t, scan_begin),
-         offsetof(hope_scan2d_opts_t, scan_end));
+         offsetof(hope_scan2d_opts_t, scan_end), offsetof(hope_scan2d_opts_t, readout),
+         offsetof(hope_scan2d_opts_t, reserved));
   return 0;
 }
 """
@@ -77,7 +78,7 @@ int main(void) {
     want = [ctypes.sizeof(F), ctypes.sizeof(O), F.dtype.offset, F.n_heads.offset,
             O.final_memories.offset, O.workspace_bytes.offset, O.eta_map.offset, O.eta_scale.offset,
             O.eps.offset, O.init_per_image.offset, O.out_dtype.offset, O.scan_begin.offset,
-            O.scan_end.offset]
+            O.scan_end.offset, O.readout.offset, O.reserved.offset]
     assert vals == want
 
 
@@ -85,7 +86,7 @@ def test_default_opts_and_status_strings(lib):
     o = opts(lib)
     assert (o.eta_map, o.eta_scale, o.alpha_bias, o.init_per_image) == (0, 1.0, 4.0, 0)
     assert abs(o.eps - 1e-6) < 1e-12 and o.final_memories is None and o.workspace is None
-    assert o.scan_begin is None and o.scan_end is None
+    assert o.scan_begin is None and o.scan_end is None and o.readout == N.HOPE_READOUT_BOUNDARY
     for code, name in [(0, b"HOPE_OK"), (-1, b"HOPE_ERR_INVALID_ARG"), (-2, b"HOPE_ERR_UNSUPPORTED"),
                        (-3, b"HOPE_ERR_WORKSPACE"), (-4, b"HOPE_ERR_HIP")]:
         assert lib.hope_status_string(code) == name
@@ -136,7 +137,8 @@ def test_argument_errors(lib):
     assert call(lib, x, out=FAKE + (1 << 30), o=o) == N.HOPE_ERR_INVALID_ARG
     for k, v in [("eta_map", 2), ("eta_scale", -1.0), ("eta_scale", float("nan")),
                  ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("out_dtype", 2),
-                 ("scan_begin", FAKE), ("scan_end", FAKE)]:  # the event pair is both or neither
+                 ("scan_begin", FAKE), ("scan_end", FAKE),  # the event pair is both or neither
+                 ("readout", 2), ("reserved", 1)]:
         assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k
     # final memories overlapping out, misaligned workspace
     assert call(lib, x, o=opts(lib, final_memories=FAKE + (2 << 30))) == N.HOPE_ERR_INVALID_ARG

@@ -166,3 +166,57 @@ def test_hires_long_memory_stress_sampled():
     e_out = check_out(out, ref_out, w.n_heads, TOL[w.dtype], heads=[1], images=[0])
     e_fin = check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=[1], images=[0])
     print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+# Running-state readout (y_t = M_mem,b G_{t-1} q_t) against the oracle's readout="running".
+RUNNING = [
+    # B, H, W, D, nh, dtype, dirs, chunk, extra
+    (1, 8, 8, 16, 1, "f32", 15, 0, {}),            # fp32 kernel, d = 16
+    (2, 3, 20, 48, 3, "f32", 15, 0, {}),           # fp32 kernel, row chunks of 20 (two blocks)
+    (1, 6, 9, 64, 1, "f32", 15, 4, {}),            # fp32 kernel, d = 64, ragged chunks
+    (2, 5, 7, 64, 2, "bf16", 15, 0, {}),           # MFMA d = 32, one block per chunk
+    (2, 5, 37, 96, 3, "bf16", 15, 0, {}),          # MFMA d = 32, chunks of 37: three blocks
+    (2, 6, 9, 128, 2, "bf16", 15, 0, {}),          # MFMA d = 64
+    (1, 16, 16, 64, 1, "bf16", 15, 0, {}),         # MFMA d = 64, chunks of exactly 16
+    (1, 20, 3, 64, 1, "bf16", 15, 0, {}),          # d = 64, column chunks of 20: fp32 kernel
+    (1, 5, 5, 32, 1, "bf16", 15, 0, dict(eta_scale=50.0, alpha_bias=-3.0)),  # clamps active
+    (2, 5, 6, 64, 1, "bf16", 15, 0,
+     dict(eta_map="softplus", eta_scale=0.025, alpha_bias=math.log(9.0))),
+]
+
+
+@pytest.mark.parametrize("case", RUNNING, ids=[_case_id(c[:8] + (True, c[8])) for c in RUNNING])
+def test_running_readout_matches_oracle(case):
+    B, H, W, D, nh, dt, dirs, chunk, extra = case
+    print("case", case, flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=7000 + B * 100 + H * 37 + W, dtype=dt, live=True)
+    out, fin = run_gpu(inp, nh, dt, dirs, chunk, readout="running", **extra)
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], nh, dirs=dirs, chunk=chunk,
+                                     readout="running", **extra)
+    e_out = check_out(out, ref_out, nh, TOL[dt])
+    e_fin = check_final(fin, ref_fin, D // nh, dirs, TOL[dt])
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("shape", [(1, 5, 6, 32, 1, "f32"), (2, 5, 7, 64, 2, "bf16"),
+                                   (1, 6, 6, 128, 2, "bf16")])
+def test_running_readout_is_boundary_at_chunk_one(shape):
+    B, H, W, D, nh, dt = shape
+    print("shape", shape, flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=77, dtype=dt, live=True)
+    ob, fb = run_gpu(inp, nh, dt, 15, 1)
+    orun, frun = run_gpu(inp, nh, dt, 15, 1, readout="running")
+    assert np.array_equal(ob, orun) and np.array_equal(fb, frun)
+
+
+def test_running_readout_full_size_stage3_sampled():
+    w = wl.WORKLOADS[3]
+    images, heads = [0, 127], [0, 5]
+    print(f"workload {w.name} running readout: images {images} heads {heads}", flush=True)
+    inp = wl.draw_workload(w, live=True)
+    out, fin = run_gpu(inp, w.n_heads, w.dtype, readout="running")
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, heads=heads, images=images,
+                                     readout="running")
+    e_out = check_out(out, ref_out, w.n_heads, TOL[w.dtype], heads=heads, images=images)
+    e_fin = check_final(fin, ref_fin, w.d, 15, TOL[w.dtype], heads=heads, images=images)
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
