@@ -50,19 +50,24 @@ KERNEL_SOURCES = ["chain_mfma.hip", "device_common.h", "kernels.h"]
 METRIC = wl_metric = "scan tokens/s (positions×dirs) for 4-dir Hope memory scan; % MFMA/HBM peak"
 
 
-def work_per_token(d: int, C: int) -> tuple[float, float]:
-    """(bf16-class MACs, fp32-class MACs) per (token, head, route)."""
+def work_per_token(d: int, C: int, readout: str = "boundary") -> tuple[float, float]:
+    """(bf16-class MACs, fp32-class MACs) per (token, head, route).
+
+    The running readout adds, per token, one d x d product of the chunk-start M_mem with
+    a write vector (or of G_{t-1} with q_t) and a causal C-long weighting: d^2 + C d / 2.
+    """
     bf16 = 4 * d * d + 2 * d
     f1 = 3 * d * d + (4 * d ** 3 + 2 * d * d) / C
     f2 = C * d + C * C / 6 + d * d + (4 * d ** 3 + 2 * d * d) / C
     f3 = C * d + C * C / 6 + 8 * d * d + 4 * d
-    return float(bf16), float(min(f1, f2, f3))
+    extra = d * d + C * d / 2 if readout == "running" else 0.0
+    return float(bf16), float(min(f1, f2, f3) + extra)
 
 
-def roofline_numbers(w: wl.Workload, n_dirs: int = 4) -> dict:
+def roofline_numbers(w: wl.Workload, n_dirs: int = 4, readout: str = "boundary") -> dict:
     d = w.d
     C = w.W  # square maps: row and column chunks are equal
-    bf16, fp32 = work_per_token(d, C)
+    bf16, fp32 = work_per_token(d, C, readout)
     units = w.scan_tokens(n_dirs) * w.n_heads
     f_bf16 = 2 * bf16 * units
     f_fp32 = 2 * fp32 * units
@@ -97,19 +102,19 @@ def recorded_traffic(w: wl.Workload):
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 12.0) -> dict:
+def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str = "boundary") -> dict:
     """Time the fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
     from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
         images = [0]
         t0 = time.perf_counter()
-        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images)
+        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images, readout=readout)
         t1 = time.perf_counter() - t0
         n_img = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
         images = list(range(n_img))
         t0 = time.perf_counter()
-        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images)
+        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images, readout=readout)
         dt = time.perf_counter() - t0
     toks = n_img * w.H * w.W * 4
     return {"value": toks / dt, "unit": "scan tokens/s", "cores": 1, "kind": "oracle",
@@ -125,6 +130,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--readout", choices=["boundary", "running"], default="boundary",
+                    help="readout memory inside a chunk (the default is the chunk-start one)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -164,7 +171,7 @@ def main() -> int:
     def step(i, ev=None):
         x, out, ws = sets[i % len(sets)]
         hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream,
-                            scan_events=ev)
+                            scan_events=ev, readout=args.readout)
 
     for i in range(args.warmup):
         step(i)
@@ -190,7 +197,7 @@ def main() -> int:
         torch.cuda.synchronize()
 
     tokens = w.scan_tokens(4)
-    roof = roofline_numbers(w)
+    roof = roofline_numbers(w, readout=args.readout)
     achieved = roof["flops"] / k_avg
     peak = roof["flops"] / roof["t_compute"]
     rec = {
@@ -208,9 +215,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
-                   "state_dtype": "f32"},
+                   "state_dtype": "f32", "readout": args.readout},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": recorded_traffic(w),
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": recorded_traffic(w) if args.readout == "boundary" else None,
                      "kernel": "chain_mfma_kernel", "kernel_ms": k_avg * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)),
                                            float(np.percentile(kernel_ms, 90))],
@@ -219,7 +227,7 @@ def main() -> int:
                      "hbm_frac": roof["hbm_bytes"] / k_avg / PEAK_HBM},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, inp)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, readout=args.readout)
     print(json.dumps(rec), flush=True)
     return 0
 
