@@ -149,10 +149,53 @@ def spectral_limit(alpha, k, inward: float = SPEC_INWARD, floor: float = KAPPA_F
     return np.nextafter(lim, dtype(0)).astype(np.float64)
 
 
-def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS):
-    """eta_tilde = min(eta_bar, eta_spec) ([VH] Eq. 20)."""
-    eta_bar, _ = soft_injection_cap(eta, alpha, delta, eps)
-    return np.minimum(eta_bar, spectral_limit(alpha, k))
+def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS, injection: str = "soft",
+                  spectral: str = "clamp", counts: dict | None = None):
+    """eta_tilde = min(eta_bar, eta_spec) ([VH] Eq. 20), or one of the ablation controls of
+    [VH] Sec. 3.5:
+
+      injection = "soft"  the soft injection cap of Eq. 19 (default);
+                  "hard"  a hard clamp at the same injection limit, min(eta, eta_inj);
+                  "none"  no injection control, eta_bar = eta;
+      spectral  = "clamp" min(eta_bar, eta_spec) (default);
+                  "soft"  a smooth map to the same spectral limit, taken as the saturating
+                          map of Eq. 19 with eta_spec in place of eta_inj:
+                          eta_spec (1 - exp(-eta_bar / eta_spec));
+                  "none"  no spectral control, eta_tilde = eta_bar.
+
+    counts (optional) accumulates, over live tokens: "updates"; "inj", tokens whose raw eta
+    exceeds the injection limit (where a hard clamp binds); "spec", tokens whose eta_bar
+    exceeds the spectral limit (where the clamp binds); and "inj_near" / "spec_near",
+    tokens within a relative 1e-5 of either boundary.
+    """
+    eta = np.asarray(eta, dtype=np.float64)
+    eta_soft, eta_inj = soft_injection_cap(eta, alpha, delta, eps)
+    if injection == "soft":
+        eta_bar = eta_soft
+    elif injection == "hard":
+        eta_bar = np.minimum(eta, eta_inj)
+    elif injection == "none":
+        eta_bar = eta
+    else:
+        raise ValueError(injection)
+    lim = spectral_limit(alpha, k)
+    if spectral == "clamp":
+        step = np.minimum(eta_bar, lim)
+    elif spectral == "soft":
+        ok = (eta_bar != 0.0) & (lim != 0.0)
+        safe = np.where(ok, lim, 1.0)
+        step = np.where(ok, safe * -np.expm1(-eta_bar / safe), 0.0)
+    elif spectral == "none":
+        step = eta_bar
+    else:
+        raise ValueError(spectral)
+    if counts is not None:
+        counts["updates"] = counts.get("updates", 0) + int(eta.size)
+        counts["inj"] = counts.get("inj", 0) + int(np.sum(eta > eta_inj))
+        counts["spec"] = counts.get("spec", 0) + int(np.sum(eta_bar > lim))
+        counts["inj_near"] = counts.get("inj_near", 0) + int(np.sum(np.abs(eta - eta_inj) <= 1e-5 * np.abs(eta_inj)))
+        counts["spec_near"] = counts.get("spec_near", 0) + int(np.sum(np.abs(eta_bar - lim) <= 1e-5 * np.abs(lim)))
+    return step
 
 
 # --------------------------------------------------------------------------
@@ -161,10 +204,15 @@ def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS):
 # M is [n, rows, d] (a 1 x d row memory has rows = 1); k is [n, d]; g is
 # [n, rows]; alpha, eta are [n].
 # --------------------------------------------------------------------------
-def retained_dgd(M, k, g, eta, alpha):
+def retained_dgd(M, k, g, eta, alpha, dgd: bool = True):
+    """dgd=False is the DGD ablation of [VH] Sec. 3.5: the key-dependent correction
+    -eta M k k^T is removed, M <- alpha M - eta g k^T, keeping the output-space signal,
+    the retention factor and the step control."""
     n, d = k.shape
     eye = np.broadcast_to(np.eye(d), (n, d, d))
-    A = alpha[:, None, None] * eye - eta[:, None, None] * (k[:, :, None] * k[:, None, :])
+    A = alpha[:, None, None] * eye
+    if dgd:
+        A = A - eta[:, None, None] * (k[:, :, None] * k[:, None, :])
     return M @ A - eta[:, None, None] * (g[:, :, None] * k[:, None, :])
 
 
@@ -180,7 +228,9 @@ def _matvec(M, x):
 # --------------------------------------------------------------------------
 def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid",
                eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
-               control: bool = True, log: list | None = None, readout: str = "boundary"):
+               control: bool = True, log: list | None = None, readout: str = "boundary",
+               injection: str = "soft", spectral: str = "clamp", frozen=(), dgd: bool = True,
+               counts: dict | None = None):
     """Run chains over ordered tokens.
 
     xs    : [n, N, d] tokens in route order
@@ -193,8 +243,15 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
     by the chunk's earlier tokens ([NL] Eq. 94, y_t = M_memory,t-1 q_t, applied inside
     the chunk; the projections still come from the chunk-start memories).  Both
     agree when every chunk is one token.
+    injection / spectral select the step controls (see executed_step); frozen names the
+    memories held fixed within the image ([VH] Sec. 3.5: without adaptive K/V, frozen =
+    ("k", "v"); without adaptive dynamics, ("eta", "alpha")); dgd=False removes the
+    key-dependent correction of the update (retained_dgd).
     Returns (ys [n, N, d], final state dict).
     """
+    for m in frozen:
+        if m not in MEMORIES:
+            raise ValueError(f"unknown memory {m!r}")
     if readout not in ("boundary", "running"):
         raise ValueError("readout must be 'boundary' or 'running'")
     xs = np.asarray(xs, dtype=np.float64)
@@ -214,21 +271,26 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
             # updated with token t here)
             ys[:, t, :] = _matvec(Mb["mem"] if readout == "boundary" else M["mem"], q)
             delta = k - v
-            step = executed_step(eta, alpha, k, delta, eps) if control else eta
+            step = (executed_step(eta, alpha, k, delta, eps, injection, spectral, counts)
+                    if control else eta)
             if log is not None:
                 log.append({"t": t, "eta": eta, "alpha": alpha, "step": step, "k": k,
                             "delta": delta})
             for m in MEMORIES:
+                if m in frozen:
+                    continue
                 vhat = _matvec(Mb[m], v)                      # self-generated target, Eq. 16
                 g = _matvec(Mb[m], k) - vhat                  # output-space signal, Eq. 16
-                M[m] = retained_dgd(M[m], k, g, step, alpha)  # Eq. 13
+                M[m] = retained_dgd(M[m], k, g, step, alpha, dgd)  # Eq. 13
     return ys, M
 
 
 def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk: int = 0,
            eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
            eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None,
-           readout: str = "boundary"):
+           readout: str = "boundary", injection: str = "soft", spectral: str = "clamp",
+           frozen=(), dgd: bool = True, route_scales=None, skip=None,
+           shared_init: bool = False, counts: dict | None = None):
     """The whole operator: serialise, run every (image, head, route) chain, merge.
 
     x    : [B, H, W, D] (any float dtype; widened to fp64)
@@ -237,6 +299,13 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
            d x d), m_eta, m_alpha.
     heads / images restrict the computation to a subset (sampled checks); the
     returned arrays then cover only those.
+    route_scales [4, D] are the channel-wise direction scales lambda_r of [VH] Eq. 26
+    (None: unit scales); skip [D] is the channel-wise skip of [VH] App. B.5, added to each
+    route's head-wise reads before its scale: Y_r = reads_r + skip * Z_r.
+    shared_init: init is [n_heads, S], the same initial memories for every route (the
+    shared-initial-state variant of [VH] Sec. 3.5; trajectories stay separate).
+    readout, injection, spectral, frozen, dgd: see srnl_chain; counts accumulates the
+    step-control counters of executed_step over every chain computed.
     Returns (out [b, H, W, D_sel] fp64, final [b, 4, h, S] fp64, NaN for
     unselected routes).
     """
@@ -257,10 +326,21 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
             if not (dirs >> r) & 1:
                 continue
             xs = cross_scan(xb[..., h * d:(h + 1) * d], r)
-            flat = init[images, r, h] if init_per_image else np.broadcast_to(init[r, h], (nb, S))
+            if shared_init:
+                flat = np.broadcast_to(init[h], (nb, S))
+            elif init_per_image:
+                flat = init[images, r, h]
+            else:
+                flat = np.broadcast_to(init[r, h], (nb, S))
             st = unflatten_state(flat, d)
             C = route_chunk(H, W, r, chunk)
-            ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout)
+            ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout,
+                                 injection=injection, spectral=spectral, frozen=frozen, dgd=dgd,
+                                 counts=counts)
+            if skip is not None:                      # Y_r = reads + skip * Z_r  ([VH] App. B.5)
+                ys = ys + np.asarray(skip, dtype=np.float64)[h * d:(h + 1) * d] * xs
+            if route_scales is not None:              # lambda_r * Y_r  ([VH] Eq. 26)
+                ys = ys * np.asarray(route_scales, dtype=np.float64)[r, h * d:(h + 1) * d]
             routes[r] = ys
             final[:, r, hi, :] = flatten_state(fin)
         if routes:
