@@ -89,6 +89,18 @@ typedef struct {
  *             BOUNDARY when every chunk is one token. */
 typedef enum { HOPE_READOUT_BOUNDARY = 0, HOPE_READOUT_RUNNING = 1 } hope_readout_t;
 
+/* Step-control variants ("VisionHOPE", Sec. 3.5 ablations).
+ *   INJECTION_SOFT  the soft injection cap of Eq. 19;  HARD  min(eta, eta_inj) at the same
+ *   limit;  NONE  no injection control.
+ *   SPECTRAL_CLAMP  min(eta_bar, eta_spec) of Eq. 20;  SOFT  eta_spec (1 - exp(-eta_bar /
+ *   eta_spec)), a smooth map to the same limit;  NONE  no spectral control. */
+typedef enum { HOPE_INJECTION_SOFT = 0, HOPE_INJECTION_HARD = 1, HOPE_INJECTION_NONE = 2 } hope_injection_t;
+typedef enum { HOPE_SPECTRAL_CLAMP = 0, HOPE_SPECTRAL_SOFT = 1, HOPE_SPECTRAL_NONE = 2 } hope_spectral_t;
+
+/* Memories held fixed within the image (Sec. 3.5: without adaptive K/V, without adaptive
+ * dynamics); the content memory always evolves. */
+typedef enum { HOPE_FREEZE_KV = 1, HOPE_FREEZE_DYNAMICS = 2, HOPE_FREEZE_Q = 4 } hope_freeze_t;
+
 /* Options of hope_scan2d_forward.  Start from hope_scan2d_default_opts(). */
 typedef struct {
   hipStream_t stream;        /* stream to enqueue on; 0 = default stream */
@@ -111,6 +123,25 @@ typedef struct {
                                 the pair times the scan kernel alone.  Both or neither. */
   int32_t readout;           /* hope_readout_t; default HOPE_READOUT_BOUNDARY */
   int32_t reserved;          /* must be 0 */
+  /* Variants of "VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"
+   * (Sec. 2.3 Eq. 26, App. B.5 and the Sec. 3.5 ablations).  Defaults reproduce the
+   * operator above. */
+  const float* route_scales; /* NULL (unit scales), or device [4][D] fp32: the channel-wise
+                                direction scales lambda_r of Eq. 26, indexed by route */
+  const float* skip;         /* NULL, or device [D] fp32: a channel-wise skip added to every
+                                route's reads before its scale, Y_r = reads_r + skip * Z_r */
+  unsigned long long* counts;/* NULL, or device [3] uint64, 8-byte aligned, accumulated (not
+                                cleared): live token updates; tokens whose raw eta exceeds the
+                                injection limit; tokens whose eta_bar exceeds the spectral limit
+                                (decided in fp32) */
+  int32_t injection;         /* hope_injection_t; default HOPE_INJECTION_SOFT */
+  int32_t spectral;          /* hope_spectral_t; default HOPE_SPECTRAL_CLAMP */
+  uint32_t frozen;           /* OR of hope_freeze_t: memories held fixed within the image */
+  int32_t no_dgd;            /* 1: drop the key-dependent correction -eta M k k^T of the
+                                update (the DGD ablation), keeping signal, retention and step */
+  int32_t shared_init;       /* 1: init_memories is [n_heads][S], shared by all routes (the
+                                trajectories stay separate); excludes init_per_image */
+  int32_t reserved2;         /* must be 0 */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

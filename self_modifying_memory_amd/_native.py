@@ -25,6 +25,9 @@ HOPE_ETA_SIGMOID = 0
 HOPE_ETA_SOFTPLUS = 1
 HOPE_READOUT_BOUNDARY = 0
 HOPE_READOUT_RUNNING = 1
+HOPE_INJECTION = {"soft": 0, "hard": 1, "none": 2}
+HOPE_SPECTRAL = {"clamp": 0, "soft": 1, "none": 2}
+HOPE_FREEZE = {"kv": 1, "dynamics": 2, "q": 4}
 HOPE_DIR_ALL = 15
 
 
@@ -41,7 +44,12 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("alpha_bias", ctypes.c_float), ("eps", ctypes.c_float),
                 ("init_per_image", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("scan_begin", ctypes.c_void_p), ("scan_end", ctypes.c_void_p),
-                ("readout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("readout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("route_scales", ctypes.c_void_p), ("skip", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("injection", ctypes.c_int32),
+                ("spectral", ctypes.c_int32), ("frozen", ctypes.c_uint32),
+                ("no_dgd", ctypes.c_int32), ("shared_init", ctypes.c_int32),
+                ("reserved2", ctypes.c_int32)]
 
 
 _lib = None

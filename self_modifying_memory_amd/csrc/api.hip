@@ -64,7 +64,16 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if ((o->scan_begin == nullptr) != (o->scan_end == nullptr)) return HOPE_ERR_INVALID_ARG;
   if (o->readout != HOPE_READOUT_BOUNDARY && o->readout != HOPE_READOUT_RUNNING)
     return HOPE_ERR_INVALID_ARG;
-  if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->reserved != 0 || o->reserved2 != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->injection < HOPE_INJECTION_SOFT || o->injection > HOPE_INJECTION_NONE) return HOPE_ERR_INVALID_ARG;
+  if (o->spectral < HOPE_SPECTRAL_CLAMP || o->spectral > HOPE_SPECTRAL_NONE) return HOPE_ERR_INVALID_ARG;
+  if (o->frozen & ~7u) return HOPE_ERR_INVALID_ARG;
+  if (o->no_dgd != 0 && o->no_dgd != 1) return HOPE_ERR_INVALID_ARG;
+  if (o->shared_init != 0 && o->shared_init != 1) return HOPE_ERR_INVALID_ARG;
+  if (o->shared_init && o->init_per_image) return HOPE_ERR_INVALID_ARG;
+  if (o->route_scales && !aligned(o->route_scales, 4)) return HOPE_ERR_INVALID_ARG;
+  if (o->skip && !aligned(o->skip, 4)) return HOPE_ERR_INVALID_ARG;
+  if (o->counts && !aligned(o->counts, 8)) return HOPE_ERR_INVALID_ARG;
   if (o->final_memories && !aligned(o->final_memories, 16)) return HOPE_ERR_INVALID_ARG;
   if (o->workspace && !aligned(o->workspace, 256)) return HOPE_ERR_INVALID_ARG;
   return HOPE_OK;
@@ -131,14 +140,25 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   const bool out_bf16 = o.out_dtype == HOPE_BF16;
   const size_t out_bytes = (size_t)n_elem * (out_bf16 ? 2 : 4);
   const size_t state_floats = (size_t)4 * d * d + 2 * (size_t)d;
-  const size_t init_bytes =
-      (o.init_per_image ? (size_t)x->B : 1) * 4 * (size_t)x->n_heads * state_floats * sizeof(float);
+  const size_t init_bytes = (o.init_per_image ? (size_t)x->B : 1) * (o.shared_init ? 1 : 4) *
+                            (size_t)x->n_heads * state_floats * sizeof(float);
   const size_t final_bytes = (size_t)x->B * 4 * x->n_heads * state_floats * sizeof(float);
   const size_t ws_need = workspace_bytes_for(x, dirs, o.out_dtype);
 
   const Range r_out = range_of(out, out_bytes);
   if (overlaps(r_out, range_of(x->data, x_bytes))) return HOPE_ERR_INVALID_ARG;
   if (overlaps(r_out, range_of(init_memories, init_bytes))) return HOPE_ERR_INVALID_ARG;
+  if (o.route_scales && overlaps(r_out, range_of(o.route_scales, 4 * (size_t)x->D * sizeof(float))))
+    return HOPE_ERR_INVALID_ARG;
+  if (o.skip && overlaps(r_out, range_of(o.skip, (size_t)x->D * sizeof(float)))) return HOPE_ERR_INVALID_ARG;
+  if (o.counts) {
+    const Range r_cnt = range_of(o.counts, 3 * sizeof(unsigned long long));
+    if (overlaps(r_out, r_cnt) || overlaps(r_cnt, range_of(x->data, x_bytes)) ||
+        overlaps(r_cnt, range_of(init_memories, init_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+    if (o.workspace && o.workspace_bytes && overlaps(r_cnt, range_of(o.workspace, o.workspace_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+  }
   if (o.final_memories) {
     const Range r_fin = range_of(o.final_memories, final_bytes);
     if (overlaps(r_out, r_fin) || overlaps(r_fin, range_of(x->data, x_bytes)) ||
@@ -183,6 +203,14 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   p.alpha_bias = o.alpha_bias;
   p.eps = o.eps;
   p.readout = o.readout;
+  p.route_scales = o.route_scales;
+  p.skip = o.skip;
+  p.counts = o.counts;
+  p.injection = o.injection;
+  p.spectral = o.spectral;
+  p.frozen = o.frozen;
+  p.no_dgd = o.no_dgd;
+  p.shared_init = o.shared_init;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;

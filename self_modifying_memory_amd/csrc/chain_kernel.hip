@@ -60,13 +60,18 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   const int64_t SS = 4 * D * D + 2 * D;
 
   float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
-  const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h
-                                                 : (int64_t)r * nh + h) * SS;
+  const float* init = p.init + init_offset(p, b, r, h, SS);
   for (int e = tid; e < R * D; e += kThreads) S[(e / D) * SP + e % D] = init[e];
 
   const int grow = tid / TPR;         // gain row owned by this thread
   const int gcol0 = (tid % TPR) * CPT;
-  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps};
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, p.injection, p.spectral};
+  unsigned long long n_upd = 0, n_inj = 0, n_spec = 0;  // step-control counters (lane 0)
+  // rows held fixed within the image: M_k, M_v (bit 0), the gate rows (bit 1), M_q (bit 2)
+  auto frozen_row = [&](int row) {
+    return ((p.frozen & 1u) && row >= D && row < 3 * D) || ((p.frozen & 4u) && row >= 3 * D && row < 4 * D) ||
+           ((p.frozen & 2u) && row >= 4 * D);
+  };
   __syncthreads();
 
   for (int s0 = 0; s0 < N; s0 += C) {
@@ -111,12 +116,16 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         if (lane == 0) {
           pt[3 * D] = step;
           pt[3 * D + 1] = alpha;
+          n_upd += 1;
+          n_inj += tg.flags & 1;
+          n_spec += (tg.flags >> 1) & 1;
         }
       }
       __syncthreads();
       // readout y_t = M_mem,b v_t with v_t = q_t (Eq. 16, boundary) or v_t = G_{t-1} q_t
       // (running: M_mem,b G_{t-1} is the memory after the chunk's earlier tokens),
       // written at the token's pixel
+      // then the channel-wise skip and direction scale: (y + skip x) lambda_r
       auto readout = [&](const float* vbase, int vstride) {
         for (int e = tid; e < nt * D; e += kThreads) {
           const int t = e / D, i = e % D;
@@ -125,8 +134,11 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
           float acc = 0.f;
 #pragma unroll 16
           for (int j = 0; j < D; ++j) acc = fmaf(mrow[j], qv[j], acc);
+          const int64_t c = (int64_t)h * D + i;
+          if (p.skip) acc = fmaf(p.skip[c], X[t * SP + i], acc);
+          if (p.route_scales) acc *= p.route_scales[(int64_t)r * Dt + c];
           const int pix = route_pixel(r, tb + t, H, W, N);
-          dst[((int64_t)b * N + pix) * Dt + (int64_t)h * D + i] = acc;
+          dst[((int64_t)b * N + pix) * Dt + c] = acc;
         }
       };
       if (!running) readout(&P[2 * D], PS);
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         }
         if (running && tid % TPR == 0) Wq[t * SP + grow] = wq;
         const float step = pt[3 * D], alpha = pt[3 * D + 1];
-        const float u = -step * (w + pt[D + grow]);
+        const float u = -step * (p.no_dgd ? pt[D + grow] : w + pt[D + grow]);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) g[c] = fmaf(alpha, g[c], u * pt[gcol0 + c]);
       }
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
 #pragma unroll
         for (int k = 0; k < kRB; ++k) {
           const int row = r0 + grp + k * NG;
-          if (row < R) S[row * SP + col] = acc[k];
+          if (row < R && !frozen_row(row)) S[row * SP + col] = acc[k];
         }
       }
     }
@@ -196,6 +208,11 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   if (p.final_mem) {
     float* fin = p.final_mem + (((int64_t)b * 4 + r) * nh + h) * SS;
     for (int e = tid; e < R * D; e += kThreads) fin[e] = S[(e / D) * SP + e % D];
+  }
+  if (p.counts && lane == 0) {
+    atomicAdd(&p.counts[0], n_upd);
+    atomicAdd(&p.counts[1], n_inj);
+    atomicAdd(&p.counts[2], n_spec);
   }
 
 }

@@ -116,7 +116,7 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // NW waves per chain: 4 for d = 32, 8 for d = 64 (at most three state-row tiles per wave,
 // so two waves fit on a SIMD).  Gates use waves 0-3 (16 lanes per token); with eight
 // waves the solve coefficients run on waves 4-7 while waves 0-3 read out.
-template <int D, bool MULTI, int NW, bool KEEP_SPLIT, bool RUN>
+template <int D, bool MULTI, int NW, bool KEEP_SPLIT, bool RUN, bool VAR>
 __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
@@ -156,6 +156,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
   // number of register tiles: Tb[cur] is the chunk-start copy, Tb[cur ^ 1] the update
   __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
+  __shared__ unsigned int cnt_lds[3];  // step-control counters of this chain
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -168,7 +169,29 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   const int H = p.H, W = p.W, N = H * W, Dt = p.D;
   const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
   const int64_t SS = 4 * D * D + 2 * D;
-  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps};
+  // variants (compiled only into the VAR instantiations; the others see the defaults)
+  const float* const v_skip = VAR ? p.skip : nullptr;
+  const float* const v_scales = VAR ? p.route_scales : nullptr;
+  unsigned long long* const v_counts = VAR ? p.counts : nullptr;
+  const unsigned v_frozen = VAR ? p.frozen : 0u;
+  const bool v_nodgd = VAR && p.no_dgd;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR ? p.injection : 0,
+                      VAR ? p.spectral : 0};
+  // register tiles held fixed within the image: M_k, M_v (bit 0) and M_q (bit 2); the gate
+  // rows (bit 1) are handled with their LDS copy
+  auto tile_frozen = [&](int m) {
+    return ((v_frozen & 1u) && m >= NT && m < 3 * NT) || ((v_frozen & 4u) && m >= 3 * NT);
+  };
+  const bool gates_frozen = (v_frozen & 2u) != 0;
+  // direction scale and skip of channel c applied to a readout y of token value xc
+  auto finish = [&](float y, int64_t c, float xc) {
+    if (v_skip) y = fmaf(v_skip[c], xc, y);
+    if (v_scales) y *= v_scales[(int64_t)r * Dt + c];
+    return y;
+  };
+  auto xs_at = [&](int t, int col) {
+    return __uint_as_float((unsigned)Xs[t * XLD + col] << 16);
+  };
   const unsigned short* xg = static_cast<const unsigned short*>(p.x);
   const float inv_h = 1.f / (float)H;
   const bool fast_pix = N < (1 << 22);
@@ -181,8 +204,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   f32x4 S[MTW][NT];
   f32x4 Acc[MULTI ? MTW : 1][MULTI ? NT : 1];
   {
-    const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h
-                                                   : (int64_t)r * nh + h) * SS;
+    const float* init = p.init + init_offset(p, b, r, h, SS);
 #pragma unroll
     for (int mi = 0; mi < MTW; ++mi) {
       const int row = (w + kWaves * mi) * 16 + c16;
@@ -190,6 +212,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       for (int n = 0; n < NT; ++n) S[mi][n] = *reinterpret_cast<const f32x4*>(init + row * D + n * 16 + 4 * g);
     }
     for (int i = threadIdx.x; i < 2 * D; i += kThreads) Tb[0][i] = init[TR * D + i];
+    if (threadIdx.x < 3) cnt_lds[threadIdx.x] = 0u;
   }
   int cur = 0;  // which Tb copy holds the chunk-start gate rows
   // B-operand values of the gate rows for column tile n (rows past the two are zero)
@@ -361,9 +384,15 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
           dd += dl[e] * dl[e];
         }
         float alpha;
+        StepFlags sf;
         const float step = executed_step(row16_sum(kk2), row16_sum(dd), Pj[t * PLD + 3 * D],
-                                         Pj[t * PLD + 3 * D + 1], gp, &alpha);
+                                         Pj[t * PLD + 3 * D + 1], gp, &alpha, &sf);
         const bool live = t < nt;
+        if (v_counts && c16 == 0 && live) {
+          atomicAdd(&cnt_lds[0], 1u);
+          atomicAdd(&cnt_lds[1], (unsigned)(sf.bits & 1));
+          atomicAdd(&cnt_lds[2], (unsigned)((sf.bits >> 1) & 1));
+        }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           const float kv = live ? kn[e] : 0.f;
@@ -386,6 +415,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       // token pixels in registers and completes y in D, once the block's U is known.
       f32x4 rq = {0.f, 0.f, 0.f, 0.f};
       int rpix[4] = {0, 0, 0, 0};
+      float rx[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi) {
         const int m = w + kWaves * mi;
@@ -408,12 +438,17 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         if (RUN) {
           rq = acc;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rpix[i] = pixs[4 * g + i];
+          for (int i = 0; i < 4; ++i) {
+            rpix[i] = pixs[4 * g + i];
+            if (v_skip) rx[i] = xs_at(4 * g + i, m * 16 + c16);
+          }
         } else {
+          const int64_t c = (int64_t)h * D + m * 16 + c16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
-            if (t < nt) dst[((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + m * 16 + c16] = acc[i];
+            if (t < nt)
+              dst[((int64_t)b * N + pixs[t]) * Dt + c] = finish(acc[i], c, v_skip ? xs_at(t, m * 16 + c16) : 0.f);
           }
         }
       }
@@ -481,8 +516,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g + i;
-          L1[i] = c16 < rr ? st_r[i] * pj[i] * gr[i] : 0.f;
-          L1T[i] = rr < c16 ? st_c * pc[i] * gr[i] : 0.f;
+          // without the key-dependent correction the writes do not interact: L = 0, T = I
+          L1[i] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
+          L1T[i] = rr < c16 && !v_nodgd ? st_c * pc[i] * gr[i] : 0.f;
         }
         // X + I for a matrix in the accumulator layout
         auto plus_eye = [&](f32x4 x) {
@@ -502,7 +538,9 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
       f32x4 gk, dl;
       if (w >= SW0) {
         const int n_own = w - SW0;
-        if (MULTI && !first) {
+        if (v_nodgd) {  // u_t = -step_t delta_t: no G_s k_t term
+          gk = (f32x4){0.f, 0.f, 0.f, 0.f};
+        } else if (MULTI && !first) {
           gk = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -577,6 +615,10 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          if (tile_frozen(w + kWaves * mi)) {  // no update: Z unused (never an M_mem tile)
+            split4(z, zh[mi], zl[mi]);
+            continue;
+          }
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             bf16x8 sh, sl;
@@ -600,13 +642,13 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
-            if (t < nt)
-              dst[((int64_t)b * N + rpix[i]) * Dt + (int64_t)h * D + w * 16 + c16] = cprev[t] * rq[i] + y[i];
+            const int64_t c = (int64_t)h * D + w * 16 + c16;
+            if (t < nt) dst[((int64_t)b * N + rpix[i]) * Dt + c] = finish(cprev[t] * rq[i] + y[i], c, rx[i]);
           }
         }
         // gate rows: every readout wave forms their Z tile and updates column tile w
         bf16x4 tzh, tzl;
-        if (w < NT) {
+        if (w < NT && !gates_frozen) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -619,6 +661,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
+          if (tile_frozen(w + kWaves * mi)) continue;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             f32x4 acc = MULTI ? Acc[MULTI ? mi : 0][MULTI ? n : 0] : S[mi][n];
@@ -631,7 +674,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
             }
           }
         }
-        if (w < NT) {
+        if (w < NT && !gates_frozen) {
           f32x4 acc = tail_tile(first ? Tb[cur] : Tb[cur ^ 1], w, c16, g);
           acc *= cc;
           // K operand of column tile w, read again (an index into kah by wave id would not
@@ -682,7 +725,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) S[mi][n] = Acc[MULTI ? mi : 0][MULTI ? n : 0];
     }
-    cur ^= 1;
+    if (!gates_frozen) cur ^= 1;  // frozen gate rows stay in the chunk-start copy
   }
 
   if (p.final_mem) {
@@ -696,6 +739,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
     }
     for (int i = threadIdx.x; i < 2 * D; i += kThreads) fin[TR * D + i] = Tb[cur][i];
   }
+  if (v_counts && threadIdx.x < 3) atomicAdd(&v_counts[threadIdx.x], (unsigned long long)cnt_lds[threadIdx.x]);
 
 }
 
@@ -720,23 +764,32 @@ bool mfma_path_supported(const ChainParams& p, int d) {
   return true;
 }
 
-hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
-  dim3 grid((unsigned)blocks);
-  if (d == 32) {
-    if (p.readout)
-      hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32, true>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((chain_mfma_kernel<32, true, 4, KEEP32, false>), grid, dim3(256), 0, stream, p);
-  } else if (d == 64) {
-    if (p.readout)
-      hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64, true>), grid, dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL((chain_mfma_kernel<64, false, 8, KEEP64, false>), grid, dim3(512), 0, stream, p);
+// true when the call asks for any variant that only the VAR instantiations implement
+bool needs_variants(const ChainParams& p) {
+  return p.route_scales || p.skip || p.counts || p.frozen || p.no_dgd || p.injection || p.spectral;
+}
+
+template <int D, bool MULTI, int NW>
+hipError_t launch_d(const ChainParams& p, dim3 grid, hipStream_t stream) {
+  constexpr bool KEEP = D == 32 ? KEEP32 : KEEP64;
+  const bool var = needs_variants(p);
+  const dim3 block(64 * NW);
+  if (p.readout) {
+    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, true, false>), grid, block, 0, stream, p);
   } else {
-    return hipErrorInvalidValue;
+    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_chain_mfma(const ChainParams& p, int d, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
+  const dim3 grid((unsigned)blocks);
+  if (d == 32) return launch_d<32, true, 4>(p, grid, stream);
+  if (d == 64) return launch_d<64, false, 8>(p, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hope

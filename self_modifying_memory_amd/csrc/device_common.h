@@ -40,11 +40,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct GateParams {
   int eta_map;   // 0 sigmoid, 1 softplus
   float eta_scale, alpha_bias, eps;
+  int injection;  // 0 soft cap (Eq. 19), 1 hard clamp at the same limit, 2 none
+  int spectral;   // 0 clamp (Eq. 20), 1 smooth map to the same limit, 2 none
+};
+
+// Which step-control limits bind for one token: bit 0 the raw eta exceeds the injection
+// limit, bit 1 eta_bar exceeds the spectral limit.
+struct StepFlags {
+  int bits;
 };
 
 struct TokenGates {
   float k, q, delta;  // this lane's component (0 for lanes >= d)
   float alpha, step;  // per token (same in every lane)
+  int flags;          // StepFlags bits (same in every lane)
 };
 
 // Executed step from the token's norms ("VisionHOPE: Visual Backbones as Self-Modifying
@@ -61,8 +70,12 @@ struct TokenGates {
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// Variants ("VisionHOPE", Sec. 3.5 ablations): a hard clamp min(eta, eta_inj) or no
+// injection control; the smooth spectral map eta_spec (1 - exp(-eta_bar / eta_spec)) or no
+// spectral control.
 __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, float s_alpha,
-                                               const GateParams& g, float* alpha_out) {
+                                               const GateParams& g, float* alpha_out,
+                                               StepFlags* flags = nullptr) {
   float eta;
   if (g.eta_map == 0) {
     eta = g.eta_scale * fast_rcp(1.f + fast_exp(-s_eta));
@@ -75,11 +88,19 @@ __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, 
   const float one_minus_alpha = ez * alpha;  // sigmoid(-z), accurate near alpha = 1
   const float rr = sqrtf(dd + g.eps * g.eps) + g.eps;
   const float inj = (1.f - 1e-3f) * one_minus_alpha * fast_rcp(rr);
-  const float bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta * fast_rcp(inj));
+  float bar;
+  if (g.injection == 0) {
+    bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta * fast_rcp(inj));
+  } else {
+    bar = g.injection == 1 ? fminf(eta, inj) : eta;
+  }
   float spec = (1.f - 1e-6f) * 2.f * alpha * fast_rcp(fmaxf(kk, 1e-20f));
   if (spec > 0.f) spec = __uint_as_float(__float_as_uint(spec) - 1u);  // one ulp toward 0
   *alpha_out = alpha;
-  return fminf(bar, spec);
+  if (flags) flags->bits = (eta > inj ? 1 : 0) | (bar > spec ? 2 : 0);
+  if (g.spectral == 0) return fminf(bar, spec);
+  if (g.spectral == 2) return bar;
+  return (bar == 0.f || spec == 0.f) ? 0.f : spec * -expm1f(-bar * fast_rcp(spec));
 }
 
 // One token on one wave, lane i holding component i of the raw projections: the
@@ -92,7 +113,9 @@ __device__ __forceinline__ TokenGates token_gates(float kr, float vr, float qr, 
   o.delta = o.k - vr;
   const float dd = wave_sum(o.delta * o.delta);
   const float kk = wave_sum(o.k * o.k);
-  o.step = executed_step(kk, dd, s_eta, s_alpha, g, &o.alpha);
+  StepFlags f;
+  o.step = executed_step(kk, dd, s_eta, s_alpha, g, &o.alpha, &f);
+  o.flags = f.bits;
   return o;
 }
 

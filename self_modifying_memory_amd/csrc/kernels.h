@@ -25,7 +25,21 @@ struct ChainParams {
   float eta_scale, alpha_bias, eps;
   int readout;            // 0 boundary (chunk-start memory), 1 running (memory after the
                           // chunk's earlier tokens)
+  // variants
+  const float* route_scales;     // [4][D] channel-wise direction scales, or nullptr (ones)
+  const float* skip;             // [D] channel-wise skip, or nullptr
+  unsigned long long* counts;    // [3] step-control counters (accumulated), or nullptr
+  int injection, spectral;       // step controls (GateParams)
+  unsigned frozen;               // 1: M_k, M_v; 2: m_eta, m_alpha; 4: M_q held fixed
+  int no_dgd;                    // 1: drop the key-dependent correction of the update
+  int shared_init;               // 1: init is [nh][S] for every route
 };
+
+// Offset (in floats) of the initial state of (image b, route r, head h).
+__host__ __device__ inline int64_t init_offset(const ChainParams& p, int b, int r, int h, int64_t SS) {
+  if (p.shared_init) return (int64_t)h * SS;
+  return (p.init_per_image ? ((int64_t)b * 4 + r) * p.nh + h : (int64_t)r * p.nh + h) * SS;
+}
 
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);

@@ -57,7 +57,7 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
               final_memories: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None,
               out_dtype: torch.dtype = torch.float32,
-              readout: str = "boundary") -> N.hope_scan2d_opts_t:
+              readout: str = "boundary", variants: dict | None = None) -> N.hope_scan2d_opts_t:
     lib = N.load_library()
     o = N.hope_scan2d_opts_t()
     lib.hope_scan2d_default_opts(ctypes.byref(o))
@@ -69,6 +69,7 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
     o.init_per_image = int(bool(init_per_image))
     o.out_dtype = N.HOPE_BF16 if out_dtype == torch.bfloat16 else N.HOPE_F32
     o.readout = _READOUTS[readout]
+    _set_variants(o, variants or {})
     if final_memories is not None:
         _require_device(final_memories, "final_memories")
         if final_memories.dtype != torch.float32:
@@ -79,6 +80,37 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
     return o
+
+
+def _f32_device(t: torch.Tensor, name: str, numel: int) -> int:
+    _require_device(t, name)
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {numel} elements")
+    return t.data_ptr()
+
+
+def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
+    """VisionHOPE variants (Eq. 26 scales, App. B.5 skip, Sec. 3.5 ablations)."""
+    unknown = set(v) - {"route_scales", "skip", "counts", "injection", "spectral", "frozen",
+                        "no_dgd", "shared_init", "D"}
+    if unknown:
+        raise ValueError(f"unknown variant options {sorted(unknown)}")
+    D = v.get("D")
+    if v.get("route_scales") is not None:
+        o.route_scales = _f32_device(v["route_scales"], "route_scales", 4 * D)
+    if v.get("skip") is not None:
+        o.skip = _f32_device(v["skip"], "skip", D)
+    if v.get("counts") is not None:
+        c = v["counts"]
+        _require_device(c, "counts")
+        if c.dtype != torch.int64 or not c.is_contiguous() or c.numel() != 3:
+            raise ValueError("counts must be a contiguous int64 tensor of 3 elements")
+        o.counts = c.data_ptr()
+    o.injection = N.HOPE_INJECTION[v.get("injection", "soft")]
+    o.spectral = N.HOPE_SPECTRAL[v.get("spectral", "clamp")]
+    o.frozen = sum(N.HOPE_FREEZE[f] for f in set(v.get("frozen", ())))
+    o.no_dgd = int(bool(v.get("no_dgd", False)))
+    o.shared_init = int(bool(v.get("shared_init", False)))
 
 
 def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
@@ -107,7 +139,10 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         final_memories: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None,
                         scan_events: tuple | None = None,
-                        readout: str = "boundary") -> torch.Tensor:
+                        readout: str = "boundary", route_scales: torch.Tensor | None = None,
+                        skip: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                        injection: str = "soft", spectral: str = "clamp", frozen=(),
+                        no_dgd: bool = False, shared_init: bool = False) -> torch.Tensor:
     """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32, or bfloat16
     when a bfloat16 ``out`` is passed: the fp32 route sum rounded once).
 
@@ -115,6 +150,10 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     init_per_image).  A workspace is allocated through torch when none is given.
     readout: "boundary" (memory frozen at the chunk start) or "running" (memory after
     the chunk's earlier tokens).
+    Variants: route_scales [4, D] and skip [D] float32 (Eq. 26, App. B.5); counts, an int64
+    [3] tensor the step-control counters are added to; injection "soft"/"hard"/"none";
+    spectral "clamp"/"soft"/"none"; frozen, a subset of {"kv", "dynamics", "q"}; no_dgd;
+    shared_init (init_memories is then [n_heads, S]).
     scan_events: optional (begin, end) torch.cuda.Event pair that the library records
     around the scan kernel alone (already recorded once, so that they exist).
     """
@@ -131,8 +170,11 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     if workspace is None:
         workspace = alloc_workspace(x, n_heads, dirs, chunk, out.dtype)
     fm = make_fmap(x, n_heads)
+    variants = dict(route_scales=route_scales, skip=skip, counts=counts, injection=injection,
+                    spectral=spectral, frozen=frozen, no_dgd=no_dgd, shared_init=shared_init,
+                    D=x.shape[3])
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
-                     workspace, out.dtype, readout)
+                     workspace, out.dtype, readout, variants)
     if scan_events is not None:
         begin, end = scan_events
         if not begin.cuda_event or not end.cuda_event:

@@ -138,7 +138,9 @@ def test_argument_errors(lib):
     for k, v in [("eta_map", 2), ("eta_scale", -1.0), ("eta_scale", float("nan")),
                  ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("out_dtype", 2),
                  ("scan_begin", FAKE), ("scan_end", FAKE),  # the event pair is both or neither
-                 ("readout", 2), ("reserved", 1)]:
+                 ("readout", 2), ("reserved", 1), ("reserved2", 1), ("injection", 3), ("spectral", -1),
+                 ("frozen", 8), ("no_dgd", 2), ("shared_init", 2), ("counts", FAKE + (3 << 30) + 4),
+                 ("skip", FAKE + (3 << 30) + 2)]:
         assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k
     # final memories overlapping out, misaligned workspace
     assert call(lib, x, o=opts(lib, final_memories=FAKE + (2 << 30))) == N.HOPE_ERR_INVALID_ARG
@@ -177,3 +179,17 @@ def test_debug_export_errors(lib):
     assert lib.hope_debug_cross_merge(FAKE, 3, 2, 4, 5, 32, 15, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG
     assert lib.hope_debug_cross_merge(FAKE, 0, 2, 4, 5, 32, 15, FAKE + 64, None) == N.HOPE_ERR_INVALID_ARG
     assert lib.hope_debug_cross_merge(FAKE, 0, 2, 0, 5, 32, 15, FAKE + (2 << 30), None) == N.HOPE_ERR_INVALID_ARG
+
+
+def test_variant_option_errors(lib):
+    x = fmap()
+    ws = lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, None)
+    base = dict(workspace=FAKE + (3 << 30), workspace_bytes=ws)
+    # shared and per-image initial states exclude each other
+    assert call(lib, x, o=opts(lib, shared_init=1, init_per_image=1, **base)) == N.HOPE_ERR_INVALID_ARG
+    # scales / skip / counters overlapping out
+    out = FAKE + (2 << 30)
+    for k in ("route_scales", "skip", "counts"):
+        assert call(lib, x, o=opts(lib, **{k: out}, **base)) == N.HOPE_ERR_INVALID_ARG, k
+    # counters overlapping the workspace
+    assert call(lib, x, o=opts(lib, counts=FAKE + (3 << 30) + 64, **base)) == N.HOPE_ERR_INVALID_ARG

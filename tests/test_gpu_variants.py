@@ -1,0 +1,119 @@
+"""GPU parity of the VisionHOPE variants (Sec. 3.5 ablations, Eq. 26 direction scales,
+App. B.5 skip) through the C ABI against the fp64 oracle, on both scan kernels.
+
+Counters of the step controls are integers decided by floating point: the GPU decides in
+fp32, the oracle in fp64, so they must agree exactly except on tokens whose margin to the
+limit is within the oracle's 1e-5 band (counted by the oracle as *_near).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from _parity import TOL, check_final, check_out, to_device
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "f32_d16": (2, 4, 6, 32, 2, "f32", 0),      # fp32 kernel
+    "f32_d64": (1, 6, 9, 64, 1, "f32", 4),      # fp32 kernel, ragged chunks
+    "bf16_d32": (2, 5, 37, 96, 3, "bf16", 0),   # MFMA kernel, multi-block chunks
+    "bf16_d64": (2, 6, 9, 128, 2, "bf16", 0),   # MFMA kernel, d = 64
+}
+FROZEN = {"kv": ("k", "v"), "dynamics": ("eta", "alpha"), "q": ("q",)}
+
+VARIANTS = {
+    "scales_skip": dict(route_scales=True, skip=True),
+    "hard_injection": dict(injection="hard"),
+    "soft_spectral": dict(spectral="soft", eta_scale=3.0),
+    "no_injection": dict(injection="none", eta_scale=0.05),
+    "no_spectral": dict(spectral="none"),
+    "frozen_kv": dict(frozen=("kv",)),
+    "frozen_dynamics": dict(frozen=("dynamics",)),
+    "frozen_all": dict(frozen=("kv", "dynamics", "q")),
+    "no_dgd": dict(no_dgd=True),
+    "shared_init": dict(shared_init=True),
+    "counts": dict(counts=True, eta_scale=0.03),                     # eta near the injection limit
+    "counts_spectral": dict(counts=True, eta_scale=4.0, alpha_bias=-2.0),  # low retention: spectral binds
+}
+
+
+def _run(shape, var, readout="boundary"):
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    B, H, W, D, nh, dt, chunk = shape
+    d = D // nh
+    inp = wl.draw(B, H, W, D, nh, seed=900 + H * 31 + W, dtype=dt, live=True)
+    rng = np.random.Generator(np.random.PCG64(17))
+    extra = {k: var[k] for k in ("eta_scale", "alpha_bias") if k in var}
+    ok = dict(readout=readout, **extra)           # oracle keyword arguments
+    gk = dict(readout=readout, **extra)           # GPU keyword arguments
+    x, init = to_device(inp, dt)
+    init_np = inp["init"]
+    if var.get("route_scales"):
+        lam = rng.uniform(0.5, 1.5, (4, D))
+        ok["route_scales"] = lam
+        gk["route_scales"] = torch.from_numpy(lam.astype(np.float32)).cuda()
+    if var.get("skip"):
+        sk = rng.standard_normal(D) * 0.3
+        ok["skip"] = sk.astype(np.float32).astype(np.float64)
+        gk["skip"] = torch.from_numpy(sk.astype(np.float32)).cuda()
+    if "route_scales" in ok:
+        ok["route_scales"] = ok["route_scales"].astype(np.float32).astype(np.float64)
+    for k in ("injection", "spectral"):
+        if k in var:
+            ok[k] = gk[k] = var[k]
+    if "frozen" in var:
+        gk["frozen"] = var["frozen"]
+        ok["frozen"] = tuple(m for f in var["frozen"] for m in FROZEN[f])
+    if var.get("no_dgd"):
+        gk["no_dgd"] = True
+        ok["dgd"] = False
+    if var.get("shared_init"):
+        init_np = inp["init"][1]                       # [n_heads, S]
+        init = torch.from_numpy(np.ascontiguousarray(init_np, dtype=np.float32)).cuda()
+        ok["shared_init"] = gk["shared_init"] = True
+    counts = None
+    if var.get("counts"):
+        counts = torch.zeros(3, dtype=torch.int64, device="cuda")
+        gk["counts"] = counts
+        ok["counts"] = {}
+    fin = torch.full((B, 4, nh, 4 * d * d + 2 * d), float("nan"), dtype=torch.float32, device="cuda")
+    out = hope_scan2d_forward(x, init, nh, 15, chunk, final_memories=fin, **gk)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle.scan2d(inp["x"], init_np, nh, dirs=15, chunk=chunk, **ok)
+    return out.cpu().numpy(), fin.cpu().numpy(), ref_out, ref_fin, d, (counts, ok.get("counts"))
+
+
+@pytest.mark.parametrize("var", list(VARIANTS), ids=list(VARIANTS))
+@pytest.mark.parametrize("shape", list(SHAPES), ids=list(SHAPES))
+def test_variant_matches_oracle(shape, var):
+    print("case", shape, var, flush=True)
+    sh = SHAPES[shape]
+    out, fin, ref_out, ref_fin, d, (cnt, ref_cnt) = _run(sh, VARIANTS[var])
+    tol = TOL[sh[5]]
+    e_out = check_out(out, ref_out, sh[4], tol)
+    e_fin = check_final(fin, ref_fin, d, 15, tol)
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+    if cnt is not None:
+        got = cnt.cpu().numpy()
+        assert got[0] == ref_cnt["updates"]
+        assert abs(int(got[1]) - ref_cnt["inj"]) <= ref_cnt["inj_near"], (got, ref_cnt)
+        assert abs(int(got[2]) - ref_cnt["spec"]) <= ref_cnt["spec_near"], (got, ref_cnt)
+        if var == "counts":            # both outcomes of the injection test occur
+            assert 0 < got[1] < got[0]
+        else:                          # the spectral limit binds on some tokens
+            assert got[2] > 0
+        print(f"  counts {got.tolist()} oracle {ref_cnt}", flush=True)
+
+
+@pytest.mark.parametrize("shape", ["f32_d16", "bf16_d32", "bf16_d64"])
+def test_variants_with_running_readout(shape):
+    var = dict(route_scales=True, skip=True, frozen=("kv",), injection="hard", no_dgd=True)
+    print("case", shape, var, flush=True)
+    sh = SHAPES[shape]
+    out, fin, ref_out, ref_fin, d, _ = _run(sh, var, readout="running")
+    tol = TOL[sh[5]]
+    e_out = check_out(out, ref_out, sh[4], tol)
+    e_fin = check_final(fin, ref_fin, d, 15, tol)
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
