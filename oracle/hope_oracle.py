@@ -230,7 +230,7 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
                eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
                control: bool = True, log: list | None = None, readout: str = "boundary",
                injection: str = "soft", spectral: str = "clamp", frozen=(), dgd: bool = True,
-               counts: dict | None = None):
+               counts: dict | None = None, qs: np.ndarray | None = None):
     """Run chains over ordered tokens.
 
     xs    : [n, N, d] tokens in route order
@@ -247,6 +247,9 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
     memories held fixed within the image ([VH] Sec. 3.5: without adaptive K/V, frozen =
     ("k", "v"); without adaptive dynamics, ("eta", "alpha")); dgd=False removes the
     key-dependent correction of the update (retained_dgd).
+    qs [n, N, d] (optional): queries given from outside in route order, the fixed outer
+    query projection of [VH] App. B.5 (and Eq. 14); q_t is then qs_t normalised within the
+    head like the generated one, and M_q takes no part (it stays at its initial value).
     Returns (ys [n, N, d], final state dict).
     """
     for m in frozen:
@@ -264,7 +267,7 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
             x = xs[:, t, :]
             k = stabilized_normalize(_matvec(Mb["k"], x), eps)
             v = _matvec(Mb["v"], x)
-            q = stabilized_normalize(_matvec(Mb["q"], x), eps)
+            q = stabilized_normalize(_matvec(Mb["q"], x) if qs is None else qs[:, t, :], eps)
             eta = phi_eta(_matvec(Mb["eta"], x)[:, 0], eta_map, eta_scale)
             alpha = phi_alpha(_matvec(Mb["alpha"], x)[:, 0], alpha_bias)
             # y_t = M^m_b q_t (boundary) or M^m_{t-1} q_t (running: M is not yet
@@ -277,7 +280,7 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
                 log.append({"t": t, "eta": eta, "alpha": alpha, "step": step, "k": k,
                             "delta": delta})
             for m in MEMORIES:
-                if m in frozen:
+                if m in frozen or (m == "q" and qs is not None):
                     continue
                 vhat = _matvec(Mb[m], v)                      # self-generated target, Eq. 16
                 g = _matvec(Mb[m], k) - vhat                  # output-space signal, Eq. 16
@@ -290,7 +293,7 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
            eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None,
            readout: str = "boundary", injection: str = "soft", spectral: str = "clamp",
            frozen=(), dgd: bool = True, route_scales=None, skip=None,
-           shared_init: bool = False, counts: dict | None = None):
+           shared_init: bool = False, counts: dict | None = None, queries=None):
     """The whole operator: serialise, run every (image, head, route) chain, merge.
 
     x    : [B, H, W, D] (any float dtype; widened to fp64)
@@ -306,6 +309,8 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
     shared-initial-state variant of [VH] Sec. 3.5; trajectories stay separate).
     readout, injection, spectral, frozen, dgd: see srnl_chain; counts accumulates the
     step-control counters of executed_step over every chain computed.
+    queries [B, H, W, D] (optional): the fixed-projection queries of [VH] App. B.5, computed
+    once per image and reused by every route (serialised like x, split into heads).
     Returns (out [b, H, W, D_sel] fp64, final [b, 4, h, S] fp64, NaN for
     unselected routes).
     """
@@ -334,9 +339,13 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
                 flat = np.broadcast_to(init[r, h], (nb, S))
             st = unflatten_state(flat, d)
             C = route_chunk(H, W, r, chunk)
+            qs = None
+            if queries is not None:
+                qsel = np.asarray(queries, dtype=np.float64)[images]
+                qs = cross_scan(qsel[..., h * d:(h + 1) * d], r)
             ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout,
                                  injection=injection, spectral=spectral, frozen=frozen, dgd=dgd,
-                                 counts=counts)
+                                 counts=counts, qs=qs)
             if skip is not None:                      # Y_r = reads + skip * Z_r  ([VH] App. B.5)
                 ys = ys + np.asarray(skip, dtype=np.float64)[h * d:(h + 1) * d] * xs
             if route_scales is not None:              # lambda_r * Y_r  ([VH] Eq. 26)

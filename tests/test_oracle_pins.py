@@ -616,3 +616,20 @@ def test_clamp_counters_edge_values():
     # a huge raw step with little retention headroom: the injection limit binds everywhere
     oracle.scan2d(inp["x"], inp["init"], 1, eta_scale=1e6, alpha_bias=6.0, counts=c1)
     assert c1["updates"] == 80 and c1["inj"] == 80
+
+
+def test_fixed_query_projection_equals_generated_queries_when_they_agree():
+    # App. B.5 / Eq. 14: with queries given from outside, q_t = n(queries[p_r(t)]) and M_q is
+    # not a memory.  If the given queries are exactly what a frozen M_q would generate
+    # (queries = x M_q^T for every head), the outputs equal the run with M_q frozen.
+    inp = wl.draw(1, 4, 5, 8, 2, seed=49, dtype="f32", live=True)
+    x, init = inp["x"], inp["init"]
+    d = 4
+    init_shared = np.broadcast_to(init[0], init.shape).copy()  # every route: route 0's memories
+    q = np.concatenate([x[..., h * d:(h + 1) * d] @ oracle.unflatten_state(init[0, h], d)["q"].T
+                        for h in range(2)], axis=-1)
+    a, fa = oracle.scan2d(x, init_shared, 2, queries=q)
+    b, fb = oracle.scan2d(x, init_shared, 2, frozen=("q",))
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fa, fb, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(oracle.unflatten_state(fa[0, 3, 1], d)["q"], oracle.unflatten_state(init[0, 1], d)["q"])
