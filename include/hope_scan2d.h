@@ -141,7 +141,12 @@ typedef struct {
                                 update (the DGD ablation), keeping signal, retention and step */
   int32_t shared_init;       /* 1: init_memories is [n_heads][S], shared by all routes (the
                                 trajectories stay separate); excludes init_per_image */
-  int32_t reserved2;         /* must be 0 */
+  int32_t queries_dtype;     /* hope_dtype_t of queries (ignored when queries is NULL) */
+  const void* queries;       /* NULL, or device [B][H][W][D] of queries_dtype: queries from the
+                                fixed outer D x D projection of App. B.5 (Eq. 14), computed
+                                once per image and shared by all routes; q_t is the route-
+                                ordered head slice, normalised within the head, and M_q takes
+                                no part (it is left at its initial value) */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

@@ -64,7 +64,9 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if ((o->scan_begin == nullptr) != (o->scan_end == nullptr)) return HOPE_ERR_INVALID_ARG;
   if (o->readout != HOPE_READOUT_BOUNDARY && o->readout != HOPE_READOUT_RUNNING)
     return HOPE_ERR_INVALID_ARG;
-  if (o->reserved != 0 || o->reserved2 != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->reserved != 0) return HOPE_ERR_INVALID_ARG;
+  if (o->queries && o->queries_dtype != HOPE_F32 && o->queries_dtype != HOPE_BF16) return HOPE_ERR_INVALID_ARG;
+  if (o->queries && !aligned(o->queries, 16)) return HOPE_ERR_INVALID_ARG;
   if (o->injection < HOPE_INJECTION_SOFT || o->injection > HOPE_INJECTION_NONE) return HOPE_ERR_INVALID_ARG;
   if (o->spectral < HOPE_SPECTRAL_CLAMP || o->spectral > HOPE_SPECTRAL_NONE) return HOPE_ERR_INVALID_ARG;
   if (o->frozen & ~7u) return HOPE_ERR_INVALID_ARG;
@@ -151,6 +153,9 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   if (o.route_scales && overlaps(r_out, range_of(o.route_scales, 4 * (size_t)x->D * sizeof(float))))
     return HOPE_ERR_INVALID_ARG;
   if (o.skip && overlaps(r_out, range_of(o.skip, (size_t)x->D * sizeof(float)))) return HOPE_ERR_INVALID_ARG;
+  if (o.queries &&
+      overlaps(r_out, range_of(o.queries, (size_t)n_elem * (o.queries_dtype == HOPE_BF16 ? 2 : 4))))
+    return HOPE_ERR_INVALID_ARG;
   if (o.counts) {
     const Range r_cnt = range_of(o.counts, 3 * sizeof(unsigned long long));
     if (overlaps(r_out, r_cnt) || overlaps(r_cnt, range_of(x->data, x_bytes)) ||
@@ -211,6 +216,8 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   p.frozen = o.frozen;
   p.no_dgd = o.no_dgd;
   p.shared_init = o.shared_init;
+  p.queries = o.queries;
+  p.queries_bf16 = o.queries_dtype == HOPE_BF16;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;

@@ -68,9 +68,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, p.injection, p.spectral};
   unsigned long long n_upd = 0, n_inj = 0, n_spec = 0;  // step-control counters (lane 0)
   // rows held fixed within the image: M_k, M_v (bit 0), the gate rows (bit 1), M_q (bit 2)
+  const unsigned frozen = p.frozen | (p.queries ? 4u : 0u);  // given queries: M_q takes no part
   auto frozen_row = [&](int row) {
-    return ((p.frozen & 1u) && row >= D && row < 3 * D) || ((p.frozen & 4u) && row >= 3 * D && row < 4 * D) ||
-           ((p.frozen & 2u) && row >= 4 * D);
+    return ((frozen & 1u) && row >= D && row < 3 * D) || ((frozen & 4u) && row >= 3 * D && row < 4 * D) ||
+           ((frozen & 2u) && row >= 4 * D);
   };
   __syncthreads();
 
@@ -105,7 +106,11 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         float* pt = &P[t * PS];
         const float kr = lane < D ? pt[lane] : 0.f;
         const float vr = lane < D ? pt[D + lane] : 0.f;
-        const float qr = lane < D ? pt[2 * D + lane] : 0.f;
+        float qr = 0.f;
+        if (lane < D) {
+          qr = p.queries ? query_at(p, b, route_pixel(r, tb + t, H, W, N), (int64_t)h * D + lane)
+                         : pt[2 * D + lane];
+        }
         const TokenGates tg = token_gates(kr, vr, qr, pt[3 * D], pt[3 * D + 1], gp);
         const float k = tg.k, q = tg.q, dl = tg.delta, step = tg.step, alpha = tg.alpha;
         if (lane < D) {

@@ -173,7 +173,8 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
   const float* const v_skip = VAR ? p.skip : nullptr;
   const float* const v_scales = VAR ? p.route_scales : nullptr;
   unsigned long long* const v_counts = VAR ? p.counts : nullptr;
-  const unsigned v_frozen = VAR ? p.frozen : 0u;
+  const void* const v_queries = VAR ? p.queries : nullptr;
+  const unsigned v_frozen = VAR ? (p.frozen | (p.queries ? 4u : 0u)) : 0u;  // M_q unused with given queries
   const bool v_nodgd = VAR && p.no_dgd;
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR ? p.injection : 0,
                       VAR ? p.spectral : 0};
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         for (int mi = 0; mi < MTW; ++mi) {
           const int m = w + kWaves * mi;
           if (m < NT) continue;
+          if (v_queries && m >= 3 * NT) continue;  // queries are given: no q projection
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) void chain_mfma_kernel(ChainParams p) {
         for (int e = 0; e < CPL; ++e) {
           kr[e] = pt[e];
           vr[e] = pt[D + e];
-          qr[e] = pt[2 * D + e];
+          qr[e] = v_queries ? query_at(p, b, pixs[t], (int64_t)h * D + c16 * CPL + e) : pt[2 * D + e];
           kk += kr[e] * kr[e];
           qq += qr[e] * qr[e];
         }
@@ -766,7 +768,8 @@ bool mfma_path_supported(const ChainParams& p, int d) {
 
 // true when the call asks for any variant that only the VAR instantiations implement
 bool needs_variants(const ChainParams& p) {
-  return p.route_scales || p.skip || p.counts || p.frozen || p.no_dgd || p.injection || p.spectral;
+  return p.route_scales || p.skip || p.counts || p.frozen || p.no_dgd || p.injection || p.spectral ||
+         p.queries;
 }
 
 template <int D, bool MULTI, int NW>

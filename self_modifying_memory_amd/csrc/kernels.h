@@ -33,7 +33,16 @@ struct ChainParams {
   unsigned frozen;               // 1: M_k, M_v; 2: m_eta, m_alpha; 4: M_q held fixed
   int no_dgd;                    // 1: drop the key-dependent correction of the update
   int shared_init;               // 1: init is [nh][S] for every route
+  const void* queries;           // [B][H][W][D] queries of a fixed projection, or nullptr
+  int queries_bf16;
 };
+
+// Raw query component c of pixel pix of image b (fixed-projection variant).
+__device__ inline float query_at(const ChainParams& p, int b, int pix, int64_t c) {
+  const int64_t i = ((int64_t)b * p.H * p.W + pix) * p.D + c;
+  if (p.queries_bf16) return __uint_as_float((unsigned)static_cast<const unsigned short*>(p.queries)[i] << 16);
+  return static_cast<const float*>(p.queries)[i];
+}
 
 // Offset (in floats) of the initial state of (image b, route r, head h).
 __host__ __device__ inline int64_t init_offset(const ChainParams& p, int b, int r, int h, int64_t SS) {

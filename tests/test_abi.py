@@ -138,7 +138,8 @@ def test_argument_errors(lib):
     for k, v in [("eta_map", 2), ("eta_scale", -1.0), ("eta_scale", float("nan")),
                  ("alpha_bias", float("inf")), ("eps", -1e-6), ("init_per_image", 2), ("out_dtype", 2),
                  ("scan_begin", FAKE), ("scan_end", FAKE),  # the event pair is both or neither
-                 ("readout", 2), ("reserved", 1), ("reserved2", 1), ("injection", 3), ("spectral", -1),
+                 ("readout", 2), ("reserved", 1), ("injection", 3), ("spectral", -1),
+                 ("queries", FAKE + (3 << 30) + 8),
                  ("frozen", 8), ("no_dgd", 2), ("shared_init", 2), ("counts", FAKE + (3 << 30) + 4),
                  ("skip", FAKE + (3 << 30) + 2)]:
         assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k

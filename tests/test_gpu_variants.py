@@ -35,6 +35,7 @@ VARIANTS = {
     "shared_init": dict(shared_init=True),
     "counts": dict(counts=True, eta_scale=0.03),                     # eta near the injection limit
     "counts_spectral": dict(counts=True, eta_scale=4.0, alpha_bias=-2.0),  # low retention: spectral binds
+    "queries": dict(queries=True),                                   # fixed outer query projection
 }
 
 
@@ -73,6 +74,15 @@ def _run(shape, var, readout="boundary"):
         init_np = inp["init"][1]                       # [n_heads, S]
         init = torch.from_numpy(np.ascontiguousarray(init_np, dtype=np.float32)).cuda()
         ok["shared_init"] = gk["shared_init"] = True
+    if var.get("queries"):
+        q = rng.standard_normal((B, H, W, D)).astype(np.float32) * 0.7
+        if dt == "bf16":
+            qt = torch.from_numpy(q).to(torch.bfloat16)
+            ok["queries"] = qt.float().numpy().astype(np.float64)
+        else:
+            qt = torch.from_numpy(q)
+            ok["queries"] = q.astype(np.float64)
+        gk["queries"] = qt.cuda()
     counts = None
     if var.get("counts"):
         counts = torch.zeros(3, dtype=torch.int64, device="cuda")
@@ -109,7 +119,8 @@ def test_variant_matches_oracle(shape, var):
 
 @pytest.mark.parametrize("shape", ["f32_d16", "bf16_d32", "bf16_d64"])
 def test_variants_with_running_readout(shape):
-    var = dict(route_scales=True, skip=True, frozen=("kv",), injection="hard", no_dgd=True)
+    var = dict(route_scales=True, skip=True, frozen=("kv",), injection="hard", no_dgd=True,
+               queries=True)
     print("case", shape, var, flush=True)
     sh = SHAPES[shape]
     out, fin, ref_out, ref_fin, d, _ = _run(sh, var, readout="running")
