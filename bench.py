@@ -132,6 +132,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--readout", choices=["boundary", "running"], default="boundary",
                     help="readout memory inside a chunk (the default is the chunk-start one)")
+    ap.add_argument("--variants", default="",
+                    help="comma-separated VisionHOPE variants to enable together: scales, skip, "
+                         "counts, hard_injection, soft_spectral, frozen_kv, frozen_dynamics, "
+                         "no_dgd, queries (synthetic scales / skip / queries)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -161,6 +165,32 @@ def main() -> int:
         sets.append((x, torch.empty(x.shape, dtype=torch.float32, device=dev),
                      alloc_workspace(x, w.n_heads, 15, w.chunk)))
     stream = torch.cuda.current_stream()
+    var = [v for v in args.variants.split(",") if v]
+    known = {"scales", "skip", "counts", "hard_injection", "soft_spectral", "frozen_kv",
+             "frozen_dynamics", "no_dgd", "queries"}
+    if set(var) - known:
+        print(f"unknown variants {sorted(set(var) - known)}", file=sys.stderr)
+        return 2
+    vkw = {}
+    vrng = np.random.Generator(np.random.PCG64(123))
+    if "scales" in var:
+        vkw["route_scales"] = torch.from_numpy(vrng.uniform(0.5, 1.5, (4, w.D)).astype(np.float32)).to(dev)
+    if "skip" in var:
+        vkw["skip"] = torch.from_numpy((vrng.standard_normal(w.D) * 0.3).astype(np.float32)).to(dev)
+    if "counts" in var:
+        vkw["counts"] = torch.zeros(3, dtype=torch.int64, device=dev)
+    if "hard_injection" in var:
+        vkw["injection"] = "hard"
+    if "soft_spectral" in var:
+        vkw["spectral"] = "soft"
+    frozen = [f for f, name in (("kv", "frozen_kv"), ("dynamics", "frozen_dynamics")) if name in var]
+    if frozen:
+        vkw["frozen"] = tuple(frozen)
+    if "no_dgd" in var:
+        vkw["no_dgd"] = True
+    if "queries" in var:
+        vkw["queries"] = torch.from_numpy(vrng.standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)).to(
+            dev).to(x_host.dtype)
     # events around the scan kernel alone, recorded by the library on this stream
     scan_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
@@ -171,7 +201,7 @@ def main() -> int:
     def step(i, ev=None):
         x, out, ws = sets[i % len(sets)]
         hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream,
-                            scan_events=ev, readout=args.readout)
+                            scan_events=ev, readout=args.readout, **vkw)
 
     for i in range(args.warmup):
         step(i)
@@ -215,10 +245,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
-                   "state_dtype": "f32", "readout": args.readout},
+                   "state_dtype": "f32", "readout": args.readout, "variants": var},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": recorded_traffic(w) if args.readout == "boundary" else None,
+                     "traffic": recorded_traffic(w) if args.readout == "boundary" and not var else None,
                      "kernel": "chain_mfma_kernel", "kernel_ms": k_avg * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)),
                                            float(np.percentile(kernel_ms, 90))],
