@@ -132,6 +132,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   constexpr int XLD = D + 8;                       // bf16 stride of the token block
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
   constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
+  constexpr int LTLD = kSB + 4;                    // fp32 stride of L^T
 
   __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
   __shared__ float cprev[kSB], bco[kSB + 1];  // block retention products
-  __shared__ __attribute__((aligned(16))) float Tis[64 * 4];  // block inverse (transposed)
+  __shared__ __attribute__((aligned(16))) float LTs[kSB * LTLD];  // L^T of the block solve
   // running readout: the masked token matrix A^T and the unscaled write vectors U
   __shared__ __attribute__((aligned(16))) float Ais[RUN ? 64 * 4 : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuH[RUN ? kSB * XLD : 4];
@@ -456,31 +457,28 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           }
         }
       }
-      // C2: the block's write vectors.
+      // C2: the block's write vectors, on one wave.
       //   (I + L) U = RHS,  L[t][j] = step_t P(j+1,t) (k_t . k_j) for j < t,
       //   RHS[t] = -step_t (P(0,t) G_s k_t + delta_t),  Ub[t] = P(t+1,16) U[t].
-      // L is strictly lower triangular (nilpotent), so (I + L)^-1 =
-      // (I - L)(I + L^2)(I + L^4)(I + L^8): six dependent 16x16 products instead of a
-      // 16-step substitution.  Matrices are held in the MFMA accumulator layout (lane
-      // (g, c16), register i = entry [4g+i][c16]) together with their transposes, which
-      // is exactly the A / B operand layout of the next product.
-      // The inverse is formed once, by the first solve wave, and published through LDS;
-      // every solve wave then applies it to its own column tile of RHS.
+      // L is strictly lower triangular and the same for every column of RHS, so the solve
+      // is a forward substitution with one lane per column, in exact fp32: once u_j is
+      // final, every later row subtracts L[t][j] u_j.  L comes from the token Gram product
+      // on MFMA and reaches every lane through LDS, stored transposed so that column j is
+      // four broadcast reads.
       if (w == SW0) {
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         // retention products over DPP rows (they need only alpha, so they overlap the
-        // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for L^T (prefix
-        // over c), and the block products P(0, t), P(t+1, 16)
+        // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for the running
+        // readout's A^T (prefix over c), and the block products P(0, t), P(t+1, 16)
         const float a_self = alph[c16];
         const float a_next = alph[min(c16 + 1, kSB - 1)], a_prev = alph[max(c16 - 1, 0)];
-        const float st_c = stp[c16];
         float pj[4], pc[4], st_r[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g + i;
           st_r[i] = stp[rr];
           pj[i] = row16_suffix_prod(c16 + 1 < rr ? a_next : 1.f);
-          pc[i] = row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f);
+          pc[i] = RUN ? row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f) : 0.f;
         }
         {
           const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
@@ -516,77 +514,76 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           for (int i = 0; i < 4; ++i) at[i] = 4 * g + i < c16 ? pc[i] * aq[i] : 0.f;
           *reinterpret_cast<f32x4*>(Ais + 4 * lane) = at;
         }
-        f32x4 L1, L1T;
+        {
+          // L^T: lane (g, c16) holds L[4g+i][c16]; without the key-dependent correction the
+          // writes do not interact (L = 0)
+          f32x4 lt;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * g + i;
-          // without the key-dependent correction the writes do not interact: L = 0, T = I
-          L1[i] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
-          L1T[i] = rr < c16 && !v_nodgd ? st_c * pc[i] * gr[i] : 0.f;
-        }
-        // X + I for a matrix in the accumulator layout
-        auto plus_eye = [&](f32x4 x) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] += (4 * g + i == c16) ? 1.f : 0.f;
-          return x;
-        };
-        const f32x4 L2 = mm16(L1T, L1), L2T = mm16(L1, L1T);
-        const f32x4 E = plus_eye(L2T - L1T - mm16(L2, L1T));  // (I + L2^T)(I - L^T)
-        const f32x4 L4 = mm16(L2T, L2), L4T = mm16(L2, L2T);
-        const f32x4 L8 = mm16(L4T, L4);
-        const f32x4 FT = plus_eye(L4 + L8 + mm16(L4T, L8));   // ((I + L8^T)(I + L4^T))^T
-        *reinterpret_cast<f32x4*>(Tis + 4 * lane) = mm16(FT, E);  // ((I + L)^-1)^T
-      }
-      // right-hand-side inputs of each solve wave's column tile (NSW == NT: one each):
-      // G_s k_t (the chunk gain so far applied to the keys) and delta_t
-      f32x4 gk, dl;
-      if (w >= SW0) {
-        const int n_own = w - SW0;
-        if (v_nodgd) {  // u_t = -step_t delta_t: no G_s k_t term
-          gk = (f32x4){0.f, 0.f, 0.f, 0.f};
-        } else if (MULTI && !first) {
-          gk = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            f32x4 k0, k1, g0, g1;
-            load_row_pair(Ks + c16 * LD, s, g, k0, k1);
-            load_row_pair(Gs + (n_own * 16 + c16) * LD, s, g, g0, g1);
-            bf16x8 kh, kl, gh, gl;
-            split8(k0, k1, kh, kl);
-            split8(g0, g1, gh, gl);
-            gk = mma32x3(kh, kl, gh, gl, gk);
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * g + i;
+            lt[i] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) gk[e] = Ks[(4 * g + e) * LD + n_own * 16 + c16];
+          *reinterpret_cast<f32x4*>(LTs + c16 * LTLD + 4 * g) = lt;
         }
+        // RHS of a later block of a multi-block chunk: G_s k_t on MFMA, per column tile,
+        // staged token-major in Ubs (overwritten below with the write vectors)
+        const bool gk_mfma = MULTI && !first && !v_nodgd;
+        if (gk_mfma) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dl[e] = Dls[(4 * g + e) * LD + n_own * 16 + c16];
-      }
-      lds_barrier();
-      // U = (I + L)^-1 RHS for each column tile, then Ub = P(t+1,16) U
-      if (w >= SW0) {
-        const int n_own = w - SW0;
-        const f32x4 TiT = *reinterpret_cast<const f32x4*>(Tis + 4 * lane);
-        f32x4 rhs;
+          for (int n = 0; n < NT; ++n) {
+            f32x4 gk = zero4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * g + e;
-          rhs[e] = -stp[j] * (cprev[j] * gk[e] + dl[e]);
+            for (int s = 0; s < KS; ++s) {
+              f32x4 k0, k1, g0, g1;
+              load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+              load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
+              bf16x8 kh, kl, gh, gl;
+              split8(k0, k1, kh, kl);
+              split8(g0, g1, gh, gl);
+              gk = mma32x3(kh, kl, gh, gl, gk);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 4 * g + i;
+              Ubs[t * LD + n * 16 + c16] = -stp[t] * (cprev[t] * gk[i] + Dls[t * LD + n * 16 + c16]);
+            }
+          }
         }
-        const f32x4 u = mm16(TiT, rhs);
+        // forward substitution, column `lane` of U
+        if (lane < D) {
+          float u[kSB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 4 * g + i, col = n_own * 16 + c16;
-          const float ub = bco[t] * u[i];
-          if (MULTI) Ubs[t * LD + col] = ub;
-          const __bf16 uh = (__bf16)ub;
-          UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
-          UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
-          if (RUN) {
-            const __bf16 vh = (__bf16)u[i];
-            UuH[t * XLD + col] = __builtin_bit_cast(unsigned short, vh);
-            UuL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(u[i] - (float)vh));
+          for (int t = 0; t < kSB; ++t) {
+            if (gk_mfma) {
+              u[t] = Ubs[t * LD + lane];
+            } else {  // G_s = I (first block) or no G_s k term (no DGD)
+              const float gk = v_nodgd ? 0.f : Ks[t * LD + lane];
+              u[t] = -stp[t] * (cprev[t] * gk + Dls[t * LD + lane]);
+            }
+          }
+          if (!v_nodgd) {
+#pragma unroll
+            for (int j = 0; j < kSB - 1; ++j) {
+              const float* col = LTs + j * LTLD;  // L[.][j], broadcast to every lane
+              f32x4 c[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
+#pragma unroll
+              for (int t = j + 1; t < kSB; ++t) u[t] = fmaf(-c[t >> 2][t & 3], u[j], u[t]);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < kSB; ++t) {
+            const float ub = bco[t] * u[t];
+            if (MULTI) Ubs[t * LD + lane] = ub;
+            const __bf16 uh = (__bf16)ub;
+            UbH[t * XLD + lane] = __builtin_bit_cast(unsigned short, uh);
+            UbL[t * XLD + lane] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
+            if (RUN) {
+              const __bf16 vh = (__bf16)u[t];
+              UuH[t * XLD + lane] = __builtin_bit_cast(unsigned short, vh);
+              UuL[t * XLD + lane] = __builtin_bit_cast(unsigned short, (__bf16)(u[t] - (float)vh));
+            }
           }
         }
       }
