@@ -363,6 +363,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
       // each lane holding CPL consecutive components.  Padding tokens get no key, no
       // write and unit retention.
       if (w < 4) {
+        __builtin_amdgcn_s_setprio(2);  // gates are on the block's critical path too
         constexpr int CPL = D / 16;
         const int t = 4 * w + g;
         const float* pt = Pj + t * PLD + c16 * CPL;
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           alph[t] = live ? alpha : 1.f;
           stp[t] = live ? step : 0.f;
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       lds_barrier();
 
@@ -466,6 +468,9 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
       // on MFMA and reaches every lane through LDS, stored transposed so that column j is
       // four broadcast reads.
       if (w == SW0) {
+        // this wave is the block's critical path: let it win issue slots on its SIMD over
+        // the waves of the other chain sharing the CU
+        __builtin_amdgcn_s_setprio(3);
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         // retention products over DPP rows (they need only alpha, so they overlap the
         // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for the running
@@ -562,14 +567,22 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
             }
           }
           if (!v_nodgd) {
+            // software-pipelined: column j+1 of L is read (a broadcast) while column j is
+            // applied, and row j+1 is updated first so the next step can start early
+            f32x4 c[4], cn[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(LTs + 4 * q);
 #pragma unroll
             for (int j = 0; j < kSB - 1; ++j) {
-              const float* col = LTs + j * LTLD;  // L[.][j], broadcast to every lane
-              f32x4 c[4];
+              if (j + 1 < kSB - 1) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
+                for (int q = (j + 2) >> 2; q < 4; ++q)
+                  cn[q] = *reinterpret_cast<const f32x4*>(LTs + (j + 1) * LTLD + 4 * q);
+              }
 #pragma unroll
               for (int t = j + 1; t < kSB; ++t) u[t] = fmaf(-c[t >> 2][t & 3], u[j], u[t]);
+#pragma unroll
+              for (int q = (j + 2) >> 2; q < 4; ++q) c[q] = cn[q];
             }
           }
 #pragma unroll
@@ -586,6 +599,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
             }
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       lds_barrier();
 
