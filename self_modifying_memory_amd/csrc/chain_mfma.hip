@@ -567,22 +567,14 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
             }
           }
           if (!v_nodgd) {
-            // software-pipelined: column j+1 of L is read (a broadcast) while column j is
-            // applied, and row j+1 is updated first so the next step can start early
-            f32x4 c[4], cn[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(LTs + 4 * q);
 #pragma unroll
             for (int j = 0; j < kSB - 1; ++j) {
-              if (j + 1 < kSB - 1) {
+              const float* col = LTs + j * LTLD;  // L[.][j], broadcast to every lane
+              f32x4 c[4];
 #pragma unroll
-                for (int q = (j + 2) >> 2; q < 4; ++q)
-                  cn[q] = *reinterpret_cast<const f32x4*>(LTs + (j + 1) * LTLD + 4 * q);
-              }
+              for (int q = (j + 1) >> 2; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
 #pragma unroll
               for (int t = j + 1; t < kSB; ++t) u[t] = fmaf(-c[t >> 2][t & 3], u[j], u[t]);
-#pragma unroll
-              for (int q = (j + 2) >> 2; q < 4; ++q) c[q] = cn[q];
             }
           }
 #pragma unroll
@@ -764,7 +756,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
 #define KEEP32 true
 #endif
 #ifndef KEEP64
-#define KEEP64 false
+#define KEEP64 true
 #endif
 
 bool mfma_path_supported(const ChainParams& p, int d) {
