@@ -151,7 +151,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
   __shared__ float cprev[kSB], bco[kSB + 1];  // block retention products
-  __shared__ __attribute__((aligned(16))) float LTs[kSB * LTLD];  // L^T of the block solve
+  // L of the block solve, one copy per solve wave
+  __shared__ __attribute__((aligned(16))) float LTs[(D / 16) * kSB * LTLD];
   // running readout: the masked token matrix A^T and the unscaled write vectors U
   __shared__ __attribute__((aligned(16))) float Ais[RUN ? 64 * 4 : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuH[RUN ? kSB * XLD : 4];
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   constexpr int kLoad0 = kThreads - kLoaders;
   static_assert(kLoaders <= kThreads, "one 16-byte load per loader thread");
   // solve waves: the last NSW waves, none of which owns an M_mem (readout) tile; each
-  // repeats the short 16x16 inverse and then handles its own column tiles of U
+  // forms the block's 16x16 triangular system and solves it for its own 16 columns of U
   constexpr int NSW = NT;
   constexpr int SW0 = kWaves - NSW;
   static_assert(SW0 >= NT, "solve waves must not own readout tiles");
@@ -459,22 +460,28 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           }
         }
       }
-      // C2: the block's write vectors, on one wave.
+      // C2: the block's write vectors, on the NSW solve waves; wave ws = w - SW0 owns
+      // columns 16 ws .. 16 ws + 15 of U.
       //   (I + L) U = RHS,  L[t][j] = step_t P(j+1,t) (k_t . k_j) for j < t,
       //   RHS[t] = -step_t (P(0,t) G_s k_t + delta_t),  Ub[t] = P(t+1,16) U[t].
       // L is strictly lower triangular and the same for every column of RHS, so the solve
-      // is a forward substitution with one lane per column, in exact fp32: once u_j is
-      // final, every later row subtracts L[t][j] u_j.  L comes from the token Gram product
-      // on MFMA and reaches every lane through LDS, stored transposed so that column j is
-      // four broadcast reads.
-      if (w == SW0) {
-        // this wave is the block's critical path: let it win issue slots on its SIMD over
-        // the waves of the other chain sharing the CU
+      // is a forward substitution in exact fp32.  A quad of lanes shares a column and
+      // splits its rows round robin (quad lane q holds rows q, q+4, q+8, q+12): once u_j is
+      // final its holder broadcasts it over the quad by DPP, and every later row subtracts
+      // L[t][j] u_j.  Each solve wave forms L itself (token Gram product on MFMA) and keeps
+      // its own copy in LDS, laid out so that one 16-byte read gives a lane its four
+      // coefficients of column j; the solve waves never wait for one another.
+      if (w >= SW0) {
+        // these waves are the block's critical path: let them win issue slots on their
+        // SIMDs over the waves of the other chain sharing the CU
         __builtin_amdgcn_s_setprio(3);
+        const int ws = w - SW0;
+        float* const LTw = LTs + ws * (kSB * LTLD);
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         // retention products over DPP rows (they need only alpha, so they overlap the
         // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for the running
         // readout's A^T (prefix over c), and the block products P(0, t), P(t+1, 16)
+        const bool ais_wave = RUN && w == SW0;
         const float a_self = alph[c16];
         const float a_next = alph[min(c16 + 1, kSB - 1)], a_prev = alph[max(c16 - 1, 0)];
         float pj[4], pc[4], st_r[4];
@@ -483,9 +490,10 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           const int rr = 4 * g + i;
           st_r[i] = stp[rr];
           pj[i] = row16_suffix_prod(c16 + 1 < rr ? a_next : 1.f);
-          pc[i] = RUN ? row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f) : 0.f;
+          pc[i] = ais_wave ? row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f) : 0.f;
         }
         {
+          // every solve wave stores the same values; each reads back only after its own store
           const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
           const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
           if (lane < kSB) {
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           bf16x8 kh, kl;
           split8(k0, k1, kh, kl);
           gr = mma32x3(kh, kl, kh, kl, gr);
-          if (RUN) {
+          if (ais_wave) {
             f32x4 q0, q1;
             load_row_pair(Qs + c16 * LD, s, g, q0, q1);
             bf16x8 qh, ql;
@@ -512,83 +520,80 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
             aq = mma32x3(kh, kl, qh, ql, aq);
           }
         }
-        if (RUN) {
+        if (ais_wave) {
           // A^T[j][t] = P(j+1, t) (k_j . q_t) for j < t, in the accumulator layout
           f32x4 at;
 #pragma unroll
           for (int i = 0; i < 4; ++i) at[i] = 4 * g + i < c16 ? pc[i] * aq[i] : 0.f;
           *reinterpret_cast<f32x4*>(Ais + 4 * lane) = at;
         }
-        {
-          // L^T: lane (g, c16) holds L[4g+i][c16]; without the key-dependent correction the
-          // writes do not interact (L = 0)
-          f32x4 lt;
+        // L[t][j] (t = 4g+i, j = c16) goes to LTw[j][4 (t mod 4) + t / 4]; without the
+        // key-dependent correction the writes do not interact (L = 0)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * g + i;
-            lt[i] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
-          }
-          *reinterpret_cast<f32x4*>(LTs + c16 * LTLD + 4 * g) = lt;
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * g + i;
+          LTw[c16 * LTLD + 4 * i + g] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
         }
-        // RHS of a later block of a multi-block chunk: G_s k_t on MFMA, per column tile,
-        // staged token-major in Ubs (overwritten below with the write vectors)
+        // RHS of a later block of a multi-block chunk: G_s k_t on MFMA for this wave's
+        // column tile, staged token-major in Ubs (overwritten below with the write vectors)
         const bool gk_mfma = MULTI && !first && !v_nodgd;
         if (gk_mfma) {
+          const int n = ws;
+          f32x4 gk = zero4;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            f32x4 gk = zero4;
+          for (int s = 0; s < KS; ++s) {
+            f32x4 k0, k1, g0, g1;
+            load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+            load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
+            bf16x8 kh, kl, gh, gl;
+            split8(k0, k1, kh, kl);
+            split8(g0, g1, gh, gl);
+            gk = mma32x3(kh, kl, gh, gl, gk);
+          }
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              f32x4 k0, k1, g0, g1;
-              load_row_pair(Ks + c16 * LD, s, g, k0, k1);
-              load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
-              bf16x8 kh, kl, gh, gl;
-              split8(k0, k1, kh, kl);
-              split8(g0, g1, gh, gl);
-              gk = mma32x3(kh, kl, gh, gl, gk);
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int t = 4 * g + i;
+            Ubs[t * LD + n * 16 + c16] = -stp[t] * (cprev[t] * gk[i] + Dls[t * LD + n * 16 + c16]);
+          }
+        }
+        // forward substitution: column `col`, rows q + 4i of this lane
+        const int col = 16 * ws + (lane >> 2), q = lane & 3;
+        float u[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 4 * g + i;
-              Ubs[t * LD + n * 16 + c16] = -stp[t] * (cprev[t] * gk[i] + Dls[t * LD + n * 16 + c16]);
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * i + q;
+          if (gk_mfma) {
+            u[i] = Ubs[t * LD + col];
+          } else {  // G_s = I (first block) or no G_s k term (no DGD)
+            const float gk = v_nodgd ? 0.f : Ks[t * LD + col];
+            u[i] = -stp[t] * (cprev[t] * gk + Dls[t * LD + col]);
+          }
+        }
+        if (!v_nodgd) {
+          // (padding rows have zero RHS and zero L; they run through unchanged)
+#pragma unroll
+          for (int j = 0; j < kSB - 1; ++j) {
+            const f32x4 c = *reinterpret_cast<const f32x4*>(LTw + j * LTLD + 4 * q);
+            const float uj = quad_bcast(u[j >> 2], j & 3);
+#pragma unroll
+            for (int i = j >> 2; i < 4; ++i) {
+              const float nu = fmaf(-c[i], uj, u[i]);
+              u[i] = (4 * i > j || q > (j & 3)) ? nu : u[i];
             }
           }
         }
-        // forward substitution, column `lane` of U
-        if (lane < D) {
-          float u[kSB];
 #pragma unroll
-          for (int t = 0; t < kSB; ++t) {
-            if (gk_mfma) {
-              u[t] = Ubs[t * LD + lane];
-            } else {  // G_s = I (first block) or no G_s k term (no DGD)
-              const float gk = v_nodgd ? 0.f : Ks[t * LD + lane];
-              u[t] = -stp[t] * (cprev[t] * gk + Dls[t * LD + lane]);
-            }
-          }
-          if (!v_nodgd) {
-#pragma unroll
-            for (int j = 0; j < kSB - 1; ++j) {
-              const float* col = LTs + j * LTLD;  // L[.][j], broadcast to every lane
-              f32x4 c[4];
-#pragma unroll
-              for (int q = (j + 1) >> 2; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(col + 4 * q);
-#pragma unroll
-              for (int t = j + 1; t < kSB; ++t) u[t] = fmaf(-c[t >> 2][t & 3], u[j], u[t]);
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < kSB; ++t) {
-            const float ub = bco[t] * u[t];
-            if (MULTI) Ubs[t * LD + lane] = ub;
-            const __bf16 uh = (__bf16)ub;
-            UbH[t * XLD + lane] = __builtin_bit_cast(unsigned short, uh);
-            UbL[t * XLD + lane] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
-            if (RUN) {
-              const __bf16 vh = (__bf16)u[t];
-              UuH[t * XLD + lane] = __builtin_bit_cast(unsigned short, vh);
-              UuL[t * XLD + lane] = __builtin_bit_cast(unsigned short, (__bf16)(u[t] - (float)vh));
-            }
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * i + q;
+          const float ub = bco[t] * u[i];
+          if (MULTI) Ubs[t * LD + col] = ub;
+          const __bf16 uh = (__bf16)ub;
+          UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
+          UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
+          if (RUN) {
+            const __bf16 vh = (__bf16)u[i];
+            UuH[t * XLD + col] = __builtin_bit_cast(unsigned short, vh);
+            UuL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(u[i] - (float)vh));
           }
         }
         __builtin_amdgcn_s_setprio(0);

@@ -125,6 +125,20 @@ __device__ __forceinline__ float dpp_move(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                 0xF, 0xF, false));
 }
+// Value held by lane k (0-3) of each quad, in every lane of that quad (k is a constant
+// once the caller's loop is unrolled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_bcast(float v, int k) {
+  switch (k) {
+    case 0: return dpp_bcast<0x00>(v);   // quad_perm [0,0,0,0]
+    case 1: return dpp_bcast<0x55>(v);   // quad_perm [1,1,1,1]
+    case 2: return dpp_bcast<0xAA>(v);   // quad_perm [2,2,2,2]
+    default: return dpp_bcast<0xFF>(v);  // quad_perm [3,3,3,3]
+  }
+}
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_move<0x128>(v);  // row_ror:8
   v += dpp_move<0x124>(v);  // row_ror:4
