@@ -198,10 +198,21 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
     return __uint_as_float((unsigned)Xs[t * XLD + col] << 16);
   };
   const unsigned short* xg = static_cast<const unsigned short*>(p.x);
-  const float inv_h = 1.f / (float)H;
-  const bool fast_pix = N < (1 << 22);
-  auto pixel = [&](int t) {
-    return fast_pix ? route_pixel_fast(r, t, H, W, N, inv_h) : route_pixel(r, t, H, W, N);
+  // pixel of token tb + i of this route (tb the same in every lane, 0 <= i < kSB): one
+  // division per block on the scalar unit, then each lane steps from it; exact integer
+  // arithmetic, so the map is the one of route_pixel
+  auto block_pixel = [&](int tb, int i) {
+    if (r < 2) return (r & 1) ? N - 1 - tb - i : tb + i;
+    const int base = (r & 1) ? N - 1 - tb : tb;
+    int q = base / H, rem = base - q * H;
+    if (r & 1) {
+      rem -= i;
+      while (rem < 0) rem += H, --q;
+    } else {
+      rem += i;
+      while (rem >= H) rem -= H, ++q;
+    }
+    return rem * W + q;
   };
   float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
 
@@ -240,12 +251,14 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   constexpr int SW0 = kWaves - NSW;
   static_assert(SW0 >= NT, "solve waves must not own readout tiles");
   static_assert(kLoad0 >= SW0 * 64, "loader threads sit on solve waves");
-  const int ld_i = (int)threadIdx.x - kLoad0;
-  const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
-  auto fetch = [&](int tb, int nt) {
+  // (loader indices come from a per-block opaque copy of the thread index, so that no
+  // address built on them stays live across the phases)
+  auto fetch = [&](int lid, int tb, int nt) {
+    const int ld_i = lid - kLoad0;
+    const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (ld_i >= 0 && ld_t < nt) {
-      const int pix = pixel(tb + ld_t);
+      const int pix = block_pixel(tb, ld_t);
       v = *reinterpret_cast<const u32x4*>(xg + ((int64_t)b * N + pix) * Dt + (int64_t)h * D + ld_c8 * 8);
     }
     return v;
@@ -256,18 +269,20 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
     tn = tb + kSB < cend ? tb + kSB : cend;
     ntn = tn < N ? min(kSB, min((tn / C + 1) * C, N) - tn) : 0;
   };
-  auto stage_block = [&](const u32x4& v, int tb, int nt) {
+  auto stage_block = [&](int lid, const u32x4& v, int tb, int nt) {
+    const int ld_i = lid - kLoad0;
+    const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
     if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
-    if (threadIdx.x < kSB)
-      pixs[threadIdx.x] = (int)threadIdx.x < nt ? pixel(tb + threadIdx.x) : 0;
+    if (lid < kSB) pixs[lid] = lid < nt ? block_pixel(tb, lid) : 0;
   };
   u32x4 pf;
   {
+    const int lid = threadIdx.x;
     const int nt0 = min(kSB, min(C, N));
-    stage_block(fetch(0, nt0), 0, nt0);
+    stage_block(lid, fetch(lid, 0, nt0), 0, nt0);
     int tn, ntn;
     next_block(0, tn, ntn);
-    pf = fetch(tn, ntn);
+    pf = fetch(lid, tn, ntn);
   }
   lds_barrier();
 
@@ -723,10 +738,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
         int tn, ntn;
         next_block(tb, tn, ntn);
         if (ntn > 0) {
-          stage_block(pf, tn, ntn);
+          int lid2 = threadIdx.x;
+          asm volatile("" : "+v"(lid2));
+          stage_block(lid2, pf, tn, ntn);
           int tn2, ntn2;
           next_block(tn, tn2, ntn2);
-          pf = fetch(tn2, ntn2);
+          pf = fetch(lid2, tn2, ntn2);
         }
       }
       lds_barrier();

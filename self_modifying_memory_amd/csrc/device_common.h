@@ -14,23 +14,6 @@ __device__ __forceinline__ int route_pixel(int r, int t, int H, int W, int N) {
   return (t % H) * W + (t / H);      // column-major: flatten of the spatial transpose
 }
 
-// Same map without an integer division: t / H through a float reciprocal and one
-// correction step, exact for t < 2^22 (callers check N).
-__device__ __forceinline__ int route_pixel_fast(int r, int t, int H, int W, int N, float inv_h) {
-  if (r & 1) t = N - 1 - t;
-  if (r < 2) return t;
-  int q = (int)((float)t * inv_h);
-  int rem = t - q * H;
-  if (rem < 0) {
-    q -= 1;
-    rem += H;
-  } else if (rem >= H) {
-    q += 1;
-    rem -= H;
-  }
-  return rem * W + q;
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
