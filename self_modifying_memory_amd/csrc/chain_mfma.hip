@@ -107,6 +107,14 @@ __device__ __forceinline__ void split4(const f32x4 v, bf16x4& hi, bf16x4& lo) {
   lo = __builtin_bit_cast(bf16x4, l);
 }
 
+// The same k slots of a token-major bf16 row (8 values, no conversion)
+__device__ __forceinline__ bf16x8 load_row_pair_bf16(const unsigned short* row, int s, int g) {
+  const u32x2 lo4 = *reinterpret_cast<const u32x2*>(row + 32 * s + 4 * g);
+  const u32x2 hi4 = *reinterpret_cast<const u32x2*>(row + 32 * s + 16 + 4 * g);
+  const u32x4 both = {lo4[0], lo4[1], hi4[0], hi4[1]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
 // A-operand k values of step s for a token-major fp32 row: cols 32s+4g.. and 32s+16+4g..
 __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f32x4& v0, f32x4& v1) {
   v0 = *reinterpret_cast<const f32x4*>(row + 32 * s + 4 * g);
@@ -138,7 +146,6 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
   __shared__ __attribute__((aligned(16))) float Ks[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Dls[kSB * LD];
-  __shared__ __attribute__((aligned(16))) float Qs[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Ubs[MULTI ? kSB * LD : 4];
   // MFMA-ready bf16 hi/lo copies: Ub rows (A operand of S_b Ub^T) and K transposed
   // (A operand of the carry), written once by their producers instead of re-split per wave
@@ -146,6 +153,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
   __shared__ __attribute__((aligned(16))) unsigned short UbL[kSB * XLD];
   __shared__ __attribute__((aligned(16))) unsigned short KtH[D * KTLD];
   __shared__ __attribute__((aligned(16))) unsigned short KtL[D * KTLD];
+  // token-major hi/lo copies of the normalised keys and queries (operands of the token
+  // Gram products and of the readout)
+  __shared__ __attribute__((aligned(16))) unsigned short KH[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short KL[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short QH[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short QL[kSB * XLD];
   __shared__ int pixs[kSB];
   __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
   __shared__ __attribute__((aligned(16))) float alph[kSB];
@@ -334,13 +347,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
       {
         bf16x8 xa[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const unsigned short* xr = Xs + c16 * XLD + 32 * s + 4 * g;
-          const u32x2 lo4 = *reinterpret_cast<const u32x2*>(xr);
-          const u32x2 hi4 = *reinterpret_cast<const u32x2*>(xr + 16);
-          const u32x4 both = {lo4[0], lo4[1], hi4[0], hi4[1]};
-          xa[s] = __builtin_bit_cast(bf16x8, both);
-        }
+        for (int s = 0; s < KS; ++s) xa[s] = load_row_pair_bf16(Xs + c16 * XLD, s, g);
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           const int m = w + kWaves * mi;
@@ -416,14 +423,25 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           atomicAdd(&cnt_lds[2], (unsigned)((sf.bits >> 1) & 1));
         }
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const float kv = live ? kn[e] : 0.f;
-          Ks[t * LD + c16 * CPL + e] = kv;
-          Dls[t * LD + c16 * CPL + e] = live ? dl[e] : 0.f;
-          Qs[t * LD + c16 * CPL + e] = live ? qn[e] : 0.f;
-          const __bf16 kh = (__bf16)kv;
-          KtH[(c16 * CPL + e) * KTLD + t] = __builtin_bit_cast(unsigned short, kh);
-          KtL[(c16 * CPL + e) * KTLD + t] = __builtin_bit_cast(unsigned short, (__bf16)(kv - (float)kh));
+        for (int e = 0; e < CPL; e += 2) {
+          const int col = c16 * CPL + e;
+          const float k0 = live ? kn[e] : 0.f, k1 = live ? kn[e + 1] : 0.f;
+          const float q0 = live ? qn[e] : 0.f, q1 = live ? qn[e + 1] : 0.f;
+          Ks[t * LD + col] = k0;
+          Ks[t * LD + col + 1] = k1;
+          Dls[t * LD + col] = live ? dl[e] : 0.f;
+          Dls[t * LD + col + 1] = live ? dl[e + 1] : 0.f;
+          unsigned kh, kl, qh, ql;
+          split_pair(k0, k1, kh, kl);
+          split_pair(q0, q1, qh, ql);
+          *reinterpret_cast<unsigned*>(KH + t * XLD + col) = kh;
+          *reinterpret_cast<unsigned*>(KL + t * XLD + col) = kl;
+          *reinterpret_cast<unsigned*>(QH + t * XLD + col) = qh;
+          *reinterpret_cast<unsigned*>(QL + t * XLD + col) = ql;
+          KtH[col * KTLD + t] = (unsigned short)kh;
+          KtH[(col + 1) * KTLD + t] = (unsigned short)(kh >> 16);
+          KtL[col * KTLD + t] = (unsigned short)kl;
+          KtL[(col + 1) * KTLD + t] = (unsigned short)(kl >> 16);
         }
         if (c16 == 0) {
           alph[t] = live ? alpha : 1.f;
@@ -446,10 +464,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          f32x4 q0, q1;
-          load_row_pair(Qs + c16 * LD, s, g, q0, q1);
-          bf16x8 ah, al;
-          split8(q0, q1, ah, al);
+          const bf16x8 ah = load_row_pair_bf16(QH + c16 * XLD, s, g);
+          const bf16x8 al = load_row_pair_bf16(QL + c16 * XLD, s, g);
           bf16x8 sh, sl;
           if (RUN && MULTI) {  // the running state of the chunk so far
             split8(Acc[MULTI ? mi : 0][MULTI ? 2 * s : 0], Acc[MULTI ? mi : 0][MULTI ? 2 * s + 1 : 0], sh, sl);
@@ -522,16 +538,12 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
         f32x4 gr = zero4, aq = zero4;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          f32x4 k0, k1;
-          load_row_pair(Ks + c16 * LD, s, g, k0, k1);
-          bf16x8 kh, kl;
-          split8(k0, k1, kh, kl);
+          const bf16x8 kh = load_row_pair_bf16(KH + c16 * XLD, s, g);
+          const bf16x8 kl = load_row_pair_bf16(KL + c16 * XLD, s, g);
           gr = mma32x3(kh, kl, kh, kl, gr);
           if (ais_wave) {
-            f32x4 q0, q1;
-            load_row_pair(Qs + c16 * LD, s, g, q0, q1);
-            bf16x8 qh, ql;
-            split8(q0, q1, qh, ql);
+            const bf16x8 qh = load_row_pair_bf16(QH + c16 * XLD, s, g);
+            const bf16x8 ql = load_row_pair_bf16(QL + c16 * XLD, s, g);
             aq = mma32x3(kh, kl, qh, ql, aq);
           }
         }
@@ -557,11 +569,11 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           f32x4 gk = zero4;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            f32x4 k0, k1, g0, g1;
-            load_row_pair(Ks + c16 * LD, s, g, k0, k1);
+            f32x4 g0, g1;
             load_row_pair(Gs + (n * 16 + c16) * LD, s, g, g0, g1);
-            bf16x8 kh, kl, gh, gl;
-            split8(k0, k1, kh, kl);
+            const bf16x8 kh = load_row_pair_bf16(KH + c16 * XLD, s, g);
+            const bf16x8 kl = load_row_pair_bf16(KL + c16 * XLD, s, g);
+            bf16x8 gh, gl;
             split8(g0, g1, gh, gl);
             gk = mma32x3(kh, kl, gh, gl, gk);
           }
