@@ -166,7 +166,8 @@ def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS, injection: str = 
     counts (optional) accumulates, over live tokens: "updates"; "inj", tokens whose raw eta
     exceeds the injection limit (where a hard clamp binds); "spec", tokens whose eta_bar
     exceeds the spectral limit (where the clamp binds); and "inj_near" / "spec_near",
-    tokens within a relative 1e-5 of either boundary.
+    tokens within a relative counts["near_rel"] (set by the caller, default 1e-5) of
+    either boundary.
     """
     eta = np.asarray(eta, dtype=np.float64)
     eta_soft, eta_inj = soft_injection_cap(eta, alpha, delta, eps)
@@ -193,8 +194,9 @@ def executed_step(eta, alpha, k, delta, eps: float = NORM_EPS, injection: str = 
         counts["updates"] = counts.get("updates", 0) + int(eta.size)
         counts["inj"] = counts.get("inj", 0) + int(np.sum(eta > eta_inj))
         counts["spec"] = counts.get("spec", 0) + int(np.sum(eta_bar > lim))
-        counts["inj_near"] = counts.get("inj_near", 0) + int(np.sum(np.abs(eta - eta_inj) <= 1e-5 * np.abs(eta_inj)))
-        counts["spec_near"] = counts.get("spec_near", 0) + int(np.sum(np.abs(eta_bar - lim) <= 1e-5 * np.abs(lim)))
+        band = counts.get("near_rel", 1e-5)
+        counts["inj_near"] = counts.get("inj_near", 0) + int(np.sum(np.abs(eta - eta_inj) <= band * np.abs(eta_inj)))
+        counts["spec_near"] = counts.get("spec_near", 0) + int(np.sum(np.abs(eta_bar - lim) <= band * np.abs(lim)))
     return step
 
 

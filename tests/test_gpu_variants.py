@@ -2,8 +2,10 @@
 App. B.5 skip) through the C ABI against the fp64 oracle, on both scan kernels.
 
 Counters of the step controls are integers decided by floating point: the GPU decides in
-fp32, the oracle in fp64, so they must agree exactly except on tokens whose margin to the
-limit is within the oracle's 1e-5 band (counted by the oracle as *_near).
+fp32, the oracle in fp64, and the quantities compared (eta and the two limits) come from
+a state that is itself only held to the parity tolerance of the input dtype.  The counts
+must therefore agree exactly except on tokens whose margin to the limit is within that
+tolerance (counted by the oracle as *_near).
 """
 import numpy as np
 import pytest
@@ -87,7 +89,7 @@ def _run(shape, var, readout="boundary"):
     if var.get("counts"):
         counts = torch.zeros(3, dtype=torch.int64, device="cuda")
         gk["counts"] = counts
-        ok["counts"] = {}
+        ok["counts"] = {"near_rel": TOL[dt]}
     fin = torch.full((B, 4, nh, 4 * d * d + 2 * d), float("nan"), dtype=torch.float32, device="cuda")
     out = hope_scan2d_forward(x, init, nh, 15, chunk, final_memories=fin, **gk)
     torch.cuda.synchronize()
