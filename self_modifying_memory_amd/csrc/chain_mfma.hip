@@ -400,8 +400,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
           kk += kr[e] * kr[e];
           qq += qr[e] * qr[e];
         }
-        const float kinv = rsqrtf(row16_sum(kk) + gp.eps);
-        const float qinv = rsqrtf(row16_sum(qq) + gp.eps);
+        const float kinv = fast_rsqrt(row16_sum(kk) + gp.eps);
+        const float qinv = fast_rsqrt(row16_sum(qq) + gp.eps);
         float kn[CPL], dl[CPL], qn[CPL];
         float kk2 = 0.f, dd = 0.f;
 #pragma unroll

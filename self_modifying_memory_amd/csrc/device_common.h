@@ -48,10 +48,26 @@ struct TokenGates {
 // gate maps of App. C.1 Eq. 53 (eta_scale * sigmoid or softplus; alpha = sigmoid(s + bias)).
 // 1 - alpha is evaluated as e^-z sigmoid(z) = sigmoid(-z) to keep its relative accuracy
 // near alpha = 1.
-// Reciprocals and exponentials use the hardware approximations (about 1 ulp); 1 - e^-x
-// keeps expm1 for its accuracy at small x.
+// Reciprocals, square roots and exponentials use the hardware approximations (about
+// 1 ulp; with eps > 0 no argument here is denormal).
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float fast_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// 1 - e^-x for x >= 0 to a few ulp: below 1/4, where 1 - e^-x would cancel, the Taylor
+// series through x^7 (truncation below 2e-9 relative); above, the hardware exponential
+// (the subtraction then loses at most two bits).
+__device__ __forceinline__ float one_minus_exp_neg(float x) {
+  float p = fmaf(x, 1.f / 5040.f, -1.f / 720.f);
+  p = fmaf(x, p, 1.f / 120.f);
+  p = fmaf(x, p, -1.f / 24.f);
+  p = fmaf(x, p, 1.f / 6.f);
+  p = fmaf(x, p, -0.5f);
+  p = fmaf(x, p, 1.f);
+  const float series = x * p;
+  return x < 0.25f ? series : 1.f - fast_exp(-x);
+}
 
 // Variants ("VisionHOPE", Sec. 3.5 ablations): a hard clamp min(eta, eta_inj) or no
 // injection control; the smooth spectral map eta_spec (1 - exp(-eta_bar / eta_spec)) or no
@@ -69,11 +85,11 @@ __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, 
   const float ez = fast_exp(-z);
   const float alpha = fast_rcp(1.f + ez);
   const float one_minus_alpha = ez * alpha;  // sigmoid(-z), accurate near alpha = 1
-  const float rr = sqrtf(dd + g.eps * g.eps) + g.eps;
+  const float rr = fast_sqrt(dd + g.eps * g.eps) + g.eps;
   const float inj = (1.f - 1e-3f) * one_minus_alpha * fast_rcp(rr);
   float bar;
   if (g.injection == 0) {
-    bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * -expm1f(-eta * fast_rcp(inj));
+    bar = (eta == 0.f || inj == 0.f) ? 0.f : inj * one_minus_exp_neg(eta * fast_rcp(inj));
   } else {
     bar = g.injection == 1 ? fminf(eta, inj) : eta;
   }
@@ -83,7 +99,7 @@ __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, 
   if (flags) flags->bits = (eta > inj ? 1 : 0) | (bar > spec ? 2 : 0);
   if (g.spectral == 0) return fminf(bar, spec);
   if (g.spectral == 2) return bar;
-  return (bar == 0.f || spec == 0.f) ? 0.f : spec * -expm1f(-bar * fast_rcp(spec));
+  return (bar == 0.f || spec == 0.f) ? 0.f : spec * one_minus_exp_neg(bar * fast_rcp(spec));
 }
 
 // One token on one wave, lane i holding component i of the raw projections: the
