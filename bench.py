@@ -8,6 +8,9 @@ bf16 inputs, fp32 state), inputs already resident in HBM.  Prints ONE JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--no-cpu-baseline]
                   [--copy-probe-mib N]
 
+Warm-up is W untimed steps and, beyond them, as many more as it takes to keep the GPU
+busy for 0.2 s, so that the clock has settled before the K timed steps.
+
 The roofline object is that of the scan kernel: its time per launch comes from HIP
 events the library records around that kernel alone (the route sum that follows it
 is excluded), on the stream the call is enqueued on.  "traffic" is the scan kernel's
@@ -125,8 +128,8 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--sets", type=int, default=5, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -205,6 +208,14 @@ def main() -> int:
 
     for i in range(args.warmup):
         step(i)
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    i = args.warmup
+    while time.perf_counter() - t_warm < 0.2:  # clock settling, untimed
+        step(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
