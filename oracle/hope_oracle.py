@@ -232,7 +232,8 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
                eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
                control: bool = True, log: list | None = None, readout: str = "boundary",
                injection: str = "soft", spectral: str = "clamp", frozen=(), dgd: bool = True,
-               counts: dict | None = None, qs: np.ndarray | None = None):
+               counts: dict | None = None, qs: np.ndarray | None = None,
+               mem_chunk: int | None = None):
     """Run chains over ordered tokens.
 
     xs    : [n, N, d] tokens in route order
@@ -252,6 +253,11 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
     qs [n, N, d] (optional): queries given from outside in route order, the fixed outer
     query projection of [VH] App. B.5 (and Eq. 14); q_t is then qs_t normalised within the
     head like the generated one, and M_q takes no part (it stays at its initial value).
+    mem_chunk (optional) gives the working memory M_mem its own chunk length, the two
+    chunk sizes of [NLz] Sec. 2.10: M_mem's boundary state (its readout in the boundary
+    form and its self-generated targets) is refreshed at multiples of mem_chunk, the other
+    five memories' (which generate k, v, q, eta, alpha) at multiples of chunk.  None or
+    chunk: one chunk size.
     Returns (ys [n, N, d], final state dict).
     """
     for m in frozen:
@@ -261,11 +267,19 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
         raise ValueError("readout must be 'boundary' or 'running'")
     xs = np.asarray(xs, dtype=np.float64)
     n, N, d = xs.shape
+    cm = chunk if mem_chunk is None else int(mem_chunk)
+    if cm < 1:
+        raise ValueError("mem_chunk must be >= 1")
     M = {m: np.array(state[m], dtype=np.float64, copy=True) for m in MEMORIES}
     ys = np.zeros((n, N, d), dtype=np.float64)
+    Mb = {}                                               # boundary states M_b
     for s in range(0, N, chunk):
-        Mb = {m: M[m].copy() for m in MEMORIES}          # boundary states M_b
+        for m in MEMORIES:
+            if m != "mem":
+                Mb[m] = M[m].copy()
         for t in range(s, min(s + chunk, N)):
+            if t % cm == 0:                               # the working memory's own boundary
+                Mb["mem"] = M["mem"].copy()
             x = xs[:, t, :]
             k = stabilized_normalize(_matvec(Mb["k"], x), eps)
             v = _matvec(Mb["v"], x)
@@ -295,7 +309,8 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
            eps: float = NORM_EPS, init_per_image: bool = False, heads=None, images=None,
            readout: str = "boundary", injection: str = "soft", spectral: str = "clamp",
            frozen=(), dgd: bool = True, route_scales=None, skip=None,
-           shared_init: bool = False, counts: dict | None = None, queries=None):
+           shared_init: bool = False, counts: dict | None = None, queries=None,
+           mem_chunk: int = 0):
     """The whole operator: serialise, run every (image, head, route) chain, merge.
 
     x    : [B, H, W, D] (any float dtype; widened to fp64)
@@ -313,6 +328,8 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
     step-control counters of executed_step over every chain computed.
     queries [B, H, W, D] (optional): the fixed-projection queries of [VH] App. B.5, computed
     once per image and reused by every route (serialised like x, split into heads).
+    mem_chunk > 0 gives the working memory its own chunk length (srnl_chain); 0 keeps one
+    chunk size for all six memories.
     Returns (out [b, H, W, D_sel] fp64, final [b, 4, h, S] fp64, NaN for
     unselected routes).
     """
@@ -347,7 +364,7 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
                 qs = cross_scan(qsel[..., h * d:(h + 1) * d], r)
             ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout,
                                  injection=injection, spectral=spectral, frozen=frozen, dgd=dgd,
-                                 counts=counts, qs=qs)
+                                 counts=counts, qs=qs, mem_chunk=mem_chunk if mem_chunk > 0 else None)
             if skip is not None:                      # Y_r = reads + skip * Z_r  ([VH] App. B.5)
                 ys = ys + np.asarray(skip, dtype=np.float64)[h * d:(h + 1) * d] * xs
             if route_scales is not None:              # lambda_r * Y_r  ([VH] Eq. 26)

@@ -633,3 +633,84 @@ def test_fixed_query_projection_equals_generated_queries_when_they_agree():
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(fa, fb, rtol=1e-12, atol=1e-14)
     assert np.array_equal(oracle.unflatten_state(fa[0, 3, 1], d)["q"], oracle.unflatten_state(init[0, 1], d)["q"])
+
+
+# --------------------------------------------------------------------------
+# Two chunk sizes ([NLz] Sec. 2.10): the working memory M_mem keeps its boundary state
+# over chunks of its own length, the five projection memories over theirs.
+# --------------------------------------------------------------------------
+def test_two_chunk_sizes_reduce_to_one_when_equal():
+    rng = _rng(71)
+    st = _state(rng, 5, 2)
+    xs = rng.standard_normal((2, 13, 5)) * 1.2
+    for C in (1, 4, 13):
+        y1, f1 = oracle.srnl_chain(xs, st, C, eta_scale=2.0)
+        y2, f2 = oracle.srnl_chain(xs, st, C, eta_scale=2.0, mem_chunk=C)
+        assert np.array_equal(y1, y2)
+        for m in oracle.MEMORIES:
+            assert np.array_equal(f1[m], f2[m])
+
+
+@pytest.mark.parametrize("C,Cm", [(4, 3), (3, 5), (6, 2), (1, 4)])
+def test_two_chunk_sizes_scalar_head_closed_form(C, Cm):
+    # d = 1: every memory is a scalar and its chunk gain is prod A + sum_j B_j prod_{s>j} A_s
+    # (Eq. 49) over the tokens of ITS chunk, from the logged per-token scalars; M_mem groups
+    # the tokens by Cm, the other memories by C.  Its readout is M_mem at the start of the
+    # token's Cm-chunk times q_t.
+    rng = _rng(72)
+    d, N = 1, 13
+    st = _state(rng, d, 2, scale=0.8)
+    xs = rng.standard_normal((2, N, d))
+    log = []
+    ys, fin = oracle.srnl_chain(xs, st, C, eta_scale=2.0, log=log, mem_chunk=Cm)
+    for c in range(2):
+        A = [log[t]["alpha"][c] - log[t]["step"][c] * log[t]["k"][c, 0] ** 2 for t in range(N)]
+        Bv = [-log[t]["step"][c] * log[t]["delta"][c, 0] * log[t]["k"][c, 0] for t in range(N)]
+
+        def run(m0, L, upto):
+            # the memory after `upto` tokens, chunked by L, and its value at each boundary
+            val, bound = m0, {}
+            for s in range(0, upto, L):
+                ts = list(range(s, min(s + L, upto)))
+                bound[s] = val
+                val *= math.prod(A[t] for t in ts) + sum(
+                    Bv[j] * math.prod(A[t] for t in ts[i + 1:]) for i, j in enumerate(ts))
+            return val, bound
+
+        for m in oracle.MEMORIES:
+            L = Cm if m == "mem" else C
+            want, _ = run(float(st[m][c, 0, 0]), L, N)
+            assert fin[m][c, 0, 0] == pytest.approx(want, rel=1e-12, abs=1e-300)
+        # readout: q_t from M_q at the start of the token's C-chunk, read by M_mem at the
+        # start of its Cm-chunk
+        _, qb = run(float(st["q"][c, 0, 0]), C, N)
+        _, mb = run(float(st["mem"][c, 0, 0]), Cm, N)
+        for t in range(N):
+            z = qb[(t // C) * C] * xs[c, t, 0]
+            q = z / math.sqrt(z * z + 1e-6)
+            assert ys[c, t, 0] == pytest.approx(mb[(t // Cm) * Cm] * q, rel=1e-12, abs=1e-300)
+
+
+@pytest.mark.parametrize("C,Cm", [(3, 5), (5, 2), (4, 4)])
+def test_two_chunk_sizes_zero_step_decay(C, Cm):
+    # eta = 0: every memory is its initial value times the running product of alpha.  The
+    # projections (so alpha and q) come from the retention and query memories at the start
+    # of the token's C-chunk; the readout from M_mem at the start of its Cm-chunk.
+    rng = _rng(73)
+    d, N, n = 4, 13, 2
+    st = _state(rng, d, n)
+    xs = rng.standard_normal((n, N, d))
+    ys, fin = oracle.srnl_chain(xs, st, C, eta_scale=0.0, alpha_bias=2.0, mem_chunk=Cm)
+    for c in range(n):
+        decay = [1.0]                                   # decay[t]: product of alpha_s, s < t
+        for t in range(N):
+            b = (t // C) * C
+            s_a = decay[b] * float(st["alpha"][c, 0] @ xs[c, t]) + 2.0
+            decay.append(decay[t] / (1.0 + math.exp(-s_a)))
+        for t in range(N):
+            q = decay[(t // C) * C] * (st["q"][c] @ xs[c, t])
+            q = q / math.sqrt(float(q @ q) + 1e-6)
+            want = decay[(t // Cm) * Cm] * (st["mem"][c] @ q)
+            np.testing.assert_allclose(ys[c, t], want, rtol=1e-12)
+        for m in oracle.MEMORIES:
+            np.testing.assert_allclose(fin[m][c], decay[N] * st[m][c], rtol=1e-12)
