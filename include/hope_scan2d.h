@@ -147,6 +147,14 @@ typedef struct {
                                 once per image and shared by all routes; q_t is the route-
                                 ordered head slice, normalised within the head, and M_q takes
                                 no part (it is left at its initial value) */
+  int32_t mem_chunk;         /* 0 (default): one chunk length for all six memories.  > 0: the
+                                working memory M_mem keeps its boundary state over chunks of
+                                this many tokens ("Nested Learning", two chunk sizes, one for
+                                the working memory and one for the projection memories): its
+                                boundary readout and its self-generated targets use M_mem at
+                                the start of the token's mem_chunk-chunk, while k, v, q, eta and
+                                alpha come from the other memories at the start of its chunk-
+                                chunk.  Runs on the fp32 chain kernel.  < 0: invalid */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

@@ -49,7 +49,8 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("counts", ctypes.c_void_p), ("injection", ctypes.c_int32),
                 ("spectral", ctypes.c_int32), ("frozen", ctypes.c_uint32),
                 ("no_dgd", ctypes.c_int32), ("shared_init", ctypes.c_int32),
-                ("queries_dtype", ctypes.c_int32), ("queries", ctypes.c_void_p)]
+                ("queries_dtype", ctypes.c_int32), ("queries", ctypes.c_void_p),
+                ("mem_chunk", ctypes.c_int32)]
 
 
 _lib = None

@@ -70,6 +70,7 @@ hope_status_t check_opts(const hope_scan2d_opts_t* o) {
   if (o->injection < HOPE_INJECTION_SOFT || o->injection > HOPE_INJECTION_NONE) return HOPE_ERR_INVALID_ARG;
   if (o->spectral < HOPE_SPECTRAL_CLAMP || o->spectral > HOPE_SPECTRAL_NONE) return HOPE_ERR_INVALID_ARG;
   if (o->frozen & ~7u) return HOPE_ERR_INVALID_ARG;
+  if (o->mem_chunk < 0) return HOPE_ERR_INVALID_ARG;
   if (o->no_dgd != 0 && o->no_dgd != 1) return HOPE_ERR_INVALID_ARG;
   if (o->shared_init != 0 && o->shared_init != 1) return HOPE_ERR_INVALID_ARG;
   if (o->shared_init && o->init_per_image) return HOPE_ERR_INVALID_ARG;
@@ -218,6 +219,7 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   p.shared_init = o.shared_init;
   p.queries = o.queries;
   p.queries_bf16 = o.queries_dtype == HOPE_BF16;
+  p.mem_chunk = o.mem_chunk;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;

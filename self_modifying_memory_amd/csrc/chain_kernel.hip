@@ -8,7 +8,10 @@
 //   Sec. 2.2 Eq. 19-20   executed step (soft injection cap, spectral clamp) with the
 //                        App. B.3 inward factors, |k|^2 floor and one-ulp rounding;
 //   App. B.4 Eq. 46      one gain G per chunk, G_t = alpha_t G_{t-1} - step_t (G_{t-1} k_t
-//                        + delta_t) k_t^T, shared by all six memories: S_end = S_b G_C.
+//                        + delta_t) k_t^T, shared by all six memories: S_end = S_b G_C;
+//   "Nested Learning"    two chunk sizes (one for the working memory, one for the
+//                        projection memories): M_mem then carries a second gain of the same
+//                        recurrence, reset at its own boundaries.
 //
 // Layout: the fp32 state (4d+2 rows of d: M_mem, M_k, M_v, M_q, m_eta, m_alpha) stays
 // in LDS for the whole sequence; tokens are processed in blocks of kTB; each thread
@@ -44,6 +47,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   __shared__ float X[kTB * SP];
   __shared__ float P[kTB * PS];
   __shared__ float Gl[D * SP];
+  __shared__ float Glm[D * SP];   // the working memory's gain (two chunk sizes)
   __shared__ float Wq[kTB * SP];  // running readout: w_t = G_{t-1} q_t per token
   const bool running = p.readout != 0;
 
@@ -57,6 +61,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   const int r = p.route_of_slot[slot];
   const int H = p.H, W = p.W, N = H * W, Dt = p.D;
   const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
+  const int Cm = p.mem_chunk > 0 ? p.mem_chunk : C;  // the working memory's chunk length
+  const bool two = Cm != C;
   const int64_t SS = 4 * D * D + 2 * D;
 
   float* dst = slot == 0 ? p.out : p.planes + (int64_t)(slot - 1) * p.plane_stride;
@@ -75,11 +81,21 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
   };
   __syncthreads();
 
-  for (int s0 = 0; s0 < N; s0 += C) {
-    const int s1 = min(s0 + C, N);
-    float g[CPT];
+  // Segments run to the next boundary of either chunk grid; g is the gain of the memories
+  // on the projection grid (all six with one chunk size), gm that of M_mem on its own.
+  float g[CPT], gm[CPT];
+  for (int s0 = 0; s0 < N;) {
+    const int end_p = min((s0 / C + 1) * C, N);
+    const int end_m = two ? min((s0 / Cm + 1) * Cm, N) : end_p;
+    const int s1 = min(end_p, end_m);
+    if (s0 % C == 0) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) g[c] = (gcol0 + c == grow) ? 1.f : 0.f;
+      for (int c = 0; c < CPT; ++c) g[c] = (gcol0 + c == grow) ? 1.f : 0.f;
+    }
+    if (two && s0 % Cm == 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) gm[c] = (gcol0 + c == grow) ? 1.f : 0.f;
+    }
 
     for (int tb = s0; tb < s1; tb += kTB) {
       const int nt = min(kTB, s1 - tb);
@@ -150,15 +166,17 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
       // shared gain, token by token (Eq. 46)
       for (int t = 0; t < nt; ++t) {
         const float* pt = &P[t * PS];
-        float w = 0.f, wq = 0.f;
+        float w = 0.f, wm = 0.f, wq = 0.f;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
           w = fmaf(g[c], pt[gcol0 + c], w);
-          if (running) wq = fmaf(g[c], pt[2 * D + gcol0 + c], wq);
+          if (two) wm = fmaf(gm[c], pt[gcol0 + c], wm);
+          if (running) wq = fmaf(two ? gm[c] : g[c], pt[2 * D + gcol0 + c], wq);
         }
 #pragma unroll
         for (int off = TPR / 2; off >= 1; off >>= 1) {
           w += __shfl_xor(w, off, 64);
+          if (two) wm += __shfl_xor(wm, off, 64);
           if (running) wq += __shfl_xor(wq, off, 64);
         }
         if (running && tid % TPR == 0) Wq[t * SP + grow] = wq;
@@ -166,6 +184,11 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         const float u = -step * (p.no_dgd ? pt[D + grow] : w + pt[D + grow]);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) g[c] = fmaf(alpha, g[c], u * pt[gcol0 + c]);
+        if (two) {
+          const float um = -step * (p.no_dgd ? pt[D + grow] : wm + pt[D + grow]);
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) gm[c] = fmaf(alpha, gm[c], um * pt[gcol0 + c]);
+        }
       }
       __syncthreads();
       if (running) {
@@ -173,26 +196,23 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         __syncthreads();
       }
     }
-    // carry: S <- S_b G_C for all six memories at once
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) Gl[grow * SP + gcol0 + c] = g[c];
-    __syncthreads();
-    {
-      // rows are independent, so the product runs in passes of kRB rows per
-      // thread; a barrier separates each pass's reads from its in-place writes
+    // carry S <- S_b G at the end of a chunk: rows [rb, re) with the gain in Gs.  Rows are
+    // independent, so the product runs in passes of kRB rows per thread; a barrier
+    // separates each pass's reads from its in-place writes
+    auto carry = [&](const float* Gs, int rb, int re) {
       constexpr int kRB = 8;
       const int col = tid % D, grp = tid / D;
       float gc[D];
 #pragma unroll
-      for (int j = 0; j < D; ++j) gc[j] = Gl[j * SP + col];
+      for (int j = 0; j < D; ++j) gc[j] = Gs[j * SP + col];
 #pragma unroll 1
-      for (int r0 = 0; r0 < R; r0 += kRB * NG) {
+      for (int r0 = rb; r0 < re; r0 += kRB * NG) {
         float acc[kRB];
 #pragma unroll
         for (int k = 0; k < kRB; ++k) {
           const int row = r0 + grp + k * NG;
           float a = 0.f;
-          if (row < R) {
+          if (row < re) {
             const float* srow = &S[row * SP];
 #pragma unroll
             for (int j = 0; j < D; ++j) a = fmaf(srow[j], gc[j], a);
@@ -203,11 +223,26 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
 #pragma unroll
         for (int k = 0; k < kRB; ++k) {
           const int row = r0 + grp + k * NG;
-          if (row < R && !frozen_row(row)) S[row * SP + col] = acc[k];
+          if (row < re && !frozen_row(row)) S[row * SP + col] = acc[k];
         }
       }
+    };
+    const bool carry_p = s1 == end_p, carry_m = s1 == end_m;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) Gl[grow * SP + gcol0 + c] = g[c];
+    if (two) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) Glm[grow * SP + gcol0 + c] = gm[c];
     }
     __syncthreads();
+    if (!two) {
+      carry(Gl, 0, R);  // all six memories at once
+    } else {
+      if (carry_m) carry(Glm, 0, D);  // M_mem at its own boundary
+      if (carry_p) carry(Gl, D, R);   // the projection memories at theirs
+    }
+    __syncthreads();
+    s0 = s1;
   }
 
   if (p.final_mem) {

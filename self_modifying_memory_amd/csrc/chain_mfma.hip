@@ -795,6 +795,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma
 
 bool mfma_path_supported(const ChainParams& p, int d) {
   if (!p.x_bf16) return false;
+  if (p.mem_chunk > 0) return false;  // two chunk sizes: the fp32 kernel
   if (d == 32) return true;
   if (d != 64) return false;
   for (int s = 0; s < p.n_sel; ++s) {

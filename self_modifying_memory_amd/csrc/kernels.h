@@ -35,6 +35,7 @@ struct ChainParams {
   int shared_init;               // 1: init is [nh][S] for every route
   const void* queries;           // [B][H][W][D] queries of a fixed projection, or nullptr
   int queries_bf16;
+  int mem_chunk;                 // 0: one chunk length; > 0: the working memory's own
 };
 
 // Raw query component c of pixel pix of image b (fixed-projection variant).

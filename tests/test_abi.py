@@ -53,14 +53,15 @@ def test_struct_layout_matches_c():
 #include <stddef.h>
 #include "hope_scan2d.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
          offsetof(hope_fmap_t, dtype), offsetof(hope_fmap_t, n_heads),
          offsetof(hope_scan2d_opts_t, final_memories), offsetof(hope_scan2d_opts_t, workspace_bytes),
          offsetof(hope_scan2d_opts_t, eta_map), offsetof(hope_scan2d_opts_t, eta_scale),
          offsetof(hope_scan2d_opts_t, eps), offsetof(hope_scan2d_opts_t, init_per_image),
          offsetof(hope_scan2d_opts_t, out_dtype), offsetof(hope_scan2d_opts_t, scan_begin),
          offsetof(hope_scan2d_opts_t, scan_end), offsetof(hope_scan2d_opts_t, readout),
-         offsetof(hope_scan2d_opts_t, reserved));
+         offsetof(hope_scan2d_opts_t, reserved), offsetof(hope_scan2d_opts_t, queries),
+         offsetof(hope_scan2d_opts_t, mem_chunk));
   return 0;
 }
 """
@@ -78,7 +79,8 @@ int main(void) {
     want = [ctypes.sizeof(F), ctypes.sizeof(O), F.dtype.offset, F.n_heads.offset,
             O.final_memories.offset, O.workspace_bytes.offset, O.eta_map.offset, O.eta_scale.offset,
             O.eps.offset, O.init_per_image.offset, O.out_dtype.offset, O.scan_begin.offset,
-            O.scan_end.offset, O.readout.offset, O.reserved.offset]
+            O.scan_end.offset, O.readout.offset, O.reserved.offset, O.queries.offset,
+            O.mem_chunk.offset]
     assert vals == want
 
 
@@ -186,6 +188,8 @@ def test_variant_option_errors(lib):
     x = fmap()
     ws = lib.hope_scan2d_workspace_size(ctypes.byref(x), 15, 0, None)
     base = dict(workspace=FAKE + (3 << 30), workspace_bytes=ws)
+    # a negative working-memory chunk length
+    assert call(lib, x, o=opts(lib, mem_chunk=-1, **base)) == N.HOPE_ERR_INVALID_ARG
     # shared and per-image initial states exclude each other
     assert call(lib, x, o=opts(lib, shared_init=1, init_per_image=1, **base)) == N.HOPE_ERR_INVALID_ARG
     # scales / skip / counters overlapping out
