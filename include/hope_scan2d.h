@@ -199,6 +199,46 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
 size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                   const hope_scan2d_opts_t* opts);
 
+/*
+ * hope_scan2d_backward -- gradients of a scalar loss L(out) of hope_scan2d_forward with
+ * respect to the feature map and the initial memories: the outer gradients through the
+ * explicit, differentiable memory trajectory ("VisionHOPE: Visual Backbones as
+ * Self-Modifying Learning Systems", Sec. 1; forward as in Sec. 2.1.3 Eq. 15-16, Sec. 2.2
+ * Eq. 19-20, App. B.4 Eq. 46).  The forward is recomputed inside the call (chunk-boundary
+ * states are checkpointed in the workspace); nothing from a forward call is needed.
+ *
+ *   x, init_memories, dirs, chunk   as for hope_scan2d_forward.
+ *   grad_out       device fp32 [B][H][W][D], dL/dout, 16-byte aligned.
+ *   grad_x         device fp32 [B][H][W][D], 16-byte aligned, overwritten with dL/dx
+ *                  (for a bf16 map: the gradient with respect to the bf16 values).
+ *   grad_init      device fp32 shaped like init_memories ([4][n_heads][S(d)], or
+ *                  [B][4][n_heads][S(d)] with init_per_image), overwritten with
+ *                  dL/dinit; rows of unselected routes are set to zero.
+ *   opts           NULL = defaults.  Honoured: stream, workspace, eta_map, eta_scale,
+ *                  alpha_bias, eps, init_per_image.  A workspace is always required
+ *                  (hope_scan2d_backward_workspace_size).
+ * Where the step of Eq. 20 is not differentiable: min(eta_bar, eta_spec) follows
+ * eta_bar when eta_bar <= eta_spec; no derivative through the |k|^2 floor or the one-ulp
+ * rounding of eta_spec; eta_bar = 0 (eta = 0 or eta_inj = 0) has derivative zero.
+ * Errors: as hope_scan2d_forward for the shared arguments; HOPE_ERR_INVALID_ARG when
+ * grad_out, grad_x or grad_init is null, misaligned or overlaps another argument;
+ * HOPE_ERR_UNSUPPORTED for d not in {16, 32, 64}, a chunk (after clipping to H*W)
+ * longer than 128 tokens (32 at d = 64), or any option outside the honoured set away
+ * from its default (running readout, variants, two chunk sizes, final_memories, bf16
+ * out); HOPE_ERR_WORKSPACE; HOPE_ERR_HIP.  Deterministic: per-route map gradients and
+ * per-image state gradients are summed in a fixed order.
+ */
+hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memories,
+                                   uint32_t dirs, int32_t chunk, const float* grad_out,
+                                   float* grad_x, float* grad_init,
+                                   const hope_scan2d_opts_t* opts);
+
+/* Bytes of workspace hope_scan2d_backward needs: the map-gradient planes of the routes
+ * beyond the first, plus per chain the checkpoints of every chunk-boundary state, the
+ * state adjoint and one chunk's gain trajectory; 0 for arguments it would reject. */
+size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                           const hope_scan2d_opts_t* opts);
+
 /* Static, human-readable name of a status code. */
 const char* hope_status_string(hope_status_t status);
 

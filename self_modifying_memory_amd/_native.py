@@ -73,6 +73,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hope_scan2d_workspace_size.argtypes = [P(hope_fmap_t), ctypes.c_uint32, ctypes.c_int32,
                                                P(hope_scan2d_opts_t)]
     lib.hope_scan2d_workspace_size.restype = ctypes.c_size_t
+    lib.hope_scan2d_backward.argtypes = [P(hope_fmap_t), ctypes.c_void_p, ctypes.c_uint32,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, P(hope_scan2d_opts_t)]
+    lib.hope_scan2d_backward.restype = ctypes.c_int
+    lib.hope_scan2d_backward_workspace_size.argtypes = [P(hope_fmap_t), ctypes.c_uint32, ctypes.c_int32,
+                                                        P(hope_scan2d_opts_t)]
+    lib.hope_scan2d_backward_workspace_size.restype = ctypes.c_size_t
     lib.hope_status_string.argtypes = [ctypes.c_int]
     lib.hope_status_string.restype = ctypes.c_char_p
     lib.hope_last_hip_error.argtypes = []

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/hope_scan2d.h: argument validation
 // (all of it before anything is enqueued), workspace accounting and kernel dispatch.
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -98,6 +99,45 @@ hope_status_t hip_status(hipError_t e) {
   if (e == hipSuccess) return HOPE_OK;
   g_last_hip_error = (int)e;
   return HOPE_ERR_HIP;
+}
+
+// Backward workspace: map-gradient planes of the selected routes beyond the first, then
+// chain_floats per chain (n_sel * B * n_heads chains, in launch order).
+struct BackLayout {
+  int n_sel;
+  int64_t plane_stride, planes_floats, chain_floats, nck, cmax;
+};
+
+BackLayout backward_layout(const hope_fmap_t* x, uint32_t dirs, int32_t chunk) {
+  BackLayout L{};
+  int route_of_slot[4];
+  L.n_sel = slots_of(dirs, route_of_slot);
+  const int d = x->D / x->n_heads;
+  const int64_t N = (int64_t)x->H * x->W;
+  for (int s = 0; s < L.n_sel; ++s) {
+    const int r = route_of_slot[s];
+    const int64_t C = chunk > 0 ? chunk : (r < 2 ? x->W : x->H);
+    L.nck = std::max<int64_t>(L.nck, (N + C - 1) / C);
+    L.cmax = std::max<int64_t>(L.cmax, std::min<int64_t>(C, N));
+  }
+  const int64_t SS = 4LL * d * d + 2LL * d;
+  L.chain_floats = ((L.nck + 1) * SS + L.cmax * d * d + 63) / 64 * 64;
+  L.plane_stride = plane_stride_elems((int64_t)x->B * x->H * x->W * x->D);
+  L.planes_floats = (int64_t)(L.n_sel - 1) * L.plane_stride;
+  return L;
+}
+
+size_t backward_workspace_bytes(const hope_fmap_t* x, const BackLayout& L) {
+  const int64_t chains = (int64_t)L.n_sel * x->B * x->n_heads;
+  return (size_t)(L.planes_floats + chains * L.chain_floats) * sizeof(float);
+}
+
+// options the backward pass honours: everything else must be at its default
+bool backward_opts_supported(const hope_scan2d_opts_t& o) {
+  return o.readout == HOPE_READOUT_BOUNDARY && !o.route_scales && !o.skip && !o.counts &&
+         o.injection == HOPE_INJECTION_SOFT && o.spectral == HOPE_SPECTRAL_CLAMP && o.frozen == 0 &&
+         o.no_dgd == 0 && o.shared_init == 0 && !o.queries && o.mem_chunk == 0 && !o.final_memories &&
+         o.out_dtype == HOPE_F32;
 }
 
 }  // namespace
@@ -234,6 +274,86 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
   if (p.n_sel == 1) return st;
   return hip_status(
       hope::launch_plane_sum(static_cast<float*>(out), p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
+}
+
+size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                           const hope_scan2d_opts_t* opts) {
+  (void)opts;
+  if (check_fmap(x) != HOPE_OK || dirs == 0 || dirs > 15 || chunk < 0) return 0;
+  return backward_workspace_bytes(x, backward_layout(x, dirs, chunk));
+}
+
+hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memories,
+                                   uint32_t dirs, int32_t chunk, const float* grad_out,
+                                   float* grad_x, float* grad_init,
+                                   const hope_scan2d_opts_t* opts) {
+  hope_scan2d_opts_t o;
+  if (opts) {
+    o = *opts;
+  } else {
+    hope_scan2d_default_opts(&o);
+  }
+  hope_status_t st = check_fmap(x);
+  if (st != HOPE_OK) return st;
+  if ((st = check_opts(&o)) != HOPE_OK) return st;
+  if (!init_memories || !grad_out || !grad_x || !grad_init) return HOPE_ERR_INVALID_ARG;
+  if (!aligned(init_memories, 16) || !aligned(grad_out, 16) || !aligned(grad_x, 16) || !aligned(grad_init, 16))
+    return HOPE_ERR_INVALID_ARG;
+  if (dirs == 0 || dirs > 15 || chunk < 0) return HOPE_ERR_INVALID_ARG;
+
+  const int d = x->D / x->n_heads;
+  const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
+  const size_t x_bytes = (size_t)n_elem * (x->dtype == HOPE_BF16 ? 2 : 4);
+  const size_t map_bytes = (size_t)n_elem * sizeof(float);
+  const size_t state_floats = (size_t)4 * d * d + 2 * (size_t)d;
+  const size_t init_bytes = (o.init_per_image ? (size_t)x->B : 1) * 4 * (size_t)x->n_heads * state_floats * sizeof(float);
+  const Range r_gx = range_of(grad_x, map_bytes), r_gi = range_of(grad_init, init_bytes);
+  const Range r_go = range_of(grad_out, map_bytes), r_x = range_of(x->data, x_bytes);
+  const Range r_init = range_of(init_memories, init_bytes);
+  if (overlaps(r_gx, r_x) || overlaps(r_gx, r_init) || overlaps(r_gx, r_go) || overlaps(r_gx, r_gi) ||
+      overlaps(r_gi, r_x) || overlaps(r_gi, r_init) || overlaps(r_gi, r_go))
+    return HOPE_ERR_INVALID_ARG;
+  if (!backward_opts_supported(o)) return HOPE_ERR_UNSUPPORTED;
+  if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
+  const BackLayout L = backward_layout(x, dirs, chunk);
+  if (L.cmax > hope::backward_max_chunk(d)) return HOPE_ERR_UNSUPPORTED;
+  const size_t ws_need = backward_workspace_bytes(x, L);
+  if (!o.workspace || o.workspace_bytes < ws_need) return HOPE_ERR_WORKSPACE;
+  const Range r_ws = range_of(o.workspace, o.workspace_bytes);
+  if (overlaps(r_ws, r_gx) || overlaps(r_ws, r_gi) || overlaps(r_ws, r_go) || overlaps(r_ws, r_x) ||
+      overlaps(r_ws, r_init))
+    return HOPE_ERR_INVALID_ARG;
+  if ((int64_t)L.n_sel * x->B * x->n_heads > INT32_MAX) return HOPE_ERR_INVALID_ARG;
+
+  hope::BackParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x->data;
+  p.init = init_memories;
+  p.grad_out = grad_out;
+  p.grad_x = grad_x;
+  p.planes = static_cast<float*>(o.workspace);
+  p.chain_ws = static_cast<float*>(o.workspace) + L.planes_floats;
+  p.plane_stride = L.plane_stride;
+  p.chain_floats = L.chain_floats;
+  p.nck = L.nck;
+  p.x_bf16 = x->dtype == HOPE_BF16;
+  p.B = x->B;
+  p.H = x->H;
+  p.W = x->W;
+  p.D = x->D;
+  p.nh = x->n_heads;
+  p.n_sel = slots_of(dirs, p.route_of_slot);
+  p.chunk = chunk;
+  p.init_per_image = o.init_per_image;
+  p.eta_map = o.eta_map;
+  p.eta_scale = o.eta_scale;
+  p.alpha_bias = o.alpha_bias;
+  p.eps = o.eps;
+
+  hipStream_t s = o.stream;
+  st = hip_status(hope::launch_chain_backward(p, d, grad_init, s));
+  if (st != HOPE_OK || p.n_sel == 1) return st;
+  return hip_status(hope::launch_plane_sum(grad_x, p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
 }
 
 const char* hope_status_string(hope_status_t status) {

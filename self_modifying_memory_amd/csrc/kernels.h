@@ -51,6 +51,31 @@ __host__ __device__ inline int64_t init_offset(const ChainParams& p, int b, int 
   return (p.init_per_image ? ((int64_t)b * 4 + r) * p.nh + h : (int64_t)r * p.nh + h) * SS;
 }
 
+// Backward pass, one chain per workgroup (fp32).  Per chain the workspace holds nck
+// checkpoints of the state, the state adjoint and the gain trajectory of one chunk:
+// chain_floats >= (nck + 1) * (4d^2 + 2d) + min(C, N) * d^2.
+struct BackParams {
+  const void* x;          // [B][H][W][D], fp32 or bf16
+  const float* init;      // [4][nh][S] or [B][4][nh][S]
+  const float* grad_out;  // [B][H][W][D] fp32
+  float* grad_x;          // [B][H][W][D] fp32: plane of slot 0
+  float* planes;          // slots 1..n_sel-1 of the map adjoint
+  float* chain_ws;        // per-chain workspace, chain_floats apart
+  int64_t plane_stride, chain_floats, nck;
+  int x_bf16;
+  int B, H, W, D, nh;
+  int n_sel;
+  int route_of_slot[4];
+  int chunk;              // 0 = aligned
+  int init_per_image;
+  int eta_map;
+  float eta_scale, alpha_bias, eps;
+};
+// longest chunk the backward kernel holds in LDS
+__host__ __device__ constexpr int backward_max_chunk(int d) { return d == 64 ? 32 : 128; }
+// writes grad_x (slot 0 plane) and the route planes, then grad_init; the caller adds the planes
+hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, hipStream_t stream);
+
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
 

@@ -199,6 +199,51 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     return out
 
 
+def hope_scan2d_backward_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15,
+                                        chunk: int = 0) -> int:
+    lib = N.load_library()
+    fm = make_fmap(x, n_heads)
+    return int(lib.hope_scan2d_backward_workspace_size(ctypes.byref(fm), dirs, chunk, None))
+
+
+def hope_scan2d_backward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: int,
+                         grad_out: torch.Tensor, dirs: int = 15, chunk: int = 0, *, stream=None,
+                         eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
+                         eps: float = 1e-6, init_per_image: bool = False,
+                         grad_x: torch.Tensor | None = None, grad_init: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None):
+    """Gradients of sum(grad_out * hope_scan2d_forward(x, init_memories, ...)) with respect
+    to x and init_memories; returns (grad_x, grad_init), float32, shaped like x and
+    init_memories.  A workspace is allocated through torch when none is given."""
+    lib = N.load_library()
+    _require_device(x, "x")
+    _require_device(init_memories, "init_memories")
+    _require_device(grad_out, "grad_out")
+    if init_memories.dtype != torch.float32 or not init_memories.is_contiguous():
+        raise TypeError("init_memories must be a contiguous float32 tensor")
+    if grad_out.dtype != torch.float32 or not grad_out.is_contiguous() or tuple(grad_out.shape) != tuple(x.shape):
+        raise ValueError("grad_out must be a contiguous float32 tensor shaped like x")
+    if grad_x is None:
+        grad_x = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    if grad_init is None:
+        grad_init = torch.empty_like(init_memories)
+    for t, name in ((grad_x, "grad_x"), (grad_init, "grad_init")):
+        _require_device(t, name)
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if workspace is None:
+        nbytes = hope_scan2d_backward_workspace_size(x, n_heads, dirs, chunk)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    fm = make_fmap(x, n_heads)
+    opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, None, workspace)
+    st = lib.hope_scan2d_backward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
+                                  grad_out.data_ptr(), grad_x.data_ptr(), grad_init.data_ptr(),
+                                  ctypes.byref(opts))
+    if st != N.HOPE_OK:
+        raise HopeError(st, "hope_scan2d_backward")
+    return grad_x, grad_init
+
+
 def hope_debug_cross_scan(x: torch.Tensor, dirs: int = 15, routes: torch.Tensor | None = None,
                           stream=None) -> torch.Tensor:
     """routes[slot, b, t, c] = x[b, p_r(t), c] for the selected routes (bit-exact)."""

@@ -39,7 +39,7 @@ def call(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, out=FAKE + (2 << 30), 
 
 def test_every_declared_function_is_exported(lib):
     names = N.header_functions()
-    assert "hope_scan2d_forward" in names and len(names) == 7
+    assert "hope_scan2d_forward" in names and "hope_scan2d_backward" in names and len(names) == 9
     for n in names:
         assert hasattr(lib, n), n
 
@@ -198,3 +198,57 @@ def test_variant_option_errors(lib):
         assert call(lib, x, o=opts(lib, **{k: out}, **base)) == N.HOPE_ERR_INVALID_ARG, k
     # counters overlapping the workspace
     assert call(lib, x, o=opts(lib, counts=FAKE + (3 << 30) + 64, **base)) == N.HOPE_ERR_INVALID_ARG
+
+
+def bcall(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, gout=FAKE + (2 << 30),
+          gx=FAKE + (4 << 30), gi=FAKE + (5 << 30), o=None):
+    return lib.hope_scan2d_backward(ctypes.byref(x), init, dirs, chunk, gout, gx, gi,
+                                    ctypes.byref(o) if o is not None else None)
+
+
+def test_backward_workspace_size(lib):
+    x = fmap(B=2, H=4, W=5, D=32, nh=1)          # d = 32, S = 4160, N = 20
+    # aligned chunks: rows of 5 (4 chunks), columns of 4 (5 chunks) -> 5 checkpoints
+    per_chain = (5 + 1) * 4160 + 5 * 32 * 32
+    per_chain = (per_chain + 63) // 64 * 64
+    n_elem = 2 * 4 * 5 * 32
+    plane = (n_elem + 63) // 64 * 64
+    want = (3 * plane + 4 * 2 * 1 * per_chain) * 4
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, 0, None) == want
+    # route 0 alone: no planes, two chains of 4 row chunks of 5 tokens
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 1, 0, None) == \
+        (2 * (((4 + 1) * 4160 + 5 * 1024 + 63) // 64 * 64)) * 4
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 0, 0, None) == 0
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, -1, None) == 0
+
+
+def test_backward_argument_errors(lib):
+    x = fmap()
+    ws = lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, 0, None)
+    base = dict(workspace=FAKE + (8 << 30), workspace_bytes=ws)
+    o = opts(lib, **base)
+    assert bcall(lib, x, gout=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert bcall(lib, x, gx=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert bcall(lib, x, gi=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    assert bcall(lib, x, gx=FAKE + 8, o=o) == N.HOPE_ERR_INVALID_ARG      # misaligned
+    assert bcall(lib, x, gx=FAKE, o=o) == N.HOPE_ERR_INVALID_ARG          # grad_x over x
+    assert bcall(lib, x, gi=FAKE + (2 << 30), o=o) == N.HOPE_ERR_INVALID_ARG  # grad_init over grad_out
+    assert bcall(lib, x, dirs=0, o=o) == N.HOPE_ERR_INVALID_ARG
+    # a workspace is always needed
+    assert bcall(lib, x, o=opts(lib)) == N.HOPE_ERR_WORKSPACE
+    assert bcall(lib, x, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=ws - 4)) == N.HOPE_ERR_WORKSPACE
+    # options outside the honoured set
+    for kw in (dict(readout=N.HOPE_READOUT_RUNNING), dict(no_dgd=1), dict(mem_chunk=3),
+               dict(injection=1), dict(spectral=2), dict(frozen=1), dict(final_memories=FAKE + (6 << 30)),
+               dict(out_dtype=N.HOPE_BF16)):
+        assert bcall(lib, x, o=opts(lib, **kw, **base)) == N.HOPE_ERR_UNSUPPORTED, kw
+    # head dimension and chunk length limits
+    assert bcall(lib, fmap(D=8, nh=1), o=o) == N.HOPE_ERR_UNSUPPORTED
+    big = fmap(B=1, H=2, W=200, D=32, nh=1)
+    wsb = lib.hope_scan2d_backward_workspace_size(ctypes.byref(big), 1, 0, None)
+    assert bcall(lib, big, dirs=1, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=wsb)) == \
+        N.HOPE_ERR_UNSUPPORTED                                            # rows of 200 > 128
+    d64 = fmap(B=1, H=4, W=40, D=64, nh=1)
+    wsd = lib.hope_scan2d_backward_workspace_size(ctypes.byref(d64), 1, 0, None)
+    assert bcall(lib, d64, dirs=1, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=wsd)) == \
+        N.HOPE_ERR_UNSUPPORTED                                            # d = 64: rows of 40 > 32
