@@ -22,8 +22,10 @@
 //
 // A forward sweep stores each chunk's boundary state in the workspace (checkpoints); per
 // chunk of the reverse sweep the gain trajectory G_{t-1} is recomputed into the workspace.
-// Layout per chain: the state S_b and the gain adjoint in LDS, the state adjoint in the
-// workspace (rows owned by fixed threads), per-token quantities of the chunk in LDS.
+// Layout per chain: the state S_b and the gain adjoint in LDS; the state adjoint in
+// registers, thread (col, grp) holding column col of rows grp, grp + NG, ...; per-token
+// quantities of the chunk in LDS.  The state adjoint reaches the workspace once, at the
+// end, for the initial-state gradient.
 #include <algorithm>
 
 #include "device_common.h"
@@ -32,8 +34,10 @@
 namespace hope {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kTB = 16;  // tokens per block of the projection passes
+// threads per chain: 512 at d = 64 (8 waves, two per SIMD: half the state-adjoint rows
+// per thread of 256), 256 below (measured faster at d = 32)
+constexpr int back_threads(int d) { return d == 64 ? 512 : 256; }
 
 __device__ __forceinline__ float load_xb(const void* x, int bf16, int64_t idx) {
   if (bf16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[idx] << 16);
@@ -41,7 +45,8 @@ __device__ __forceinline__ float load_xb(const void* x, int bf16, int64_t idx) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) {
+__global__ __launch_bounds__(back_threads(D)) void chain_backward_kernel(BackParams p) {
+  constexpr int kThreads = back_threads(D);
   constexpr int R = 4 * D + 2;        // state rows
   constexpr int SP = D + 1;           // padded LDS row stride
   constexpr int NP = 3 * D + 2;       // projected rows: k, v, q, s_eta, s_alpha
@@ -50,6 +55,8 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
   constexpr int CPT = D / TPR;        // gain columns per thread
   constexpr int NG = kThreads / D;    // row groups
   constexpr int MC = backward_max_chunk(D);
+  constexpr int RPT = (R + NG - 1) / NG;  // state-adjoint rows per thread
+  constexpr int kSR = 4;                  // row slots staged per pass of dS G^T
   constexpr float kInjInward = 1.f - 1e-3f, kSpecInward = 1.f - 1e-6f, kKappaFloor = 1e-20f;
 
   __shared__ float S[R * SP];         // boundary state of the chunk
@@ -64,7 +71,9 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
   __shared__ float DY[kTB * SP];      // dL/dy_t of the block
   __shared__ float va[D], vb[D], vk[D];
   __shared__ float red[kThreads / 64];
+  __shared__ float red2[kThreads];       // column partial sums, [row group][column]
   __shared__ int pixb[kTB];
+  __shared__ float Stg[kSR * kThreads];  // staging of dS rows (kSR slots x NG rows x D)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,6 +94,8 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
   float* const gdst = slot == 0 ? p.grad_x : p.planes + (int64_t)(slot - 1) * p.plane_stride;
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, 0, 0};
   const int grow = tid / TPR, gcol0 = (tid % TPR) * CPT;
+  const int col = tid % D, grp = tid / D;  // state-adjoint ownership
+  float dsr[RPT];                          // dS[grp + k NG][col]
 
   {
     const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h : (int64_t)r * nh + h) * SS;
@@ -167,7 +178,6 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
   // passes of kRB per thread with a barrier between each pass's reads and writes
   auto rows_times_gain = [&](float* M, int stride, bool trans) {
     constexpr int kRB = 8;
-    const int col = tid % D, grp = tid / D;
     float gc[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) gc[j] = trans ? Gb[col * SP + j] : Gb[j * SP + col];
@@ -204,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
     gain_forward(s0, s1, false);
     rows_times_gain(S, SP, false);
   }
-  for (int e = tid; e < R * D; e += kThreads) dSg[e] = 0.f;  // no loss on the final state
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) dsr[k] = 0.f;  // no loss on the final state
 
   // ---- reverse sweep ------------------------------------------------------------------
   for (int c = nck - 1; c >= 0; --c) {
@@ -215,48 +225,107 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
     chunk_gates(s0, s1);
     gain_forward(s0, s1, true);
 
-    // dG_e = S_b^T dS (row strips), then dS <- dS G_e^T
+    // dG_e = S_b^T dS: each thread's partial over its rows, added into dG one row group
+    // at a time (a fixed order)
+    // (16 rows of dG per pass, to bound the partials held in registers)
+    for (int i0 = 0; i0 < D; i0 += 16) {
+      float part[16];
 #pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) {
-      const int j = gcol0 + cc;
-      float acc = 0.f;
-      for (int rr = 0; rr < R; ++rr) acc = fmaf(S[rr * SP + grow], dSg[(int64_t)rr * D + j], acc);
-      dG[grow * SP + j] = acc;
+      for (int i = 0; i < 16; ++i) part[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int row = grp + k * NG;
+        if (row < R) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part[i] = fmaf(S[row * SP + i0 + i], dsr[k], part[i]);
+        }
+      }
+      for (int gsel = 0; gsel < NG; ++gsel) {
+        if (grp == gsel) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            dG[(i0 + i) * SP + col] = gsel == 0 ? part[i] : dG[(i0 + i) * SP + col] + part[i];
+        }
+        __syncthreads();
+      }
     }
-    __syncthreads();
-    rows_times_gain(dSg, D, true);
+    // dS <- dS G_e^T: rows staged through LDS, kSR row slots per pass (unrolled, so that
+    // the register array is indexed statically)
+#pragma unroll
+    for (int k0 = 0; k0 < RPT; k0 += kSR) {
+#pragma unroll
+      for (int kk = 0; kk < kSR; ++kk)
+        if (k0 + kk < RPT) Stg[kk * kThreads + tid] = dsr[k0 + kk];  // = [slot][grp][col]
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < kSR; ++kk) {
+        if (k0 + kk < RPT) {
+          const float* srow = &Stg[kk * kThreads + grp * D];
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < D; ++i) acc = fmaf(srow[i], Gb[col * SP + i], acc);
+          dsr[k0 + kk] = acc;
+        }
+      }
+      __syncthreads();
+    }
 
     // gain recurrence backwards, token by token
+    constexpr int GPT = D * D / kThreads;
+    float gpre[GPT];
+#pragma unroll
+    for (int m = 0; m < GPT; ++m) gpre[m] = gtr[(int64_t)(s1 - 1 - s0) * D * D + tid + m * kThreads];
     for (int t = s1 - 1; t >= s0; --t) {
       const int tl = t - s0;
-      for (int e = tid; e < D * D; e += kThreads) Gb[(e / D) * SP + e % D] = gtr[(int64_t)tl * D * D + e];
+#pragma unroll
+      for (int m = 0; m < GPT; ++m) {
+        const int e = tid + m * kThreads;
+        Gb[(e / D) * SP + e % D] = gpre[m];
+      }
+      if (tl > 0) {
+#pragma unroll
+        for (int m = 0; m < GPT; ++m) gpre[m] = gtr[(int64_t)(tl - 1) * D * D + tid + m * kThreads];
+      }
       if (tid < D) vk[tid] = Kc[tl * SP + tid];
       __syncthreads();
       const float step = Ec[tl], alpha = Ac[tl];
-      float trp = 0.f;
+      // row parts: a_i = (dG k)_i, b_i = (G k)_i, and <G, dG>
+      float trp = 0.f, pa = 0.f, pb = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) trp = fmaf(Gb[grow * SP + gcol0 + cc], dG[grow * SP + gcol0 + cc], trp);
+      for (int cc = 0; cc < CPT; ++cc) {
+        const int j = gcol0 + cc;
+        const float gv = Gb[grow * SP + j], dv = dG[grow * SP + j], kj = vk[j];
+        trp = fmaf(gv, dv, trp);
+        pa = fmaf(dv, kj, pa);
+        pb = fmaf(gv, kj, pb);
+      }
+#pragma unroll
+      for (int off = TPR / 2; off >= 1; off >>= 1) {
+        pa += __shfl_xor(pa, off, 64);
+        pb += __shfl_xor(pb, off, 64);
+      }
       trp = wave_sum(trp);
       if (lane == 0) red[wave] = trp;
-      if (tid < D) {
-        float a = 0.f, bk = 0.f;
-        for (int j = 0; j < D; ++j) {
-          a = fmaf(dG[tid * SP + j], vk[j], a);
-          bk = fmaf(Gb[tid * SP + j], vk[j], bk);
-        }
-        va[tid] = a;
-        vb[tid] = bk + Dc[tl * SP + tid];  // b + delta
+      if (tid % TPR == 0) {
+        va[grow] = pa;
+        vb[grow] = pb + Dc[tl * SP + grow];  // b + delta
+      }
+      __syncthreads();
+      // column parts: (G^T a + dG^T (b + delta))_j over rows q, q + NG, ...
+      {
+        const int q = tid / D;
+        float ce = 0.f;
+#pragma unroll 4
+        for (int i = q; i < D; i += NG) ce = fmaf(Gb[i * SP + col], va[i], fmaf(dG[i * SP + col], vb[i], ce));
+        red2[q * D + col] = ce;
       }
       __syncthreads();
       if (wave == 0) {
         float dk = 0.f, ddl = 0.f, part = 0.f;
         if (lane < D) {
-          float cj = 0.f, ej = 0.f;
-          for (int i = 0; i < D; ++i) {
-            cj = fmaf(Gb[i * SP + lane], va[i], cj);
-            ej = fmaf(dG[i * SP + lane], vb[i], ej);
-          }
-          dk = -step * (cj + ej);
+          float ce = 0.f;
+          for (int q = 0; q < NG; ++q) ce += red2[q * D + lane];
+          dk = -step * ce;
           ddl = -step * va[lane];
           part = vb[lane] * va[lane];
         }
@@ -286,10 +355,17 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
     for (int tb = s0; tb < s1; tb += kTB) {
       const int nt = min(kTB, s1 - tb);
       load_block(tb, nt);
-      for (int e = tid; e < nt * D; e += kThreads) {
+      for (int e = tid; e < kTB * D; e += kThreads) {
         const int t = e / D, i = e % D;
-        DY[t * SP + i] = p.grad_out[((int64_t)b * N + pixb[t]) * Dt + (int64_t)h * D + i];
+        if (t < nt) {
+          DY[t * SP + i] = p.grad_out[((int64_t)b * N + pixb[t]) * Dt + (int64_t)h * D + i];
+        } else {  // padding tokens: zero rows, so the sums below run over all kTB
+          DY[t * SP + i] = 0.f;
+          X[t * SP + i] = 0.f;
+          Qb[t * SP + i] = 0.f;
+        }
       }
+      for (int e = tid; e < (kTB - nt) * NP; e += kThreads) P[(nt + e / NP) * PS + e % NP] = 0.f;
       __syncthreads();
       for (int t = wave; t < nt; t += kThreads / 64) {
         float* pt = &P[t * PS];
@@ -370,15 +446,21 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
       __syncthreads();
       // state adjoint: dM_mem += dy q^T; the projection rows += (their adjoint) x^T
       {
-        const int col = tid % D, grp = tid / D;
-        for (int rr = grp; rr < R; rr += NG) {
-          float acc = 0.f;
-          if (rr < D) {
-            for (int t = 0; t < nt; ++t) acc = fmaf(DY[t * SP + rr], Qb[t * SP + col], acc);
-          } else {
-            for (int t = 0; t < nt; ++t) acc = fmaf(P[t * PS + rr - D], X[t * SP + col], acc);
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+          const int rr = grp + k * NG;
+          if (rr < R) {
+            float acc = 0.f;
+            if (rr < D) {
+#pragma unroll 4
+              for (int t = 0; t < kTB; ++t) acc = fmaf(DY[t * SP + rr], Qb[t * SP + col], acc);
+            } else {
+#pragma unroll 4
+              for (int t = 0; t < kTB; ++t) acc = fmaf(P[t * PS + rr - D], X[t * SP + col], acc);
+            }
+            dsr[k] += acc;
           }
-          dSg[(int64_t)rr * D + col] += acc;
+          __builtin_amdgcn_sched_barrier(0);  // one row's loads in flight at a time
         }
       }
       // map adjoint of this route: dx_t = sum over projection rows of (their adjoint) row
@@ -390,6 +472,12 @@ __global__ __launch_bounds__(kThreads) void chain_backward_kernel(BackParams p) 
       }
       __syncthreads();
     }
+  }
+  // the initial-state adjoint of this chain, for the gradient reduction
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int rr = grp + k * NG;
+    if (rr < R) dSg[(int64_t)rr * D + col] = dsr[k];
   }
 }
 
@@ -422,7 +510,7 @@ __global__ void init_grad_kernel(BackParams p, float* grad_init, int64_t SS, int
 
 hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
-  dim3 grid((unsigned)blocks), block(kThreads);
+  dim3 grid((unsigned)blocks), block(back_threads(d));
   switch (d) {
     case 16: chain_backward_kernel<16><<<grid, block, 0, stream>>>(p); break;
     case 32: chain_backward_kernel<32><<<grid, block, 0, stream>>>(p); break;
