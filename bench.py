@@ -6,7 +6,9 @@ workload (B=128, 14x14 map, D=384 as 6 heads of 64, row/column chunks of 14,
 bf16 inputs, fp32 state), inputs already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--no-cpu-baseline]
-                  [--copy-probe-mib N]
+                  [--copy-probe-mib N] [--readout running] [--variants ...] [--backward]
+
+--backward times the gradient pass (hope_scan2d_backward) instead, as its own JSON line.
 
 Warm-up is W untimed steps and, beyond them, as many more as it takes to keep the GPU
 busy for 0.2 s, so that the clock has settled before the K timed steps.
@@ -125,6 +127,98 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str
                       f"({toks} scan tokens) in {dt:.1f} s, fp64 numpy, 1 BLAS thread"}
 
 
+def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: float = 15.0) -> dict:
+    """Time the gradient oracle (autograd of the fp64 forward), as it stands, on a bounded
+    sample: the first image with as many of its heads as fit the budget, all routes."""
+    import torch as _torch
+    from oracle import hope_backward as hb
+    threads = _torch.get_num_threads()
+    _torch.set_num_threads(1)
+    try:
+        d = w.d
+        t0 = time.perf_counter()
+        hb.scan2d_backward(inp["x"][:1, ..., :d], inp["init"][:, :1], 1, g[:1, ..., :d], chunk=w.chunk)
+        t1 = time.perf_counter() - t0
+        nh = max(1, min(w.n_heads, int(budget_s / max(t1, 1e-3))))
+        t0 = time.perf_counter()
+        hb.scan2d_backward(inp["x"][:1, ..., :nh * d], inp["init"][:, :nh], nh, g[:1, ..., :nh * d],
+                           chunk=w.chunk)
+        dt = time.perf_counter() - t0
+    finally:
+        _torch.set_num_threads(threads)
+    toks = w.H * w.W * 4 * nh / w.n_heads
+    return {"value": toks / dt, "unit": "scan tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 of {w.B} images, {nh} of {w.n_heads} heads, 4 routes ({toks:.0f} "
+                      f"scan-token equivalents) in {dt:.1f} s, torch fp64 autograd, 1 thread"}
+
+
+def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
+    """The backward pass (hope_scan2d_backward) as the timed step.  Roofline: the gradient
+    of every forward product costs two products of the same size and the forward is
+    recomputed once, so the algorithmic work is 3x the forward's; the kernel computes it
+    all in fp32 on the vector ALUs, so it is charged at the fp32 vector peak."""
+    import torch
+    from self_modifying_memory_amd.scan2d import (hope_scan2d_backward,
+                                                  hope_scan2d_backward_workspace_size)
+    x = x_host.to(dev)
+    init = torch.from_numpy(inp["init"].copy()).to(dev)
+    g_np = np.random.Generator(np.random.PCG64(7)).standard_normal(
+        (w.B, w.H, w.W, w.D)).astype(np.float32)
+    g = torch.from_numpy(g_np).to(dev)
+    ws = torch.empty(max(256, hope_scan2d_backward_workspace_size(x, w.n_heads, 15, w.chunk)),
+                     dtype=torch.uint8, device=dev)
+    gx = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    gi = torch.empty_like(init)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hope_scan2d_backward(x, init, w.n_heads, g, 15, w.chunk, stream=stream, grad_x=gx,
+                             grad_init=gi, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:  # clock settling, untimed
+        step()
+        torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    c_avg = float(np.mean(call_ms)) * 1e-3
+    roof = roofline_numbers(w)
+    flops = 3 * roof["flops"]
+    rec = {
+        "metric": "backward scan tokens/s (positions x dirs): gradients of the 4-dir Hope memory "
+                  "scan with respect to the map and the initial memories",
+        "value": w.scan_tokens(4) * args.steps / wall,
+        "unit": "scan tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
+                   "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
+                   "pass": "backward"},
+        "roofline": {"bound": "alu", "achieved": flops / c_avg / 1e12, "peak": PEAK_FP32 / 1e12,
+                     "unit": "TFLOP/s", "frac": flops / c_avg / PEAK_FP32, "traffic": None,
+                     "kernel": "chain_backward_kernel (with the gradient reduction and route sum)",
+                     "kernel_ms": c_avg * 1e3,
+                     "kernel_ms_p10_p90": [float(np.percentile(call_ms, 10)),
+                                           float(np.percentile(call_ms, 90))]},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_backward(w, inp, g_np.astype(np.float64))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +233,8 @@ def main() -> int:
                     help="comma-separated VisionHOPE variants to enable together: scales, skip, "
                          "counts, hard_injection, soft_spectral, frozen_kv, frozen_dynamics, "
                          "no_dgd, queries (synthetic scales / skip / queries)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients) instead of the forward scan")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -161,6 +257,8 @@ def main() -> int:
         x_host = torch.from_numpy(inp["x_bits"].view(np.int16).copy()).view(torch.bfloat16)
     else:
         x_host = torch.from_numpy(inp["x"].copy())
+    if args.backward:
+        return run_backward(args, w, inp, x_host, dev)
     init = torch.from_numpy(inp["init"].copy()).to(dev)
     sets = []
     for _ in range(max(1, args.sets)):
