@@ -124,10 +124,11 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // NW waves per chain: 4 for d = 32, 8 for d = 64 (at most three state-row tiles per wave,
 // so two waves fit on a SIMD).  Gates use waves 0-3 (16 lanes per token); with eight
 // waves the solve coefficients run on waves 4-7 while waves 0-3 read out.
-// The d = 64 boundary kernels are held to 4 waves per SIMD (128 registers) so that two
-// chains share a CU; the variant instantiation then spills two registers.
+// The d = 64 kernels are held to 4 waves per SIMD (128 registers) so that two chains share
+// a CU: the running-readout and variant instantiations then spill (35 and up to 48
+// registers), which costs less than running one chain per CU.
 template <int D, bool MULTI, int NW, bool KEEP_SPLIT, bool RUN, bool VAR>
-__global__ __launch_bounds__(64 * NW, (D == 64 && !RUN) ? 4 : 1) void chain_mfma_kernel(ChainParams p) {
+__global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
   constexpr int NT = D / 16;                       // column tiles of the state
