@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // The d = 64 kernels are held to 4 waves per SIMD (128 registers) so that two chains share
 // a CU: the running-readout and variant instantiations then spill (35 and up to 48
 // registers), which costs less than running one chain per CU.
-template <int D, bool MULTI, int NW, bool KEEP_SPLIT, bool RUN, bool VAR>
+template <int D, bool MULTI, int NW, bool RUN, bool VAR>
 __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
@@ -300,22 +300,13 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   }
   lds_barrier();
 
-  // bf16 hi/lo split of the chunk-start state, shared by the projections, the readout
-  // and the carry of every block of the chunk (S_b is constant over the chunk)
-  // KEEP_SPLIT holds it across the chunk; otherwise each phase splits its own tiles
-  // again (fewer live registers, more VALU work)
-  bf16x8 Sh[KEEP_SPLIT ? MTW : 1][KEEP_SPLIT ? KS : 1], Sl[KEEP_SPLIT ? MTW : 1][KEEP_SPLIT ? KS : 1];
+  // bf16 hi/lo split of the chunk-start state, formed once per chunk and kept in registers:
+  // shared by the projections, the readout and the carry of every block of the chunk
+  // (S_b is constant over the chunk)
+  bf16x8 Sh[MTW][KS], Sl[MTW][KS];
   auto state_split = [&](int mi, int s, bf16x8& hi, bf16x8& lo) {
-    if (KEEP_SPLIT) {
-      hi = Sh[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0];
-      lo = Sl[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0];
-    } else {
-      // opaque copies: the compiler would otherwise share one split between the phases
-      // and keep it live across all of them
-      f32x4 a = S[mi][2 * s], c = S[mi][2 * s + 1];
-      asm volatile("" : "+v"(a), "+v"(c));
-      split8(a, c, hi, lo);
-    }
+    hi = Sh[mi][s];
+    lo = Sl[mi][s];
   };
 
   for (int s0 = 0; s0 < N; s0 += C) {
@@ -324,8 +315,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        if (KEEP_SPLIT) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0],
-                               Sl[KEEP_SPLIT ? mi : 0][KEEP_SPLIT ? s : 0]);
+        split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
     if (MULTI) {
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
@@ -787,13 +777,6 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
 
 }  // namespace
 
-#ifndef KEEP32
-#define KEEP32 true
-#endif
-#ifndef KEEP64
-#define KEEP64 true
-#endif
-
 bool mfma_path_supported(const ChainParams& p, int d) {
   if (!p.x_bf16) return false;
   if (p.mem_chunk > 0) return false;  // two chunk sizes: the fp32 kernel
@@ -815,15 +798,14 @@ bool needs_variants(const ChainParams& p) {
 
 template <int D, bool MULTI, int NW>
 hipError_t launch_d(const ChainParams& p, dim3 grid, hipStream_t stream) {
-  constexpr bool KEEP = D == 32 ? KEEP32 : KEEP64;
   const bool var = needs_variants(p);
   const dim3 block(64 * NW);
   if (p.readout) {
-    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, true, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, true, false>), grid, block, 0, stream, p);
+    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, false>), grid, block, 0, stream, p);
   } else {
-    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, KEEP, false, false>), grid, block, 0, stream, p);
+    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
