@@ -78,3 +78,35 @@ def test_backward_is_deterministic():
     a = [t.cpu().numpy() for t in hope_scan2d_backward(x, init, 2, g)]
     b = [t.cpu().numpy() for t in hope_scan2d_backward(x, init, 2, g)]
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("idx", [3, 2])
+def test_backward_full_size_content_memory_linear_response(idx):
+    # The output is linear in the initial content memory M_mem (its trajectory is
+    # M_mem,b G and G does not depend on it), so for any direction V of the M_mem rows
+    #   <dL/dM_mem, V> = <grad_out, out(M_mem = V) - out(M_mem = 0)>
+    # exactly; both sides come from the GPU (the backward, and two forward calls) at the
+    # workload's full size and launch configuration.  The fp32 forward kernel is used on
+    # both runs so that the two outputs share their arithmetic.
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_backward, hope_scan2d_forward
+    w = wl.WORKLOADS[idx]
+    print("workload", w.name, flush=True)
+    inp = wl.draw_workload(w, live=True)
+    x = torch.from_numpy(inp["x"].astype(np.float32)).cuda()      # the bf16 values, as fp32
+    init_np = inp["init"].astype(np.float32)
+    d = w.d
+    rng = np.random.Generator(np.random.PCG64(94))
+    g = torch.from_numpy(rng.standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)).cuda()
+    V = rng.standard_normal((4, w.n_heads, d * d)).astype(np.float32) / np.sqrt(d)
+    _, gi = hope_scan2d_backward(x, torch.from_numpy(init_np).cuda(), w.n_heads, g)
+    lhs = float(np.sum(gi.cpu().numpy()[:, :, :d * d].astype(np.float64) * V))
+    with_v, zero = init_np.copy(), init_np.copy()
+    with_v[:, :, :d * d] = V
+    zero[:, :, :d * d] = 0.0
+    out_v = hope_scan2d_forward(x, torch.from_numpy(with_v).cuda(), w.n_heads)
+    out_0 = hope_scan2d_forward(x, torch.from_numpy(zero).cuda(), w.n_heads)
+    rhs = float(torch.sum((out_v.double() - out_0.double()) * g.double()).item())
+    rel = abs(lhs - rhs) / max(abs(rhs), 1e-30)
+    print(f"  <grad, V> {lhs:.6e}  linear response {rhs:.6e}  rel {rel:.2e}", flush=True)
+    assert rel <= TOL["f32"]
