@@ -147,7 +147,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
   __shared__ __attribute__((aligned(16))) float Ks[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Dls[kSB * LD];
-  __shared__ __attribute__((aligned(16))) float Ubs[MULTI ? kSB * LD : 4];
+  __shared__ __attribute__((aligned(16))) float Ubs[kSB * LD];  // write vectors Ub, fp32
   // MFMA-ready bf16 hi/lo copies: Ub rows (A operand of S_b Ub^T) and K transposed
   // (A operand of the carry), written once by their producers instead of re-split per wave
   __shared__ __attribute__((aligned(16))) unsigned short UbH[kSB * XLD];
@@ -175,6 +175,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   // number of register tiles: Tb[cur] is the chunk-start copy, Tb[cur ^ 1] the update
   __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
   __shared__ unsigned int cnt_lds[3];  // step-control counters of this chain
+  __shared__ __attribute__((aligned(16))) float ztl[2 * kSB];  // z_t of the two gate rows
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -604,7 +605,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         for (int i = 0; i < 4; ++i) {
           const int t = 4 * i + q;
           const float ub = bco[t] * u[i];
-          if (MULTI) Ubs[t * LD + col] = ub;
+          Ubs[t * LD + col] = ub;
           const __bf16 uh = (__bf16)ub;
           UbH[t * XLD + col] = __builtin_bit_cast(unsigned short, uh);
           UbL[t * XLD + col] = __builtin_bit_cast(unsigned short, (__bf16)(ub - (float)uh));
@@ -676,9 +677,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
             if (t < nt) dst[((int64_t)b * N + rpix[i]) * Dt + c] = finish(cprev[t] * rq[i] + y[i], c, rx[i]);
           }
         }
-        // gate rows: every readout wave forms their Z tile and updates column tile w
+        // gate rows at d = 32: every readout wave forms their Z tile and updates column
+        // tile w on MFMA (at d = 64 they are carried in fp32 below)
+        constexpr bool tail_mfma = D != 64;
         bf16x4 tzh, tzl;
-        if (w < NT && !gates_frozen) {
+        if (tail_mfma && w < NT && !gates_frozen) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
             }
           }
         }
-        if (w < NT && !gates_frozen) {
+        if (tail_mfma && w < NT && !gates_frozen) {
           f32x4 acc = tail_tile(first ? Tb[cur] : Tb[cur ^ 1], w, c16, g);
           acc *= cc;
           // K operand of column tile w, read again (an index into kah by wave id would not
@@ -713,6 +716,37 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           const bf16x4 kl = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (w * 16 + c16) * KTLD + 4 * g));
           acc = mma16x3(kh, kl, tzh, tzl, acc);
           if (c16 < 2) *reinterpret_cast<f32x4*>(Tb[cur ^ 1] + c16 * D + w * 16 + 4 * g) = acc;
+        }
+        // gate rows at d = 64, in exact fp32 on the vector ALUs (two rows fill an eighth of an
+        // MFMA tile), on two solve waves, which carry less here than the readout waves:
+        // wave SW0 + r takes row r,  z_t = Ub_t . m_b,  m <- c m + sum_t z_t k_t.
+        // (Measured: at d = 32, four chains per CU, the MFMA form above is faster.)
+        if (!tail_mfma && !gates_frozen && (w == SW0 || w == SW0 + 1)) {
+          const int rrow = w - SW0;
+          const float* mb = Tb[cur] + rrow * D;  // chunk-start row
+          const int t = lane >> 2, qq = lane & 3;
+          float z = 0.f;
+#pragma unroll
+          for (int j4 = 0; j4 < D / 16; ++j4) {  // 16-byte reads: D/4 columns per lane
+            const int j = qq * (D / 4) + 4 * j4;
+            const f32x4 u4 = *reinterpret_cast<const f32x4*>(Ubs + t * LD + j);
+            const f32x4 m4 = *reinterpret_cast<const f32x4*>(mb + j);
+            z = fmaf(u4[0], m4[0], fmaf(u4[1], m4[1], fmaf(u4[2], m4[2], fmaf(u4[3], m4[3], z))));
+          }
+          z += dpp_move<0xB1>(z);  // quad_perm [1,0,3,2]
+          z += dpp_move<0x4E>(z);  // quad_perm [2,3,0,1]
+          if (qq == 0) ztl[rrow * kSB + t] = z;
+          // (this wave's LDS writes above precede its reads below)
+          if (lane < D) {
+            float acc = cc * (first ? Tb[cur] : Tb[cur ^ 1])[rrow * D + lane];
+#pragma unroll
+            for (int t4 = 0; t4 < kSB / 4; ++t4) {
+              const f32x4 z4 = *reinterpret_cast<const f32x4*>(ztl + rrow * kSB + 4 * t4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc = fmaf(Ks[(4 * t4 + e) * LD + lane], z4[e], acc);
+            }
+            Tb[cur ^ 1][rrow * D + lane] = acc;
+          }
         }
         // gain of the chunk so far, needed by the next block of the same chunk
         if (MULTI && !last_block) {
