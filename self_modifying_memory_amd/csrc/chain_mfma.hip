@@ -142,6 +142,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
   constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
   constexpr int LTLD = kSB + 4;                    // fp32 stride of L^T
+  constexpr bool kDeferMemSplit = D == 64;
 
   __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
@@ -312,11 +313,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
 
   for (int s0 = 0; s0 < N; s0 += C) {
     const int s1 = min(s0 + C, N);
+    // (at d = 64 the M_mem tiles, first read in the readout, are split there, off the
+    // projections' path; measured slower at d = 32)
 #pragma unroll
     for (int mi = 0; mi < MTW; ++mi)
+      if (!kDeferMemSplit || w + kWaves * mi >= NT) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
+        for (int s = 0; s < KS; ++s) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
+      }
     if (MULTI) {
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
@@ -453,6 +457,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
       for (int mi = 0; mi < MTW; ++mi) {
         const int m = w + kWaves * mi;
         if (m >= NT) continue;
+        if (kDeferMemSplit && first) {  // the chunk-start split of this M_mem tile
+#pragma unroll
+          for (int s = 0; s < KS; ++s) split8(S[mi][2 * s], S[mi][2 * s + 1], Sh[mi][s], Sl[mi][s]);
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
