@@ -511,13 +511,18 @@ __global__ void init_grad_kernel(BackParams p, float* grad_init, int64_t SS, int
 hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
   dim3 grid((unsigned)blocks), block(back_threads(d));
-  switch (d) {
-    case 16: chain_backward_kernel<16><<<grid, block, 0, stream>>>(p); break;
-    case 32: chain_backward_kernel<32><<<grid, block, 0, stream>>>(p); break;
-    case 64: chain_backward_kernel<64><<<grid, block, 0, stream>>>(p); break;
-    default: return hipErrorInvalidValue;
+  hipError_t err = hipSuccess;
+  if (backward_wy_supported(p, d)) {
+    err = launch_chain_backward_wy(p, stream);
+  } else {
+    switch (d) {
+      case 16: chain_backward_kernel<16><<<grid, block, 0, stream>>>(p); break;
+      case 32: chain_backward_kernel<32><<<grid, block, 0, stream>>>(p); break;
+      case 64: chain_backward_kernel<64><<<grid, block, 0, stream>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    err = hipGetLastError();
   }
-  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t SS = 4LL * d * d + 2LL * d;
   const int64_t n_out = (p.init_per_image ? (int64_t)p.B : 1) * 4 * p.nh * SS;

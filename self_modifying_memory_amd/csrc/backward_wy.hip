@@ -1,0 +1,661 @@
+// Backward pass of the four-direction scan at d = 64 with chunks of at most 16 tokens,
+// gfx950: the chunk-parallel form, fp32 matrix cores (v_mfma_f32_16x16x4_f32, exact fp32
+// products and fp32 sums), one (image, head, route) chain per workgroup of 8 waves.
+//
+// Forward, per chunk c of a chain ("VisionHOPE: Visual Backbones as Self-Modifying Learning
+// Systems", Sec. 2.1.3 Eq. 15-16, Sec. 2.2 Eq. 19-20 with the App. B.3 safeguards, App. B.4
+// Eq. 46): all six memories share the chunk's gain G_c, so the boundary state of chunk c is
+// S_0 P_c with P_c = G_0 G_1 ... G_{c-1} (d x d) and the state S_0 (4d+2 rows) fixed.  The
+// chunk's projections are S_0 (P_c x_t), its readout S_0[mem] (P_c q_t), and its gain, with
+// A_t = alpha_t I - step_t k_t k_t^T, is
+//   G_t = alpha_t G_{t-1} + u_t k_t^T,  u_t = -step_t w_t,  w_t = G_{t-1} k_t + delta_t,
+//   G_{t-1} = Gam_{t-1} I + sum_{j<t} beta_{j,t-1} u_j k_j^T   (Gam prefix products of alpha,
+//   beta_{j,t} = alpha_{j+1} ... alpha_t),
+// so u_t follows from a C x C triangular recurrence over the Gram matrix K^T K, and
+// P_{c+1} = Gam_C P_c + (P_c U) diag(beta_{., C-1}) K^T.
+//
+// Reverse (the memory trajectory is explicit and differentiable, Sec. 1), with dP the
+// adjoint of P_{c+1} and D_e = P_c^T dP the adjoint of the chunk's end gain:
+//   dG_t = Gam'_t D_e - sum_{m>t} beta_{t,m-1} step_m a_m k_m^T  (Gam'_t = alpha_{t+1} ...),
+//   a_t = dG_t k_t = Gam'_t D_e k_t - sum_{m>t} beta_{t,m-1} step_m (k_m^T k_t) a_m,
+//   dstep_t = -w_t^T a_t,  ddelta_t = -step_t a_t,  dalpha_t = <G_{t-1}, dG_t>,
+//   dk_t = -step_t (G_{t-1}^T a_t + dG_t^T w_t),
+// each expanded through the two low-rank forms into C x C Gram matrices (U^T A, A^T W,
+// K^T A, (P U)^T (dP K)) and the vectors D_e k_t = P^T (dP k_t), D_e^T w_t = dP^T (P w_t);
+// then the gates, the normalisation and the projections token by token, and
+//   dP_c = Gam_C dP + (dP K) diag(beta_{., C-1}) U^T + sum_t (dx~_t x_t^T + dq~_t q_t^T),
+//   dS_0 += sum_t [dy_t (P q_t)^T ; dp_t (P x_t)^T],  dx_t = P^T dx~_t,
+// with dx~_t = S_0[proj]^T dp_t and dq~_t = S_0[mem]^T dy_t.  Where the step is not
+// differentiable: min(eta_bar, eta_spec) follows eta_bar when eta_bar <= eta_spec; no
+// derivative through the |k|^2 floor or the one-ulp rounding of eta_spec; eta_bar = 0
+// (eta = 0 or eta_inj = 0) has derivative 0.
+//
+// A forward sweep writes P_c of every chunk to the workspace; the reverse sweep recomputes
+// the chunk's projections and gates from it.  S_0 stays in registers for the whole chain:
+// waves 0-3 hold column tile w of every row (for S_0^T products), waves 4-7 the rows of
+// their projection row tiles (for S_0 products); the state adjoint dS_0 is accumulated in
+// registers as 68 16 x 16 tiles spread over the 8 waves.  P_c, dP and the chunk's per-token
+// vectors (token-major, 16 token slots, padding slots zero) live in LDS.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hope {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;            // head dimension
+constexpr int kTT = 16;           // token slots per chunk
+constexpr int kLD = kD + 4;       // LDS row stride of d-vectors and d x d matrices
+constexpr int kR = 4 * kD + 2;    // state rows: M_mem, M_k, M_v, M_q, m_eta, m_alpha
+constexpr int kPL = 212;          // stride of a token's projection row (13 row tiles = 208)
+constexpr int kCL = 17;           // stride of the C x C matrices
+constexpr float kInjInward = 1.f - 1e-3f, kSpecInward = 1.f - 1e-6f, kKappaFloor = 1e-20f;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float load_xw(const void* x, int bf16, int64_t idx) {
+  if (bf16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[idx] << 16);
+  return static_cast<const float*>(x)[idx];
+}
+
+struct Lane {
+  int lane, r16, q4;
+};
+
+// The thread index through an opaque copy: LDS addresses derived from it are recomputed in
+// each stage instead of being hoisted out of the chunk loops and held for the whole kernel.
+__device__ __forceinline__ int stage_lane(int tid) {
+  asm volatile("" : "+v"(tid));
+  return tid;
+}
+__device__ __forceinline__ Lane stage_lane_of(int tid) {
+  const int t = stage_lane(tid);
+  return Lane{t & 63, t & 15, (t & 63) >> 4};
+}
+
+// Rows 16m..16m+15 of M (or of M^T) times the 16 token vectors of In (token-major):
+// Out[t][16m + i] = sum_k M(16m + i, k) In[t][k].  MFMA operands: lane (r16, q4) feeds
+// A[r16][k = 4s + q4] and B[k = 4s + q4][t = r16]; result D[4 q4 + v][r16].
+__device__ __forceinline__ f32x4 dmat_tokens(const float* M, bool trans, const float* In, int m,
+                                             const Lane& L) {
+  const int base = trans ? 16 * m + L.r16 : (16 * m + L.r16) * kLD;
+  const int ks = trans ? kLD : 1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kD / 4; ++s) {
+    const int k = 4 * s + L.q4;
+    acc = mfma4(M[base + k * ks], In[L.r16 * kLD + k], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void store_tokens(float* Out, int m, f32x4 acc, const Lane& L) {
+  *reinterpret_cast<f32x4*>(&Out[L.r16 * kLD + 16 * m + 4 * L.q4]) = acc;
+}
+
+// C x C Gram matrix Out[j][t] = A_j . B_t of two token-major arrays.
+__device__ __forceinline__ f32x4 gram_tokens(const float* A, const float* B, const Lane& L) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kD / 4; ++s) {
+    const int k = 4 * s + L.q4;
+    acc = mfma4(A[L.r16 * kLD + k], B[L.r16 * kLD + k], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void store_cc(float* Out, f32x4 acc, const Lane& L) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) Out[(4 * L.q4 + v) * kCL + L.r16] = acc[v];
+}
+
+// diagonal of a C x C result tile into Out[16]
+__device__ __forceinline__ void store_diag(float* Out, f32x4 acc, const Lane& L) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (4 * L.q4 + v == L.r16) Out[L.r16] = acc[v];
+}
+
+__global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
+  // One LDS block, small and uniformly read arrays first so that their addresses fit the
+  // 16-bit immediate offset of the LDS instructions (one base register serves them all).
+  constexpr int kTok = kTT * kLD;
+  constexpr int oSc = 0;                      // per-token scalars, 8 x 16
+  constexpr int oCC = oSc + 8 * kTT;          // C x C matrices, 4 x 16 x 17
+  constexpr int oTok = oCC + 4 * kTT * kCL;   // token-major d-vectors, 18 of them
+  constexpr int oProj = oTok + 18 * kTok;     // projections [16][kPL]
+  constexpr int oP = oProj + kTT * kPL;       // P_c, dP
+  constexpr int kSmem = oP + 2 * kD * kLD;
+  __shared__ __align__(16) float smem[kSmem];
+  float* const tSt = smem + oSc;  // step_t
+  float* const tAl = tSt + kTT;   // alpha_t
+  float* const tGam = tAl + kTT;  // Gam_{t-1}
+  float* const tGp = tGam + kTT;  // Gam'_t
+  float* const tL = tGp + kTT;    // k_t . a_t
+  float* const tUd = tL + kTT;    // (P u_t) . (dP k_t)
+  float* const tTr = tUd + kTT;   // <P, dP> in 4 parts, then Gam_C
+  float* const tGC = tTr + 4;
+  int* const pixb = reinterpret_cast<int*>(tTr + kTT);
+  float* const sGm = smem + oCC;  // K^T K
+  float* const sBt = sGm + kTT * kCL;
+  float* const sH = sBt + kTT * kCL;  // U^T A
+  float* const sJ = sH + kTT * kCL;   // A^T W
+  float* const sK = smem + oTok;
+  float* const sDl = sK + kTok;
+  float* const sQ = sDl + kTok;
+  float* const sU = sQ + kTok;
+  float* const sW = sU + kTok;
+  float* const sA = sW + kTok;
+  float* const sZ = sA + kTok;
+  float* const sE = sZ + kTok;
+  float* const sF = sE + kTok;
+  float* const sX = sF + kTok;
+  float* const sXt = sX + kTok;
+  float* const sDY = sXt + kTok;
+  float* const sQt = sDY + kTok;
+  float* const sdQt = sQt + kTok;
+  float* const sdQ = sdQt + kTok;
+  float* const sY = sdQ + kTok;
+  float* const sPU = sY + kTok;
+  float* const sdXt = sPU + kTok;
+  float* const sProj = smem + oProj;  // raw projections, then their adjoints
+  float* const sP = smem + oP;        // P_c
+  float* const sdP = sP + kD * kLD;   // adjoint of P_{c+1}, then of P_c
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int nh = p.nh;
+  const int h = blockIdx.x % nh;
+  const int b = (blockIdx.x / nh) % p.B;
+  const int slot = blockIdx.x / (nh * p.B);
+  const int r = p.route_of_slot[slot];
+  const int H = p.H, W = p.W, N = H * W, Dt = p.D;
+  const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
+  const int nck = (N + C - 1) / C;
+  const int64_t SS = (int64_t)kR * kD;
+  float* const ckpt = p.chain_ws + (int64_t)blockIdx.x * p.chain_floats;
+  float* const dSg = ckpt + p.nck * SS;
+  float* const gdst = slot == 0 ? p.grad_x : p.planes + (int64_t)(slot - 1) * p.plane_stride;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, 0, 0};
+  const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h : (int64_t)r * nh + h) * SS;
+
+  // S_0 in registers.  Waves 0-3 (column tile w): s0f[4T + s] = S_0[16T + 4s + q4][16w + r16]
+  // for the 17 row tiles T.  Waves 4-7: row tiles 4 + j + 4 slot (slot 0-2) and, on wave 4,
+  // tile 16: s0f[16 slot + s] = S_0[16T + r16][4s + q4].
+  float s0f[68];
+  {
+    const Lane L = stage_lane_of(tid);
+    if (w < 4) {
+#pragma unroll
+      for (int e = 0; e < 68; ++e) {
+        const int row = 16 * (e >> 2) + 4 * (e & 3) + L.q4;
+        s0f[e] = row < kR ? init[(int64_t)row * kD + 16 * w + L.r16] : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 64; ++e) {
+        const int sl = e >> 4, s = e & 15;
+        const int T = sl < 3 ? 4 + (w - 4) + 4 * sl : 16;
+        const int row = 16 * T + L.r16;
+        s0f[e] = ((sl < 3 || w == 4) && row < kR) ? init[(int64_t)row * kD + 4 * s + L.q4] : 0.f;
+      }
+#pragma unroll
+      for (int e = 64; e < 68; ++e) s0f[e] = 0.f;
+    }
+  }
+  f32x4 dsa[9];  // dS_0 tiles o = w + 8 i: rows 16 (o >> 2) .., columns 16 (o & 3) ..
+#pragma unroll
+  for (int i = 0; i < 9; ++i) dsa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // identity P_0, zero dP
+  for (int e = tid; e < kD * kD; e += 512) {
+    const int i = e >> 6, j = e & 63;
+    sP[i * kLD + j] = i == j ? 1.f : 0.f;
+    sdP[i * kLD + j] = 0.f;
+  }
+
+  // x (and dL/dy) of the chunk's tokens into LDS, zero padding slots
+  auto load_chunk = [&](int s0, int cl, bool with_dy) {
+    const int t0 = stage_lane(tid);
+    for (int e = t0; e < kTT * kD; e += 512) {
+      const int t = e >> 6, i = e & 63;
+      float xv = 0.f, gv = 0.f;
+      if (t < cl) {
+        const int pix = route_pixel(r, s0 + t, H, W, N);
+        const int64_t idx = ((int64_t)b * N + pix) * Dt + (int64_t)h * kD + i;
+        xv = load_xw(p.x, p.x_bf16, idx);
+        if (with_dy) gv = p.grad_out[idx];
+      }
+      sX[t * kLD + i] = xv;
+      if (with_dy) sDY[t * kLD + i] = gv;
+    }
+    if (t0 < kTT) pixb[t0] = t0 < cl ? route_pixel(r, s0 + t0, H, W, N) : 0;
+  };
+  // projections of the chunk: waves 4-7, Proj[t][pr] = S_0[64 + pr] . x~_t
+  auto projections = [&]() {
+    const Lane L = stage_lane_of(tid);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int T = sl < 3 ? 4 + (w - 4) + 4 * sl : 16;
+      if (sl < 3 || w == 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) acc = mfma4(s0f[16 * sl + s], sXt[L.r16 * kLD + 4 * s + L.q4], acc);
+        *reinterpret_cast<f32x4*>(&sProj[L.r16 * kPL + 16 * T - 64 + 4 * L.q4]) = acc;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // k, delta, q, step, alpha of every token slot (wave per token)
+  auto gates = [&](int cl) {
+    const Lane L = stage_lane_of(tid);
+    const int lane = L.lane;
+    for (int t = w; t < kTT; t += 8) {
+      if (t < cl) {
+        const float* pt = &sProj[t * kPL];
+        const TokenGates tg = token_gates(pt[lane], pt[kD + lane], pt[2 * kD + lane], pt[3 * kD],
+                                          pt[3 * kD + 1], gp);
+        sK[t * kLD + lane] = tg.k;
+        sDl[t * kLD + lane] = tg.delta;
+        sQ[t * kLD + lane] = tg.q;
+        if (lane == 0) {
+          tSt[t] = tg.step;
+          tAl[t] = tg.alpha;
+        }
+      } else {
+        sK[t * kLD + lane] = 0.f;
+        sDl[t * kLD + lane] = 0.f;
+        sQ[t * kLD + lane] = 0.f;
+        if (lane == 0) {
+          tSt[t] = 0.f;
+          tAl[t] = 1.f;
+        }
+      }
+    }
+  };
+  // products of alpha over token ranges (lanes of waves 4-7, one (j, t) pair each):
+  // Bt[j][t] = alpha_{j+1} .. alpha_t (j <= t, else 0), Gam_{t-1}, Gam'_t, Gam_C
+  auto alpha_products = [&]() {
+    const int e = stage_lane(tid) - 256, t = e >> 4, j = e & 15;
+    float bt = 0.f;
+    if (j <= t) {
+      bt = 1.f;
+      for (int i = j + 1; i <= t; ++i) bt *= tAl[i];
+    }
+    sBt[j * kCL + t] = bt;
+    if (j == 0) {
+      float g = 1.f;
+      for (int i = 0; i < t; ++i) g *= tAl[i];
+      tGam[t] = g;
+    } else if (j == 1) {
+      float g = 1.f;
+      for (int i = t + 1; i < kTT; ++i) g *= tAl[i];
+      tGp[t] = g;
+    } else if (j == 2 && t == 0) {
+      float g = 1.f;
+      for (int i = 0; i < kTT; ++i) g *= tAl[i];
+      tGC[0] = g;
+    }
+  };
+  // u_t and w_t of the chunk (one wave, lane = component), token order
+  auto solve_u = [&](int cl) {
+    const int lane = stage_lane(tid) & 63;
+    float u[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) {
+      float wv = 0.f, uv = 0.f;
+      if (t < cl) {
+        wv = fmaf(tGam[t], sK[t * kLD + lane], sDl[t * kLD + lane]);
+#pragma unroll
+        for (int j = 0; j < t; ++j) wv = fmaf(sBt[j * kCL + t - 1] * sGm[j * kCL + t], u[j], wv);
+        uv = -tSt[t] * wv;
+      }
+      u[t] = uv;
+      sU[t * kLD + lane] = uv;
+      sW[t * kLD + lane] = wv;
+      __builtin_amdgcn_sched_barrier(0);  // one token's coefficient loads in flight at a time
+    }
+  };
+  // a_t of the chunk (one wave, reverse token order)
+  auto solve_a = [&](int cl) {
+    const int lane = stage_lane(tid) & 63;
+    float a[kTT];
+#pragma unroll
+    for (int t = kTT - 1; t >= 0; --t) {
+      float av = 0.f;
+      if (t < cl) {
+        av = tGp[t] * sE[t * kLD + lane];
+#pragma unroll
+        for (int m = t + 1; m < kTT; ++m)
+          av = fmaf(-(sBt[t * kCL + m - 1] * tSt[m] * sGm[m * kCL + t]), a[m], av);
+      }
+      a[t] = av;
+      sA[t * kLD + lane] = av;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // P <- Gam_C P + (P U) diag(beta_{., cl-1}) K^T (M = sP), or the adjoint carry
+  // dP <- Gam_C dP + (dP K) diag(beta) U^T + dX~ X^T + dQ~ Q^T (M = sdP); 16 tiles, 2 per wave
+  auto carry_update = [&](bool adjoint, int cl) {
+    const Lane L = stage_lane_of(tid);
+    const int r16 = L.r16, q4 = L.q4;
+    float* M = adjoint ? sdP : sP;
+    const float gc = tGC[0];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int idx = w + 8 * k2, mi = idx >> 2, nj = idx & 3;
+      f32x4 acc;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = gc * M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tk = 4 * s + q4;
+        const float bet = sBt[tk * kCL + cl - 1];
+        if (adjoint) {
+          acc = mfma4(sZ[tk * kLD + 16 * mi + r16] * bet, sU[tk * kLD + 16 * nj + r16], acc);
+          acc = mfma4(sdXt[tk * kLD + 16 * mi + r16], sX[tk * kLD + 16 * nj + r16], acc);
+          acc = mfma4(sdQt[tk * kLD + 16 * mi + r16], sQ[tk * kLD + 16 * nj + r16], acc);
+        } else {
+          acc = mfma4(sPU[tk * kLD + 16 * mi + r16] * bet, sK[tk * kLD + 16 * nj + r16], acc);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto dtok = [&](float* Out, const float* M, bool trans, const float* In, int m) {
+    const Lane L = stage_lane_of(tid);
+    store_tokens(Out, m, dmat_tokens(M, trans, In, m, L), L);
+  };
+  auto gram = [&](float* Out, const float* A, const float* B) {
+    const Lane L = stage_lane_of(tid);
+    store_cc(Out, gram_tokens(A, B, L), L);
+  };
+  auto gram_diag = [&](float* Out, const float* A, const float* B) {
+    const Lane L = stage_lane_of(tid);
+    store_diag(Out, gram_tokens(A, B, L), L);
+  };
+
+  __syncthreads();
+
+  // ---- forward sweep: P_c of every chunk into the workspace ---------------------------
+  for (int c = 0; c < nck; ++c) {
+    const int s0 = c * C, cl = min(C, N - s0);
+    for (int e = stage_lane(tid); e < kD * kD; e += 512) ckpt[(int64_t)c * kD * kD + e] = sP[(e >> 6) * kLD + (e & 63)];
+    if (c == nck - 1) break;  // P after the last chunk is not needed
+    load_chunk(s0, cl, false);
+    __syncthreads();
+    if (w < 4) dtok(sXt, sP, false, sX, w);
+    __syncthreads();
+    if (w >= 4) projections();
+    __syncthreads();
+    gates(cl);
+    __syncthreads();
+    if (w == 0) gram(sGm, sK, sK);
+    if (w >= 4) alpha_products();
+    __syncthreads();
+    if (w == 0) solve_u(cl);
+    __syncthreads();
+    if (w < 4) dtok(sPU, sP, false, sU, w);
+    __syncthreads();
+    carry_update(false, cl);
+    __syncthreads();
+  }
+
+  // ---- reverse sweep ---------------------------------------------------------------------
+  for (int c = nck - 1; c >= 0; --c) {
+    const int s0 = c * C, cl = min(C, N - s0);
+    __syncthreads();
+    for (int e = stage_lane(tid); e < kD * kD; e += 512) sP[(e >> 6) * kLD + (e & 63)] = ckpt[(int64_t)c * kD * kD + e];
+    load_chunk(s0, cl, true);
+    __syncthreads();
+    // x~ = P x; <P, dP> in parts
+    if (w < 4) {
+      dtok(sXt, sP, false, sX, w);
+    } else {
+      const int t0 = stage_lane(tid);
+      float tr = 0.f;
+      for (int e = t0 - 256; e < kD * kD; e += 256) {
+        const int o = (e >> 6) * kLD + (e & 63);
+        tr = fmaf(sP[o], sdP[o], tr);
+      }
+      tr = wave_sum(tr);
+      if ((t0 & 63) == 0) tTr[w - 4] = tr;
+    }
+    __syncthreads();
+    // projections; dq~ = S_0[mem]^T dy (waves 0-3)
+    if (w >= 4) {
+      projections();
+    } else {
+      const Lane L = stage_lane_of(tid);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc = mfma4(s0f[4 * T + s], sDY[L.r16 * kLD + 16 * T + 4 * s + L.q4], acc);
+      store_tokens(sdQt, w, acc, L);
+    }
+    __syncthreads();
+    gates(cl);
+    __syncthreads();
+    // K^T K, alpha products; q~ = P q, Z = dP K, dq = P^T dq~
+    if (w == 0) gram(sGm, sK, sK);
+    if (w >= 4) alpha_products();
+    for (int jb = w; jb < 12; jb += 8) {
+      const int kind = jb >> 2, m = jb & 3;
+      if (kind == 0) dtok(sQt, sP, false, sQ, m);
+      else if (kind == 1) dtok(sZ, sdP, false, sK, m);
+      else dtok(sdQ, sP, true, sdQt, m);
+    }
+    __syncthreads();
+    // u, w (wave 0); E = P^T Z = D_e K
+    if (w == 0) {
+      solve_u(cl);
+    } else if (w <= 4) {
+      dtok(sE, sP, true, sZ, w - 1);
+    }
+    __syncthreads();
+    // a (wave 0); Y = P W, PU = P U
+    if (w == 0) {
+      solve_a(cl);
+    } else {
+      for (int jb = w - 1; jb < 8; jb += 7) {
+        const int m = jb & 3;
+        if (jb < 4) dtok(sY, sP, false, sW, m);
+        else dtok(sPU, sP, false, sU, m);
+      }
+    }
+    __syncthreads();
+    // F = dP^T Y = D_e^T W; H = U^T A, J = A^T W, diag(K^T A), diag((P U)^T Z)
+    if (w < 4) dtok(sF, sdP, true, sY, w);
+    else if (w == 4) gram(sH, sU, sA);
+    else if (w == 5) gram(sJ, sA, sW);
+    else if (w == 6) gram_diag(tL, sK, sA);
+    else gram_diag(tUd, sPU, sZ);
+    __syncthreads();
+    // token by token: the gain adjoints, then the readout, the step, the gates, the
+    // normalisation and the projections; dProj replaces Proj in place
+    for (int t = w; t < cl; t += 8) {
+      const int lane = stage_lane(tid) & 63;
+      const float st = tSt[t], gam = tGam[t], gp1 = tGp[t];
+      // lanes j < 16: the coefficient of k_j in dk_t and the j-part of dalpha_t
+      float cf = 0.f, term = 0.f;
+      if (lane < kTT) {
+        const int j = lane;
+        if (j < t) {
+          const float bj = sBt[j * kCL + t - 1];
+          cf = bj * sH[j * kCL + t];
+          float inner = 0.f;
+          for (int m = t + 1; m < kTT; ++m)
+            inner = fmaf(sBt[t * kCL + m - 1] * tSt[m], sH[j * kCL + m] * sGm[j * kCL + m], inner);
+          term = bj * (gp1 * tUd[j] - inner);
+        } else if (j > t) {
+          cf = -sBt[t * kCL + j - 1] * tSt[j] * sJ[j * kCL + t];
+        } else {
+          float lsum = 0.f;
+          for (int m = t + 1; m < kTT; ++m) lsum = fmaf(sBt[t * kCL + m - 1] * tSt[m], tL[m], lsum);
+          const float tr = (tTr[0] + tTr[1]) + (tTr[2] + tTr[3]);
+          term = gam * (gp1 * tr - lsum);
+        }
+      }
+      term = row16_sum(term);
+      float dalpha = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, term)));
+      const float at = sA[t * kLD + lane];
+      float gk = fmaf(gam, at, gp1 * sF[t * kLD + lane]);
+#pragma unroll
+      for (int j = 0; j < kTT; ++j) {
+        const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cf), j));
+        gk = fmaf(cj, sK[j * kLD + lane], gk);
+      }
+      float dk = -st * gk;
+      float ddl = -st * at;
+      const float dstep = -sJ[t * kCL + t];
+      const float dq = sdQ[t * kLD + lane];
+
+      float* pt = &sProj[t * kPL];
+      const float kr = pt[lane], vr = pt[kD + lane], qr = pt[2 * kD + lane];
+      const float se = pt[3 * kD], sa = pt[3 * kD + 1];
+      // forward values, as in token_gates / executed_step
+      const float nk = sqrtf(wave_sum(kr * kr) + gp.eps);
+      const float nq = sqrtf(wave_sum(qr * qr) + gp.eps);
+      const float k = kr / nk, q = qr / nq;
+      const float dl = k - vr;
+      const float dd = wave_sum(dl * dl), kk = wave_sum(k * k);
+      float eta, deta_dse;
+      if (gp.eta_map == 0) {
+        const float sg = fast_rcp(1.f + fast_exp(-se));
+        eta = gp.eta_scale * sg;
+        deta_dse = gp.eta_scale * sg * (1.f - sg);
+      } else {
+        eta = gp.eta_scale * (fmaxf(se, 0.f) + log1pf(fast_exp(-fabsf(se))));
+        deta_dse = gp.eta_scale * fast_rcp(1.f + fast_exp(-se));
+      }
+      const float ez = fast_exp(-(sa + gp.alpha_bias));
+      const float alpha = fast_rcp(1.f + ez);
+      const float oma = ez * alpha;  // 1 - alpha
+      const float rr0 = fast_sqrt(dd + gp.eps * gp.eps);
+      const float rr = rr0 + gp.eps;
+      const float inj = kInjInward * oma * fast_rcp(rr);
+      const bool ok = eta != 0.f && inj != 0.f;
+      const float xr = ok ? eta * fast_rcp(inj) : 0.f;
+      const float ex = fast_exp(-xr);
+      const float bar = ok ? inj * one_minus_exp_neg(xr) : 0.f;
+      const float kap = fmaxf(kk, kKappaFloor);
+      const float spec_raw = kSpecInward * 2.f * alpha * fast_rcp(kap);
+      const float spec = spec_raw > 0.f ? __uint_as_float(__float_as_uint(spec_raw) - 1u) : spec_raw;
+      // step = min(eta_bar, eta_spec)
+      float deta = 0.f, ddd = 0.f, dkk = 0.f;
+      if (bar <= spec) {
+        if (ok) {
+          deta = dstep * ex;
+          const float dinj = dstep * ((1.f - ex) - xr * ex);
+          dalpha -= dinj * kInjInward * fast_rcp(rr);
+          const float drr = -dinj * inj * fast_rcp(rr);
+          ddd = drr * 0.5f * fast_rcp(rr0);
+        }
+      } else {
+        dalpha += dstep * kSpecInward * 2.f * fast_rcp(kap);
+        if (kk > kKappaFloor) dkk = -dstep * spec_raw * fast_rcp(kap);
+      }
+      ddl = fmaf(2.f * dl, ddd, ddl);
+      dk = fmaf(2.f * k, dkk, dk);
+      dk += ddl;  // delta = k - v
+      const float dv = -ddl;
+      const float kdk = wave_sum(k * dk), qdq = wave_sum(q * dq);
+      const float dkr = (dk - k * kdk) / nk;
+      const float dqr = (dq - q * qdq) / nq;
+      pt[lane] = dkr;
+      pt[kD + lane] = dv;
+      pt[2 * kD + lane] = dqr;
+      if (lane == 0) {
+        pt[3 * kD] = deta * deta_dse;
+        pt[3 * kD + 1] = dalpha * alpha * oma;
+      }
+    }
+    __syncthreads();
+    // dx~ = S_0[proj]^T dProj (waves 0-3); dS_0 += [dy q~^T ; dProj x~^T] (all waves)
+    {
+      const Lane L = stage_lane_of(tid);
+      const int r16 = L.r16, q4 = L.q4;
+      if (w < 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int T = 4; T < 17; ++T) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc = mfma4(s0f[4 * T + s], sProj[r16 * kPL + 16 * T - 64 + 4 * s + q4], acc);
+          __builtin_amdgcn_sched_barrier(0);  // bounded operand prefetch
+        }
+        store_tokens(sdXt, w, acc, L);
+      }
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const int o = w + 8 * i;
+        if (o < 68) {
+          const int RT = o >> 2, n = o & 3;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int tk = 4 * s + q4;
+            const float av = RT < 4 ? sDY[tk * kLD + 16 * RT + r16] : sProj[tk * kPL + 16 * RT - 64 + r16];
+            const float bv = RT < 4 ? sQt[tk * kLD + 16 * n + r16] : sXt[tk * kLD + 16 * n + r16];
+            dsa[i] = mfma4(av, bv, dsa[i]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    // dx = P^T dx~ to the route plane (waves 0-3); the adjoint carry to P_c
+    if (w < 4) {
+      const Lane L = stage_lane_of(tid);
+      const f32x4 dx = dmat_tokens(sP, true, sdXt, w, L);
+      if (L.r16 < cl) {
+        float* dst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
+        *reinterpret_cast<f32x4*>(dst) = dx;
+      }
+    }
+    carry_update(true, cl);
+  }
+
+  // the initial-state adjoint of this chain, for the gradient reduction
+  {
+    const Lane L = stage_lane_of(tid);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int o = w + 8 * i;
+      if (o < 68) {
+        const int RT = o >> 2, n = o & 3;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * RT + 4 * L.q4 + v;
+          if (row < kR) dSg[(int64_t)row * kD + 16 * n + L.r16] = dsa[i][v];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool backward_wy_supported(const BackParams& p, int d) {
+  if (d != kD) return false;
+  for (int s = 0; s < p.n_sel; ++s) {
+    const int r = p.route_of_slot[s];
+    const int C = p.chunk > 0 ? p.chunk : (r < 2 ? p.W : p.H);
+    if (C > kTT) return false;
+  }
+  return true;
+}
+
+hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
+  chain_backward_wy_kernel<<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace hope

@@ -75,6 +75,9 @@ struct BackParams {
 __host__ __device__ constexpr int backward_max_chunk(int d) { return d == 64 ? 32 : 128; }
 // writes grad_x (slot 0 plane) and the route planes, then grad_init; the caller adds the planes
 hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, hipStream_t stream);
+// chunk-parallel backward on the fp32 matrix cores: d = 64, every chunk <= 16 tokens
+bool backward_wy_supported(const BackParams& p, int d);
+hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream);
 
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);

@@ -28,6 +28,15 @@ CASES = [
      dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),           # softplus gates
     (1, 4, 4, 16, 1, "f32", 15, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),  # clamps bind
     (2, 3, 4, 32, 1, "f32", 5, 0, dict(init_per_image=True)),             # routes 0 and 2, per image
+    # d = 64 with chunks of at most 16 tokens (the chunk-parallel matrix-core kernel)
+    (1, 3, 4, 64, 1, "f32", 15, 16, {}),                                  # one chunk, 12 of 16 slots
+    (1, 4, 9, 64, 1, "f32", 15, 16, dict(eta_scale=2.0)),                # full 16-token chunks, tail 4
+    (1, 4, 5, 64, 1, "f32", 15, 1, {}),                                   # one token per chunk
+    (1, 4, 4, 64, 1, "f32", 15, 3,
+     dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),           # softplus gates
+    (1, 4, 4, 64, 1, "f32", 15, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),  # clamps bind
+    (2, 3, 4, 128, 2, "f32", 5, 0, dict(init_per_image=True)),            # two heads, per image
+    (1, 5, 7, 128, 2, "bf16", 10, 0, {}),                                 # routes 1 and 3, bf16
 ]
 
 
@@ -110,3 +119,24 @@ def test_backward_full_size_content_memory_linear_response(idx):
     rel = abs(lhs - rhs) / max(abs(rhs), 1e-30)
     print(f"  <grad, V> {lhs:.6e}  linear response {rhs:.6e}  rel {rel:.2e}", flush=True)
     assert rel <= TOL["f32"]
+
+
+def test_backward_full_size_stage3_image0():
+    # The map gradient of one image depends only on that image's chains: the backward at
+    # the full 128-image batch (the launch the benchmark times) against the gradient
+    # oracle run on image 0 alone.  The backward computes in fp32 on the map's bf16 values,
+    # held to the fp32 parity tolerance.
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_backward
+    w = wl.WORKLOADS[3]
+    print("workload", w.name, flush=True)
+    inp = wl.draw_workload(w, live=True)
+    x, init = to_device(inp, w.dtype)
+    g = np.random.Generator(np.random.PCG64(95)).standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)
+    gx, _ = hope_scan2d_backward(x, init, w.n_heads, torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    got = gx[0].cpu().numpy()
+    ref, _ = hb.scan2d_backward(inp["x"][:1], inp["init"], w.n_heads, g[:1])
+    e = _rel(got, ref[0])
+    print(f"  rel grad_x[0] {e:.2e}", flush=True)
+    assert e <= TOL["f32"]
