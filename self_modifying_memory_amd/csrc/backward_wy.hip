@@ -56,14 +56,20 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float load_xw(const void* x, int bf16, int64_t idx) {
-  if (bf16) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[idx] << 16);
-  return static_cast<const float*>(x)[idx];
-}
-
 struct Lane {
   int lane, r16, q4;
 };
+
+// Sum over the wave, in every lane: DPP sums within the four 16-lane rows, then the four
+// row totals read as scalars.
+__device__ __forceinline__ float wave_total(float v) {
+  v = row16_sum(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 
 // The thread index through an opaque copy: LDS addresses derived from it are recomputed in
 // each stage instead of being hoisted out of the chunk loops and held for the whole kernel.
@@ -119,31 +125,50 @@ __device__ __forceinline__ void store_diag(float* Out, f32x4 acc, const Lane& L)
     if (4 * L.q4 + v == L.r16) Out[L.r16] = acc[v];
 }
 
+// Per-chunk record in the workspace, written by the forward sweep and read back by the
+// reverse sweep (floats): P_c (d x d), the token-major [16][d] arrays x~, k, delta, q, u, w,
+// and eight per-token scalars (step, alpha, the two norms, |k|^2, |delta|^2, s_eta, s_alpha).
+constexpr int kRecTok = kTT * kD;
+constexpr int kRec = kD * kD + 6 * kRecTok + 8 * kTT;
+
+template <bool XBF>  // the map is bf16 (else fp32)
 __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   // One LDS block, small and uniformly read arrays first so that their addresses fit the
   // 16-bit immediate offset of the LDS instructions (one base register serves them all).
   constexpr int kTok = kTT * kLD;
-  constexpr int oSc = 0;                      // per-token scalars, 8 x 16
-  constexpr int oCC = oSc + 8 * kTT;          // C x C matrices, 4 x 16 x 17
-  constexpr int oTok = oCC + 4 * kTT * kCL;   // token-major d-vectors, 18 of them
-  constexpr int oProj = oTok + 18 * kTok;     // projections [16][kPL]
-  constexpr int oP = oProj + kTT * kPL;       // P_c, dP
-  constexpr int kSmem = oP + 2 * kD * kLD;
+  constexpr int oSc = 0;                      // per-token scalars, 16 x 16
+  constexpr int oCC = oSc + 16 * kTT;         // C x C matrices, 7 x 16 x 17
+  constexpr int oTok = oCC + 7 * kTT * kCL;   // token-major d-vectors, 17 of them
+  constexpr int oProj = oTok + 17 * kTok;     // projections [16][kPL], then their adjoints
+  constexpr int oP = oProj + kTT * kPL;       // P_c, dP, D_e
+  constexpr int kSmem = oP + 3 * kD * kLD;
   __shared__ __align__(16) float smem[kSmem];
+  // per-token scalars; the first eight in record order
   float* const tSt = smem + oSc;  // step_t
   float* const tAl = tSt + kTT;   // alpha_t
-  float* const tGam = tAl + kTT;  // Gam_{t-1}
+  float* const tNk = tAl + kTT;   // sqrt(|k_raw|^2 + eps)
+  float* const tNq = tNk + kTT;   // sqrt(|q_raw|^2 + eps)
+  float* const tKk = tNq + kTT;   // |k|^2
+  float* const tDd = tKk + kTT;   // |delta|^2
+  float* const tSe = tDd + kTT;   // s_eta
+  float* const tSa = tSe + kTT;   // s_alpha
+  float* const tGam = tSa + kTT;  // Gam_{t-1}
   float* const tGp = tGam + kTT;  // Gam'_t
   float* const tL = tGp + kTT;    // k_t . a_t
-  float* const tUd = tL + kTT;    // (P u_t) . (dP k_t)
-  float* const tTr = tUd + kTT;   // <P, dP> in 4 parts, then Gam_C
-  float* const tGC = tTr + 4;
-  int* const pixb = reinterpret_cast<int*>(tTr + kTT);
-  float* const sGm = smem + oCC;  // K^T K
-  float* const sBt = sGm + kTT * kCL;
-  float* const sH = sBt + kTT * kCL;  // U^T A
-  float* const sJ = sH + kTT * kCL;   // A^T W
-  float* const sK = smem + oTok;
+  float* const tUd = tL + kTT;    // u_t . D_e k_t
+  float* const tDal = tUd + kTT;  // dalpha_t from the gain
+  float* const tMisc = tDal + kTT;  // [0] Gam_C, [1] tr(D_e)
+  int* const pixb = reinterpret_cast<int*>(tMisc + kTT);
+  float* const sGm = smem + oCC;       // K^T K
+  float* const sBt = sGm + kTT * kCL;  // beta[j][t]
+  float* const sH = sBt + kTT * kCL;   // U^T A
+  float* const sJ = sH + kTT * kCL;    // A^T W
+  float* const sCm = sJ + kTT * kCL;   // c[t][m] = beta_{t,m-1} step_m for m > t
+  float* const sNb = sCm + kTT * kCL;  // c[t][m] (k_m . k_t)
+  float* const sCf = sNb + kTT * kCL;  // coefficient of k_j in dk_t
+  // token-major arrays; the first six in record order
+  float* const sXt = smem + oTok;
+  float* const sK = sXt + kTok;
   float* const sDl = sK + kTok;
   float* const sQ = sDl + kTok;
   float* const sU = sQ + kTok;
@@ -153,17 +178,16 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   float* const sE = sZ + kTok;
   float* const sF = sE + kTok;
   float* const sX = sF + kTok;
-  float* const sXt = sX + kTok;
-  float* const sDY = sXt + kTok;
+  float* const sDY = sX + kTok;
   float* const sQt = sDY + kTok;
   float* const sdQt = sQt + kTok;
   float* const sdQ = sdQt + kTok;
-  float* const sY = sdQ + kTok;
-  float* const sPU = sY + kTok;
+  float* const sPU = sdQ + kTok;
   float* const sdXt = sPU + kTok;
-  float* const sProj = smem + oProj;  // raw projections, then their adjoints
-  float* const sP = smem + oP;        // P_c
-  float* const sdP = sP + kD * kLD;   // adjoint of P_{c+1}, then of P_c
+  float* const sProj = smem + oProj;
+  float* const sP = smem + oP;         // P_c
+  float* const sdP = sP + kD * kLD;    // adjoint of P_{c+1}, then of P_c
+  float* const sDe = sdP + kD * kLD;   // D_e = P_c^T dP
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -217,22 +241,74 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     sdP[i * kLD + j] = 0.f;
   }
 
-  // x (and dL/dy) of the chunk's tokens into LDS, zero padding slots
-  auto load_chunk = [&](int s0, int cl, bool with_dy) {
-    const int t0 = stage_lane(tid);
-    for (int e = t0; e < kTT * kD; e += 512) {
-      const int t = e >> 6, i = e & 63;
-      float xv = 0.f, gv = 0.f;
-      if (t < cl) {
-        const int pix = route_pixel(r, s0 + t, H, W, N);
-        const int64_t idx = ((int64_t)b * N + pix) * Dt + (int64_t)h * kD + i;
-        xv = load_xw(p.x, p.x_bf16, idx);
-        if (with_dy) gv = p.grad_out[idx];
+  // Inputs of a chunk, fetched into registers one chunk ahead and written to LDS when the
+  // chunk starts.  The loads are unconditional (padding slots read the chunk's last token
+  // and are zeroed when written to LDS), so nothing waits for them before then.
+  uint32_t fx[2];  // raw bits of x (bf16 in the low half, or fp32)
+  float fdy[2], fP[8], fT[12], fS;
+  auto fetch = [&](int c, bool rev) {
+    const int t0 = stage_lane(tid), s0 = c * C, cl = min(C, N - s0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = t0 + 512 * k, t = min(e >> 6, cl - 1), i = e & 63;
+      const int pix = route_pixel(r, s0 + t, H, W, N);
+      const int64_t idx = ((int64_t)b * N + pix) * Dt + (int64_t)h * kD + i;
+      if (XBF) fx[k] = static_cast<const uint16_t*>(p.x)[idx];
+      else fx[k] = __float_as_uint(static_cast<const float*>(p.x)[idx]);
+      if (rev) fdy[k] = p.grad_out[idx];
+    }
+    if (rev) {
+      const float* rec = ckpt + (int64_t)c * kRec;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) fP[k] = rec[t0 + 512 * k];
+#pragma unroll
+      for (int k = 0; k < 12; ++k) fT[k] = rec[kD * kD + t0 + 512 * k];
+      fS = rec[kD * kD + 6 * kRecTok + (t0 & 127)];
+    }
+  };
+  auto commit = [&](int c, bool rev) {
+    const int t0 = stage_lane(tid), s0 = c * C, cl = min(C, N - s0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = t0 + 512 * k, t = e >> 6, i = e & 63;
+      const float xv = XBF ? __uint_as_float(fx[k] << 16) : __uint_as_float(fx[k]);
+      sX[t * kLD + i] = t < cl ? xv : 0.f;
+      if (rev) sDY[t * kLD + i] = t < cl ? fdy[k] : 0.f;
+    }
+    if (rev) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = t0 + 512 * k;
+        sP[(e >> 6) * kLD + (e & 63)] = fP[k];
       }
-      sX[t * kLD + i] = xv;
-      if (with_dy) sDY[t * kLD + i] = gv;
+#pragma unroll
+      for (int k = 0; k < 12; ++k) {
+        const int e = t0 + 512 * k, a = e >> 10, t = (e >> 6) & 15, i = e & 63;
+        sXt[a * kTok + t * kLD + i] = fT[k];
+      }
+      if (t0 < 8 * kTT) tSt[t0] = fS;
     }
     if (t0 < kTT) pixb[t0] = t0 < cl ? route_pixel(r, s0 + t0, H, W, N) : 0;
+  };
+  // the forward sweep's record of chunk c: P_c, or the token arrays and scalars
+  auto store_P = [&](int c) {
+    const int t0 = stage_lane(tid);
+    float* rec = ckpt + (int64_t)c * kRec;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int e = t0 + 512 * k;
+      rec[e] = sP[(e >> 6) * kLD + (e & 63)];
+    }
+  };
+  auto store_tokens_rec = [&](int c) {
+    const int t0 = stage_lane(tid);
+    float* rec = ckpt + (int64_t)c * kRec;
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      const int e = t0 + 512 * k, a = e >> 10, t = (e >> 6) & 15, i = e & 63;
+      rec[kD * kD + e] = sXt[a * kTok + t * kLD + i];
+    }
+    if (t0 < 8 * kTT) rec[kD * kD + 6 * kRecTok + t0] = tSt[t0];
   };
   // projections of the chunk: waves 4-7, Proj[t][pr] = S_0[64 + pr] . x~_t
   auto projections = [&]() {
@@ -249,21 +325,34 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // k, delta, q, step, alpha of every token slot (wave per token)
+  // the stabilised normalisation of k and q (App. C.1), delta = k - v and the step of every
+  // token slot (wave per token), with the norms and gate inputs the backward reuses
   auto gates = [&](int cl) {
-    const Lane L = stage_lane_of(tid);
-    const int lane = L.lane;
+    const int lane = stage_lane(tid) & 63;
     for (int t = w; t < kTT; t += 8) {
       if (t < cl) {
         const float* pt = &sProj[t * kPL];
-        const TokenGates tg = token_gates(pt[lane], pt[kD + lane], pt[2 * kD + lane], pt[3 * kD],
-                                          pt[3 * kD + 1], gp);
-        sK[t * kLD + lane] = tg.k;
-        sDl[t * kLD + lane] = tg.delta;
-        sQ[t * kLD + lane] = tg.q;
+        const float kr = pt[lane], vr = pt[kD + lane], qr = pt[2 * kD + lane];
+        const float se = pt[3 * kD], sa = pt[3 * kD + 1];
+        const float nk = sqrtf(wave_total(kr * kr) + gp.eps);
+        const float nq = sqrtf(wave_total(qr * qr) + gp.eps);
+        const float k = kr / nk, q = qr / nq;
+        const float dl = k - vr;
+        const float kk = wave_total(k * k), dd = wave_total(dl * dl);
+        float alpha;
+        const float step = executed_step(kk, dd, se, sa, gp, &alpha);
+        sK[t * kLD + lane] = k;
+        sDl[t * kLD + lane] = dl;
+        sQ[t * kLD + lane] = q;
         if (lane == 0) {
-          tSt[t] = tg.step;
-          tAl[t] = tg.alpha;
+          tSt[t] = step;
+          tAl[t] = alpha;
+          tNk[t] = nk;
+          tNq[t] = nq;
+          tKk[t] = kk;
+          tDd[t] = dd;
+          tSe[t] = se;
+          tSa[t] = sa;
         }
       } else {
         sK[t * kLD + lane] = 0.f;
@@ -272,6 +361,12 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
         if (lane == 0) {
           tSt[t] = 0.f;
           tAl[t] = 1.f;
+          tNk[t] = 1.f;
+          tNq[t] = 1.f;
+          tKk[t] = 0.f;
+          tDd[t] = 0.f;
+          tSe[t] = 0.f;
+          tSa[t] = 0.f;
         }
       }
     }
@@ -297,7 +392,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     } else if (j == 2 && t == 0) {
       float g = 1.f;
       for (int i = 0; i < kTT; ++i) g *= tAl[i];
-      tGC[0] = g;
+      tMisc[0] = g;
     }
   };
   // u_t and w_t of the chunk (one wave, lane = component), token order
@@ -329,43 +424,31 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       if (t < cl) {
         av = tGp[t] * sE[t * kLD + lane];
 #pragma unroll
-        for (int m = t + 1; m < kTT; ++m)
-          av = fmaf(-(sBt[t * kCL + m - 1] * tSt[m] * sGm[m * kCL + t]), a[m], av);
+        for (int m = t + 1; m < kTT; ++m) av = fmaf(-sNb[t * kCL + m], a[m], av);
       }
       a[t] = av;
       sA[t * kLD + lane] = av;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // P <- Gam_C P + (P U) diag(beta_{., cl-1}) K^T (M = sP), or the adjoint carry
-  // dP <- Gam_C dP + (dP K) diag(beta) U^T + dX~ X^T + dQ~ Q^T (M = sdP); 16 tiles, 2 per wave
-  auto carry_update = [&](bool adjoint, int cl) {
+  // tile idx (0-15) of a d x d matrix in LDS: M <- gc M + sum over the 16 token slots of
+  // (A1_t scaled by sc_t) B1_t^T [+ A2_t B2_t^T]
+  auto dd_update = [&](float* M, int idx, float gc, const float* A1, const float* B1, bool scale,
+                       int cl, const float* A2, const float* B2) {
     const Lane L = stage_lane_of(tid);
-    const int r16 = L.r16, q4 = L.q4;
-    float* M = adjoint ? sdP : sP;
-    const float gc = tGC[0];
+    const int r16 = L.r16, q4 = L.q4, mi = idx >> 2, nj = idx & 3;
+    f32x4 acc;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int idx = w + 8 * k2, mi = idx >> 2, nj = idx & 3;
-      f32x4 acc;
+    for (int v = 0; v < 4; ++v) acc[v] = gc * M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = gc * M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int tk = 4 * s + q4;
-        const float bet = sBt[tk * kCL + cl - 1];
-        if (adjoint) {
-          acc = mfma4(sZ[tk * kLD + 16 * mi + r16] * bet, sU[tk * kLD + 16 * nj + r16], acc);
-          acc = mfma4(sdXt[tk * kLD + 16 * mi + r16], sX[tk * kLD + 16 * nj + r16], acc);
-          acc = mfma4(sdQt[tk * kLD + 16 * mi + r16], sQ[tk * kLD + 16 * nj + r16], acc);
-        } else {
-          acc = mfma4(sPU[tk * kLD + 16 * mi + r16] * bet, sK[tk * kLD + 16 * nj + r16], acc);
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
-      __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < 4; ++s) {
+      const int tk = 4 * s + q4;
+      const float sc = scale ? sBt[tk * kCL + cl - 1] : 1.f;
+      acc = mfma4(A1[tk * kLD + 16 * mi + r16] * sc, B1[tk * kLD + 16 * nj + r16], acc);
+      if (A2) acc = mfma4(A2[tk * kLD + 16 * mi + r16], B2[tk * kLD + 16 * nj + r16], acc);
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
   };
   auto dtok = [&](float* Out, const float* M, bool trans, const float* In, int m) {
     const Lane L = stage_lane_of(tid);
@@ -380,152 +463,184 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     store_diag(Out, gram_tokens(A, B, L), L);
   };
 
+  fetch(0, false);
   __syncthreads();
 
-  // ---- forward sweep: P_c of every chunk into the workspace ---------------------------
+  // ---- forward sweep: the record of every chunk into the workspace --------------------
+  // (barriers order LDS only; global loads stay in flight across them, and the stores are
+  // issued after each chunk's prefetch so that waiting for the prefetch skips them)
   for (int c = 0; c < nck; ++c) {
     const int s0 = c * C, cl = min(C, N - s0);
-    for (int e = stage_lane(tid); e < kD * kD; e += 512) ckpt[(int64_t)c * kD * kD + e] = sP[(e >> 6) * kLD + (e & 63)];
-    if (c == nck - 1) break;  // P after the last chunk is not needed
-    load_chunk(s0, cl, false);
-    __syncthreads();
+    commit(c, false);
+    fetch(min(c + 1, nck - 1), false);  // (the last fetch is not used)
+    store_P(c);
+    if (c > 0) store_tokens_rec(c - 1);
+    lds_barrier();
     if (w < 4) dtok(sXt, sP, false, sX, w);
-    __syncthreads();
+    lds_barrier();
     if (w >= 4) projections();
-    __syncthreads();
+    lds_barrier();
     gates(cl);
-    __syncthreads();
+    lds_barrier();
     if (w == 0) gram(sGm, sK, sK);
     if (w >= 4) alpha_products();
-    __syncthreads();
+    lds_barrier();
     if (w == 0) solve_u(cl);
-    __syncthreads();
+    lds_barrier();
+    if (c == nck - 1) break;
     if (w < 4) dtok(sPU, sP, false, sU, w);
-    __syncthreads();
-    carry_update(false, cl);
-    __syncthreads();
+    lds_barrier();
+    // P <- Gam_C P + (P U) diag(beta_{., cl-1}) K^T
+    {
+      const float gc = tMisc[0];
+      dd_update(sP, w, gc, sPU, sK, true, cl, nullptr, nullptr);
+      dd_update(sP, w + 8, gc, sPU, sK, true, cl, nullptr, nullptr);
+      (void)s0;
+    }
+    lds_barrier();
   }
+  store_tokens_rec(nck - 1);
 
   // ---- reverse sweep ---------------------------------------------------------------------
+  __syncthreads();  // the records written above are visible to every thread
+  fetch(nck - 1, true);
+  // dx of a chunk is stored after the next chunk's prefetch is issued (same reason)
+  f32x4 dxv = {0.f, 0.f, 0.f, 0.f};
+  float* dxdst = gdst;
+  bool dxok = false;
   for (int c = nck - 1; c >= 0; --c) {
-    const int s0 = c * C, cl = min(C, N - s0);
-    __syncthreads();
-    for (int e = stage_lane(tid); e < kD * kD; e += 512) sP[(e >> 6) * kLD + (e & 63)] = ckpt[(int64_t)c * kD * kD + e];
-    load_chunk(s0, cl, true);
-    __syncthreads();
-    // x~ = P x; <P, dP> in parts
-    if (w < 4) {
-      dtok(sXt, sP, false, sX, w);
-    } else {
-      const int t0 = stage_lane(tid);
-      float tr = 0.f;
-      for (int e = t0 - 256; e < kD * kD; e += 256) {
-        const int o = (e >> 6) * kLD + (e & 63);
-        tr = fmaf(sP[o], sdP[o], tr);
-      }
-      tr = wave_sum(tr);
-      if ((t0 & 63) == 0) tTr[w - 4] = tr;
-    }
-    __syncthreads();
-    // projections; dq~ = S_0[mem]^T dy (waves 0-3)
-    if (w >= 4) {
-      projections();
-    } else {
+    const int cl = min(C, N - c * C);
+    lds_barrier();
+    commit(c, true);
+    fetch(max(c - 1, 0), true);  // (the last fetch is not used)
+    if (dxok) *reinterpret_cast<f32x4*>(dxdst) = dxv;
+    lds_barrier();
+    // D_e = P^T dP (16 tiles, 2 per wave); dq~ = S_0[mem]^T dy (waves 0-3); K^T K; beta
+    {
       const Lane L = stage_lane_of(tid);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int r16 = L.r16, q4 = L.q4;
 #pragma unroll
-      for (int T = 0; T < 4; ++T)
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int idx = 2 * w + k2, mi = idx >> 2, nj = idx & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc = mfma4(s0f[4 * T + s], sDY[L.r16 * kLD + 16 * T + 4 * s + L.q4], acc);
-      store_tokens(sdQt, w, acc, L);
+        for (int s = 0; s < kD / 4; ++s) {
+          const int k = 4 * s + q4;
+          acc = mfma4(sP[k * kLD + 16 * mi + r16], sdP[k * kLD + 16 * nj + r16], acc);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sDe[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (w < 4) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) acc = mfma4(s0f[4 * T + s], sDY[r16 * kLD + 16 * T + 4 * s + q4], acc);
+        store_tokens(sdQt, w, acc, L);
+      }
     }
-    __syncthreads();
-    gates(cl);
-    __syncthreads();
-    // K^T K, alpha products; q~ = P q, Z = dP K, dq = P^T dq~
-    if (w == 0) gram(sGm, sK, sK);
+    if (w == 4) gram(sGm, sK, sK);
     if (w >= 4) alpha_products();
-    for (int jb = w; jb < 12; jb += 8) {
+    lds_barrier();
+    // E = D_e K, Z = dP K, q~ = P q, dq = P^T dq~, F = D_e^T W; tr(D_e); c and c (k.k)
+    for (int jb = w; jb < 20; jb += 8) {
       const int kind = jb >> 2, m = jb & 3;
-      if (kind == 0) dtok(sQt, sP, false, sQ, m);
+      if (kind == 0) dtok(sE, sDe, false, sK, m);
       else if (kind == 1) dtok(sZ, sdP, false, sK, m);
-      else dtok(sdQ, sP, true, sdQt, m);
+      else if (kind == 2) dtok(sQt, sP, false, sQ, m);
+      else if (kind == 3) dtok(sdQ, sP, true, sdQt, m);
+      else dtok(sF, sDe, true, sW, m);
     }
-    __syncthreads();
-    // u, w (wave 0); E = P^T Z = D_e K
-    if (w == 0) {
-      solve_u(cl);
-    } else if (w <= 4) {
-      dtok(sE, sP, true, sZ, w - 1);
+    if (w == 7) {
+      const int lane = stage_lane(tid) & 63;
+      const float tr = wave_total(sDe[lane * kLD + lane]);
+      if (lane == 0) tMisc[1] = tr;
     }
-    __syncthreads();
-    // a (wave 0); Y = P W, PU = P U
+    if (w >= 4) {
+      const int e = stage_lane(tid) - 256, t = e >> 4, m = e & 15;
+      const float cm = m > t ? sBt[t * kCL + m - 1] * tSt[m] : 0.f;
+      sCm[t * kCL + m] = cm;
+      sNb[t * kCL + m] = cm * sGm[m * kCL + t];
+    }
+    lds_barrier();
+    // a (wave 0); the adjoint carry's first part on waves 1-7:
+    // dP <- Gam_C dP + (dP K) diag(beta_{., cl-1}) U^T + dq~ q^T
     if (w == 0) {
       solve_a(cl);
     } else {
-      for (int jb = w - 1; jb < 8; jb += 7) {
-        const int m = jb & 3;
-        if (jb < 4) dtok(sY, sP, false, sW, m);
-        else dtok(sPU, sP, false, sU, m);
-      }
+      const float gc = tMisc[0];
+      for (int idx = w - 1; idx < 16; idx += 7) dd_update(sdP, idx, gc, sZ, sU, true, cl, sdQt, sQ);
     }
-    __syncthreads();
-    // F = dP^T Y = D_e^T W; H = U^T A, J = A^T W, diag(K^T A), diag((P U)^T Z)
-    if (w < 4) dtok(sF, sdP, true, sY, w);
-    else if (w == 4) gram(sH, sU, sA);
+    lds_barrier();
+    // H = U^T A, J = A^T W, diag(K^T A), diag(U^T E)
+    if (w == 4) gram(sH, sU, sA);
     else if (w == 5) gram(sJ, sA, sW);
     else if (w == 6) gram_diag(tL, sK, sA);
-    else gram_diag(tUd, sPU, sZ);
-    __syncthreads();
-    // token by token: the gain adjoints, then the readout, the step, the gates, the
-    // normalisation and the projections; dProj replaces Proj in place
-    for (int t = w; t < cl; t += 8) {
-      const int lane = stage_lane(tid) & 63;
-      const float st = tSt[t], gam = tGam[t], gp1 = tGp[t];
-      // lanes j < 16: the coefficient of k_j in dk_t and the j-part of dalpha_t
-      float cf = 0.f, term = 0.f;
-      if (lane < kTT) {
-        const int j = lane;
-        if (j < t) {
-          const float bj = sBt[j * kCL + t - 1];
-          cf = bj * sH[j * kCL + t];
-          float inner = 0.f;
-          for (int m = t + 1; m < kTT; ++m)
-            inner = fmaf(sBt[t * kCL + m - 1] * tSt[m], sH[j * kCL + m] * sGm[j * kCL + m], inner);
-          term = bj * (gp1 * tUd[j] - inner);
-        } else if (j > t) {
-          cf = -sBt[t * kCL + j - 1] * tSt[j] * sJ[j * kCL + t];
-        } else {
-          float lsum = 0.f;
-          for (int m = t + 1; m < kTT; ++m) lsum = fmaf(sBt[t * kCL + m - 1] * tSt[m], tL[m], lsum);
-          const float tr = (tTr[0] + tTr[1]) + (tTr[2] + tTr[3]);
-          term = gam * (gp1 * tr - lsum);
-        }
-      }
-      term = row16_sum(term);
-      float dalpha = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, term)));
-      const float at = sA[t * kLD + lane];
-      float gk = fmaf(gam, at, gp1 * sF[t * kLD + lane]);
+    else if (w == 7) gram_diag(tUd, sU, sE);
+    lds_barrier();
+    // dalpha_t from the gain (wave 0, through the C x C product inner = (H o K^T K) c^T);
+    // the coefficients of k_j in dk_t (waves 1-4)
+    if (w == 0) {
+      const Lane L = stage_lane_of(tid);
+      const int r16 = L.r16, q4 = L.q4;
+      f32x4 inner = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kTT; ++j) {
-        const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cf), j));
-        gk = fmaf(cj, sK[j * kLD + lane], gk);
+      for (int s = 0; s < 4; ++s) {
+        const int m = 4 * s + q4;
+        inner = mfma4(sH[r16 * kCL + m] * sGm[r16 * kCL + m], sCm[r16 * kCL + m], inner);
       }
+      // inner[j = 4 q4 + v][t = r16]
+      const int t = r16;
+      const float gp1 = tGp[t];
+      float part = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 4 * q4 + v;
+        if (j < t) part = fmaf(sBt[j * kCL + t - 1], gp1 * tUd[j] - inner[v], part);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (q4 == 0) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int m = 0; m < kTT; ++m) lsum = fmaf(sCm[t * kCL + m], tL[m], lsum);
+        tDal[t] = part + tGam[t] * (gp1 * tMisc[1] - lsum);
+      }
+    } else if (w <= 4) {
+      const int e = stage_lane(tid) - 64, t = e >> 4, j = e & 15;
+      float cf = 0.f;
+      if (j < t) cf = sBt[j * kCL + t - 1] * sH[j * kCL + t];
+      else if (j > t) cf = -sCm[t * kCL + j] * sJ[j * kCL + t];
+      sCf[j * kCL + t] = cf;
+    }
+    lds_barrier();
+    // token by token: the gain adjoints, then the readout, the step, the gates, the
+    // normalisation and the projections; dProj replaces Proj (zero rows in padding slots)
+    for (int t = w; t < kTT; t += 8) {
+      const int lane = stage_lane(tid) & 63;
+      float* pt = &sProj[t * kPL];
+      if (t >= cl) {
+        pt[lane] = 0.f;
+        pt[kD + lane] = 0.f;
+        pt[2 * kD + lane] = 0.f;
+        if (lane < 16) pt[3 * kD + lane] = 0.f;
+        continue;
+      }
+      const float st = tSt[t];
+      const float at = sA[t * kLD + lane];
+      float gk = fmaf(tGam[t], at, tGp[t] * sF[t * kLD + lane]);
+#pragma unroll
+      for (int j = 0; j < kTT; ++j) gk = fmaf(sCf[j * kCL + t], sK[j * kLD + lane], gk);
       float dk = -st * gk;
       float ddl = -st * at;
       const float dstep = -sJ[t * kCL + t];
+      float dalpha = tDal[t];
       const float dq = sdQ[t * kLD + lane];
-
-      float* pt = &sProj[t * kPL];
-      const float kr = pt[lane], vr = pt[kD + lane], qr = pt[2 * kD + lane];
-      const float se = pt[3 * kD], sa = pt[3 * kD + 1];
-      // forward values, as in token_gates / executed_step
-      const float nk = sqrtf(wave_sum(kr * kr) + gp.eps);
-      const float nq = sqrtf(wave_sum(qr * qr) + gp.eps);
-      const float k = kr / nk, q = qr / nq;
-      const float dl = k - vr;
-      const float dd = wave_sum(dl * dl), kk = wave_sum(k * k);
+      // forward values, as in the gates and executed_step
+      const float k = sK[t * kLD + lane], q = sQ[t * kLD + lane], dl = sDl[t * kLD + lane];
+      const float nk = tNk[t], nq = tNq[t], kk = tKk[t], dd = tDd[t], se = tSe[t], sa = tSa[t];
       float eta, deta_dse;
       if (gp.eta_map == 0) {
         const float sg = fast_rcp(1.f + fast_exp(-se));
@@ -566,7 +681,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       dk = fmaf(2.f * k, dkk, dk);
       dk += ddl;  // delta = k - v
       const float dv = -ddl;
-      const float kdk = wave_sum(k * dk), qdq = wave_sum(q * dq);
+      const float kdk = wave_total(k * dk), qdq = wave_total(q * dq);
       const float dkr = (dk - k * kdk) / nk;
       const float dqr = (dq - q * qdq) / nq;
       pt[lane] = dkr;
@@ -577,7 +692,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
         pt[3 * kD + 1] = dalpha * alpha * oma;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dx~ = S_0[proj]^T dProj (waves 0-3); dS_0 += [dy q~^T ; dProj x~^T] (all waves)
     {
       const Lane L = stage_lane_of(tid);
@@ -609,18 +724,19 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
-    // dx = P^T dx~ to the route plane (waves 0-3); the adjoint carry to P_c
+    lds_barrier();
+    // dx = P^T dx~ (waves 0-3, stored next chunk); the adjoint carry's last part
+    // dP <- dP + dx~ x^T
     if (w < 4) {
       const Lane L = stage_lane_of(tid);
-      const f32x4 dx = dmat_tokens(sP, true, sdXt, w, L);
-      if (L.r16 < cl) {
-        float* dst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
-        *reinterpret_cast<f32x4*>(dst) = dx;
-      }
+      dxv = dmat_tokens(sP, true, sdXt, w, L);
+      dxok = L.r16 < cl;
+      dxdst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
     }
-    carry_update(true, cl);
+    dd_update(sdP, w, 1.f, sdXt, sX, false, cl, nullptr, nullptr);
+    dd_update(sdP, w + 8, 1.f, sdXt, sX, false, cl, nullptr, nullptr);
   }
+  if (dxok) *reinterpret_cast<f32x4*>(dxdst) = dxv;
 
   // the initial-state adjoint of this chain, for the gradient reduction
   {
@@ -654,7 +770,8 @@ bool backward_wy_supported(const BackParams& p, int d) {
 
 hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
-  chain_backward_wy_kernel<<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(p);
+  if (p.x_bf16) chain_backward_wy_kernel<true><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(p);
+  else chain_backward_wy_kernel<false><<<dim3((unsigned)blocks), dim3(512), 0, stream>>>(p);
   return hipGetLastError();
 }
 
