@@ -127,7 +127,8 @@ __device__ __forceinline__ void store_diag(float* Out, f32x4 acc, const Lane& L)
 
 // Per-chunk record in the workspace, written by the forward sweep and read back by the
 // reverse sweep (floats): P_c (d x d), the token-major [16][d] arrays x~, k, delta, q, u, w,
-// and eight per-token scalars (step, alpha, the two norms, |k|^2, |delta|^2, s_eta, s_alpha).
+// and eight per-token scalars (step, alpha, the two reciprocal norms, |k|^2, |delta|^2, s_eta,
+// s_alpha).
 constexpr int kRecTok = kTT * kD;
 constexpr int kRec = kD * kD + 6 * kRecTok + 8 * kTT;
 
@@ -137,17 +138,18 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   // 16-bit immediate offset of the LDS instructions (one base register serves them all).
   constexpr int kTok = kTT * kLD;
   constexpr int oSc = 0;                      // per-token scalars, 16 x 16
-  constexpr int oCC = oSc + 16 * kTT;         // C x C matrices, 7 x 16 x 17
-  constexpr int oTok = oCC + 7 * kTT * kCL;   // token-major d-vectors, 17 of them
-  constexpr int oProj = oTok + 17 * kTok;     // projections [16][kPL], then their adjoints
-  constexpr int oP = oProj + kTT * kPL;       // P_c, dP, D_e
-  constexpr int kSmem = oP + 3 * kD * kLD;
+  constexpr int oCC = oSc + 16 * kTT;         // C x C matrices, 6 x 16 x 17
+  constexpr int oRow = oCC + 6 * kTT * kCL;   // solve coefficient rows, 16 x 16
+  constexpr int oTok = oRow + kTT * kTT;      // token-major d-vectors, 18 of them
+  constexpr int oProj = oTok + 18 * kTok;     // projections [16][kPL], then their adjoints
+  constexpr int oP = oProj + kTT * kPL;       // P_c, dP
+  constexpr int kSmem = oP + 2 * kD * kLD;
   __shared__ __align__(16) float smem[kSmem];
   // per-token scalars; the first eight in record order
   float* const tSt = smem + oSc;  // step_t
   float* const tAl = tSt + kTT;   // alpha_t
-  float* const tNk = tAl + kTT;   // sqrt(|k_raw|^2 + eps)
-  float* const tNq = tNk + kTT;   // sqrt(|q_raw|^2 + eps)
+  float* const tNk = tAl + kTT;   // 1 / sqrt(|k_raw|^2 + eps)
+  float* const tNq = tNk + kTT;   // 1 / sqrt(|q_raw|^2 + eps)
   float* const tKk = tNq + kTT;   // |k|^2
   float* const tDd = tKk + kTT;   // |delta|^2
   float* const tSe = tDd + kTT;   // s_eta
@@ -157,15 +159,17 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   float* const tL = tGp + kTT;    // k_t . a_t
   float* const tUd = tL + kTT;    // u_t . D_e k_t
   float* const tDal = tUd + kTT;  // dalpha_t from the gain
-  float* const tMisc = tDal + kTT;  // [0] Gam_C, [1] tr(D_e)
+  float* const tMisc = tDal + kTT;  // [0] Gam_C, [8..11] parts of <P, dP> = tr(D_e)
   int* const pixb = reinterpret_cast<int*>(tMisc + kTT);
   float* const sGm = smem + oCC;       // K^T K
   float* const sBt = sGm + kTT * kCL;  // beta[j][t]
   float* const sH = sBt + kTT * kCL;   // U^T A
   float* const sJ = sH + kTT * kCL;    // A^T W
   float* const sCm = sJ + kTT * kCL;   // c[t][m] = beta_{t,m-1} step_m for m > t
-  float* const sNb = sCm + kTT * kCL;  // c[t][m] (k_m . k_t)
-  float* const sCf = sNb + kTT * kCL;  // coefficient of k_j in dk_t
+  float* const sCf = sCm + kTT * kCL;  // coefficient of k_j in dk_t
+  // row t of a solve's coefficients: beta_{j,t-1} (k_j . k_t) for j < t (u), or
+  // c[t][m] (k_m . k_t) for m > t (a)
+  float* const sRow = smem + oRow;
   // token-major arrays; the first six in record order
   float* const sXt = smem + oTok;
   float* const sK = sXt + kTok;
@@ -184,10 +188,10 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   float* const sdQ = sdQt + kTok;
   float* const sPU = sdQ + kTok;
   float* const sdXt = sPU + kTok;
+  float* const sY = sdXt + kTok;
   float* const sProj = smem + oProj;
   float* const sP = smem + oP;         // P_c
   float* const sdP = sP + kD * kLD;    // adjoint of P_{c+1}, then of P_c
-  float* const sDe = sdP + kD * kLD;   // D_e = P_c^T dP
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -329,45 +333,51 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   // token slot (wave per token), with the norms and gate inputs the backward reuses
   auto gates = [&](int cl) {
     const int lane = stage_lane(tid) & 63;
-    for (int t = w; t < kTT; t += 8) {
-      if (t < cl) {
-        const float* pt = &sProj[t * kPL];
-        const float kr = pt[lane], vr = pt[kD + lane], qr = pt[2 * kD + lane];
-        const float se = pt[3 * kD], sa = pt[3 * kD + 1];
-        const float nk = sqrtf(wave_total(kr * kr) + gp.eps);
-        const float nq = sqrtf(wave_total(qr * qr) + gp.eps);
-        const float k = kr / nk, q = qr / nq;
-        const float dl = k - vr;
-        const float kk = wave_total(k * k), dd = wave_total(dl * dl);
-        float alpha;
-        const float step = executed_step(kk, dd, se, sa, gp, &alpha);
-        sK[t * kLD + lane] = k;
-        sDl[t * kLD + lane] = dl;
-        sQ[t * kLD + lane] = q;
-        if (lane == 0) {
-          tSt[t] = step;
-          tAl[t] = alpha;
-          tNk[t] = nk;
-          tNq[t] = nq;
-          tKk[t] = kk;
-          tDd[t] = dd;
-          tSe[t] = se;
-          tSa[t] = sa;
-        }
-      } else {
-        sK[t * kLD + lane] = 0.f;
-        sDl[t * kLD + lane] = 0.f;
-        sQ[t * kLD + lane] = 0.f;
-        if (lane == 0) {
-          tSt[t] = 0.f;
-          tAl[t] = 1.f;
-          tNk[t] = 1.f;
-          tNq[t] = 1.f;
-          tKk[t] = 0.f;
-          tDd[t] = 0.f;
-          tSe[t] = 0.f;
-          tSa[t] = 0.f;
-        }
+    float kr[2], vr[2], qr[2], se[2], sa[2], nk[2], nq[2], k[2], q[2], dl[2], kk[2], dd[2], al[2], st[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float* pt = &sProj[(w + 8 * u) * kPL];
+      kr[u] = pt[lane];
+      vr[u] = pt[kD + lane];
+      qr[u] = pt[2 * kD + lane];
+      se[u] = pt[3 * kD];
+      sa[u] = pt[3 * kD + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      nk[u] = fast_rsqrt(wave_total(kr[u] * kr[u]) + gp.eps);
+      nq[u] = fast_rsqrt(wave_total(qr[u] * qr[u]) + gp.eps);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      k[u] = kr[u] * nk[u];
+      q[u] = qr[u] * nq[u];
+      dl[u] = k[u] - vr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kk[u] = wave_total(k[u] * k[u]);
+      dd[u] = wave_total(dl[u] * dl[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) st[u] = executed_step(kk[u], dd[u], se[u], sa[u], gp, &al[u]);
+    // padding slots (t >= cl): zero vectors, step 0, alpha 1, unit norms
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = w + 8 * u;
+      const bool on = t < cl;
+      sK[t * kLD + lane] = on ? k[u] : 0.f;
+      sDl[t * kLD + lane] = on ? dl[u] : 0.f;
+      sQ[t * kLD + lane] = on ? q[u] : 0.f;
+      if (lane == 0) {
+        tSt[t] = on ? st[u] : 0.f;
+        tAl[t] = on ? al[u] : 1.f;
+        tNk[t] = on ? nk[u] : 1.f;
+        tNq[t] = on ? nq[u] : 1.f;
+        tKk[t] = on ? kk[u] : 0.f;
+        tDd[t] = on ? dd[u] : 0.f;
+        tSe[t] = on ? se[u] : 0.f;
+        tSa[t] = on ? sa[u] : 0.f;
       }
     }
   };
@@ -375,59 +385,59 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   // Bt[j][t] = alpha_{j+1} .. alpha_t (j <= t, else 0), Gam_{t-1}, Gam'_t, Gam_C
   auto alpha_products = [&]() {
     const int e = stage_lane(tid) - 256, t = e >> 4, j = e & 15;
-    float bt = 0.f;
-    if (j <= t) {
-      bt = 1.f;
-      for (int i = j + 1; i <= t; ++i) bt *= tAl[i];
+    float al[kTT];
+#pragma unroll
+    for (int i = 0; i < kTT; ++i) al[i] = tAl[i];
+    float bt = 1.f, gm = 1.f, gq = 1.f, gc = 1.f;
+#pragma unroll
+    for (int i = 0; i < kTT; ++i) {
+      bt *= (i > j && i <= t) ? al[i] : 1.f;
+      gm *= i < t ? al[i] : 1.f;
+      gq *= i > t ? al[i] : 1.f;
+      gc *= al[i];
     }
-    sBt[j * kCL + t] = bt;
-    if (j == 0) {
-      float g = 1.f;
-      for (int i = 0; i < t; ++i) g *= tAl[i];
-      tGam[t] = g;
-    } else if (j == 1) {
-      float g = 1.f;
-      for (int i = t + 1; i < kTT; ++i) g *= tAl[i];
-      tGp[t] = g;
-    } else if (j == 2 && t == 0) {
-      float g = 1.f;
-      for (int i = 0; i < kTT; ++i) g *= tAl[i];
-      tMisc[0] = g;
-    }
+    sBt[j * kCL + t] = j <= t ? bt : 0.f;
+    if (j == 0) tGam[t] = gm;
+    else if (j == 1) tGp[t] = gq;
+    else if (j == 2 && t == 0) tMisc[0] = gc;
   };
-  // u_t and w_t of the chunk (one wave, lane = component), token order
-  auto solve_u = [&](int cl) {
+  // A one-wave triangular recurrence over the 16 token slots, lane = component:
+  // v_t = base_t + sum_j sRow[t][j] v_j over the already computed j (j < t forward,
+  // j > t backward); the coefficient row of the next step is loaded during this one.
+  auto solve_rows = [&](bool backward, int cl, const float* g0, const float* B0, const float* B1,
+                        float* Out, float* Out2, const float* gscale) {
     const int lane = stage_lane(tid) & 63;
-    float u[kTT];
+    float v[kTT];
 #pragma unroll
-    for (int t = 0; t < kTT; ++t) {
-      float wv = 0.f, uv = 0.f;
-      if (t < cl) {
-        wv = fmaf(tGam[t], sK[t * kLD + lane], sDl[t * kLD + lane]);
+    for (int t = 0; t < kTT; ++t) v[t] = 0.f;
+    f32x4 row[4], nxt[4];
+    float ng, nb0, nb1 = 0.f, ngs = 0.f;
+    auto load_step = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < t; ++j) wv = fmaf(sBt[j * kCL + t - 1] * sGm[j * kCL + t], u[j], wv);
-        uv = -tSt[t] * wv;
-      }
-      u[t] = uv;
-      sU[t * kLD + lane] = uv;
-      sW[t * kLD + lane] = wv;
-      __builtin_amdgcn_sched_barrier(0);  // one token's coefficient loads in flight at a time
-    }
-  };
-  // a_t of the chunk (one wave, reverse token order)
-  auto solve_a = [&](int cl) {
-    const int lane = stage_lane(tid) & 63;
-    float a[kTT];
+      for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const f32x4*>(&sRow[t * kTT + 4 * q]);
+      ng = g0[t];
+      nb0 = B0[t * kLD + lane];
+      if (B1) nb1 = B1[t * kLD + lane];
+      if (gscale) ngs = gscale[t];
+    };
+    load_step(backward ? kTT - 1 : 0);
 #pragma unroll
-    for (int t = kTT - 1; t >= 0; --t) {
-      float av = 0.f;
-      if (t < cl) {
-        av = tGp[t] * sE[t * kLD + lane];
+    for (int n = 0; n < kTT; ++n) {
+      const int t = backward ? kTT - 1 - n : n;
 #pragma unroll
-        for (int m = t + 1; m < kTT; ++m) av = fmaf(-sNb[t * kCL + m], a[m], av);
-      }
-      a[t] = av;
-      sA[t * kLD + lane] = av;
+      for (int q = 0; q < 4; ++q) row[q] = nxt[q];
+      const float g = ng, b0 = nb0, b1 = nb1, gs = ngs;
+      if (n + 1 < kTT) load_step(backward ? t - 1 : t + 1);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kTT; ++j)
+        if (backward ? j > t : j < t) acc[j & 3] = fmaf(row[j >> 2][j & 3], v[j], acc[j & 3]);
+      const float base = B1 ? fmaf(g, b0, b1) : g * b0;
+      const float pre = t < cl ? base + ((acc[0] + acc[1]) + (acc[2] + acc[3])) : 0.f;
+      const float val = gscale ? -gs * pre : pre;
+      v[t] = val;
+      Out[t * kLD + lane] = val;
+      if (Out2) Out2[t * kLD + lane] = pre;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -463,6 +473,20 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     store_diag(Out, gram_tokens(A, B, L), L);
   };
 
+  // dS_0[M_mem rows] += dy q~^T for this wave's two M_mem tiles (i = 0, 1)
+  auto mem_rows_dS0 = [&]() {
+    const Lane L = stage_lane_of(tid);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int o = w + 8 * i, RT = o >> 2, n = o & 3;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int tk = 4 * s + L.q4;
+        dsa[i] = mfma4(sDY[tk * kLD + 16 * RT + L.r16], sQt[tk * kLD + 16 * n + L.r16], dsa[i]);
+      }
+    }
+  };
+
   fetch(0, false);
   __syncthreads();
 
@@ -485,7 +509,16 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     if (w == 0) gram(sGm, sK, sK);
     if (w >= 4) alpha_products();
     lds_barrier();
-    if (w == 0) solve_u(cl);
+    if (w == 0) {
+      // coefficient rows beta_{j,t-1} (k_j . k_t), j < t, then the recurrence for w and u
+      const int lane = stage_lane(tid) & 63;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = lane + 64 * k, t = e >> 4, j = e & 15;
+        sRow[e] = j < t ? sBt[j * kCL + t - 1] * sGm[j * kCL + t] : 0.f;
+      }
+      solve_rows(false, cl, tGam, sK, sDl, sU, sW, tSt);
+    }
     lds_barrier();
     if (c == nck - 1) break;
     if (w < 4) dtok(sPU, sP, false, sU, w);
@@ -515,63 +548,54 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     fetch(max(c - 1, 0), true);  // (the last fetch is not used)
     if (dxok) *reinterpret_cast<f32x4*>(dxdst) = dxv;
     lds_barrier();
-    // D_e = P^T dP (16 tiles, 2 per wave); dq~ = S_0[mem]^T dy (waves 0-3); K^T K; beta
-    {
+    // dq~ = S_0[mem]^T dy and parts of <P, dP> (waves 0-3); Z = dP K, Y = P W (waves 4-7);
+    // K^T K (wave 4); beta (waves 4-7)
+    if (w < 4) {
       const Lane L = stage_lane_of(tid);
-      const int r16 = L.r16, q4 = L.q4;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int idx = 2 * w + k2, mi = idx >> 2, nj = idx & 3;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int T = 0; T < 4; ++T)
 #pragma unroll
-        for (int s = 0; s < kD / 4; ++s) {
-          const int k = 4 * s + q4;
-          acc = mfma4(sP[k * kLD + 16 * mi + r16], sdP[k * kLD + 16 * nj + r16], acc);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sDe[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < 4; ++s) acc = mfma4(s0f[4 * T + s], sDY[L.r16 * kLD + 16 * T + 4 * s + L.q4], acc);
+      store_tokens(sdQt, w, acc, L);
+      float tr = 0.f;
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const int e = 64 * w + L.lane + 256 * k, o = (e >> 6) * kLD + (e & 63);
+        tr = fmaf(sP[o], sdP[o], tr);
       }
-      if (w < 4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma4(s0f[4 * T + s], sDY[r16 * kLD + 16 * T + 4 * s + q4], acc);
-        store_tokens(sdQt, w, acc, L);
-      }
+      tr = wave_total(tr);
+      if (L.lane == 0) tMisc[8 + w] = tr;
+    } else {
+      dtok(sZ, sdP, false, sK, w - 4);
+      dtok(sY, sP, false, sW, w - 4);
+      if (w == 4) gram(sGm, sK, sK);
+      alpha_products();
     }
-    if (w == 4) gram(sGm, sK, sK);
-    if (w >= 4) alpha_products();
     lds_barrier();
-    // E = D_e K, Z = dP K, q~ = P q, dq = P^T dq~, F = D_e^T W; tr(D_e); c and c (k.k)
-    for (int jb = w; jb < 20; jb += 8) {
+    // E = P^T Z = D_e K, F = dP^T Y = D_e^T W, q~ = P q, dq = P^T dq~; c and the a-solve rows
+    for (int jb = w; jb < 16; jb += 8) {
       const int kind = jb >> 2, m = jb & 3;
-      if (kind == 0) dtok(sE, sDe, false, sK, m);
-      else if (kind == 1) dtok(sZ, sdP, false, sK, m);
+      if (kind == 0) dtok(sE, sP, true, sZ, m);
+      else if (kind == 1) dtok(sF, sdP, true, sY, m);
       else if (kind == 2) dtok(sQt, sP, false, sQ, m);
-      else if (kind == 3) dtok(sdQ, sP, true, sdQt, m);
-      else dtok(sF, sDe, true, sW, m);
-    }
-    if (w == 7) {
-      const int lane = stage_lane(tid) & 63;
-      const float tr = wave_total(sDe[lane * kLD + lane]);
-      if (lane == 0) tMisc[1] = tr;
+      else dtok(sdQ, sP, true, sdQt, m);
     }
     if (w >= 4) {
       const int e = stage_lane(tid) - 256, t = e >> 4, m = e & 15;
       const float cm = m > t ? sBt[t * kCL + m - 1] * tSt[m] : 0.f;
       sCm[t * kCL + m] = cm;
-      sNb[t * kCL + m] = cm * sGm[m * kCL + t];
+      sRow[t * kTT + m] = -cm * sGm[m * kCL + t];
     }
     lds_barrier();
     // a (wave 0); the adjoint carry's first part on waves 1-7:
     // dP <- Gam_C dP + (dP K) diag(beta_{., cl-1}) U^T + dq~ q^T
     if (w == 0) {
-      solve_a(cl);
+      solve_rows(true, cl, tGp, sE, nullptr, sA, nullptr, nullptr);
     } else {
       const float gc = tMisc[0];
       for (int idx = w - 1; idx < 16; idx += 7) dd_update(sdP, idx, gc, sZ, sU, true, cl, sdQt, sQ);
+      mem_rows_dS0();
     }
     lds_barrier();
     // H = U^T A, J = A^T W, diag(K^T A), diag(U^T E)
@@ -606,7 +630,8 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
         float lsum = 0.f;
 #pragma unroll
         for (int m = 0; m < kTT; ++m) lsum = fmaf(sCm[t * kCL + m], tL[m], lsum);
-        tDal[t] = part + tGam[t] * (gp1 * tMisc[1] - lsum);
+        const float trd = (tMisc[8] + tMisc[9]) + (tMisc[10] + tMisc[11]);
+        tDal[t] = part + tGam[t] * (gp1 * trd - lsum);
       }
     } else if (w <= 4) {
       const int e = stage_lane(tid) - 64, t = e >> 4, j = e & 15;
@@ -618,78 +643,91 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     lds_barrier();
     // token by token: the gain adjoints, then the readout, the step, the gates, the
     // normalisation and the projections; dProj replaces Proj (zero rows in padding slots)
-    for (int t = w; t < kTT; t += 8) {
+    {
       const int lane = stage_lane(tid) & 63;
-      float* pt = &sProj[t * kPL];
-      if (t >= cl) {
-        pt[lane] = 0.f;
-        pt[kD + lane] = 0.f;
-        pt[2 * kD + lane] = 0.f;
-        if (lane < 16) pt[3 * kD + lane] = 0.f;
-        continue;
-      }
-      const float st = tSt[t];
-      const float at = sA[t * kLD + lane];
-      float gk = fmaf(tGam[t], at, tGp[t] * sF[t * kLD + lane]);
+      float dk[2], ddl[2], dstep[2], dalpha[2], dq[2], k[2], q[2], dl[2];
+      float eta[2], deta_dse[2], alpha[2], oma[2];
 #pragma unroll
-      for (int j = 0; j < kTT; ++j) gk = fmaf(sCf[j * kCL + t], sK[j * kLD + lane], gk);
-      float dk = -st * gk;
-      float ddl = -st * at;
-      const float dstep = -sJ[t * kCL + t];
-      float dalpha = tDal[t];
-      const float dq = sdQ[t * kLD + lane];
-      // forward values, as in the gates and executed_step
-      const float k = sK[t * kLD + lane], q = sQ[t * kLD + lane], dl = sDl[t * kLD + lane];
-      const float nk = tNk[t], nq = tNq[t], kk = tKk[t], dd = tDd[t], se = tSe[t], sa = tSa[t];
-      float eta, deta_dse;
-      if (gp.eta_map == 0) {
-        const float sg = fast_rcp(1.f + fast_exp(-se));
-        eta = gp.eta_scale * sg;
-        deta_dse = gp.eta_scale * sg * (1.f - sg);
-      } else {
-        eta = gp.eta_scale * (fmaxf(se, 0.f) + log1pf(fast_exp(-fabsf(se))));
-        deta_dse = gp.eta_scale * fast_rcp(1.f + fast_exp(-se));
+      for (int u = 0; u < 2; ++u) {
+        const int t = w + 8 * u;
+        const float st = tSt[t];
+        const float at = sA[t * kLD + lane];
+        float gk = fmaf(tGam[t], at, tGp[t] * sF[t * kLD + lane]);
+#pragma unroll
+        for (int j = 0; j < kTT; ++j) gk = fmaf(sCf[j * kCL + t], sK[j * kLD + lane], gk);
+        dk[u] = -st * gk;
+        ddl[u] = -st * at;
+        dstep[u] = -sJ[t * kCL + t];
+        dalpha[u] = tDal[t];
+        dq[u] = sdQ[t * kLD + lane];
+        k[u] = sK[t * kLD + lane];
+        q[u] = sQ[t * kLD + lane];
+        dl[u] = sDl[t * kLD + lane];
       }
-      const float ez = fast_exp(-(sa + gp.alpha_bias));
-      const float alpha = fast_rcp(1.f + ez);
-      const float oma = ez * alpha;  // 1 - alpha
-      const float rr0 = fast_sqrt(dd + gp.eps * gp.eps);
-      const float rr = rr0 + gp.eps;
-      const float inj = kInjInward * oma * fast_rcp(rr);
-      const bool ok = eta != 0.f && inj != 0.f;
-      const float xr = ok ? eta * fast_rcp(inj) : 0.f;
-      const float ex = fast_exp(-xr);
-      const float bar = ok ? inj * one_minus_exp_neg(xr) : 0.f;
-      const float kap = fmaxf(kk, kKappaFloor);
-      const float spec_raw = kSpecInward * 2.f * alpha * fast_rcp(kap);
-      const float spec = spec_raw > 0.f ? __uint_as_float(__float_as_uint(spec_raw) - 1u) : spec_raw;
-      // step = min(eta_bar, eta_spec)
-      float deta = 0.f, ddd = 0.f, dkk = 0.f;
-      if (bar <= spec) {
-        if (ok) {
-          deta = dstep * ex;
-          const float dinj = dstep * ((1.f - ex) - xr * ex);
-          dalpha -= dinj * kInjInward * fast_rcp(rr);
-          const float drr = -dinj * inj * fast_rcp(rr);
-          ddd = drr * 0.5f * fast_rcp(rr0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // forward values, as in the gates and executed_step
+        const int t = w + 8 * u;
+        const float kk = tKk[t], dd = tDd[t], se = tSe[t], sa = tSa[t];
+        if (gp.eta_map == 0) {
+          const float sg = fast_rcp(1.f + fast_exp(-se));
+          eta[u] = gp.eta_scale * sg;
+          deta_dse[u] = gp.eta_scale * sg * (1.f - sg);
+        } else {
+          eta[u] = gp.eta_scale * (fmaxf(se, 0.f) + log1pf(fast_exp(-fabsf(se))));
+          deta_dse[u] = gp.eta_scale * fast_rcp(1.f + fast_exp(-se));
         }
-      } else {
-        dalpha += dstep * kSpecInward * 2.f * fast_rcp(kap);
-        if (kk > kKappaFloor) dkk = -dstep * spec_raw * fast_rcp(kap);
+        const float ez = fast_exp(-(sa + gp.alpha_bias));
+        alpha[u] = fast_rcp(1.f + ez);
+        oma[u] = ez * alpha[u];  // 1 - alpha
+        const float rr0 = fast_sqrt(dd + gp.eps * gp.eps);
+        const float rr = rr0 + gp.eps;
+        const float inj = kInjInward * oma[u] * fast_rcp(rr);
+        const bool ok = eta[u] != 0.f && inj != 0.f;
+        const float xr = ok ? eta[u] * fast_rcp(inj) : 0.f;
+        const float ex = fast_exp(-xr);
+        const float bar = ok ? inj * one_minus_exp_neg(xr) : 0.f;
+        const float kap = fmaxf(kk, kKappaFloor);
+        const float spec_raw = kSpecInward * 2.f * alpha[u] * fast_rcp(kap);
+        const float spec = spec_raw > 0.f ? __uint_as_float(__float_as_uint(spec_raw) - 1u) : spec_raw;
+        // step = min(eta_bar, eta_spec)
+        float deta = 0.f, ddd = 0.f, dkk = 0.f;
+        if (bar <= spec) {
+          if (ok) {
+            deta = dstep[u] * ex;
+            const float dinj = dstep[u] * ((1.f - ex) - xr * ex);
+            dalpha[u] -= dinj * kInjInward * fast_rcp(rr);
+            const float drr = -dinj * inj * fast_rcp(rr);
+            ddd = drr * 0.5f * fast_rcp(rr0);
+          }
+        } else {
+          dalpha[u] += dstep[u] * kSpecInward * 2.f * fast_rcp(kap);
+          if (kk > kKappaFloor) dkk = -dstep[u] * spec_raw * fast_rcp(kap);
+        }
+        ddl[u] = fmaf(2.f * dl[u], ddd, ddl[u]);
+        dk[u] = fmaf(2.f * k[u], dkk, dk[u]);
+        dk[u] += ddl[u];  // delta = k - v
+        deta_dse[u] *= deta;
       }
-      ddl = fmaf(2.f * dl, ddd, ddl);
-      dk = fmaf(2.f * k, dkk, dk);
-      dk += ddl;  // delta = k - v
-      const float dv = -ddl;
-      const float kdk = wave_total(k * dk), qdq = wave_total(q * dq);
-      const float dkr = (dk - k * kdk) / nk;
-      const float dqr = (dq - q * qdq) / nq;
-      pt[lane] = dkr;
-      pt[kD + lane] = dv;
-      pt[2 * kD + lane] = dqr;
-      if (lane == 0) {
-        pt[3 * kD] = deta * deta_dse;
-        pt[3 * kD + 1] = dalpha * alpha * oma;
+      float kdk[2], qdq[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        kdk[u] = wave_total(k[u] * dk[u]);
+        qdq[u] = wave_total(q[u] * dq[u]);
+      }
+      // dProj rows; zero in padding slots
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = w + 8 * u;
+        const bool on = t < cl;
+        float* pt = &sProj[t * kPL];
+        pt[lane] = on ? (dk[u] - k[u] * kdk[u]) * tNk[t] : 0.f;
+        pt[kD + lane] = on ? -ddl[u] : 0.f;
+        pt[2 * kD + lane] = on ? (dq[u] - q[u] * qdq[u]) * tNq[t] : 0.f;
+        if (lane < 16) {
+          const float g = lane == 0 ? deta_dse[u] : (lane == 1 ? dalpha[u] * alpha[u] * oma[u] : 0.f);
+          pt[3 * kD + lane] = on ? g : 0.f;
+        }
       }
     }
     lds_barrier();
@@ -698,20 +736,23 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       const Lane L = stage_lane_of(tid);
       const int r16 = L.r16, q4 = L.q4;
       if (w < 4) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int T = 4; T < 17; ++T) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc = mfma4(s0f[4 * T + s], sProj[r16 * kPL + 16 * T - 64 + 4 * s + q4], acc);
+          for (int s = 0; s < 4; ++s) {
+            const float bv = sProj[r16 * kPL + 16 * T - 64 + 4 * s + q4];
+            if (s & 1) acc1 = mfma4(s0f[4 * T + s], bv, acc1);
+            else acc0 = mfma4(s0f[4 * T + s], bv, acc0);
+          }
           __builtin_amdgcn_sched_barrier(0);  // bounded operand prefetch
         }
-        store_tokens(sdXt, w, acc, L);
+        store_tokens(sdXt, w, acc0 + acc1, L);
       }
 #pragma unroll
       for (int i = 0; i < 9; ++i) {
         const int o = w + 8 * i;
-        if (o < 68) {
+        if (o < 68 && (i >= 2 || w == 0)) {
           const int RT = o >> 2, n = o & 3;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
