@@ -83,18 +83,33 @@ __device__ __forceinline__ Lane stage_lane_of(int tid) {
 }
 
 // Rows 16m..16m+15 of M (or of M^T) times the 16 token vectors of In (token-major):
-// Out[t][16m + i] = sum_k M(16m + i, k) In[t][k].  MFMA operands: lane (r16, q4) feeds
-// A[r16][k = 4s + q4] and B[k = 4s + q4][t = r16]; result D[4 q4 + v][r16].
+// Out[t][16m + i] = sum_k M(16m + i, k) In[t][k].  MFMA operands: in step s, lane (r16, q4)
+// feeds A[r16][k] and B[k][t = r16] with k = 16 q4 + s, so that a lane's operands are 16
+// consecutive floats (four 16-byte LDS reads; the transposed A is read column-wise), all
+// loaded before the products; result D[4 q4 + v][r16].
 __device__ __forceinline__ f32x4 dmat_tokens(const float* M, bool trans, const float* In, int m,
                                              const Lane& L) {
-  const int base = trans ? 16 * m + L.r16 : (16 * m + L.r16) * kLD;
-  const int ks = trans ? kLD : 1;
+  float a[16], bv[16];
+  if (trans) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = M[(16 * L.q4 + s) * kLD + 16 * m + L.r16];
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&M[(16 * m + L.r16) * kLD + 16 * L.q4 + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * g + e] = v[e];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&In[L.r16 * kLD + 16 * L.q4 + 4 * g]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[4 * g + e] = v[e];
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kD / 4; ++s) {
-    const int k = 4 * s + L.q4;
-    acc = mfma4(M[base + k * ks], In[L.r16 * kLD + k], acc);
-  }
+  for (int s = 0; s < 16; ++s) acc = mfma4(a[s], bv[s], acc);
   return acc;
 }
 
@@ -102,14 +117,22 @@ __device__ __forceinline__ void store_tokens(float* Out, int m, f32x4 acc, const
   *reinterpret_cast<f32x4*>(&Out[L.r16 * kLD + 16 * m + 4 * L.q4]) = acc;
 }
 
-// C x C Gram matrix Out[j][t] = A_j . B_t of two token-major arrays.
+// C x C Gram matrix Out[j][t] = A_j . B_t of two token-major arrays (same operand mapping).
 __device__ __forceinline__ f32x4 gram_tokens(const float* A, const float* B, const Lane& L) {
+  float a[16], bv[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 va = *reinterpret_cast<const f32x4*>(&A[L.r16 * kLD + 16 * L.q4 + 4 * g]);
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(&B[L.r16 * kLD + 16 * L.q4 + 4 * g]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[4 * g + e] = va[e];
+      bv[4 * g + e] = vb[e];
+    }
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kD / 4; ++s) {
-    const int k = 4 * s + L.q4;
-    acc = mfma4(A[L.r16 * kLD + k], B[L.r16 * kLD + k], acc);
-  }
+  for (int s = 0; s < 16; ++s) acc = mfma4(a[s], bv[s], acc);
   return acc;
 }
 
@@ -142,8 +165,8 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   constexpr int oRow = oCC + 6 * kTT * kCL;   // solve coefficient rows, 16 x 16
   constexpr int oTok = oRow + kTT * kTT;      // token-major d-vectors, 18 of them
   constexpr int oProj = oTok + 18 * kTok;     // projections [16][kPL], then their adjoints
-  constexpr int oP = oProj + kTT * kPL;       // P_c, dP
-  constexpr int kSmem = oP + 2 * kD * kLD;
+  constexpr int oP = oProj + kTT * kPL;       // P_c, dP, P_c^T
+  constexpr int kSmem = oP + 3 * kD * kLD;
   __shared__ __align__(16) float smem[kSmem];
   // per-token scalars; the first eight in record order
   float* const tSt = smem + oSc;  // step_t
@@ -192,6 +215,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   float* const sProj = smem + oProj;
   float* const sP = smem + oP;         // P_c
   float* const sdP = sP + kD * kLD;    // adjoint of P_{c+1}, then of P_c
+  float* const sPT = sdP + kD * kLD;   // P_c^T (reverse sweep)
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -210,16 +234,17 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, 0, 0};
   const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h : (int64_t)r * nh + h) * SS;
 
-  // S_0 in registers.  Waves 0-3 (column tile w): s0f[4T + s] = S_0[16T + 4s + q4][16w + r16]
+  // S_0 in registers.  Waves 0-3 (column tile w): s0f[4T + s] = S_0[16T + 4q4 + s][16w + r16]
   // for the 17 row tiles T.  Waves 4-7: row tiles 4 + j + 4 slot (slot 0-2) and, on wave 4,
-  // tile 16: s0f[16 slot + s] = S_0[16T + r16][4s + q4].
+  // tile 16: s0f[16 slot + s] = S_0[16T + r16][16q4 + s].  (k = 16 q4 + s, or 4 q4 + s within
+  // a row tile, as in the products below.)
   float s0f[68];
   {
     const Lane L = stage_lane_of(tid);
     if (w < 4) {
 #pragma unroll
       for (int e = 0; e < 68; ++e) {
-        const int row = 16 * (e >> 2) + 4 * (e & 3) + L.q4;
+        const int row = 16 * (e >> 2) + 4 * L.q4 + (e & 3);
         s0f[e] = row < kR ? init[(int64_t)row * kD + 16 * w + L.r16] : 0.f;
       }
     } else {
@@ -228,7 +253,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
         const int sl = e >> 4, s = e & 15;
         const int T = sl < 3 ? 4 + (w - 4) + 4 * sl : 16;
         const int row = 16 * T + L.r16;
-        s0f[e] = ((sl < 3 || w == 4) && row < kR) ? init[(int64_t)row * kD + 4 * s + L.q4] : 0.f;
+        s0f[e] = ((sl < 3 || w == 4) && row < kR) ? init[(int64_t)row * kD + 16 * L.q4 + s] : 0.f;
       }
 #pragma unroll
       for (int e = 64; e < 68; ++e) s0f[e] = 0.f;
@@ -284,6 +309,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       for (int k = 0; k < 8; ++k) {
         const int e = t0 + 512 * k;
         sP[(e >> 6) * kLD + (e & 63)] = fP[k];
+        sPT[(e & 63) * kLD + (e >> 6)] = fP[k];
       }
 #pragma unroll
       for (int k = 0; k < 12; ++k) {
@@ -321,9 +347,16 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     for (int sl = 0; sl < 4; ++sl) {
       const int T = sl < 3 ? 4 + (w - 4) + 4 * sl : 16;
       if (sl < 3 || w == 4) {
+        float bv[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&sXt[L.r16 * kLD + 16 * L.q4 + 4 * g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bv[4 * g + e] = v[e];
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 16; ++s) acc = mfma4(s0f[16 * sl + s], sXt[L.r16 * kLD + 4 * s + L.q4], acc);
+        for (int s = 0; s < 16; ++s) acc = mfma4(s0f[16 * sl + s], bv[s], acc);
         *reinterpret_cast<f32x4*>(&sProj[L.r16 * kPL + 16 * T - 64 + 4 * L.q4]) = acc;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -552,11 +585,14 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     // K^T K (wave 4); beta (waves 4-7)
     if (w < 4) {
       const Lane L = stage_lane_of(tid);
+      f32x4 dy4[4];
+#pragma unroll
+      for (int T = 0; T < 4; ++T) dy4[T] = *reinterpret_cast<const f32x4*>(&sDY[L.r16 * kLD + 16 * T + 4 * L.q4]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int T = 0; T < 4; ++T)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma4(s0f[4 * T + s], sDY[L.r16 * kLD + 16 * T + 4 * s + L.q4], acc);
+        for (int s = 0; s < 4; ++s) acc = mfma4(s0f[4 * T + s], dy4[T][s], acc);
       store_tokens(sdQt, w, acc, L);
       float tr = 0.f;
 #pragma unroll 4
@@ -576,10 +612,10 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     // E = P^T Z = D_e K, F = dP^T Y = D_e^T W, q~ = P q, dq = P^T dq~; c and the a-solve rows
     for (int jb = w; jb < 16; jb += 8) {
       const int kind = jb >> 2, m = jb & 3;
-      if (kind == 0) dtok(sE, sP, true, sZ, m);
+      if (kind == 0) dtok(sE, sPT, false, sZ, m);
       else if (kind == 1) dtok(sF, sdP, true, sY, m);
       else if (kind == 2) dtok(sQt, sP, false, sQ, m);
-      else dtok(sdQ, sP, true, sdQt, m);
+      else dtok(sdQ, sPT, false, sdQt, m);
     }
     if (w >= 4) {
       const int e = stage_lane(tid) - 256, t = e >> 4, m = e & 15;
@@ -738,13 +774,18 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       if (w < 4) {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int T = 4; T < 17; ++T) {
+        for (int T0 = 4; T0 < 17; T0 += 5) {
+          f32x4 pv[5];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float bv = sProj[r16 * kPL + 16 * T - 64 + 4 * s + q4];
-            if (s & 1) acc1 = mfma4(s0f[4 * T + s], bv, acc1);
-            else acc0 = mfma4(s0f[4 * T + s], bv, acc0);
-          }
+          for (int T = T0; T < T0 + 5 && T < 17; ++T)
+            pv[T - T0] = *reinterpret_cast<const f32x4*>(&sProj[r16 * kPL + 16 * T - 64 + 4 * q4]);
+#pragma unroll
+          for (int T = T0; T < T0 + 5 && T < 17; ++T)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              if (s & 1) acc1 = mfma4(s0f[4 * T + s], pv[T - T0][s], acc1);
+              else acc0 = mfma4(s0f[4 * T + s], pv[T - T0][s], acc0);
+            }
           __builtin_amdgcn_sched_barrier(0);  // bounded operand prefetch
         }
         store_tokens(sdXt, w, acc0 + acc1, L);
@@ -770,7 +811,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     // dP <- dP + dx~ x^T
     if (w < 4) {
       const Lane L = stage_lane_of(tid);
-      dxv = dmat_tokens(sP, true, sdXt, w, L);
+      dxv = dmat_tokens(sPT, false, sdXt, w, L);
       dxok = L.r16 < cl;
       dxdst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
     }
