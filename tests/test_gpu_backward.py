@@ -37,6 +37,7 @@ CASES = [
     (1, 4, 4, 64, 1, "f32", 15, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),  # clamps bind
     (2, 3, 4, 128, 2, "f32", 5, 0, dict(init_per_image=True)),            # two heads, per image
     (1, 5, 7, 128, 2, "bf16", 10, 0, {}),                                 # routes 1 and 3, bf16
+    (1, 3, 20, 64, 1, "f32", 15, 0, {}),                                  # d = 64, 20-token rows
 ]
 
 
