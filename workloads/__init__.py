@@ -133,3 +133,53 @@ def split_state(flat: np.ndarray, d: int) -> dict:
     out["eta"] = flat[..., 4 * dd:4 * dd + d].reshape(flat.shape[:-1] + (1, d))
     out["alpha"] = flat[..., 4 * dd + d:4 * dd + 2 * d].reshape(flat.shape[:-1] + (1, d))
     return out
+
+
+BLOCK_LINEAR = ("w_in", "w_q", "w_out", "w1", "w2")
+
+
+def draw_block_weights(D: int, n_heads: int, ffn_dim: int, seed: int) -> dict:
+    """Synthetic weights of one VisionHOPE block (the pages' trained weights are absent).
+
+    Linear weights [out, in] ~ N(0, 1/in), rounded to bf16 (values as fp32 under their
+    names, bit patterns under name + "_bits"); depthwise 3x3 weights [3, 3, C] ~ N(0, 1/9)
+    scaled by 0.5; biases ~ N(0, 0.02^2); LayerNorm gains 1 + N(0, 0.1^2) and shifts
+    N(0, 0.1^2); direction scales 1 + N(0, 0.1^2) [4, D]; skip N(0, 0.1^2) [D]; initial
+    memories [4, n_heads, 4d^2 + 2d] ~ N(0, 1/d), M_mem kept.  Draw order: the names in the
+    order listed by the returned dict's construction below, one PCG64 stream."""
+    d = D // n_heads
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out: dict = {}
+
+    def lin(name, n_out, n_in):
+        v, bits = round_to_bf16((rng.standard_normal((n_out, n_in)) / np.sqrt(n_in)).astype(np.float32))
+        out[name], out[name + "_bits"] = v, bits
+
+    def dw(name, C):
+        out[name + "_w"] = (rng.standard_normal((3, 3, C)) * (0.5 / 3.0)).astype(np.float32)
+        out[name + "_b"] = (rng.standard_normal(C) * 0.02).astype(np.float32)
+
+    def vec(name, n, mean, sd):
+        out[name] = (mean + rng.standard_normal(n) * sd).astype(np.float32)
+
+    dw("cpe", D)
+    vec("ln1_g", D, 1.0, 0.1)
+    vec("ln1_b", D, 0.0, 0.1)
+    lin("w_in", D, D)
+    vec("b_in", D, 0.0, 0.02)
+    dw("dw", D)
+    lin("w_q", D, D)
+    out["scales"] = (1.0 + rng.standard_normal((4, D)) * 0.1).astype(np.float32)
+    vec("skip", D, 0.0, 0.1)
+    S = 4 * d * d + 2 * d
+    out["init"] = (rng.standard_normal((4, n_heads, S)) / np.sqrt(d)).astype(np.float32)
+    dw("lpe", D)
+    lin("w_out", D, D)
+    vec("b_out", D, 0.0, 0.02)
+    vec("ln2_g", D, 1.0, 0.1)
+    vec("ln2_b", D, 0.0, 0.1)
+    lin("w1", ffn_dim, D)
+    vec("b1", ffn_dim, 0.0, 0.02)
+    lin("w2", D, ffn_dim)
+    vec("b2", D, 0.0, 0.02)
+    return out
