@@ -1,4 +1,4 @@
-"""ctypes view of libhopescan.so (the C ABI of include/hope_scan2d.h).
+"""ctypes view of libhopescan.so (the C ABI of include/hope_scan2d.h and include/hope_block.h).
 
 Loading fails loudly when the library has not been built: there is no other
 implementation of the scan in this package.
@@ -12,6 +12,7 @@ import re
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libhopescan.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "hope_scan2d.h")
+BLOCK_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "hope_block.h")
 
 HOPE_OK = 0
 HOPE_ERR_INVALID_ARG = -1
@@ -53,6 +54,15 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("mem_chunk", ctypes.c_int32)]
 
 
+BLOCK_WEIGHT_FIELDS = ("cpe_w", "cpe_b", "ln1_g", "ln1_b", "w_in", "b_in", "dw_w", "dw_b", "w_q",
+                      "init_memories", "route_scales", "skip", "lpe_w", "lpe_b", "w_out", "b_out",
+                      "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")
+
+
+class hope_block_weights_t(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in BLOCK_WEIGHT_FIELDS]
+
+
 _lib = None
 
 
@@ -91,13 +101,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
     lib.hope_debug_cross_merge.restype = ctypes.c_int
+    lib.hope_block_workspace_size.argtypes = [ctypes.c_int32] * 7
+    lib.hope_block_workspace_size.restype = ctypes.c_size_t
+    lib.hope_block_forward.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 7 + [
+        P(hope_block_weights_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hope_block_forward.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
-def header_functions(path: str = HEADER_PATH) -> list[str]:
+def header_functions(path: str | None = None) -> list[str]:
     """Names of the functions declared in the public header."""
-    text = open(path).read()
+    paths = [path] if path else [HEADER_PATH, BLOCK_HEADER_PATH]
+    text = "".join(open(p).read() for p in paths)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b(hope_[a-z0-9_]+)\s*\(", text)
     return sorted(set(names))

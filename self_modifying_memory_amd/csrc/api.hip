@@ -101,6 +101,14 @@ hope_status_t hip_status(hipError_t e) {
   return HOPE_ERR_HIP;
 }
 
+}  // namespace
+
+// The status of a HIP result for the entry points of other translation units (records the
+// error for hope_last_hip_error, as the entry points here do).
+hope_status_t hope_status_of(hipError_t e) { return hip_status(e); }
+
+namespace {
+
 // Backward workspace: map-gradient planes of the selected routes beyond the first, then
 // chain_floats per chain (n_sel * B * n_heads chains, in launch order).
 struct BackLayout {

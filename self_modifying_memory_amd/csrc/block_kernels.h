@@ -1,0 +1,32 @@
+// Internal launch interface of the block kernels (block_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hope {
+
+enum { kEpiF32 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
+
+// out[m][n] = epi(sum_k A[m][k] Wt[n][k] + bias[n]): kEpiF32 -> fp32 out; kEpiGeluBf16 ->
+// bf16 GELU(.) (erf form); kEpiResidualF32 -> fp32 res[m][n] + (.) (res may equal out).
+// bias may be null.  N % 128 == 0, K % 32 == 0; A, Wt 16-byte aligned.
+hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
+                            const float* bias, const float* res, void* out, hipStream_t s);
+
+// x1 = x + DW(x) (the conditional positional encoding), fp32
+hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
+                             int H, int W, int C, hipStream_t s);
+// z = bf16(u + SiLU(DW(u))) (the gated depthwise branch)
+hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
+                               int H, int W, int C, hipStream_t s);
+// out = bf16(y + DW(z)) (the local positional branch added to the operator output)
+hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* w, const float* b,
+                             uint16_t* out, int B, int H, int W, int C, hipStream_t s);
+// y = bf16(LayerNorm(x) g + b); if x_plus: x_plus = x + addv.  C % 64 == 0, C / 64 in
+// {1, 2, 3, 4, 6, 8, 12, 16}.
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, uint16_t* y,
+                            const float* addv, float* x_plus, int64_t M, int C, float eps,
+                            hipStream_t s);
+
+}  // namespace hope

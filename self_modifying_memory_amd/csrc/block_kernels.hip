@@ -1,0 +1,283 @@
+// Kernels of the VisionHOPE block around the scan, gfx950 ("VisionHOPE: Visual Backbones as
+// Self-Modifying Learning Systems", Sec. 2.3 Eq. 27 and App. B.5): the pointwise
+// projections as bf16 matrix-core GEMMs with fused epilogues (bias, GELU, residual), the
+// 3x3 depthwise convolutions with their residual / gate fused, and LayerNorm.
+// Feature maps are channels-last [M = B*H*W][C]; linear weights are [out][in] bf16.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "block_kernels.h"
+
+namespace hope {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {  // round to nearest even (finite f)
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
+// Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
+// K in steps of 32 through double-buffered LDS (rows padded to 40 bf16), one barrier a step.
+// Operands: lane (r16, q4) feeds row r16 of the A tile and column r16 of the B tile with the
+// 8 consecutive k values 8 q4 .. 8 q4 + 7 of the step (the same k order on both sides).
+// Requires N % 128 == 0 and K % 32 == 0; rows past M are read clamped and not written.
+constexpr int kBM = 128, kBN = 128, kBK = 32, kLDK = kBK + 8;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ Wt, int M,
+                                                         int N, int K, const float* bias,
+                                                         const float* res, void* out) {
+  __shared__ __align__(16) uint16_t sA[2][kBM * kLDK];
+  __shared__ __align__(16) uint16_t sB[2][kBN * kLDK];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4, wm = w >> 1, wn = w & 1;
+  const int tiles_n = N / kBN;
+  const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
+
+  // global -> registers -> LDS: 2 chunks of 8 bf16 per thread for each operand
+  const int row0 = tid >> 2, row1 = row0 + 64, ch = 8 * (tid & 3);
+  const uint16_t* pa0 = A + (int64_t)min(m0 + row0, M - 1) * K + ch;
+  const uint16_t* pa1 = A + (int64_t)min(m0 + row1, M - 1) * K + ch;
+  const uint16_t* pb0 = Wt + (int64_t)(n0 + row0) * K + ch;
+  const uint16_t* pb1 = Wt + (int64_t)(n0 + row1) * K + ch;
+  uint4 ga0 = *reinterpret_cast<const uint4*>(pa0), ga1 = *reinterpret_cast<const uint4*>(pa1);
+  uint4 gb0 = *reinterpret_cast<const uint4*>(pb0), gb1 = *reinterpret_cast<const uint4*>(pb1);
+  *reinterpret_cast<uint4*>(&sA[0][row0 * kLDK + ch]) = ga0;
+  *reinterpret_cast<uint4*>(&sA[0][row1 * kLDK + ch]) = ga1;
+  *reinterpret_cast<uint4*>(&sB[0][row0 * kLDK + ch]) = gb0;
+  *reinterpret_cast<uint4*>(&sB[0][row1 * kLDK + ch]) = gb1;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < K; k0 += kBK) {
+    const bool more = k0 + kBK < K;
+    if (more) {
+      ga0 = *reinterpret_cast<const uint4*>(pa0 + k0 + kBK);
+      ga1 = *reinterpret_cast<const uint4*>(pa1 + k0 + kBK);
+      gb0 = *reinterpret_cast<const uint4*>(pb0 + k0 + kBK);
+      gb1 = *reinterpret_cast<const uint4*>(pb1 + k0 + kBK);
+    }
+    bf16x8 a[4], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 64 + 16 * i + r16) * kLDK + 8 * q4]);
+      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[cur][(wn * 64 + 16 * i + r16) * kLDK + 8 * q4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
+    if (more) {
+      const int nb = cur ^ 1;
+      *reinterpret_cast<uint4*>(&sA[nb][row0 * kLDK + ch]) = ga0;
+      *reinterpret_cast<uint4*>(&sA[nb][row1 * kLDK + ch]) = ga1;
+      *reinterpret_cast<uint4*>(&sB[nb][row0 * kLDK + ch]) = gb0;
+      *reinterpret_cast<uint4*>(&sB[nb][row1 * kLDK + ch]) = gb1;
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + 4 q4 + v][n0 + 64 wn + 16 j + r16]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 64 + 16 * j + r16;
+    const float bn = bias ? bias[n] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * 64 + 16 * i + 4 * q4 + v;
+        if (m >= M) continue;
+        const int64_t o = (int64_t)m * N + n;
+        const float t = acc[i][j][v] + bn;
+        if (EPI == kEpiF32) {
+          static_cast<float*>(out)[o] = t;
+        } else if (EPI == kEpiGeluBf16) {
+          static_cast<uint16_t*>(out)[o] = to_bf16(0.5f * t * (1.f + erff(t * 0.70710678118654752f)));
+        } else {
+          static_cast<float*>(out)[o] = res[o] + t;
+        }
+      }
+    }
+  }
+}
+
+// ---- depthwise 3x3 convolution with a fused residual --------------------------------------
+// out[p][c] = res[p][c] + act(bias[c] + sum over the 3x3 neighbourhood (zero padding) of
+// w[dy][dx][c] src[p + (dy - 1, dx - 1)][c]); four channels per thread.
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
+  uint2 u;
+  u.x = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
+  u.y = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+template <typename SrcT, typename ResT, typename OutT, bool SILU>
+__global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__ src,
+                                                         const ResT* __restrict__ res,
+                                                         const float* __restrict__ wgt,
+                                                         const float* __restrict__ bias, OutT* out,
+                                                         int B, int H, int W, int C) {
+  const int cq = C / 4;
+  const int64_t total = (int64_t)B * H * W * cq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % cq) * 4;
+    const int64_t p = i / cq;
+    const int x = (int)(p % W), y = (int)((p / W) % H);
+    const int64_t img = p / ((int64_t)H * W);
+    f32x4 acc = *reinterpret_cast<const f32x4*>(&bias[c]);
+#pragma unroll
+    for (int dy = 0; dy < 3; ++dy) {
+      const int yy = y + dy - 1;
+      if (yy < 0 || yy >= H) continue;
+#pragma unroll
+      for (int dx = 0; dx < 3; ++dx) {
+        const int xx = x + dx - 1;
+        if (xx < 0 || xx >= W) continue;
+        const f32x4 v = load4(&src[((img * H + yy) * W + xx) * C + c]);
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + dx) * C + c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e], v[e], acc[e]);
+      }
+    }
+    if (SILU) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = acc[e] / (1.f + expf(-acc[e]));
+    }
+    const f32x4 r = load4(&res[p * C + c]);
+    store4(&out[p * C + c], r + acc);
+  }
+}
+
+// ---- LayerNorm over the channels of each pixel (one wave per pixel) ------------------------
+// y = bf16((x - mean) / sqrt(var + eps) * g + b) with the biased variance; optionally
+// x_plus = x + addv (fp32).  VPL = C / 64 values per lane.
+template <int VPL>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ g,
+                                                         const float* __restrict__ b,
+                                                         uint16_t* __restrict__ y,
+                                                         const float* __restrict__ addv,
+                                                         float* __restrict__ x_plus, int64_t M,
+                                                         float eps) {
+  constexpr int C = 64 * VPL;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t p = wave; p < M; p += nwaves) {
+    float v[VPL];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      v[k] = x[p * C + lane + 64 * k];
+      s += v[k];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    const float mean = s * (1.f / C);
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const float dv = v[k] - mean;
+      q = fmaf(dv, dv, q);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off, 64);
+    const float rstd = 1.f / sqrtf(q * (1.f / C) + eps);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int c = lane + 64 * k;
+      y[p * C + c] = to_bf16((v[k] - mean) * rstd * g[c] + b[c]);
+      if (x_plus) x_plus[p * C + c] = v[k] + addv[c];
+    }
+  }
+}
+
+unsigned grid_for(int64_t work, int per_block) {
+  const int64_t g = (work + per_block - 1) / per_block;
+  return (unsigned)(g < 65535 * 16 ? (g < 1 ? 1 : g) : 65535 * 16);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
+                            const float* bias, const float* res, void* out, hipStream_t s) {
+  if (N % kBN || K % kBK || M <= 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(((M + kBM - 1) / kBM) * (N / kBN))), block(256);
+  switch (epi) {
+    case kEpiF32: gemm_bf16_kernel<kEpiF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    case kEpiGeluBf16: gemm_bf16_kernel<kEpiGeluBf16><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    case kEpiResidualF32: gemm_bf16_kernel<kEpiResidualF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
+                             int H, int W, int C, hipStream_t s) {
+  const int64_t work = (int64_t)B * H * W * (C / 4);
+  dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, out, B, H, W, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
+                               int H, int W, int C, hipStream_t s) {
+  const int64_t work = (int64_t)B * H * W * (C / 4);
+  dwconv3x3_kernel<float, float, uint16_t, true><<<grid_for(work, 256), 256, 0, s>>>(u, u, w, b, z, B, H, W, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* w, const float* b,
+                             uint16_t* out, int B, int H, int W, int C, hipStream_t s) {
+  const int64_t work = (int64_t)B * H * W * (C / 4);
+  dwconv3x3_kernel<uint16_t, float, uint16_t, false><<<grid_for(work, 256), 256, 0, s>>>(z, y, w, b, out, B, H, W, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, uint16_t* y,
+                            const float* addv, float* x_plus, int64_t M, int C, float eps,
+                            hipStream_t s) {
+  const unsigned grid = grid_for(M * 64, 256);
+  switch (C / 64) {
+#define HOPE_LN(V) \
+  case V: layernorm_kernel<V><<<grid, 256, 0, s>>>(x, g, b, y, addv, x_plus, M, eps); break;
+    HOPE_LN(1) HOPE_LN(2) HOPE_LN(3) HOPE_LN(4) HOPE_LN(6) HOPE_LN(8) HOPE_LN(12) HOPE_LN(16)
+#undef HOPE_LN
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hope

@@ -39,7 +39,8 @@ def call(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, out=FAKE + (2 << 30), 
 
 def test_every_declared_function_is_exported(lib):
     names = N.header_functions()
-    assert "hope_scan2d_forward" in names and "hope_scan2d_backward" in names and len(names) == 9
+    assert "hope_scan2d_forward" in names and "hope_scan2d_backward" in names
+    assert "hope_block_forward" in names and "hope_block_workspace_size" in names and len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
 
@@ -252,3 +253,55 @@ def test_backward_argument_errors(lib):
     wsd = lib.hope_scan2d_backward_workspace_size(ctypes.byref(d64), 1, 0, None)
     assert bcall(lib, d64, dirs=1, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=wsd)) == \
         N.HOPE_ERR_UNSUPPORTED                                            # d = 64: rows of 40 > 32
+
+
+def test_block_weights_layout_matches_c():
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "hope_block.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(hope_block_weights_t), offsetof(hope_block_weights_t, w_q),
+         offsetof(hope_block_weights_t, init_memories), offsetof(hope_block_weights_t, b2));
+  return 0;
+}
+"""
+    import subprocess, tempfile, os
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+        r = subprocess.run([gcc, c, "-o", exe, "-I", inc,
+                            "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"], capture_output=True, text=True)
+        if r.returncode:
+            pytest.skip("cannot compile the layout probe: " + r.stderr[:200])
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    S = N.hope_block_weights_t
+    assert got == [ctypes.sizeof(S), S.w_q.offset, S.init_memories.offset, S.b2.offset]
+
+
+def test_block_workspace_size_and_errors(lib):
+    assert lib.hope_block_workspace_size(2, 14, 14, 384, 6, 1536, 0) > 0
+    assert lib.hope_block_workspace_size(2, 14, 14, 100, 2, 400, 0) == 0   # D % 128
+    assert lib.hope_block_workspace_size(2, 14, 14, 128, 3, 512, 0) == 0   # D % n_heads
+    assert lib.hope_block_workspace_size(2, 14, 14, 128, 2, 500, 0) == 0   # ffn_dim % 128
+    assert lib.hope_block_workspace_size(0, 14, 14, 128, 2, 512, 0) == 0
+    w = N.hope_block_weights_t()
+    # null weights: rejected before anything is enqueued (no device needed)
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+                                  FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_INVALID_ARG
+    for name in N.BLOCK_WEIGHT_FIELDS:
+        setattr(w, name, FAKE + (3 << 30))
+    # a head dimension of 128 is well formed but not supported
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 1, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+                                  FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_UNSUPPORTED
+    # x and out alias
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE,
+                                  FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_INVALID_ARG
+    # short workspace
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+                                  FAKE + (2 << 30), 256, None) == N.HOPE_ERR_WORKSPACE
