@@ -224,6 +224,89 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
     return 0
 
 
+def run_block(args, w: wl.Workload, dev) -> int:
+    """One VisionHOPE block (hope_block_forward: positional encoding, LayerNorms, the five
+    projections, the depthwise branches, the operator and the FFN) on the workload's shape
+    with synthetic weights, as the timed step.  Roofline: the projections' flops at the
+    bf16 matrix peak plus the operator's (its bf16 part at the bf16 peak, its fp32 part at
+    the fp32 peak); the depthwise and LayerNorm passes are left out of the count."""
+    import torch
+    from self_modifying_memory_amd import _native as N
+    from self_modifying_memory_amd.block import hope_block_forward, hope_block_workspace_size
+    F = 4 * w.D
+    rng = np.random.Generator(np.random.PCG64(31))
+    x_np = rng.standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)
+    wts = wl.draw_block_weights(w.D, w.n_heads, F, seed=32)
+    names = {"init_memories": "init", "route_scales": "scales"}
+    wd = {}
+    for name in N.BLOCK_WEIGHT_FIELDS:
+        key = names.get(name, name)
+        if key + "_bits" in wts:
+            wd[name] = torch.from_numpy(wts[key + "_bits"].view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        else:
+            wd[name] = torch.from_numpy(np.ascontiguousarray(wts[key], dtype=np.float32)).to(dev)
+    x = torch.from_numpy(x_np).to(dev)
+    out = torch.empty_like(x)
+    ws = torch.empty(hope_block_workspace_size(w.B, w.H, w.W, w.D, w.n_heads, F, w.chunk),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hope_block_forward(x, wd, w.n_heads, F, w.chunk, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:  # clock settling, untimed
+        step()
+        torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    c_avg = float(np.mean(call_ms)) * 1e-3
+    M = w.B * w.H * w.W
+    f_gemm = 2.0 * M * (3 * w.D * w.D + 2 * w.D * F)
+    roof = roofline_numbers(w)
+    t_roof = (f_gemm + roof["flops_bf16"]) / PEAK_BF16 + roof["flops_fp32"] / PEAK_FP32
+    rec = {
+        "metric": "block pixels/s: one VisionHOPE block (Eq. 27, App. B.5) per pixel of the map",
+        "value": M * args.steps / wall, "unit": "pixels/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + "_block", "B": w.B, "H": w.H, "W": w.W, "D": w.D,
+                   "n_heads": w.n_heads, "ffn_dim": F, "chunk": w.chunk or w.W, "dirs": 4},
+        "roofline": {"bound": "mfma", "achieved": (f_gemm + roof["flops"]) / c_avg / 1e12,
+                     "peak": (f_gemm + roof["flops"]) / t_roof / 1e12, "unit": "TFLOP/s",
+                     "frac": t_roof / c_avg, "traffic": None,
+                     "kernel": "whole block call (blended peaks: projections and the operator's "
+                               "bf16 part at 2.5 PFLOP/s, its fp32 part at 157.3 TFLOP/s)",
+                     "kernel_ms": c_avg * 1e3, "t_roof_ms": t_roof * 1e3,
+                     "kernel_ms_p10_p90": [float(np.percentile(call_ms, 10)),
+                                           float(np.percentile(call_ms, 90))]},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import hope_block as hbk
+        ow = {k: v.astype(np.float64) for k, v in wts.items() if not k.endswith("_bits")}
+        t0 = time.perf_counter()
+        hbk.block_forward(x_np[:1], ow, w.n_heads, chunk=w.chunk)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": w.H * w.W / dt, "unit": "pixels/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"1 of {w.B} images ({w.H * w.W} pixels) in {dt:.1f} s, "
+                                         f"fp64 numpy"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +323,8 @@ def main() -> int:
                          "no_dgd, queries (synthetic scales / skip / queries)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients) instead of the forward scan")
+    ap.add_argument("--block", action="store_true",
+                    help="time one VisionHOPE block around the scan instead of the scan alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -264,6 +349,8 @@ def main() -> int:
         x_host = torch.from_numpy(inp["x"].copy())
     if args.backward:
         return run_backward(args, w, inp, x_host, dev)
+    if args.block:
+        return run_block(args, w, dev)
     init = torch.from_numpy(inp["init"].copy()).to(dev)
     sets = []
     for _ in range(max(1, args.sets)):
