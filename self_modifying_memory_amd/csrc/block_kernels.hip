@@ -19,13 +19,29 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {  // round to nearest even
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// erf by Abramowitz and Stegun 7.1.26 (|error| <= 1.5e-7): for x >= 0,
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-x^2}, t = 1 / (1 + p x); odd.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  float y = fmaf(1.061405429f, t, -1.453152027f);
+  y = fmaf(y, t, 1.421413741f);
+  y = fmaf(y, t, -0.284496736f);
+  y = fmaf(y, t, 0.254829592f);
+  y = 1.f - y * t * __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(y, x);
+}
+
 // ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
 // Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
-// K in steps of 32 through double-buffered LDS (rows padded to 40 bf16), one barrier a step.
-// Operands: lane (r16, q4) feeds row r16 of the A tile and column r16 of the B tile with the
-// 8 consecutive k values 8 q4 .. 8 q4 + 7 of the step (the same k order on both sides).
-// Requires N % 128 == 0 and K % 32 == 0; rows past M are read clamped and not written.
-constexpr int kBM = 128, kBN = 128, kBK = 32, kLDK = kBK + 8;
+// K in steps of 64 (two MFMA k-steps) through double-buffered LDS (rows padded to 72 bf16),
+// one barrier a step.  The MFMA computes the transposed tile (weights as its A operand), so
+// that a lane's four results are four consecutive output columns of one row: lane (r16, q4)
+// feeds row r16 of the weight tile and row r16 of the activation tile with the 8 consecutive
+// k values 8 q4 .. 8 q4 + 7 of each 32-deep half (the same k order on both sides), and holds
+// C[m = 16 i + r16][n = 16 j + 4 q4 + v].
+// Requires N % 128 == 0 and K % 64 == 0; rows past M are read clamped and not written.
+constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
@@ -39,18 +55,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   const int tiles_n = N / kBN;
   const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
 
-  // global -> registers -> LDS: 2 chunks of 8 bf16 per thread for each operand
-  const int row0 = tid >> 2, row1 = row0 + 64, ch = 8 * (tid & 3);
-  const uint16_t* pa0 = A + (int64_t)min(m0 + row0, M - 1) * K + ch;
-  const uint16_t* pa1 = A + (int64_t)min(m0 + row1, M - 1) * K + ch;
-  const uint16_t* pb0 = Wt + (int64_t)(n0 + row0) * K + ch;
-  const uint16_t* pb1 = Wt + (int64_t)(n0 + row1) * K + ch;
-  uint4 ga0 = *reinterpret_cast<const uint4*>(pa0), ga1 = *reinterpret_cast<const uint4*>(pa1);
-  uint4 gb0 = *reinterpret_cast<const uint4*>(pb0), gb1 = *reinterpret_cast<const uint4*>(pb1);
-  *reinterpret_cast<uint4*>(&sA[0][row0 * kLDK + ch]) = ga0;
-  *reinterpret_cast<uint4*>(&sA[0][row1 * kLDK + ch]) = ga1;
-  *reinterpret_cast<uint4*>(&sB[0][row0 * kLDK + ch]) = gb0;
-  *reinterpret_cast<uint4*>(&sB[0][row1 * kLDK + ch]) = gb1;
+  // global -> registers -> LDS: 4 chunks of 8 bf16 per thread for each operand
+  // (rows tid / 8 + 32 c, k chunk 8 (tid % 8))
+  const int row = tid >> 3, ch = 8 * (tid & 7);
+  const uint16_t* pa = A + (int64_t)min(m0 + row, M - 1) * K + ch;
+  const int64_t da1 = (int64_t)(min(m0 + row + 32, M - 1) - min(m0 + row, M - 1)) * K;
+  const int64_t da2 = (int64_t)(min(m0 + row + 64, M - 1) - min(m0 + row, M - 1)) * K;
+  const int64_t da3 = (int64_t)(min(m0 + row + 96, M - 1) - min(m0 + row, M - 1)) * K;
+  const uint16_t* pb = Wt + (int64_t)(n0 + row) * K + ch;
+  const int64_t db = (int64_t)32 * K;
+  uint4 ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
+#define HOPE_GEMM_FETCH(k)                                           \
+  ga0 = *reinterpret_cast<const uint4*>(pa + (k));                   \
+  ga1 = *reinterpret_cast<const uint4*>(pa + da1 + (k));             \
+  ga2 = *reinterpret_cast<const uint4*>(pa + da2 + (k));             \
+  ga3 = *reinterpret_cast<const uint4*>(pa + da3 + (k));             \
+  gb0 = *reinterpret_cast<const uint4*>(pb + (k));                   \
+  gb1 = *reinterpret_cast<const uint4*>(pb + db + (k));              \
+  gb2 = *reinterpret_cast<const uint4*>(pb + 2 * db + (k));          \
+  gb3 = *reinterpret_cast<const uint4*>(pb + 3 * db + (k));
+#define HOPE_GEMM_STORE(buf)                                                       \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga0;                \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 32) * kLDK + ch]) = ga1;               \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga2;               \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 96) * kLDK + ch]) = ga3;               \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb0;                \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 32) * kLDK + ch]) = gb1;               \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb2;               \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 96) * kLDK + ch]) = gb3;
+  HOPE_GEMM_FETCH(0)
+  HOPE_GEMM_STORE(0)
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -63,52 +97,54 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   for (int k0 = 0; k0 < K; k0 += kBK) {
     const bool more = k0 + kBK < K;
     if (more) {
-      ga0 = *reinterpret_cast<const uint4*>(pa0 + k0 + kBK);
-      ga1 = *reinterpret_cast<const uint4*>(pa1 + k0 + kBK);
-      gb0 = *reinterpret_cast<const uint4*>(pb0 + k0 + kBK);
-      gb1 = *reinterpret_cast<const uint4*>(pb1 + k0 + kBK);
-    }
-    bf16x8 a[4], bv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 64 + 16 * i + r16) * kLDK + 8 * q4]);
-      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[cur][(wn * 64 + 16 * i + r16) * kLDK + 8 * q4]);
+      HOPE_GEMM_FETCH(k0 + kBK)
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 a[4], bv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]);
+        bv[i] = *reinterpret_cast<const bf16x8*>(&sB[cur][(wn * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);
+    }
     if (more) {
-      const int nb = cur ^ 1;
-      *reinterpret_cast<uint4*>(&sA[nb][row0 * kLDK + ch]) = ga0;
-      *reinterpret_cast<uint4*>(&sA[nb][row1 * kLDK + ch]) = ga1;
-      *reinterpret_cast<uint4*>(&sB[nb][row0 * kLDK + ch]) = gb0;
-      *reinterpret_cast<uint4*>(&sB[nb][row1 * kLDK + ch]) = gb1;
+      HOPE_GEMM_STORE(cur ^ 1)
     }
     __syncthreads();
     cur ^= 1;
   }
 
-  // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + 4 q4 + v][n0 + 64 wn + 16 j + r16]
+#undef HOPE_GEMM_FETCH
+#undef HOPE_GEMM_STORE
+  // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + r16][n0 + 64 wn + 16 j + 4 q4 + v]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + 16 * j + r16;
-    const float bn = bias ? bias[n] : 0.f;
+    const int n = n0 + wn * 64 + 16 * j + 4 * q4;
+    const f32x4 bn = bias ? *reinterpret_cast<const f32x4*>(&bias[n]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + 16 * i + r16;
+      if (m >= M) continue;
+      const int64_t o = (int64_t)m * N + n;
+      const f32x4 t = acc[i][j] + bn;
+      if (EPI == kEpiF32) {
+        *reinterpret_cast<f32x4*>(&static_cast<float*>(out)[o]) = t;
+      } else if (EPI == kEpiGeluBf16) {
+        f32x4 gv;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * 64 + 16 * i + 4 * q4 + v;
-        if (m >= M) continue;
-        const int64_t o = (int64_t)m * N + n;
-        const float t = acc[i][j][v] + bn;
-        if (EPI == kEpiF32) {
-          static_cast<float*>(out)[o] = t;
-        } else if (EPI == kEpiGeluBf16) {
-          static_cast<uint16_t*>(out)[o] = to_bf16(0.5f * t * (1.f + erff(t * 0.70710678118654752f)));
-        } else {
-          static_cast<float*>(out)[o] = res[o] + t;
-        }
+        for (int v = 0; v < 4; ++v) gv[v] = 0.5f * t[v] * (1.f + erf_as(t[v] * 0.70710678118654752f));
+        uint2 u;
+        u.x = (uint32_t)to_bf16(gv[0]) | ((uint32_t)to_bf16(gv[1]) << 16);
+        u.y = (uint32_t)to_bf16(gv[2]) | ((uint32_t)to_bf16(gv[3]) << 16);
+        *reinterpret_cast<uint2*>(&static_cast<uint16_t*>(out)[o]) = u;
+      } else {
+        const f32x4 rv = *reinterpret_cast<const f32x4*>(&res[o]);
+        *reinterpret_cast<f32x4*>(&static_cast<float*>(out)[o]) = rv + t;
       }
     }
   }
