@@ -170,6 +170,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   __shared__ __attribute__((aligned(16))) float LTs[(D / 16) * kSB * LTLD];
   // running readout: the masked token matrix A^T and the unscaled write vectors U
   __shared__ __attribute__((aligned(16))) float Ais[RUN ? 64 * 4 : 4];
+  // given queries of the current block (fp32), staged one block ahead like x
+  __shared__ __attribute__((aligned(16))) float Qs[VAR && !RUN ? kSB * D : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuH[RUN ? kSB * XLD : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuL[RUN ? kSB * XLD : 4];
   // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
@@ -204,10 +206,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     return ((v_frozen & 1u) && m >= NT && m < 3 * NT) || ((v_frozen & 4u) && m >= 3 * NT);
   };
   const bool gates_frozen = (v_frozen & 2u) != 0;
-  // direction scale and skip of channel c applied to a readout y of token value xc
-  auto finish = [&](float y, int64_t c, float xc) {
-    if (v_skip) y = fmaf(v_skip[c], xc, y);
-    if (v_scales) y *= v_scales[(int64_t)r * Dt + c];
+  // direction scale and skip of channel c (read once per readout tile) applied to a
+  // readout y of token value xc
+  auto finish = [&](float y, float skip_c, float scale_c, float xc) {
+    if (v_skip) y = fmaf(skip_c, xc, y);
+    if (v_scales) y *= scale_c;
     return y;
   };
   auto xs_at = [&](int t, int col) {
@@ -291,14 +294,52 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
     if (lid < kSB) pixs[lid] = lid < nt ? block_pixel(tb, lid) : 0;
   };
-  u32x4 pf;
+  // given queries (boundary-readout variant instantiations; the running readout reads them
+  // directly): 16 bytes per loader thread, threads from 0, fp32 (4 values) or bf16 (8
+  // values) per load; staged to Qs as fp32, zero past nt
+  constexpr int kQPer32 = 4, kQPer16 = 8;
+  constexpr bool kStageQ = VAR && !RUN;
+  auto fetch_q = [&](int lid, int tb, int nt) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kStageQ && v_queries) {
+      const int per = p.queries_bf16 ? kQPer16 : kQPer32;
+      const int lt = lid / (D / per), lc = lid % (D / per);
+      if (lt < nt) {
+        const int64_t e = ((int64_t)b * N + block_pixel(tb, lt)) * Dt + (int64_t)h * D + lc * per;
+        v = p.queries_bf16 ? *reinterpret_cast<const u32x4*>(static_cast<const unsigned short*>(v_queries) + e)
+                           : *reinterpret_cast<const u32x4*>(static_cast<const float*>(v_queries) + e);
+      }
+    }
+    return v;
+  };
+  auto stage_q = [&](int lid, const u32x4& v) {
+    if (kStageQ && v_queries) {
+      const int per = p.queries_bf16 ? kQPer16 : kQPer32;
+      const int lt = lid / (D / per), lc = lid % (D / per);
+      if (lt < kSB) {
+        float* q = Qs + lt * D + lc * per;
+        if (p.queries_bf16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            q[2 * e] = __uint_as_float(v[e] << 16);
+            q[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+          }
+        } else {
+          *reinterpret_cast<u32x4*>(q) = v;
+        }
+      }
+    }
+  };
+  u32x4 pf, qpf;
   {
     const int lid = threadIdx.x;
     const int nt0 = min(kSB, min(C, N));
     stage_block(lid, fetch(lid, 0, nt0), 0, nt0);
+    stage_q(lid, fetch_q(lid, 0, nt0));
     int tn, ntn;
     next_block(0, tn, ntn);
     pf = fetch(lid, tn, ntn);
+    qpf = fetch_q(lid, tn, ntn);
   }
   lds_barrier();
 
@@ -392,7 +433,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         for (int e = 0; e < CPL; ++e) {
           kr[e] = pt[e];
           vr[e] = pt[D + e];
-          qr[e] = v_queries ? query_at(p, b, pixs[t], (int64_t)h * D + c16 * CPL + e) : pt[2 * D + e];
+          qr[e] = !v_queries ? pt[2 * D + e]
+                  : kStageQ ? Qs[t * D + c16 * CPL + e]
+                            : query_at(p, b, pixs[t], (int64_t)h * D + c16 * CPL + e);
           kk += kr[e] * kr[e];
           qq += qr[e] * qr[e];
         }
@@ -483,11 +526,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           }
         } else {
           const int64_t c = (int64_t)h * D + m * 16 + c16;
+          const float skip_c = v_skip ? v_skip[c] : 0.f;
+          const float scale_c = v_scales ? v_scales[(int64_t)r * Dt + c] : 1.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
             if (t < nt)
-              dst[((int64_t)b * N + pixs[t]) * Dt + c] = finish(acc[i], c, v_skip ? xs_at(t, m * 16 + c16) : 0.f);
+              dst[((int64_t)b * N + pixs[t]) * Dt + c] =
+                  finish(acc[i], skip_c, scale_c, v_skip ? xs_at(t, m * 16 + c16) : 0.f);
           }
         }
       }
@@ -678,11 +724,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           // y_t = P(0,t) (M_mem,b G_s q_t) + sum_{j<t} P(j+1,t) (k_j . q_t) (M_mem,b u_j)
           const f32x4 at = *reinterpret_cast<const f32x4*>(Ais + 4 * lane);
           const f32x4 y = mm16(at, zu);
+          const int64_t c = (int64_t)h * D + w * 16 + c16;
+          const float skip_c = v_skip ? v_skip[c] : 0.f;
+          const float scale_c = v_scales ? v_scales[(int64_t)r * Dt + c] : 1.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
-            const int64_t c = (int64_t)h * D + w * 16 + c16;
-            if (t < nt) dst[((int64_t)b * N + rpix[i]) * Dt + c] = finish(cprev[t] * rq[i] + y[i], c, rx[i]);
+            if (t < nt)
+              dst[((int64_t)b * N + rpix[i]) * Dt + c] = finish(cprev[t] * rq[i] + y[i], skip_c, scale_c, rx[i]);
           }
         }
         // gate rows at d = 32: every readout wave forms their Z tile and updates column
@@ -786,9 +835,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           int lid2 = threadIdx.x;
           asm volatile("" : "+v"(lid2));
           stage_block(lid2, pf, tn, ntn);
+          stage_q(lid2, qpf);
           int tn2, ntn2;
           next_block(tn, tn2, ntn2);
           pf = fetch(lid2, tn2, ntn2);
+          qpf = fetch_q(lid2, tn2, ntn2);
         }
       }
       lds_barrier();
