@@ -30,6 +30,7 @@ bool sizes_ok(int32_t B, int32_t H, int32_t W, int32_t D, int32_t n_heads, int32
   if (D % 128 || ffn_dim % 128 || D % n_heads) return false;
   const int vpl = D / 64;
   if (vpl != 2 && vpl != 4 && vpl != 6 && vpl != 8 && vpl != 12 && vpl != 16) return false;
+  if ((int64_t)B * H * ((W + 3) / 4) * (D / 4) >= (int64_t)1 << 31) return false;  // stencil indexing
   if ((int64_t)B * H * W > (int64_t)1 << 31) return false;
   return true;
 }

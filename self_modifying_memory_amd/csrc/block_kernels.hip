@@ -185,35 +185,51 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
                                                          const float* __restrict__ wgt,
                                                          const float* __restrict__ bias, OutT* out,
                                                          int B, int H, int W, int C) {
-  const int cq = C / 4;
-  const int64_t total = (int64_t)B * H * W * cq;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i % cq) * 4;
-    const int64_t p = i / cq;
-    const int x = (int)(p % W), y = (int)((p / W) % H);
-    const int64_t img = p / ((int64_t)H * W);
-    f32x4 acc = *reinterpret_cast<const f32x4*>(&bias[c]);
+  // one thread: four channels of four consecutive pixels of a row (x0 .. x0 + 3), so that
+  // the 3 x 6 input neighbourhood and the nine weights are read once for four outputs
+  // (32-bit index arithmetic: the host bounds B * H * ceil(W / 4) * C / 4 below 2^31)
+  const int cq = C / 4, xq = (W + 3) / 4;
+  const int total = B * H * xq * cq;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int c = (i % cq) * 4;
+    const int rest = i / cq;
+    const int x0 = (rest % xq) * 4;
+    const int y = (rest / xq) % H;
+    const int64_t img = rest / (xq * H);
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bias[c]);
+    f32x4 acc[4] = {b4, b4, b4, b4};
 #pragma unroll
     for (int dy = 0; dy < 3; ++dy) {
       const int yy = y + dy - 1;
       if (yy < 0 || yy >= H) continue;
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 0) * C + c]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 1) * C + c]);
+      const f32x4 w2 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 2) * C + c]);
+      const SrcT* row = src + ((img * H + yy) * W) * (int64_t)C + c;
+      f32x4 v[6];
 #pragma unroll
-      for (int dx = 0; dx < 3; ++dx) {
-        const int xx = x + dx - 1;
-        if (xx < 0 || xx >= W) continue;
-        const f32x4 v = load4(&src[((img * H + yy) * W + xx) * C + c]);
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + dx) * C + c]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e], v[e], acc[e]);
+      for (int k = 0; k < 6; ++k) {
+        const int xx = x0 - 1 + k;
+        v[k] = (xx >= 0 && xx < W) ? load4(row + (int64_t)xx * C) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    if (SILU) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = acc[e] / (1.f + expf(-acc[e]));
+      for (int o = 0; o < 4; ++o)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[o][e] = fmaf(w2[e], v[o + 2][e], fmaf(w1[e], v[o + 1][e], fmaf(w0[e], v[o][e], acc[o][e])));
     }
-    const f32x4 r = load4(&res[p * C + c]);
-    store4(&out[p * C + c], r + acc);
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      if (x0 + o >= W) break;
+      f32x4 a = acc[o];
+      if (SILU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = a[e] / (1.f + expf(-a[e]));
+      }
+      const int64_t p = (img * H + y) * W + x0 + o;
+      const f32x4 r = load4(&res[p * C + c]);
+      store4(&out[p * C + c], r + a);
+    }
   }
 }
 
@@ -283,21 +299,21 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int 
 
 hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
                              int H, int W, int C, hipStream_t s) {
-  const int64_t work = (int64_t)B * H * W * (C / 4);
+  const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
   dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, out, B, H, W, C);
   return hipGetLastError();
 }
 
 hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
                                int H, int W, int C, hipStream_t s) {
-  const int64_t work = (int64_t)B * H * W * (C / 4);
+  const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
   dwconv3x3_kernel<float, float, uint16_t, true><<<grid_for(work, 256), 256, 0, s>>>(u, u, w, b, z, B, H, W, C);
   return hipGetLastError();
 }
 
 hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* w, const float* b,
                              uint16_t* out, int B, int H, int W, int C, hipStream_t s) {
-  const int64_t work = (int64_t)B * H * W * (C / 4);
+  const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
   dwconv3x3_kernel<uint16_t, float, uint16_t, false><<<grid_for(work, 256), 256, 0, s>>>(z, y, w, b, out, B, H, W, C);
   return hipGetLastError();
 }
