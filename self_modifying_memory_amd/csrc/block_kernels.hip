@@ -14,9 +14,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {  // round to nearest even (finite f)
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats to bf16, round to nearest even (one v_cvt_pk_bf16_f32): a in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // erf by Abramowitz and Stegun 7.1.26 (|error| <= 1.5e-7): for x >= 0,
@@ -32,6 +38,15 @@ __device__ __forceinline__ float erf_as(float x) {
   return copysignf(y, x);
 }
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round robin by their index.  The
+// logical tile index below gives each XCD one contiguous range of the G tiles instead, so
+// that the tiles sharing an operand panel (GEMM) or a halo row (convolution) meet in one L2:
+// with G = 8 q + r, XCD x < r takes q + 1 tiles, the others q.
+__device__ __forceinline__ int xcd_tile(int bid, int G) {
+  const int x = bid & 7, j = bid >> 3, q = G >> 3, r = G & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
 // ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
 // Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
 // K in steps of 64 (two MFMA k-steps) through double-buffered LDS (rows padded to 72 bf16),
@@ -40,7 +55,7 @@ __device__ __forceinline__ float erf_as(float x) {
 // feeds row r16 of the weight tile and row r16 of the activation tile with the 8 consecutive
 // k values 8 q4 .. 8 q4 + 7 of each 32-deep half (the same k order on both sides), and holds
 // C[m = 16 i + r16][n = 16 j + 4 q4 + v].
-// Requires N % 128 == 0 and K % 64 == 0; rows past M are read clamped and not written.
+// Requires N % 128 == 0 and K % 128 == 0; rows past M are read clamped and not written.
 constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
 
 template <int EPI>
@@ -53,7 +68,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4, wm = w >> 1, wn = w & 1;
   const int tiles_n = N / kBN;
-  const int m0 = (blockIdx.x / tiles_n) * kBM, n0 = (blockIdx.x % tiles_n) * kBN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / tiles_n) * kBM, n0 = (tile % tiles_n) * kBN;
 
   // global -> registers -> LDS: 4 chunks of 8 bf16 per thread for each operand
   // (rows tid / 8 + 32 c, k chunk 8 (tid % 8))
@@ -64,27 +80,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   const int64_t da3 = (int64_t)(min(m0 + row + 96, M - 1) - min(m0 + row, M - 1)) * K;
   const uint16_t* pb = Wt + (int64_t)(n0 + row) * K + ch;
   const int64_t db = (int64_t)32 * K;
-  uint4 ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
-#define HOPE_GEMM_FETCH(k)                                           \
-  ga0 = *reinterpret_cast<const uint4*>(pa + (k));                   \
-  ga1 = *reinterpret_cast<const uint4*>(pa + da1 + (k));             \
-  ga2 = *reinterpret_cast<const uint4*>(pa + da2 + (k));             \
-  ga3 = *reinterpret_cast<const uint4*>(pa + da3 + (k));             \
-  gb0 = *reinterpret_cast<const uint4*>(pb + (k));                   \
-  gb1 = *reinterpret_cast<const uint4*>(pb + db + (k));              \
-  gb2 = *reinterpret_cast<const uint4*>(pb + 2 * db + (k));          \
-  gb3 = *reinterpret_cast<const uint4*>(pb + 3 * db + (k));
-#define HOPE_GEMM_STORE(buf)                                                       \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga0;                \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 32) * kLDK + ch]) = ga1;               \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga2;               \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 96) * kLDK + ch]) = ga3;               \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb0;                \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 32) * kLDK + ch]) = gb1;               \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb2;               \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 96) * kLDK + ch]) = gb3;
-  HOPE_GEMM_FETCH(0)
-  HOPE_GEMM_STORE(0)
+  // two register sets (0, 1) of the global -> LDS staging, so that a tile's loads are issued
+  // two steps before its LDS store
+  uint4 ga00, ga01, ga02, ga03, gb00, gb01, gb02, gb03;
+  uint4 ga10, ga11, ga12, ga13, gb10, gb11, gb12, gb13;
+#define HOPE_GEMM_FETCH(S, k)                                        \
+  ga##S##0 = *reinterpret_cast<const uint4*>(pa + (k));              \
+  ga##S##1 = *reinterpret_cast<const uint4*>(pa + da1 + (k));        \
+  ga##S##2 = *reinterpret_cast<const uint4*>(pa + da2 + (k));        \
+  ga##S##3 = *reinterpret_cast<const uint4*>(pa + da3 + (k));        \
+  gb##S##0 = *reinterpret_cast<const uint4*>(pb + (k));              \
+  gb##S##1 = *reinterpret_cast<const uint4*>(pb + db + (k));         \
+  gb##S##2 = *reinterpret_cast<const uint4*>(pb + 2 * db + (k));     \
+  gb##S##3 = *reinterpret_cast<const uint4*>(pb + 3 * db + (k));
+#define HOPE_GEMM_STORE(S, buf)                                                    \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga##S##0;           \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 32) * kLDK + ch]) = ga##S##1;          \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga##S##2;          \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 96) * kLDK + ch]) = ga##S##3;          \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb##S##0;           \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 32) * kLDK + ch]) = gb##S##1;          \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb##S##2;          \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 96) * kLDK + ch]) = gb##S##3;
+#define HOPE_GEMM_COMPUTE(buf)                                                                   \
+  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
+    bf16x8 a[4], bv[4];                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]); \
+      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]); \
+    }                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);    \
+  }
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -92,35 +120,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K = 128 n: tile t (64 deep) is loaded into set t % 2 at step t - 3 (the first three
+  // before the loop), stored into LDS buffer t % 2 at step t - 1 and multiplied at step t;
+  // the barrier closing step t - 1 retires every read of the buffer that step t stores to
+  HOPE_GEMM_FETCH(0, 0)
+  HOPE_GEMM_STORE(0, 0)
+  HOPE_GEMM_FETCH(1, kBK)
+  if (2 * kBK < K) {
+    HOPE_GEMM_FETCH(0, 2 * kBK)
+  }
   __syncthreads();
-  int cur = 0;
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    const bool more = k0 + kBK < K;
-    if (more) {
-      HOPE_GEMM_FETCH(k0 + kBK)
+  for (int k0 = 0; k0 < K; k0 += 2 * kBK) {
+    HOPE_GEMM_STORE(1, 1)
+    if (k0 + 3 * kBK < K) {
+      HOPE_GEMM_FETCH(1, k0 + 3 * kBK)
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 a[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]);
-        bv[i] = *reinterpret_cast<const bf16x8*>(&sB[cur][(wn * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      HOPE_GEMM_STORE(cur ^ 1)
-    }
+    HOPE_GEMM_COMPUTE(0)
     __syncthreads();
-    cur ^= 1;
+    if (k0 + 2 * kBK < K) {
+      HOPE_GEMM_STORE(0, 0)
+      if (k0 + 4 * kBK < K) {
+        HOPE_GEMM_FETCH(0, k0 + 4 * kBK)
+      }
+    }
+    HOPE_GEMM_COMPUTE(1)
+    __syncthreads();
   }
 
 #undef HOPE_GEMM_FETCH
 #undef HOPE_GEMM_STORE
+#undef HOPE_GEMM_COMPUTE
   // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + r16][n0 + 64 wn + 16 j + 4 q4 + v]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -137,10 +166,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
       } else if (EPI == kEpiGeluBf16) {
         f32x4 gv;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) gv[v] = 0.5f * t[v] * (1.f + erf_as(t[v] * 0.70710678118654752f));
+        for (int v = 0; v < 4; ++v) {  // GELU(t) = t / 2 + (t / 2) erf(t / sqrt 2)
+          const float hv = 0.5f * t[v];
+          gv[v] = fmaf(hv, erf_as(t[v] * 0.70710678118654752f), hv);
+        }
         uint2 u;
-        u.x = (uint32_t)to_bf16(gv[0]) | ((uint32_t)to_bf16(gv[1]) << 16);
-        u.y = (uint32_t)to_bf16(gv[2]) | ((uint32_t)to_bf16(gv[3]) << 16);
+        u.x = pack_bf16(gv[0], gv[1]);
+        u.y = pack_bf16(gv[2], gv[3]);
         *reinterpret_cast<uint2*>(&static_cast<uint16_t*>(out)[o]) = u;
       } else {
         const f32x4 rv = *reinterpret_cast<const f32x4*>(&res[o]);
@@ -174,8 +206,8 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
 template <>
 __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4 v) {
   uint2 u;
-  u.x = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
-  u.y = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
+  u.x = pack_bf16(v[0], v[1]);
+  u.y = pack_bf16(v[2], v[3]);
   *reinterpret_cast<uint2*>(p) = u;
 }
 
@@ -190,7 +222,8 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
   // (32-bit index arithmetic: the host bounds B * H * ceil(W / 4) * C / 4 below 2^31)
   const int cq = C / 4, xq = (W + 3) / 4;
   const int total = B * H * xq * cq;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+  for (int i = xcd_tile(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x; i < total;
+       i += gridDim.x * blockDim.x) {
     const int c = (i % cq) * 4;
     const int rest = i / cq;
     const int x0 = (rest % xq) * 4;
@@ -286,7 +319,7 @@ unsigned grid_for(int64_t work, int per_block) {
 
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s) {
-  if (N % kBN || K % kBK || M <= 0) return hipErrorInvalidValue;
+  if (N % kBN || K % (2 * kBK) || M <= 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(((M + kBM - 1) / kBM) * (N / kBN))), block(256);
   switch (epi) {
     case kEpiF32: gemm_bf16_kernel<kEpiF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
