@@ -6,6 +6,7 @@
 
 #include "../../include/hope_scan2d.h"
 #include "kernels.h"
+#include "scan_api.h"
 
 namespace {
 
@@ -150,28 +151,12 @@ bool backward_opts_supported(const hope_scan2d_opts_t& o) {
 
 }  // namespace
 
-extern "C" {
+namespace hope {
 
-void hope_scan2d_default_opts(hope_scan2d_opts_t* opts) {
-  if (!opts) return;
-  memset(opts, 0, sizeof(*opts));
-  opts->eta_map = HOPE_ETA_SIGMOID;
-  opts->eta_scale = 1.0f;
-  opts->alpha_bias = 4.0f;
-  opts->eps = 1e-6f;
-}
-
-size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
-                                  const hope_scan2d_opts_t* opts) {
-  if (check_fmap(x) != HOPE_OK || dirs == 0 || dirs > 15 || chunk < 0) return 0;
-  const int32_t out_dtype = opts ? opts->out_dtype : HOPE_F32;
-  if (out_dtype != HOPE_F32 && out_dtype != HOPE_BF16) return 0;
-  return workspace_bytes_for(x, dirs, out_dtype);
-}
-
-hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
-                                  uint32_t dirs, int32_t chunk, void* out,
-                                  const hope_scan2d_opts_t* opts) {
+hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uint32_t dirs,
+                           int32_t chunk, void* out, const hope_scan2d_opts_t* opts,
+                           RoutePlanes* defer) {
+  if (defer) *defer = RoutePlanes{nullptr, 0, 0};
   hope_scan2d_opts_t o;
   if (opts) {
     o = *opts;
@@ -280,8 +265,41 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
     return hip_status(hope::launch_plane_sum_bf16(static_cast<unsigned short*>(out), p.out,
                                                   p.plane_stride, p.n_sel, n_elem, s));
   if (p.n_sel == 1) return st;
+  if (defer) {  // the caller adds the planes to out
+    defer->planes = p.planes;
+    defer->stride = p.plane_stride;
+    defer->n = p.n_sel - 1;
+    return st;
+  }
   return hip_status(
       hope::launch_plane_sum(static_cast<float*>(out), p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
+}
+
+}  // namespace hope
+
+extern "C" {
+
+void hope_scan2d_default_opts(hope_scan2d_opts_t* opts) {
+  if (!opts) return;
+  memset(opts, 0, sizeof(*opts));
+  opts->eta_map = HOPE_ETA_SIGMOID;
+  opts->eta_scale = 1.0f;
+  opts->alpha_bias = 4.0f;
+  opts->eps = 1e-6f;
+}
+
+size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                  const hope_scan2d_opts_t* opts) {
+  if (check_fmap(x) != HOPE_OK || dirs == 0 || dirs > 15 || chunk < 0) return 0;
+  const int32_t out_dtype = opts ? opts->out_dtype : HOPE_F32;
+  if (out_dtype != HOPE_F32 && out_dtype != HOPE_BF16) return 0;
+  return workspace_bytes_for(x, dirs, out_dtype);
+}
+
+hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memories,
+                                  uint32_t dirs, int32_t chunk, void* out,
+                                  const hope_scan2d_opts_t* opts) {
+  return hope::scan_forward(x, init_memories, dirs, chunk, out, opts, nullptr);
 }
 
 size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,

@@ -8,6 +8,7 @@
 
 #include "../../include/hope_block.h"
 #include "block_kernels.h"
+#include "scan_api.h"
 
 hope_status_t hope_status_of(hipError_t e);
 
@@ -140,9 +141,13 @@ hope_status_t hope_block_forward(const float* x, int32_t B, int32_t H, int32_t W
   if ((e = hope::launch_gemm_bf16(hope::kEpiF32, z, wt->w_q, Mi, D, D, nullptr, nullptr, q, stream)))
     return hope_status_of(e);
   // y = VH(z; q, skip, scales); y2 = y + LPE(z)
-  const hope_status_t st = hope_scan2d_forward(&zm, wt->init_memories, HOPE_DIR_ALL, chunk, y, &o);
+  // (the operator's route sum, in slot order, is fused into the local positional branch)
+  hope::RoutePlanes rp;
+  const hope_status_t st = hope::scan_forward(&zm, wt->init_memories, HOPE_DIR_ALL, chunk, y, &o, &rp);
   if (st != HOPE_OK) return st;
-  if ((e = hope::launch_dwconv_lpe(z, y, wt->lpe_w, wt->lpe_b, y2, B, H, W, D, stream))) return hope_status_of(e);
+  if ((e = hope::launch_dwconv_lpe(z, y, rp.planes, rp.stride, rp.n, wt->lpe_w, wt->lpe_b, y2, B, H, W,
+                                   D, stream)))
+    return hope_status_of(e);
   // x' = r + y2 W_out^T (b_out already in r); a = LN2(x'); out = x' + b2
   if ((e = hope::launch_gemm_bf16(hope::kEpiResidualF32, y2, wt->w_out, Mi, D, D, nullptr, r, r, stream)))
     return hope_status_of(e);

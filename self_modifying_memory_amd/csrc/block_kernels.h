@@ -20,8 +20,11 @@ hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, flo
 // z = bf16(u + SiLU(DW(u))) (the gated depthwise branch)
 hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
                                int H, int W, int C, hipStream_t s);
-// out = bf16(y + DW(z)) (the local positional branch added to the operator output)
-hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* w, const float* b,
+// out = bf16(y' + DW(z)) (the local positional branch added to the operator output), where
+// y' = y + planes[0] + ... + planes[n_planes - 1] (left to right, planes plane_stride floats
+// apart: the operator's unsummed route planes; n_planes may be 0)
+hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* planes,
+                             int64_t plane_stride, int n_planes, const float* w, const float* b,
                              uint16_t* out, int B, int H, int W, int C, hipStream_t s);
 // y = bf16(LayerNorm(x) g + b); if x_plus: x_plus = x + addv.  C % 64 == 0, C / 64 in
 // {1, 2, 3, 4, 6, 8, 12, 16}.

@@ -183,8 +183,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 }
 
 // ---- depthwise 3x3 convolution with a fused residual --------------------------------------
-// out[p][c] = res[p][c] + act(bias[c] + sum over the 3x3 neighbourhood (zero padding) of
-// w[dy][dx][c] src[p + (dy - 1, dx - 1)][c]); four channels per thread.
+// out[p][c] = res'[p][c] + act(bias[c] + sum over the 3x3 neighbourhood (zero padding) of
+// w[dy][dx][c] src[p + (dy - 1, dx - 1)][c]), res' = res + planes[0] + ... + planes[n - 1]
+// (added left to right); four channels per thread.
 template <typename T>
 __device__ __forceinline__ f32x4 load4(const T* p);
 template <>
@@ -216,7 +217,9 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
                                                          const ResT* __restrict__ res,
                                                          const float* __restrict__ wgt,
                                                          const float* __restrict__ bias, OutT* out,
-                                                         int B, int H, int W, int C) {
+                                                         int B, int H, int W, int C,
+                                                         const float* __restrict__ planes,
+                                                         int64_t plane_stride, int n_planes) {
   // one thread: four channels of four consecutive pixels of a row (x0 .. x0 + 3), so that
   // the 3 x 6 input neighbourhood and the nine weights are read once for four outputs
   // (32-bit index arithmetic: the host bounds B * H * ceil(W / 4) * C / 4 below 2^31)
@@ -260,7 +263,8 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
         for (int e = 0; e < 4; ++e) a[e] = a[e] / (1.f + expf(-a[e]));
       }
       const int64_t p = (img * H + y) * W + x0 + o;
-      const f32x4 r = load4(&res[p * C + c]);
+      f32x4 r = load4(&res[p * C + c]);
+      for (int k = 0; k < n_planes; ++k) r += load4(&planes[k * plane_stride + p * C + c]);
       store4(&out[p * C + c], r + a);
     }
   }
@@ -333,21 +337,22 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int 
 hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
                              int H, int W, int C, hipStream_t s) {
   const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
-  dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, out, B, H, W, C);
+  dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, out, B, H, W, C, nullptr, 0, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
                                int H, int W, int C, hipStream_t s) {
   const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
-  dwconv3x3_kernel<float, float, uint16_t, true><<<grid_for(work, 256), 256, 0, s>>>(u, u, w, b, z, B, H, W, C);
+  dwconv3x3_kernel<float, float, uint16_t, true><<<grid_for(work, 256), 256, 0, s>>>(u, u, w, b, z, B, H, W, C, nullptr, 0, 0);
   return hipGetLastError();
 }
 
-hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* w, const float* b,
+hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* planes,
+                             int64_t plane_stride, int n_planes, const float* w, const float* b,
                              uint16_t* out, int B, int H, int W, int C, hipStream_t s) {
   const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
-  dwconv3x3_kernel<uint16_t, float, uint16_t, false><<<grid_for(work, 256), 256, 0, s>>>(z, y, w, b, out, B, H, W, C);
+  dwconv3x3_kernel<uint16_t, float, uint16_t, false><<<grid_for(work, 256), 256, 0, s>>>(z, y, w, b, out, B, H, W, C, planes, plane_stride, n_planes);
   return hipGetLastError();
 }
 
