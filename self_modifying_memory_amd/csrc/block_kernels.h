@@ -10,7 +10,7 @@ enum { kEpiF32 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
 
 // out[m][n] = epi(sum_k A[m][k] Wt[n][k] + bias[n]): kEpiF32 -> fp32 out; kEpiGeluBf16 ->
 // bf16 GELU(.) (erf form, erf by Abramowitz-Stegun 7.1.26); kEpiResidualF32 -> fp32 res[m][n] + (.) (res may equal out).
-// bias may be null.  N % 128 == 0, K % 128 == 0; A, Wt, bias, res, out 16-byte aligned.
+// bias may be null.  N % 128 == 0, K % 64 == 0; A, Wt, bias, res, out 16-byte aligned.
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s);
 

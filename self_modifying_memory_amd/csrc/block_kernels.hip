@@ -49,20 +49,21 @@ __device__ __forceinline__ int xcd_tile(int bid, int G) {
 
 // ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
 // Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
-// K in steps of 64 (two MFMA k-steps) through double-buffered LDS (rows padded to 72 bf16),
-// one barrier a step.  The MFMA computes the transposed tile (weights as its A operand), so
-// that a lane's four results are four consecutive output columns of one row: lane (r16, q4)
-// feeds row r16 of the weight tile and row r16 of the activation tile with the 8 consecutive
-// k values 8 q4 .. 8 q4 + 7 of each 32-deep half (the same k order on both sides), and holds
+// K in steps of 32 (one MFMA k-step) through double-buffered LDS (rows padded to 40 bf16:
+// 40 KB a workgroup, so that four share a CU and hide each other's barriers), one barrier a
+// step.  The MFMA computes the transposed tile (weights as its A operand), so that a lane's
+// four results are four consecutive output columns of one row: lane (r16, q4) feeds row r16
+// of the weight tile and row r16 of the activation tile with the 8 consecutive k values
+// 8 q4 .. 8 q4 + 7 (the same k order on both sides), and holds
 // C[m = 16 i + r16][n = 16 j + 4 q4 + v].
-// Requires N % 128 == 0 and K % 128 == 0; rows past M are read clamped and not written.
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
+// Requires N % 128 == 0 and K % 64 == 0; rows past M are read clamped and not written.
+constexpr int kBM = 128, kBN = 128, kBK = 32, kLDK = kBK + 8;
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ Wt, int M,
-                                                         int N, int K, const float* bias,
-                                                         const float* res, void* out) {
+__global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                            const uint16_t* __restrict__ Wt, int M,
+                                                            int N, int K, const float* bias,
+                                                            const float* res, void* out) {
   __shared__ __align__(16) uint16_t sA[2][kBM * kLDK];
   __shared__ __align__(16) uint16_t sB[2][kBN * kLDK];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -71,43 +72,30 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * kBM, n0 = (tile % tiles_n) * kBN;
 
-  // global -> registers -> LDS: 4 chunks of 8 bf16 per thread for each operand
-  // (rows tid / 8 + 32 c, k chunk 8 (tid % 8))
-  const int row = tid >> 3, ch = 8 * (tid & 7);
+  // global -> registers -> LDS: 2 chunks of 8 bf16 per thread for each operand
+  // (rows tid / 4 and tid / 4 + 64, k chunk 8 (tid % 4))
+  const int row = tid >> 2, ch = 8 * (tid & 3);
   const uint16_t* pa = A + (int64_t)min(m0 + row, M - 1) * K + ch;
-  const int64_t da1 = (int64_t)(min(m0 + row + 32, M - 1) - min(m0 + row, M - 1)) * K;
-  const int64_t da2 = (int64_t)(min(m0 + row + 64, M - 1) - min(m0 + row, M - 1)) * K;
-  const int64_t da3 = (int64_t)(min(m0 + row + 96, M - 1) - min(m0 + row, M - 1)) * K;
+  const int64_t da1 = (int64_t)(min(m0 + row + 64, M - 1) - min(m0 + row, M - 1)) * K;
   const uint16_t* pb = Wt + (int64_t)(n0 + row) * K + ch;
-  const int64_t db = (int64_t)32 * K;
-  // two register sets (0, 1) of the global -> LDS staging, so that a tile's loads are issued
-  // two steps before its LDS store
-  uint4 ga00, ga01, ga02, ga03, gb00, gb01, gb02, gb03;
-  uint4 ga10, ga11, ga12, ga13, gb10, gb11, gb12, gb13;
-#define HOPE_GEMM_FETCH(S, k)                                        \
-  ga##S##0 = *reinterpret_cast<const uint4*>(pa + (k));              \
-  ga##S##1 = *reinterpret_cast<const uint4*>(pa + da1 + (k));        \
-  ga##S##2 = *reinterpret_cast<const uint4*>(pa + da2 + (k));        \
-  ga##S##3 = *reinterpret_cast<const uint4*>(pa + da3 + (k));        \
-  gb##S##0 = *reinterpret_cast<const uint4*>(pb + (k));              \
-  gb##S##1 = *reinterpret_cast<const uint4*>(pb + db + (k));         \
-  gb##S##2 = *reinterpret_cast<const uint4*>(pb + 2 * db + (k));     \
-  gb##S##3 = *reinterpret_cast<const uint4*>(pb + 3 * db + (k));
-#define HOPE_GEMM_STORE(S, buf)                                                    \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga##S##0;           \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 32) * kLDK + ch]) = ga##S##1;          \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga##S##2;          \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 96) * kLDK + ch]) = ga##S##3;          \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb##S##0;           \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 32) * kLDK + ch]) = gb##S##1;          \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb##S##2;          \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 96) * kLDK + ch]) = gb##S##3;
+  const int64_t db = (int64_t)64 * K;
+  uint4 ga00, ga01, gb00, gb01;
+#define HOPE_GEMM_FETCH(S, k)                                 \
+  ga##S##0 = *reinterpret_cast<const uint4*>(pa + (k));       \
+  ga##S##1 = *reinterpret_cast<const uint4*>(pa + da1 + (k)); \
+  gb##S##0 = *reinterpret_cast<const uint4*>(pb + (k));       \
+  gb##S##1 = *reinterpret_cast<const uint4*>(pb + db + (k));
+#define HOPE_GEMM_STORE(S, buf)                                            \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga##S##0;   \
+  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga##S##1;  \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb##S##0;   \
+  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb##S##1;
 #define HOPE_GEMM_COMPUTE(buf)                                                                   \
-  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                \
+  {                                                                                              \
     bf16x8 a[4], bv[4];                                                                          \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]); \
-      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + 16 * i + r16) * kLDK + 32 * h + 8 * q4]); \
+      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + 16 * i + r16) * kLDK + 8 * q4]); \
+      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + 16 * i + r16) * kLDK + 8 * q4]); \
     }                                                                                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
@@ -120,27 +108,25 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K = 128 n: tile t (64 deep) is loaded into set t % 2 at step t - 3 (the first three
-  // before the loop), stored into LDS buffer t % 2 at step t - 1 and multiplied at step t;
-  // the barrier closing step t - 1 retires every read of the buffer that step t stores to
+  // tile t (32 deep) is loaded into registers during step t - 2, stored into LDS buffer
+  // t % 2 during step t - 1 and multiplied at step t; the barrier closing step t - 1 retires
+  // every read of the buffer that step t - 1 stores to (the four workgroups on a CU hide
+  // the latency that the single register set leaves)
   HOPE_GEMM_FETCH(0, 0)
   HOPE_GEMM_STORE(0, 0)
-  HOPE_GEMM_FETCH(1, kBK)
-  if (2 * kBK < K) {
-    HOPE_GEMM_FETCH(0, 2 * kBK)
-  }
+  HOPE_GEMM_FETCH(0, kBK)
   __syncthreads();
   for (int k0 = 0; k0 < K; k0 += 2 * kBK) {
-    HOPE_GEMM_STORE(1, 1)
-    if (k0 + 3 * kBK < K) {
-      HOPE_GEMM_FETCH(1, k0 + 3 * kBK)
+    HOPE_GEMM_STORE(0, 1)
+    if (k0 + 2 * kBK < K) {
+      HOPE_GEMM_FETCH(0, k0 + 2 * kBK)
     }
     HOPE_GEMM_COMPUTE(0)
     __syncthreads();
     if (k0 + 2 * kBK < K) {
       HOPE_GEMM_STORE(0, 0)
-      if (k0 + 4 * kBK < K) {
-        HOPE_GEMM_FETCH(0, k0 + 4 * kBK)
+      if (k0 + 3 * kBK < K) {
+        HOPE_GEMM_FETCH(0, k0 + 3 * kBK)
       }
     }
     HOPE_GEMM_COMPUTE(1)
