@@ -71,7 +71,8 @@ size_t hope_block_workspace_size(int32_t B, int32_t H, int32_t W, int32_t D, int
  * hope_block_forward -- one block on x (fp32 [B][H][W][D]) into out (fp32, same shape; may
  * not alias x).  chunk: the operator's chunk length (0 = aligned, Eq. 25).  workspace:
  * device scratch of at least hope_block_workspace_size() bytes, 256-byte aligned; its
- * contents are not kept.  Returns HOPE_ERR_INVALID_ARG for bad sizes, null or misaligned
+ * contents are not kept.  The weights are only read; they must not overlap out or the
+ * workspace (the aliasing check covers x, out and the workspace only).  Returns HOPE_ERR_INVALID_ARG for bad sizes, null or misaligned
  * pointers or aliasing, HOPE_ERR_UNSUPPORTED for a head dimension other than 16/32/64,
  * HOPE_ERR_WORKSPACE for a short workspace, HOPE_ERR_HIP when a launch fails.
  */

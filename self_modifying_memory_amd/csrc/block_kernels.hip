@@ -309,8 +309,10 @@ unsigned grid_for(int64_t work, int per_block) {
 
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s) {
-  if (N % kBN || K % (2 * kBK) || M <= 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(((M + kBM - 1) / kBM) * (N / kBN))), block(256);
+  if (N % kBN || K % (2 * kBK) || M <= 0 || K <= 0) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * (N / kBN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), block(256);
   switch (epi) {
     case kEpiF32: gemm_bf16_kernel<kEpiF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
     case kEpiGeluBf16: gemm_bf16_kernel<kEpiGeluBf16><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
