@@ -46,6 +46,7 @@ CASES = [
     (2, 3, 7, 128, 4, 256, 3),     # d = 32, ragged chunks
     (1, 5, 4, 128, 8, 512, 0),     # d = 16
     (1, 6, 6, 256, 4, 1024, 0),    # d = 64, wider
+    (3, 9, 10, 128, 2, 256, 5),    # d = 64, 270 pixels: three GEMM row tiles, the last ragged
 ]
 
 
