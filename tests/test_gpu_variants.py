@@ -130,3 +130,55 @@ def test_variants_with_running_readout(shape):
     e_out = check_out(out, ref_out, sh[4], tol)
     e_fin = check_final(fin, ref_fin, d, 15, tol)
     print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+# The two variant sets the benchmark times, at the full stage-3 size and launch
+# configuration; the oracle checks sampled (image, head) slices (all four routes).
+FULL_SETS = {
+    "scales_skip_hard_injection": dict(route_scales=True, skip=True, injection="hard"),
+    "frozen_kv_no_dgd_queries": dict(frozen=("kv",), no_dgd=True, queries=True),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SETS), ids=list(FULL_SETS))
+def test_variant_sets_full_size_stage3_sampled(name):
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    var = FULL_SETS[name]
+    w = wl.WORKLOADS[3]
+    images, heads = [0, 127], [0, 5]
+    print(f"workload {w.name} variants {name}: images {images} heads {heads}", flush=True)
+    inp = wl.draw_workload(w, live=True)
+    x, init = to_device(inp, w.dtype)
+    rng = np.random.Generator(np.random.PCG64(29))
+    ok, gk = {}, {}
+    if var.get("route_scales"):
+        lam = rng.uniform(0.5, 1.5, (4, w.D)).astype(np.float32)
+        ok["route_scales"] = lam.astype(np.float64)
+        gk["route_scales"] = torch.from_numpy(lam).cuda()
+    if var.get("skip"):
+        sk = (rng.standard_normal(w.D) * 0.3).astype(np.float32)
+        ok["skip"] = sk.astype(np.float64)
+        gk["skip"] = torch.from_numpy(sk).cuda()
+    if "injection" in var:
+        ok["injection"] = gk["injection"] = var["injection"]
+    if "frozen" in var:
+        gk["frozen"] = var["frozen"]
+        ok["frozen"] = tuple(m for f in var["frozen"] for m in FROZEN[f])
+    if var.get("no_dgd"):
+        gk["no_dgd"] = True
+        ok["dgd"] = False
+    if var.get("queries"):
+        qt = torch.from_numpy(rng.standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32) * 0.7).to(torch.bfloat16)
+        ok["queries"] = qt.float().numpy().astype(np.float64)
+        gk["queries"] = qt.cuda()
+    d = w.d
+    fin = torch.full((w.B, 4, w.n_heads, 4 * d * d + 2 * d), float("nan"), dtype=torch.float32, device="cuda")
+    out = hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, final_memories=fin, **gk)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], w.n_heads, dirs=15, chunk=w.chunk,
+                                     heads=heads, images=images, **ok)
+    tol = TOL[w.dtype]
+    e_out = check_out(out.cpu().numpy(), ref_out, w.n_heads, tol, heads=heads, images=images)
+    e_fin = check_final(fin.cpu().numpy(), ref_fin, d, 15, tol, heads=heads, images=images)
+    print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
