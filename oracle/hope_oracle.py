@@ -310,7 +310,7 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
            readout: str = "boundary", injection: str = "soft", spectral: str = "clamp",
            frozen=(), dgd: bool = True, route_scales=None, skip=None,
            shared_init: bool = False, counts: dict | None = None, queries=None,
-           mem_chunk: int = 0):
+           mem_chunk: int = 0, step_map: np.ndarray | None = None):
     """The whole operator: serialise, run every (image, head, route) chain, merge.
 
     x    : [B, H, W, D] (any float dtype; widened to fp64)
@@ -330,6 +330,10 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
     once per image and reused by every route (serialised like x, split into heads).
     mem_chunk > 0 gives the working memory its own chunk length (srnl_chain); 0 keeps one
     chunk size for all six memories.
+    step_map [b, 4, h, H, W] (optional, filled in place): the executed step eta_tilde of
+    [VH] Eq. 20 (or of the selected ablation control) of every token of a computed chain,
+    at the token's pixel, indexed by route; entries of unselected routes are not written.
+    The step maps are the per-pixel view of the step controls that [VH] Sec. 3.5 inspects.
     Returns (out [b, H, W, D_sel] fp64, final [b, 4, h, S] fp64, NaN for
     unselected routes).
     """
@@ -362,9 +366,16 @@ def scan2d(x: np.ndarray, init: np.ndarray, n_heads: int, dirs: int = 15, chunk:
             if queries is not None:
                 qsel = np.asarray(queries, dtype=np.float64)[images]
                 qs = cross_scan(qsel[..., h * d:(h + 1) * d], r)
+            log = [] if step_map is not None else None
             ys, fin = srnl_chain(xs, st, C, eta_map, eta_scale, alpha_bias, eps, readout=readout,
                                  injection=injection, spectral=spectral, frozen=frozen, dgd=dgd,
-                                 counts=counts, qs=qs, mem_chunk=mem_chunk if mem_chunk > 0 else None)
+                                 counts=counts, qs=qs, mem_chunk=mem_chunk if mem_chunk > 0 else None,
+                                 log=log)
+            if log is not None:                       # token t of route r sits at pixel order[t]
+                order = route_order(H, W, r)
+                for entry in log:
+                    pix = order[entry["t"]]
+                    step_map[:, r, hi, pix // W, pix % W] = entry["step"]
             if skip is not None:                      # Y_r = reads + skip * Z_r  ([VH] App. B.5)
                 ys = ys + np.asarray(skip, dtype=np.float64)[h * d:(h + 1) * d] * xs
             if route_scales is not None:              # lambda_r * Y_r  ([VH] Eq. 26)
