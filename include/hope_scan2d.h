@@ -155,6 +155,13 @@ typedef struct {
                                 the start of the token's mem_chunk-chunk, while k, v, q, eta and
                                 alpha come from the other memories at the start of its chunk-
                                 chunk.  Runs on the fp32 chain kernel.  < 0: invalid */
+  float* step_map;           /* NULL, or device [B][4][n_heads][H][W] fp32, 4-byte aligned: the
+                                executed step eta_tilde (Sec. 2.2 Eq. 20, or the selected
+                                ablation control) of every token of a selected route, written
+                                at the token's pixel; entries of unselected routes are left
+                                untouched.  The per-pixel step maps that the Sec. 3.5 analysis
+                                of the step controls inspects.  Must not overlap out, x,
+                                init_memories, final_memories, counts or the workspace. */
 } hope_scan2d_opts_t;
 
 /* Fill *opts with the defaults listed above (no stream, no final state, no workspace). */

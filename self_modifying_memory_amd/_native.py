@@ -51,7 +51,7 @@ class hope_scan2d_opts_t(ctypes.Structure):
                 ("spectral", ctypes.c_int32), ("frozen", ctypes.c_uint32),
                 ("no_dgd", ctypes.c_int32), ("shared_init", ctypes.c_int32),
                 ("queries_dtype", ctypes.c_int32), ("queries", ctypes.c_void_p),
-                ("mem_chunk", ctypes.c_int32)]
+                ("mem_chunk", ctypes.c_int32), ("step_map", ctypes.c_void_p)]
 
 
 BLOCK_WEIGHT_FIELDS = ("cpe_w", "cpe_b", "ln1_g", "ln1_b", "w_in", "b_in", "dw_w", "dw_b", "w_q",

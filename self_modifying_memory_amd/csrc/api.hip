@@ -212,6 +212,19 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
     if (o.final_memories && overlaps(r_ws, range_of(o.final_memories, final_bytes)))
       return HOPE_ERR_INVALID_ARG;
   }
+  if (o.step_map) {
+    const size_t steps_bytes = (size_t)x->B * 4 * x->n_heads * x->H * x->W * sizeof(float);
+    const Range r_st = range_of(o.step_map, steps_bytes);
+    if (!aligned(o.step_map, 4) || overlaps(r_out, r_st) || overlaps(r_st, range_of(x->data, x_bytes)) ||
+        overlaps(r_st, range_of(init_memories, init_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+    if (o.workspace && o.workspace_bytes && overlaps(r_st, range_of(o.workspace, o.workspace_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+    if (o.final_memories && overlaps(r_st, range_of(o.final_memories, final_bytes)))
+      return HOPE_ERR_INVALID_ARG;
+    if (o.counts && overlaps(r_st, range_of(o.counts, 3 * sizeof(unsigned long long))))
+      return HOPE_ERR_INVALID_ARG;
+  }
   if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
   if (ws_need > 0 && (!o.workspace || o.workspace_bytes < ws_need)) return HOPE_ERR_WORKSPACE;
 
@@ -253,6 +266,7 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
   p.queries = o.queries;
   p.queries_bf16 = o.queries_dtype == HOPE_BF16;
   p.mem_chunk = o.mem_chunk;
+  p.steps = o.step_map;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
   hipStream_t s = o.stream;

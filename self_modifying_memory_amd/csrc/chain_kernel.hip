@@ -137,6 +137,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainParams p) {
         if (lane == 0) {
           pt[3 * D] = step;
           pt[3 * D + 1] = alpha;
+          if (p.steps)
+            p.steps[(((int64_t)b * 4 + r) * p.nh + h) * N + route_pixel(r, tb + t, H, W, N)] = step;
           n_upd += 1;
           n_inj += tg.flags & 1;
           n_spec += (tg.flags >> 1) & 1;

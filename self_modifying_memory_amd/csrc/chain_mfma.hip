@@ -195,6 +195,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   const float* const v_skip = VAR ? p.skip : nullptr;
   const float* const v_scales = VAR ? p.route_scales : nullptr;
   unsigned long long* const v_counts = VAR ? p.counts : nullptr;
+  float* const v_steps = VAR ? p.steps : nullptr;
   const void* const v_queries = VAR ? p.queries : nullptr;
   const unsigned v_frozen = VAR ? (p.frozen | (p.queries ? 4u : 0u)) : 0u;  // M_q unused with given queries
   const bool v_nodgd = VAR && p.no_dgd;
@@ -461,6 +462,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           atomicAdd(&cnt_lds[1], (unsigned)(sf.bits & 1));
           atomicAdd(&cnt_lds[2], (unsigned)((sf.bits >> 1) & 1));
         }
+        if (v_steps && c16 == 0 && live)
+          v_steps[(((int64_t)b * 4 + r) * p.nh + h) * ((int64_t)p.H * p.W) + pixs[t]] = step;
 #pragma unroll
         for (int e = 0; e < CPL; e += 2) {
           const int col = c16 * CPL + e;
@@ -886,7 +889,7 @@ bool mfma_path_supported(const ChainParams& p, int d) {
 // true when the call asks for any variant that only the VAR instantiations implement
 bool needs_variants(const ChainParams& p) {
   return p.route_scales || p.skip || p.counts || p.frozen || p.no_dgd || p.injection || p.spectral ||
-         p.queries;
+         p.queries || p.steps;
 }
 
 template <int D, bool MULTI, int NW>

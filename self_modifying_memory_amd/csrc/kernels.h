@@ -36,6 +36,8 @@ struct ChainParams {
   const void* queries;           // [B][H][W][D] queries of a fixed projection, or nullptr
   int queries_bf16;
   int mem_chunk;                 // 0: one chunk length; > 0: the working memory's own
+  float* steps;                  // [B][4][nh][H*W] executed step of each token at its pixel,
+                                 // or nullptr
 };
 
 // Raw query component c of pixel pix of image b (fixed-projection variant).

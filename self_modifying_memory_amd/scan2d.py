@@ -92,7 +92,8 @@ def _f32_device(t: torch.Tensor, name: str, numel: int) -> int:
 def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
     """VisionHOPE variants (Eq. 26 scales, App. B.5 skip, Sec. 3.5 ablations)."""
     unknown = set(v) - {"route_scales", "skip", "counts", "injection", "spectral", "frozen",
-                        "no_dgd", "shared_init", "queries", "mem_chunk", "shape", "D"}
+                        "no_dgd", "shared_init", "queries", "mem_chunk", "step_map", "n_heads",
+                        "shape", "D"}
     if unknown:
         raise ValueError(f"unknown variant options {sorted(unknown)}")
     D = v.get("D")
@@ -120,6 +121,13 @@ def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
         o.queries = q.data_ptr()
         o.queries_dtype = N.HOPE_BF16 if q.dtype == torch.bfloat16 else N.HOPE_F32
     o.mem_chunk = int(v.get("mem_chunk", 0))
+    sm = v.get("step_map")
+    if sm is not None:
+        B, H, W, _ = v["shape"]
+        _require_device(sm, "step_map")
+        if sm.dtype != torch.float32 or not sm.is_contiguous() or sm.numel() != B * 4 * v["n_heads"] * H * W:
+            raise ValueError("step_map must be a contiguous float32 tensor [B, 4, n_heads, H, W]")
+        o.step_map = sm.data_ptr()
 
 
 def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
@@ -152,7 +160,8 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         skip: torch.Tensor | None = None, counts: torch.Tensor | None = None,
                         injection: str = "soft", spectral: str = "clamp", frozen=(),
                         no_dgd: bool = False, shared_init: bool = False,
-                        queries: torch.Tensor | None = None, mem_chunk: int = 0) -> torch.Tensor:
+                        queries: torch.Tensor | None = None, mem_chunk: int = 0,
+                        step_map: torch.Tensor | None = None) -> torch.Tensor:
     """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32, or bfloat16
     when a bfloat16 ``out`` is passed: the fp32 route sum rounded once).
 
@@ -165,7 +174,9 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     spectral "clamp"/"soft"/"none"; frozen, a subset of {"kv", "dynamics", "q"}; no_dgd;
     shared_init (init_memories is then [n_heads, S]); queries, a [B, H, W, D] tensor of
     queries from a fixed outer projection (M_q is then unused); mem_chunk > 0, the working
-    memory's own chunk length (two chunk sizes; 0 = one length for all six memories).
+    memory's own chunk length (two chunk sizes; 0 = one length for all six memories);
+    step_map, a float32 [B, 4, n_heads, H, W] tensor that receives the executed step of every
+    token of a selected route at its pixel.
     scan_events: optional (begin, end) torch.cuda.Event pair that the library records
     around the scan kernel alone (already recorded once, so that they exist).
     """
@@ -184,7 +195,8 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     fm = make_fmap(x, n_heads)
     variants = dict(route_scales=route_scales, skip=skip, counts=counts, injection=injection,
                     spectral=spectral, frozen=frozen, no_dgd=no_dgd, shared_init=shared_init,
-                    queries=queries, mem_chunk=mem_chunk, shape=tuple(x.shape), D=x.shape[3])
+                    queries=queries, mem_chunk=mem_chunk, step_map=step_map, n_heads=n_heads,
+                    shape=tuple(x.shape), D=x.shape[3])
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, final_memories,
                      workspace, out.dtype, readout, variants)
     if scan_events is not None:

@@ -54,7 +54,7 @@ def test_struct_layout_matches_c():
 #include <stddef.h>
 #include "hope_scan2d.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(hope_fmap_t), sizeof(hope_scan2d_opts_t),
          offsetof(hope_fmap_t, dtype), offsetof(hope_fmap_t, n_heads),
          offsetof(hope_scan2d_opts_t, final_memories), offsetof(hope_scan2d_opts_t, workspace_bytes),
          offsetof(hope_scan2d_opts_t, eta_map), offsetof(hope_scan2d_opts_t, eta_scale),
@@ -62,7 +62,7 @@ int main(void) {
          offsetof(hope_scan2d_opts_t, out_dtype), offsetof(hope_scan2d_opts_t, scan_begin),
          offsetof(hope_scan2d_opts_t, scan_end), offsetof(hope_scan2d_opts_t, readout),
          offsetof(hope_scan2d_opts_t, reserved), offsetof(hope_scan2d_opts_t, queries),
-         offsetof(hope_scan2d_opts_t, mem_chunk));
+         offsetof(hope_scan2d_opts_t, mem_chunk), offsetof(hope_scan2d_opts_t, step_map));
   return 0;
 }
 """
@@ -81,7 +81,7 @@ int main(void) {
             O.final_memories.offset, O.workspace_bytes.offset, O.eta_map.offset, O.eta_scale.offset,
             O.eps.offset, O.init_per_image.offset, O.out_dtype.offset, O.scan_begin.offset,
             O.scan_end.offset, O.readout.offset, O.reserved.offset, O.queries.offset,
-            O.mem_chunk.offset]
+            O.mem_chunk.offset, O.step_map.offset]
     assert vals == want
 
 
@@ -144,7 +144,8 @@ def test_argument_errors(lib):
                  ("readout", 2), ("reserved", 1), ("injection", 3), ("spectral", -1),
                  ("queries", FAKE + (3 << 30) + 8),
                  ("frozen", 8), ("no_dgd", 2), ("shared_init", 2), ("counts", FAKE + (3 << 30) + 4),
-                 ("skip", FAKE + (3 << 30) + 2)]:
+                 ("skip", FAKE + (3 << 30) + 2), ("step_map", FAKE + (3 << 30) + 2),
+                 ("step_map", FAKE + (2 << 30) + 64)]:  # misaligned; overlapping out
         assert call(lib, x, o=opts(lib, **{k: v})) == N.HOPE_ERR_INVALID_ARG, k
     # final memories overlapping out, misaligned workspace
     assert call(lib, x, o=opts(lib, final_memories=FAKE + (2 << 30))) == N.HOPE_ERR_INVALID_ARG

@@ -182,3 +182,57 @@ def test_variant_sets_full_size_stage3_sampled(name):
     e_out = check_out(out.cpu().numpy(), ref_out, w.n_heads, tol, heads=heads, images=images)
     e_fin = check_final(fin.cpu().numpy(), ref_fin, d, 15, tol, heads=heads, images=images)
     print(f"  rel_inf out {e_out:.2e} final {e_fin:.2e}", flush=True)
+
+
+# The executed-step map (per token, at its pixel, by route and head) against the oracle's,
+# on both kernels, with the default controls and with the controls binding on most tokens.
+STEP_CASES = [
+    ("f32_d16", {}),
+    ("f32_d64", dict(eta_scale=50.0, alpha_bias=-3.0)),
+    ("bf16_d32", {}),
+    ("bf16_d64", {}),
+    ("bf16_d64", dict(eta_scale=50.0, alpha_bias=-3.0)),
+    ("bf16_d64", dict(injection="hard", route_scales=True)),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=[f"{s}_{'_'.join(v) or 'default'}" for s, v in STEP_CASES])
+def test_step_map_matches_oracle(case):
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    shape, var = case
+    B, H, W, D, nh, dt, chunk = SHAPES[shape]
+    print("case", shape, var, flush=True)
+    d = D // nh
+    inp = wl.draw(B, H, W, D, nh, seed=1300 + H * 31 + W, dtype=dt, live=True)
+    x, init = to_device(inp, dt)
+    extra = {k: var[k] for k in ("eta_scale", "alpha_bias", "injection") if k in var}
+    gk, ok = dict(extra), dict(extra)
+    if var.get("route_scales"):
+        lam = np.random.Generator(np.random.PCG64(5)).uniform(0.5, 1.5, (4, D)).astype(np.float32)
+        gk["route_scales"] = torch.from_numpy(lam).cuda()
+        ok["route_scales"] = lam.astype(np.float64)
+    sm = torch.full((B, 4, nh, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    out = hope_scan2d_forward(x, init, nh, 15, chunk, step_map=sm, **gk)
+    torch.cuda.synchronize()
+    ref_sm = np.full((B, 4, nh, H, W), np.nan)
+    ref_out, _ = oracle.scan2d(inp["x"], inp["init"], nh, dirs=15, chunk=chunk, step_map=ref_sm, **ok)
+    got = sm.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    e_step = float(np.max(np.abs(got - ref_sm)) / np.max(np.abs(ref_sm)))
+    e_out = check_out(out.cpu().numpy(), ref_out, nh, TOL[dt])
+    print(f"  rel_inf step {e_step:.2e} out {e_out:.2e}", flush=True)
+    assert e_step <= TOL[dt]
+
+
+def test_step_map_only_selected_routes():
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    B, H, W, D, nh, dt, chunk = SHAPES["bf16_d64"]
+    inp = wl.draw(B, H, W, D, nh, seed=1400, dtype=dt, live=True)
+    x, init = to_device(inp, dt)
+    sm = torch.full((B, 4, nh, H, W), -7.0, dtype=torch.float32, device="cuda")
+    hope_scan2d_forward(x, init, nh, 0b0110, chunk, step_map=sm)
+    got = sm.cpu().numpy()
+    assert np.all(got[:, [0, 3]] == -7.0)
+    assert np.all(got[:, [1, 2]] > 0.0)
