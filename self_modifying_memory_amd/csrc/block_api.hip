@@ -21,7 +21,7 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
 
 struct BlockLayout {
-  size_t x1, r, a, u, z, q, y, y2, h, op, total;  // byte offsets
+  size_t r, a, u, z, q, y, y2, h, op, total;  // byte offsets
 };
 
 bool sizes_ok(int32_t B, int32_t H, int32_t W, int32_t D, int32_t n_heads, int32_t ffn_dim,
@@ -58,7 +58,6 @@ BlockLayout layout(int32_t B, int32_t H, int32_t W, int32_t D, int32_t n_heads, 
     o += align256(bytes);
     return at;
   };
-  L.x1 = take(M * D * 4);
   L.r = take(M * D * 4);
   L.a = take(M * D * 2);
   L.u = take(M * D * 4);
@@ -107,7 +106,6 @@ hope_status_t hope_block_forward(const float* x, int32_t B, int32_t H, int32_t W
     return HOPE_ERR_INVALID_ARG;
 
   char* ws = static_cast<char*>(workspace);
-  float* x1 = reinterpret_cast<float*>(ws + L.x1);
   float* r = reinterpret_cast<float*>(ws + L.r);
   uint16_t* a = reinterpret_cast<uint16_t*>(ws + L.a);
   float* u = reinterpret_cast<float*>(ws + L.u);
@@ -131,8 +129,9 @@ hope_status_t hope_block_forward(const float* x, int32_t B, int32_t H, int32_t W
 
   hipError_t e;
   // x1 = x + CPE(x); a = LN1(x1); r = x1 + b_out
-  if ((e = hope::launch_dwconv_cpe(x, wt->cpe_w, wt->cpe_b, x1, B, H, W, D, stream))) return hope_status_of(e);
-  if ((e = hope::launch_layernorm(x1, wt->ln1_g, wt->ln1_b, a, wt->b_out, r, M, D, kLnEps, stream)))
+  // (one fused pass: x1 stays on chip)
+  if ((e = hope::launch_cpe_layernorm(x, wt->cpe_w, wt->cpe_b, wt->ln1_g, wt->ln1_b, wt->b_out, a, r, B, H,
+                                      W, D, kLnEps, stream)))
     return hope_status_of(e);
   // u = a W_in^T + b_in; z = u + SiLU(DW(u)); q = z W_q^T
   if ((e = hope::launch_gemm_bf16(hope::kEpiF32, a, wt->w_in, Mi, D, D, wt->b_in, nullptr, u, stream)))

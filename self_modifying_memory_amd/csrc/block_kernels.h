@@ -14,9 +14,11 @@ enum { kEpiF32 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s);
 
-// x1 = x + DW(x) (the conditional positional encoding), fp32
-hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
-                             int H, int W, int C, hipStream_t s);
+// x1 = x + DW(x) (the conditional positional encoding), a = bf16(LayerNorm(x1) g + lb),
+// r = x1 + addv, x1 itself not stored.  C % 128 == 0, C <= 1024.
+hipError_t launch_cpe_layernorm(const float* x, const float* w, const float* b, const float* g,
+                                const float* lb, const float* addv, uint16_t* a, float* r, int B,
+                                int H, int W, int C, float eps, hipStream_t s);
 // z = bf16(u + SiLU(DW(u))) (the gated depthwise branch)
 hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, uint16_t* z, int B,
                                int H, int W, int C, hipStream_t s);

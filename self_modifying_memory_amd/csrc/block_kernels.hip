@@ -256,6 +256,105 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
   }
 }
 
+// ---- CPE and LayerNorm 1 fused -----------------------------------------------------------
+// x1 = x + bias + DW(x) (the conditional positional encoding), then a = bf16(LN(x1) g + lb)
+// (biased variance) and r = x1 + addv, without x1 leaving the chip.  A workgroup of D / 2
+// threads covers two groups of four consecutive pixels of a row; thread (slot, c) holds
+// channels 4c .. 4c + 3 of its group's four pixels (the stencil of dwconv3x3_kernel).  The
+// per-pixel sums go through 32-lane halves (D / 4 is a multiple of 32) and LDS; the
+// variance is taken about the mean from the values in registers.
+__global__ __launch_bounds__(512) void cpe_layernorm_kernel(
+    const float* __restrict__ x, const float* __restrict__ wgt, const float* __restrict__ bias,
+    const float* __restrict__ g, const float* __restrict__ lb, const float* __restrict__ addv,
+    uint16_t* __restrict__ a, float* __restrict__ r, int B, int H, int W, int C, float eps) {
+  __shared__ float red[2][16][4];  // [pass][half-wave][pixel]: up to 512 threads
+  const int cq = C / 4, xq = (W + 3) / 4;
+  const int slot = threadIdx.x / cq, c = (threadIdx.x % cq) * 4;
+  const int half = threadIdx.x >> 5, halves = cq / 32;  // a slot's halves: slot * halves + i
+  const int grp = xcd_tile(blockIdx.x, gridDim.x) * 2 + slot;
+  const int total = B * H * xq;
+  const bool on = grp < total;
+  const int gq = on ? grp : total - 1;  // a missing second group computes in bounds, stores nothing
+  const int x0 = (gq % xq) * 4;
+  const int y = (gq / xq) % H;
+  const int64_t img = gq / (xq * H);
+  const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bias[c]);
+  f32x4 acc[4] = {b4, b4, b4, b4};
+#pragma unroll
+  for (int dy = 0; dy < 3; ++dy) {
+    const int yy = y + dy - 1;
+    if (yy < 0 || yy >= H) continue;
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 0) * C + c]);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 1) * C + c]);
+    const f32x4 w2 = *reinterpret_cast<const f32x4*>(&wgt[(dy * 3 + 2) * C + c]);
+    const float* row = x + ((img * H + yy) * W) * (int64_t)C + c;
+    f32x4 v[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int xx = x0 - 1 + k;
+      v[k] = (xx >= 0 && xx < W) ? *reinterpret_cast<const f32x4*>(row + (int64_t)xx * C) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[o][e] = fmaf(w2[e], v[o + 2][e], fmaf(w1[e], v[o + 1][e], fmaf(w0[e], v[o][e], acc[o][e])));
+  }
+  // residual (pixels past the row end read the last pixel: in bounds, never stored)
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    const int64_t p = (img * H + y) * W + min(x0 + o, W - 1);
+    acc[o] += *reinterpret_cast<const f32x4*>(&x[p * C + c]);
+  }
+  // per-pixel sums over the slot's channels: 32-lane halves, then LDS
+  float mean[4], rstd[4];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    float s[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dv = pass == 0 ? acc[o][e] : acc[o][e] - mean[o];
+        t = pass == 0 ? t + dv : fmaf(dv, dv, t);
+      }
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+      s[o] = t;
+    }
+    if ((threadIdx.x & 31) == 0) {
+#pragma unroll
+      for (int o = 0; o < 4; ++o) red[pass][half][o] = s[o];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      float t = 0.f;
+      for (int i = 0; i < halves; ++i) t += red[pass][slot * halves + i][o];
+      if (pass == 0) mean[o] = t / C;
+      else rstd[o] = 1.f / sqrtf(t / C + eps);
+    }
+  }
+  if (!on) return;
+  const f32x4 g4 = *reinterpret_cast<const f32x4*>(&g[c]);
+  const f32x4 lb4 = *reinterpret_cast<const f32x4*>(&lb[c]);
+  const f32x4 ad4 = *reinterpret_cast<const f32x4*>(&addv[c]);
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    if (x0 + o >= W) break;
+    const int64_t p = (img * H + y) * W + x0 + o;
+    f32x4 nv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) nv[e] = (acc[o][e] - mean[o]) * rstd[o] * g4[e] + lb4[e];
+    uint2 u;
+    u.x = pack_bf16(nv[0], nv[1]);
+    u.y = pack_bf16(nv[2], nv[3]);
+    *reinterpret_cast<uint2*>(&a[p * C + c]) = u;
+    *reinterpret_cast<f32x4*>(&r[p * C + c]) = acc[o] + ad4;
+  }
+}
+
 // ---- LayerNorm over the channels of each pixel (one wave per pixel) ------------------------
 // y = bf16((x - mean) / sqrt(var + eps) * g + b) with the biased variance; optionally
 // x_plus = x + addv (fp32).  VPL = C / 64 values per lane.
@@ -322,10 +421,14 @@ hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int 
   return hipGetLastError();
 }
 
-hipError_t launch_dwconv_cpe(const float* x, const float* w, const float* b, float* out, int B,
-                             int H, int W, int C, hipStream_t s) {
-  const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
-  dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, out, B, H, W, C, nullptr, 0, 0);
+hipError_t launch_cpe_layernorm(const float* x, const float* w, const float* b, const float* g,
+                                const float* lb, const float* addv, uint16_t* a, float* r, int B,
+                                int H, int W, int C, float eps, hipStream_t s) {
+  if (C % 128 || C > 1024) return hipErrorInvalidValue;
+  const int64_t groups = (int64_t)B * H * ((W + 3) / 4);
+  const int64_t blocks = (groups + 1) / 2;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  cpe_layernorm_kernel<<<(unsigned)blocks, C / 2, 0, s>>>(x, w, b, g, lb, addv, a, r, B, H, W, C, eps);
   return hipGetLastError();
 }
 
