@@ -7,6 +7,7 @@ bf16 inputs, fp32 state), inputs already resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX] [--no-cpu-baseline]
                   [--copy-probe-mib N] [--readout running] [--variants ...] [--backward]
+                  [--block] [--exports]
 
 --backward times the gradient pass (hope_scan2d_backward) instead, as its own JSON line.
 
@@ -307,6 +308,70 @@ def run_block(args, w: wl.Workload, dev) -> int:
     return 0
 
 
+def run_exports(args, w: wl.Workload, x_host, dev) -> int:
+    """The gather and merge exports alone (hope_debug_cross_scan: the map into the four
+    route orders; hope_debug_cross_merge: the four route sequences summed back into place,
+    fp32), one pair per step on the workload's map.  Both are pure data movement, so the
+    roofline is HBM: algorithmic bytes = the map read once and four route copies written
+    (scan), four route copies read and the fp32 map written (merge)."""
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_debug_cross_merge, hope_debug_cross_scan
+    x = x_host.to(dev)
+    es = x.element_size()
+    n = w.B * w.H * w.W * w.D
+    routes = torch.empty((4, w.B, w.H * w.W, w.D), dtype=x.dtype, device=dev)
+    out = torch.empty((w.B, w.H, w.W, w.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        hope_debug_cross_scan(x, 15, routes, stream=stream)
+        hope_debug_cross_merge(routes, w.H, w.W, 15, out, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        hope_debug_cross_scan(x, 15, routes, stream=stream)
+        e[1].record(stream)
+        hope_debug_cross_merge(routes, w.H, w.W, 15, out, stream=stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_scan = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_merge = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    b_scan = n * es * 5
+    b_merge = n * es * 4 + n * 4
+    step_s = wall / args.steps
+    rec = {
+        "metric": "scan tokens/s through the gather and merge exports (cross-scan + cross-merge)",
+        "value": w.B * w.H * w.W * 4 / step_s, "unit": "scan tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if es == 2 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D, "dirs": 4,
+                   "path": "exports"},
+        "roofline": {"bound": "hbm", "achieved": b_merge / t_merge / 1e9, "peak": 8000.0,
+                     "unit": "GB/s", "frac": b_merge / t_merge / 8e12, "traffic": None,
+                     "kernel": "cross_merge_vec_kernel", "kernel_ms": t_merge * 1e3,
+                     "cross_scan_ms": t_scan * 1e3, "cross_scan_GBps": b_scan / t_scan / 1e9,
+                     "cross_scan_frac": b_scan / t_scan / 8e12},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        xs = x_host.float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 2.0:
+            seqs = {r: oracle.cross_scan(xs, r) for r in range(4)}
+            oracle.cross_merge(seqs, w.H, w.W)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        rec["cpu_baseline"] = {"value": w.B * w.H * w.W * 4 / dt, "unit": "scan tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the whole map, {reps} passes in {dt * reps:.1f} s, numpy"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +390,8 @@ def main() -> int:
                     help="time the backward pass (gradients) instead of the forward scan")
     ap.add_argument("--block", action="store_true",
                     help="time one VisionHOPE block around the scan instead of the scan alone")
+    ap.add_argument("--exports", action="store_true",
+                    help="time the gather / merge exports (cross-scan, cross-merge) alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -351,6 +418,8 @@ def main() -> int:
         return run_backward(args, w, inp, x_host, dev)
     if args.block:
         return run_block(args, w, dev)
+    if args.exports:
+        return run_exports(args, w, x_host, dev)
     init = torch.from_numpy(inp["init"].copy()).to(dev)
     sets = []
     for _ in range(max(1, args.sets)):

@@ -51,6 +51,65 @@ __global__ void cross_scan_kernel(const T* __restrict__ x, int B, int H, int W, 
   }
 }
 
+// Vector forms: 16 bytes per thread (8 bf16 or 4 fp32 channels of one pixel), 32-bit index
+// arithmetic (the host checks the sizes); D a multiple of the vector width.
+template <typename T>
+__global__ void cross_scan_vec_kernel(const T* __restrict__ x, int B, int H, int W, int D,
+                                      Routes4 rs, int n_sel, T* __restrict__ routes) {
+  constexpr int V = 16 / sizeof(T);
+  const unsigned N = (unsigned)H * W, DV = (unsigned)D / V;
+  const unsigned total = (unsigned)n_sel * B * N * DV;
+  for (unsigned i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const unsigned cv = i % DV;
+    unsigned rem = i / DV;
+    const unsigned t = rem % N;
+    rem /= N;
+    const unsigned b = rem % B, slot = rem / B;
+    const int r = rs.r[slot];
+    unsigned tt = (r & 1) ? N - 1 - t : t;
+    const unsigned p = r < 2 ? tt : (tt % H) * W + tt / H;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + ((int64_t)b * N + p) * D + (int64_t)cv * V);
+    *reinterpret_cast<uint4*>(routes + (int64_t)i * V) = v;
+  }
+}
+
+template <bool BF16>
+__global__ void cross_merge_vec_kernel(const void* __restrict__ routes, int B, int H, int W, int D,
+                                       Routes4 rs, int n_sel, float* __restrict__ out) {
+  const unsigned N = (unsigned)H * W, DQ = (unsigned)D / 4;
+  const unsigned total = (unsigned)B * N * DQ;
+  const int64_t per_route = (int64_t)B * N * D;
+  for (unsigned i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const unsigned cq = i % DQ;
+    const unsigned rem = i / DQ;
+    const unsigned p = rem % N, b = rem / N;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_sel; ++s) {
+      const int r = rs.r[s];
+      unsigned t = r < 2 ? p : (p % W) * H + p / W;
+      if (r & 1) t = N - 1 - t;
+      const int64_t idx = s * per_route + ((int64_t)b * N + t) * D + (int64_t)cq * 4;
+      float4 v;
+      if (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(routes) + idx);
+        v = float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
+      } else {
+        v = *reinterpret_cast<const float4*>(static_cast<const float*>(routes) + idx);
+      }
+      if (s == 0) {
+        acc = v;
+      } else {
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    }
+    *reinterpret_cast<float4*>(out + (int64_t)i * 4) = acc;
+  }
+}
+
 template <bool BF16>
 __global__ void cross_merge_kernel(const void* __restrict__ routes, int B, int H, int W, int D,
                                    Routes4 rs, int n_sel, float* __restrict__ out) {
@@ -184,6 +243,19 @@ hipError_t launch_cross_scan(const void* x, int elem_bytes, int B, int H, int W,
   Routes4 rs{{0, 0, 0, 0}};
   for (int i = 0; i < n_sel; ++i) rs.r[i] = route_of_slot[i];
   const int64_t total = (int64_t)n_sel * B * H * W * D;
+  const int vec = 16 / elem_bytes;
+  if (D % vec == 0 && total / vec < ((int64_t)1 << 31) && total < ((int64_t)1 << 40)) {
+    const dim3 grid(grid_for(total / vec, 256)), block(256);
+    if (elem_bytes == 2)
+      hipLaunchKernelGGL(cross_scan_vec_kernel<uint16_t>, grid, block, 0, stream,
+                         static_cast<const uint16_t*>(x), B, H, W, D, rs, n_sel,
+                         static_cast<uint16_t*>(routes));
+    else
+      hipLaunchKernelGGL(cross_scan_vec_kernel<uint32_t>, grid, block, 0, stream,
+                         static_cast<const uint32_t*>(x), B, H, W, D, rs, n_sel,
+                         static_cast<uint32_t*>(routes));
+    return hipGetLastError();
+  }
   const dim3 grid(grid_for(total, 256)), block(256);
   if (elem_bytes == 2) {
     hipLaunchKernelGGL(cross_scan_kernel<uint16_t>, grid, block, 0, stream,
@@ -203,6 +275,16 @@ hipError_t launch_cross_merge(const void* routes, int bf16, int B, int H, int W,
   Routes4 rs{{0, 0, 0, 0}};
   for (int i = 0; i < n_sel; ++i) rs.r[i] = route_of_slot[i];
   const int64_t total = (int64_t)B * H * W * D;
+  if (D % 4 == 0 && total / 4 < ((int64_t)1 << 31)) {
+    const dim3 grid(grid_for(total / 4, 256)), block(256);
+    if (bf16)
+      hipLaunchKernelGGL(cross_merge_vec_kernel<true>, grid, block, 0, stream, routes, B, H, W, D,
+                         rs, n_sel, out);
+    else
+      hipLaunchKernelGGL(cross_merge_vec_kernel<false>, grid, block, 0, stream, routes, B, H, W, D,
+                         rs, n_sel, out);
+    return hipGetLastError();
+  }
   const dim3 grid(grid_for(total, 256)), block(256);
   if (bf16) {
     hipLaunchKernelGGL(cross_merge_kernel<true>, grid, block, 0, stream, routes, B, H, W, D, rs,
