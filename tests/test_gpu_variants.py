@@ -236,3 +236,27 @@ def test_step_map_only_selected_routes():
     got = sm.cpu().numpy()
     assert np.all(got[:, [0, 3]] == -7.0)
     assert np.all(got[:, [1, 2]] > 0.0)
+
+
+@pytest.mark.parametrize("shape,kw", [("bf16_d64", dict(readout="running")),
+                                      ("bf16_d32", dict(readout="running")),
+                                      ("f32_d64", dict(mem_chunk=2))],
+                         ids=["bf16_d64_running", "bf16_d32_running", "f32_d64_mem_chunk2"])
+def test_step_map_with_running_readout_and_two_chunk_sizes(shape, kw):
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_forward
+    B, H, W, D, nh, dt, chunk = SHAPES[shape]
+    print("case", shape, kw, flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=1500 + H * 31 + W, dtype=dt, live=True)
+    x, init = to_device(inp, dt)
+    sm = torch.full((B, 4, nh, H, W), float("nan"), dtype=torch.float32, device="cuda")
+    out = hope_scan2d_forward(x, init, nh, 15, chunk, step_map=sm, **kw)
+    torch.cuda.synchronize()
+    ref_sm = np.full((B, 4, nh, H, W), np.nan)
+    ref_out, _ = oracle.scan2d(inp["x"], inp["init"], nh, dirs=15, chunk=chunk, step_map=ref_sm, **kw)
+    got = sm.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    e_step = float(np.max(np.abs(got - ref_sm)) / np.max(np.abs(ref_sm)))
+    e_out = check_out(out.cpu().numpy(), ref_out, nh, TOL[dt])
+    print(f"  rel_inf step {e_step:.2e} out {e_out:.2e}", flush=True)
+    assert e_step <= TOL[dt]
