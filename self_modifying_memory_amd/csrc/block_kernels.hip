@@ -246,7 +246,9 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
       f32x4 a = acc[o];
       if (SILU) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = a[e] / (1.f + expf(-a[e]));
+        for (int e = 0; e < 4; ++e)  // SiLU; hardware exp2 and reciprocal (about 1 ulp each, the
+                                     // result is rounded to bf16)
+          a[e] = a[e] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-a[e] * 1.4426950408889634f));
       }
       const int64_t p = (img * H + y) * W + x0 + o;
       f32x4 r = load4(&res[p * C + c]);
