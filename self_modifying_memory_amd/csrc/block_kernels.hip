@@ -252,7 +252,13 @@ __global__ __launch_bounds__(256) void dwconv3x3_kernel(const SrcT* __restrict__
       }
       const int64_t p = (img * H + y) * W + x0 + o;
       f32x4 r = load4(&res[p * C + c]);
-      for (int k = 0; k < n_planes; ++k) r += load4(&planes[k * plane_stride + p * C + c]);
+      if (n_planes == 3) {  // the four-route operator: the three loads issued together
+        const float* pp = &planes[p * C + c];
+        const f32x4 p0 = load4(pp), p1 = load4(pp + plane_stride), p2 = load4(pp + 2 * plane_stride);
+        r = ((r + p0) + p1) + p2;
+      } else {
+        for (int k = 0; k < n_planes; ++k) r += load4(&planes[k * plane_stride + p * C + c]);
+      }
       store4(&out[p * C + c], r + a);
     }
   }
