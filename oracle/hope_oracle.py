@@ -233,7 +233,7 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
                control: bool = True, log: list | None = None, readout: str = "boundary",
                injection: str = "soft", spectral: str = "clamp", frozen=(), dgd: bool = True,
                counts: dict | None = None, qs: np.ndarray | None = None,
-               mem_chunk: int | None = None):
+               mem_chunk: int | None = None, norm_log: list | None = None):
     """Run chains over ordered tokens.
 
     xs    : [n, N, d] tokens in route order
@@ -258,6 +258,8 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
     form and its self-generated targets) is refreshed at multiples of mem_chunk, the other
     five memories' (which generate k, v, q, eta, alpha) at multiples of chunk.  None or
     chunk: one chunk size.
+    norm_log (optional list): after each chunk, {"end": e, m: ||M_m||_F per chain for every
+    memory m} is appended (the per-chunk memory norms).
     Returns (ys [n, N, d], final state dict).
     """
     for m in frozen:
@@ -301,6 +303,11 @@ def srnl_chain(xs: np.ndarray, state: dict, chunk: int, eta_map: str = "sigmoid"
                 vhat = _matvec(Mb[m], v)                      # self-generated target, Eq. 16
                 g = _matvec(Mb[m], k) - vhat                  # output-space signal, Eq. 16
                 M[m] = retained_dgd(M[m], k, g, step, alpha, dgd)  # Eq. 13
+        if norm_log is not None:
+            entry = {"end": min(s + chunk, N)}
+            for m in MEMORIES:
+                entry[m] = np.sqrt(np.sum(M[m] ** 2, axis=(1, 2)))
+            norm_log.append(entry)
     return ys, M
 
 

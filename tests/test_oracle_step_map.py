@@ -70,3 +70,23 @@ def test_step_map_leaves_unselected_routes():
     sm = np.full((1, 4, NH, H, W), np.nan)
     oracle.scan2d(inp["x"], inp["init"], NH, dirs=0b0101, step_map=sm)
     assert np.all(np.isfinite(sm[:, [0, 2]])) and np.all(np.isnan(sm[:, [1, 3]]))
+
+
+def test_norm_log_pure_decay_keeps_norm_ratios():
+    # eta = 0 (eta_scale 0): every memory only decays, M <- alpha_t M, by the same factor per
+    # token ([VH] Eq. 13 with a zero step), so the per-chunk Frobenius norms of any two
+    # memories keep their initial ratio, and each chunk's norms shrink
+    inp = wl.draw(2, H, W, D, NH, seed=47, live=True)
+    d0 = D // NH
+    xs = oracle.cross_scan(inp["x"][..., :d0].astype(np.float64), 0)
+    st = oracle.unflatten_state(np.broadcast_to(inp["init"][0, 0], (2, 4 * d0 * d0 + 2 * d0)), d0)
+    log = []
+    oracle.srnl_chain(xs, st, W, eta_scale=0.0, norm_log=log)
+    assert [e["end"] for e in log] == [W * (i + 1) for i in range(H)]
+    n0 = {m: np.sqrt(np.sum(st[m] ** 2, axis=(1, 2))) for m in oracle.MEMORIES}
+    prev = n0["k"]
+    for e in log:
+        for m in oracle.MEMORIES:
+            np.testing.assert_allclose(e[m] / e["k"], n0[m] / n0["k"], rtol=1e-12)
+        assert np.all(e["k"] < prev)
+        prev = e["k"]
