@@ -47,6 +47,7 @@ CASES = [
     (1, 5, 4, 128, 8, 512, 0),     # d = 16
     (1, 6, 6, 256, 4, 1024, 0),    # d = 64, wider
     (3, 9, 10, 128, 2, 256, 5),    # d = 64, 270 pixels: three GEMM row tiles, the last ragged
+    (1, 4, 6, 512, 8, 512, 0),     # d = 64, D = 512: eight values per lane in the LayerNorm
 ]
 
 
