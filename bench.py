@@ -52,7 +52,7 @@ PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
 PEAK_FP32 = 157.3e12    # fp32 matrix / vector, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_traffic.json")
-KERNEL_SOURCES = ["chain_mfma.hip", "device_common.h", "kernels.h"]
+KERNEL_SOURCES = ["chain_mfma.hip", "chain_kernel.hip", "device_common.h", "kernels.h"]
 METRIC = wl_metric = "scan tokens/s (positions×dirs) for 4-dir Hope memory scan; % MFMA/HBM peak"
 
 
@@ -72,18 +72,25 @@ def work_per_token(d: int, C: int, readout: str = "boundary") -> tuple[float, fl
 
 def roofline_numbers(w: wl.Workload, n_dirs: int = 4, readout: str = "boundary") -> dict:
     d = w.d
-    C = w.W  # square maps: row and column chunks are equal
-    bf16, fp32 = work_per_token(d, C, readout)
     units = w.scan_tokens(n_dirs) * w.n_heads
-    f_bf16 = 2 * bf16 * units
-    f_fp32 = 2 * fp32 * units
+    f_bf16 = f_fp32 = 0.0
+    for C in (w.chunk or w.W, w.chunk or w.H):  # row routes, column routes: half the units each
+        bf16, fp32 = work_per_token(d, min(C, w.H * w.W), readout)
+        f_bf16 += bf16 * units  # 2 flops per MAC over half the units
+        f_fp32 += fp32 * units
     t_compute = f_bf16 / PEAK_BF16 + f_fp32 / PEAK_FP32
     x_bytes = w.B * w.H * w.W * w.D * (2 if w.dtype == "bf16" else 4)
     out_bytes = w.B * w.H * w.W * w.D * 4
     init_bytes = 4 * w.n_heads * w.state_size * 4
     hbm = x_bytes + out_bytes + init_bytes
+    # the same work at the bf16 matrix peak as the MFMA kernels execute it: the projections
+    # as two bf16 products (x is exact bf16, the state split hi + lo), the readout
+    # (d^2 of the bf16-class MACs) and every fp32-class product as three (hi*hi + hi*lo + lo*hi)
+    f_read = 2.0 * d * d * units
+    t_exec = (2 * (f_bf16 - f_read) + 3 * f_read + 3 * f_fp32) / PEAK_BF16
     return {"flops": f_bf16 + f_fp32, "flops_bf16": f_bf16, "flops_fp32": f_fp32,
-            "t_compute": t_compute, "hbm_bytes": hbm, "t_hbm": hbm / PEAK_HBM}
+            "t_compute": t_compute, "t_as_executed": t_exec, "hbm_bytes": hbm,
+            "t_hbm": hbm / PEAK_HBM}
 
 
 def kernel_source_hash() -> str:
@@ -97,35 +104,61 @@ def kernel_source_hash() -> str:
 
 def recorded_traffic(w: wl.Workload):
     """HBM bytes per scan launch from the counter record, or None when the record is
-    missing, is for another workload, or predates the current kernel sources."""
+    missing, has no entry for this workload, or predates the current kernel sources."""
     try:
         with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f)["records"].get(w.name)
+    except (OSError, ValueError, KeyError, AttributeError):
         return None
-    if rec.get("workload") != w.name or rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return float(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str = "boundary") -> dict:
-    """Time the fp64 oracle, as it stands, on a bounded sample of the same workload."""
+HOST_WORKERS_MAX = 16  # the GPU box's CPU share for one GPU
+
+
+def _oracle_part(args) -> float:
+    """One host worker of the CPU baseline: the oracle, as it stands, on a slice of
+    (image, head) chains; returns its own busy time."""
+    x, init, n_heads, heads, readout, chunk = args
     import oracle
     from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
-        images = [0]
         t0 = time.perf_counter()
-        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images, readout=readout)
-        t1 = time.perf_counter() - t0
-        n_img = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
-        images = list(range(n_img))
+        oracle.scan2d(x, init, n_heads, heads=heads, readout=readout, chunk=chunk)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str = "boundary") -> dict:
+    """Time the fp64 oracle, as it stands, on a bounded sample of the same workload, split
+    over the host cores by (image, head) with one process and one BLAS thread per core."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), HOST_WORKERS_MAX))
+    # probe: one (image, head) chain set on one core
+    probe = _oracle_part((inp["x"][:1], inp["init"], w.n_heads, [0], readout, w.chunk))
+    per_core = max(1, int(budget_s / max(probe, 1e-3)))
+    units = [(b, h) for b in range(w.B) for h in range(w.n_heads)][:per_core * cores]
+    jobs = []
+    for c in range(cores):
+        mine = units[c::cores]
+        if not mine:
+            continue
+        imgs = sorted({b for b, _ in mine})
+        for b in imgs:  # one job per (image, its heads on this core)
+            hs = [h for bb, h in mine if bb == b]
+            jobs.append((c, (inp["x"][b:b + 1], inp["init"], w.n_heads, hs, readout, w.chunk)))
+    ctx = mp.get_context("spawn")  # fresh interpreters: nothing of this process's GPU state
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_part, [(inp["x"][:1, :2, :2], inp["init"], w.n_heads, [0], readout, 0)] * cores)
         t0 = time.perf_counter()
-        oracle.scan2d(inp["x"], inp["init"], w.n_heads, images=images, readout=readout)
+        pool.map(_oracle_part, [j for _, j in jobs], chunksize=1)
         dt = time.perf_counter() - t0
-    toks = n_img * w.H * w.W * 4
-    return {"value": toks / dt, "unit": "scan tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_img} of {w.B} images, all {w.n_heads} heads and 4 routes "
-                      f"({toks} scan tokens) in {dt:.1f} s, fp64 numpy, 1 BLAS thread"}
+    toks = len(units) * w.H * w.W * 4 / w.n_heads
+    return {"value": toks / dt, "unit": "scan tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(units)} of {w.B * w.n_heads} (image, head) chain sets, 4 routes each "
+                      f"({toks:.0f} scan-token equivalents) in {dt:.1f} s wall on {cores} worker "
+                      f"processes (fp64 numpy, 1 BLAS thread each)"}
 
 
 def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: float = 15.0) -> dict:
@@ -228,16 +261,22 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
 def run_block(args, w: wl.Workload, dev) -> int:
     """One VisionHOPE block (hope_block_forward: positional encoding, LayerNorms, the five
     projections, the depthwise branches, the operator and the FFN) on the workload's shape
-    with synthetic weights, as the timed step.  Roofline: the projections' flops at the
-    bf16 matrix peak plus the operator's (its bf16 part at the bf16 peak, its fp32 part at
-    the fp32 peak); the depthwise and LayerNorm passes are left out of the count."""
+    with synthetic weights, as the timed step, in the pages' evaluated form (VisionHOPE
+    App. C.3: inner width D_m = D / 2, D / 32 heads of 16; --block-inner full keeps D_m = D
+    with the workload's heads).  Roofline: the projections' flops at the bf16 matrix peak
+    plus the operator's at its own kernel's bound; the depthwise and LayerNorm passes are
+    left out of the count."""
+    import dataclasses
     import torch
     from self_modifying_memory_amd import _native as N
     from self_modifying_memory_amd.block import hope_block_forward, hope_block_workspace_size
+    from self_modifying_memory_amd.scan2d import hope_scan2d_kernel_name
     F = 4 * w.D
+    Dm, nh = (w.D, w.n_heads) if args.block_inner == "full" else (w.D // 2, w.D // 32)
+    op = dataclasses.replace(w, D=Dm, n_heads=nh)
     rng = np.random.Generator(np.random.PCG64(31))
     x_np = rng.standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)
-    wts = wl.draw_block_weights(w.D, w.n_heads, F, seed=32)
+    wts = wl.draw_block_weights(w.D, nh, F, seed=32, D_m=Dm)
     names = {"init_memories": "init", "route_scales": "scales"}
     wd = {}
     for name in N.BLOCK_WEIGHT_FIELDS:
@@ -248,12 +287,16 @@ def run_block(args, w: wl.Workload, dev) -> int:
             wd[name] = torch.from_numpy(np.ascontiguousarray(wts[key], dtype=np.float32)).to(dev)
     x = torch.from_numpy(x_np).to(dev)
     out = torch.empty_like(x)
-    ws = torch.empty(hope_block_workspace_size(w.B, w.H, w.W, w.D, w.n_heads, F, w.chunk),
+    ws = torch.empty(hope_block_workspace_size(w.B, w.H, w.W, w.D, nh, F, w.chunk, Dm),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    zq = torch.empty((w.B, w.H, w.W, Dm), dtype=torch.bfloat16, device=dev)
+    kname = hope_scan2d_kernel_name(zq, nh, 15, w.chunk, queries=torch.empty_like(zq, dtype=torch.float32),
+                                    skip=wd["skip"], route_scales=wd["route_scales"])
+    del zq
 
     def step():
-        hope_block_forward(x, wd, w.n_heads, F, w.chunk, out=out, workspace=ws, stream=stream)
+        hope_block_forward(x, wd, nh, F, w.chunk, D_m=Dm, out=out, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -275,22 +318,27 @@ def run_block(args, w: wl.Workload, dev) -> int:
     call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     c_avg = float(np.mean(call_ms)) * 1e-3
     M = w.B * w.H * w.W
-    f_gemm = 2.0 * M * (3 * w.D * w.D + 2 * w.D * F)
-    roof = roofline_numbers(w)
-    t_roof = (f_gemm + roof["flops_bf16"]) / PEAK_BF16 + roof["flops_fp32"] / PEAK_FP32
+    f_gemm = 2.0 * M * (2 * w.D * Dm + Dm * Dm + 2 * w.D * F)
+    roof = roofline_numbers(op)
+    on_mfma = kname != "chain_kernel"
+    t_op = roof["t_compute"] if on_mfma else roof["flops"] / PEAK_FP32
+    t_roof = f_gemm / PEAK_BF16 + t_op
     rec = {
         "metric": "block pixels/s: one VisionHOPE block (Eq. 27, App. B.5) per pixel of the map",
         "value": M * args.steps / wall, "unit": "pixels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name + "_block", "B": w.B, "H": w.H, "W": w.W, "D": w.D,
-                   "n_heads": w.n_heads, "ffn_dim": F, "chunk": w.chunk or w.W, "dirs": 4},
+                   "D_m": Dm, "n_heads": nh, "d": Dm // nh, "ffn_dim": F,
+                   "chunk": w.chunk or w.W, "dirs": 4},
         "roofline": {"bound": "mfma", "achieved": (f_gemm + roof["flops"]) / c_avg / 1e12,
                      "peak": (f_gemm + roof["flops"]) / t_roof / 1e12, "unit": "TFLOP/s",
                      "frac": t_roof / c_avg, "traffic": None,
-                     "kernel": "whole block call (blended peaks: projections and the operator's "
-                               "bf16 part at 2.5 PFLOP/s, its fp32 part at 157.3 TFLOP/s)",
-                     "kernel_ms": c_avg * 1e3, "t_roof_ms": t_roof * 1e3,
+                     "kernel": "whole block call (projections at the bf16 peak, 2.5 PFLOP/s; the "
+                               f"operator ({kname}) at its own bound)",
+                     "operator_kernel": kname,
+                     "kernel_ms": c_avg * 1e3, "kernel_ms_median": float(np.median(call_ms)),
+                     "t_roof_ms": t_roof * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(call_ms, 10)),
                                            float(np.percentile(call_ms, 90))]},
     }
@@ -298,7 +346,7 @@ def run_block(args, w: wl.Workload, dev) -> int:
         from oracle import hope_block as hbk
         ow = {k: v.astype(np.float64) for k, v in wts.items() if not k.endswith("_bits")}
         t0 = time.perf_counter()
-        hbk.block_forward(x_np[:1], ow, w.n_heads, chunk=w.chunk)
+        hbk.block_forward(x_np[:1], ow, nh, chunk=w.chunk)
         dt = time.perf_counter() - t0
         rec["cpu_baseline"] = {"value": w.H * w.W / dt, "unit": "pixels/s", "cores": 1,
                                "kind": "oracle",
@@ -390,6 +438,9 @@ def main() -> int:
                     help="time the backward pass (gradients) instead of the forward scan")
     ap.add_argument("--block", action="store_true",
                     help="time one VisionHOPE block around the scan instead of the scan alone")
+    ap.add_argument("--block-inner", choices=["half", "full"], default="half",
+                    help="the block's inner width: D/2 with heads of 16 (the pages' evaluated "
+                         "models) or D with the workload's heads")
     ap.add_argument("--exports", action="store_true",
                     help="time the gather / merge exports (cross-scan, cross-merge) alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -402,7 +453,8 @@ def main() -> int:
         return 2
 
     import torch
-    from self_modifying_memory_amd.scan2d import alloc_workspace, hope_scan2d_forward
+    from self_modifying_memory_amd.scan2d import (alloc_workspace, hope_scan2d_forward,
+                                                  hope_scan2d_kernel_name)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -498,8 +550,14 @@ def main() -> int:
 
     tokens = w.scan_tokens(4)
     roof = roofline_numbers(w, readout=args.readout)
+    kname = hope_scan2d_kernel_name(sets[0][0], w.n_heads, 15, w.chunk, readout=args.readout, **vkw)
+    on_mfma = kname != "chain_kernel"
     achieved = roof["flops"] / k_avg
-    peak = roof["flops"] / roof["t_compute"]
+    # the fp32 VALU kernel runs every product in fp32 on the vector ALUs (157.3 TFLOP/s);
+    # the MFMA kernels are held to the blend of the two classes' peaks
+    t_roof = roof["t_compute"] if on_mfma else roof["flops"] / PEAK_FP32
+    peak = roof["flops"] / t_roof
+    k_med = float(np.median(kernel_ms)) * 1e-3
     rec = {
         "metric": METRIC,
         "value": tokens * args.steps / wall,
@@ -511,18 +569,26 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # inputs bf16, state and accumulation fp32; on the MFMA kernels the fp32 state's
+        # products run as three bf16 products of a hi/lo split (about 2^-16 relative)
+        "dtype": "bf16-in/f32-state(bf16x3)" if on_mfma else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
                    "state_dtype": "f32", "readout": args.readout, "variants": var},
-        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
+        "roofline": {"bound": "mfma" if on_mfma else "alu", "achieved": achieved / 1e12,
+                     "peak": peak / 1e12, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": recorded_traffic(w) if args.readout == "boundary" and not var else None,
-                     "kernel": "chain_mfma_kernel", "kernel_ms": k_avg * 1e3,
+                     "kernel": kname, "kernel_ms": k_avg * 1e3, "kernel_ms_median": k_med * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)),
                                            float(np.percentile(kernel_ms, 90))],
+                     "calls_timed": len(kernel_ms),
+                     "t_roof_ms": t_roof * 1e3,
+                     # the same flops at the bf16 matrix peak, counted as executed (hi/lo
+                     # split products): the bound of this kernel's own instruction mix
+                     "frac_as_executed": roof["t_as_executed"] / k_avg if on_mfma else None,
                      "call_ms": float(np.mean(call_ms)),
+                     "call_ms_median": float(np.median(call_ms)),
                      "hbm_algorithmic_bytes": roof["hbm_bytes"],
                      "hbm_frac": roof["hbm_bytes"] / k_avg / PEAK_HBM},
     }

@@ -246,6 +246,13 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
 size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                            const hope_scan2d_opts_t* opts);
 
+/* Name of the scan kernel hope_scan2d_forward launches for these arguments (opts NULL =
+ * defaults; only the shape, dtype, routes, chunk and option flags are read, no pointer is
+ * dereferenced), e.g. "chain_mfma_kernel"; "" for arguments it would reject.  A static
+ * string.  For profiling: it names the kernel a trace of the call shows. */
+const char* hope_scan2d_kernel_name(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                    const hope_scan2d_opts_t* opts);
+
 /* Static, human-readable name of a status code. */
 const char* hope_status_string(hope_status_t status);
 

@@ -18,10 +18,12 @@ stochastic depth):
   x'  = x1 + y W_out^T + b_out                output projection D_m -> D, residual
   out = x' + GELU(LN2(x') W_1^T + b_1) W_2^T + b_2   the FFN branch (expansion 4), residual
 
-Readings where the pages leave the form open (listed in the design notes as R21-R26):
-D_m = D; all depthwise convolutions are 3x3 with zero padding and a bias; the gated branch
-is u + SiLU(DW(u)); LayerNorm eps 1e-5 with an affine map; GELU is the erf form; W_q has
-no bias.  Linear weights are stored [out, in] (y = x W^T + b); depthwise weights [3][3][C].
+The inner width D_m is whatever the weights give (w_in is [D_m, D]); the pages' evaluated
+models use D_m = D / 2 with heads of 16 (App. C.3).  Readings where the pages leave the form
+open (listed in the design notes as R22-R26): all depthwise convolutions are 3x3 with zero
+padding and a bias; the gated branch is u + SiLU(DW(u)); LayerNorm eps 1e-5 with an affine
+map; GELU is the erf form; W_q has no bias.  Linear weights are stored [out, in]
+(y = x W^T + b); depthwise weights [3][3][C].
 
 Pins: tests/test_oracle_block_pins.py.
 """

@@ -90,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hope_scan2d_backward_workspace_size.argtypes = [P(hope_fmap_t), ctypes.c_uint32, ctypes.c_int32,
                                                         P(hope_scan2d_opts_t)]
     lib.hope_scan2d_backward_workspace_size.restype = ctypes.c_size_t
+    lib.hope_scan2d_kernel_name.argtypes = [P(hope_fmap_t), ctypes.c_uint32, ctypes.c_int32,
+                                            P(hope_scan2d_opts_t)]
+    lib.hope_scan2d_kernel_name.restype = ctypes.c_char_p
     lib.hope_status_string.argtypes = [ctypes.c_int]
     lib.hope_status_string.restype = ctypes.c_char_p
     lib.hope_last_hip_error.argtypes = []
@@ -101,9 +104,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
     lib.hope_debug_cross_merge.restype = ctypes.c_int
-    lib.hope_block_workspace_size.argtypes = [ctypes.c_int32] * 7
+    lib.hope_block_workspace_size.argtypes = [ctypes.c_int32] * 8
     lib.hope_block_workspace_size.restype = ctypes.c_size_t
-    lib.hope_block_forward.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 7 + [
+    lib.hope_block_forward.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 8 + [
         P(hope_block_weights_t), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.hope_block_forward.restype = ctypes.c_int
     _lib = lib

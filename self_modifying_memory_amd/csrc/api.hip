@@ -153,6 +153,26 @@ bool backward_opts_supported(const hope_scan2d_opts_t& o) {
 
 namespace hope {
 
+ScanPath select_scan_path(const ChainParams& p, int d) {
+  return mfma_path_supported(p, d) ? kPathMfma : kPathChain;
+}
+
+const char* scan_path_kernel(ScanPath path) {
+  switch (path) {
+    case kPathMfma: return "chain_mfma_kernel";
+    case kPathChain: return "chain_kernel";
+  }
+  return "";
+}
+
+hipError_t launch_scan(const ChainParams& p, int d, hipStream_t s) {
+  switch (select_scan_path(p, d)) {
+    case kPathMfma: return launch_chain_mfma(p, d, s);
+    case kPathChain: return launch_chain(p, d, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uint32_t dirs,
                            int32_t chunk, void* out, const hope_scan2d_opts_t* opts,
                            RoutePlanes* defer) {
@@ -271,8 +291,7 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
 
   hipStream_t s = o.stream;
   if (o.scan_begin && (st = hip_status(hipEventRecord(o.scan_begin, s))) != HOPE_OK) return st;
-  st = hip_status(hope::mfma_path_supported(p, d) ? hope::launch_chain_mfma(p, d, s)
-                                                  : hope::launch_chain(p, d, s));
+  st = hip_status(launch_scan(p, d, s));
   if (st == HOPE_OK && o.scan_end) st = hip_status(hipEventRecord(o.scan_end, s));
   if (st != HOPE_OK) return st;
   if (out_bf16)
@@ -394,6 +413,43 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
   st = hip_status(hope::launch_chain_backward(p, d, grad_init, s));
   if (st != HOPE_OK || p.n_sel == 1) return st;
   return hip_status(hope::launch_plane_sum(grad_x, p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
+}
+
+const char* hope_scan2d_kernel_name(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
+                                    const hope_scan2d_opts_t* opts) {
+  hope_scan2d_opts_t o;
+  if (opts) {
+    o = *opts;
+  } else {
+    hope_scan2d_default_opts(&o);
+  }
+  if (check_fmap(x) != HOPE_OK || check_opts(&o) != HOPE_OK) return "";
+  if (dirs == 0 || dirs > 15 || chunk < 0) return "";
+  const int d = x->D / x->n_heads;
+  if (d != 16 && d != 32 && d != 64) return "";
+  hope::ChainParams p;
+  memset(&p, 0, sizeof(p));
+  p.x_bf16 = x->dtype == HOPE_BF16;
+  p.B = x->B;
+  p.H = x->H;
+  p.W = x->W;
+  p.D = x->D;
+  p.nh = x->n_heads;
+  p.n_sel = slots_of(dirs, p.route_of_slot);
+  p.chunk = chunk;
+  p.readout = o.readout;
+  p.route_scales = o.route_scales;
+  p.skip = o.skip;
+  p.counts = o.counts;
+  p.injection = o.injection;
+  p.spectral = o.spectral;
+  p.frozen = o.frozen;
+  p.no_dgd = o.no_dgd;
+  p.shared_init = o.shared_init;
+  p.queries = o.queries;
+  p.mem_chunk = o.mem_chunk;
+  p.steps = o.step_map;
+  return hope::scan_path_kernel(hope::select_scan_path(p, d));
 }
 
 const char* hope_status_string(hope_status_t status) {

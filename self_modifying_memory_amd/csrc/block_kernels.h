@@ -10,7 +10,8 @@ enum { kEpiF32 = 0, kEpiGeluBf16 = 1, kEpiResidualF32 = 2 };
 
 // out[m][n] = epi(sum_k A[m][k] Wt[n][k] + bias[n]): kEpiF32 -> fp32 out; kEpiGeluBf16 ->
 // bf16 GELU(.) (erf form, erf by Abramowitz-Stegun 7.1.26); kEpiResidualF32 -> fp32 res[m][n] + (.) (res may equal out).
-// bias may be null.  N % 128 == 0, K % 64 == 0; A, Wt, bias, res, out 16-byte aligned.
+// bias may be null.  N % 4 == 0, K % 8 == 0 (ragged tiles); A, Wt, bias, res, out 16-byte
+// aligned.
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s);
 
@@ -28,8 +29,10 @@ hipError_t launch_dwconv_gated(const float* u, const float* w, const float* b, u
 hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* planes,
                              int64_t plane_stride, int n_planes, const float* w, const float* b,
                              uint16_t* out, int B, int H, int W, int C, hipStream_t s);
-// y = bf16(LayerNorm(x) g + b); if x_plus: x_plus = x + addv.  C % 64 == 0, C / 64 in
-// {1, 2, 3, 4, 6, 8, 12, 16}.
+// x1 = x + bias + DW(x) (the conditional positional encoding alone, fp32), any C % 4 == 0.
+hipError_t launch_cpe(const float* x, const float* w, const float* b, float* x1, int B, int H, int W,
+                      int C, hipStream_t s);
+// y = bf16(LayerNorm(x) g + b); if x_plus: x_plus = x + addv (x_plus may equal x).  C <= 1024.
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, uint16_t* y,
                             const float* addv, float* x_plus, int64_t M, int C, float eps,
                             hipStream_t s);

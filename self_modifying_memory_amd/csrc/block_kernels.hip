@@ -49,97 +49,107 @@ __device__ __forceinline__ int xcd_tile(int bid, int G) {
 
 // ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
 // Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
-// K in steps of 32 (one MFMA k-step) through double-buffered LDS (rows padded to 40 bf16:
-// 40 KB a workgroup, so that four share a CU and hide each other's barriers), one barrier a
-// step.  The MFMA computes the transposed tile (weights as its A operand), so that a lane's
-// four results are four consecutive output columns of one row: lane (r16, q4) feeds row r16
-// of the weight tile and row r16 of the activation tile with the 8 consecutive k values
-// 8 q4 .. 8 q4 + 7 (the same k order on both sides), and holds
-// C[m = 16 i + r16][n = 16 j + 4 q4 + v].
-// Requires N % 128 == 0 and K % 64 == 0; rows past M are read clamped and not written.
-constexpr int kBM = 128, kBN = 128, kBK = 32, kLDK = kBK + 8;
+// K in steps of 32 (one MFMA k-step) through double-buffered LDS, one barrier a step (32 KB a
+// workgroup, so that four share a CU and hide each other's barriers).  The MFMA computes the
+// transposed tile (weights as its A operand), so that a lane's four results are four
+// consecutive output columns of one row: lane (r16, q4) feeds row r16 of the weight tile and
+// row r16 of the activation tile with the 8 consecutive k values 8 q4 .. 8 q4 + 7 (the same k
+// order on both sides), and holds C[m = 16 i + r16][n = 16 j + 4 q4 + v].
+//
+// LDS rows are the 64 bytes of one row's 32-deep k-slice, unpadded, as four 16-byte chunks;
+// chunk c of row r sits at chunk c ^ swz(r), swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1).  A
+// read of one chunk by 16 consecutive rows and a write of four rows' four chunks by 16
+// consecutive threads then touch 16 distinct 4-bank groups of a 64-bank LDS (and 8 distinct
+// groups per 8 lanes of a 32-bank one): no bank conflicts either way.
+//
+// Ragged edges: rows past M and weight rows past N are read clamped (in bounds) and not
+// written; k chunks past K are zero on both operands.  Requires K % 8 == 0 and N % 4 == 0.
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+
+__device__ __forceinline__ int lds_chunk(int row, int c) {
+  return row * 4 + (c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1)));
+}
 
 template <int EPI>
 __global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
                                                             const uint16_t* __restrict__ Wt, int M,
                                                             int N, int K, const float* bias,
                                                             const float* res, void* out) {
-  __shared__ __align__(16) uint16_t sA[2][kBM * kLDK];
-  __shared__ __align__(16) uint16_t sB[2][kBN * kLDK];
+  __shared__ __align__(16) uint4 sA[2][kBM * 4];
+  __shared__ __align__(16) uint4 sB[2][kBN * 4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4, wm = w >> 1, wn = w & 1;
-  const int tiles_n = N / kBN;
+  const int tiles_n = (N + kBN - 1) / kBN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * kBM, n0 = (tile % tiles_n) * kBN;
 
-  // global -> registers -> LDS: 2 chunks of 8 bf16 per thread for each operand
-  // (rows tid / 4 and tid / 4 + 64, k chunk 8 (tid % 4))
-  const int row = tid >> 2, ch = 8 * (tid & 3);
-  const uint16_t* pa = A + (int64_t)min(m0 + row, M - 1) * K + ch;
-  const int64_t da1 = (int64_t)(min(m0 + row + 64, M - 1) - min(m0 + row, M - 1)) * K;
-  const uint16_t* pb = Wt + (int64_t)(n0 + row) * K + ch;
-  const int64_t db = (int64_t)64 * K;
-  uint4 ga00, ga01, gb00, gb01;
-#define HOPE_GEMM_FETCH(S, k)                                 \
-  ga##S##0 = *reinterpret_cast<const uint4*>(pa + (k));       \
-  ga##S##1 = *reinterpret_cast<const uint4*>(pa + da1 + (k)); \
-  gb##S##0 = *reinterpret_cast<const uint4*>(pb + (k));       \
-  gb##S##1 = *reinterpret_cast<const uint4*>(pb + db + (k));
-#define HOPE_GEMM_STORE(S, buf)                                            \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 0) * kLDK + ch]) = ga##S##0;   \
-  *reinterpret_cast<uint4*>(&sA[buf][(row + 64) * kLDK + ch]) = ga##S##1;  \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 0) * kLDK + ch]) = gb##S##0;   \
-  *reinterpret_cast<uint4*>(&sB[buf][(row + 64) * kLDK + ch]) = gb##S##1;
-#define HOPE_GEMM_COMPUTE(buf)                                                                   \
-  {                                                                                              \
-    bf16x8 a[4], bv[4];                                                                          \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * 64 + 16 * i + r16) * kLDK + 8 * q4]); \
-      bv[i] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * 64 + 16 * i + r16) * kLDK + 8 * q4]); \
-    }                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                              \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);    \
-  }
+  // global -> registers -> LDS: for each operand, rows tid / 4 and tid / 4 + 64 of the tile,
+  // 16-byte chunk tid % 4 of the step's 32-deep k-slice
+  const int row = tid >> 2, ch = tid & 3;
+  const uint16_t* pa0 = A + (int64_t)min(m0 + row, M - 1) * K + 8 * ch;
+  const uint16_t* pa1 = A + (int64_t)min(m0 + row + 64, M - 1) * K + 8 * ch;
+  const uint16_t* pb0 = Wt + (int64_t)min(n0 + row, N - 1) * K + 8 * ch;
+  const uint16_t* pb1 = Wt + (int64_t)min(n0 + row + 64, N - 1) * K + 8 * ch;
+  const int st0 = lds_chunk(row, ch), st1 = lds_chunk(row + 64, ch);
+  uint4 ga0, ga1, gb0, gb1;
+  auto fetch = [&](int k0) {
+    const bool in = k0 + 8 * ch < K;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    ga0 = in ? *reinterpret_cast<const uint4*>(pa0 + k0) : z;
+    ga1 = in ? *reinterpret_cast<const uint4*>(pa1 + k0) : z;
+    gb0 = in ? *reinterpret_cast<const uint4*>(pb0 + k0) : z;
+    gb1 = in ? *reinterpret_cast<const uint4*>(pb1 + k0) : z;
+  };
+  auto store = [&](int buf) {
+    sA[buf][st0] = ga0;
+    sA[buf][st1] = ga1;
+    sB[buf][st0] = gb0;
+    sB[buf][st1] = gb1;
+  };
 
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int rd_a[4], rd_b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rd_a[i] = lds_chunk(wm * 64 + 16 * i + r16, q4);
+    rd_b[i] = lds_chunk(wn * 64 + 16 * i + r16, q4);
+  }
 
-  // tile t (32 deep) is loaded into registers during step t - 2, stored into LDS buffer
-  // t % 2 during step t - 1 and multiplied at step t; the barrier closing step t - 1 retires
-  // every read of the buffer that step t - 1 stores to (the four workgroups on a CU hide
-  // the latency that the single register set leaves)
-  HOPE_GEMM_FETCH(0, 0)
-  HOPE_GEMM_STORE(0, 0)
-  HOPE_GEMM_FETCH(0, kBK)
+  // step s multiplies k-slice s from buffer s % 2; slice s + 1 (fetched during step s - 1)
+  // is stored into the other buffer at the start of step s, and slice s + 2 fetched.  The
+  // barrier closing step s - 1 retires every read of the buffer that step s stores to.
+  const int steps = (K + kBK - 1) / kBK;
+  fetch(0);
+  store(0);
+  if (steps > 1) fetch(kBK);
   __syncthreads();
-  for (int k0 = 0; k0 < K; k0 += 2 * kBK) {
-    HOPE_GEMM_STORE(0, 1)
-    if (k0 + 2 * kBK < K) {
-      HOPE_GEMM_FETCH(0, k0 + 2 * kBK)
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) store(buf ^ 1);
+    if (s + 2 < steps) fetch((s + 2) * kBK);
+    bf16x8 a[4], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = __builtin_bit_cast(bf16x8, sA[buf][rd_a[i]]);
+      bv[i] = __builtin_bit_cast(bf16x8, sB[buf][rd_b[i]]);
     }
-    HOPE_GEMM_COMPUTE(0)
-    __syncthreads();
-    if (k0 + 2 * kBK < K) {
-      HOPE_GEMM_STORE(0, 0)
-      if (k0 + 3 * kBK < K) {
-        HOPE_GEMM_FETCH(0, k0 + 3 * kBK)
-      }
-    }
-    HOPE_GEMM_COMPUTE(1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);
     __syncthreads();
   }
 
-#undef HOPE_GEMM_FETCH
-#undef HOPE_GEMM_STORE
-#undef HOPE_GEMM_COMPUTE
   // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + r16][n0 + 64 wn + 16 j + 4 q4 + v]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn * 64 + 16 * j + 4 * q4;
+    if (n >= N) continue;  // N % 4 == 0: the lane's four columns are all in or all out
     const f32x4 bn = bias ? *reinterpret_cast<const f32x4*>(&bias[n]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -365,42 +375,45 @@ __global__ __launch_bounds__(512) void cpe_layernorm_kernel(
 
 // ---- LayerNorm over the channels of each pixel (one wave per pixel) ------------------------
 // y = bf16((x - mean) / sqrt(var + eps) * g + b) with the biased variance; optionally
-// x_plus = x + addv (fp32).  VPL = C / 64 values per lane.
+// x_plus = x + addv (fp32; x_plus may equal x).  Lane l holds channels l + 64 k, k < VPL,
+// those below C (C <= 64 VPL).
 template <int VPL>
-__global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict__ x,
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* x,
                                                          const float* __restrict__ g,
                                                          const float* __restrict__ b,
                                                          uint16_t* __restrict__ y,
                                                          const float* __restrict__ addv,
-                                                         float* __restrict__ x_plus, int64_t M,
+                                                         float* x_plus, int64_t M, int C,
                                                          float eps) {
-  constexpr int C = 64 * VPL;
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const float inv_c = 1.f / C;
   for (int64_t p = wave; p < M; p += nwaves) {
     float v[VPL];
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      v[k] = x[p * C + lane + 64 * k];
+      const int c = lane + 64 * k;
+      v[k] = c < C ? x[p * C + c] : 0.f;
       s += v[k];
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    const float mean = s * (1.f / C);
+    const float mean = s * inv_c;
     float q = 0.f;
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-      const float dv = v[k] - mean;
+      const float dv = lane + 64 * k < C ? v[k] - mean : 0.f;
       q = fmaf(dv, dv, q);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off, 64);
-    const float rstd = 1.f / sqrtf(q * (1.f / C) + eps);
+    const float rstd = 1.f / sqrtf(q * inv_c + eps);
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
       const int c = lane + 64 * k;
+      if (c >= C) break;
       y[p * C + c] = to_bf16((v[k] - mean) * rstd * g[c] + b[c]);
       if (x_plus) x_plus[p * C + c] = v[k] + addv[c];
     }
@@ -416,8 +429,8 @@ unsigned grid_for(int64_t work, int per_block) {
 
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s) {
-  if (N % kBN || K % (2 * kBK) || M <= 0 || K <= 0) return hipErrorInvalidValue;
-  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * (N / kBN);
+  if (N % 4 || K % 8 || M <= 0 || N <= 0 || K <= 0) return hipErrorInvalidValue;
+  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)tiles), block(256);
   switch (epi) {
@@ -458,14 +471,24 @@ hipError_t launch_dwconv_lpe(const uint16_t* z, const float* y, const float* pla
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, uint16_t* y,
                             const float* addv, float* x_plus, int64_t M, int C, float eps,
                             hipStream_t s) {
+  if (C <= 0 || C > 1024) return hipErrorInvalidValue;
   const unsigned grid = grid_for(M * 64, 256);
-  switch (C / 64) {
-#define HOPE_LN(V) \
-  case V: layernorm_kernel<V><<<grid, 256, 0, s>>>(x, g, b, y, addv, x_plus, M, eps); break;
-    HOPE_LN(1) HOPE_LN(2) HOPE_LN(3) HOPE_LN(4) HOPE_LN(6) HOPE_LN(8) HOPE_LN(12) HOPE_LN(16)
-#undef HOPE_LN
-    default: return hipErrorInvalidValue;
+  const int vpl = (C + 63) / 64;
+#define HOPE_LN(V)                                                                        \
+  if (vpl <= V) {                                                                         \
+    layernorm_kernel<V><<<grid, 256, 0, s>>>(x, g, b, y, addv, x_plus, M, C, eps);        \
+    return hipGetLastError();                                                             \
   }
+  HOPE_LN(1) HOPE_LN(2) HOPE_LN(3) HOPE_LN(4) HOPE_LN(6) HOPE_LN(8) HOPE_LN(12) HOPE_LN(16)
+#undef HOPE_LN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_cpe(const float* x, const float* w, const float* b, float* x1, int B, int H, int W,
+                      int C, hipStream_t s) {
+  if (C % 4) return hipErrorInvalidValue;
+  const int64_t work = (int64_t)B * H * ((W + 3) / 4) * (C / 4);
+  dwconv3x3_kernel<float, float, float, false><<<grid_for(work, 256), 256, 0, s>>>(x, x, w, b, x1, B, H, W, C, nullptr, 0, 0);
   return hipGetLastError();
 }
 

@@ -81,6 +81,12 @@ hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, h
 bool backward_wy_supported(const BackParams& p, int d);
 hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream);
 
+// The scan kernel a forward call launches (host-side dispatch, api.hip).
+enum ScanPath { kPathChain = 0, kPathMfma = 1 };
+ScanPath select_scan_path(const ChainParams& p, int d);
+const char* scan_path_kernel(ScanPath path);
+hipError_t launch_scan(const ChainParams& p, int d, hipStream_t stream);
+
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
 

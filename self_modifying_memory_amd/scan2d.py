@@ -45,6 +45,33 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _keep_for_stream(t: torch.Tensor | None, stream) -> None:
+    """Tell torch's caching allocator that a tensor this wrapper allocated is used by the
+    work enqueued on ``stream``: without it, the memory could be handed to a later
+    allocation on the current stream while the kernels still write it."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
+def state_numel(x: torch.Tensor, n_heads: int, init_per_image: bool = False,
+                shared_init: bool = False) -> int:
+    """Elements of an initial-state tensor for x: S = 4d^2 + 2d floats per (route, head),
+    times 4 routes (1 with shared_init), times B with init_per_image."""
+    D = x.shape[3]
+    if n_heads <= 0 or D % n_heads:
+        return -1
+    d = D // n_heads
+    S = 4 * d * d + 2 * d
+    return (x.shape[0] if init_per_image else 1) * (1 if shared_init else 4) * n_heads * S
+
+
+def _check_numel(t: torch.Tensor, want: int, name: str) -> None:
+    # a short buffer would be read or written out of bounds on the device: the C ABI
+    # sees only pointers, so sizes are checked here, before the call
+    if want >= 0 and t.numel() != want:
+        raise ValueError(f"{name} must have {want} elements, has {t.numel()}")
+
+
 def make_fmap(x: torch.Tensor, n_heads: int) -> N.hope_fmap_t:
     if x.dim() != 4:
         raise ValueError("x must be [B, H, W, D]")
@@ -82,15 +109,17 @@ def make_opts(stream=None, eta_map: str = "sigmoid", eta_scale: float = 1.0,
     return o
 
 
-def _f32_device(t: torch.Tensor, name: str, numel: int) -> int:
-    _require_device(t, name)
+def _f32_device(t: torch.Tensor, name: str, numel: int, check_device: bool = True) -> int:
+    if check_device:
+        _require_device(t, name)
     if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != numel:
         raise ValueError(f"{name} must be a contiguous float32 tensor of {numel} elements")
     return t.data_ptr()
 
 
-def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
+def _set_variants(o: N.hope_scan2d_opts_t, v: dict, check_device: bool = True) -> None:
     """VisionHOPE variants (Eq. 26 scales, App. B.5 skip, Sec. 3.5 ablations)."""
+    req = _require_device if check_device else (lambda t, name: None)
     unknown = set(v) - {"route_scales", "skip", "counts", "injection", "spectral", "frozen",
                         "no_dgd", "shared_init", "queries", "mem_chunk", "step_map", "n_heads",
                         "shape", "D"}
@@ -98,12 +127,12 @@ def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
         raise ValueError(f"unknown variant options {sorted(unknown)}")
     D = v.get("D")
     if v.get("route_scales") is not None:
-        o.route_scales = _f32_device(v["route_scales"], "route_scales", 4 * D)
+        o.route_scales = _f32_device(v["route_scales"], "route_scales", 4 * D, check_device)
     if v.get("skip") is not None:
-        o.skip = _f32_device(v["skip"], "skip", D)
+        o.skip = _f32_device(v["skip"], "skip", D, check_device)
     if v.get("counts") is not None:
         c = v["counts"]
-        _require_device(c, "counts")
+        req(c, "counts")
         if c.dtype != torch.int64 or not c.is_contiguous() or c.numel() != 3:
             raise ValueError("counts must be a contiguous int64 tensor of 3 elements")
         o.counts = c.data_ptr()
@@ -114,7 +143,7 @@ def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
     o.shared_init = int(bool(v.get("shared_init", False)))
     q = v.get("queries")
     if q is not None:
-        _require_device(q, "queries")
+        req(q, "queries")
         if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous() or \
                 tuple(q.shape) != tuple(v["shape"]):
             raise ValueError("queries must be a contiguous float32 / bfloat16 tensor shaped like x")
@@ -124,10 +153,28 @@ def _set_variants(o: N.hope_scan2d_opts_t, v: dict) -> None:
     sm = v.get("step_map")
     if sm is not None:
         B, H, W, _ = v["shape"]
-        _require_device(sm, "step_map")
+        req(sm, "step_map")
         if sm.dtype != torch.float32 or not sm.is_contiguous() or sm.numel() != B * 4 * v["n_heads"] * H * W:
             raise ValueError("step_map must be a contiguous float32 tensor [B, 4, n_heads, H, W]")
         o.step_map = sm.data_ptr()
+
+
+def hope_scan2d_kernel_name(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
+                            readout: str = "boundary", out_dtype: torch.dtype = torch.float32,
+                            **variants) -> str:
+    """Name of the scan kernel hope_scan2d_forward launches for these arguments ("" when
+    it would reject them).  Only shapes, dtypes and option flags are read; variant
+    tensors may be given as in hope_scan2d_forward (their pointers are not dereferenced)."""
+    lib = N.load_library()
+    fm = make_fmap(x, n_heads)
+    o = N.hope_scan2d_opts_t()
+    lib.hope_scan2d_default_opts(ctypes.byref(o))
+    o.out_dtype = N.HOPE_BF16 if out_dtype == torch.bfloat16 else N.HOPE_F32
+    o.readout = _READOUTS[readout]
+    v = dict(variants)
+    v.update(n_heads=n_heads, shape=tuple(x.shape), D=x.shape[3])
+    _set_variants(o, v, check_device=False)
+    return lib.hope_scan2d_kernel_name(ctypes.byref(fm), dirs, chunk, ctypes.byref(o)).decode()
 
 
 def hope_scan2d_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15, chunk: int = 0,
@@ -185,13 +232,18 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     _require_device(init_memories, "init_memories")
     if init_memories.dtype != torch.float32:
         raise TypeError("init_memories must be float32")
+    _check_numel(init_memories, state_numel(x, n_heads, init_per_image, shared_init), "init_memories")
+    if final_memories is not None:
+        _check_numel(final_memories, state_numel(x, n_heads, True), "final_memories")
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        _keep_for_stream(out, stream)
     _require_device(out, "out")
     if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != tuple(x.shape):
         raise ValueError("out must be float32 or bfloat16 with the shape of x")
     if workspace is None:
         workspace = alloc_workspace(x, n_heads, dirs, chunk, out.dtype)
+        _keep_for_stream(workspace, stream)
     fm = make_fmap(x, n_heads)
     variants = dict(route_scales=route_scales, skip=skip, counts=counts, injection=injection,
                     spectral=spectral, frozen=frozen, no_dgd=no_dgd, shared_init=shared_init,
@@ -235,17 +287,24 @@ def hope_scan2d_backward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: 
         raise TypeError("init_memories must be a contiguous float32 tensor")
     if grad_out.dtype != torch.float32 or not grad_out.is_contiguous() or tuple(grad_out.shape) != tuple(x.shape):
         raise ValueError("grad_out must be a contiguous float32 tensor shaped like x")
+    _check_numel(init_memories, state_numel(x, n_heads, init_per_image), "init_memories")
     if grad_x is None:
         grad_x = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        _keep_for_stream(grad_x, stream)
     if grad_init is None:
         grad_init = torch.empty_like(init_memories)
+        _keep_for_stream(grad_init, stream)
     for t, name in ((grad_x, "grad_x"), (grad_init, "grad_init")):
         _require_device(t, name)
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if tuple(grad_x.shape) != tuple(x.shape):
+        raise ValueError("grad_x must be shaped like x")
+    _check_numel(grad_init, init_memories.numel(), "grad_init")
     if workspace is None:
         nbytes = hope_scan2d_backward_workspace_size(x, n_heads, dirs, chunk)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+        _keep_for_stream(workspace, stream)
     fm = make_fmap(x, n_heads)
     opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, None, workspace)
     st = lib.hope_scan2d_backward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
@@ -265,7 +324,12 @@ def hope_debug_cross_scan(x: torch.Tensor, dirs: int = 15, routes: torch.Tensor 
     n_sel = bin(dirs & 15).count("1")
     if routes is None:
         routes = torch.empty((max(n_sel, 1), B, H * W, D), dtype=x.dtype, device=x.device)
+        _keep_for_stream(routes, stream)
     _require_device(routes, "routes")
+    if routes.dtype != x.dtype:
+        raise ValueError("routes must have the dtype of x")
+    if routes.numel() < n_sel * B * H * W * D:
+        raise ValueError(f"routes must hold {n_sel * B * H * W * D} elements")
     fm = make_fmap(x, 1)
     st = lib.hope_debug_cross_scan(ctypes.byref(fm), dirs, routes.data_ptr(), _stream_handle(stream))
     if st != N.HOPE_OK:
@@ -281,7 +345,13 @@ def hope_debug_cross_merge(routes: torch.Tensor, H: int, W: int, dirs: int = 15,
     _, B, Nn, D = routes.shape
     if out is None:
         out = torch.empty((B, H, W, D), dtype=torch.float32, device=routes.device)
+        _keep_for_stream(out, stream)
     _require_device(out, "out")
+    if out.dtype != torch.float32:
+        raise ValueError("out must be float32")
+    if Nn != H * W or routes.shape[0] < bin(dirs & 15).count("1"):
+        raise ValueError("routes must be [n_selected, B, H*W, D]")
+    _check_numel(out, B * H * W * D, "out")
     st = lib.hope_debug_cross_merge(routes.data_ptr(), _dtype_code(routes), B, H, W, D, dirs,
                                     out.data_ptr(), _stream_handle(stream))
     if st != N.HOPE_OK:

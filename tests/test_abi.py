@@ -40,7 +40,7 @@ def call(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, out=FAKE + (2 << 30), 
 def test_every_declared_function_is_exported(lib):
     names = N.header_functions()
     assert "hope_scan2d_forward" in names and "hope_scan2d_backward" in names
-    assert "hope_block_forward" in names and "hope_block_workspace_size" in names and len(names) == 11
+    assert "hope_block_forward" in names and "hope_block_workspace_size" in names and len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
 
@@ -286,23 +286,29 @@ int main(void) {
 
 
 def test_block_workspace_size_and_errors(lib):
-    assert lib.hope_block_workspace_size(2, 14, 14, 384, 6, 1536, 0) > 0
-    assert lib.hope_block_workspace_size(2, 14, 14, 100, 2, 400, 0) == 0   # D % 128
-    assert lib.hope_block_workspace_size(2, 14, 14, 128, 3, 512, 0) == 0   # D % n_heads
-    assert lib.hope_block_workspace_size(2, 14, 14, 128, 2, 500, 0) == 0   # ffn_dim % 128
-    assert lib.hope_block_workspace_size(0, 14, 14, 128, 2, 512, 0) == 0
+    #                                   B, H,  W,  D,   D_m, nh, ffn,  chunk
+    assert lib.hope_block_workspace_size(2, 14, 14, 384, 192, 12, 1536, 0) > 0   # the pages' evaluated form
+    assert lib.hope_block_workspace_size(2, 14, 14, 96, 48, 3, 384, 0) > 0
+    assert lib.hope_block_workspace_size(2, 14, 14, 384, 384, 6, 1536, 0) > 0
+    assert lib.hope_block_workspace_size(2, 14, 14, 100, 48, 3, 400, 0) == 0   # D % 16
+    assert lib.hope_block_workspace_size(2, 14, 14, 96, 40, 2, 384, 0) == 0    # D_m % 16
+    assert lib.hope_block_workspace_size(2, 14, 14, 128, 128, 3, 512, 0) == 0  # D_m % n_heads
+    assert lib.hope_block_workspace_size(2, 14, 14, 128, 64, 2, 500, 0) == 0   # ffn_dim % 16
+    assert lib.hope_block_workspace_size(2, 14, 14, 2048, 64, 2, 512, 0) == 0  # D > 1024
+    assert lib.hope_block_workspace_size(0, 14, 14, 128, 64, 2, 512, 0) == 0
+    assert lib.hope_block_workspace_size(2, 14, 14, 128, 0, 2, 512, 0) == 0
     w = N.hope_block_weights_t()
     # null weights: rejected before anything is enqueued (no device needed)
-    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 64, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
                                   FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_INVALID_ARG
     for name in N.BLOCK_WEIGHT_FIELDS:
         setattr(w, name, FAKE + (3 << 30))
     # a head dimension of 128 is well formed but not supported
-    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 1, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 128, 1, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
                                   FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_UNSUPPORTED
     # x and out alias
-    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE,
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 64, 2, 512, 0, ctypes.byref(w), FAKE,
                                   FAKE + (2 << 30), 1 << 30, None) == N.HOPE_ERR_INVALID_ARG
     # short workspace
-    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
+    assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 64, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
                                   FAKE + (2 << 30), 256, None) == N.HOPE_ERR_WORKSPACE

@@ -141,3 +141,56 @@ def test_backward_full_size_stage3_image0():
     e = _rel(got, ref[0])
     print(f"  rel grad_x[0] {e:.2e}", flush=True)
     assert e <= TOL["f32"]
+
+
+#             B, H,   W,   D,  nh, dirs, options
+LONG_CASES = [
+    (1, 28, 28, 32, 1, 15, {}),                     # 28-token rows and columns (stage-2 chunks)
+    (1, 6, 56, 32, 1, 3, {}),                       # 56-token rows (stage-1 chunks)
+    (1, 56, 6, 32, 1, 12, dict(eta_scale=2.0)),     # 56-token columns
+    (1, 4, 128, 32, 1, 3, {}),                      # 128-token rows (high-resolution chunks)
+    (1, 128, 3, 32, 1, 12, dict(eta_scale=2.0)),    # 128-token columns
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES,
+                         ids=[f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}_dirs{c[5]}" for c in LONG_CASES])
+def test_backward_long_chunks_match_gradient_oracle(case):
+    # The chunk lengths of the stage-1, stage-2 and high-resolution workloads at d = 32:
+    # several 16-token gate blocks and up to 128 gain rows per chunk, through the gain
+    # adjoint (k, delta, the step, alpha) into grad_x and every memory's grad_init.  The
+    # backward computes in fp32 on the bf16 map's values, so it is held to the fp32 bar.
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_backward
+    B, H, W, D, nh, dirs, kw = case
+    print("case", case, flush=True)
+    inp = wl.draw(B, H, W, D, nh, seed=9300 + H + W, dtype="bf16", live=True)
+    g = np.random.Generator(np.random.PCG64(96)).standard_normal((B, H, W, D)).astype(np.float32)
+    x, init = to_device(inp, "bf16")
+    gx, gi = hope_scan2d_backward(x, init, nh, torch.from_numpy(g).cuda(), dirs, 0, **kw)
+    torch.cuda.synchronize()
+    ref_x, ref_i = hb.scan2d_backward(inp["x"], inp["init"], nh, g, dirs=dirs, **kw)
+    e_x, e_i = _rel(gx.cpu().numpy(), ref_x), _rel(gi.cpu().numpy(), ref_i)
+    print(f"  rel grad_x {e_x:.2e} grad_init {e_i:.2e}", flush=True)
+    assert e_x <= TOL["f32"] and e_i <= TOL["f32"]
+
+
+def test_backward_full_size_stage2_image0_head0():
+    # The map gradient of one image's head slice depends only on that head's chains: the
+    # backward at the full stage-2 batch (64 images, 6 heads of 32, 28-token chunks)
+    # against the gradient oracle on image 0, head 0 alone.
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_backward
+    w = wl.WORKLOADS[2]
+    print("workload", w.name, flush=True)
+    inp = wl.draw_workload(w, live=True)
+    x, init = to_device(inp, w.dtype)
+    g = np.random.Generator(np.random.PCG64(97)).standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)
+    gx, _ = hope_scan2d_backward(x, init, w.n_heads, torch.from_numpy(g).cuda())
+    torch.cuda.synchronize()
+    d = w.d
+    got = gx[0, ..., :d].cpu().numpy()
+    ref, _ = hb.scan2d_backward(inp["x"][:1, ..., :d], inp["init"][:, :1], 1, g[:1, ..., :d])
+    e = _rel(got, ref[0])
+    print(f"  rel grad_x[0, head 0] {e:.2e}", flush=True)
+    assert e <= TOL["f32"]

@@ -40,26 +40,31 @@ def _rel_branch(got, ref, x):
     return float(np.max(np.abs((got - x) - d_ref)) / np.max(np.abs(d_ref)))
 
 
-#        B, H, W, D, nh, ffn, chunk
+#        B, H, W, D, D_m, nh, ffn, chunk
 CASES = [
-    (1, 4, 5, 128, 2, 512, 0),     # d = 64
-    (2, 3, 7, 128, 4, 256, 3),     # d = 32, ragged chunks
-    (1, 5, 4, 128, 8, 512, 0),     # d = 16
-    (1, 6, 6, 256, 4, 1024, 0),    # d = 64, wider
-    (3, 9, 10, 128, 2, 256, 5),    # d = 64, 270 pixels: three GEMM row tiles, the last ragged
-    (1, 4, 6, 512, 8, 512, 0),     # d = 64, D = 512: eight values per lane in the LayerNorm
+    (1, 4, 5, 128, 128, 2, 512, 0),     # d = 64
+    (2, 3, 7, 128, 128, 4, 256, 3),     # d = 32, ragged chunks
+    (1, 5, 4, 128, 128, 8, 512, 0),     # d = 16
+    (1, 6, 6, 256, 256, 4, 1024, 0),    # d = 64, wider
+    (3, 9, 10, 128, 128, 2, 256, 5),    # d = 64, 270 pixels: three GEMM row tiles, the last ragged
+    (1, 4, 6, 512, 512, 8, 512, 0),     # d = 64, D = 512: eight values per lane in the LayerNorm
+    # the pages' evaluated form (VisionHOPE App. C.3): D_m = D / 2, n_heads = D / 32 heads of 16
+    (1, 14, 14, 384, 192, 12, 1536, 0),  # stage-3 width: ragged GEMM N (192) and K (192)
+    (2, 9, 8, 192, 96, 6, 768, 0),       # stage-2 width: D % 128 != 0 (CPE and LayerNorm apart)
+    (1, 8, 8, 96, 48, 3, 384, 0),        # stage-1 width: K = 48 (a half MFMA k-step)
+    (1, 6, 7, 96, 48, 3, 400, 5),        # ffn_dim not a multiple of 32, ragged chunks
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}h{c[4]}_F{c[5]}_c{c[6]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}m{c[4]}h{c[5]}_F{c[6]}_c{c[7]}" for c in CASES])
 def test_block_matches_oracle(case):
     import torch
     from self_modifying_memory_amd.block import hope_block_forward
-    B, H, W, D, nh, F, chunk = case
+    B, H, W, D, Dm, nh, F, chunk = case
     print("case", case, flush=True)
     x = np.random.Generator(np.random.PCG64(500 + D + H)).standard_normal((B, H, W, D)).astype(np.float32)
-    wts = wl.draw_block_weights(D, nh, F, seed=600 + D + W)
-    out = hope_block_forward(torch.from_numpy(x).cuda(), _device_weights(wts), nh, F, chunk)
+    wts = wl.draw_block_weights(D, nh, F, seed=600 + D + W, D_m=Dm)
+    out = hope_block_forward(torch.from_numpy(x).cuda(), _device_weights(wts), nh, F, chunk, D_m=Dm)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     ref = hbk.block_forward(x, _oracle_weights(wts), nh, chunk=chunk)
@@ -72,26 +77,29 @@ def test_block_is_deterministic():
     import torch
     from self_modifying_memory_amd.block import hope_block_forward
     x = torch.from_numpy(np.random.Generator(np.random.PCG64(7)).standard_normal((2, 5, 6, 128)).astype(np.float32)).cuda()
-    w = _device_weights(wl.draw_block_weights(128, 2, 512, seed=8))
-    a = hope_block_forward(x, w, 2).cpu().numpy()
-    b = hope_block_forward(x, w, 2).cpu().numpy()
+    w = _device_weights(wl.draw_block_weights(128, 4, 512, seed=8, D_m=64))
+    a = hope_block_forward(x, w, 4, D_m=64).cpu().numpy()
+    b = hope_block_forward(x, w, 4, D_m=64).cpu().numpy()
     assert np.array_equal(a, b)
 
 
-def test_block_full_size_stage3_image0():
+@pytest.mark.parametrize("Dm_half", [False, True], ids=["Dm=D_6x64", "Dm=D/2_12x16"])
+def test_block_full_size_stage3_image0(Dm_half):
     # every step of the block is per image, so image 0 of the full 128-image batch (the
-    # launch the benchmark times) is checked against the oracle run on image 0 alone
+    # launch the benchmark times) is checked against the oracle run on image 0 alone; once
+    # at D_m = D with the scan workload's heads, once in the pages' evaluated form
     import torch
     from self_modifying_memory_amd.block import hope_block_forward
     w = wl.WORKLOADS[3]
-    print("workload", w.name, flush=True)
+    Dm, nh = (w.D // 2, w.D // 32) if Dm_half else (w.D, w.n_heads)
+    print("workload", w.name, "D_m", Dm, "heads", nh, flush=True)
     F = 4 * w.D
     x = np.random.Generator(np.random.PCG64(31)).standard_normal((w.B, w.H, w.W, w.D)).astype(np.float32)
-    wts = wl.draw_block_weights(w.D, w.n_heads, F, seed=32)
-    out = hope_block_forward(torch.from_numpy(x).cuda(), _device_weights(wts), w.n_heads, F)
+    wts = wl.draw_block_weights(w.D, nh, F, seed=32, D_m=Dm)
+    out = hope_block_forward(torch.from_numpy(x).cuda(), _device_weights(wts), nh, F, D_m=Dm)
     torch.cuda.synchronize()
     got = out[0:1].cpu().numpy().astype(np.float64)
-    ref = hbk.block_forward(x[:1], _oracle_weights(wts), w.n_heads)
+    ref = hbk.block_forward(x[:1], _oracle_weights(wts), nh)
     e = _rel_branch(got, ref, x[:1].astype(np.float64))
     print(f"  rel branch error image 0 {e:.2e}", flush=True)
     assert e <= TOL_BF16

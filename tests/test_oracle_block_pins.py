@@ -75,8 +75,8 @@ def test_layer_norm_matches_torch_and_invariants():
     np.testing.assert_allclose((n ** 2).mean(-1), var / (var + hbk.LN_EPS), rtol=1e-12)
 
 
-def _weights(D=16, nh=1, F=32, seed=11):
-    w = wl.draw_block_weights(D, nh, F, seed)
+def _weights(D=16, nh=1, F=32, seed=11, Dm=None):
+    w = wl.draw_block_weights(D, nh, F, seed, D_m=Dm)
     return {k: v.astype(np.float64) for k, v in w.items() if not k.endswith("_bits")}
 
 
@@ -105,24 +105,28 @@ def test_ffn_branch_reduces_to_torch_ops():
     np.testing.assert_allclose(hbk.block_forward(x, w, 1), ref, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("nh", [1, 2])
-def test_operator_branch_reduces_to_the_operator_oracle(nh):
-    # zero positional encodings, zero depthwise branches, identity output projection and a
-    # zero FFN output: out - x = VH(u) with u = LN1(x) W_in^T + b_in (torch's layer_norm and
-    # linear), the operator oracle's result with the same queries, skip and scales
+@pytest.mark.parametrize("nh,Dm", [(1, 16), (2, 16), (2, 8)])
+def test_operator_branch_reduces_to_the_operator_oracle(nh, Dm):
+    # zero positional encodings, zero depthwise branches and a zero FFN output: out - x =
+    # VH(u) W_out^T with u = LN1(x) W_in^T + b_in (torch's layer_norm and linear), the
+    # operator oracle's result with the same queries, skip and scales; with D_m < D the
+    # operator runs at the inner width and W_out maps it back (VisionHOPE Sec. 2.3)
     import torch
     D = 16
-    w = _weights(D=D, nh=nh)
+    w = _weights(D=D, nh=nh, Dm=Dm)
     for k in ("cpe_w", "cpe_b", "dw_w", "dw_b", "lpe_w", "lpe_b", "b_out", "w2", "b2"):
         w[k] = np.zeros_like(w[k])
-    w["w_out"] = np.eye(D)
+    if Dm == D:
+        w["w_out"] = np.eye(D)
+    assert w["w_in"].shape == (Dm, D) and w["w_out"].shape == (D, Dm) and w["w_q"].shape == (Dm, Dm)
     x = _x((1, 3, 5, D), 14)
     F = torch.nn.functional
     t = lambda a: torch.tensor(a)
     u = F.linear(F.layer_norm(t(x), (D,), t(w["ln1_g"]), t(w["ln1_b"]), eps=1e-5),
                  t(w["w_in"]), t(w["b_in"])).numpy()
     q = F.linear(t(u), t(w["w_q"])).numpy()
-    ref, _ = oracle.scan2d(u, w["init"], nh, queries=q, route_scales=w["scales"], skip=w["skip"])
+    y, _ = oracle.scan2d(u, w["init"], nh, queries=q, route_scales=w["scales"], skip=w["skip"])
+    ref = F.linear(t(y), t(w["w_out"])).numpy()
     got = hbk.block_forward(x, w, nh) - x
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
 
@@ -145,15 +149,15 @@ def test_positional_encoding_branch():
                                rtol=1e-12, atol=1e-12)
 
 
-def test_gated_and_local_positional_branches():
-    # identity output projection, zero FFN output, zero CPE: out - x = VH(z) + LPE(z) with
-    # z = u + SiLU(DW(u)), the convolutions and SiLU from torch
+@pytest.mark.parametrize("Dm", [16, 8])
+def test_gated_and_local_positional_branches(Dm):
+    # zero FFN output, zero CPE: out - x = (VH(z) + LPE(z)) W_out^T with z = u + SiLU(DW(u)),
+    # the convolutions, SiLU and projections from torch
     import torch
     D = 16
-    w = _weights(D=D, nh=2, seed=17)
+    w = _weights(D=D, nh=2, seed=17, Dm=Dm)
     for k in ("cpe_w", "cpe_b", "b_out", "w2", "b2"):
         w[k] = np.zeros_like(w[k])
-    w["w_out"] = np.eye(D)
     x = _x((1, 4, 5, D), 16)
     F = torch.nn.functional
     t = lambda a: torch.tensor(a)
@@ -162,5 +166,5 @@ def test_gated_and_local_positional_branches():
     z = u + F.silu(t(_torch_dw(u, w["dw_w"], w["dw_b"]))).numpy()
     q = F.linear(t(z), t(w["w_q"])).numpy()
     y, _ = oracle.scan2d(z, w["init"], 2, queries=q, route_scales=w["scales"], skip=w["skip"])
-    ref = y + _torch_dw(z, w["lpe_w"], w["lpe_b"])
+    ref = F.linear(t(y + _torch_dw(z, w["lpe_w"], w["lpe_b"])), t(w["w_out"])).numpy()
     np.testing.assert_allclose(hbk.block_forward(x, w, 2) - x, ref, rtol=1e-10, atol=1e-12)

@@ -138,16 +138,21 @@ def split_state(flat: np.ndarray, d: int) -> dict:
 BLOCK_LINEAR = ("w_in", "w_q", "w_out", "w1", "w2")
 
 
-def draw_block_weights(D: int, n_heads: int, ffn_dim: int, seed: int) -> dict:
+def draw_block_weights(D: int, n_heads: int, ffn_dim: int, seed: int, D_m: int | None = None) -> dict:
     """Synthetic weights of one VisionHOPE block (the pages' trained weights are absent).
 
+    D is the block width, D_m the operator's inner width (default D; the pages' evaluated
+    models use D_m = D / 2 with n_heads = D / 32 heads of 16), split into n_heads heads.
     Linear weights [out, in] ~ N(0, 1/in), rounded to bf16 (values as fp32 under their
-    names, bit patterns under name + "_bits"); depthwise 3x3 weights [3, 3, C] ~ N(0, 1/9)
-    scaled by 0.5; biases ~ N(0, 0.02^2); LayerNorm gains 1 + N(0, 0.1^2) and shifts
-    N(0, 0.1^2); direction scales 1 + N(0, 0.1^2) [4, D]; skip N(0, 0.1^2) [D]; initial
-    memories [4, n_heads, 4d^2 + 2d] ~ N(0, 1/d), M_mem kept.  Draw order: the names in the
-    order listed by the returned dict's construction below, one PCG64 stream."""
-    d = D // n_heads
+    names, bit patterns under name + "_bits"): w_in [D_m, D], w_q [D_m, D_m], w_out [D, D_m],
+    w1 [ffn_dim, D], w2 [D, ffn_dim]; depthwise 3x3 weights [3, 3, C] ~ N(0, 1/9) scaled by
+    0.5 (C = D for the positional encoding, D_m for the two branches inside); biases
+    ~ N(0, 0.02^2); LayerNorm gains 1 + N(0, 0.1^2) and shifts N(0, 0.1^2); direction scales
+    1 + N(0, 0.1^2) [4, D_m]; skip N(0, 0.1^2) [D_m]; initial memories [4, n_heads, 4d^2 + 2d]
+    ~ N(0, 1/d), d = D_m / n_heads, M_mem kept.  Draw order: the names in the order listed by
+    the returned dict's construction below, one PCG64 stream."""
+    Dm = D if D_m is None else D_m
+    d = Dm // n_heads
     rng = np.random.Generator(np.random.PCG64(seed))
     out: dict = {}
 
@@ -165,16 +170,16 @@ def draw_block_weights(D: int, n_heads: int, ffn_dim: int, seed: int) -> dict:
     dw("cpe", D)
     vec("ln1_g", D, 1.0, 0.1)
     vec("ln1_b", D, 0.0, 0.1)
-    lin("w_in", D, D)
-    vec("b_in", D, 0.0, 0.02)
-    dw("dw", D)
-    lin("w_q", D, D)
-    out["scales"] = (1.0 + rng.standard_normal((4, D)) * 0.1).astype(np.float32)
-    vec("skip", D, 0.0, 0.1)
+    lin("w_in", Dm, D)
+    vec("b_in", Dm, 0.0, 0.02)
+    dw("dw", Dm)
+    lin("w_q", Dm, Dm)
+    out["scales"] = (1.0 + rng.standard_normal((4, Dm)) * 0.1).astype(np.float32)
+    vec("skip", Dm, 0.0, 0.1)
     S = 4 * d * d + 2 * d
     out["init"] = (rng.standard_normal((4, n_heads, S)) / np.sqrt(d)).astype(np.float32)
-    dw("lpe", D)
-    lin("w_out", D, D)
+    dw("lpe", Dm)
+    lin("w_out", D, Dm)
     vec("b_out", D, 0.0, 0.02)
     vec("ln2_g", D, 1.0, 0.1)
     vec("ln2_b", D, 0.0, 0.1)
