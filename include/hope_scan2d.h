@@ -199,6 +199,34 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
                                   uint32_t dirs, int32_t chunk, void* out,
                                   const hope_scan2d_opts_t* opts);
 
+/* Size of the device array that serves hope_scan2d_forward_noalloc as its route-plane
+ * scratch: 64 MiB, one array per GPU the library runs on, held until the process ends. */
+#define HOPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * hope_scan2d_forward_noalloc -- hope_scan2d_forward for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results (bit for bit) and checks, except:
+ *   - opts->workspace must be NULL and opts->workspace_bytes 0 (else HOPE_ERR_INVALID_ARG):
+ *     the route planes live in the library's own device array of
+ *     HOPE_NOALLOC_SCRATCH_BYTES bytes.  The batch is processed in consecutive slices of
+ *     whole images whose planes fit in it (one slice when none is needed: one route with
+ *     an fp32 out).  HOPE_ERR_WORKSPACE when one image's planes do not fit:
+ *     (popcount(dirs) - 1) * H * W * D * 4 bytes for an fp32 out, popcount(dirs) * ... for
+ *     a bf16 out, above HOPE_NOALLOC_SCRATCH_BYTES.
+ *   - opts->scan_begin / scan_end, when given, bracket every slice's scan kernel together
+ *     (with the route sums of the slices before the last).
+ *   - The array is per GPU (the current device) and shared by every call on that GPU: calls
+ *     that overlap in time on one GPU (other streams, other host threads) race on it and
+ *     must be serialised by the caller.  It keeps the last call's contents; every element
+ *     a call reads it has written first.
+ * Calls no allocating routine (no hipMalloc, no hipFree).  The stream must belong to the
+ * current device.
+ */
+hope_status_t hope_scan2d_forward_noalloc(const hope_fmap_t* x, const float* init_memories,
+                                          uint32_t dirs, int32_t chunk, void* out,
+                                          const hope_scan2d_opts_t* opts);
+
 /* Bytes of workspace hope_scan2d_forward needs for this call with these options (NULL =
  * defaults): one fp32 plane of the map per selected route beyond the first, or per
  * selected route for a bf16 out; 0 when none is needed, and 0 for arguments that

@@ -30,6 +30,7 @@ HOPE_INJECTION = {"soft": 0, "hard": 1, "none": 2}
 HOPE_SPECTRAL = {"clamp": 0, "soft": 1, "none": 2}
 HOPE_FREEZE = {"kv": 1, "dynamics": 2, "q": 4}
 HOPE_DIR_ALL = 15
+HOPE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class hope_fmap_t(ctypes.Structure):
@@ -80,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hope_scan2d_forward.argtypes = [P(hope_fmap_t), ctypes.c_void_p, ctypes.c_uint32,
                                         ctypes.c_int32, ctypes.c_void_p, P(hope_scan2d_opts_t)]
     lib.hope_scan2d_forward.restype = ctypes.c_int
+    lib.hope_scan2d_forward_noalloc.argtypes = [P(hope_fmap_t), ctypes.c_void_p, ctypes.c_uint32,
+                                                ctypes.c_int32, ctypes.c_void_p, P(hope_scan2d_opts_t)]
+    lib.hope_scan2d_forward_noalloc.restype = ctypes.c_int
     lib.hope_scan2d_workspace_size.argtypes = [P(hope_fmap_t), ctypes.c_uint32, ctypes.c_int32,
                                                P(hope_scan2d_opts_t)]
     lib.hope_scan2d_workspace_size.restype = ctypes.c_size_t

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/hope_scan2d.h: argument validation
 // (all of it before anything is enqueued), workspace accounting and kernel dispatch.
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 #include <string.h>
 
@@ -173,16 +174,11 @@ hipError_t launch_scan(const ChainParams& p, int d, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uint32_t dirs,
-                           int32_t chunk, void* out, const hope_scan2d_opts_t* opts,
-                           RoutePlanes* defer) {
-  if (defer) *defer = RoutePlanes{nullptr, 0, 0};
-  hope_scan2d_opts_t o;
-  if (opts) {
-    o = *opts;
-  } else {
-    hope_scan2d_default_opts(&o);
-  }
+// Every check of hope_scan2d_forward (the workspace's only with check_workspace) and the
+// kernel parameters of the call, without the route planes (attach_planes).
+hope_status_t plan_forward(const hope_fmap_t* x, const float* init_memories, uint32_t dirs,
+                           int32_t chunk, void* out, const hope_scan2d_opts_t& o, bool check_workspace,
+                           ChainParams& p, int& d) {
   hope_status_t st = check_fmap(x);
   if (st != HOPE_OK) return st;
   if ((st = check_opts(&o)) != HOPE_OK) return st;
@@ -190,7 +186,7 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
   if (!aligned(init_memories, 16) || !aligned(out, 16)) return HOPE_ERR_INVALID_ARG;
   if (dirs == 0 || dirs > 15 || chunk < 0) return HOPE_ERR_INVALID_ARG;
 
-  const int d = x->D / x->n_heads;
+  d = x->D / x->n_heads;
   const int64_t n_elem = (int64_t)x->B * x->H * x->W * x->D;
   const size_t x_bytes = (size_t)n_elem * (x->dtype == HOPE_BF16 ? 2 : 4);
   const bool out_bf16 = o.out_dtype == HOPE_BF16;
@@ -246,20 +242,11 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
       return HOPE_ERR_INVALID_ARG;
   }
   if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
-  if (ws_need > 0 && (!o.workspace || o.workspace_bytes < ws_need)) return HOPE_ERR_WORKSPACE;
+  if (check_workspace && ws_need > 0 && (!o.workspace || o.workspace_bytes < ws_need)) return HOPE_ERR_WORKSPACE;
 
-  hope::ChainParams p;
   memset(&p, 0, sizeof(p));
   p.x = x->data;
   p.init = init_memories;
-  p.plane_stride = plane_stride_elems(n_elem);
-  if (out_bf16) {  // every route writes an fp32 plane; the route sum rounds once
-    p.out = static_cast<float*>(o.workspace);
-    p.planes = p.out + p.plane_stride;
-  } else {
-    p.out = static_cast<float*>(out);
-    if (ws_need > 0) p.planes = static_cast<float*>(o.workspace);
-  }
   p.final_mem = o.final_memories;
   p.x_bf16 = x->dtype == HOPE_BF16;
   p.B = x->B;
@@ -289,11 +276,31 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
   p.steps = o.step_map;
   if ((int64_t)p.n_sel * p.B * p.nh > INT32_MAX) return HOPE_ERR_INVALID_ARG;
 
-  hipStream_t s = o.stream;
-  if (o.scan_begin && (st = hip_status(hipEventRecord(o.scan_begin, s))) != HOPE_OK) return st;
-  st = hip_status(launch_scan(p, d, s));
-  if (st == HOPE_OK && o.scan_end) st = hip_status(hipEventRecord(o.scan_end, s));
-  if (st != HOPE_OK) return st;
+  return HOPE_OK;
+}
+
+// Route planes of a planned call: with a bf16 out every route writes an fp32 plane (the
+// route sum rounds once); with an fp32 out route slot 0 writes out and the others planes.
+void attach_planes(ChainParams& p, void* out, float* planes, bool out_bf16) {
+  p.plane_stride = plane_stride_elems((int64_t)p.B * p.H * p.W * p.D);
+  if (out_bf16) {
+    p.out = planes;
+    p.planes = planes + p.plane_stride;
+  } else {
+    p.out = static_cast<float*>(out);
+    p.planes = planes;
+  }
+}
+
+// The scan kernel of a planned call with its planes (bracketed by the events when given),
+// then the route sum (left to the caller through defer for an fp32 out when defer is given).
+hope_status_t enqueue_forward(const ChainParams& p, int d, void* out, bool out_bf16, hipStream_t s,
+                              hipEvent_t begin, hipEvent_t end, RoutePlanes* defer) {
+  const int64_t n_elem = (int64_t)p.B * p.H * p.W * p.D;
+  hope_status_t st;
+  if (begin && (st = hip_status(hipEventRecord(begin, s))) != HOPE_OK) return st;
+  if ((st = hip_status(launch_scan(p, d, s))) != HOPE_OK) return st;
+  if (end && (st = hip_status(hipEventRecord(end, s))) != HOPE_OK) return st;
   if (out_bf16)
     return hip_status(hope::launch_plane_sum_bf16(static_cast<unsigned short*>(out), p.out,
                                                   p.plane_stride, p.n_sel, n_elem, s));
@@ -308,7 +315,71 @@ hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uin
       hope::launch_plane_sum(static_cast<float*>(out), p.planes, p.plane_stride, p.n_sel - 1, n_elem, s));
 }
 
+hope_status_t scan_forward(const hope_fmap_t* x, const float* init_memories, uint32_t dirs,
+                           int32_t chunk, void* out, const hope_scan2d_opts_t* opts,
+                           RoutePlanes* defer) {
+  if (defer) *defer = RoutePlanes{nullptr, 0, 0};
+  hope_scan2d_opts_t o;
+  if (opts) {
+    o = *opts;
+  } else {
+    hope_scan2d_default_opts(&o);
+  }
+  ChainParams p;
+  int d = 0;
+  const hope_status_t st = plan_forward(x, init_memories, dirs, chunk, out, o, true, p, d);
+  if (st != HOPE_OK) return st;
+  const bool out_bf16 = o.out_dtype == HOPE_BF16;
+  attach_planes(p, out, static_cast<float*>(o.workspace), out_bf16);
+  return enqueue_forward(p, d, out, out_bf16, o.stream, o.scan_begin, o.scan_end, defer);
+}
+
+// Images per launch of the no-allocation forward: the most whose route planes fit in
+// scratch_floats (all of them when no plane is needed); 0 when one image's do not.
+int32_t images_per_slice(const hope_fmap_t* x, uint32_t dirs, int32_t out_dtype, int64_t scratch_floats) {
+  const int n_planes = planes_for(dirs, out_dtype);
+  if (n_planes <= 0) return x->B;
+  const int64_t per_image = (int64_t)x->H * x->W * x->D;
+  const int64_t cap = scratch_floats / n_planes;  // floats per plane, padding included
+  int64_t b = std::min<int64_t>(cap / per_image, x->B);
+  while (b > 0 && plane_stride_elems(b * per_image) > cap) --b;
+  return (int32_t)b;
+}
+
 }  // namespace hope
+
+// ---- the entry point that allocates nothing ---------------------------------------------
+// Route planes in a file-scope device array of fixed size: each GPU the library runs on holds
+// its own copy until the process ends.  In host code the array's name is not a device
+// address: host code uses only the address hipGetSymbolAddress returns on each device.
+constexpr size_t kScratchBytes = HOPE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once per device
+// (with that device current) and kept.
+hipError_t scratch_of_current_device(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(addr);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -333,6 +404,51 @@ hope_status_t hope_scan2d_forward(const hope_fmap_t* x, const float* init_memori
                                   uint32_t dirs, int32_t chunk, void* out,
                                   const hope_scan2d_opts_t* opts) {
   return hope::scan_forward(x, init_memories, dirs, chunk, out, opts, nullptr);
+}
+
+hope_status_t hope_scan2d_forward_noalloc(const hope_fmap_t* x, const float* init_memories,
+                                          uint32_t dirs, int32_t chunk, void* out,
+                                          const hope_scan2d_opts_t* opts) {
+  hope_scan2d_opts_t o;
+  if (opts) {
+    o = *opts;
+  } else {
+    hope_scan2d_default_opts(&o);
+  }
+  if (o.workspace || o.workspace_bytes) return HOPE_ERR_INVALID_ARG;  // the scratch array serves
+  hope::ChainParams p;
+  int d = 0;
+  hope_status_t st = hope::plan_forward(x, init_memories, dirs, chunk, out, o, false, p, d);
+  if (st != HOPE_OK) return st;
+  const int64_t scratch_floats = (int64_t)(kScratchBytes / sizeof(float));
+  const int32_t per_slice = hope::images_per_slice(x, dirs, o.out_dtype, scratch_floats);
+  if (per_slice <= 0) return HOPE_ERR_WORKSPACE;  // one image's route planes exceed the scratch
+  float* planes = nullptr;
+  if ((st = hip_status(scratch_of_current_device(&planes))) != HOPE_OK) return st;
+
+  // whole images per launch: every per-image pointer moves by the slice's first image
+  const bool out_bf16 = o.out_dtype == HOPE_BF16;
+  const int64_t map_elems = (int64_t)x->H * x->W * x->D;
+  const int64_t state_floats = 4LL * d * d + 2LL * d;
+  const int64_t per_image_state = 4LL * x->n_heads * state_floats;
+  hipStream_t s = o.stream;
+  if (o.scan_begin && (st = hip_status(hipEventRecord(o.scan_begin, s))) != HOPE_OK) return st;
+  for (int32_t b0 = 0; b0 < x->B; b0 += per_slice) {
+    const int32_t nb = std::min(per_slice, x->B - b0);
+    hope::ChainParams q = p;
+    q.B = nb;
+    q.x = static_cast<const char*>(p.x) + b0 * map_elems * (p.x_bf16 ? 2 : 4);
+    if (p.init_per_image) q.init = p.init + b0 * per_image_state;
+    if (p.final_mem) q.final_mem = p.final_mem + b0 * per_image_state;
+    if (p.steps) q.steps = p.steps + b0 * 4LL * x->n_heads * x->H * x->W;
+    if (p.queries) q.queries = static_cast<const char*>(p.queries) + b0 * map_elems * (p.queries_bf16 ? 2 : 4);
+    void* out_b = static_cast<char*>(out) + b0 * map_elems * (out_bf16 ? 2 : 4);
+    hope::attach_planes(q, out_b, planes, out_bf16);
+    const bool last = b0 + nb >= x->B;
+    st = hope::enqueue_forward(q, d, out_b, out_bf16, s, nullptr, last ? o.scan_end : nullptr, nullptr);
+    if (st != HOPE_OK) return st;
+  }
+  return HOPE_OK;
 }
 
 size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,

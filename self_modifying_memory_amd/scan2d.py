@@ -208,7 +208,7 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
                         injection: str = "soft", spectral: str = "clamp", frozen=(),
                         no_dgd: bool = False, shared_init: bool = False,
                         queries: torch.Tensor | None = None, mem_chunk: int = 0,
-                        step_map: torch.Tensor | None = None) -> torch.Tensor:
+                        step_map: torch.Tensor | None = None, _noalloc: bool = False) -> torch.Tensor:
     """Run the four-direction scan; returns ``out`` ([B, H, W, D] float32, or bfloat16
     when a bfloat16 ``out`` is passed: the fp32 route sum rounded once).
 
@@ -241,7 +241,7 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
     _require_device(out, "out")
     if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != tuple(x.shape):
         raise ValueError("out must be float32 or bfloat16 with the shape of x")
-    if workspace is None:
+    if workspace is None and not _noalloc:
         workspace = alloc_workspace(x, n_heads, dirs, chunk, out.dtype)
         _keep_for_stream(workspace, stream)
     fm = make_fmap(x, n_heads)
@@ -256,11 +256,27 @@ def hope_scan2d_forward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: i
         if not begin.cuda_event or not end.cuda_event:
             raise ValueError("scan_events must have been recorded once before use")
         opts.scan_begin, opts.scan_end = begin.cuda_event, end.cuda_event
-    st = lib.hope_scan2d_forward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
-                                 out.data_ptr(), ctypes.byref(opts))
+    entry = lib.hope_scan2d_forward_noalloc if _noalloc else lib.hope_scan2d_forward
+    st = entry(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk, out.data_ptr(), ctypes.byref(opts))
     if st != N.HOPE_OK:
-        raise HopeError(st, "hope_scan2d_forward")
+        raise HopeError(st, "hope_scan2d_forward_noalloc" if _noalloc else "hope_scan2d_forward")
     return out
+
+
+def hope_scan2d_forward_noalloc(x: torch.Tensor, init_memories: torch.Tensor, n_heads: int,
+                                dirs: int = 15, chunk: int = 0, out: torch.Tensor | None = None,
+                                **kwargs) -> torch.Tensor:
+    """hope_scan2d_forward through the entry point that allocates nothing: the route planes
+    live in the library's own per-GPU device array (HOPE_NOALLOC_SCRATCH_BYTES), the batch
+    runs in slices of whole images that fit it.  ``out`` must be given (this wrapper
+    allocates nothing either); the other keyword arguments are those of hope_scan2d_forward
+    except ``workspace``.  Calls that overlap in time on one GPU race on the scratch array."""
+    if out is None:
+        raise ValueError("out must be given: the no-allocation entry point allocates nothing")
+    if kwargs.get("workspace") is not None:
+        raise ValueError("the no-allocation entry point takes no workspace")
+    kwargs.pop("workspace", None)
+    return hope_scan2d_forward(x, init_memories, n_heads, dirs, chunk, out, _noalloc=True, **kwargs)
 
 
 def hope_scan2d_backward_workspace_size(x: torch.Tensor, n_heads: int, dirs: int = 15,

@@ -40,7 +40,7 @@ def call(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, out=FAKE + (2 << 30), 
 def test_every_declared_function_is_exported(lib):
     names = N.header_functions()
     assert "hope_scan2d_forward" in names and "hope_scan2d_backward" in names
-    assert "hope_block_forward" in names and "hope_block_workspace_size" in names and len(names) == 12
+    assert "hope_block_forward" in names and "hope_block_workspace_size" in names and len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
 
@@ -312,3 +312,34 @@ def test_block_workspace_size_and_errors(lib):
     # short workspace
     assert lib.hope_block_forward(FAKE, 1, 4, 4, 128, 64, 2, 512, 0, ctypes.byref(w), FAKE + (1 << 30),
                                   FAKE + (2 << 30), 256, None) == N.HOPE_ERR_WORKSPACE
+
+
+def test_noalloc_entry_errors(lib):
+    # the entry point that allocates nothing: every check before anything is enqueued (no
+    # device is touched for these: the scratch array is looked up only after them)
+    x = fmap(B=2, H=4, W=5, D=32, nh=1)
+    assert lib.hope_scan2d_forward_noalloc(ctypes.byref(x), FAKE + (1 << 30), 15, 0, FAKE + (2 << 30),
+                                           ctypes.byref(opts(lib, workspace=FAKE + (4 << 30),
+                                                             workspace_bytes=1 << 20))) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_scan2d_forward_noalloc(ctypes.byref(x), FAKE + (1 << 30), 0, 0, FAKE + (2 << 30),
+                                           None) == N.HOPE_ERR_INVALID_ARG
+    assert lib.hope_scan2d_forward_noalloc(ctypes.byref(fmap(D=8, nh=1)), FAKE + (1 << 30), 15, 0,
+                                           FAKE + (2 << 30), None) == N.HOPE_ERR_UNSUPPORTED
+    # one image's three fp32 route planes (256 x 256 x 128 x 4 bytes each) exceed the 64 MiB
+    big = fmap(B=1, H=256, W=256, D=128, nh=2, data=FAKE)
+    assert 3 * 256 * 256 * 128 * 4 > N.HOPE_NOALLOC_SCRATCH_BYTES
+    assert lib.hope_scan2d_forward_noalloc(ctypes.byref(big), FAKE + (1 << 33), 15, 0, FAKE + (1 << 34),
+                                           None) == N.HOPE_ERR_WORKSPACE
+    # header constant and binding agree
+    text = open(N.HEADER_PATH).read()
+    assert "#define HOPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+
+
+def test_kernel_name_query(lib):
+    def name(x, dirs=15, chunk=0, o=None):
+        return lib.hope_scan2d_kernel_name(ctypes.byref(x), dirs, chunk,
+                                           ctypes.byref(o) if o is not None else None).decode()
+    assert name(fmap(B=128, H=14, W=14, D=384, nh=6, dtype=N.HOPE_BF16)) == "chain_mfma_kernel"
+    assert name(fmap(B=1, H=8, W=8, D=16, nh=1, dtype=N.HOPE_F32)) == "chain_kernel"
+    assert name(fmap(D=8, nh=1)) == ""                       # d = 8: rejected by the forward
+    assert name(fmap(), dirs=0) == ""
