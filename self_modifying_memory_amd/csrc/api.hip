@@ -154,12 +154,17 @@ bool backward_opts_supported(const hope_scan2d_opts_t& o) {
 
 namespace hope {
 
+// bf16 maps: the chunk-parallel kernel at d = 16 and 32 (boundary readout, one chunk
+// length), the register-resident block kernel for the rest of d = 32 and for d = 64 with
+// chunks of at most 16 tokens; everything else on the fp32 kernel
 ScanPath select_scan_path(const ChainParams& p, int d) {
+  if (chunk_path_supported(p, d)) return kPathChunk;
   return mfma_path_supported(p, d) ? kPathMfma : kPathChain;
 }
 
 const char* scan_path_kernel(ScanPath path) {
   switch (path) {
+    case kPathChunk: return "chain_chunk_kernel";
     case kPathMfma: return "chain_mfma_kernel";
     case kPathChain: return "chain_kernel";
   }
@@ -168,6 +173,7 @@ const char* scan_path_kernel(ScanPath path) {
 
 hipError_t launch_scan(const ChainParams& p, int d, hipStream_t s) {
   switch (select_scan_path(p, d)) {
+    case kPathChunk: return launch_chain_chunk(p, d, s);
     case kPathMfma: return launch_chain_mfma(p, d, s);
     case kPathChain: return launch_chain(p, d, s);
   }

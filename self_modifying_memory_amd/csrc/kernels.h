@@ -82,13 +82,20 @@ bool backward_wy_supported(const BackParams& p, int d);
 hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream);
 
 // The scan kernel a forward call launches (host-side dispatch, api.hip).
-enum ScanPath { kPathChain = 0, kPathMfma = 1 };
+enum ScanPath { kPathChain = 0, kPathMfma = 1, kPathChunk = 2 };
 ScanPath select_scan_path(const ChainParams& p, int d);
 const char* scan_path_kernel(ScanPath path);
 hipError_t launch_scan(const ChainParams& p, int d, hipStream_t stream);
 
 // fp32 VALU kernel: any supported head dimension and dtype (exact fp32 arithmetic).
 hipError_t launch_chain(const ChainParams& p, int d, hipStream_t stream);
+
+// Chunk-parallel MFMA kernel for bf16 maps at d = 16 or 32 (any chunk length; boundary
+// readout, one chunk length).
+bool chunk_path_supported(const ChainParams& p, int d);
+hipError_t launch_chain_chunk(const ChainParams& p, int d, hipStream_t stream);
+// true when the call asks for any variant that only the variant instantiations implement
+bool needs_variants(const ChainParams& p);
 
 // MFMA kernel for bf16 maps (d = 32, or d = 64 with every chunk <= 16 tokens).
 bool mfma_path_supported(const ChainParams& p, int d);

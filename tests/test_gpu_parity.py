@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from _parity import TOL, check_final, check_out, run_gpu
+from _parity import TOL, check_final, check_out, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -138,7 +138,7 @@ BF16_OUT = [
 def test_bf16_out_is_the_fp32_sum_rounded_once(case):
     import torch
     from self_modifying_memory_amd.scan2d import hope_scan2d_forward
-    from _parity import to_device
+
     B, H, W, D, nh, dt, dirs, chunk = case
     print("case", case, flush=True)
     inp = wl.draw(B, H, W, D, nh, seed=5000 + H * 37 + W, dtype=dt, live=True)
@@ -201,12 +201,24 @@ def test_running_readout_matches_oracle(case):
 @pytest.mark.parametrize("shape", [(1, 5, 6, 32, 1, "f32"), (2, 5, 7, 64, 2, "bf16"),
                                    (1, 6, 6, 128, 2, "bf16")])
 def test_running_readout_is_boundary_at_chunk_one(shape):
+    # At one token per chunk the running memory is the chunk-start memory: bit for bit when
+    # both readouts run on the same kernel, within the fp32 bar when the boundary readout
+    # runs on the chunk-parallel kernel and the running one on the register-resident kernel
+    from self_modifying_memory_amd.scan2d import hope_scan2d_kernel_name
     B, H, W, D, nh, dt = shape
     print("shape", shape, flush=True)
     inp = wl.draw(B, H, W, D, nh, seed=77, dtype=dt, live=True)
+    x, _ = to_device(inp, dt)
+    same = hope_scan2d_kernel_name(x, nh, 15, 1) == hope_scan2d_kernel_name(x, nh, 15, 1, readout="running")
     ob, fb = run_gpu(inp, nh, dt, 15, 1)
     orun, frun = run_gpu(inp, nh, dt, 15, 1, readout="running")
-    assert np.array_equal(ob, orun) and np.array_equal(fb, frun)
+    if same:
+        assert np.array_equal(ob, orun) and np.array_equal(fb, frun)
+    else:
+        e = float(np.max(np.abs(ob - orun)) / np.max(np.abs(orun)))
+        ef = float(np.max(np.abs(fb - frun)) / np.max(np.abs(frun)))
+        print(f"  boundary vs running: out {e:.2e} final {ef:.2e}", flush=True)
+        assert e <= TOL["f32"] and ef <= TOL["f32"]
 
 
 def test_running_readout_full_size_stage3_sampled():

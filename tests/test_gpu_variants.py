@@ -1,5 +1,5 @@
 """GPU parity of the VisionHOPE variants (Sec. 3.5 ablations, Eq. 26 direction scales,
-App. B.5 skip) through the C ABI against the fp64 oracle, on both scan kernels.
+App. B.5 skip) through the C ABI against the fp64 oracle, on the three scan kernels.
 
 Counters of the step controls are integers decided by floating point: the GPU decides in
 fp32, the oracle in fp64, and the quantities compared (eta and the two limits) come from
@@ -19,8 +19,10 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     "f32_d16": (2, 4, 6, 32, 2, "f32", 0),      # fp32 kernel
     "f32_d64": (1, 6, 9, 64, 1, "f32", 4),      # fp32 kernel, ragged chunks
-    "bf16_d32": (2, 5, 37, 96, 3, "bf16", 0),   # MFMA kernel, multi-block chunks
-    "bf16_d64": (2, 6, 9, 128, 2, "bf16", 0),   # MFMA kernel, d = 64
+    "bf16_d32": (2, 5, 37, 96, 3, "bf16", 0),   # chunk-parallel kernel, three token tiles
+    "bf16_d64": (2, 6, 9, 128, 2, "bf16", 0),   # register-resident MFMA kernel, d = 64
+    "bf16_d16": (2, 5, 20, 48, 3, "bf16", 0),   # chunk-parallel kernel, d = 16
+    "bf16_d32_seg": (1, 3, 100, 32, 1, "bf16", 0),  # row chunks of 100: two segments of the chunk kernel
 }
 FROZEN = {"kv": ("k", "v"), "dynamics": ("eta", "alpha"), "q": ("q",)}
 
