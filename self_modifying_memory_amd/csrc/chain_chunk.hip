@@ -1,5 +1,5 @@
 // Chunk-parallel recurrence on MFMA: one (image, head, route) chain per workgroup, for bf16
-// feature maps at head dimension 16 or 32 and chunks of any length (gfx950).
+// feature maps at head dimension 16, 32 or 64 and chunks of any length (gfx950).
 //
 // Method ("VisionHOPE: Visual Backbones as Self-Modifying Learning Systems"):
 //   Sec. 2.1.3 Eq. 15-16  projections k, v, q, eta, alpha and the readout M_mem q come from
@@ -9,8 +9,8 @@
 //   App. B.4 Eq. 45-47    all six memories follow one gain, G_t = alpha_t G_{t-1} + w_t k_t^T
 //                         with w_t = -step_t (G_{t-1} k_t + delta_t).
 //
-// A chunk is processed in segments of up to SEG tokens (64 at d = 32, 128 at d = 16; one
-// segment when the chunk fits).  With P(a, b) = prod_{a <= s < b} alpha_s over the segment's
+// A chunk is processed in segments of up to SEG tokens (16 or 64 at d = 16, 64 at d = 32, 32
+// at d = 64; one segment when the chunk fits).  With P(a, b) = prod_{a <= s < b} alpha_s over the segment's
 // tokens and G_s the chunk gain at the segment's start (the identity for the first segment),
 // the segment's write vectors solve the unit lower-triangular system
 //   (I + L) W = R,   L[t][j] = step_t P(j+1, t) (k_j . k_t)  for j < t,
@@ -42,7 +42,8 @@
 namespace hope {
 namespace {
 
-// Contraction over the head dimension: one 16x16x32 step at d = 32, one 16x16x16 at d = 16.
+// Contraction over the head dimension: one 16x16x16 step at d = 16, one 16x16x32 step at
+// d = 32, two at d = 64.
 template <int D>
 struct HeadOps;
 template <>
@@ -52,6 +53,27 @@ struct HeadOps<32> {
   static __device__ __forceinline__ void split(const f32x4* s, V& hi, V& lo) { split8(s[0], s[1], hi, lo); }
   static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) { return mma32(a, b, c); }
   static __device__ __forceinline__ f32x4 mma3(V ah, V al, V bh, V bl, f32x4 c) { return mma32x3(ah, al, bh, bl, c); }
+};
+// d = 64: two 32-deep steps (column tiles 0-1, then 2-3)
+struct Bf16x8x2 {
+  bf16x8 s[2];
+};
+template <>
+struct HeadOps<64> {
+  typedef Bf16x8x2 V;
+  static __device__ __forceinline__ V row(const unsigned short* r, int g) {
+    return V{{load_row_pair_bf16(r, 0, g), load_row_pair_bf16(r, 1, g)}};
+  }
+  static __device__ __forceinline__ void split(const f32x4* s, V& hi, V& lo) {
+    split8(s[0], s[1], hi.s[0], lo.s[0]);
+    split8(s[2], s[3], hi.s[1], lo.s[1]);
+  }
+  static __device__ __forceinline__ f32x4 mma(V a, V b, f32x4 c) {
+    return mma32(a.s[1], b.s[1], mma32(a.s[0], b.s[0], c));
+  }
+  static __device__ __forceinline__ f32x4 mma3(V ah, V al, V bh, V bl, f32x4 c) {
+    return mma32x3(ah.s[1], al.s[1], bh.s[1], bl.s[1], mma32x3(ah.s[0], al.s[0], bh.s[0], bl.s[0], c));
+  }
 };
 template <>
 struct HeadOps<16> {
@@ -753,7 +775,9 @@ ChunkLds launch_lds(const ChainParams& p, int d, int seg, bool exchange, int& TT
   const int cmax = longest_chunk(p);
   TT = (std::min(cmax, seg) + 15) / 16;
   multi = cmax > seg ? 1 : 0;
-  return d == 16 ? chunk_lds<16>(TT, multi != 0, exchange) : chunk_lds<32>(TT, multi != 0, exchange);
+  if (d == 16) return chunk_lds<16>(TT, multi != 0, exchange);
+  if (d == 32) return chunk_lds<32>(TT, multi != 0, exchange);
+  return chunk_lds<64>(TT, multi != 0, exchange);
 }
 
 constexpr int kChunkLdsMax = 150 * 1024;  // dynamic LDS of one workgroup, at most
@@ -789,8 +813,9 @@ hipError_t launch_v(const ChainParams& p, hipStream_t stream) {
 }
 
 // Segment length of a launch: one 16-token tile at d = 16 when every chunk fits in it (fewer
-// registers, more chains per CU), else 64 tokens
+// registers, more chains per CU), 32 tokens at d = 64 (LDS), else 64 tokens
 int segment_of(const ChainParams& p, int d) {
+  if (d == 64) return 32;
   return (d == 16 && longest_chunk(p) <= 16) ? 16 : 64;
 }
 
@@ -804,10 +829,11 @@ int waves_of_d32(const ChainParams& p) {
 
 bool chunk_path_supported(const ChainParams& p, int d) {
   if (!p.x_bf16 || p.mem_chunk > 0 || p.readout) return false;
-  if (d != 16 && d != 32) return false;
-  // d = 32 with chunks of at most 32 tokens: the register-resident block kernel keeps four
-  // chains on a CU and is faster there
+  if (d != 16 && d != 32 && d != 64) return false;
+  // d = 32 with chunks of at most 32 tokens, d = 64 with chunks of at most 16: the
+  // register-resident block kernel is faster there
   if (d == 32 && longest_chunk(p) <= 32) return false;
+  if (d == 64 && longest_chunk(p) <= 16) return false;
   int TT = 0, multi = 0;
   return launch_lds(p, d, segment_of(p, d), d == 32, TT, multi).total <= kChunkLdsMax;
 }
@@ -817,6 +843,7 @@ hipError_t launch_chain_chunk(const ChainParams& p, int d, hipStream_t stream) {
     return segment_of(p, d) == 16 ? launch_v<16, 16, 4>(p, stream) : launch_v<16, 64, 4>(p, stream);
   }
   if (d == 32) return waves_of_d32(p) == 16 ? launch_v<32, 64, 16>(p, stream) : launch_v<32, 64, 8>(p, stream);
+  if (d == 64) return launch_v<64, 32, 16>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,4 +1,4 @@
-"""GPU parity of the chunk-parallel kernel (chain_chunk_kernel: bf16 maps, d = 16 and 32,
+"""GPU parity of the chunk-parallel kernel (chain_chunk_kernel: bf16 maps, d = 16, 32, 64,
 boundary readout) against the fp64 oracle, through the C ABI: token-tile counts from one to
 a full segment, ragged tiles and chunks, chunks that span several segments (the gain carried
 between segments), one-token chunks, active step controls and the VisionHOPE gate maps.
@@ -36,6 +36,11 @@ CASES = [
     (2, 6, 30, 64, 2, 15, 0,
      dict(eta_map="softplus", eta_scale=0.025, alpha_bias=math.log(9.0))),  # VisionHOPE gates
     (1, 4, 140, 16, 1, 3, 0, dict(alpha_bias=8.0)),  # long memory, two d = 16 segments
+    (1, 3, 20, 64, 1, 15, 0, {}),           # d = 64, row chunks of 20: one segment of two tiles
+    (1, 2, 40, 64, 1, 3, 0, {}),            # d = 64, row chunks of 40: segments of 32 and 8
+    (2, 5, 33, 128, 2, 15, 0, {}),          # d = 64, two heads, a segment of 32 and one of 1
+    (1, 6, 9, 64, 1, 15, 17, {}),           # d = 64, chunk 17 over 54 tokens
+    (1, 4, 28, 64, 1, 15, 0, dict(eta_scale=50.0, alpha_bias=-3.0)),  # d = 64, clamps bind
 ]
 
 
@@ -52,12 +57,14 @@ def test_chunk_kernel_matches_oracle(case):
     print("case", _id(case), flush=True)
     inp = wl.draw(B, H, W, D, nh, seed=6100 + B * 100 + H * 37 + W, dtype="bf16", live=True)
     x, _ = to_device(inp, "bf16")
-    # d = 16 always runs on this kernel; d = 32 when some chunk is longer than 32 tokens
-    # (shorter ones go to the register-resident kernel, checked here as well)
+    # d = 16 always runs on this kernel; d = 32 when some chunk is longer than 32 tokens and
+    # d = 64 when some chunk is longer than 16 (shorter ones go to the register-resident
+    # kernel, checked here as well)
     d = D // nh
     routes = [r for r in range(4) if (dirs >> r) & 1]
     longest = max(min(chunk or (W if r < 2 else H), H * W) for r in routes)
-    want = "chain_chunk_kernel" if d == 16 or longest > 32 else "chain_mfma_kernel"
+    on_chunk = d == 16 or (d == 32 and longest > 32) or (d == 64 and longest > 16)
+    want = "chain_chunk_kernel" if on_chunk else "chain_mfma_kernel"
     assert hope_scan2d_kernel_name(x, nh, dirs, chunk) == want
     out, fin = run_gpu(inp, nh, "bf16", dirs, chunk, **extra)
     ref_out, ref_fin = oracle.scan2d(inp["x"], inp["init"], nh, dirs=dirs, chunk=chunk, **extra)

@@ -37,7 +37,7 @@ SMALL = [
     # bf16 maps with d = 32 / 64 run on the MFMA kernel
     (2, 6, 9, 128, 2, "bf16", 15, 0, True, {}),         # d = 64, row chunks 9, column chunks 6
     (1, 16, 16, 64, 1, "bf16", 15, 0, True, {}),        # d = 64, chunks of exactly 16
-    (1, 20, 3, 64, 1, "bf16", 15, 0, True, {}),         # d = 64, column chunks 20 (> 16): fp32 kernel
+    (1, 20, 3, 64, 1, "bf16", 15, 0, True, {}),         # d = 64, column chunks 20 (> 16): chunk-parallel kernel
     (2, 5, 37, 96, 3, "bf16", 15, 0, True, {}),         # d = 32, row chunks 37: three token blocks
     (1, 9, 9, 32, 1, "bf16", 15, 33, True, {}),         # d = 32, chunk 33 over 81 tokens
     (2, 7, 7, 64, 2, "bf16", 8, 0, True, {}),           # d = 32, single route (no workspace)
@@ -178,7 +178,7 @@ RUNNING = [
     (2, 5, 37, 96, 3, "bf16", 15, 0, {}),          # MFMA d = 32, chunks of 37: three blocks
     (2, 6, 9, 128, 2, "bf16", 15, 0, {}),          # MFMA d = 64
     (1, 16, 16, 64, 1, "bf16", 15, 0, {}),         # MFMA d = 64, chunks of exactly 16
-    (1, 20, 3, 64, 1, "bf16", 15, 0, {}),          # d = 64, column chunks of 20: fp32 kernel
+    (1, 20, 3, 64, 1, "bf16", 15, 0, {}),          # d = 64, column chunks of 20: running readout on the fp32 kernel
     (1, 5, 5, 32, 1, "bf16", 15, 0, dict(eta_scale=50.0, alpha_bias=-3.0)),  # clamps active
     (2, 5, 6, 64, 1, "bf16", 15, 0,
      dict(eta_map="softplus", eta_scale=0.025, alpha_bias=math.log(9.0))),

@@ -23,6 +23,7 @@ SHAPES = {
     "bf16_d64": (2, 6, 9, 128, 2, "bf16", 0),   # register-resident MFMA kernel, d = 64
     "bf16_d16": (2, 5, 20, 48, 3, "bf16", 0),   # chunk-parallel kernel, d = 16
     "bf16_d32_seg": (1, 3, 100, 32, 1, "bf16", 0),  # row chunks of 100: two segments of the chunk kernel
+    "bf16_d64_seg": (1, 3, 40, 64, 1, "bf16", 0),   # d = 64, row chunks of 40: two segments
 }
 FROZEN = {"kv": ("k", "v"), "dynamics": ("eta", "alpha"), "q": ("q",)}
 
