@@ -31,8 +31,9 @@ bool sizes_ok(int32_t B, int32_t H, int32_t W, int32_t D, int32_t Dm, int32_t n_
   if (D % 16 || Dm % 16 || ffn_dim % 16 || Dm % n_heads) return false;
   if (D > 1024 || Dm > 1024 || ffn_dim > 16384) return false;
   const int32_t cmax = D > Dm ? D : Dm;
-  if ((int64_t)B * H * ((W + 3) / 4) * (cmax / 4) >= (int64_t)1 << 31) return false;  // stencil indexing
-  if ((int64_t)B * H * W > (int64_t)1 << 31) return false;
+  // (64-bit throughout: each factor is below 2^31, so no product of two overflows)
+  if ((int64_t)B * H > ((int64_t)1 << 31) || (int64_t)B * H * W > ((int64_t)1 << 31)) return false;
+  if ((int64_t)B * H * (((int64_t)W + 3) / 4) * (cmax / 4) >= (int64_t)1 << 31) return false;  // stencil indexing
   return true;
 }
 
