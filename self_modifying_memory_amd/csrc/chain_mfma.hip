@@ -137,7 +137,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   constexpr int MTW = MT / kWaves;                 // tiles per wave (round robin)
   static_assert(MT % kWaves == 0, "every wave holds the same number of state-row tiles");
   constexpr int TR = 4 * D;                        // first tail row: m_eta, then m_alpha
-  constexpr int LD = D + 4;                        // fp32 stride of token-major tiles
+  // fp32 stride of token-major tiles: at d = 64, 72 floats (72 = 8 mod 32) puts the four
+  // rows a quad reads in the solve (t = 4i + q) on disjoint banks; d = 32 keeps D + 4 (its
+  // LDS budget holds four chains on a CU)
+  constexpr int LD = D == 64 ? D + 8 : D + 4;
   constexpr int XLD = D + 8;                       // bf16 stride of the token block
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
   constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
