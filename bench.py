@@ -52,7 +52,7 @@ PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
 PEAK_FP32 = 157.3e12    # fp32 matrix / vector, FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "scan_traffic.json")
-KERNEL_SOURCES = ["chain_mfma.hip", "chain_kernel.hip", "device_common.h", "kernels.h"]
+KERNEL_SOURCES = ["chain_mfma.hip", "chain_chunk.hip", "chain_kernel.hip", "mfma_ops.h", "device_common.h", "kernels.h"]
 METRIC = wl_metric = "scan tokens/s (positions×dirs) for 4-dir Hope memory scan; % MFMA/HBM peak"
 
 
