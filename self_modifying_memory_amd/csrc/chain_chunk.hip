@@ -292,7 +292,11 @@ __global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, in
     for (int n = 0; n < NT; ++n) Acc[n] = (RW == 1 || u == 0) ? St[n] : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int a0 = s0; a0 < s1; a0 += SEG) {
       const int ns = min(SEG, s1 - a0);   // tokens in this segment
-      const int TS = (ns + 15) >> 4;      // token tiles in this segment
+      // Every segment runs TT token tiles, the launch's maximum: tokens from ns on are
+      // padding (no key, no write, unit retention), so a shorter segment costs the work of a
+      // full one, and every tile loop below has a compile-time trip count (straight-line
+      // code whose LDS reads the compiler can issue ahead of their uses)
+      constexpr int TS = TT;
       const bool first = a0 == s0;
       const bool last = a0 + SEG >= s1;
       // lane indices re-derived through an opaque copy each segment: the address arithmetic
@@ -517,9 +521,17 @@ __global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, in
             float uu[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) uu[i] = (4 * i + qd == col) ? 1.f : 0.f;
+            // coefficient rows are read kPf steps ahead of their use, so that the steps wait
+            // on one another rather than on LDS (all of them at d = 32, whose launches are
+            // latency-bound; four elsewhere, within the register budget)
+            constexpr int kPf = D == 32 ? 15 : 4;
+            f32x4 cfs[kPf];
+#pragma unroll
+            for (int j = 0; j < kPf; ++j) cfs[j] = *reinterpret_cast<const f32x4*>(LTw + j * LTLD + 4 * qd);
 #pragma unroll
             for (int j = 0; j < 15; ++j) {
-              const f32x4 cf = *reinterpret_cast<const f32x4*>(LTw + j * LTLD + 4 * qd);
+              const f32x4 cf = cfs[j % kPf];
+              if (j + kPf < 15) cfs[j % kPf] = *reinterpret_cast<const f32x4*>(LTw + (j + kPf) * LTLD + 4 * qd);
               const float uj = quad_bcast(uu[j >> 2], j & 3);
 #pragma unroll
               for (int i = j >> 2; i < 4; ++i) {
@@ -554,19 +566,30 @@ __global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, in
           for (int e = 0; e < NT; ++e) gv[e] = *reinterpret_cast<const f32x4*>(Gs + (16 * n + c16) * LD + 16 * e + 4 * g);
           Ops::split(gv, gh, gl);
         }
+        // (the wave-uniform choice is taken once, outside the loops, so that each form is
+        // straight-line code)
+        if (gk_mfma) {
 #pragma unroll
-        for (int tau = 0; tau < TMAX; ++tau) {
-          if (tau >= TS) break;
-          f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-          if (gk_mfma) {
+          for (int tau = 0; tau < TMAX; ++tau) {
+            if (tau >= TS) break;
             const V kh = Ops::row(KH + (16 * tau + c16) * XLD, g), kl = Ops::row(KL + (16 * tau + c16) * XLD, g);
-            gk = Ops::mma3(kh, kl, gh, gl, gk);
-          }
+            const f32x4 gk = Ops::mma3(kh, kl, gh, gl, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * tau + 4 * g + i;
-            const float kt = v_nodgd ? 0.f : gk_mfma ? gk[i] : Ks[t * LD + 16 * n + c16];
-            R[tau][i] = -stp[t] * fmaf(P0s[t], kt, Dls[t * LD + 16 * n + c16]);
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * tau + 4 * g + i;
+              R[tau][i] = -stp[t] * fmaf(P0s[t], gk[i], Dls[t * LD + 16 * n + c16]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int tau = 0; tau < TMAX; ++tau) {
+            if (tau >= TS) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = 16 * tau + 4 * g + i;
+              const float kt = v_nodgd ? 0.f : Ks[t * LD + 16 * n + c16];
+              R[tau][i] = -stp[t] * fmaf(P0s[t], kt, Dls[t * LD + 16 * n + c16]);
+            }
           }
         }
         // W_J = T_JJ R_J, then R_I -= L_IJ W_J for the later tiles; W_J replaces R_J
