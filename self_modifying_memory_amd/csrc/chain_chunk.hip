@@ -709,9 +709,9 @@ __global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, in
         if (c16 < 2) *reinterpret_cast<f32x4*>(Tb[cur ^ 1] + c16 * D + 16 * w + 4 * g) = acc;
       }
       // gain of the chunk so far, for the next segment: G <- cseg G + Ub^T K, tiles of 16 x 16
-      // on the waves between the readout and solve waves
+      // dealt from wave NT on, after the waves that carry the gate rows above
       if (multi && !last && !v_nodgd) {
-        for (int tile = w; tile < NT * NT; tile += NW) {
+        for (int tile = (w + NW - NT) % NW; tile < NT * NT; tile += NW) {
           const int ti = tile / NT, tn = tile % NT;
           f32x4 acc;
 #pragma unroll
