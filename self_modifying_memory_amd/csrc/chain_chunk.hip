@@ -151,8 +151,10 @@ __host__ __device__ constexpr ChunkLds chunk_lds(int TT, bool multi, bool exchan
   return L;
 }
 
+// The one-tile d = 16 launches (the block's operator: thousands of four-wave chains) are
+// throughput-bound: they are held to 72 registers, seven chains per CU
 template <int D, int SEG_, int NW_, int TT, bool VAR>
-__global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, int multi) {
+__global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void chain_chunk_kernel(ChainParams p, int multi) {
   typedef ChunkShape<D, SEG_, NW_> S;
   typedef HeadOps<D> Ops;
   typedef typename Ops::V V;
@@ -382,12 +384,34 @@ __global__ __launch_bounds__(64 * NW_) void chain_chunk_kernel(ChainParams p, in
             Sc[32 * TT + t] = pt[3 * D];
             Sc[48 * TT + t] = pt[3 * D + 1];
           }
+          if constexpr (CPL >= 2) {
+            // consecutive components in pairs: one 8-byte store per fp32 row and one 4-byte
+            // store per bf16 row (only the transposed key copy stays 2-byte)
+            typedef float f32x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) {
-            const int col = c16 * CPL + e;
-            const float k0 = live ? kn[e] : 0.f, q0 = live ? qn[e] : 0.f;
+            for (int e = 0; e < CPL; e += 2) {
+              const int col = c16 * CPL + e;
+              const float k0 = live ? kn[e] : 0.f, k1 = live ? kn[e + 1] : 0.f;
+              const float q0 = live ? qn[e] : 0.f, q1 = live ? qn[e + 1] : 0.f;
+              *reinterpret_cast<f32x2v*>(Ks + t * LD + col) = f32x2v{k0, k1};
+              *reinterpret_cast<f32x2v*>(Dls + t * LD + col) = f32x2v{live ? dl[e] : 0.f, live ? dl[e + 1] : 0.f};
+              unsigned kh, kl, qh, ql;
+              split_pair(k0, k1, kh, kl);
+              split_pair(q0, q1, qh, ql);
+              *reinterpret_cast<unsigned*>(KH + t * XLD + col) = kh;
+              *reinterpret_cast<unsigned*>(KL + t * XLD + col) = kl;
+              *reinterpret_cast<unsigned*>(QH + t * XLD + col) = qh;
+              *reinterpret_cast<unsigned*>(QL + t * XLD + col) = ql;
+              KtH[col * KTLD + t] = (unsigned short)kh;
+              KtH[(col + 1) * KTLD + t] = (unsigned short)(kh >> 16);
+              KtL[col * KTLD + t] = (unsigned short)kl;
+              KtL[(col + 1) * KTLD + t] = (unsigned short)(kl >> 16);
+            }
+          } else {
+            const int col = c16;
+            const float k0 = live ? kn[0] : 0.f, q0 = live ? qn[0] : 0.f;
             Ks[t * LD + col] = k0;
-            Dls[t * LD + col] = live ? dl[e] : 0.f;
+            Dls[t * LD + col] = live ? dl[0] : 0.f;
             const __bf16 khv = (__bf16)k0, qhv = (__bf16)q0;
             const __bf16 klv = (__bf16)(k0 - (float)khv), qlv = (__bf16)(q0 - (float)qhv);
             const unsigned short khb = __builtin_bit_cast(unsigned short, khv);
