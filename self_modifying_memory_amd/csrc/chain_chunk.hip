@@ -124,8 +124,10 @@ __host__ __device__ constexpr ChunkLds chunk_lds(int TT, bool multi, bool exchan
   const int nl = TT * (TT + 1) / 2;
   const int pj_bytes = nt * S::PLD * 4, lt_bytes = nl * 64 * 16;
   L.pj = take(pj_bytes > lt_bytes ? pj_bytes : lt_bytes);
-  L.ks = take(nt * S::LD * 4);
-  L.dls = take(nt * S::LD * 4);
+  // normalised keys and delta, column-major (stride nt + 4): the right-hand side reads four
+  // consecutive tokens of a column at once
+  L.ks = take(D * (nt + 4) * 4);
+  L.dls = take(D * (nt + 4) * 4);
   L.kh = take(nt * S::XLD * 2);
   L.kl = take(nt * S::XLD * 2);
   L.qh = take(nt * S::XLD * 2);
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
   float* const Tt = reinterpret_cast<float*>(lds + Lo.tt);    // prod of alpha over each tile
   float* const LTs = reinterpret_cast<float*>(lds + Lo.lts);
   constexpr int KTLD = Lo.ktld;
+  constexpr int KSLD = 16 * TT + 4;  // fp32 stride of the column-major keys and delta
   // the two gate rows (m_eta, m_alpha): Tb[cur] the chunk-start copy, Tb[cur ^ 1] the running one
   __shared__ __attribute__((aligned(16))) float Tb[2][2 * D];
   __shared__ unsigned int cnt_lds[3];
@@ -393,8 +396,10 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
               const int col = c16 * CPL + e;
               const float k0 = live ? kn[e] : 0.f, k1 = live ? kn[e + 1] : 0.f;
               const float q0 = live ? qn[e] : 0.f, q1 = live ? qn[e + 1] : 0.f;
-              *reinterpret_cast<f32x2v*>(Ks + t * LD + col) = f32x2v{k0, k1};
-              *reinterpret_cast<f32x2v*>(Dls + t * LD + col) = f32x2v{live ? dl[e] : 0.f, live ? dl[e + 1] : 0.f};
+              Ks[col * KSLD + t] = k0;
+              Ks[(col + 1) * KSLD + t] = k1;
+              Dls[col * KSLD + t] = live ? dl[e] : 0.f;
+              Dls[(col + 1) * KSLD + t] = live ? dl[e + 1] : 0.f;
               unsigned kh, kl, qh, ql;
               split_pair(k0, k1, kh, kl);
               split_pair(q0, q1, qh, ql);
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
           } else {
             const int col = c16;
             const float k0 = live ? kn[0] : 0.f, q0 = live ? qn[0] : 0.f;
-            Ks[t * LD + col] = k0;
-            Dls[t * LD + col] = live ? dl[0] : 0.f;
+            Ks[col * KSLD + t] = k0;
+            Dls[col * KSLD + t] = live ? dl[0] : 0.f;
             const __bf16 khv = (__bf16)k0, qhv = (__bf16)q0;
             const __bf16 klv = (__bf16)(k0 - (float)khv), qlv = (__bf16)(q0 - (float)qhv);
             const unsigned short khb = __builtin_bit_cast(unsigned short, khv);
@@ -598,22 +603,22 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
             if (tau >= TS) break;
             const V kh = Ops::row(KH + (16 * tau + c16) * XLD, g), kl = Ops::row(KL + (16 * tau + c16) * XLD, g);
             const f32x4 gk = Ops::mma3(kh, kl, gh, gl, f32x4{0.f, 0.f, 0.f, 0.f});
+            const int t0 = 16 * tau + 4 * g;
+            const f32x4 st4 = *reinterpret_cast<const f32x4*>(stp + t0), p04 = *reinterpret_cast<const f32x4*>(P0s + t0);
+            const f32x4 dv = *reinterpret_cast<const f32x4*>(Dls + (16 * n + c16) * KSLD + t0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 16 * tau + 4 * g + i;
-              R[tau][i] = -stp[t] * fmaf(P0s[t], gk[i], Dls[t * LD + 16 * n + c16]);
-            }
+            for (int i = 0; i < 4; ++i) R[tau][i] = -st4[i] * fmaf(p04[i], gk[i], dv[i]);
           }
         } else {
 #pragma unroll
           for (int tau = 0; tau < TMAX; ++tau) {
             if (tau >= TS) break;
+            const int t0 = 16 * tau + 4 * g;
+            const f32x4 st4 = *reinterpret_cast<const f32x4*>(stp + t0), p04 = *reinterpret_cast<const f32x4*>(P0s + t0);
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(Ks + (16 * n + c16) * KSLD + t0);
+            const f32x4 dv = *reinterpret_cast<const f32x4*>(Dls + (16 * n + c16) * KSLD + t0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int t = 16 * tau + 4 * g + i;
-              const float kt = v_nodgd ? 0.f : Ks[t * LD + 16 * n + c16];
-              R[tau][i] = -stp[t] * fmaf(P0s[t], kt, Dls[t * LD + 16 * n + c16]);
-            }
+            for (int i = 0; i < 4; ++i) R[tau][i] = -st4[i] * fmaf(p04[i], v_nodgd ? 0.f : kv[i], dv[i]);
           }
         }
         // W_J = T_JJ R_J, then R_I -= L_IJ W_J for the later tiles; W_J replaces R_J
