@@ -153,10 +153,12 @@ __host__ __device__ constexpr ChunkLds chunk_lds(int TT, bool multi, bool exchan
   return L;
 }
 
-// The one-tile d = 16 launches (the block's operator: thousands of four-wave chains) are
-// throughput-bound: they are held to 72 registers, seven chains per CU
+// Register budgets of the throughput-bound launches: the one-tile d = 16 launches (the
+// block's operator, thousands of four-wave chains) are held to 72 registers, seven chains per
+// CU; the eight-wave d = 32 launches with up to three token tiles to 128, two chains per CU
+// (four tiles would spill)
 template <int D, int SEG_, int NW_, int TT, bool VAR>
-__global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void chain_chunk_kernel(ChainParams p, int multi) {
+__global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 && NW_ == 8 && TT <= 3) ? 4 : 1) void chain_chunk_kernel(ChainParams p, int multi) {
   typedef ChunkShape<D, SEG_, NW_> S;
   typedef HeadOps<D> Ops;
   typedef typename Ops::V V;
@@ -239,6 +241,11 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
   f32x4 St[NT];    // the chunk-start state S_b of this row tile
   f32x4 Acc[NT];   // S_b G_s, the state after the chunk's earlier segments; with two waves per
                    // row tile each carries its own token tiles' share (the two shares sum to it)
+  // At d = 32 one wave per row tile keeps the two shares apart too (Acc2: the odd token tiles)
+  // and adds them in the same order, so that 8 and 16 waves per chain (chosen by the number
+  // of chains in the call) give bitwise the same result
+  constexpr bool kTwoShares = D == 32 && RW == 1;
+  f32x4 Acc2[kTwoShares ? NT : 1];
   {
     const float* init = p.init + init_offset(p, b, r, h, SS);
     const int row = 16 * m + c16;
@@ -295,6 +302,10 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
     Ops::split(St, Sh, Sl);
 #pragma unroll
     for (int n = 0; n < NT; ++n) Acc[n] = (RW == 1 || u == 0) ? St[n] : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kTwoShares) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) Acc2[kTwoShares ? n : 0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int a0 = s0; a0 < s1; a0 += SEG) {
       const int ns = min(SEG, s1 - a0);   // tokens in this segment
       // Every segment runs TT token tiles, the launch's maximum: tokens from ns on are
@@ -685,13 +696,18 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
       // ---- D: carry  S_b G_e = cseg (S_b G_s) + (S_b Ub^T) K, per token tile ----------
       if (!my_tile_frozen) {
         // this wave's token tiles: tau = u (mod RW)
-        f32x4 acc[NT];
+        f32x4 acc[NT], acc2[kTwoShares ? NT : 1];
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = Acc[n] * cseg;
+        if (kTwoShares) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc2[kTwoShares ? n : 0] = Acc2[kTwoShares ? n : 0] * cseg;
+        }
 #pragma unroll
         for (int tau = 0; tau < TMAX; ++tau) {
           if (tau >= TS) break;
           if (RW > 1 && tau % RW != u) continue;
+          f32x4* const share = (kTwoShares && (tau & 1)) ? acc2 : acc;
           // Z^T[t][row] = Ub_t . S_b[row]
           const V uh = Ops::row(UbH + (16 * tau + c16) * XLD, g), ul = Ops::row(UbL + (16 * tau + c16) * XLD, g);
           const f32x4 z = Ops::mma3(uh, ul, Sh, Sl, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -701,11 +717,15 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
           for (int n = 0; n < NT; ++n) {
             const bf16x4 kh = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtH + (16 * n + c16) * KTLD + 16 * tau + 4 * g));
             const bf16x4 kl = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (16 * n + c16) * KTLD + 16 * tau + 4 * g));
-            acc[n] = mma16x3(kh, kl, zh, zl, acc[n]);
+            share[n] = mma16x3(kh, kl, zh, zl, share[n]);
           }
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) Acc[n] = acc[n];
+        if (kTwoShares) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) Acc2[kTwoShares ? n : 0] = acc2[kTwoShares ? n : 0];
+        }
       }
       // gate rows: the M_mem waves each update column tile w (rows m_eta, m_alpha in lanes
       // c16 < 2 of the accumulator layout)
@@ -795,6 +815,10 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : 1) void cha
 #pragma unroll
       for (int n = 0; n < NT; ++n) Acc[n] = xch[((m * RW + 0) * NT + n) * 64 + ln] + xch[((m * RW + 1) * NT + n) * 64 + ln];
     }
+    if (kTwoShares) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) Acc[n] = Acc[n] + Acc2[kTwoShares ? n : 0];
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) St[n] = Acc[n];
     if (!gates_frozen) cur ^= 1;  // frozen gate rows stay in the chunk-start copy
@@ -882,9 +906,9 @@ int waves_of_d32(const ChainParams& p) {
 bool chunk_path_supported(const ChainParams& p, int d) {
   if (!p.x_bf16 || p.mem_chunk > 0 || p.readout) return false;
   if (d != 16 && d != 32 && d != 64) return false;
-  // d = 32 with chunks of at most 32 tokens, d = 64 with chunks of at most 16: the
-  // register-resident block kernel is faster there
-  if (d == 32 && longest_chunk(p) <= 32) return false;
+  // chunks that fit one 16-token block at d = 32 and 64: the register-resident block
+  // kernel is faster there
+  if (d == 32 && longest_chunk(p) <= 16) return false;
   if (d == 64 && longest_chunk(p) <= 16) return false;
   int TT = 0, multi = 0;
   return launch_lds(p, d, segment_of(p, d), d == 32, TT, multi).total <= kChunkLdsMax;
