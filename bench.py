@@ -434,6 +434,9 @@ def main() -> int:
                     help="comma-separated VisionHOPE variants to enable together: scales, skip, "
                          "counts, hard_injection, soft_spectral, frozen_kv, frozen_dynamics, "
                          "no_dgd, queries (synthetic scales / skip / queries)")
+    ap.add_argument("--mem-chunk", type=int, default=0,
+                    help="two chunk sizes: the working memory's boundary every this many tokens "
+                         "(0: one chunk size)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients) instead of the forward scan")
     ap.add_argument("--block", action="store_true",
@@ -515,7 +518,7 @@ def main() -> int:
     def step(i, ev=None):
         x, out, ws = sets[i % len(sets)]
         hope_scan2d_forward(x, init, w.n_heads, 15, w.chunk, out, workspace=ws, stream=stream,
-                            scan_events=ev, readout=args.readout, **vkw)
+                            scan_events=ev, readout=args.readout, mem_chunk=args.mem_chunk, **vkw)
 
     for i in range(args.warmup):
         step(i)
@@ -550,7 +553,8 @@ def main() -> int:
 
     tokens = w.scan_tokens(4)
     roof = roofline_numbers(w, readout=args.readout)
-    kname = hope_scan2d_kernel_name(sets[0][0], w.n_heads, 15, w.chunk, readout=args.readout, **vkw)
+    kname = hope_scan2d_kernel_name(sets[0][0], w.n_heads, 15, w.chunk, readout=args.readout,
+                                    mem_chunk=args.mem_chunk, **vkw)
     on_mfma = kname != "chain_kernel"
     achieved = roof["flops"] / k_avg
     # the fp32 VALU kernel runs every product in fp32 on the vector ALUs (157.3 TFLOP/s);
@@ -575,7 +579,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
-                   "state_dtype": "f32", "readout": args.readout, "variants": var},
+                   "state_dtype": "f32", "readout": args.readout, "variants": var,
+                   "mem_chunk": args.mem_chunk},
         "roofline": {"bound": "mfma" if on_mfma else "alu", "achieved": achieved / 1e12,
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": recorded_traffic(w) if args.readout == "boundary" and not var else None,
