@@ -157,7 +157,9 @@ __host__ __device__ constexpr ChunkLds chunk_lds(int TT, bool multi, bool exchan
 // block's operator, thousands of four-wave chains) are held to 72 registers, seven chains per
 // CU; the eight-wave d = 32 launches with up to three token tiles to 128, two chains per CU
 // (four tiles would spill)
-template <int D, int SEG_, int NW_, int TT, bool VAR>
+// VAR: 0 the default operator, 1 every variant option, 2 only those of the VisionHOPE block
+// (skip, direction scales, given queries: fewer live scalars, no register spills)
+template <int D, int SEG_, int NW_, int TT, int VAR>
 __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 && NW_ == 8 && TT <= 3) ? 4 : 1) void chain_chunk_kernel(ChainParams p, int multi) {
   typedef ChunkShape<D, SEG_, NW_> S;
   typedef HeadOps<D> Ops;
@@ -213,15 +215,18 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
   const int H = p.H, W = p.W, N = H * W, Dt = p.D;
   const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
   const int64_t SS = 4 * D * D + 2 * D;
-  const float* const v_skip = VAR ? p.skip : nullptr;
-  const float* const v_scales = VAR ? p.route_scales : nullptr;
-  unsigned long long* const v_counts = VAR ? p.counts : nullptr;
-  float* const v_steps = VAR ? p.steps : nullptr;
-  const void* const v_queries = VAR ? p.queries : nullptr;
-  const unsigned v_frozen = VAR ? (p.frozen | (p.queries ? 4u : 0u)) : 0u;
-  const bool v_nodgd = VAR && p.no_dgd;
-  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR ? p.injection : 0,
-                      VAR ? p.spectral : 0};
+  // the skip, direction-scale and query pointers are kept in LDS and read where used: held
+  // in scalar registers across the loop they would spill (these kernels are at the scalar
+  // register limit)
+  __shared__ const void* vptr[3];
+  const bool has_skip = VAR && p.skip, has_scales = VAR && p.route_scales;
+  unsigned long long* const v_counts = VAR == 1 ? p.counts : nullptr;
+  float* const v_steps = VAR == 1 ? p.steps : nullptr;
+  const bool has_q = VAR && p.queries;
+  const unsigned v_frozen = VAR == 1 ? (p.frozen | (p.queries ? 4u : 0u)) : (VAR && p.queries ? 4u : 0u);
+  const bool v_nodgd = VAR == 1 && p.no_dgd;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR == 1 ? p.injection : 0,
+                      VAR == 1 ? p.spectral : 0};
   const int m = w % MT, u = w / MT;  // this wave's state-row tile, and its share of the tile's work
   // row tiles held fixed within the image: M_k, M_v (bit 0) and M_q (bit 2)
   const bool my_tile_frozen = ((v_frozen & 1u) && m >= NT && m < 3 * NT) || ((v_frozen & 4u) && m >= 3 * NT);
@@ -253,6 +258,11 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
     for (int n = 0; n < NT; ++n) St[n] = *reinterpret_cast<const f32x4*>(init + row * D + 16 * n + 4 * g);
     for (int i = threadIdx.x; i < 2 * D; i += kThreads) Tb[0][i] = init[TR * D + i];
     if (threadIdx.x < 3) cnt_lds[threadIdx.x] = 0u;
+    if (VAR && threadIdx.x == 0) {
+      vptr[0] = p.skip;
+      vptr[1] = p.route_scales;
+      vptr[2] = p.queries;
+    }
   }
   int cur = 0;
 
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
       const int lane = lid & 63, c16 = lid & 15, g = (lid >> 4) & 3;
 
       // ---- A: projections P[t][row] = x_t . S_b[row] for the k, v, q and gate rows ----
-      if (m >= NT && !(v_queries && m >= 3 * NT)) {
+      if (m >= NT && !(has_q && m >= 3 * NT)) {
 #pragma unroll
         for (int tau = 0; tau < TMAX; ++tau) {
           if (tau >= TS) break;
@@ -374,7 +384,13 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
           for (int e = 0; e < CPL; ++e) {
             kr[e] = pt[e];
             vr[e] = pt[D + e];
-            qr[e] = !v_queries ? pt[2 * D + e] : query_at(p, b, pixs[t], (int64_t)h * D + c16 * CPL + e);
+            if (!has_q) {
+              qr[e] = pt[2 * D + e];
+            } else {
+              const int64_t qi = ((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + c16 * CPL + e;
+              qr[e] = p.queries_bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(vptr[2])[qi] << 16)
+                                     : static_cast<const float*>(vptr[2])[qi];
+            }
             kk += kr[e] * kr[e];
             qq += qr[e] * qr[e];
           }
@@ -671,8 +687,8 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
       } else if (m < NT) {
         // readout y_t = M_mem,b q_t for this wave's 16 rows of M_mem
         const int64_t c = (int64_t)h * D + 16 * m + c16;
-        const float skip_c = v_skip ? v_skip[c] : 0.f;
-        const float scale_c = v_scales ? v_scales[(int64_t)r * Dt + c] : 1.f;
+        const float skip_c = has_skip ? static_cast<const float*>(vptr[0])[c] : 0.f;
+        const float scale_c = has_scales ? static_cast<const float*>(vptr[1])[(int64_t)r * Dt + c] : 1.f;
 #pragma unroll
         for (int tau = 0; tau < TMAX; ++tau) {
           if (tau >= TS) break;
@@ -684,8 +700,8 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             const int t = 16 * tau + 4 * g + i;
             if (t < ns) {
               float yv = y[i];
-              if (v_skip) yv = fmaf(skip_c, __uint_as_float((unsigned)Xs[t * XLD + 16 * m + c16] << 16), yv);
-              if (v_scales) yv *= scale_c;
+              if (has_skip) yv = fmaf(skip_c, __uint_as_float((unsigned)Xs[t * XLD + 16 * m + c16] << 16), yv);
+              if (has_scales) yv *= scale_c;
               dst[((int64_t)b * N + pixs[t]) * Dt + c] = yv;
             }
           }
@@ -858,7 +874,7 @@ ChunkLds launch_lds(const ChainParams& p, int d, int seg, bool exchange, int& TT
 
 constexpr int kChunkLdsMax = 150 * 1024;  // dynamic LDS of one workgroup, at most
 
-template <int D, int SEG, int NW, int TT, bool VAR>
+template <int D, int SEG, int NW, int TT, int VAR>
 hipError_t launch_tt(const ChainParams& p, int multi, int lds_bytes, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&chain_chunk_kernel<D, SEG, NW, TT, VAR>),
@@ -869,7 +885,7 @@ hipError_t launch_tt(const ChainParams& p, int multi, int lds_bytes, hipStream_t
   return hipGetLastError();
 }
 
-template <int D, int SEG, int NW, bool VAR>
+template <int D, int SEG, int NW, int VAR>
 hipError_t launch_cfg(const ChainParams& p, hipStream_t stream) {
   int TT = 0, multi = 0;
   const ChunkLds L = launch_lds(p, D, SEG, NW > D / 4, TT, multi);
@@ -885,7 +901,9 @@ hipError_t launch_cfg(const ChainParams& p, hipStream_t stream) {
 
 template <int D, int SEG, int NW>
 hipError_t launch_v(const ChainParams& p, hipStream_t stream) {
-  return needs_variants(p) ? launch_cfg<D, SEG, NW, true>(p, stream) : launch_cfg<D, SEG, NW, false>(p, stream);
+  if (!needs_variants(p)) return launch_cfg<D, SEG, NW, 0>(p, stream);
+  const bool block_only = !(p.counts || p.frozen || p.no_dgd || p.injection || p.spectral || p.steps);
+  return block_only ? launch_cfg<D, SEG, NW, 2>(p, stream) : launch_cfg<D, SEG, NW, 1>(p, stream);
 }
 
 // Segment length of a launch: one 16-token tile at d = 16 when every chunk fits in it (fewer
