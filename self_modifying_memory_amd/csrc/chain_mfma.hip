@@ -127,7 +127,9 @@ __device__ __forceinline__ void load_row_pair(const float* row, int s, int g, f3
 // The d = 64 kernels are held to 4 waves per SIMD (128 registers) so that two chains share
 // a CU: the running-readout and variant instantiations then spill (35 and up to 48
 // registers), which costs less than running one chain per CU.
-template <int D, bool MULTI, int NW, bool RUN, bool VAR>
+// VAR: 0 the default operator, 1 every variant option, 2 only those of the VisionHOPE block
+// (skip, direction scales, given queries)
+template <int D, bool MULTI, int NW, bool RUN, int VAR>
 __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(ChainParams p) {
   constexpr int kWaves = NW;
   constexpr int kThreads = 64 * NW;
@@ -195,15 +197,17 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
   const int64_t SS = 4 * D * D + 2 * D;
   // variants (compiled only into the VAR instantiations; the others see the defaults)
-  const float* const v_skip = VAR ? p.skip : nullptr;
-  const float* const v_scales = VAR ? p.route_scales : nullptr;
-  unsigned long long* const v_counts = VAR ? p.counts : nullptr;
-  float* const v_steps = VAR ? p.steps : nullptr;
-  const void* const v_queries = VAR ? p.queries : nullptr;
-  const unsigned v_frozen = VAR ? (p.frozen | (p.queries ? 4u : 0u)) : 0u;  // M_q unused with given queries
-  const bool v_nodgd = VAR && p.no_dgd;
-  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR ? p.injection : 0,
-                      VAR ? p.spectral : 0};
+  // (the skip, direction-scale and query pointers are kept in LDS and read where used:
+  // held in scalar registers across the block loop they would spill)
+  __shared__ const void* vptr[3];
+  const bool has_skip = VAR && p.skip, has_scales = VAR && p.route_scales, has_q = VAR && p.queries;
+  unsigned long long* const v_counts = VAR == 1 ? p.counts : nullptr;
+  float* const v_steps = VAR == 1 ? p.steps : nullptr;
+  // M_q unused with given queries
+  const unsigned v_frozen = VAR == 1 ? (p.frozen | (p.queries ? 4u : 0u)) : (VAR && p.queries ? 4u : 0u);
+  const bool v_nodgd = VAR == 1 && p.no_dgd;
+  const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, VAR == 1 ? p.injection : 0,
+                      VAR == 1 ? p.spectral : 0};
   // register tiles held fixed within the image: M_k, M_v (bit 0) and M_q (bit 2); the gate
   // rows (bit 1) are handled with their LDS copy
   auto tile_frozen = [&](int m) {
@@ -213,8 +217,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   // direction scale and skip of channel c (read once per readout tile) applied to a
   // readout y of token value xc
   auto finish = [&](float y, float skip_c, float scale_c, float xc) {
-    if (v_skip) y = fmaf(skip_c, xc, y);
-    if (v_scales) y *= scale_c;
+    if (has_skip) y = fmaf(skip_c, xc, y);
+    if (has_scales) y *= scale_c;
     return y;
   };
   auto xs_at = [&](int t, int col) {
@@ -252,6 +256,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     }
     for (int i = threadIdx.x; i < 2 * D; i += kThreads) Tb[0][i] = init[TR * D + i];
     if (threadIdx.x < 3) cnt_lds[threadIdx.x] = 0u;
+    if (VAR && threadIdx.x == 0) {
+      vptr[0] = p.skip;
+      vptr[1] = p.route_scales;
+      vptr[2] = p.queries;
+    }
   }
   int cur = 0;  // which Tb copy holds the chunk-start gate rows
   // B-operand values of the gate rows for column tile n (rows past the two are zero)
@@ -303,9 +312,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   // values) per load; staged to Qs as fp32, zero past nt
   constexpr int kQPer32 = 4, kQPer16 = 8;
   constexpr bool kStageQ = VAR && !RUN;
-  auto fetch_q = [&](int lid, int tb, int nt) {
+  auto fetch_q = [&](int lid, int tb, int nt, const void* v_queries) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (kStageQ && v_queries) {
+    if (kStageQ && has_q) {
       const int per = p.queries_bf16 ? kQPer16 : kQPer32;
       const int lt = lid / (D / per), lc = lid % (D / per);
       if (lt < nt) {
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     return v;
   };
   auto stage_q = [&](int lid, const u32x4& v) {
-    if (kStageQ && v_queries) {
+    if (kStageQ && has_q) {
       const int per = p.queries_bf16 ? kQPer16 : kQPer32;
       const int lt = lid / (D / per), lc = lid % (D / per);
       if (lt < kSB) {
@@ -339,11 +348,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     const int lid = threadIdx.x;
     const int nt0 = min(kSB, min(C, N));
     stage_block(lid, fetch(lid, 0, nt0), 0, nt0);
-    stage_q(lid, fetch_q(lid, 0, nt0));
+    stage_q(lid, fetch_q(lid, 0, nt0, p.queries));
     int tn, ntn;
     next_block(0, tn, ntn);
     pf = fetch(lid, tn, ntn);
-    qpf = fetch_q(lid, tn, ntn);
+    qpf = fetch_q(lid, tn, ntn, p.queries);
   }
   lds_barrier();
 
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         for (int mi = 0; mi < MTW; ++mi) {
           const int m = w + kWaves * mi;
           if (m < NT) continue;
-          if (v_queries && m >= 3 * NT) continue;  // queries are given: no q projection
+          if (has_q && m >= 3 * NT) continue;  // queries are given: no q projection
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
@@ -437,9 +446,15 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         for (int e = 0; e < CPL; ++e) {
           kr[e] = pt[e];
           vr[e] = pt[D + e];
-          qr[e] = !v_queries ? pt[2 * D + e]
-                  : kStageQ ? Qs[t * D + c16 * CPL + e]
-                            : query_at(p, b, pixs[t], (int64_t)h * D + c16 * CPL + e);
+          if (!has_q) {
+            qr[e] = pt[2 * D + e];
+          } else if (kStageQ) {
+            qr[e] = Qs[t * D + c16 * CPL + e];
+          } else {
+            const int64_t qi = ((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + c16 * CPL + e;
+            qr[e] = p.queries_bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(vptr[2])[qi] << 16)
+                                   : static_cast<const float*>(vptr[2])[qi];
+          }
           kk += kr[e] * kr[e];
           qq += qr[e] * qr[e];
         }
@@ -528,18 +543,18 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             rpix[i] = pixs[4 * g + i];
-            if (v_skip) rx[i] = xs_at(4 * g + i, m * 16 + c16);
+            if (has_skip) rx[i] = xs_at(4 * g + i, m * 16 + c16);
           }
         } else {
           const int64_t c = (int64_t)h * D + m * 16 + c16;
-          const float skip_c = v_skip ? v_skip[c] : 0.f;
-          const float scale_c = v_scales ? v_scales[(int64_t)r * Dt + c] : 1.f;
+          const float skip_c = has_skip ? static_cast<const float*>(vptr[0])[c] : 0.f;
+          const float scale_c = has_scales ? static_cast<const float*>(vptr[1])[(int64_t)r * Dt + c] : 1.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
             if (t < nt)
               dst[((int64_t)b * N + pixs[t]) * Dt + c] =
-                  finish(acc[i], skip_c, scale_c, v_skip ? xs_at(t, m * 16 + c16) : 0.f);
+                  finish(acc[i], skip_c, scale_c, has_skip ? xs_at(t, m * 16 + c16) : 0.f);
           }
         }
       }
@@ -731,8 +746,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           const f32x4 at = *reinterpret_cast<const f32x4*>(Ais + 4 * lane);
           const f32x4 y = mm16(at, zu);
           const int64_t c = (int64_t)h * D + w * 16 + c16;
-          const float skip_c = v_skip ? v_skip[c] : 0.f;
-          const float scale_c = v_scales ? v_scales[(int64_t)r * Dt + c] : 1.f;
+          const float skip_c = has_skip ? static_cast<const float*>(vptr[0])[c] : 0.f;
+          const float scale_c = has_scales ? static_cast<const float*>(vptr[1])[(int64_t)r * Dt + c] : 1.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
@@ -845,7 +860,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           int tn2, ntn2;
           next_block(tn, tn2, ntn2);
           pf = fetch(lid2, tn2, ntn2);
-          qpf = fetch_q(lid2, tn2, ntn2);
+          qpf = fetch_q(lid2, tn2, ntn2, vptr[2]);
         }
       }
       lds_barrier();
@@ -897,14 +912,18 @@ bool needs_variants(const ChainParams& p) {
 
 template <int D, bool MULTI, int NW>
 hipError_t launch_d(const ChainParams& p, dim3 grid, hipStream_t stream) {
-  const bool var = needs_variants(p);
   const dim3 block(64 * NW);
+  // 0: no variant; 2: only the block's (skip, direction scales, given queries); 1: any
+  const int var = !needs_variants(p) ? 0
+                  : !(p.counts || p.frozen || p.no_dgd || p.injection || p.spectral || p.steps) ? 2 : 1;
   if (p.readout) {
-    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, false>), grid, block, 0, stream, p);
+    if (var == 1) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, 1>), grid, block, 0, stream, p);
+    else if (var == 2) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, 2>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, true, 0>), grid, block, 0, stream, p);
   } else {
-    if (var) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, false>), grid, block, 0, stream, p);
+    if (var == 1) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, 1>), grid, block, 0, stream, p);
+    else if (var == 2) hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, 2>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((chain_mfma_kernel<D, MULTI, NW, false, 0>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
