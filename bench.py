@@ -189,10 +189,10 @@ def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: fl
 def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
     """The backward pass (hope_scan2d_backward) as the timed step.  Roofline: the gradient
     of every forward product costs two products of the same size and the forward is
-    recomputed once, so the algorithmic work is 3x the forward's.  At d = 64 with chunks of
-    at most 16 tokens the kernel runs its products on the fp32 matrix cores (the rest on the
-    vector ALUs); the whole of it is charged at the fp32 peak (157.3 TFLOP/s, matrix and
-    vector alike)."""
+    recomputed once, so the algorithmic work is 3x the forward's.  At d = 32 (any chunk
+    length, in 16-token blocks) and at d = 64 with chunks of at most 16 tokens the kernel
+    runs its products on the fp32 matrix cores (the rest on the vector ALUs); the whole of
+    it is charged at the fp32 peak (157.3 TFLOP/s, matrix and vector alike)."""
     import torch
     from self_modifying_memory_amd.scan2d import (hope_scan2d_backward,
                                                   hope_scan2d_backward_workspace_size)
@@ -233,6 +233,9 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
     roof = roofline_numbers(w)
     flops = 3 * roof["flops"]
     wy = w.d == 64 and max(w.chunk or w.W, w.chunk or w.H) <= 16
+    kname = ("chain_backward_wy_kernel" if wy else
+             "chain_backward_wy32_kernel" if w.d == 32 else "chain_backward_kernel")
+    wy = wy or w.d == 32
     rec = {
         "metric": "backward scan tokens/s (positions x dirs): gradients of the 4-dir Hope memory "
                   "scan with respect to the map and the initial memories",
@@ -246,8 +249,7 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
         "roofline": {"bound": "mfma" if wy else "alu", "achieved": flops / c_avg / 1e12,
                      "peak": PEAK_FP32 / 1e12,
                      "unit": "TFLOP/s", "frac": flops / c_avg / PEAK_FP32, "traffic": None,
-                     "kernel": ("chain_backward_wy_kernel" if wy else "chain_backward_kernel")
-                               + " (with the gradient reduction and route sum)",
+                     "kernel": kname + " (with the gradient reduction and route sum)",
                      "kernel_ms": c_avg * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(call_ms, 10)),
                                            float(np.percentile(call_ms, 90))]},

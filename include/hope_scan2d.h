@@ -258,7 +258,8 @@ size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t c
  * Errors: as hope_scan2d_forward for the shared arguments; HOPE_ERR_INVALID_ARG when
  * grad_out, grad_x or grad_init is null, misaligned or overlaps another argument;
  * HOPE_ERR_UNSUPPORTED for d not in {16, 32, 64}, a chunk (after clipping to H*W)
- * longer than 128 tokens (32 at d = 64), or any option outside the honoured set away
+ * longer than 128 tokens at d = 16 or 32 tokens at d = 64 (d = 32 takes any chunk
+ * length), or any option outside the honoured set away
  * from its default (running readout, variants, two chunk sizes, final_memories, bf16
  * out); HOPE_ERR_WORKSPACE; HOPE_ERR_HIP.  Deterministic: per-route map gradients and
  * per-image state gradients are summed in a fixed order.
@@ -269,8 +270,10 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
                                    const hope_scan2d_opts_t* opts);
 
 /* Bytes of workspace hope_scan2d_backward needs: the map-gradient planes of the routes
- * beyond the first, plus per chain the checkpoints of every chunk-boundary state, the
- * state adjoint and one chunk's gain trajectory; 0 for arguments it would reject. */
+ * beyond the first, plus per chain the state adjoint and the forward records (at d = 32
+ * the product of the earlier chunks' gains and the gain after every 16-token block of
+ * each chunk; otherwise every chunk-boundary state and one chunk's gain trajectory);
+ * 0 for arguments it would reject. */
 size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                            const hope_scan2d_opts_t* opts);
 

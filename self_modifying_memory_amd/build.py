@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhopescan.so")
-SOURCES = ["api.hip", "backward_kernel.hip", "backward_wy.hip", "block_api.hip", "block_kernels.hip", "chain_chunk.hip", "chain_kernel.hip", "chain_mfma.hip", "permute_kernels.hip"]
+SOURCES = ["api.hip", "backward_kernel.hip", "backward_wy.hip", "backward_wy32.hip", "block_api.hip", "block_kernels.hip", "chain_chunk.hip", "chain_kernel.hip", "chain_mfma.hip", "permute_kernels.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of generated code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

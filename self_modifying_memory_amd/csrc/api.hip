@@ -131,7 +131,8 @@ BackLayout backward_layout(const hope_fmap_t* x, uint32_t dirs, int32_t chunk) {
     L.cmax = std::max<int64_t>(L.cmax, std::min<int64_t>(C, N));
   }
   const int64_t SS = 4LL * d * d + 2LL * d;
-  L.chain_floats = ((L.nck + 1) * SS + L.cmax * d * d + 63) / 64 * 64;
+  L.chain_floats = d == 32 ? hope::backward_wy32_chain_floats(L.nck, L.cmax)
+                           : ((L.nck + 1) * SS + L.cmax * d * d + 63) / 64 * 64;
   L.plane_stride = plane_stride_elems((int64_t)x->B * x->H * x->W * x->D);
   L.planes_floats = (int64_t)(L.n_sel - 1) * L.plane_stride;
   return L;
@@ -497,7 +498,7 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
   if (!backward_opts_supported(o)) return HOPE_ERR_UNSUPPORTED;
   if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
   const BackLayout L = backward_layout(x, dirs, chunk);
-  if (L.cmax > hope::backward_max_chunk(d)) return HOPE_ERR_UNSUPPORTED;
+  if (d != 32 && L.cmax > hope::backward_max_chunk(d)) return HOPE_ERR_UNSUPPORTED;
   const size_t ws_need = backward_workspace_bytes(x, L);
   if (!o.workspace || o.workspace_bytes < ws_need) return HOPE_ERR_WORKSPACE;
   const Range r_ws = range_of(o.workspace, o.workspace_bytes);

@@ -512,22 +512,25 @@ hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, h
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
   dim3 grid((unsigned)blocks), block(back_threads(d));
   hipError_t err = hipSuccess;
+  const int64_t SS = 4LL * d * d + 2LL * d;
+  int64_t dS_off = p.nck * SS;  // where a chain's state adjoint sits in its workspace
   if (backward_wy_supported(p, d)) {
     err = launch_chain_backward_wy(p, stream);
+  } else if (backward_wy32_supported(p, d)) {
+    err = launch_chain_backward_wy32(p, stream);
+    dS_off = 0;
   } else {
     switch (d) {
       case 16: chain_backward_kernel<16><<<grid, block, 0, stream>>>(p); break;
-      case 32: chain_backward_kernel<32><<<grid, block, 0, stream>>>(p); break;
       case 64: chain_backward_kernel<64><<<grid, block, 0, stream>>>(p); break;
       default: return hipErrorInvalidValue;
     }
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;
-  const int64_t SS = 4LL * d * d + 2LL * d;
   const int64_t n_out = (p.init_per_image ? (int64_t)p.B : 1) * 4 * p.nh * SS;
   const int64_t nb = std::min<int64_t>((n_out + 255) / 256, 65535);
-  init_grad_kernel<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(p, grad_init, SS, p.nck * SS);
+  init_grad_kernel<<<dim3((unsigned)nb), dim3(256), 0, stream>>>(p, grad_init, SS, dS_off);
   return hipGetLastError();
 }
 

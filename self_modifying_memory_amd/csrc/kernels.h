@@ -73,13 +73,18 @@ struct BackParams {
   int eta_map;
   float eta_scale, alpha_bias, eps;
 };
-// longest chunk the backward kernel holds in LDS
+// longest chunk the token-serial backward kernel holds in LDS (d = 16 and 64)
 __host__ __device__ constexpr int backward_max_chunk(int d) { return d == 64 ? 32 : 128; }
 // writes grad_x (slot 0 plane) and the route planes, then grad_init; the caller adds the planes
 hipError_t launch_chain_backward(const BackParams& p, int d, float* grad_init, hipStream_t stream);
 // chunk-parallel backward on the fp32 matrix cores: d = 64, every chunk <= 16 tokens
 bool backward_wy_supported(const BackParams& p, int d);
 hipError_t launch_chain_backward_wy(const BackParams& p, hipStream_t stream);
+// chunk-parallel backward on the fp32 matrix cores in 16-token blocks: d = 32, any chunk
+// length; its workspace per chain (the state adjoint first, then the chunk records)
+bool backward_wy32_supported(const BackParams& p, int d);
+int64_t backward_wy32_chain_floats(int64_t nck, int64_t cmax);
+hipError_t launch_chain_backward_wy32(const BackParams& p, hipStream_t stream);
 
 // The scan kernel a forward call launches (host-side dispatch, api.hip).
 enum ScanPath { kPathChain = 0, kPathMfma = 1, kPathChunk = 2 };

@@ -118,7 +118,7 @@ int main() {
   EXPECT(hope_scan2d_backward(&x, init, 15, 0, go, static_cast<float*>(fake(0)), gi, &o), HOPE_ERR_INVALID_ARG);
   o.readout = HOPE_READOUT_RUNNING;
   EXPECT(hope_scan2d_backward(&x, init, 15, 0, go, gx, gi, &o), HOPE_ERR_UNSUPPORTED);
-  hope_fmap_t rows200 = fmap(1, 2, 200, 32, 1);
+  hope_fmap_t rows200 = fmap(1, 2, 200, 16, 1);  // d = 16: rows of 200 > 128
   o = defaults(); o.workspace = fake(8); o.workspace_bytes = hope_scan2d_backward_workspace_size(&rows200, 1, 0, nullptr);
   EXPECT(hope_scan2d_backward(&rows200, init, 1, 0, go, gx, gi, &o), HOPE_ERR_UNSUPPORTED);
 

@@ -209,17 +209,27 @@ def bcall(lib, x, init=FAKE + (1 << 30), dirs=15, chunk=0, gout=FAKE + (2 << 30)
 
 
 def test_backward_workspace_size(lib):
-    x = fmap(B=2, H=4, W=5, D=32, nh=1)          # d = 32, S = 4160, N = 20
-    # aligned chunks: rows of 5 (4 chunks), columns of 4 (5 chunks) -> 5 checkpoints
-    per_chain = (5 + 1) * 4160 + 5 * 32 * 32
-    per_chain = (per_chain + 63) // 64 * 64
     n_elem = 2 * 4 * 5 * 32
     plane = (n_elem + 63) // 64 * 64
+    # d = 16 (token-serial kernel), S = 1056, N = 20: aligned chunks are rows of 5 (4 chunks)
+    # and columns of 4 (5 chunks) -> 5 + 1 state records and one chunk's gain trajectory
+    x16 = fmap(B=2, H=4, W=5, D=32, nh=2)
+    per_chain = ((5 + 1) * 1056 + 5 * 16 * 16 + 63) // 64 * 64
+    want = (3 * plane + 4 * 2 * 2 * per_chain) * 4
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x16), 15, 0, None) == want
+    # d = 32 (blocked kernel), S = 4160: the state adjoint, then per chunk P_c and the gain
+    # after each 16-token block (one block of the 5-token chunks), 5 chunks at most
+    x = fmap(B=2, H=4, W=5, D=32, nh=1)
+    per_chain = (4160 + 5 * (1 + 1) * 1024 + 63) // 64 * 64
     want = (3 * plane + 4 * 2 * 1 * per_chain) * 4
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, 0, None) == want
     # route 0 alone: no planes, two chains of 4 row chunks of 5 tokens
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 1, 0, None) == \
-        (2 * (((4 + 1) * 4160 + 5 * 1024 + 63) // 64 * 64)) * 4
+        (2 * ((4160 + 4 * 2 * 1024 + 63) // 64 * 64)) * 4
+    # rows of 200 tokens at d = 32: one chunk per row, 13 blocks each
+    big = fmap(B=1, H=2, W=200, D=32, nh=1)
+    assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(big), 1, 0, None) == \
+        ((4160 + 2 * (1 + 13) * 1024 + 63) // 64 * 64) * 4
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 0, 0, None) == 0
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, -1, None) == 0
 
@@ -246,10 +256,10 @@ def test_backward_argument_errors(lib):
         assert bcall(lib, x, o=opts(lib, **kw, **base)) == N.HOPE_ERR_UNSUPPORTED, kw
     # head dimension and chunk length limits
     assert bcall(lib, fmap(D=8, nh=1), o=o) == N.HOPE_ERR_UNSUPPORTED
-    big = fmap(B=1, H=2, W=200, D=32, nh=1)
+    big = fmap(B=1, H=2, W=200, D=16, nh=1)
     wsb = lib.hope_scan2d_backward_workspace_size(ctypes.byref(big), 1, 0, None)
     assert bcall(lib, big, dirs=1, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=wsb)) == \
-        N.HOPE_ERR_UNSUPPORTED                                            # rows of 200 > 128
+        N.HOPE_ERR_UNSUPPORTED                                            # d = 16: rows of 200 > 128
     d64 = fmap(B=1, H=4, W=40, D=64, nh=1)
     wsd = lib.hope_scan2d_backward_workspace_size(ctypes.byref(d64), 1, 0, None)
     assert bcall(lib, d64, dirs=1, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=wsd)) == \

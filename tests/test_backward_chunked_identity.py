@@ -1,5 +1,5 @@
-"""The algebra of the chunk-parallel backward kernel (backward_wy.hip), restated in float64
-and checked against the gradient oracle (oracle/hope_backward.py, itself pinned by finite
+"""The algebra of the chunk-parallel backward kernels (backward_wy.hip, and its blocked form
+in backward_wy32.hip), restated in float64 and checked against the gradient oracle (oracle/hope_backward.py, itself pinned by finite
 differences in test_oracle_backward_pins.py).
 
 Two identities carry the kernel ("VisionHOPE: Visual Backbones as Self-Modifying Learning
@@ -152,6 +152,149 @@ def test_chunk_parallel_backward_equals_gradient_oracle(name):
     init = rng.standard_normal((4, nh, S)) / np.sqrt(d)
     g = rng.standard_normal((B, H, W, D))
     gx, gi = scan_bwd(x, init, nh, g, chunk, **kw)
+    rx, ri = hb.scan2d_backward(x, init, nh, g, chunk=chunk, **kw)
+    assert np.abs(gx - rx).max() <= 1e-12 * np.abs(rx).max()
+    assert np.abs(gi - ri).max() <= 1e-12 * np.abs(ri).max()
+
+
+# The blocked form of the d = 32 kernel (backward_wy32.hip): each chunk is cut into blocks of
+# TB tokens; G_s, the gain before a block, replaces I in the low-rank forms, the adjoint of
+# each block's end gain is carried to the previous block, and P_c's adjoint picks up
+# dP_{c+1} G_C^T with G_C the chunk's end gain.
+def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, eta_map="sigmoid"):
+    N, d = xs.shape
+    nck = (N + C - 1) // C
+    I = np.eye(d)
+
+    def beta(al, j, t):  # prod_{i=j+1..t} al_i
+        return float(np.prod(al[j + 1:t + 1]))
+
+    def block_fwd(P, Gs, s0, s1):
+        X = xs[s0:s1].T
+        Xt = P @ X
+        Proj = S0[d:] @ Xt
+        c = s1 - s0
+        K = np.zeros((d, c)); Dl = np.zeros((d, c)); Q = np.zeros((d, c)); st = np.zeros(c); al = np.zeros(c)
+        for t in range(c):
+            k, dl, s, a, q = gates_t(torch.tensor(Proj[:, t]), d, eta_scale, alpha_bias, eps, eta_map)
+            K[:, t], Dl[:, t], Q[:, t], st[t], al[t] = k.numpy(), dl.numpy(), q.numpy(), float(s), float(a)
+        Gm = K.T @ K
+        Gk = Gs @ K
+        U = np.zeros((d, c)); Wm = np.zeros((d, c))
+        for t in range(c):
+            acc = float(np.prod(al[:t])) * Gk[:, t] + Dl[:, t]
+            for j in range(t):
+                acc = acc + beta(al, j, t - 1) * Gm[j, t] * U[:, j]
+            Wm[:, t] = acc
+            U[:, t] = -st[t] * acc
+        bE = np.array([beta(al, j, c - 1) for j in range(c)])
+        Ge = np.prod(al) * Gs + U @ np.diag(bE) @ K.T
+        return X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, Ge
+
+    def blocks(c):
+        s0, s1 = c * C, min(N, (c + 1) * C)
+        return [(b0, min(s1, b0 + TB)) for b0 in range(s0, s1, TB)]
+
+    # forward sweep: P_c and every block's start gain
+    P = I.copy(); Ps = []; starts = []
+    for c in range(nck):
+        Ps.append(P.copy())
+        Gs = I.copy(); st_c = []
+        for b0, b1 in blocks(c):
+            st_c.append(Gs.copy())
+            Gs = block_fwd(P, Gs, b0, b1)[-1]
+        starts.append((st_c, Gs))
+        P = P @ Gs
+    dPn = np.zeros((d, d)); dS0 = np.zeros_like(S0); dxs = np.zeros_like(xs)
+    for c in range(nck - 1, -1, -1):
+        P = Ps[c]
+        st_c, GC = starts[c]
+        dG = P.T @ dPn
+        dPc = dPn @ GC.T
+        for i in range(len(st_c) - 1, -1, -1):
+            b0, b1 = blocks(c)[i]
+            Gs = st_c[i]
+            X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, _ = block_fwd(P, Gs, b0, b1)
+            cl = b1 - b0
+            Gam = np.array([np.prod(al[:t]) for t in range(cl)])        # Gamma_{t-1}
+            Gp = np.array([np.prod(al[t + 1:]) for t in range(cl)])     # Gamma'_t
+            E = dG @ K; F = dG.T @ Wm; trD = np.sum(Gs * dG); ud = np.sum(U * E, 0)
+            A = np.zeros((d, cl))
+            for t in range(cl - 1, -1, -1):
+                acc = Gp[t] * E[:, t]
+                for m in range(t + 1, cl):
+                    acc = acc - beta(al, t, m - 1) * st[m] * Gm[m, t] * A[:, m]
+                A[:, t] = acc
+            H = U.T @ A; J = A.T @ Wm; L = np.sum(Gk * A, 0); GA = Gs.T @ A
+            dkg = np.zeros((d, cl)); ddl = np.zeros((d, cl)); dst = np.zeros(cl); dal = np.zeros(cl)
+            for t in range(cl):
+                v = Gam[t] * GA[:, t] + Gp[t] * F[:, t]
+                for j in range(t): v = v + beta(al, j, t - 1) * H[j, t] * K[:, j]
+                for m in range(t + 1, cl): v = v - beta(al, t, m - 1) * st[m] * J[m, t] * K[:, m]
+                dkg[:, t] = -st[t] * v
+                ddl[:, t] = -st[t] * A[:, t]
+                dst[t] = -J[t, t]
+                a = Gam[t] * Gp[t] * trD
+                for m in range(t + 1, cl): a -= Gam[t] * beta(al, t, m - 1) * st[m] * L[m]
+                for j in range(t): a += Gp[t] * beta(al, j, t - 1) * ud[j]
+                for j in range(t):
+                    for m in range(t + 1, cl):
+                        a -= beta(al, j, t - 1) * beta(al, t, m - 1) * st[m] * H[j, m] * Gm[j, m]
+                dal[t] = a
+            DY = dys[b0:b1].T
+            dQt = S0[:d].T @ DY; dQ = P.T @ dQt; Qt = P @ Q
+            dProj = np.zeros_like(Proj)
+            for t in range(cl):
+                p = torch.tensor(Proj[:, t], requires_grad=True)
+                k, dl, s, a, q = gates_t(p, d, eta_scale, alpha_bias, eps, eta_map)
+                lo = (k * torch.tensor(dkg[:, t])).sum() + (dl * torch.tensor(ddl[:, t])).sum() + s * dst[t] + a * dal[t] + (q * torch.tensor(dQ[:, t])).sum()
+                lo.backward(); dProj[:, t] = p.grad.numpy()
+            dXt = S0[d:].T @ dProj
+            dxs[b0:b1] = (P.T @ dXt).T
+            dS0[:d] += DY @ Qt.T
+            dS0[d:] += dProj @ Xt.T
+            dPc += dXt @ X.T + dQt @ Q.T
+            dG = np.prod(al) * dG - (A * (Gam * st)) @ K.T
+        dPn = dPc
+    return dxs, dS0
+
+
+def scan_bwd_blocked(x, init, nh, g, chunk, TB, **kw):
+    B, H, W, D = x.shape; d = D // nh; N = H * W
+    gx = np.zeros_like(x); gi = np.zeros_like(init)
+    for b in range(B):
+        for h in range(nh):
+            for r in range(4):
+                order = route_order(H, W, r)
+                xs = x[b].reshape(N, D)[order, h*d:(h+1)*d]
+                dys = g[b].reshape(N, D)[order, h*d:(h+1)*d]
+                S0 = init[r, h].reshape(4*d + 2, d)
+                dxs, dS0 = chain_blocked(xs, S0, dys, route_chunk(H, W, r, chunk), TB, **kw)
+                tmp = np.zeros((N, d)); tmp[order] = dxs
+                gx[b].reshape(N, D)[:, h*d:(h+1)*d] += tmp
+                gi[r, h] += dS0.reshape(-1)
+    return gx, gi
+
+
+#            B, H, W, D, nh, chunk, TB, options
+BLOCKED_CASES = {
+    "rows7_blocks3": (1, 3, 7, 6, 1, 0, 3, dict(eta_scale=2.0)),           # 7-token rows: blocks 3, 3, 1
+    "chunk10_blocks4_softplus": (1, 4, 5, 8, 2, 10, 4, dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),
+    "clamps_blocks2": (1, 3, 4, 6, 1, 5, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),
+    "chunk20_blocks16": (1, 4, 10, 4, 1, 20, 16, dict(eta_scale=3.0)),      # one full and one 4-token block
+}
+
+
+@pytest.mark.parametrize("name", list(BLOCKED_CASES))
+def test_blocked_backward_equals_gradient_oracle(name):
+    B, H, W, D, nh, chunk, TB, kw = BLOCKED_CASES[name]
+    rng = np.random.Generator(np.random.PCG64(2))
+    d = D // nh
+    S = 4 * d * d + 2 * d
+    x = rng.standard_normal((B, H, W, D))
+    init = rng.standard_normal((4, nh, S)) / np.sqrt(d)
+    g = rng.standard_normal((B, H, W, D))
+    gx, gi = scan_bwd_blocked(x, init, nh, g, chunk, TB, **kw)
     rx, ri = hb.scan2d_backward(x, init, nh, g, chunk=chunk, **kw)
     assert np.abs(gx - rx).max() <= 1e-12 * np.abs(rx).max()
     assert np.abs(gi - ri).max() <= 1e-12 * np.abs(ri).max()
