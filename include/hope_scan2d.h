@@ -271,8 +271,9 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
 
 /* Bytes of workspace hope_scan2d_backward needs: the map-gradient planes of the routes
  * beyond the first, plus per chain the state adjoint and the forward records (at d = 32
- * the product of the earlier chunks' gains and the gain after every 16-token block of
- * each chunk; otherwise every chunk-boundary state and one chunk's gain trajectory);
+ * the product of the earlier chunks' gains and, per 16-token block of each chunk, its end
+ * gain, its token vectors and gates; otherwise every chunk-boundary state and one chunk's
+ * gain trajectory);
  * 0 for arguments it would reject. */
 size_t hope_scan2d_backward_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t chunk,
                                            const hope_scan2d_opts_t* opts);

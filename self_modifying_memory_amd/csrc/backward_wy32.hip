@@ -35,13 +35,15 @@
 // derivative through the |k|^2 floor or the one-ulp rounding of eta_spec; eta_bar = 0
 // (eta = 0 or eta_inj = 0) has derivative 0.
 //
-// A forward sweep writes P_c and every block's end gain to the workspace; the reverse sweep
-// recomputes each block's projections, gates and gain recurrence from them.  S_0 stays in
+// A forward sweep writes P_c and, per block, its end gain, its token vectors (x~, k, delta,
+// q, u, w) and gates to the workspace; the reverse sweep reads them back one block ahead.  S_0 stays in
 // registers for the whole chain: waves 0 and 1 hold column tile w of every row (for S_0^T
 // products), and waves 0-3 the rows of their projection row tiles (for S_0 products); the
-// state adjoint dS_0 is accumulated in registers as 18 16 x 16 tiles spread over the 4
-// waves.  P_c, P_c^T, the two adjoints of P, G_s, dG and the block's per-token vectors
-// (token-major, 16 token slots, padding slots zero) live in LDS: 79 KiB, two chains per CU.
+// state adjoint dS_0 is accumulated in registers as 18 16 x 16 tiles, 8 on each of waves
+// 2-3 and one on each of waves 0-1 (which also form S_0^T products in that phase).  P_c,
+// P_c^T, the two adjoints of P, G_s, dG and the block's per-token vectors (token-major, 16
+// token slots, padding slots zero) live in LDS: 76 KiB, two chains per CU.  The triangular
+// recurrences run right-looking (column by column) on one wave.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -58,6 +60,11 @@ constexpr int kPL = 116;          // stride of a token's projection row (7 row t
 constexpr int kCL = 17;           // stride of the 16 x 16 token matrices
 constexpr int kDD = kD * kD;
 constexpr int kSS = kR * kD;      // state floats
+// Workspace record of a 16-token block, written by the forward sweep: its end gain, then the
+// token-major [16][d] arrays x~, k, delta, q, u, w and eight per-token scalars (step, alpha,
+// the two reciprocal norms, |k|^2, |delta|^2, s_eta, s_alpha).
+constexpr int kBTok = 16 * kD;
+constexpr int kBR = kD * kD + 6 * kBTok + 8 * 16;
 constexpr int kNT = 256;          // threads per chain
 constexpr float kInjInward = 1.f - 1e-3f, kSpecInward = 1.f - 1e-6f, kKappaFloor = 1e-20f;
 
@@ -70,10 +77,14 @@ struct Lane {
 };
 
 // Sum over the 32 lanes of a half wave, in every lane of that half: DPP sums within the
-// 16-lane rows, then the neighbouring row.
+// 16-lane rows, then v_permlane16_swap of the row totals with themselves, which hands each
+// row of a pair (0-1, 2-3) the total of the even row in one result and of the odd row in
+// the other.
 __device__ __forceinline__ float half_total(float v) {
   v = row16_sum(v);
-  return v + __shfl_xor(v, 16, 64);
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
 }
 
 // The thread index through an opaque copy: LDS addresses derived from it are recomputed in
@@ -168,10 +179,11 @@ __device__ __forceinline__ void store_dd(float* M, int mi, int nj, f32x4 acc, co
 }
 
 // Tile idx (0-3) of a d x d matrix in LDS: M <- gc M + sum over the 16 token slots of
-// (A1_t scaled by sc_t) B1_t^T [+ A2_t B2_t^T].
+// (A1_t, scaled by sc_t if kScale) B1_t^T.  (Which operands are present is a template
+// argument: a test of a pointer into LDS against null is not folded by the compiler.)
+template <bool kScale>
 __device__ __forceinline__ void dd_update(float* M, int idx, float gc, const float* A1,
-                                          const float* B1, const float* sc, const float* A2,
-                                          const float* B2, const Lane& L) {
+                                          const float* B1, const float* sc, const Lane& L) {
   const int mi = idx >> 1, nj = idx & 1;
   f32x4 acc;
 #pragma unroll
@@ -179,12 +191,59 @@ __device__ __forceinline__ void dd_update(float* M, int idx, float gc, const flo
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int tk = 4 * s + L.q4;
-    const float f = sc ? sc[tk] : 1.f;
-    acc = mfma4(A1[tk * kLD + 16 * mi + L.r16] * f, B1[tk * kLD + 16 * nj + L.r16], acc);
-    if (A2) acc = mfma4(A2[tk * kLD + 16 * mi + L.r16], B2[tk * kLD + 16 * nj + L.r16], acc);
+    const float a = A1[tk * kLD + 16 * mi + L.r16];
+    acc = mfma4(kScale ? a * sc[tk] : a, B1[tk * kLD + 16 * nj + L.r16], acc);
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * L.q4 + v) * kLD + 16 * nj + L.r16] = acc[v];
+}
+
+// A one-wave triangular recurrence over the 16 token slots, lane = component (the two half
+// waves compute the same values; the lower half stores), right-looking: slot t starts from
+// base_t = g0_t B0_t (+ B1_t), and once v_j is final every later slot t (t > j forward,
+// t < j backward) adds cols[j][t] v_j, so one FMA per step is on the critical path; the
+// coefficient columns are loaded two steps ahead.  kU: the u-recurrence (forward, with the
+// B1 term, v = -gscale * pre stored to Out and pre to Out2); else the a-recurrence
+// (backward, v = pre stored to Out).
+template <bool kU>
+__device__ __forceinline__ void solve_cols(int lane, int bl, const float* cols, const float* g0,
+                                           const float* B0, const float* B1, float* Out,
+                                           float* Out2, const float* gscale) {
+  constexpr bool kBack = !kU;
+  const int c = lane & 31;
+  float acc[kTT], gs[kTT];
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    const float b0 = B0[t * kLD + c];
+    if constexpr (kU) {
+      acc[t] = fmaf(g0[t], b0, B1[t * kLD + c]);
+      gs[t] = gscale[t];
+    } else {
+      acc[t] = g0[t] * b0;
+    }
+  }
+  f32x4 col[3][4];
+  auto load_col = [&](int n) {
+    const int j = kBack ? kTT - 1 - n : n;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) col[n % 3][q] = *reinterpret_cast<const f32x4*>(&cols[j * kTT + 4 * q]);
+  };
+  load_col(0);
+  load_col(1);
+#pragma unroll
+  for (int n = 0; n < kTT; ++n) {
+    const int j = kBack ? kTT - 1 - n : n;
+    if (n + 2 < kTT) load_col(n + 2);
+    const float pre = j < bl ? acc[j] : 0.f;
+    const float val = kU ? -gs[j] * pre : pre;
+    if (lane < 32) {
+      Out[j * kLD + c] = val;
+      if constexpr (kU) Out2[j * kLD + c] = pre;
+    }
+#pragma unroll
+    for (int t = 0; t < kTT; ++t)
+      if (kBack ? t < j : t > j) acc[t] = fmaf(col[n % 3][t >> 2][t & 3], val, acc[t]);
+  }
 }
 
 template <bool XBF>  // the map is bf16 (else fp32)
@@ -193,8 +252,8 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   constexpr int kTok = kTT * kLD;
   constexpr int kMat = kD * kLD;
   constexpr int oSc = 0;                      // per-token scalars, 16 x 16
-  constexpr int oCC = oSc + 16 * kTT;         // 16 x 16 token matrices, 6 x 16 x 17
-  constexpr int oRow = oCC + 6 * kTT * kCL;   // solve coefficient rows, 2 x 16 x 16
+  constexpr int oCC = oSc + 16 * kTT;         // 16 x 16 token matrices, 5 x 16 x 17
+  constexpr int oRow = oCC + 5 * kTT * kCL;   // solve coefficient columns, 2 x 16 x 16
   constexpr int oTok = oRow + 2 * kTT * kTT;  // token-major d-vectors, 15 of them
   constexpr int oProj = oTok + 15 * kTok;     // projections [16][kPL], then their adjoints
   constexpr int oMat = oProj + kTT * kPL;     // P, P^T, two adjoints of P, G_s, dG
@@ -221,25 +280,25 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   float* const sH = sBt + kTT * kCL;   // U^T A
   float* const sJ = sH + kTT * kCL;    // A^T W
   float* const sCm = sJ + kTT * kCL;   // c[t][m] = beta_{t,m-1} step_m for m > t
-  float* const sCf = sCm + kTT * kCL;  // coefficient of k_j in dk_t
-  float* const sRowU = smem + oRow;    // beta_{j,t-1} (k_j . k_t), j < t
-  float* const sRowA = sRowU + kTT * kTT;  // -c[t][m] (k_m . k_t), m > t
+  float* const sColU = smem + oRow;    // [j][t]: beta_{j,t-1} (k_j . k_t), t > j
+  float* const sColA = sColU + kTT * kTT;  // [m][t]: -c[t][m] (k_m . k_t), t < m
   float* const sX = smem + oTok;   // x
+  // x~, k, delta, q, u, w: consecutive, in the order of the block record
   float* const sXt = sX + kTok;    // x~ = P x
   float* const sK = sXt + kTok;    // k
   float* const sDl = sK + kTok;    // delta
   float* const sQ = sDl + kTok;    // q
-  float* const sG = sQ + kTok;     // G_s k
+  float* const sU = sQ + kTok;     // u
+  float* const sW = sU + kTok;     // w
+  float* const sG = sW + kTok;     // G_s k
   float* const sE = sG + kTok;     // dG_e k, then G_s^T a
   float* const sGA = sE;
   float* const sQt = sE + kTok;    // q~ = P q
   float* const sdQt = sQt + kTok;  // dq~ = S_0[mem]^T dy, then dx~
   float* const sdXt = sdQt;
   float* const sdQ = sdQt + kTok;  // P^T dq~
-  float* const sU = sdQ + kTok;    // u
-  float* const sW = sU + kTok;     // w
-  float* const sA = sW + kTok;     // a
-  float* const sF = sA + kTok;     // dG_e^T w
+  float* const sA = sdQ + kTok;    // a
+  float* const sF = sA + kTok;     // dG_e^T w, then the gain part of dk / -step
   float* const sDY = sF + kTok;    // dy
   float* const sProj = smem + oProj;
   float* const sP = smem + oMat;   // P_c
@@ -260,23 +319,36 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   const int C = p.chunk > 0 ? p.chunk : (r < 2 ? W : H);
   const int nck = (N + C - 1) / C;
   const int nbc = (min(C, N) + kTT - 1) / kTT;  // blocks of a full chunk
-  const int64_t kRecC = (int64_t)(1 + nbc) * kDD;
+  // chunk record: P_c, then the records of its blocks
+  const int64_t kRecC = (int64_t)kDD + (int64_t)nbc * kBR;
   float* const dSg = p.chain_ws + (int64_t)blockIdx.x * p.chain_floats;
   float* const recs = dSg + kSS;
   float* const gdst = slot == 0 ? p.grad_x : p.planes + (int64_t)(slot - 1) * p.plane_stride;
   const GateParams gp{p.eta_map, p.eta_scale, p.alpha_bias, p.eps, 0, 0};
   const float* init = p.init + (p.init_per_image ? ((int64_t)b * 4 + r) * nh + h : (int64_t)r * nh + h) * kSS;
 
-  // S_0 in registers.  Waves 0-1 (column tile w): s0t[4T + s] = S_0[16T + 4q4 + s][16w + r16]
-  // for the 9 row tiles T.  Every wave: projection row tiles T = 2 + 2w + sl (sl = 0, 1;
-  // T <= 8): s0p[8 sl + s] = S_0[16T + r16][8q4 + s].
-  float s0t[36], s0p[16];
+  // Registers held for the whole chain, by role:
+  //   waves 0-1: reg4[T][s] = S_0[16T + 4q4 + s][16w + r16] for the 9 row tiles T (column
+  //     tile w of S_0, for S_0^T products), and reg4[9] their one tile of dS_0;
+  //   waves 2-3: reg4[0..7] their eight tiles of dS_0;
+  //   every wave: projection row tiles T = 2 + 2w + sl (sl = 0, 1; T <= 8) of S_0,
+  //     s0p[8 sl + s] = S_0[16T + r16][8q4 + s].
+  // dS_0 tiles (row tile RT, column tile n): waves 0-1 hold (8, w), the gate rows; wave 2 the
+  // row tiles 0, 2, 3, 4 and wave 3 the row tiles 1, 5, 6, 7 (both column tiles each), so
+  // that every wave runs the same number of products in the adjoint phase.
+  f32x4 reg4[10];
+  float s0p[16];
   {
     const Lane L = stage_lane_of(tid);
 #pragma unroll
     for (int e = 0; e < 36; ++e) {
       const int row = 16 * (e >> 2) + 4 * L.q4 + (e & 3);
-      s0t[e] = (w < 2 && row < kR) ? init[row * kD + 16 * w + L.r16] : 0.f;
+      reg4[e >> 2][e & 3] = (w < 2 && row < kR) ? init[row * kD + 16 * w + L.r16] : 0.f;
+    }
+    reg4[9] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (w >= 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) reg4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -284,9 +356,11 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
       s0p[e] = row < kR ? init[row * kD + 8 * L.q4 + (e & 7)] : 0.f;
     }
   }
-  f32x4 dsa[5];  // dS_0 tiles o = w + 4 i (o < 18): rows 16 (o >> 1) .., columns 16 (o & 1) ..
-#pragma unroll
-  for (int i = 0; i < 5; ++i) dsa[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row tile of dS_0 tile i (0-7, column tile i & 1) of waves 2-3
+  auto dtile_row = [&](int i) {
+    const int g = i >> 1;
+    return g == 0 ? w - 2 : (w == 2 ? 1 : 4) + g;
+  };
 
   // identity P_0, zero adjoint of P_nck
   for (int e = tid; e < kDD; e += kNT) {
@@ -299,7 +373,22 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   // block starts.  The loads are unconditional (padding slots read the block's last token
   // and are zeroed when written to LDS), so nothing waits for them before then.
   uint32_t fx[2];  // raw bits of x (bf16 in the low half, or fp32)
-  float fdy[2], fg[4];
+  float fdy[2], fg[4], ftk[12], fsc;
+  // Route pixel of position s0 + t (t < 16) of this chain's route: for the column routes one
+  // division of the block's first position by H (uniform) and a per-slot step from it.
+  auto block_pixel = [&](int s0, int t) {
+    if (r < 2) return (r & 1) ? N - 1 - s0 - t : s0 + t;
+    const int b0 = (r & 1) ? N - 1 - s0 : s0;
+    int q = b0 / H, m = b0 - q * H;
+    if (r & 1) {
+      m -= t;
+      while (m < 0) { m += H; --q; }
+    } else {
+      m += t;
+      while (m >= H) { m -= H; ++q; }
+    }
+    return m * W + q;
+  };
   auto block_len = [&](int c, int i) {
     const int cl = min(C, N - c * C);
     return min(kTT, cl - kTT * i);
@@ -309,16 +398,23 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int e = t0 + kNT * k, t = min(e >> 5, bl - 1), j = e & 31;
-      const int pix = route_pixel(r, s0 + t, H, W, N);
+      const int pix = block_pixel(s0, t);
       const int64_t idx = ((int64_t)b * N + pix) * Dt + (int64_t)h * kD + j;
       if (XBF) fx[k] = static_cast<const uint16_t*>(p.x)[idx];
       else fx[k] = __float_as_uint(static_cast<const float*>(p.x)[idx]);
       if (rev) fdy[k] = p.grad_out[idx];
     }
-    if (rev && i > 0) {
-      const float* g = recs + (int64_t)c * kRecC + (int64_t)i * kDD;  // end gain of block i - 1
+    if (rev) {
+      // block i's record, and the end gain of block i - 1 (for block 0 a load of its own,
+      // unused: every load here is unconditional, so that the registers it fills are the
+      // ones the commit reads and nothing waits for it before then)
+      const float* br = recs + (int64_t)c * kRecC + kDD + (int64_t)i * kBR;
+      const float* g = i > 0 ? br - kBR : br;
 #pragma unroll
       for (int k = 0; k < 4; ++k) fg[k] = g[t0 + kNT * k];
+#pragma unroll
+      for (int k = 0; k < 12; ++k) ftk[k] = br[kDD + t0 + kNT * k];
+      fsc = br[kDD + 6 * kBTok + (t0 & (8 * kTT - 1))];
     }
   };
   auto commit = [&](int c, int i, bool rev) {
@@ -336,8 +432,15 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         const int e = t0 + kNT * k, ri = e >> 5, j = e & 31;
         sGs[ri * kLD + j] = i > 0 ? fg[k] : (ri == j ? 1.f : 0.f);
       }
+      // x~, k, delta, q, u, w (six consecutive token arrays) and the scalars
+#pragma unroll
+      for (int k = 0; k < 12; ++k) {
+        const int e = t0 + kNT * k, a = e >> 9, t = (e >> 5) & 15, j = e & 31;
+        sXt[a * kTok + t * kLD + j] = ftk[k];
+      }
+      if (t0 < 8 * kTT) tSt[t0] = fsc;
     }
-    if (t0 < kTT) pixb[t0] = t0 < bl ? route_pixel(r, s0 + t0, H, W, N) : 0;
+    if (t0 < kTT) pixb[t0] = t0 < bl ? block_pixel(s0, t0) : 0;
   };
   // projections of the block: Proj[t][pr] = S_0[32 + pr] . x~_t, row tiles 2 + 2w + sl
   auto projections = [&]() {
@@ -430,49 +533,6 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
     else if (j == 2) tGS[t] = -gm * tSt[t];
     else if (j == 3 && t == 0) tMisc[0] = gc;
   };
-  // A one-wave triangular recurrence over the 16 token slots, lane = component (the two
-  // half waves compute the same values; the lower half stores):
-  // v_t = base_t + sum_j rows[t][j] v_j over the already computed j (j < t forward,
-  // j > t backward); the coefficient row of the next step is loaded during this one.
-  auto solve_rows = [&](bool backward, int bl, const float* rows, const float* g0, const float* B0,
-                        const float* B1, float* Out, float* Out2, const float* gscale) {
-    const int lane = stage_lane(tid) & 63, c = lane & 31;
-    float v[kTT];
-#pragma unroll
-    for (int t = 0; t < kTT; ++t) v[t] = 0.f;
-    f32x4 row[4], nxt[4];
-    float ng, nb0, nb1 = 0.f, ngs = 0.f;
-    auto load_step = [&](int t) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const f32x4*>(&rows[t * kTT + 4 * q]);
-      ng = g0[t];
-      nb0 = B0[t * kLD + c];
-      if (B1) nb1 = B1[t * kLD + c];
-      if (gscale) ngs = gscale[t];
-    };
-    load_step(backward ? kTT - 1 : 0);
-#pragma unroll
-    for (int n = 0; n < kTT; ++n) {
-      const int t = backward ? kTT - 1 - n : n;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) row[q] = nxt[q];
-      const float g = ng, b0 = nb0, b1 = nb1, gs = ngs;
-      if (n + 1 < kTT) load_step(backward ? t - 1 : t + 1);
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < kTT; ++j)
-        if (backward ? j > t : j < t) acc[j & 3] = fmaf(row[j >> 2][j & 3], v[j], acc[j & 3]);
-      const float base = B1 ? fmaf(g, b0, b1) : g * b0;
-      const float pre = t < bl ? base + ((acc[0] + acc[1]) + (acc[2] + acc[3])) : 0.f;
-      const float val = gscale ? -gs * pre : pre;
-      v[t] = val;
-      if (lane < 32) {
-        Out[t * kLD + c] = val;
-        if (Out2) Out2[t * kLD + c] = pre;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
   auto dtok = [&](float* Out, const float* M, bool trans, const float* In, int m) {
     const Lane L = stage_lane_of(tid);
     store_tokens(Out, m, tok_prod(M, trans, In, m, L), L);
@@ -485,25 +545,29 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
     const Lane L = stage_lane_of(tid);
     store_diag(Out, gram_tokens(A, B, L), L);
   };
-  auto ddu = [&](float* M, int idx, float gc, const float* A1, const float* B1, const float* sc,
-                 const float* A2, const float* B2) {
+  auto ddu = [&](float* M, int idx, float gc, const float* A1, const float* B1) {
     const Lane L = stage_lane_of(tid);
-    dd_update(M, idx, gc, A1, B1, sc, A2, B2, L);
+    dd_update<false>(M, idx, gc, A1, B1, nullptr, L);
   };
-  // u-solve coefficient rows beta_{j,t-1} (k_j . k_t), j < t (wave 0, 4 per lane)
-  auto u_rows = [&]() {
+  auto ddu_scaled = [&](float* M, int idx, float gc, const float* A1, const float* B1, const float* sc) {
+    const Lane L = stage_lane_of(tid);
+    dd_update<true>(M, idx, gc, A1, B1, sc, L);
+  };
+  // u-solve coefficient columns: u_j enters w_t with beta_{j,t-1} (k_j . k_t), t > j
+  // (wave 0, 4 per lane)
+  auto u_cols = [&]() {
     const int lane = stage_lane(tid) & 63;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int e = lane + 64 * k, t = e >> 4, j = e & 15;
-      sRowU[e] = j < t ? sBt[j * kCL + t - 1] * sGm[j * kCL + t] : 0.f;
+      const int e = lane + 64 * k, j = e >> 4, t = e & 15;
+      sColU[e] = j < t ? sBt[j * kCL + t - 1] * sGm[j * kCL + t] : 0.f;
     }
   };
 
   fetch(0, 0, false);
   __syncthreads();
 
-  // ---- forward sweep: P_c and every block's end gain into the workspace -------------------
+  // ---- forward sweep: P_c and every block's record into the workspace ---------------------
   // (barriers order LDS only; global loads stay in flight across them, and the stores are
   // issued after the next block's prefetch so that waiting for the prefetch skips them)
   for (int c = 0; c < nck; ++c) {
@@ -516,8 +580,11 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
     for (int i = 0; i < nb; ++i) {
       const int bl = block_len(c, i);
       commit(c, i, false);
-      if (i + 1 < nb) fetch(c, i + 1, false);
-      else if (c + 1 < nck) fetch(c + 1, 0, false);
+      {
+        // the next block (the current one again after the last: fetched, unused)
+        const bool last_in_chunk = i + 1 == nb, more = c + 1 < nck;
+        fetch(last_in_chunk ? (more ? c + 1 : c) : c, last_in_chunk ? (more ? 0 : i) : i + 1, false);
+      }
       if (i == 0) {
         const int t0 = stage_lane(tid);
 #pragma unroll
@@ -541,20 +608,29 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
       }
       lds_barrier();
       if (w == 0) {
-        u_rows();
-        solve_rows(false, bl, sRowU, tGam, sG, sDl, sU, sW, tSt);
+        u_cols();
+        solve_cols<true>(stage_lane(tid) & 63, bl, sColU, tGam, sG, sDl, sU, sW, tSt);
       }
       lds_barrier();
-      // G_e = Gam_15 G_s + U diag(beta_{., 15}) K^T, in place, and its record
-      ddu(sGs, w, tMisc[0], sU, sK, tGp, nullptr, nullptr);
+      // G_e = Gam_15 G_s + U diag(beta_{., 15}) K^T, in place; the block's record
+      ddu_scaled(sGs, w, tMisc[0], sU, sK, tGp);
+      float* const br = rec + kDD + (int64_t)i * kBR;
+      {
+        const int t0 = stage_lane(tid);
+#pragma unroll
+        for (int k = 0; k < 12; ++k) {
+          const int e = t0 + kNT * k, a = e >> 9, t = (e >> 5) & 15, j = e & 31;
+          br[kDD + e] = sXt[a * kTok + t * kLD + j];
+        }
+        if (t0 < 8 * kTT) br[kDD + 6 * kBTok + t0] = tSt[t0];
+      }
       lds_barrier();
       {
         const int t0 = stage_lane(tid);
-        float* g = rec + (int64_t)(1 + i) * kDD;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int e = t0 + kNT * k;
-          g[e] = sGs[(e >> 5) * kLD + (e & 31)];
+          br[e] = sGs[(e >> 5) * kLD + (e & 31)];
         }
       }
     }
@@ -579,13 +655,24 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
     const int cl = min(C, N - (nck - 1) * C);
     fetch(nck - 1, (cl + kTT - 1) / kTT - 1, true);
   }
+  // P_c and G_C of a chunk, fetched one chunk ahead
+  float fP[4], fGC[4];
+  auto fetch_chunk = [&](int c) {
+    const int t0 = stage_lane(tid), cl = min(C, N - c * C), nb = (cl + kTT - 1) / kTT;
+    const float* rec = recs + (int64_t)c * kRecC;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      fP[k] = rec[t0 + kNT * k];
+      fGC[k] = rec[kDD + (int64_t)(nb - 1) * kBR + t0 + kNT * k];  // end gain of the last block
+    }
+  };
+  fetch_chunk(nck - 1);
   // dx of a block is stored after the next block's prefetch is issued (same reason)
   f32x4 dxv = {0.f, 0.f, 0.f, 0.f};
   float* dxdst = gdst;
   bool dxok = false;
   for (int c = nck - 1; c >= 0; --c) {
     const int cl = min(C, N - c * C), nb = (cl + kTT - 1) / kTT;
-    const float* const rec = recs + (int64_t)c * kRecC;
     // chunk start: P_c, P_c^T and G_C from the record
     lds_barrier();
     {
@@ -593,12 +680,12 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = t0 + kNT * k, i = e >> 5, j = e & 31;
-        const float pv = rec[e];
-        sP[i * kLD + j] = pv;
-        sPT[j * kLD + i] = pv;
-        sGs[i * kLD + j] = rec[(int64_t)nb * kDD + e];
+        sP[i * kLD + j] = fP[k];
+        sPT[j * kLD + i] = fP[k];
+        sGs[i * kLD + j] = fGC[k];
       }
     }
+    if (c > 0) fetch_chunk(c - 1);
     lds_barrier();
     // dG_e of the last block = P_c^T dP_{c+1}; dP_c = dP_{c+1} G_C^T + (the blocks' terms)
     {
@@ -616,14 +703,19 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
       const int bl = block_len(c, i);
       lds_barrier();
       commit(c, i, true);
-      if (i > 0) fetch(c, i - 1, true);
-      else if (c > 0) {
-        const int clp = min(C, N - (c - 1) * C);
-        fetch(c - 1, (clp + kTT - 1) / kTT - 1, true);
+      {
+        // the next block in reverse order (the current one again after the first)
+        const int cn = i > 0 ? c : (c > 0 ? c - 1 : c);
+        const int cln = min(C, N - cn * C);
+        const int in = i > 0 ? i - 1 : (c > 0 ? (cln + kTT - 1) / kTT - 1 : i);
+        fetch(cn, in, true);
       }
       if (dxok) *reinterpret_cast<f32x4*>(dxdst) = dxv;
       lds_barrier();
-      // dq~ = S_0[mem]^T dy (waves 0-1); x~ = P x (waves 2-3)
+      // the block's forward values come from its record; alpha products (every thread);
+      // dq~ = S_0[mem]^T dy tile w and K^T K (wave 0) or G_s k (wave 1); dG_e k (wave 2);
+      // q~ = P q (wave 3)
+      alpha_products();
       if (w < 2) {
         const Lane L = stage_lane_of(tid);
         f32x4 dy4[2];
@@ -633,25 +725,14 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) acc = mfma4(s0t[4 * T + s], dy4[T][s], acc);
+          for (int s = 0; s < 4; ++s) acc = mfma4(reg4[T][s], dy4[T][s], acc);
         store_tokens(sdQt, w, acc, L);
-      } else {
-        dtok(sXt, sP, false, sX, w - 2);
-      }
-      lds_barrier();
-      projections();
-      lds_barrier();
-      gates(bl);
-      lds_barrier();
-      // K^T K and dq = P^T dq~ (wave 0), G_s k (wave 1), dG_e k (wave 2), q~ = P q (wave 3)
-      alpha_products();
-      if (w == 0) {
-        gram(sGm, sK, sK);
-        dtok(sdQ, sPT, false, sdQt, 0);
-        dtok(sdQ, sPT, false, sdQt, 1);
-      } else if (w == 1) {
-        dtok(sG, sGs, false, sK, 0);
-        dtok(sG, sGs, false, sK, 1);
+        if (w == 0) {
+          gram(sGm, sK, sK);
+        } else {
+          dtok(sG, sGs, false, sK, 0);
+          dtok(sG, sGs, false, sK, 1);
+        }
       } else if (w == 2) {
         dtok(sE, sdG, false, sK, 0);
         dtok(sE, sdG, false, sK, 1);
@@ -660,32 +741,28 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         dtok(sQt, sP, false, sQ, 1);
       }
       lds_barrier();
-      // u and w (wave 0); c and the a-solve rows (wave 1); dP_c += dq~ q^T (waves 2-3)
+      // c, the a-solve columns and a (wave 0); F = dG_e^T W (wave 1); dq = P^T dq~ and
+      // diag(U^T E) (wave 2); dP_c += dq~ q^T and <G_s, dG_e> (wave 3)
       if (w == 0) {
-        u_rows();
-        solve_rows(false, bl, sRowU, tGam, sG, sDl, sU, sW, tSt);
-      } else if (w == 1) {
         const int lane = stage_lane(tid) & 63;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int e = lane + 64 * k, t = e >> 4, m = e & 15;
           const float cm = m > t ? sBt[t * kCL + m - 1] * tSt[m] : 0.f;
           sCm[t * kCL + m] = cm;
-          sRowA[t * kTT + m] = -cm * sGm[m * kCL + t];
+          sColA[m * kTT + t] = -cm * sGm[m * kCL + t];
         }
-      } else {
-        ddu(sdPc, 2 * (w - 2), 1.f, sdQt, sQ, nullptr, nullptr, nullptr);
-        ddu(sdPc, 2 * (w - 2) + 1, 1.f, sdQt, sQ, nullptr, nullptr, nullptr);
-      }
-      lds_barrier();
-      // a (wave 0); F = dG_e^T W (wave 1); diag(U^T E) and <G_s, dG_e> (wave 2)
-      if (w == 0) {
-        solve_rows(true, bl, sRowA, tGp, sE, nullptr, sA, nullptr, nullptr);
+        solve_cols<false>(lane, bl, sColA, tGp, sE, nullptr, sA, nullptr, nullptr);
       } else if (w == 1) {
         dtok(sF, sdG, true, sW, 0);
         dtok(sF, sdG, true, sW, 1);
       } else if (w == 2) {
+        dtok(sdQ, sPT, false, sdQt, 0);
+        dtok(sdQ, sPT, false, sdQt, 1);
         gram_diag(tUd, sU, sE);
+      } else {
+#pragma unroll
+        for (int idx = 0; idx < 4; ++idx) ddu(sdPc, idx, 1.f, sdQt, sQ);
         const int lane = stage_lane(tid) & 63;
         float tr = 0.f;
 #pragma unroll 4
@@ -708,12 +785,14 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         dtok(sGA, sGs, true, sA, 1);
       } else {
         if (w == 2) gram_diag(tL, sG, sA);
-        ddu(sdG, 2 * (w - 2), tMisc[0], sA, sK, tGS, nullptr, nullptr);
-        ddu(sdG, 2 * (w - 2) + 1, tMisc[0], sA, sK, tGS, nullptr, nullptr);
+        ddu_scaled(sdG, 2 * (w - 2), tMisc[0], sA, sK, tGS);
+        ddu_scaled(sdG, 2 * (w - 2) + 1, tMisc[0], sA, sK, tGS);
       }
       lds_barrier();
       // dalpha_t from the gain (wave 0, through the 16 x 16 product inner = (H o K^T K) c^T);
-      // the coefficients of k_j in dk_t (waves 1-3)
+      // the gain part of dk_t / -step_t (waves 1-2, column tile w - 1, over F in place):
+      // Gam_{t-1} G_s^T a_t + Gam'_t F_t + sum_j cf[j][t] k_j with cf[j][t] =
+      // beta_{j,t-1} H[j][t] (j < t) or -c[t][j] J[j][t] (j > t)
       if (w == 0) {
         const Lane L = stage_lane_of(tid);
         const int r16 = L.r16, q4 = L.q4;
@@ -740,14 +819,26 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           for (int m = 0; m < kTT; ++m) lsum = fmaf(sCm[t * kCL + m], tL[m], lsum);
           tDal[t] = part + tGam[t] * (gp1 * tMisc[1] - lsum);
         }
-      } else {
-        for (int e = stage_lane(tid) - 64; e < kTT * kTT; e += 192) {
-          const int t = e >> 4, j = e & 15;
+      } else if (w <= 2) {
+        const Lane L = stage_lane_of(tid);
+        const int n = w - 1, r16 = L.r16, q4 = L.q4, col = 16 * n + r16;
+        f32x4 acc;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = 4 * q4 + v;
+          acc[v] = fmaf(tGam[t], sGA[t * kLD + col], tGp[t] * sF[t * kLD + col]);
+        }
+        // A[t = r16][j = 4 s + q4] = cf[j][t], B[j][c] = k_j[16 n + c]
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int j = 4 * s4 + q4, t = r16;
           float cf = 0.f;
           if (j < t) cf = sBt[j * kCL + t - 1] * sH[j * kCL + t];
           else if (j > t) cf = -sCm[t * kCL + j] * sJ[j * kCL + t];
-          sCf[j * kCL + t] = cf;
+          acc = mfma4(cf, sK[j * kLD + col], acc);
         }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sF[(4 * q4 + v) * kLD + col] = acc[v];
       }
       lds_barrier();
       // token by token: the gain adjoints, then the readout, the step, the gates, the
@@ -761,10 +852,7 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           const int t = w + 4 * hh + 8 * u;
           const float st = tSt[t];
           const float at = sA[t * kLD + c];
-          float gk = fmaf(tGam[t], sGA[t * kLD + c], tGp[t] * sF[t * kLD + c]);
-#pragma unroll
-          for (int j = 0; j < kTT; ++j) gk = fmaf(sCf[j * kCL + t], sK[j * kLD + c], gk);
-          dk[u] = -st * gk;
+          dk[u] = -st * sF[t * kLD + c];
           ddl[u] = -st * at;
           dstep[u] = -sJ[t * kCL + t];
           dalpha[u] = tDal[t];
@@ -854,25 +942,32 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           for (int T = 2; T < 9; ++T)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              if (s & 1) acc1 = mfma4(s0t[4 * T + s], pv[T - 2][s], acc1);
-              else acc0 = mfma4(s0t[4 * T + s], pv[T - 2][s], acc0);
+              if (s & 1) acc1 = mfma4(reg4[T][s], pv[T - 2][s], acc1);
+              else acc0 = mfma4(reg4[T][s], pv[T - 2][s], acc0);
             }
           store_tokens(sdXt, w, acc0 + acc1, L);
         }
+        // acc += sum over the token slots of [dy ; dProj]_t (rows of tile RT) [q~ ; x~]_t^T
+        // (columns of tile n)
+        // (mem: a tile of the M_mem rows, RT < 2)
+        auto ds_update = [&](f32x4 acc, bool mem, int RT, int n) {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          const int o = w + 4 * i;
-          if (o < 18) {
-            const int RT = o >> 1, n = o & 1;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int tk = 4 * s + q4;
-              const float av = RT < 2 ? sDY[tk * kLD + 16 * RT + r16] : sProj[tk * kPL + 16 * (RT - 2) + r16];
-              const float bv = RT < 2 ? sQt[tk * kLD + 16 * n + r16] : sXt[tk * kLD + 16 * n + r16];
-              dsa[i] = mfma4(av, bv, dsa[i]);
-            }
+          for (int s = 0; s < 4; ++s) {
+            const int tk = 4 * s + q4;
+            const float av = mem ? sDY[tk * kLD + 16 * RT + r16] : sProj[tk * kPL + 16 * (RT - 2) + r16];
+            const float bv = mem ? sQt[tk * kLD + 16 * n + r16] : sXt[tk * kLD + 16 * n + r16];
+            acc = mfma4(av, bv, acc);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          return acc;
+        };
+        if (w < 2) {
+          reg4[9] = ds_update(reg4[9], false, 8, w);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            reg4[i] = ds_update(reg4[i], i < 2, dtile_row(i), i & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       lds_barrier();
@@ -883,8 +978,8 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         dxok = L.r16 < bl;
         dxdst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
       } else {
-        ddu(sdPc, 2 * (w - 2), 1.f, sdXt, sX, nullptr, nullptr, nullptr);
-        ddu(sdPc, 2 * (w - 2) + 1, 1.f, sdXt, sX, nullptr, nullptr, nullptr);
+        ddu(sdPc, 2 * (w - 2), 1.f, sdXt, sX);
+        ddu(sdPc, 2 * (w - 2) + 1, 1.f, sdXt, sX);
       }
     }
     // dP_c is complete: it is the next chunk's dP_{c+1}
@@ -897,17 +992,18 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   // the initial-state adjoint of this chain, for the gradient reduction
   {
     const Lane L = stage_lane_of(tid);
+    auto store_tile = [&](f32x4 acc, int RT, int n) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int o = w + 4 * i;
-      if (o < 18) {
-        const int RT = o >> 1, n = o & 1;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 16 * RT + 4 * L.q4 + v;
-          if (row < kR) dSg[row * kD + 16 * n + L.r16] = dsa[i][v];
-        }
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * RT + 4 * L.q4 + v;
+        if (row < kR) dSg[row * kD + 16 * n + L.r16] = acc[v];
       }
+    };
+    if (w < 2) {
+      store_tile(reg4[9], 8, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) store_tile(reg4[i], dtile_row(i), i & 1);
     }
   }
 }
@@ -919,11 +1015,11 @@ bool backward_wy32_supported(const BackParams& p, int d) {
   return d == kD;
 }
 
-// Workspace floats per chain: the state adjoint, then per chunk P_c and the end gain of
-// each 16-token block.
+// Workspace floats per chain: the state adjoint, then per chunk P_c and the records of its
+// 16-token blocks.
 int64_t backward_wy32_chain_floats(int64_t nck, int64_t cmax) {
   const int64_t nb = (cmax + kTT - 1) / kTT;
-  return ((int64_t)kSS + nck * (1 + nb) * kDD + 63) / 64 * 64;
+  return ((int64_t)kSS + nck * ((int64_t)kDD + nb * kBR) + 63) / 64 * 64;
 }
 
 hipError_t launch_chain_backward_wy32(const BackParams& p, hipStream_t stream) {

@@ -217,19 +217,21 @@ def test_backward_workspace_size(lib):
     per_chain = ((5 + 1) * 1056 + 5 * 16 * 16 + 63) // 64 * 64
     want = (3 * plane + 4 * 2 * 2 * per_chain) * 4
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x16), 15, 0, None) == want
-    # d = 32 (blocked kernel), S = 4160: the state adjoint, then per chunk P_c and the gain
-    # after each 16-token block (one block of the 5-token chunks), 5 chunks at most
+    # d = 32 (blocked kernel), S = 4160: the state adjoint, then per chunk P_c (1024) and a
+    # record per 16-token block (its end gain, six 16 x 32 token arrays, 8 x 16 scalars:
+    # 4224); one block per 5-token chunk, 5 chunks at most
+    blk = 1024 + 6 * 16 * 32 + 8 * 16
     x = fmap(B=2, H=4, W=5, D=32, nh=1)
-    per_chain = (4160 + 5 * (1 + 1) * 1024 + 63) // 64 * 64
+    per_chain = (4160 + 5 * (1024 + blk) + 63) // 64 * 64
     want = (3 * plane + 4 * 2 * 1 * per_chain) * 4
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, 0, None) == want
     # route 0 alone: no planes, two chains of 4 row chunks of 5 tokens
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 1, 0, None) == \
-        (2 * ((4160 + 4 * 2 * 1024 + 63) // 64 * 64)) * 4
+        (2 * ((4160 + 4 * (1024 + blk) + 63) // 64 * 64)) * 4
     # rows of 200 tokens at d = 32: one chunk per row, 13 blocks each
     big = fmap(B=1, H=2, W=200, D=32, nh=1)
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(big), 1, 0, None) == \
-        ((4160 + 2 * (1 + 13) * 1024 + 63) // 64 * 64) * 4
+        ((4160 + 2 * (1024 + 13 * blk) + 63) // 64 * 64) * 4
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 0, 0, None) == 0
     assert lib.hope_scan2d_backward_workspace_size(ctypes.byref(x), 15, -1, None) == 0
 
