@@ -150,6 +150,10 @@ LONG_CASES = [
     (1, 56, 6, 32, 1, 12, dict(eta_scale=2.0)),     # 56-token columns
     (1, 4, 128, 32, 1, 3, {}),                      # 128-token rows (high-resolution chunks)
     (1, 128, 3, 32, 1, 12, dict(eta_scale=2.0)),    # 128-token columns
+    (1, 2, 200, 32, 1, 3, {}),                      # 200-token rows: 13 blocks, the last of 8
+    (2, 5, 12, 64, 2, 15, dict(chunk=20, init_per_image=True)),  # chunks of 20 (16 + 4) across rows
+    (1, 6, 7, 32, 1, 15, dict(chunk=42, eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),  # one 42-token chunk
+    (1, 4, 10, 32, 1, 15, dict(chunk=17, eta_scale=40.0, alpha_bias=-1.0)),  # 16 + 1 blocks, clamps bind
 ]
 
 
@@ -163,13 +167,16 @@ def test_backward_long_chunks_match_gradient_oracle(case):
     import torch
     from self_modifying_memory_amd.scan2d import hope_scan2d_backward
     B, H, W, D, nh, dirs, kw = case
+    kw = dict(kw)
+    chunk = kw.pop("chunk", 0)
     print("case", case, flush=True)
-    inp = wl.draw(B, H, W, D, nh, seed=9300 + H + W, dtype="bf16", live=True)
+    inp = wl.draw(B, H, W, D, nh, seed=9300 + H + W, dtype="bf16", live=True,
+                  init_per_image=kw.get("init_per_image", False))
     g = np.random.Generator(np.random.PCG64(96)).standard_normal((B, H, W, D)).astype(np.float32)
     x, init = to_device(inp, "bf16")
-    gx, gi = hope_scan2d_backward(x, init, nh, torch.from_numpy(g).cuda(), dirs, 0, **kw)
+    gx, gi = hope_scan2d_backward(x, init, nh, torch.from_numpy(g).cuda(), dirs, chunk, **kw)
     torch.cuda.synchronize()
-    ref_x, ref_i = hb.scan2d_backward(inp["x"], inp["init"], nh, g, dirs=dirs, **kw)
+    ref_x, ref_i = hb.scan2d_backward(inp["x"], inp["init"], nh, g, dirs=dirs, chunk=chunk, **kw)
     e_x, e_i = _rel(gx.cpu().numpy(), ref_x), _rel(gi.cpu().numpy(), ref_i)
     print(f"  rel grad_x {e_x:.2e} grad_init {e_i:.2e}", flush=True)
     assert e_x <= TOL["f32"] and e_i <= TOL["f32"]
