@@ -8,8 +8,8 @@ outer gradients of the memories' initial states and of the inputs flow through e
 chunk).  The gradient that the backward pass must produce is therefore the derivative
 of the forward operator itself.  This module restates the forward of
 ``hope_oracle.srnl_chain`` / ``scan2d`` step for step in PyTorch float64 operations
-(same order, same formulas; boundary readout, the two gate maps, the default step
-controls) and differentiates it with ``torch.autograd``: the exact derivative of that
+(same order, same formulas; the boundary and the running readout, the two gate maps, the
+default step controls) and differentiates it with ``torch.autograd``: the exact derivative of that
 composition.  Its agreement with the numpy forward and with central finite differences
 of the numpy oracle is pinned in ``tests/test_oracle_backward_pins.py``.
 
@@ -67,9 +67,10 @@ def _executed_step(eta, alpha, k, delta, eps):
     return torch.where(eta_bar <= lim, eta_bar, lim)
 
 
-def _chain(xs, st, chunk, eta_map, eta_scale, alpha_bias, eps):
-    """srnl_chain (boundary readout, default controls) in torch fp64: xs [n, N, d],
-    st name -> [n, rows, d]; returns ys [n, N, d]."""
+def _chain(xs, st, chunk, eta_map, eta_scale, alpha_bias, eps, readout="boundary"):
+    """srnl_chain (default controls) in torch fp64: xs [n, N, d], st name -> [n, rows, d];
+    returns ys [n, N, d].  readout "boundary" reads the chunk-start memory, "running" the
+    memory as updated by every earlier token."""
     n, N, d = xs.shape
     M = dict(st)
     eye = torch.eye(d, dtype=_T)
@@ -83,7 +84,8 @@ def _chain(xs, st, chunk, eta_map, eta_scale, alpha_bias, eps):
             q = _normalize(_mv(Mb["q"], x), eps)
             eta = _phi_eta(_mv(Mb["eta"], x)[:, 0], eta_map, eta_scale)
             alpha = torch.sigmoid(_mv(Mb["alpha"], x)[:, 0] + alpha_bias)
-            ys.append(_mv(Mb["mem"], q))                        # y_t = M^m_b q_t
+            # y_t = M^m_b q_t, or M^m_{t-1} q_t (running: M not yet updated by token t)
+            ys.append(_mv(Mb["mem"] if readout == "boundary" else M["mem"], q))
             delta = k - v
             step = _executed_step(eta, alpha, k, delta, eps)
             A = alpha[:, None, None] * eye - step[:, None, None] * (k[:, :, None] * k[:, None, :])
@@ -105,7 +107,7 @@ def _unflatten(flat, d):
 
 def scan2d_torch(x, init, n_heads: int, dirs: int = 15, chunk: int = 0, eta_map: str = "sigmoid",
                  eta_scale: float = 1.0, alpha_bias: float = 4.0, eps: float = NORM_EPS,
-                 init_per_image: bool = False):
+                 init_per_image: bool = False, readout: str = "boundary"):
     """The whole operator of ``hope_oracle.scan2d`` in torch fp64 (x, init: fp64 tensors)."""
     B, H, W, D = x.shape
     d = D // n_heads
@@ -120,7 +122,7 @@ def scan2d_torch(x, init, n_heads: int, dirs: int = 15, chunk: int = 0, eta_map:
             xs = flat_x[:, order, h * d:(h + 1) * d]           # cross-scan ([VH] Eq. 24)
             flat = init[:, r, h] if init_per_image else init[r, h].expand(B, -1)
             st = _unflatten(flat, d)
-            ys = _chain(xs, st, route_chunk(H, W, r, chunk), eta_map, eta_scale, alpha_bias, eps)
+            ys = _chain(xs, st, route_chunk(H, W, r, chunk), eta_map, eta_scale, alpha_bias, eps, readout)
             pad = torch.zeros((B, N, D), dtype=_T)
             pad[:, :, h * d:(h + 1) * d] = pad[:, :, h * d:(h + 1) * d].index_add(1, order, ys)
             out = out + pad                                     # cross-merge ([VH] Eq. 26)
@@ -129,12 +131,13 @@ def scan2d_torch(x, init, n_heads: int, dirs: int = 15, chunk: int = 0, eta_map:
 
 def scan2d_backward(x, init, n_heads: int, grad_out, dirs: int = 15, chunk: int = 0,
                     eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
-                    eps: float = NORM_EPS, init_per_image: bool = False):
+                    eps: float = NORM_EPS, init_per_image: bool = False, readout: str = "boundary"):
     """Gradients of sum(grad_out * scan2d(x, init)) with respect to x [B, H, W, D] and
     init ([4, n_heads, S], or [B, 4, n_heads, S] with init_per_image); fp64 numpy arrays."""
     xt = torch.tensor(np.asarray(x, dtype=np.float64), dtype=_T, requires_grad=True)
     it = torch.tensor(np.asarray(init, dtype=np.float64), dtype=_T, requires_grad=True)
     go = torch.tensor(np.asarray(grad_out, dtype=np.float64), dtype=_T)
-    out = scan2d_torch(xt, it, n_heads, dirs, chunk, eta_map, eta_scale, alpha_bias, eps, init_per_image)
+    out = scan2d_torch(xt, it, n_heads, dirs, chunk, eta_map, eta_scale, alpha_bias, eps, init_per_image,
+                       readout)
     (out * go).sum().backward()
     return xt.grad.numpy(), it.grad.numpy()

@@ -161,10 +161,18 @@ def test_chunk_parallel_backward_equals_gradient_oracle(name):
 # TB tokens; G_s, the gain before a block, replaces I in the low-rank forms, the adjoint of
 # each block's end gain is carried to the previous block, and P_c's adjoint picks up
 # dP_{c+1} G_C^T with G_C the chunk's end gain.
-def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, eta_map="sigmoid"):
+# With the running readout y_t = S0[mem] P_c G_{t-1} q_t, the readout adjoint r_t = P_c^T S0[mem]^T dy_t
+# enters every earlier gain: dG_{t-1} gains r_t q_t^T, so inside a block
+#   dG_t = Gam'_t dG_e + sum_{m>t} beta_{t,m-1} (r_m q_m^T - step_m a_m k_m^T),
+# the a-recurrence's base gains sum_{m>t} beta_{t,m-1} (q_m . k_t) r_m, dk and dalpha gain the
+# matching terms, dq_t = G_{t-1}^T r_t, and the readout's reads of P_c and S0[mem] use
+# G_{t-1} q_t in place of q_t.
+def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, eta_map="sigmoid",
+                  readout="boundary"):
     N, d = xs.shape
     nck = (N + C - 1) // C
     I = np.eye(d)
+    running = readout == "running"
 
     def beta(al, j, t):  # prod_{i=j+1..t} al_i
         return float(np.prod(al[j + 1:t + 1]))
@@ -189,7 +197,15 @@ def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, e
             U[:, t] = -st[t] * acc
         bE = np.array([beta(al, j, c - 1) for j in range(c)])
         Ge = np.prod(al) * Gs + U @ np.diag(bE) @ K.T
-        return X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, Ge
+        # G_{t-1} q_t: what the running readout reads (q_t itself for the boundary readout)
+        RQ = Q.copy()
+        if running:
+            for t in range(c):
+                acc = float(np.prod(al[:t])) * (Gs @ Q[:, t])
+                for j in range(t):
+                    acc = acc + beta(al, j, t - 1) * float(K[:, j] @ Q[:, t]) * U[:, j]
+                RQ[:, t] = acc
+        return X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, Ge, RQ
 
     def blocks(c):
         s0, s1 = c * C, min(N, (c + 1) * C)
@@ -202,7 +218,7 @@ def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, e
         Gs = I.copy(); st_c = []
         for b0, b1 in blocks(c):
             st_c.append(Gs.copy())
-            Gs = block_fwd(P, Gs, b0, b1)[-1]
+            Gs = block_fwd(P, Gs, b0, b1)[-2]
         starts.append((st_c, Gs))
         P = P @ Gs
     dPn = np.zeros((d, d)); dS0 = np.zeros_like(S0); dxs = np.zeros_like(xs)
@@ -214,23 +230,31 @@ def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, e
         for i in range(len(st_c) - 1, -1, -1):
             b0, b1 = blocks(c)[i]
             Gs = st_c[i]
-            X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, _ = block_fwd(P, Gs, b0, b1)
+            X, Xt, Proj, K, Dl, Q, st, al, Gm, Gk, U, Wm, _, RQ = block_fwd(P, Gs, b0, b1)
             cl = b1 - b0
             Gam = np.array([np.prod(al[:t]) for t in range(cl)])        # Gamma_{t-1}
             Gp = np.array([np.prod(al[t + 1:]) for t in range(cl)])     # Gamma'_t
             E = dG @ K; F = dG.T @ Wm; trD = np.sum(Gs * dG); ud = np.sum(U * E, 0)
+            DY = dys[b0:b1].T
+            dQt = S0[:d].T @ DY
+            R = P.T @ dQt                                                # readout adjoints r_t
             A = np.zeros((d, cl))
             for t in range(cl - 1, -1, -1):
                 acc = Gp[t] * E[:, t]
                 for m in range(t + 1, cl):
                     acc = acc - beta(al, t, m - 1) * st[m] * Gm[m, t] * A[:, m]
+                    if running:
+                        acc = acc + beta(al, t, m - 1) * float(Q[:, m] @ K[:, t]) * R[:, m]
                 A[:, t] = acc
             H = U.T @ A; J = A.T @ Wm; L = np.sum(Gk * A, 0); GA = Gs.T @ A
             dkg = np.zeros((d, cl)); ddl = np.zeros((d, cl)); dst = np.zeros(cl); dal = np.zeros(cl)
+            dQ = R.copy()                                                # G_{t-1}^T r_t (running)
             for t in range(cl):
                 v = Gam[t] * GA[:, t] + Gp[t] * F[:, t]
                 for j in range(t): v = v + beta(al, j, t - 1) * H[j, t] * K[:, j]
                 for m in range(t + 1, cl): v = v - beta(al, t, m - 1) * st[m] * J[m, t] * K[:, m]
+                if running:
+                    for m in range(t + 1, cl): v = v + beta(al, t, m - 1) * float(R[:, m] @ Wm[:, t]) * Q[:, m]
                 dkg[:, t] = -st[t] * v
                 ddl[:, t] = -st[t] * A[:, t]
                 dst[t] = -J[t, t]
@@ -240,9 +264,16 @@ def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, e
                 for j in range(t):
                     for m in range(t + 1, cl):
                         a -= beta(al, j, t - 1) * beta(al, t, m - 1) * st[m] * H[j, m] * Gm[j, m]
+                if running:
+                    for m in range(t + 1, cl):
+                        a += Gam[t] * beta(al, t, m - 1) * float(R[:, m] @ (Gs @ Q[:, m]))
+                        for j in range(t):
+                            a += (beta(al, j, t - 1) * beta(al, t, m - 1) * float(U[:, j] @ R[:, m])
+                                  * float(K[:, j] @ Q[:, m]))
+                    dQ[:, t] = Gam[t] * (Gs.T @ R[:, t])
+                    for j in range(t): dQ[:, t] += beta(al, j, t - 1) * float(U[:, j] @ R[:, t]) * K[:, j]
                 dal[t] = a
-            DY = dys[b0:b1].T
-            dQt = S0[:d].T @ DY; dQ = P.T @ dQt; Qt = P @ Q
+            Qt = P @ RQ
             dProj = np.zeros_like(Proj)
             for t in range(cl):
                 p = torch.tensor(Proj[:, t], requires_grad=True)
@@ -253,8 +284,10 @@ def chain_blocked(xs, S0, dys, C, TB, eta_scale=1.0, alpha_bias=4.0, eps=1e-6, e
             dxs[b0:b1] = (P.T @ dXt).T
             dS0[:d] += DY @ Qt.T
             dS0[d:] += dProj @ Xt.T
-            dPc += dXt @ X.T + dQt @ Q.T
+            dPc += dXt @ X.T + dQt @ RQ.T
             dG = np.prod(al) * dG - (A * (Gam * st)) @ K.T
+            if running:
+                dG = dG + (R * Gam) @ Q.T
         dPn = dPc
     return dxs, dS0
 
@@ -282,6 +315,10 @@ BLOCKED_CASES = {
     "chunk10_blocks4_softplus": (1, 4, 5, 8, 2, 10, 4, dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),
     "clamps_blocks2": (1, 3, 4, 6, 1, 5, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),
     "chunk20_blocks16": (1, 4, 10, 4, 1, 20, 16, dict(eta_scale=3.0)),      # one full and one 4-token block
+    "running_rows7_blocks3": (1, 3, 7, 6, 1, 0, 3, dict(eta_scale=2.0, readout="running")),
+    "running_chunk10_blocks4_softplus": (1, 4, 5, 8, 2, 10, 4, dict(eta_map="softplus", eta_scale=0.5,
+                                                                  alpha_bias=1.0, readout="running")),
+    "running_clamps_blocks2": (1, 3, 4, 6, 1, 5, 2, dict(eta_scale=40.0, alpha_bias=-1.0, readout="running")),
 }
 
 

@@ -5,7 +5,8 @@
   the input map and the initial memories, with the step controls active;
 * the content memory enters the output linearly (M_mem,t = M_mem,b G_t and G does not
   depend on M_mem), so its gradient is exactly <grad_out, out(M_mem,0 = E_ij)>, the
-  output with that memory set to a basis matrix and every other memory unchanged.
+  output with that memory set to a basis matrix and every other memory unchanged (for the
+  boundary and the running readout alike).
 """
 import numpy as np
 import pytest
@@ -19,6 +20,11 @@ CASES = {
     "chunk5_softplus": (2, 4, 3, 4, 1, 5, dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),
     "clamps": (1, 3, 3, 6, 1, 2, dict(eta_scale=40.0, alpha_bias=-1.0)),
     "scalar_heads": (1, 3, 3, 2, 2, 0, dict(eta_scale=3.0)),
+    # the running readout ([VH] Sec. 2.2 reading of the memory as updated token by token)
+    "running_aligned": (1, 3, 4, 8, 2, 0, dict(eta_scale=2.0, readout="running")),
+    "running_chunk5_softplus": (2, 4, 3, 4, 1, 5, dict(eta_map="softplus", eta_scale=0.5, alpha_bias=1.0,
+                                                       readout="running")),
+    "running_clamps": (1, 3, 3, 6, 1, 2, dict(eta_scale=40.0, alpha_bias=-1.0, readout="running")),
 }
 
 
@@ -82,7 +88,7 @@ def test_gradients_per_image_initial_state():
     assert np.sum(gi * v) == pytest.approx(fd, rel=2e-6, abs=1e-7)
 
 
-@pytest.mark.parametrize("name", ["aligned_sigmoid", "clamps"])
+@pytest.mark.parametrize("name", ["aligned_sigmoid", "clamps", "running_clamps"])
 def test_content_memory_gradient_is_exact_linear_response(name):
     B, H, W, D, nh, chunk, kw = CASES[name]
     x, init, g = _draw(B, H, W, D, nh, 6)
