@@ -161,7 +161,8 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float = 15.0, readout: str
                       f"processes (fp64 numpy, 1 BLAS thread each)"}
 
 
-def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: float = 15.0) -> dict:
+def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: float = 15.0,
+                          readout: str = "boundary") -> dict:
     """Time the gradient oracle (autograd of the fp64 forward), as it stands, on a bounded
     sample of the first image: its first rows (all of them, and then more heads, when the
     whole map fits the budget), one head, all four routes; the column routes of a crop run
@@ -174,7 +175,7 @@ def cpu_baseline_backward(w: wl.Workload, inp: dict, g: np.ndarray, budget_s: fl
 
     def run(rows, nh):
         hb.scan2d_backward(inp["x"][:1, :rows, :, :nh * d], inp["init"][:, :nh], nh,
-                           g[:1, :rows, :, :nh * d], chunk=w.chunk)
+                           g[:1, :rows, :, :nh * d], chunk=w.chunk, readout=readout)
 
     try:
         r0 = min(w.H, 4)
@@ -219,7 +220,7 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
 
     def step():
         hope_scan2d_backward(x, init, w.n_heads, g, 15, w.chunk, stream=stream, grad_x=gx,
-                             grad_init=gi, workspace=ws)
+                             grad_init=gi, workspace=ws, readout=args.readout)
 
     for _ in range(args.warmup):
         step()
@@ -240,7 +241,7 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
     wall = time.perf_counter() - t0
     call_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     c_avg = float(np.mean(call_ms)) * 1e-3
-    roof = roofline_numbers(w)
+    roof = roofline_numbers(w, readout=args.readout)
     flops = 3 * roof["flops"]
     wy = w.d == 64 and max(w.chunk or w.W, w.chunk or w.H) <= 16
     kname = ("chain_backward_wy_kernel" if wy else
@@ -255,7 +256,7 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "W": w.W, "D": w.D,
                    "n_heads": w.n_heads, "chunk": w.chunk or w.W, "dirs": 4, "x_dtype": w.dtype,
-                   "pass": "backward"},
+                   "pass": "backward", "readout": args.readout},
         "roofline": {"bound": "mfma" if wy else "alu", "achieved": flops / c_avg / 1e12,
                      "peak": PEAK_FP32 / 1e12,
                      "unit": "TFLOP/s", "frac": flops / c_avg / PEAK_FP32, "traffic": None,
@@ -266,7 +267,7 @@ def run_backward(args, w: wl.Workload, inp: dict, x_host, dev) -> int:
                      "calls_timed": len(call_ms)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline_backward(w, inp, g_np.astype(np.float64))
+        rec["cpu_baseline"] = cpu_baseline_backward(w, inp, g_np.astype(np.float64), readout=args.readout)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -250,7 +250,8 @@ size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t c
  *                  [B][4][n_heads][S(d)] with init_per_image), overwritten with
  *                  dL/dinit; rows of unselected routes are set to zero.
  *   opts           NULL = defaults.  Honoured: stream, workspace, eta_map, eta_scale,
- *                  alpha_bias, eps, init_per_image.  A workspace is always required
+ *                  alpha_bias, eps, init_per_image, and at d = 32 readout (boundary or
+ *                  running).  A workspace is always required
  *                  (hope_scan2d_backward_workspace_size).
  * Where the step of Eq. 20 is not differentiable: min(eta_bar, eta_spec) follows
  * eta_bar when eta_bar <= eta_spec; no derivative through the |k|^2 floor or the one-ulp
@@ -260,8 +261,8 @@ size_t hope_scan2d_workspace_size(const hope_fmap_t* x, uint32_t dirs, int32_t c
  * HOPE_ERR_UNSUPPORTED for d not in {16, 32, 64}, a chunk (after clipping to H*W)
  * longer than 128 tokens at d = 16 or 32 tokens at d = 64 (d = 32 takes any chunk
  * length), or any option outside the honoured set away
- * from its default (running readout, variants, two chunk sizes, final_memories, bf16
- * out); HOPE_ERR_WORKSPACE; HOPE_ERR_HIP.  Deterministic: per-route map gradients and
+ * from its default (the running readout at d = 16 or 64, variants, two chunk sizes,
+ * final_memories, bf16 out); HOPE_ERR_WORKSPACE; HOPE_ERR_HIP.  Deterministic: per-route map gradients and
  * per-image state gradients are summed in a fixed order.
  */
 hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memories,

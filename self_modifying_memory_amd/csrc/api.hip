@@ -145,7 +145,7 @@ size_t backward_workspace_bytes(const hope_fmap_t* x, const BackLayout& L) {
 
 // options the backward pass honours: everything else must be at its default
 bool backward_opts_supported(const hope_scan2d_opts_t& o) {
-  return o.readout == HOPE_READOUT_BOUNDARY && !o.route_scales && !o.skip && !o.counts &&
+  return (o.readout == HOPE_READOUT_BOUNDARY || o.readout == HOPE_READOUT_RUNNING) && !o.route_scales && !o.skip && !o.counts &&
          o.injection == HOPE_INJECTION_SOFT && o.spectral == HOPE_SPECTRAL_CLAMP && o.frozen == 0 &&
          o.no_dgd == 0 && o.shared_init == 0 && !o.queries && o.mem_chunk == 0 && !o.final_memories &&
          o.out_dtype == HOPE_F32;
@@ -497,6 +497,7 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
     return HOPE_ERR_INVALID_ARG;
   if (!backward_opts_supported(o)) return HOPE_ERR_UNSUPPORTED;
   if (d != 16 && d != 32 && d != 64) return HOPE_ERR_UNSUPPORTED;
+  if (o.readout == HOPE_READOUT_RUNNING && d != 32) return HOPE_ERR_UNSUPPORTED;
   const BackLayout L = backward_layout(x, dirs, chunk);
   if (d != 32 && L.cmax > hope::backward_max_chunk(d)) return HOPE_ERR_UNSUPPORTED;
   const size_t ws_need = backward_workspace_bytes(x, L);
@@ -531,6 +532,7 @@ hope_status_t hope_scan2d_backward(const hope_fmap_t* x, const float* init_memor
   p.eta_scale = o.eta_scale;
   p.alpha_bias = o.alpha_bias;
   p.eps = o.eps;
+  p.readout = o.readout == HOPE_READOUT_RUNNING ? 1 : 0;
 
   hipStream_t s = o.stream;
   st = hip_status(hope::launch_chain_backward(p, d, grad_init, s));

@@ -181,9 +181,11 @@ __device__ __forceinline__ void store_dd(float* M, int mi, int nj, f32x4 acc, co
 // Tile idx (0-3) of a d x d matrix in LDS: M <- gc M + sum over the 16 token slots of
 // (A1_t, scaled by sc_t if kScale) B1_t^T.  (Which operands are present is a template
 // argument: a test of a pointer into LDS against null is not folded by the compiler.)
-template <bool kScale>
+template <bool kScale, bool kTwo = false>
 __device__ __forceinline__ void dd_update(float* M, int idx, float gc, const float* A1,
-                                          const float* B1, const float* sc, const Lane& L) {
+                                          const float* B1, const float* sc, const Lane& L,
+                                          const float* A2 = nullptr, const float* B2 = nullptr,
+                                          const float* sc2 = nullptr) {
   const int mi = idx >> 1, nj = idx & 1;
   f32x4 acc;
 #pragma unroll
@@ -193,6 +195,7 @@ __device__ __forceinline__ void dd_update(float* M, int idx, float gc, const flo
     const int tk = 4 * s + L.q4;
     const float a = A1[tk * kLD + 16 * mi + L.r16];
     acc = mfma4(kScale ? a * sc[tk] : a, B1[tk * kLD + 16 * nj + L.r16], acc);
+    if constexpr (kTwo) acc = mfma4(A2[tk * kLD + 16 * mi + L.r16] * sc2[tk], B2[tk * kLD + 16 * nj + L.r16], acc);
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * L.q4 + v) * kLD + 16 * nj + L.r16] = acc[v];
@@ -204,8 +207,8 @@ __device__ __forceinline__ void dd_update(float* M, int idx, float gc, const flo
 // t < j backward) adds cols[j][t] v_j, so one FMA per step is on the critical path; the
 // coefficient columns are loaded two steps ahead.  kU: the u-recurrence (forward, with the
 // B1 term, v = -gscale * pre stored to Out and pre to Out2); else the a-recurrence
-// (backward, v = pre stored to Out).
-template <bool kU>
+// (backward, v = pre stored to Out; with kB1 its base has the B1 term too).
+template <bool kU, bool kB1 = kU>
 __device__ __forceinline__ void solve_cols(int lane, int bl, const float* cols, const float* g0,
                                            const float* B0, const float* B1, float* Out,
                                            float* Out2, const float* gscale) {
@@ -215,12 +218,8 @@ __device__ __forceinline__ void solve_cols(int lane, int bl, const float* cols, 
 #pragma unroll
   for (int t = 0; t < kTT; ++t) {
     const float b0 = B0[t * kLD + c];
-    if constexpr (kU) {
-      acc[t] = fmaf(g0[t], b0, B1[t * kLD + c]);
-      gs[t] = gscale[t];
-    } else {
-      acc[t] = g0[t] * b0;
-    }
+    acc[t] = kB1 ? fmaf(g0[t], b0, B1[t * kLD + c]) : g0[t] * b0;
+    if constexpr (kU) gs[t] = gscale[t];
   }
   f32x4 col[3][4];
   auto load_col = [&](int n) {
@@ -246,8 +245,16 @@ __device__ __forceinline__ void solve_cols(int lane, int bl, const float* cols, 
   }
 }
 
-template <bool XBF>  // the map is bf16 (else fp32)
-__global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams p) {
+// XBF: the map is bf16 (else fp32).  RUN: the running readout y_t = S_0[mem] P_c G_{t-1} q_t
+// (the memory after the chunk's earlier tokens): its adjoint r_t = P_c^T S_0[mem]^T dy_t
+// enters every earlier gain, dG_{t-1} += r_t q_t^T, which adds to the a-recurrence's base
+// sum_{m>t} beta_{t,m-1} (q_m . k_t) r_m, to dk_t the term sum_{m>t} beta_{t,m-1} (r_m . w_t) q_m
+// (times -step_t), to dalpha_t Gam_{t-1} sum_{m>t} beta_{t,m-1} r_m . (G_s q_m) +
+// sum_{j<t, m>t} beta_{j,t-1} beta_{t,m-1} (u_j . r_m)(k_j . q_m), to dG_s the sum
+// sum_t Gam_{t-1} r_t q_t^T, and makes dq_t = G_{t-1}^T r_t; the readout's reads of P_c and
+// S_0[mem] take G_{t-1} q_t in place of q_t.  Its extra arrays cost one chain per CU.
+template <bool XBF, bool RUN>
+__global__ __launch_bounds__(kNT, RUN ? 1 : 2) void chain_backward_wy32_kernel(BackParams p) {
   // One LDS block, small and uniformly read arrays first.
   constexpr int kTok = kTT * kLD;
   constexpr int kMat = kD * kLD;
@@ -258,7 +265,10 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   constexpr int oProj = oTok + 15 * kTok;     // projections [16][kPL], then their adjoints
   constexpr int oMat = oProj + kTT * kPL;     // P, P^T, two adjoints of P, G_s, dG
   constexpr int kSmem = oMat + 6 * kMat;
-  __shared__ __align__(16) float smem[kSmem];
+  // running readout only: K^T Q, U^T R, R^T W (16 x 16), r . (G_s q) per token, then the
+  // token vectors r, G_{t-1} q, G_s q and the a-recurrence's readout base
+  constexpr int kRunExtra = 3 * kTT * kCL + kTT + 4 * kTok;
+  __shared__ __align__(16) float smem[kSmem + (RUN ? kRunExtra : 0)];
   float* const tSt = smem + oSc;    // step_t
   float* const tAl = tSt + kTT;     // alpha_t
   float* const tNk = tAl + kTT;     // 1 / sqrt(|k_raw|^2 + eps)
@@ -307,6 +317,14 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
   float* sdPc = sdPn + kMat;       // adjoint of P_c (accumulating)
   float* const sGs = sdPc + kMat;  // G_s (block start gain)
   float* const sdG = sGs + kMat;   // adjoint of the block's end gain
+  float* const sKQ = smem + kSmem;     // [j][t]: k_j . q_t            (running readout only)
+  float* const sUR = sKQ + kTT * kCL;  // [j][t]: u_j . r_t
+  float* const sRW = sUR + kTT * kCL;  // [m][t]: r_m . w_t
+  float* const tRg = sRW + kTT * kCL;  // r_t . (G_s q_t)
+  float* const sR = tRg + kTT;         // r_t = P^T dq~_t
+  float* const sRQ = sR + kTok;        // G_{t-1} q_t
+  float* const sGQ = sRQ + kTok;       // G_s q_t
+  float* const sXB = sGQ + kTok;       // sum_{m>t} beta_{t,m-1} (q_m . k_t) r_m
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -736,13 +754,59 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
       } else if (w == 2) {
         dtok(sE, sdG, false, sK, 0);
         dtok(sE, sdG, false, sK, 1);
+      } else if constexpr (RUN) {
+        gram(sKQ, sK, sQ);
+        dtok(sGQ, sGs, false, sQ, 0);
+        dtok(sGQ, sGs, false, sQ, 1);
       } else {
         dtok(sQt, sP, false, sQ, 0);
         dtok(sQt, sP, false, sQ, 1);
       }
       lds_barrier();
+      if constexpr (RUN) {
+        // r = P^T dq~ and the a-recurrence's readout base (wave 0); G_{t-1} q_t (wave 1)
+        const Lane L = stage_lane_of(tid);
+        const int r16 = L.r16, q4 = L.q4;
+        if (w == 0) {
+          dtok(sR, sPT, false, sdQt, 0);
+          dtok(sR, sPT, false, sdQt, 1);
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int m = 4 * s4 + q4, t = r16;
+              const float cq = m > t ? sBt[t * kCL + m - 1] * sKQ[t * kCL + m] : 0.f;
+              acc = mfma4(cq, sR[m * kLD + 16 * n + r16], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sXB[(4 * q4 + v) * kLD + 16 * n + r16] = acc[v];
+          }
+        } else if (w == 1) {
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            f32x4 acc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int t = 4 * q4 + v;
+              acc[v] = tGam[t] * sGQ[t * kLD + 16 * n + r16];
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int j = 4 * s4 + q4, t = r16;
+              const float aq = j < t ? sBt[j * kCL + t - 1] * sKQ[j * kCL + t] : 0.f;
+              acc = mfma4(aq, sU[j * kLD + 16 * n + r16], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sRQ[(4 * q4 + v) * kLD + 16 * n + r16] = acc[v];
+          }
+        }
+        lds_barrier();
+      }
       // c, the a-solve columns and a (wave 0); F = dG_e^T W (wave 1); dq = P^T dq~ and
-      // diag(U^T E) (wave 2); dP_c += dq~ q^T and <G_s, dG_e> (wave 3)
+      // diag(U^T E) (wave 2); dP_c += dq~ q^T and <G_s, dG_e> (wave 3).  Running readout:
+      // the a-recurrence's base adds the readout term; dq = G_{t-1}^T r (wave 2); dP_c takes
+      // G_{t-1} q, and wave 3 also forms q~ = P G_{t-1} q, r . (G_s q) and R^T W
       if (w == 0) {
         const int lane = stage_lane(tid) & 63;
 #pragma unroll
@@ -752,17 +816,53 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           sCm[t * kCL + m] = cm;
           sColA[m * kTT + t] = -cm * sGm[m * kCL + t];
         }
-        solve_cols<false>(lane, bl, sColA, tGp, sE, nullptr, sA, nullptr, nullptr);
+        if constexpr (RUN) solve_cols<false, true>(lane, bl, sColA, tGp, sE, sXB, sA, nullptr, nullptr);
+        else solve_cols<false>(lane, bl, sColA, tGp, sE, nullptr, sA, nullptr, nullptr);
       } else if (w == 1) {
         dtok(sF, sdG, true, sW, 0);
         dtok(sF, sdG, true, sW, 1);
       } else if (w == 2) {
-        dtok(sdQ, sPT, false, sdQt, 0);
-        dtok(sdQ, sPT, false, sdQt, 1);
+        if constexpr (RUN) {
+          // dq_t = Gam_{t-1} G_s^T r_t + sum_{j<t} beta_{j,t-1} (u_j . r_t) k_j
+          gram(sUR, sU, sR);
+          dtok(sdQ, sGs, true, sR, 0);
+          dtok(sdQ, sGs, true, sR, 1);
+          const Lane L = stage_lane_of(tid);
+          const int r16 = L.r16, q4 = L.q4;
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            f32x4 acc;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int t = 4 * q4 + v;
+              acc[v] = tGam[t] * sdQ[t * kLD + 16 * n + r16];
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int j = 4 * s4 + q4, t = r16;
+              const float cu = j < t ? sBt[j * kCL + t - 1] * sUR[j * kCL + t] : 0.f;
+              acc = mfma4(cu, sK[j * kLD + 16 * n + r16], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sdQ[(4 * q4 + v) * kLD + 16 * n + r16] = acc[v];
+          }
+        } else {
+          dtok(sdQ, sPT, false, sdQt, 0);
+          dtok(sdQ, sPT, false, sdQt, 1);
+        }
         gram_diag(tUd, sU, sE);
       } else {
+        if constexpr (RUN) {
 #pragma unroll
-        for (int idx = 0; idx < 4; ++idx) ddu(sdPc, idx, 1.f, sdQt, sQ);
+          for (int idx = 0; idx < 4; ++idx) ddu(sdPc, idx, 1.f, sdQt, sRQ);
+          dtok(sQt, sP, false, sRQ, 0);
+          dtok(sQt, sP, false, sRQ, 1);
+          gram_diag(tRg, sR, sGQ);
+          gram(sRW, sR, sW);
+        } else {
+#pragma unroll
+          for (int idx = 0; idx < 4; ++idx) ddu(sdPc, idx, 1.f, sdQt, sQ);
+        }
         const int lane = stage_lane(tid) & 63;
         float tr = 0.f;
 #pragma unroll 4
@@ -785,8 +885,15 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         dtok(sGA, sGs, true, sA, 1);
       } else {
         if (w == 2) gram_diag(tL, sG, sA);
-        ddu_scaled(sdG, 2 * (w - 2), tMisc[0], sA, sK, tGS);
-        ddu_scaled(sdG, 2 * (w - 2) + 1, tMisc[0], sA, sK, tGS);
+        if constexpr (RUN) {
+          // dG_s also gains sum_t Gam_{t-1} r_t q_t^T
+          const Lane L = stage_lane_of(tid);
+          dd_update<true, true>(sdG, 2 * (w - 2), tMisc[0], sA, sK, tGS, L, sR, sQ, tGam);
+          dd_update<true, true>(sdG, 2 * (w - 2) + 1, tMisc[0], sA, sK, tGS, L, sR, sQ, tGam);
+        } else {
+          ddu_scaled(sdG, 2 * (w - 2), tMisc[0], sA, sK, tGS);
+          ddu_scaled(sdG, 2 * (w - 2) + 1, tMisc[0], sA, sK, tGS);
+        }
       }
       lds_barrier();
       // dalpha_t from the gain (wave 0, through the 16 x 16 product inner = (H o K^T K) c^T);
@@ -801,6 +908,11 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
         for (int s = 0; s < 4; ++s) {
           const int m = 4 * s + q4;
           inner = mfma4(sH[r16 * kCL + m] * sGm[r16 * kCL + m], sCm[r16 * kCL + m], inner);
+          if constexpr (RUN) {
+            // minus the readout's part: (U^T R o K^T Q) beta^T, beta[t][m] = beta_{t,m-1} (m > t)
+            const float bm = m > r16 ? sBt[r16 * kCL + m - 1] : 0.f;
+            inner = mfma4(-sUR[r16 * kCL + m] * sKQ[r16 * kCL + m], bm, inner);
+          }
         }
         // inner[j = 4 q4 + v][t = r16]
         const int t = r16;
@@ -817,6 +929,11 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           float lsum = 0.f;
 #pragma unroll
           for (int m = 0; m < kTT; ++m) lsum = fmaf(sCm[t * kCL + m], tL[m], lsum);
+          if constexpr (RUN) {
+#pragma unroll
+            for (int m = 0; m < kTT; ++m)
+              if (m > t) lsum = fmaf(-sBt[t * kCL + m - 1], tRg[m], lsum);
+          }
           tDal[t] = part + tGam[t] * (gp1 * tMisc[1] - lsum);
         }
       } else if (w <= 2) {
@@ -836,6 +953,11 @@ __global__ __launch_bounds__(kNT, 2) void chain_backward_wy32_kernel(BackParams 
           if (j < t) cf = sBt[j * kCL + t - 1] * sH[j * kCL + t];
           else if (j > t) cf = -sCm[t * kCL + j] * sJ[j * kCL + t];
           acc = mfma4(cf, sK[j * kLD + col], acc);
+          if constexpr (RUN) {
+            // + sum_{m>t} beta_{t,m-1} (r_m . w_t) q_m
+            const float cr = j > t ? sBt[t * kCL + j - 1] * sRW[j * kCL + t] : 0.f;
+            acc = mfma4(cr, sQ[j * kLD + col], acc);
+          }
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) sF[(4 * q4 + v) * kLD + col] = acc[v];
@@ -1024,8 +1146,14 @@ int64_t backward_wy32_chain_floats(int64_t nck, int64_t cmax) {
 
 hipError_t launch_chain_backward_wy32(const BackParams& p, hipStream_t stream) {
   const int64_t blocks = (int64_t)p.n_sel * p.B * p.nh;
-  if (p.x_bf16) chain_backward_wy32_kernel<true><<<dim3((unsigned)blocks), dim3(kNT), 0, stream>>>(p);
-  else chain_backward_wy32_kernel<false><<<dim3((unsigned)blocks), dim3(kNT), 0, stream>>>(p);
+  const dim3 grid((unsigned)blocks), block(kNT);
+  if (p.readout) {
+    if (p.x_bf16) chain_backward_wy32_kernel<true, true><<<grid, block, 0, stream>>>(p);
+    else chain_backward_wy32_kernel<false, true><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (p.x_bf16) chain_backward_wy32_kernel<true, false><<<grid, block, 0, stream>>>(p);
+    else chain_backward_wy32_kernel<false, false><<<grid, block, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -72,6 +72,7 @@ struct BackParams {
   int init_per_image;
   int eta_map;
   float eta_scale, alpha_bias, eps;
+  int readout;            // 0 boundary, 1 running (d = 32 only)
 };
 // longest chunk the token-serial backward kernel holds in LDS (d = 16 and 64)
 __host__ __device__ constexpr int backward_max_chunk(int d) { return d == 64 ? 32 : 128; }

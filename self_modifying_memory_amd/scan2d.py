@@ -291,10 +291,11 @@ def hope_scan2d_backward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: 
                          eta_map: str = "sigmoid", eta_scale: float = 1.0, alpha_bias: float = 4.0,
                          eps: float = 1e-6, init_per_image: bool = False,
                          grad_x: torch.Tensor | None = None, grad_init: torch.Tensor | None = None,
-                         workspace: torch.Tensor | None = None):
+                         workspace: torch.Tensor | None = None, readout: str = "boundary"):
     """Gradients of sum(grad_out * hope_scan2d_forward(x, init_memories, ...)) with respect
     to x and init_memories; returns (grad_x, grad_init), float32, shaped like x and
-    init_memories.  A workspace is allocated through torch when none is given."""
+    init_memories.  A workspace is allocated through torch when none is given.  readout
+    "running" (the memory after the chunk's earlier tokens) is supported at d = 32."""
     lib = N.load_library()
     _require_device(x, "x")
     _require_device(init_memories, "init_memories")
@@ -322,7 +323,8 @@ def hope_scan2d_backward(x: torch.Tensor, init_memories: torch.Tensor, n_heads: 
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
         _keep_for_stream(workspace, stream)
     fm = make_fmap(x, n_heads)
-    opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, None, workspace)
+    opts = make_opts(stream, eta_map, eta_scale, alpha_bias, eps, init_per_image, None, workspace,
+                     readout=readout)
     st = lib.hope_scan2d_backward(ctypes.byref(fm), init_memories.data_ptr(), dirs, chunk,
                                   grad_out.data_ptr(), grad_x.data_ptr(), grad_init.data_ptr(),
                                   ctypes.byref(opts))

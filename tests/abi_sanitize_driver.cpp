@@ -116,8 +116,10 @@ int main() {
   o = defaults(); o.workspace = fake(8); o.workspace_bytes = bws;
   EXPECT(hope_scan2d_backward(&x, init, 15, 0, nullptr, gx, gi, &o), HOPE_ERR_INVALID_ARG);
   EXPECT(hope_scan2d_backward(&x, init, 15, 0, go, static_cast<float*>(fake(0)), gi, &o), HOPE_ERR_INVALID_ARG);
+  hope_fmap_t x16 = fmap(2, 4, 5, 32, 2);  // d = 16: the running readout is honoured at d = 32 only
+  o = defaults(); o.workspace = fake(8); o.workspace_bytes = hope_scan2d_backward_workspace_size(&x16, 15, 0, nullptr);
   o.readout = HOPE_READOUT_RUNNING;
-  EXPECT(hope_scan2d_backward(&x, init, 15, 0, go, gx, gi, &o), HOPE_ERR_UNSUPPORTED);
+  EXPECT(hope_scan2d_backward(&x16, init, 15, 0, go, gx, gi, &o), HOPE_ERR_UNSUPPORTED);
   hope_fmap_t rows200 = fmap(1, 2, 200, 16, 1);  // d = 16: rows of 200 > 128
   o = defaults(); o.workspace = fake(8); o.workspace_bytes = hope_scan2d_backward_workspace_size(&rows200, 1, 0, nullptr);
   EXPECT(hope_scan2d_backward(&rows200, init, 1, 0, go, gx, gi, &o), HOPE_ERR_UNSUPPORTED);

@@ -252,10 +252,15 @@ def test_backward_argument_errors(lib):
     assert bcall(lib, x, o=opts(lib)) == N.HOPE_ERR_WORKSPACE
     assert bcall(lib, x, o=opts(lib, workspace=FAKE + (8 << 30), workspace_bytes=ws - 4)) == N.HOPE_ERR_WORKSPACE
     # options outside the honoured set
-    for kw in (dict(readout=N.HOPE_READOUT_RUNNING), dict(no_dgd=1), dict(mem_chunk=3),
+    for kw in (dict(no_dgd=1), dict(mem_chunk=3),
                dict(injection=1), dict(spectral=2), dict(frozen=1), dict(final_memories=FAKE + (6 << 30)),
                dict(out_dtype=N.HOPE_BF16)):
         assert bcall(lib, x, o=opts(lib, **kw, **base)) == N.HOPE_ERR_UNSUPPORTED, kw
+    # the running readout is honoured at d = 32 only
+    x16 = fmap(D=32, nh=2)
+    ws16 = lib.hope_scan2d_backward_workspace_size(ctypes.byref(x16), 15, 0, None)
+    assert bcall(lib, x16, o=opts(lib, readout=N.HOPE_READOUT_RUNNING, workspace=FAKE + (8 << 30),
+                                  workspace_bytes=ws16)) == N.HOPE_ERR_UNSUPPORTED
     # head dimension and chunk length limits
     assert bcall(lib, fmap(D=8, nh=1), o=o) == N.HOPE_ERR_UNSUPPORTED
     big = fmap(B=1, H=2, W=200, D=16, nh=1)

@@ -38,6 +38,9 @@ CASES = [
     (2, 3, 4, 128, 2, "f32", 5, 0, dict(init_per_image=True)),            # two heads, per image
     (1, 5, 7, 128, 2, "bf16", 10, 0, {}),                                 # routes 1 and 3, bf16
     (1, 3, 20, 64, 1, "f32", 15, 0, {}),                                  # d = 64, 20-token rows
+    # the running readout (d = 32: the blocked kernel)
+    (1, 5, 6, 32, 1, "f32", 15, 4, dict(eta_scale=2.0, readout="running")),   # ragged chunks
+    (2, 3, 4, 64, 2, "bf16", 15, 0, dict(readout="running")),                  # bf16 map, two heads
 ]
 
 
@@ -154,11 +157,22 @@ LONG_CASES = [
     (2, 5, 12, 64, 2, 15, dict(chunk=20, init_per_image=True)),  # chunks of 20 (16 + 4) across rows
     (1, 6, 7, 32, 1, 15, dict(chunk=42, eta_map="softplus", eta_scale=0.5, alpha_bias=1.0)),  # one 42-token chunk
     (1, 4, 10, 32, 1, 15, dict(chunk=17, eta_scale=40.0, alpha_bias=-1.0)),  # 16 + 1 blocks, clamps bind
+    # the running readout: the readout adjoint enters every earlier gain of the chunk
+    (1, 28, 28, 32, 1, 15, dict(readout="running")),                        # stage-2 chunks
+    (1, 4, 128, 32, 1, 3, dict(eta_scale=2.0, readout="running")),          # 128-token rows
+    (2, 5, 12, 64, 2, 15, dict(chunk=20, init_per_image=True, readout="running")),
+    (1, 6, 7, 32, 1, 15, dict(chunk=42, eta_map="softplus", eta_scale=0.5, alpha_bias=1.0,
+                              readout="running")),
+    (1, 4, 10, 32, 1, 15, dict(chunk=17, eta_scale=40.0, alpha_bias=-1.0, readout="running")),
 ]
 
 
-@pytest.mark.parametrize("case", LONG_CASES,
-                         ids=[f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}_dirs{c[5]}" for c in LONG_CASES])
+def _long_id(c):
+    tag = "_".join(f"{k}{v}" for k, v in c[6].items())
+    return f"B{c[0]}_{c[1]}x{c[2]}_D{c[3]}_dirs{c[5]}" + (f"_{tag}" if tag else "")
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=[_long_id(c) for c in LONG_CASES])
 def test_backward_long_chunks_match_gradient_oracle(case):
     # The chunk lengths of the stage-1, stage-2 and high-resolution workloads at d = 32:
     # several 16-token gate blocks and up to 128 gain rows per chunk, through the gain
