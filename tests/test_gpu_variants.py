@@ -3,9 +3,12 @@ App. B.5 skip) through the C ABI against the fp64 oracle, on the three scan kern
 
 Counters of the step controls are integers decided by floating point: the GPU decides in
 fp32, the oracle in fp64, and the quantities compared (eta and the two limits) come from
-a state that is itself only held to the parity tolerance of the input dtype.  The counts
-must therefore agree exactly except on tokens whose margin to the limit is within that
-tolerance (counted by the oracle as *_near).
+the projections of the fp32 state.  The counts must therefore agree exactly except on
+tokens whose relative margin to the limit is within a band (counted by the oracle as
+*_near).  The band is not the output tolerance: the state's products are split bf16
+products (about 2^-16 relative), so the decision inputs are held far closer than a bf16
+output is; COUNT_BAND is 2e-3 for a bf16 map (about a hundred times the split products'
+error), the fp32 output tolerance for an fp32 map.
 """
 import numpy as np
 import pytest
@@ -26,6 +29,7 @@ SHAPES = {
     "bf16_d64_seg": (1, 3, 40, 64, 1, "bf16", 0),   # d = 64, row chunks of 40: two segments
 }
 FROZEN = {"kv": ("k", "v"), "dynamics": ("eta", "alpha"), "q": ("q",)}
+COUNT_BAND = {"f32": TOL["f32"], "bf16": 2e-3}
 
 VARIANTS = {
     "scales_skip": dict(route_scales=True, skip=True),
@@ -92,7 +96,7 @@ def _run(shape, var, readout="boundary"):
     if var.get("counts"):
         counts = torch.zeros(3, dtype=torch.int64, device="cuda")
         gk["counts"] = counts
-        ok["counts"] = {"near_rel": TOL[dt]}
+        ok["counts"] = {"near_rel": COUNT_BAND[dt]}
     fin = torch.full((B, 4, nh, 4 * d * d + 2 * d), float("nan"), dtype=torch.float32, device="cuda")
     out = hope_scan2d_forward(x, init, nh, 15, chunk, final_memories=fin, **gk)
     torch.cuda.synchronize()
@@ -119,7 +123,8 @@ def test_variant_matches_oracle(shape, var):
             assert 0 < got[1] < got[0]
         else:                          # the spectral limit binds on some tokens
             assert got[2] > 0
-        print(f"  counts {got.tolist()} oracle {ref_cnt}", flush=True)
+        print(f"  counts {got.tolist()} oracle {ref_cnt} (differences "
+              f"{int(got[1]) - ref_cnt['inj']}, {int(got[2]) - ref_cnt['spec']})", flush=True)
 
 
 @pytest.mark.parametrize("shape", ["f32_d16", "bf16_d32", "bf16_d64"])
