@@ -36,6 +36,8 @@
 // their projection row tiles (for S_0 products); the state adjoint dS_0 is accumulated in
 // registers as 68 16 x 16 tiles spread over the 8 waves.  P_c, dP and the chunk's per-token
 // vectors (token-major, 16 token slots, padding slots zero) live in LDS.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   constexpr int kTok = kTT * kLD;
   constexpr int oSc = 0;                      // per-token scalars, 16 x 16
   constexpr int oCC = oSc + 16 * kTT;         // C x C matrices, 6 x 16 x 17
-  constexpr int oRow = oCC + 6 * kTT * kCL;   // solve coefficient rows, 16 x 16
+  constexpr int oRow = oCC + 6 * kTT * kCL;   // solve coefficient columns, 16 x 16
   constexpr int oTok = oRow + kTT * kTT;      // token-major d-vectors, 18 of them
   constexpr int oProj = oTok + 18 * kTok;     // projections [16][kPL], then their adjoints
   constexpr int oP = oProj + kTT * kPL;       // P_c, dP, P_c^T
@@ -190,8 +192,8 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
   float* const sJ = sH + kTT * kCL;    // A^T W
   float* const sCm = sJ + kTT * kCL;   // c[t][m] = beta_{t,m-1} step_m for m > t
   float* const sCf = sCm + kTT * kCL;  // coefficient of k_j in dk_t
-  // row t of a solve's coefficients: beta_{j,t-1} (k_j . k_t) for j < t (u), or
-  // c[t][m] (k_m . k_t) for m > t (a)
+  // a solve's coefficient columns: [j][t] = beta_{j,t-1} (k_j . k_t) for t > j (u), or
+  // [m][t] = -c[t][m] (k_m . k_t) for t < m (a)
   float* const sRow = smem + oRow;
   // token-major arrays; the first six in record order
   float* const sXt = smem + oTok;
@@ -434,50 +436,56 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     else if (j == 1) tGp[t] = gq;
     else if (j == 2 && t == 0) tMisc[0] = gc;
   };
-  // A one-wave triangular recurrence over the 16 token slots, lane = component:
-  // v_t = base_t + sum_j sRow[t][j] v_j over the already computed j (j < t forward,
-  // j > t backward); the coefficient row of the next step is loaded during this one.
-  auto solve_rows = [&](bool backward, int cl, const float* g0, const float* B0, const float* B1,
+  // A one-wave triangular recurrence over the 16 token slots, lane = component,
+  // right-looking: slot t starts from base_t = g0_t B0_t (+ B1_t), and once v_j is final
+  // every later slot t (t > j forward, t < j backward) adds sCol[j][t] v_j, so one FMA per
+  // step is on the critical path; the coefficient columns are loaded two steps ahead.
+  // kU: the u-recurrence (forward, with the B1 term, v = -gscale * pre to Out and pre to
+  // Out2); else the a-recurrence (backward, v = pre to Out).  (Which operands are present is
+  // a template argument: a test of a pointer into LDS against null is not folded by the
+  // compiler, and the branches it leaves serialise the steps' LDS reads.)
+  auto solve_cols = [&](auto kU_tag, int cl, const float* g0, const float* B0, const float* B1,
                         float* Out, float* Out2, const float* gscale) {
+    constexpr bool kU = decltype(kU_tag)::value;
+    constexpr bool kBack = !kU;
     const int lane = stage_lane(tid) & 63;
-    float v[kTT];
+    float acc[kTT], gs[kTT];
 #pragma unroll
-    for (int t = 0; t < kTT; ++t) v[t] = 0.f;
-    f32x4 row[4], nxt[4];
-    float ng, nb0, nb1 = 0.f, ngs = 0.f;
-    auto load_step = [&](int t) {
+    for (int t = 0; t < kTT; ++t) {
+      const float b0 = B0[t * kLD + lane];
+      if constexpr (kU) {
+        acc[t] = fmaf(g0[t], b0, B1[t * kLD + lane]);
+        gs[t] = gscale[t];
+      } else {
+        acc[t] = g0[t] * b0;
+      }
+    }
+    f32x4 col[3][4];
+    auto load_col = [&](int n) {
+      const int j = kBack ? kTT - 1 - n : n;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) nxt[q] = *reinterpret_cast<const f32x4*>(&sRow[t * kTT + 4 * q]);
-      ng = g0[t];
-      nb0 = B0[t * kLD + lane];
-      if (B1) nb1 = B1[t * kLD + lane];
-      if (gscale) ngs = gscale[t];
+      for (int q = 0; q < 4; ++q) col[n % 3][q] = *reinterpret_cast<const f32x4*>(&sRow[j * kTT + 4 * q]);
     };
-    load_step(backward ? kTT - 1 : 0);
+    load_col(0);
+    load_col(1);
 #pragma unroll
     for (int n = 0; n < kTT; ++n) {
-      const int t = backward ? kTT - 1 - n : n;
+      const int j = kBack ? kTT - 1 - n : n;
+      if (n + 2 < kTT) load_col(n + 2);
+      const float pre = j < cl ? acc[j] : 0.f;
+      const float val = kU ? -gs[j] * pre : pre;
+      Out[j * kLD + lane] = val;
+      if constexpr (kU) Out2[j * kLD + lane] = pre;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) row[q] = nxt[q];
-      const float g = ng, b0 = nb0, b1 = nb1, gs = ngs;
-      if (n + 1 < kTT) load_step(backward ? t - 1 : t + 1);
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < kTT; ++j)
-        if (backward ? j > t : j < t) acc[j & 3] = fmaf(row[j >> 2][j & 3], v[j], acc[j & 3]);
-      const float base = B1 ? fmaf(g, b0, b1) : g * b0;
-      const float pre = t < cl ? base + ((acc[0] + acc[1]) + (acc[2] + acc[3])) : 0.f;
-      const float val = gscale ? -gs * pre : pre;
-      v[t] = val;
-      Out[t * kLD + lane] = val;
-      if (Out2) Out2[t * kLD + lane] = pre;
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < kTT; ++t)
+        if (kBack ? t < j : t > j) acc[t] = fmaf(col[n % 3][t >> 2][t & 3], val, acc[t]);
     }
   };
   // tile idx (0-15) of a d x d matrix in LDS: M <- gc M + sum over the 16 token slots of
-  // (A1_t scaled by sc_t) B1_t^T [+ A2_t B2_t^T]
-  auto dd_update = [&](float* M, int idx, float gc, const float* A1, const float* B1, bool scale,
-                       int cl, const float* A2, const float* B2) {
+  // (A1_t, scaled by beta_{t,cl-1} if kScale) B1_t^T [+ A2_t B2_t^T if kTwo]
+  auto dd_update = [&](auto kScale_tag, auto kTwo_tag, float* M, int idx, float gc, const float* A1,
+                       const float* B1, int cl, const float* A2, const float* B2) {
+    constexpr bool kScale = decltype(kScale_tag)::value, kTwo = decltype(kTwo_tag)::value;
     const Lane L = stage_lane_of(tid);
     const int r16 = L.r16, q4 = L.q4, mi = idx >> 2, nj = idx & 3;
     f32x4 acc;
@@ -486,9 +494,9 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int tk = 4 * s + q4;
-      const float sc = scale ? sBt[tk * kCL + cl - 1] : 1.f;
-      acc = mfma4(A1[tk * kLD + 16 * mi + r16] * sc, B1[tk * kLD + 16 * nj + r16], acc);
-      if (A2) acc = mfma4(A2[tk * kLD + 16 * mi + r16], B2[tk * kLD + 16 * nj + r16], acc);
+      const float a = A1[tk * kLD + 16 * mi + r16];
+      acc = mfma4(kScale ? a * sBt[tk * kCL + cl - 1] : a, B1[tk * kLD + 16 * nj + r16], acc);
+      if constexpr (kTwo) acc = mfma4(A2[tk * kLD + 16 * mi + r16], B2[tk * kLD + 16 * nj + r16], acc);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) M[(16 * mi + 4 * q4 + v) * kLD + 16 * nj + r16] = acc[v];
@@ -543,14 +551,14 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     if (w >= 4) alpha_products();
     lds_barrier();
     if (w == 0) {
-      // coefficient rows beta_{j,t-1} (k_j . k_t), j < t, then the recurrence for w and u
+      // coefficient columns beta_{j,t-1} (k_j . k_t), t > j, then the recurrence for w and u
       const int lane = stage_lane(tid) & 63;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = lane + 64 * k, t = e >> 4, j = e & 15;
-        sRow[e] = j < t ? sBt[j * kCL + t - 1] * sGm[j * kCL + t] : 0.f;
+        sRow[j * kTT + t] = j < t ? sBt[j * kCL + t - 1] * sGm[j * kCL + t] : 0.f;
       }
-      solve_rows(false, cl, tGam, sK, sDl, sU, sW, tSt);
+      solve_cols(std::true_type{}, cl, tGam, sK, sDl, sU, sW, tSt);
     }
     lds_barrier();
     if (c == nck - 1) break;
@@ -559,8 +567,8 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
     // P <- Gam_C P + (P U) diag(beta_{., cl-1}) K^T
     {
       const float gc = tMisc[0];
-      dd_update(sP, w, gc, sPU, sK, true, cl, nullptr, nullptr);
-      dd_update(sP, w + 8, gc, sPU, sK, true, cl, nullptr, nullptr);
+      dd_update(std::true_type{}, std::false_type{}, sP, w, gc, sPU, sK, cl, nullptr, nullptr);
+      dd_update(std::true_type{}, std::false_type{}, sP, w + 8, gc, sPU, sK, cl, nullptr, nullptr);
       (void)s0;
     }
     lds_barrier();
@@ -621,16 +629,17 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       const int e = stage_lane(tid) - 256, t = e >> 4, m = e & 15;
       const float cm = m > t ? sBt[t * kCL + m - 1] * tSt[m] : 0.f;
       sCm[t * kCL + m] = cm;
-      sRow[t * kTT + m] = -cm * sGm[m * kCL + t];
+      sRow[m * kTT + t] = -cm * sGm[m * kCL + t];
     }
     lds_barrier();
     // a (wave 0); the adjoint carry's first part on waves 1-7:
     // dP <- Gam_C dP + (dP K) diag(beta_{., cl-1}) U^T + dq~ q^T
     if (w == 0) {
-      solve_rows(true, cl, tGp, sE, nullptr, sA, nullptr, nullptr);
+      solve_cols(std::false_type{}, cl, tGp, sE, nullptr, sA, nullptr, nullptr);
     } else {
       const float gc = tMisc[0];
-      for (int idx = w - 1; idx < 16; idx += 7) dd_update(sdP, idx, gc, sZ, sU, true, cl, sdQt, sQ);
+      for (int idx = w - 1; idx < 16; idx += 7)
+        dd_update(std::true_type{}, std::true_type{}, sdP, idx, gc, sZ, sU, cl, sdQt, sQ);
       mem_rows_dS0();
     }
     lds_barrier();
@@ -815,8 +824,8 @@ __global__ __launch_bounds__(512) void chain_backward_wy_kernel(BackParams p) {
       dxok = L.r16 < cl;
       dxdst = gdst + ((int64_t)b * N + pixb[L.r16]) * Dt + (int64_t)h * kD + 16 * w + 4 * L.q4;
     }
-    dd_update(sdP, w, 1.f, sdXt, sX, false, cl, nullptr, nullptr);
-    dd_update(sdP, w + 8, 1.f, sdXt, sX, false, cl, nullptr, nullptr);
+    dd_update(std::false_type{}, std::false_type{}, sdP, w, 1.f, sdXt, sX, cl, nullptr, nullptr);
+    dd_update(std::false_type{}, std::false_type{}, sdP, w + 8, 1.f, sdXt, sX, cl, nullptr, nullptr);
   }
   if (dxok) *reinterpret_cast<f32x4*>(dxdst) = dxv;
 
