@@ -215,3 +215,22 @@ def test_backward_full_size_stage2_image0_head0():
     e = _rel(got, ref[0])
     print(f"  rel grad_x[0, head 0] {e:.2e}", flush=True)
     assert e <= TOL["f32"]
+
+
+@pytest.mark.parametrize("D,nh,chunk", [(64, 2, 0), (64, 1, 0), (96, 3, 20)],
+                         ids=["d32_aligned", "d64_aligned", "d32_chunk20"])
+def test_backward_map_gradient_does_not_depend_on_batch(D, nh, chunk):
+    # Every chain is one (image, head, route) and the route planes are summed per pixel in
+    # a fixed order, so an image's map gradient is the same bit for bit whatever else is in
+    # the batch (the initial-state gradient is a sum over the batch and is not compared).
+    import torch
+    from self_modifying_memory_amd.scan2d import hope_scan2d_backward
+    B, H, W = 6, 5, 7
+    inp = wl.draw(B, H, W, D, nh, seed=9400 + D + chunk, dtype="bf16", live=True)
+    x, init = to_device(inp, "bf16")
+    g = torch.from_numpy(np.random.Generator(np.random.PCG64(98)).standard_normal((B, H, W, D))
+                         .astype(np.float32)).cuda()
+    gx_all, _ = hope_scan2d_backward(x, init, nh, g, 15, chunk)
+    gx_one, _ = hope_scan2d_backward(x[:1].contiguous(), init, nh, g[:1].contiguous(), 15, chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(gx_all[:1].cpu().numpy(), gx_one.cpu().numpy())
