@@ -964,7 +964,8 @@ __global__ __launch_bounds__(kNT, RUN ? 1 : 2) void chain_backward_wy32_kernel(B
       }
       lds_barrier();
       // token by token: the gain adjoints, then the readout, the step, the gates, the
-      // normalisation and the projections; dProj replaces Proj (zero rows in padding slots)
+      // normalisation and the projections; dProj goes to the projections' area (zero rows in
+      // padding slots)
       {
         const int lane = stage_lane(tid) & 63, c = lane & 31, hh = lane >> 5;
         float dk[2], ddl[2], dstep[2], dalpha[2], dq[2], k[2], q[2], dl[2];
