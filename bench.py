@@ -354,7 +354,8 @@ def run_block(args, w: wl.Workload, dev) -> int:
                      "kernel_ms": c_avg * 1e3, "kernel_ms_median": float(np.median(call_ms)),
                      "t_roof_ms": t_roof * 1e3,
                      "kernel_ms_p10_p90": [float(np.percentile(call_ms, 10)),
-                                           float(np.percentile(call_ms, 90))]},
+                                           float(np.percentile(call_ms, 90))],
+                     "calls_timed": len(call_ms)},
     }
     if not args.no_cpu_baseline:
         from oracle import hope_block as hbk

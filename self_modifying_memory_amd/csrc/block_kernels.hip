@@ -13,6 +13,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -48,13 +49,15 @@ __device__ __forceinline__ int xcd_tile(int bid, int G) {
 }
 
 // ---- GEMM: out[m][n] = epilogue(sum_k A[m][k] Wt[n][k]) -----------------------------------
-// Block tile 128 x 128, 4 waves as 2 x 2, each 64 x 64 = 4 x 4 tiles of v_mfma_f32_16x16x32_bf16;
-// K in steps of 32 (one MFMA k-step) through double-buffered LDS, one barrier a step (32 KB a
-// workgroup, so that four share a CU and hide each other's barriers).  The MFMA computes the
-// transposed tile (weights as its A operand), so that a lane's four results are four
-// consecutive output columns of one row: lane (r16, q4) feeds row r16 of the weight tile and
-// row r16 of the activation tile with the 8 consecutive k values 8 q4 .. 8 q4 + 7 (the same k
-// order on both sides), and holds C[m = 16 i + r16][n = 16 j + 4 q4 + v].
+// Block tile 128 x BN (BN = 128, or 64 when N is not a multiple of 128, so that N = 192 is not
+// covered by a three-quarters-empty tile), 4 waves as 2 x 2, each 64 x (BN / 2) = 4 x NJ tiles
+// of v_mfma_f32_16x16x32_bf16; K in steps of 32 (one MFMA k-step) through double-buffered LDS,
+// one barrier a step (32 KB a workgroup at BN = 128, so that four share a CU and hide each
+// other's barriers).  The MFMA computes the transposed tile (weights as its A operand), so
+// that a lane's four results are four consecutive output columns of one row: lane (r16, q4)
+// feeds row r16 of the weight tile and row r16 of the activation tile with the 8 consecutive
+// k values 8 q4 .. 8 q4 + 7 (the same k order on both sides), and holds
+// C[m = 16 i + r16][n = 16 j + 4 q4 + v].
 //
 // LDS rows are the 64 bytes of one row's 32-deep k-slice, unpadded, as four 16-byte chunks;
 // chunk c of row r sits at chunk c ^ swz(r), swz(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1).  A
@@ -64,96 +67,112 @@ __device__ __forceinline__ int xcd_tile(int bid, int G) {
 //
 // Ragged edges: rows past M and weight rows past N are read clamped (in bounds) and not
 // written; k chunks past K are zero on both operands.  Requires K % 8 == 0 and N % 4 == 0.
-constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kBK = 32;
 
 __device__ __forceinline__ int lds_chunk(int row, int c) {
   return row * 4 + (c ^ (((row >> 1) & 3) ^ ((row >> 3) & 1)));
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 4) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
-                                                            const uint16_t* __restrict__ Wt, int M,
-                                                            int N, int K, const float* bias,
-                                                            const float* res, void* out) {
-  __shared__ __align__(16) uint4 sA[2][kBM * 4];
-  __shared__ __align__(16) uint4 sB[2][kBN * 4];
+template <int EPI, int BN>
+__global__ __launch_bounds__(256, BN == 128 ? 4 : 5) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wt, int M, int N, int K,
+    const float* bias, const float* res, void* out) {
+  constexpr int BM = 128, NI = BM / 32, NJ = BN / 32;  // MFMA tiles of a wave: rows, columns
+  constexpr int RB = BN / 64;  // 16-byte weight staging loads per thread
+  static_assert(BN == 64 || BN == 128, "tile");
+  __shared__ __align__(16) u32x4 sA[2][BM * 4];
+  __shared__ __align__(16) u32x4 sB[2][BN * 4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4, wm = w >> 1, wn = w & 1;
-  const int tiles_n = (N + kBN - 1) / kBN;
+  const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * kBM, n0 = (tile % tiles_n) * kBN;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
 
-  // global -> registers -> LDS: for each operand, rows tid / 4 and tid / 4 + 64 of the tile,
-  // 16-byte chunk tid % 4 of the step's 32-deep k-slice
+  // global -> registers -> LDS: for each operand, rows tid / 4 (and tid / 4 + 64 when the tile
+  // has 128 of them) of the tile, 16-byte chunk tid % 4 of the step's 32-deep k-slice (named
+  // registers and native vector types: arrays, or selects between 16-byte structs, are placed
+  // in scratch memory)
   const int row = tid >> 2, ch = tid & 3;
-  const uint16_t* pa0 = A + (int64_t)min(m0 + row, M - 1) * K + 8 * ch;
-  const uint16_t* pa1 = A + (int64_t)min(m0 + row + 64, M - 1) * K + 8 * ch;
-  const uint16_t* pb0 = Wt + (int64_t)min(n0 + row, N - 1) * K + 8 * ch;
-  const uint16_t* pb1 = Wt + (int64_t)min(n0 + row + 64, N - 1) * K + 8 * ch;
+  const uint16_t* const pa0 = A + (int64_t)min(m0 + row, M - 1) * K + 8 * ch;
+  const uint16_t* const pa1 = A + (int64_t)min(m0 + row + 64, M - 1) * K + 8 * ch;
+  const uint16_t* const pb0 = Wt + (int64_t)min(n0 + row, N - 1) * K + 8 * ch;
+  const uint16_t* const pb1 = Wt + (int64_t)min(n0 + row + 64, N - 1) * K + 8 * ch;
   const int st0 = lds_chunk(row, ch), st1 = lds_chunk(row + 64, ch);
-  uint4 ga0, ga1, gb0, gb1;
-  auto fetch = [&](int k0) {
-    const bool in = k0 + 8 * ch < K;
-    const uint4 z = {0u, 0u, 0u, 0u};
-    ga0 = in ? *reinterpret_cast<const uint4*>(pa0 + k0) : z;
-    ga1 = in ? *reinterpret_cast<const uint4*>(pa1 + k0) : z;
-    gb0 = in ? *reinterpret_cast<const uint4*>(pb0 + k0) : z;
-    gb1 = in ? *reinterpret_cast<const uint4*>(pb1 + k0) : z;
+  struct Slice {
+    u32x4 a0, a1, b0, b1;
+    bool in;  // the chunk lies below K (else it is stored as zeros)
   };
-  auto store = [&](int buf) {
-    sA[buf][st0] = ga0;
-    sA[buf][st1] = ga1;
-    sB[buf][st0] = gb0;
-    sB[buf][st1] = gb1;
+  // A chunk past K loads chunk 0 of its row (in bounds) and is replaced by zeros when it is
+  // stored, not when it arrives: a select right after the load would wait for it there.  The
+  // loads are unconditional, so no branch or select of addresses enters the step loop; the
+  // helpers are forced inline, as a call would keep the captured registers in scratch memory.
+  auto fetch = [&](Slice& r, int k0) __attribute__((always_inline)) {
+    r.in = k0 + 8 * ch < K;
+    const int kk = r.in ? k0 : 0;
+    r.a0 = *reinterpret_cast<const u32x4*>(pa0 + kk);
+    r.b0 = *reinterpret_cast<const u32x4*>(pb0 + kk);
+    r.a1 = *reinterpret_cast<const u32x4*>(pa1 + kk);
+    if constexpr (RB > 1) r.b1 = *reinterpret_cast<const u32x4*>(pb1 + kk);
+  };
+  auto store = [&](const Slice& r, int buf) __attribute__((always_inline)) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    sA[buf][st0] = r.in ? r.a0 : z;
+    sB[buf][st0] = r.in ? r.b0 : z;
+    sA[buf][st1] = r.in ? r.a1 : z;
+    if constexpr (RB > 1) sB[buf][st1] = r.in ? r.b1 : z;
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int rd_a[4], rd_b[4];
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int rd_a[NI], rd_b[NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    rd_a[i] = lds_chunk(wm * 64 + 16 * i + r16, q4);
-    rd_b[i] = lds_chunk(wn * 64 + 16 * i + r16, q4);
-  }
+  for (int i = 0; i < NI; ++i) rd_a[i] = lds_chunk(wm * (BM / 2) + 16 * i + r16, q4);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rd_b[j] = lds_chunk(wn * (BN / 2) + 16 * j + r16, q4);
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    bf16x8 a[NI], bv[NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[i] = __builtin_bit_cast(bf16x8, sA[buf][rd_a[i]]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bv[j] = __builtin_bit_cast(bf16x8, sB[buf][rd_b[j]]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);
+  };
 
-  // step s multiplies k-slice s from buffer s % 2; slice s + 1 (fetched during step s - 1)
-  // is stored into the other buffer at the start of step s, and slice s + 2 fetched.  The
-  // barrier closing step s - 1 retires every read of the buffer that step s stores to.
+  // Step s multiplies k-slice s from LDS buffer s % 2: slice s + 1 (fetched during step s - 1)
+  // is stored into the other buffer at the start of step s, and slice s + 2 fetched into the
+  // same registers.  The barrier closing step s - 1 retires every read of the buffer that step
+  // s stores to.  (A second register set, fetching two slices ahead, was measured slower: the
+  // registers it takes cost more occupancy than the latency it hides.)
   const int steps = (K + kBK - 1) / kBK;
-  fetch(0);
-  store(0);
-  if (steps > 1) fetch(kBK);
+  Slice X;
+  fetch(X, 0);
+  store(X, 0);
+  if (steps > 1) fetch(X, kBK);
   __syncthreads();
   for (int s = 0; s < steps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < steps) store(buf ^ 1);
-    if (s + 2 < steps) fetch((s + 2) * kBK);
-    bf16x8 a[4], bv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = __builtin_bit_cast(bf16x8, sA[buf][rd_a[i]]);
-      bv[i] = __builtin_bit_cast(bf16x8, sB[buf][rd_b[i]]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], a[i], acc[i][j], 0, 0, 0);
+    if (s + 1 < steps) store(X, buf ^ 1);
+    if (s + 2 < steps) fetch(X, (s + 2) * kBK);
+    compute(buf);
     __syncthreads();
   }
 
-  // epilogue: acc[i][j][v] = C[m0 + 64 wm + 16 i + r16][n0 + 64 wn + 16 j + 4 q4 + v]
+  // epilogue: acc[i][j][v] = C[m0 + (BM / 2) wm + 16 i + r16][n0 + (BN / 2) wn + 16 j + 4 q4 + v]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 64 + 16 * j + 4 * q4;
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn * (BN / 2) + 16 * j + 4 * q4;
     if (n >= N) continue;  // N % 4 == 0: the lane's four columns are all in or all out
     const f32x4 bn = bias ? *reinterpret_cast<const f32x4*>(&bias[n]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + 16 * i + r16;
+    for (int i = 0; i < NI; ++i) {
+      const int m = m0 + wm * (BM / 2) + 16 * i + r16;
       if (m >= M) continue;
       const int64_t o = (int64_t)m * N + n;
       const f32x4 t = acc[i][j] + bn;
@@ -425,21 +444,28 @@ unsigned grid_for(int64_t work, int per_block) {
   return (unsigned)(g < 65535 * 16 ? (g < 1 ? 1 : g) : 65535 * 16);
 }
 
+template <int BN>
+hipError_t launch_gemm_tile(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
+                            const float* bias, const float* res, void* out, hipStream_t s) {
+  const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + BN - 1) / BN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles), block(256);
+  switch (epi) {
+    case kEpiF32: gemm_bf16_kernel<kEpiF32, BN><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    case kEpiGeluBf16: gemm_bf16_kernel<kEpiGeluBf16, BN><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    case kEpiResidualF32: gemm_bf16_kernel<kEpiResidualF32, BN><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(int epi, const uint16_t* A, const uint16_t* Wt, int M, int N, int K,
                             const float* bias, const float* res, void* out, hipStream_t s) {
   if (N % 4 || K % 8 || M <= 0 || N <= 0 || K <= 0) return hipErrorInvalidValue;
-  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), block(256);
-  switch (epi) {
-    case kEpiF32: gemm_bf16_kernel<kEpiF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
-    case kEpiGeluBf16: gemm_bf16_kernel<kEpiGeluBf16><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
-    case kEpiResidualF32: gemm_bf16_kernel<kEpiResidualF32><<<grid, block, 0, s>>>(A, Wt, M, N, K, bias, res, out); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (N % 128) return launch_gemm_tile<64>(epi, A, Wt, M, N, K, bias, res, out, s);
+  return launch_gemm_tile<128>(epi, A, Wt, M, N, K, bias, res, out, s);
 }
 
 hipError_t launch_cpe_layernorm(const float* x, const float* w, const float* b, const float* g,
