@@ -148,6 +148,11 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
   constexpr int LTLD = kSB + 4;                    // fp32 stride of L^T
   constexpr bool kDeferMemSplit = D == 64;
+  // d = 64, boundary readout, no variant options: the solve waves, idle while waves 0-3
+  // form the gates, use that phase for the block's retention products, the Gram matrix of
+  // the raw keys and the staging of the next block's tokens, all of which need only the
+  // projections
+  constexpr bool kEarly = D == 64 && !RUN && VAR == 0;
 
   __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
@@ -166,7 +171,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   __shared__ __attribute__((aligned(16))) unsigned short KL[kSB * XLD];
   __shared__ __attribute__((aligned(16))) unsigned short QH[kSB * XLD];
   __shared__ __attribute__((aligned(16))) unsigned short QL[kSB * XLD];
-  __shared__ int pixs[kSB];
+  __shared__ int pixs[2][kSB];  // token pixels; two buffers when the next block is staged early
+  __shared__ float kinvs[kEarly ? kSB : 1];  // 1 / |k_raw| of each token (early Gram)
   __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     const int ld_i = lid - kLoad0;
     const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
     if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = v;
-    if (lid < kSB) pixs[lid] = lid < nt ? block_pixel(tb, lid) : 0;
+    if (lid < kSB) pixs[0][lid] = lid < nt ? block_pixel(tb, lid) : 0;
   };
   // given queries (boundary-readout variant instantiations; the running readout reads them
   // directly): 16 bytes per loader thread, threads from 0, fp32 (4 values) or bf16 (8
@@ -365,6 +371,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     lo = Sl[mi][s];
   };
 
+  int bpar = 0;  // pixel-table buffer of the current block (early staging)
   for (int s0 = 0; s0 < N; s0 += C) {
     const int s1 = min(s0 + C, N);
     // (at d = 64 the M_mem tiles, first read in the readout, are split there, off the
@@ -392,6 +399,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
       const int nt = min(kSB, s1 - tb);
       const bool first = tb == s0;
       const bool last_block = tb + kSB >= s1;
+      const int* const pixc = pixs[kEarly ? bpar : 0];
 
       // A: projections P[t][row] = x_t . S_b[row] for the k, v, q, eta, alpha rows
       {
@@ -432,6 +440,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
       }
       lds_barrier();
 
+      f32x4 gr_e = {0.f, 0.f, 0.f, 0.f};  // early Gram and retention products (kEarly)
+      float pj_e[4] = {0.f, 0.f, 0.f, 0.f};
       // B: normalisation, gates and executed step; 16 lanes per token (one DPP row),
       // each lane holding CPL consecutive components.  Padding tokens get no key, no
       // write and unit retention.
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           } else if (kStageQ) {
             qr[e] = Qs[t * D + c16 * CPL + e];
           } else {
-            const int64_t qi = ((int64_t)b * N + pixs[t]) * Dt + (int64_t)h * D + c16 * CPL + e;
+            const int64_t qi = ((int64_t)b * N + pixc[t]) * Dt + (int64_t)h * D + c16 * CPL + e;
             qr[e] = p.queries_bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(vptr[2])[qi] << 16)
                                    : static_cast<const float*>(vptr[2])[qi];
           }
@@ -481,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           atomicAdd(&cnt_lds[2], (unsigned)((sf.bits >> 1) & 1));
         }
         if (v_steps && c16 == 0 && live)
-          v_steps[(((int64_t)b * 4 + r) * p.nh + h) * ((int64_t)p.H * p.W) + pixs[t]] = step;
+          v_steps[(((int64_t)b * 4 + r) * p.nh + h) * ((int64_t)p.H * p.W) + pixc[t]] = step;
 #pragma unroll
         for (int e = 0; e < CPL; e += 2) {
           const int col = c16 * CPL + e;
@@ -506,8 +516,57 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         if (c16 == 0) {
           alph[t] = live ? alpha : 1.f;
           stp[t] = live ? step : 0.f;
+          if (kEarly) kinvs[t] = kinv;
         }
         __builtin_amdgcn_s_setprio(0);
+      } else if (kEarly) {
+        // the solve waves meanwhile.  (1) The loader threads stage the next block's tokens,
+        // fetched a block ago (X was last read in A), with its pixel table in the other
+        // buffer, and request the block after it.
+        {
+          int tn, ntn;
+          next_block(tb, tn, ntn);
+          if (ntn > 0) {
+            const int ld_i = lid - kLoad0;
+            const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
+            if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
+            if (ld_i >= 0 && ld_i < kSB) pixs[bpar ^ 1][ld_i] = ld_i < ntn ? block_pixel(tn, ld_i) : 0;
+            int tn2, ntn2;
+            next_block(tn, tn2, ntn2);
+            pf = fetch(lid, tn2, ntn2);
+          }
+        }
+        // (2) retention of token c16, computed from its score exactly as in the gate phase
+        // (unit for padding tokens), and the retention products: P(j+1, t) for L (suffix
+        // over j = c16) and the block products P(0, t), P(t+1, 16)
+        float ez;
+        const float a_self = c16 < nt ? gate_alpha(Pj[c16 * PLD + 3 * D + 1], gp, &ez) : 1.f;
+        const int one = __builtin_bit_cast(int, 1.f);
+        const float a_next = __builtin_bit_cast(  // row_shl:1, lane 15 reads 1
+            float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x101, 0xF, 0xF, false));
+        const float a_prev = __builtin_bit_cast(  // row_shr:1, lane 0 reads 1
+            float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pj_e[i] = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+        if (w == SW0) {
+          const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
+          const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
+          if (lane < kSB) {
+            cprev[lane] = pre;
+            bco[lane] = suf;
+            if (lane == kSB - 1) bco[kSB] = pre * a_self;
+          }
+        }
+        // (3) Gram matrix of the raw keys, gr_e[i] = k_raw,{4g+i} . k_raw,{c16} (fp32 rows of
+        // the projections split into bf16 hi/lo); the normalised Gram is kinv_t kinv_j times it
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          f32x4 v0, v1;
+          load_row_pair(Pj + c16 * PLD, s, g, v0, v1);
+          bf16x8 kh, kl;
+          split8(v0, v1, kh, kl);
+          gr_e = mma32x3(kh, kl, kh, kl, gr_e);
+        }
       }
       lds_barrier();
 
@@ -542,7 +601,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           rq = acc;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            rpix[i] = pixs[4 * g + i];
+            rpix[i] = pixc[4 * g + i];
             if (has_skip) rx[i] = xs_at(4 * g + i, m * 16 + c16);
           }
         } else {
@@ -553,7 +612,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           for (int i = 0; i < 4; ++i) {
             const int t = 4 * g + i;
             if (t < nt)
-              dst[((int64_t)b * N + pixs[t]) * Dt + c] =
+              dst[((int64_t)b * N + pixc[t]) * Dt + c] =
                   finish(acc[i], skip_c, scale_c, has_skip ? xs_at(t, m * 16 + c16) : 0.f);
           }
         }
@@ -580,46 +639,59 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         // Gram product): P(j+1, t) for L (suffix over j), P(r+1, c) for the running
         // readout's A^T (prefix over c), and the block products P(0, t), P(t+1, 16)
         const bool ais_wave = RUN && w == SW0;
-        const float a_self = alph[c16];
-        const float a_next = alph[min(c16 + 1, kSB - 1)], a_prev = alph[max(c16 - 1, 0)];
         float pj[4], pc[4], st_r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * g + i;
-          st_r[i] = stp[rr];
-          pj[i] = row16_suffix_prod(c16 + 1 < rr ? a_next : 1.f);
-          pc[i] = ais_wave ? row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f) : 0.f;
-        }
-        {
-          // every solve wave stores the same values; each reads back only after its own store
-          const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
-          const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
-          if (lane < kSB) {
-            cprev[lane] = pre;
-            bco[lane] = suf;
-            if (lane == kSB - 1) bco[kSB] = pre * a_self;
-          }
-        }
-        // token Gram matrix, gr[i] = k_{4g+i} . k_{c16} (and, for the running readout,
-        // aq[i] = k_{4g+i} . q_{c16})
         f32x4 gr = zero4, aq = zero4;
+        if (kEarly) {
+          // retention products and raw Gram from the gate phase; normalise the Gram here
+          const float kv_j = kinvs[c16];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 kh = load_row_pair_bf16(KH + c16 * XLD, s, g);
-          const bf16x8 kl = load_row_pair_bf16(KL + c16 * XLD, s, g);
-          gr = mma32x3(kh, kl, kh, kl, gr);
-          if (ais_wave) {
-            const bf16x8 qh = load_row_pair_bf16(QH + c16 * XLD, s, g);
-            const bf16x8 ql = load_row_pair_bf16(QL + c16 * XLD, s, g);
-            aq = mma32x3(kh, kl, qh, ql, aq);
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * g + i;
+            st_r[i] = stp[rr];
+            pj[i] = pj_e[i];
+            pc[i] = 0.f;
+            gr[i] = kinvs[rr] * kv_j * gr_e[i];
           }
-        }
-        if (ais_wave) {
-          // A^T[j][t] = P(j+1, t) (k_j . q_t) for j < t, in the accumulator layout
-          f32x4 at;
+        } else {
+          const float a_self = alph[c16];
+          const float a_next = alph[min(c16 + 1, kSB - 1)], a_prev = alph[max(c16 - 1, 0)];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) at[i] = 4 * g + i < c16 ? pc[i] * aq[i] : 0.f;
-          *reinterpret_cast<f32x4*>(Ais + 4 * lane) = at;
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * g + i;
+            st_r[i] = stp[rr];
+            pj[i] = row16_suffix_prod(c16 + 1 < rr ? a_next : 1.f);
+            pc[i] = ais_wave ? row16_prefix_prod(c16 >= rr + 2 ? a_prev : 1.f) : 0.f;
+          }
+          {
+            // every solve wave stores the same values; each reads back only after its own store
+            const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
+            const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
+            if (lane < kSB) {
+              cprev[lane] = pre;
+              bco[lane] = suf;
+              if (lane == kSB - 1) bco[kSB] = pre * a_self;
+            }
+          }
+          // token Gram matrix, gr[i] = k_{4g+i} . k_{c16} (and, for the running readout,
+          // aq[i] = k_{4g+i} . q_{c16})
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const bf16x8 kh = load_row_pair_bf16(KH + c16 * XLD, s, g);
+            const bf16x8 kl = load_row_pair_bf16(KL + c16 * XLD, s, g);
+            gr = mma32x3(kh, kl, kh, kl, gr);
+            if (ais_wave) {
+              const bf16x8 qh = load_row_pair_bf16(QH + c16 * XLD, s, g);
+              const bf16x8 ql = load_row_pair_bf16(QL + c16 * XLD, s, g);
+              aq = mma32x3(kh, kl, qh, ql, aq);
+            }
+          }
+          if (ais_wave) {
+            // A^T[j][t] = P(j+1, t) (k_j . q_t) for j < t, in the accumulator layout
+            f32x4 at;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) at[i] = 4 * g + i < c16 ? pc[i] * aq[i] : 0.f;
+            *reinterpret_cast<f32x4*>(Ais + 4 * lane) = at;
+          }
         }
         // L[t][j] (t = 4g+i, j = c16) goes to LTw[j][4 (t mod 4) + t / 4]; without the
         // key-dependent correction the writes do not interact (L = 0)
@@ -849,8 +921,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         }
       }
       // stage the next block (X was last read in A, the pixel table in C) and request
-      // the one after it
-      {
+      // the one after it (done during the gate phase in the early form)
+      if (!kEarly) {
         int tn, ntn;
         next_block(tb, tn, ntn);
         if (ntn > 0) {
@@ -864,6 +936,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           qpf = fetch_q(lid2, tn2, ntn2, vptr[2]);
         }
       }
+      bpar ^= 1;
       lds_barrier();
     }
     if (MULTI) {

@@ -69,6 +69,16 @@ __device__ __forceinline__ float one_minus_exp_neg(float x) {
   return x < 0.25f ? series : 1.f - fast_exp(-x);
 }
 
+// Retention alpha = sigmoid(s_alpha + bias) (App. C.1 Eq. 53), with e^-z for 1 - alpha; the
+// chain kernels that need alpha outside the gate phase call this same function, so both
+// uses agree bit for bit.
+__device__ __forceinline__ float gate_alpha(float s_alpha, const GateParams& g, float* ez_out) {
+  const float z = s_alpha + g.alpha_bias;
+  const float ez = fast_exp(-z);
+  *ez_out = ez;
+  return fast_rcp(1.f + ez);
+}
+
 // Variants ("VisionHOPE", Sec. 3.5 ablations): a hard clamp min(eta, eta_inj) or no
 // injection control; the smooth spectral map eta_spec (1 - exp(-eta_bar / eta_spec)) or no
 // spectral control.
@@ -81,9 +91,8 @@ __device__ __forceinline__ float executed_step(float kk, float dd, float s_eta, 
   } else {
     eta = g.eta_scale * (fmaxf(s_eta, 0.f) + log1pf(fast_exp(-fabsf(s_eta))));
   }
-  const float z = s_alpha + g.alpha_bias;
-  const float ez = fast_exp(-z);
-  const float alpha = fast_rcp(1.f + ez);
+  float ez;
+  const float alpha = gate_alpha(s_alpha, g, &ez);
   const float one_minus_alpha = ez * alpha;  // sigmoid(-z), accurate near alpha = 1
   const float rr = fast_sqrt(dd + g.eps * g.eps) + g.eps;
   const float inj = (1.f - 1e-3f) * one_minus_alpha * fast_rcp(rr);
