@@ -173,6 +173,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   __shared__ __attribute__((aligned(16))) unsigned short QL[kSB * XLD];
   __shared__ int pixs[2][kSB];  // token pixels; two buffers when the next block is staged early
   __shared__ float kinvs[kEarly ? kSB : 1];  // 1 / |k_raw| of each token (early Gram)
+  // early form: raw-key Gram matrix and retention products, accumulator layout
+  __shared__ __attribute__((aligned(16))) float GrS[kEarly ? 256 : 4];
+  __shared__ __attribute__((aligned(16))) float PrS[kEarly ? 256 : 4];
   __shared__ __attribute__((aligned(16))) float Gs[MULTI ? D * LD : 4];
   __shared__ __attribute__((aligned(16))) float alph[kSB];
   __shared__ __attribute__((aligned(16))) float stp[kSB];
@@ -440,8 +443,6 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
       }
       lds_barrier();
 
-      f32x4 gr_e = {0.f, 0.f, 0.f, 0.f};  // early Gram and retention products (kEarly)
-      float pj_e[4] = {0.f, 0.f, 0.f, 0.f};
       // B: normalisation, gates and executed step; 16 lanes per token (one DPP row),
       // each lane holding CPL consecutive components.  Padding tokens get no key, no
       // write and unit retention.
@@ -520,35 +521,39 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         }
         __builtin_amdgcn_s_setprio(0);
       } else if (kEarly) {
-        // the solve waves meanwhile.  (1) The loader threads stage the next block's tokens,
-        // fetched a block ago (X was last read in A), with its pixel table in the other
-        // buffer, and request the block after it.
-        {
-          int tn, ntn;
-          next_block(tb, tn, ntn);
-          if (ntn > 0) {
-            const int ld_i = lid - kLoad0;
-            const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
-            if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
-            if (ld_i >= 0 && ld_i < kSB) pixs[bpar ^ 1][ld_i] = ld_i < ntn ? block_pixel(tn, ld_i) : 0;
-            int tn2, ntn2;
-            next_block(tn, tn2, ntn2);
-            pf = fetch(lid, tn2, ntn2);
-          }
-        }
-        // (2) retention of token c16, computed from its score exactly as in the gate phase
-        // (unit for padding tokens), and the retention products: P(j+1, t) for L (suffix
-        // over j = c16) and the block products P(0, t), P(t+1, 16)
-        float ez;
-        const float a_self = c16 < nt ? gate_alpha(Pj[c16 * PLD + 3 * D + 1], gp, &ez) : 1.f;
-        const int one = __builtin_bit_cast(int, 1.f);
-        const float a_next = __builtin_bit_cast(  // row_shl:1, lane 15 reads 1
-            float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x101, 0xF, 0xF, false));
-        const float a_prev = __builtin_bit_cast(  // row_shr:1, lane 0 reads 1
-            float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pj_e[i] = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+        // the solve waves meanwhile, each part on one wave and published in LDS in the
+        // accumulator layout (lane (g, c16), entry i: t = 4g + i, j = c16) for the solve
+        // phase.  (1) Wave SW0: the Gram matrix of the raw keys, Graw[t][j] = k_raw,t .
+        // k_raw,j (fp32 rows of the projections split into bf16 hi/lo); the normalised Gram
+        // is kinv_t kinv_j times it.
+        __builtin_amdgcn_s_setprio(2);  // as urgent as the gates: L needs both
         if (w == SW0) {
+          f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            f32x4 v0, v1;
+            load_row_pair(Pj + c16 * PLD, s, g, v0, v1);
+            bf16x8 kh, kl;
+            split8(v0, v1, kh, kl);
+            gr = mma32x3(kh, kl, kh, kl, gr);
+          }
+          *reinterpret_cast<f32x4*>(GrS + 4 * lane) = gr;
+        }
+        // (2) Wave SW0 + 1: retention of token c16, computed from its score exactly as in
+        // the gate phase (unit for padding tokens), the suffix products P(j+1, t) for L, and
+        // the block products P(0, t), P(t+1, 16)
+        if (w == SW0 + 1) {
+          float ez;
+          const float a_self = c16 < nt ? gate_alpha(Pj[c16 * PLD + 3 * D + 1], gp, &ez) : 1.f;
+          const int one = __builtin_bit_cast(int, 1.f);
+          const float a_next = __builtin_bit_cast(  // row_shl:1, lane 15 reads 1
+              float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x101, 0xF, 0xF, false));
+          const float a_prev = __builtin_bit_cast(  // row_shr:1, lane 0 reads 1
+              float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
+          f32x4 pr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[i] = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+          *reinterpret_cast<f32x4*>(PrS + 4 * lane) = pr;
           const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
           const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
           if (lane < kSB) {
@@ -557,15 +562,20 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
             if (lane == kSB - 1) bco[kSB] = pre * a_self;
           }
         }
-        // (3) Gram matrix of the raw keys, gr_e[i] = k_raw,{4g+i} . k_raw,{c16} (fp32 rows of
-        // the projections split into bf16 hi/lo); the normalised Gram is kinv_t kinv_j times it
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          f32x4 v0, v1;
-          load_row_pair(Pj + c16 * PLD, s, g, v0, v1);
-          bf16x8 kh, kl;
-          split8(v0, v1, kh, kl);
-          gr_e = mma32x3(kh, kl, kh, kl, gr_e);
+        __builtin_amdgcn_s_setprio(0);
+        // (3) The loader threads stage the next block's tokens, fetched a block ago (X was
+        // last read in A), with its pixel table in the other buffer, and request the block
+        // after it.  At d = 64 every chunk is one block (at most 16 tokens), so the next
+        // blocks start at s1 and s1 + C.
+        const int tn = s1;
+        if (tn < N) {
+          const int ntn = min(C, N - tn);
+          const int ld_i = lid - kLoad0;
+          const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
+          if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
+          if (ld_i >= 0 && ld_i < kSB) pixs[bpar ^ 1][ld_i] = ld_i < ntn ? block_pixel(tn, ld_i) : 0;
+          const int tn2 = tn + C;
+          pf = fetch(lid, tn2, tn2 < N ? min(C, N - tn2) : 0);
         }
       }
       lds_barrier();
@@ -644,6 +654,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         if (kEarly) {
           // retention products and raw Gram from the gate phase; normalise the Gram here
           const float kv_j = kinvs[c16];
+          const f32x4 gr_e = *reinterpret_cast<const f32x4*>(GrS + 4 * lane);
+          const f32x4 pj_e = *reinterpret_cast<const f32x4*>(PrS + 4 * lane);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int rr = 4 * g + i;
@@ -737,9 +749,16 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         }
         if (!v_nodgd) {
           // (padding rows have zero RHS and zero L; they run through unchanged)
+          // Coefficient rows are read kPF steps ahead of their use (a rotating set of
+          // registers), so that each step's LDS latency hides behind the steps before it.
+          constexpr int kPF = 7;
+          f32x4 crow[kPF];
+#pragma unroll
+          for (int j = 0; j < kPF; ++j) crow[j] = *reinterpret_cast<const f32x4*>(LTw + j * LTLD + 4 * q);
 #pragma unroll
           for (int j = 0; j < kSB - 1; ++j) {
-            const f32x4 c = *reinterpret_cast<const f32x4*>(LTw + j * LTLD + 4 * q);
+            const f32x4 c = crow[j % kPF];
+            if (j + kPF < kSB - 1) crow[j % kPF] = *reinterpret_cast<const f32x4*>(LTw + (j + kPF) * LTLD + 4 * q);
             const float uj = quad_bcast(u[j >> 2], j & 3);
 #pragma unroll
             for (int i = j >> 2; i < 4; ++i) {
