@@ -469,21 +469,23 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           kk += kr[e] * kr[e];
           qq += qr[e] * qr[e];
         }
-        const float kinv = fast_rsqrt(row16_sum(kk) + gp.eps);
+        const float kk_all = row16_sum(kk);
+        const float kinv = fast_rsqrt(kk_all + gp.eps);
         const float qinv = fast_rsqrt(row16_sum(qq) + gp.eps);
         float kn[CPL], dl[CPL], qn[CPL];
-        float kk2 = 0.f, dd = 0.f;
+        float dd = 0.f;
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           kn[e] = kr[e] * kinv;
           qn[e] = qr[e] * qinv;
           dl[e] = kn[e] - vr[e];
-          kk2 += kn[e] * kn[e];
           dd += dl[e] * dl[e];
         }
+        // |k|^2 of the normalised key: |k_raw|^2 kinv^2
+        const float kk2 = kk_all * kinv * kinv;
         float alpha;
         StepFlags sf;
-        const float step = executed_step(row16_sum(kk2), row16_sum(dd), Pj[t * PLD + 3 * D],
+        const float step = executed_step(kk2, row16_sum(dd), Pj[t * PLD + 3 * D],
                                          Pj[t * PLD + 3 * D + 1], gp, &alpha, &sf);
         const bool live = t < nt;
         if (v_counts && c16 == 0 && live) {
@@ -496,12 +498,15 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
 #pragma unroll
         for (int e = 0; e < CPL; e += 2) {
           const int col = c16 * CPL + e;
-          const float k0 = live ? kn[e] : 0.f, k1 = live ? kn[e + 1] : 0.f;
-          const float q0 = live ? qn[e] : 0.f, q1 = live ? qn[e + 1] : 0.f;
+          // padding tokens have x = 0, so their raw projections, k and delta are exactly
+          // zero; only queries read from the map need the mask
+          const bool qlive = live || !(has_q && !kStageQ);
+          const float k0 = kn[e], k1 = kn[e + 1];
+          const float q0 = qlive ? qn[e] : 0.f, q1 = qlive ? qn[e + 1] : 0.f;
           Ks[t * LD + col] = k0;
           Ks[t * LD + col + 1] = k1;
-          Dls[t * LD + col] = live ? dl[e] : 0.f;
-          Dls[t * LD + col + 1] = live ? dl[e + 1] : 0.f;
+          Dls[t * LD + col] = dl[e];
+          Dls[t * LD + col + 1] = dl[e + 1];
           unsigned kh, kl, qh, ql;
           split_pair(k0, k1, kh, kl);
           split_pair(q0, q1, qh, ql);
@@ -552,7 +557,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
               float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
           f32x4 pr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pr[i] = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+          for (int i = 0; i < 4; ++i) {
+            const float sp = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+            pr[i] = c16 < 4 * g + i ? sp : 0.f;  // strictly lower triangle: L's mask
+          }
           *reinterpret_cast<f32x4*>(PrS + 4 * lane) = pr;
           const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
           const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
@@ -710,7 +718,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g + i;
-          LTw[c16 * LTLD + 4 * i + g] = c16 < rr && !v_nodgd ? st_r[i] * pj[i] * gr[i] : 0.f;
+          const float lv = st_r[i] * pj[i] * gr[i];  // (the early pj is already masked)
+          LTw[c16 * LTLD + 4 * i + g] = kEarly || (c16 < rr && !v_nodgd) ? lv : 0.f;
         }
         // RHS of a later block of a multi-block chunk: G_s k_t on MFMA for this wave's
         // column tile, staged token-major in Ubs (overwritten below with the write vectors)
@@ -748,7 +757,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           }
         }
         if (!v_nodgd) {
-          // (padding rows have zero RHS and zero L; they run through unchanged)
+          // (padding rows have zero RHS and zero L; they run through unchanged.  L is zero on
+          // and above the diagonal, so the rows t <= j of step j subtract an exact zero and
+          // need no mask)
           // Coefficient rows are read kPF steps ahead of their use (a rotating set of
           // registers), so that each step's LDS latency hides behind the steps before it.
           constexpr int kPF = 7;
@@ -761,10 +772,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
             if (j + kPF < kSB - 1) crow[j % kPF] = *reinterpret_cast<const f32x4*>(LTw + (j + kPF) * LTLD + 4 * q);
             const float uj = quad_bcast(u[j >> 2], j & 3);
 #pragma unroll
-            for (int i = j >> 2; i < 4; ++i) {
-              const float nu = fmaf(-c[i], uj, u[i]);
-              u[i] = (4 * i > j || q > (j & 3)) ? nu : u[i];
-            }
+            for (int i = j >> 2; i < 4; ++i) u[i] = fmaf(-c[i], uj, u[i]);
           }
         }
 #pragma unroll
