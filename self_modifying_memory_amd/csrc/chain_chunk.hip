@@ -394,19 +394,19 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             kk += kr[e] * kr[e];
             qq += qr[e] * qr[e];
           }
-          const float kinv = fast_rsqrt(row16_sum(kk) + gp.eps);
+          const float kk_all = row16_sum(kk);
+          const float kinv = fast_rsqrt(kk_all + gp.eps);
           const float qinv = fast_rsqrt(row16_sum(qq) + gp.eps);
           float kn[CPL], dl[CPL], qn[CPL];
-          float kk2 = 0.f, dd = 0.f;
+          float dd = 0.f;
 #pragma unroll
           for (int e = 0; e < CPL; ++e) {
             kn[e] = kr[e] * kinv;
             qn[e] = qr[e] * qinv;
             dl[e] = kn[e] - vr[e];
-            kk2 += kn[e] * kn[e];
             dd += dl[e] * dl[e];
           }
-          kk2 = row16_sum(kk2);
+          const float kk2 = kk_all * kinv * kinv;  // |k|^2 of the normalised key
           dd = row16_sum(dd);
           if (c16 == 0) {
             Sc[t] = kk2;
@@ -421,12 +421,15 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
 #pragma unroll
             for (int e = 0; e < CPL; e += 2) {
               const int col = c16 * CPL + e;
-              const float k0 = live ? kn[e] : 0.f, k1 = live ? kn[e + 1] : 0.f;
-              const float q0 = live ? qn[e] : 0.f, q1 = live ? qn[e + 1] : 0.f;
+              // padding tokens have x = 0: k and delta are exactly zero; only queries read
+              // from the map need the mask
+              const bool qlive = live || !has_q;
+              const float k0 = kn[e], k1 = kn[e + 1];
+              const float q0 = qlive ? qn[e] : 0.f, q1 = qlive ? qn[e + 1] : 0.f;
               Ks[col * KSLD + t] = k0;
               Ks[(col + 1) * KSLD + t] = k1;
-              Dls[col * KSLD + t] = live ? dl[e] : 0.f;
-              Dls[(col + 1) * KSLD + t] = live ? dl[e + 1] : 0.f;
+              Dls[col * KSLD + t] = dl[e];
+              Dls[(col + 1) * KSLD + t] = dl[e + 1];
               unsigned kh, kl, qh, ql;
               split_pair(k0, k1, kh, kl);
               split_pair(q0, q1, qh, ql);
@@ -441,9 +444,9 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             }
           } else {
             const int col = c16;
-            const float k0 = live ? kn[0] : 0.f, q0 = live ? qn[0] : 0.f;
+            const float k0 = kn[0], q0 = (live || !has_q) ? qn[0] : 0.f;
             Ks[col * KSLD + t] = k0;
-            Dls[col * KSLD + t] = live ? dl[0] : 0.f;
+            Dls[col * KSLD + t] = dl[0];
             const __bf16 khv = (__bf16)k0, qhv = (__bf16)q0;
             const __bf16 klv = (__bf16)(k0 - (float)khv), qlv = (__bf16)(q0 - (float)qhv);
             const unsigned short khb = __builtin_bit_cast(unsigned short, khv);
@@ -589,11 +592,9 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
               const f32x4 cf = cfs[j % kPf];
               if (j + kPf < 15) cfs[j % kPf] = *reinterpret_cast<const f32x4*>(LTw + (j + kPf) * LTLD + 4 * qd);
               const float uj = quad_bcast(uu[j >> 2], j & 3);
+              // (L is zero on and above its diagonal: rows t <= j subtract an exact zero)
 #pragma unroll
-              for (int i = j >> 2; i < 4; ++i) {
-                const float nu = fmaf(-cf[i], uj, uu[i]);
-                uu[i] = (4 * i > j || qd > (j & 3)) ? nu : uu[i];
-              }
+              for (int i = j >> 2; i < 4; ++i) uu[i] = fmaf(-cf[i], uj, uu[i]);
             }
             // back through LDS into the A layout: lane (g, c) takes T[c][4g + i]
 #pragma unroll
@@ -650,12 +651,18 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
         }
         // W_J = T_JJ R_J, then R_I -= L_IJ W_J for the later tiles; W_J replaces R_J
         if (!v_nodgd) {
+          // the tiles on the dependent chain (T_JJ and L_{J+1,J}) are read a step ahead
+          const u32x4 zq = {0u, 0u, 0u, 0u};
+          u32x4 tq_n = Lt[lane];
+          u32x4 lq_n = TS > 1 ? Lt[64 + lane] : zq;
 #pragma unroll
           for (int J = 0; J < TMAX; ++J) {
             if (J >= TS) break;
+            const u32x4 tq = tq_n, lq1 = lq_n;
+            if (J + 1 < TS) tq_n = Lt[((J + 1) * (J + 2) / 2 + J + 1) * 64 + lane];
+            if (J + 2 < TS) lq_n = Lt[((J + 2) * (J + 3) / 2 + J + 1) * 64 + lane];
             bf16x4 rh, rl;
             split4(R[J], rh, rl);
-            const u32x4 tq = Lt[(J * (J + 1) / 2 + J) * 64 + lane];
             const bf16x4 th = __builtin_bit_cast(bf16x4, u32x2{tq[0], tq[1]});
             const bf16x4 tl = __builtin_bit_cast(bf16x4, u32x2{tq[2], tq[3]});
             R[J] = mma16x3(th, tl, rh, rl, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -664,7 +671,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
 #pragma unroll
             for (int I = J + 1; I < TMAX; ++I) {
               if (I >= TS) break;
-              const u32x4 lq = Lt[(I * (I + 1) / 2 + J) * 64 + lane];
+              const u32x4 lq = I == J + 1 ? lq1 : Lt[(I * (I + 1) / 2 + J) * 64 + lane];
               R[I] = mma16x3(__builtin_bit_cast(bf16x4, u32x2{lq[0], lq[1]}),
                              __builtin_bit_cast(bf16x4, u32x2{lq[2], lq[3]}), wh, wl, R[I]);
             }
