@@ -765,6 +765,9 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
         const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
         f32x4 acc = c16 < 2 ? *reinterpret_cast<const f32x4*>(run + c16 * D + 16 * w + 4 * g) : zz;
         acc *= cseg;
+        // even and odd token tiles accumulate apart (two independent product chains), then
+        // add in that order
+        f32x4 acc_odd = zz;
 #pragma unroll
         for (int tau = 0; tau < TMAX; ++tau) {
           if (tau >= TS) break;
@@ -774,8 +777,13 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
           split4(z, zh, zl);
           const bf16x4 kh = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtH + (16 * w + c16) * KTLD + 16 * tau + 4 * g));
           const bf16x4 kl = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (16 * w + c16) * KTLD + 16 * tau + 4 * g));
-          acc = mma16x3(kh, kl, zh, zl, acc);
+          if (tau & 1) {
+            acc_odd = mma16x3(kh, kl, zh, zl, acc_odd);
+          } else {
+            acc = mma16x3(kh, kl, zh, zl, acc);
+          }
         }
+        acc += acc_odd;
         // (every wave read the running rows before the barrier above; only this wave
         // writes its column tile)
         if (c16 < 2) *reinterpret_cast<f32x4*>(Tb[cur ^ 1] + c16 * D + 16 * w + 4 * g) = acc;
@@ -783,7 +791,12 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
       // gain of the chunk so far, for the next segment: G <- cseg G + Ub^T K, tiles of 16 x 16
       // dealt from wave NT on, after the waves that carry the gate rows above
       if (multi && !last && !v_nodgd) {
-        for (int tile = (w + NW - NT) % NW; tile < NT * NT; tile += NW) {
+        // (at d = 32 with 16 waves the four tiles go to waves 2, 3, 6 and 7: SIMDs 2 and 3,
+        // whose matrix cores do not also carry the gate rows, so the four SIMDs end the carry
+        // with equal product counts)
+        const int tile0 = (NT == 2 && NW == 16) ? (((w & 3) >= 2 && w < 8) ? (w & 1) + 2 * (w >> 2) : NT * NT)
+                                                : (w + NW - NT) % NW;
+        for (int tile = tile0; tile < NT * NT; tile += NW) {
           const int ti = tile / NT, tn = tile % NT;
           f32x4 acc;
 #pragma unroll
@@ -791,6 +804,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             const int gi = 16 * ti + 4 * g + e, gn = 16 * tn + c16;
             acc[e] = first ? (gi == gn ? cseg : 0.f) : cseg * Gs[gi * LD + gn];
           }
+          f32x4 acc_odd = {0.f, 0.f, 0.f, 0.f};  // odd token tiles, added at the end
 #pragma unroll
           for (int tau = 0; tau < TMAX; ++tau) {
             if (tau >= TS) break;
@@ -807,8 +821,13 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             const u32x2 al2 = {(unsigned)al[0] | ((unsigned)al[1] << 16), (unsigned)al[2] | ((unsigned)al[3] << 16)};
             const bf16x4 kh = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtH + (16 * tn + c16) * KTLD + 16 * tau + 4 * g));
             const bf16x4 kl = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(KtL + (16 * tn + c16) * KTLD + 16 * tau + 4 * g));
-            acc = mma16x3(__builtin_bit_cast(bf16x4, ah2), __builtin_bit_cast(bf16x4, al2), kh, kl, acc);
+            if (tau & 1) {
+              acc_odd = mma16x3(__builtin_bit_cast(bf16x4, ah2), __builtin_bit_cast(bf16x4, al2), kh, kl, acc_odd);
+            } else {
+              acc = mma16x3(__builtin_bit_cast(bf16x4, ah2), __builtin_bit_cast(bf16x4, al2), kh, kl, acc);
+            }
           }
+          acc += acc_odd;
 #pragma unroll
           for (int e = 0; e < 4; ++e) Gs[(16 * ti + 4 * g + e) * LD + 16 * tn + c16] = acc[e];
         }

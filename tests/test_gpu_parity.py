@@ -45,6 +45,11 @@ SMALL = [
     (2, 5, 6, 64, 1, "bf16", 15, 0, True,
      dict(eta_map="softplus", eta_scale=0.025, alpha_bias=math.log(9.0))),
     (1, 5, 5, 32, 1, "bf16", 15, 0, True, dict(eta_scale=50.0, alpha_bias=-3.0)),  # clamps
+    # d = 64 blocks staged during the gate phase: the next blocks start at the chunk ends
+    (2, 6, 9, 64, 1, "bf16", 15, 5, True, {}),          # d = 64, chunk 5 over 54 tokens (ragged)
+    (1, 4, 5, 64, 1, "bf16", 15, 1, True, {}),          # d = 64, one-token chunks
+    (1, 5, 6, 64, 1, "bf16", 4, 7, True, {}),           # d = 64, one column route, chunk 7
+    (1, 6, 6, 64, 1, "bf16", 15, 0, True, dict(eta_scale=50.0, alpha_bias=-3.0)),  # d = 64 clamps
 ]
 
 
