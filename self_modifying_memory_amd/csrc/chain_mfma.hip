@@ -510,8 +510,10 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           unsigned kh, kl, qh, ql;
           split_pair(k0, k1, kh, kl);
           split_pair(q0, q1, qh, ql);
-          *reinterpret_cast<unsigned*>(KH + t * XLD + col) = kh;
-          *reinterpret_cast<unsigned*>(KL + t * XLD + col) = kl;
+          if (!kEarly) {  // (the early form's Gram reads the raw keys)
+            *reinterpret_cast<unsigned*>(KH + t * XLD + col) = kh;
+            *reinterpret_cast<unsigned*>(KL + t * XLD + col) = kl;
+          }
           *reinterpret_cast<unsigned*>(QH + t * XLD + col) = qh;
           *reinterpret_cast<unsigned*>(QL + t * XLD + col) = ql;
           KtH[col * KTLD + t] = (unsigned short)kh;
@@ -544,30 +546,34 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           }
           *reinterpret_cast<f32x4*>(GrS + 4 * lane) = gr;
         }
-        // (2) Wave SW0 + 1: retention of token c16, computed from its score exactly as in
-        // the gate phase (unit for padding tokens), the suffix products P(j+1, t) for L, and
+        // (2) Waves SW0 + 1 and SW0 + 3: the retention of token c16, computed from its
+        // score exactly as in the gate phase (unit for padding tokens); wave SW0 + 1 forms the
+        // masked suffix products P(j+1, t) for L, wave SW0 + 3 (a loader wave, done early)
         // the block products P(0, t), P(t+1, 16)
-        if (w == SW0 + 1) {
+        if (w == SW0 + 1 || w == SW0 + 3) {
           float ez;
           const float a_self = c16 < nt ? gate_alpha(Pj[c16 * PLD + 3 * D + 1], gp, &ez) : 1.f;
           const int one = __builtin_bit_cast(int, 1.f);
           const float a_next = __builtin_bit_cast(  // row_shl:1, lane 15 reads 1
               float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x101, 0xF, 0xF, false));
-          const float a_prev = __builtin_bit_cast(  // row_shr:1, lane 0 reads 1
-              float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
-          f32x4 pr;
+          if (w == SW0 + 1) {
+            f32x4 pr;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sp = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
-            pr[i] = c16 < 4 * g + i ? sp : 0.f;  // strictly lower triangle: L's mask
-          }
-          *reinterpret_cast<f32x4*>(PrS + 4 * lane) = pr;
-          const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
-          const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
-          if (lane < kSB) {
-            cprev[lane] = pre;
-            bco[lane] = suf;
-            if (lane == kSB - 1) bco[kSB] = pre * a_self;
+            for (int i = 0; i < 4; ++i) {
+              const float sp = row16_suffix_prod(c16 + 1 < 4 * g + i ? a_next : 1.f);
+              pr[i] = c16 < 4 * g + i ? sp : 0.f;  // strictly lower triangle: L's mask
+            }
+            *reinterpret_cast<f32x4*>(PrS + 4 * lane) = pr;
+          } else {
+            const float a_prev = __builtin_bit_cast(  // row_shr:1, lane 0 reads 1
+                float, __builtin_amdgcn_update_dpp(one, __builtin_bit_cast(int, a_self), 0x111, 0xF, 0xF, false));
+            const float pre = row16_prefix_prod(c16 >= 1 ? a_prev : 1.f);
+            const float suf = row16_suffix_prod(c16 < kSB - 1 ? a_next : 1.f);
+            if (lane < kSB) {
+              cprev[lane] = pre;
+              bco[lane] = suf;
+              if (lane == kSB - 1) bco[kSB] = pre * a_self;
+            }
           }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -576,7 +582,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
         // after it.  At d = 64 every chunk is one block (at most 16 tokens), so the next
         // blocks start at s1 and s1 + C.
         const int tn = s1;
-        if (tn < N) {
+        if (w >= kLoad0 / 64 && tn < N) {  // (the loader waves only)
           const int ntn = min(C, N - tn);
           const int ld_i = lid - kLoad0;
           const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
