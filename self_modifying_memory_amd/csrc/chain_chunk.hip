@@ -465,9 +465,14 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
       // ---- B2: the executed step (Eq. 19-20) and the retention products, one token per lane
       // on wave 0 (a DPP row is a 16-token tile); the other waves form their token Gram tiles
       // G'[4g+i][c] = k_{16J+4g+i} . k_{16I+c} for tile pairs (I >= J), q = I (I + 1) / 2 + J,
-      // dealt round robin to waves 1 .. NW-1
+      // dealt round robin to the "pair waves" (rank pw): waves 1 .. NW-1, or, in the 8-wave
+      // launches, the waves that hold no M_mem rows, which then read out during C1 (measured:
+      // faster there, slower in the 16-wave launches)
       const int npairs = v_nodgd ? 0 : TS * (TS + 1) / 2;
-      constexpr int kMaxPairsPerWave = (TMAX * (TMAX + 1) / 2 + NW - 2) / (NW - 1);
+      constexpr bool kReadC1 = RW == 1 && NW == 8;
+      constexpr int kPairWaves = kReadC1 ? MT - NT : NW - 1;
+      const int pw = kReadC1 ? (m >= NT ? m - NT : -1) : w - 1;
+      constexpr int kMaxPairsPerWave = (TMAX * (TMAX + 1) / 2 + kPairWaves - 1) / kPairWaves;
       f32x4 gram[kMaxPairsPerWave];
       if (w == 0) {
 #pragma unroll
@@ -507,8 +512,8 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
       } else {
 #pragma unroll
         for (int k = 0; k < kMaxPairsPerWave; ++k) {
-          const int q = (w - 1) + k * (NW - 1);
-          if (q >= npairs) break;
+          const int q = pw + k * kPairWaves;
+          if (pw < 0 || q >= npairs) break;
           int I = 0;
           while ((I + 1) * (I + 2) / 2 <= q) ++I;
           const int J = q - I * (I + 1) / 2;
@@ -540,11 +545,12 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
         }
       }
 
-      // ---- C1: the L tiles (negated, in the A layout, hi/lo) and the diagonal inverses ----
-      if (w != 0) {
+      // ---- C1: the L tiles (negated, in the A layout, hi/lo) and the diagonal inverses on
+      // the pair waves; the readout on the M_mem waves ----
+      if (pw >= 0) {
 #pragma unroll
         for (int k = 0; k < kMaxPairsPerWave; ++k) {
-          const int q = (w - 1) + k * (NW - 1);
+          const int q = pw + k * kPairWaves;
           if (q >= npairs) break;
           int I = 0;
           while ((I + 1) * (I + 2) / 2 <= q) ++I;
@@ -607,9 +613,33 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
           }
         }
       }
+      // readout y_t = M_mem,b q_t for this wave's 16 rows of M_mem (the M_mem waves)
+      auto readout = [&]() {
+        const int64_t c = (int64_t)h * D + 16 * m + c16;
+        const float skip_c = has_skip ? static_cast<const float*>(vptr[0])[c] : 0.f;
+        const float scale_c = has_scales ? static_cast<const float*>(vptr[1])[(int64_t)r * Dt + c] : 1.f;
+#pragma unroll
+        for (int tau = 0; tau < TMAX; ++tau) {
+          if (tau >= TS) break;
+          if (RW > 1 && tau % RW != u) continue;
+          const V qh = Ops::row(QH + (16 * tau + c16) * XLD, g), ql = Ops::row(QL + (16 * tau + c16) * XLD, g);
+          const f32x4 y = Ops::mma3(qh, ql, Sh, Sl, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * tau + 4 * g + i;
+            if (t < ns) {
+              float yv = y[i];
+              if (has_skip) yv = fmaf(skip_c, __uint_as_float((unsigned)Xs[t * XLD + 16 * m + c16] << 16), yv);
+              if (has_scales) yv *= scale_c;
+              dst[((int64_t)b * N + pixs[t]) * Dt + c] = yv;
+            }
+          }
+        }
+      };
+      if (kReadC1 && m < NT) readout();
       lds_barrier();
 
-      // ---- C2: the write vectors (solve waves) and the readout (M_mem waves) -------------
+      // ---- C2: the write vectors (solve waves) -------------------------------------------
       if (w >= SW0) {
         __builtin_amdgcn_s_setprio(3);  // the segment's critical path
         const int n = w - SW0;          // this wave's 16 columns of W
@@ -691,28 +721,8 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
           }
         }
         __builtin_amdgcn_s_setprio(0);
-      } else if (m < NT) {
-        // readout y_t = M_mem,b q_t for this wave's 16 rows of M_mem
-        const int64_t c = (int64_t)h * D + 16 * m + c16;
-        const float skip_c = has_skip ? static_cast<const float*>(vptr[0])[c] : 0.f;
-        const float scale_c = has_scales ? static_cast<const float*>(vptr[1])[(int64_t)r * Dt + c] : 1.f;
-#pragma unroll
-        for (int tau = 0; tau < TMAX; ++tau) {
-          if (tau >= TS) break;
-          if (RW > 1 && tau % RW != u) continue;
-          const V qh = Ops::row(QH + (16 * tau + c16) * XLD, g), ql = Ops::row(QL + (16 * tau + c16) * XLD, g);
-          const f32x4 y = Ops::mma3(qh, ql, Sh, Sl, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * tau + 4 * g + i;
-            if (t < ns) {
-              float yv = y[i];
-              if (has_skip) yv = fmaf(skip_c, __uint_as_float((unsigned)Xs[t * XLD + 16 * m + c16] << 16), yv);
-              if (has_scales) yv *= scale_c;
-              dst[((int64_t)b * N + pixs[t]) * Dt + c] = yv;
-            }
-          }
-        }
+      } else if (!kReadC1 && m < NT) {
+        readout();
       }
       lds_barrier();
 
