@@ -580,6 +580,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             // lane qd holding rows qd, qd + 4, qd + 8, qd + 12; L copied so that one 16-byte
             // read gives a lane its four coefficients of column j
             float* const LTw = LTs + J * (16 * LTLD);
+            __builtin_amdgcn_s_setprio(2);  // the inverses end the phase: let them issue first
 #pragma unroll
             for (int i = 0; i < 4; ++i) LTw[(4 * g + i) * LTLD + 4 * (c16 & 3) + (c16 >> 2)] = lv[i];
             const int col = lane >> 2, qd = lane & 3;
@@ -610,6 +611,7 @@ __global__ __launch_bounds__(64 * NW_, (D == 16 && SEG_ == 16) ? 7 : (D == 32 &&
             split4(tv, hi, lo);
             const u32x2 h2 = __builtin_bit_cast(u32x2, hi), l2 = __builtin_bit_cast(u32x2, lo);
             Lt[q * 64 + lane] = u32x4{h2[0], h2[1], l2[0], l2[1]};
+            __builtin_amdgcn_s_setprio(0);
           }
         }
       }
