@@ -147,12 +147,14 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   constexpr int PLD = 3 * D + 4;                   // fp32 stride of the projections
   constexpr int KTLD = kSB + 4;                    // bf16 stride of transposed K (per column)
   constexpr int LTLD = kSB + 4;                    // fp32 stride of L^T
-  constexpr bool kDeferMemSplit = D == 64;
   // d = 64, boundary readout, no variant options: the solve waves, idle while waves 0-3
   // form the gates, use that phase for the block's retention products, the Gram matrix of
   // the raw keys and the staging of the next block's tokens, all of which need only the
   // projections
   constexpr bool kEarly = D == 64 && !RUN && VAR == 0;
+  // the M_mem tiles' split waits for the readout, off the projections' path, except in the
+  // early form, whose readout waves wait for the solve waves' projections anyway
+  constexpr bool kDeferMemSplit = D == 64 && !kEarly;
 
   __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
@@ -377,8 +379,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   int bpar = 0;  // pixel-table buffer of the current block (early staging)
   for (int s0 = 0; s0 < N; s0 += C) {
     const int s1 = min(s0 + C, N);
-    // (at d = 64 the M_mem tiles, first read in the readout, are split there, off the
-    // projections' path; measured slower at d = 32)
+    // (at d = 64 outside the early form the M_mem tiles, first read in the readout, are split
+    // there, off the projections' path; measured slower at d = 32)
 #pragma unroll
     for (int mi = 0; mi < MTW; ++mi)
       if (!kDeferMemSplit || w + kWaves * mi >= NT) {
