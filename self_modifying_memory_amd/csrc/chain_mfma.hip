@@ -151,12 +151,16 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   // form the gates, use that phase for the block's retention products, the Gram matrix of
   // the raw keys and the staging of the next block's tokens, all of which need only the
   // projections
-  constexpr bool kEarly = D == 64 && !RUN && VAR == 0;
+  constexpr bool kEarly = D == 64 && !RUN && VAR != 1;
+  // the early form stages the next block while this one's tokens (skip) and given queries
+  // may still be read: two buffers of each with the block's options (the default operator
+  // reads its tokens only in the projections, before the staging)
+  constexpr int kXB = kEarly && VAR != 0 ? 2 : 1;
   // the M_mem tiles' split waits for the readout, off the projections' path, except in the
   // early form, whose readout waves wait for the solve waves' projections anyway
   constexpr bool kDeferMemSplit = D == 64 && !kEarly;
 
-  __shared__ __attribute__((aligned(16))) unsigned short Xs[kSB * XLD];
+  __shared__ __attribute__((aligned(16))) unsigned short Xs[kXB * kSB * XLD];
   __shared__ __attribute__((aligned(16))) float Pj[kSB * PLD];
   __shared__ __attribute__((aligned(16))) float Ks[kSB * LD];
   __shared__ __attribute__((aligned(16))) float Dls[kSB * LD];
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
   // running readout: the masked token matrix A^T and the unscaled write vectors U
   __shared__ __attribute__((aligned(16))) float Ais[RUN ? 64 * 4 : 4];
   // given queries of the current block (fp32), staged one block ahead like x
-  __shared__ __attribute__((aligned(16))) float Qs[VAR && !RUN ? kSB * D : 4];
+  __shared__ __attribute__((aligned(16))) float Qs[VAR && !RUN ? kXB * kSB * D : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuH[RUN ? kSB * XLD : 4];
   __shared__ __attribute__((aligned(16))) unsigned short UuL[RUN ? kSB * XLD : 4];
   // the two gate rows (m_eta, m_alpha) live in LDS so that every wave holds the same
@@ -232,8 +236,9 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     if (has_scales) y *= scale_c;
     return y;
   };
+  const unsigned short* Xcur = Xs;  // this block's tokens (a buffer of Xs)
   auto xs_at = [&](int t, int col) {
-    return __uint_as_float((unsigned)Xs[t * XLD + col] << 16);
+    return __uint_as_float((unsigned)Xcur[t * XLD + col] << 16);
   };
   const unsigned short* xg = static_cast<const unsigned short*>(p.x);
   // pixel of token tb + i of this route (tb the same in every lane, 0 <= i < kSB): one
@@ -336,12 +341,12 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     }
     return v;
   };
-  auto stage_q = [&](int lid, const u32x4& v) {
+  auto stage_q = [&](int lid, const u32x4& v, int buf) {
     if (kStageQ && has_q) {
       const int per = p.queries_bf16 ? kQPer16 : kQPer32;
       const int lt = lid / (D / per), lc = lid % (D / per);
       if (lt < kSB) {
-        float* q = Qs + lt * D + lc * per;
+        float* q = Qs + buf * (kSB * D) + lt * D + lc * per;
         if (p.queries_bf16) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
     const int lid = threadIdx.x;
     const int nt0 = min(kSB, min(C, N));
     stage_block(lid, fetch(lid, 0, nt0), 0, nt0);
-    stage_q(lid, fetch_q(lid, 0, nt0, p.queries));
+    stage_q(lid, fetch_q(lid, 0, nt0, p.queries), 0);
     int tn, ntn;
     next_block(0, tn, ntn);
     pf = fetch(lid, tn, ntn);
@@ -405,12 +410,13 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
       const bool first = tb == s0;
       const bool last_block = tb + kSB >= s1;
       const int* const pixc = pixs[kEarly ? bpar : 0];
+      Xcur = Xs + (kXB > 1 ? bpar : 0) * (kSB * XLD);
 
       // A: projections P[t][row] = x_t . S_b[row] for the k, v, q, eta, alpha rows
       {
         bf16x8 xa[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) xa[s] = load_row_pair_bf16(Xs + c16 * XLD, s, g);
+        for (int s = 0; s < KS; ++s) xa[s] = load_row_pair_bf16(Xcur + c16 * XLD, s, g);
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           const int m = w + kWaves * mi;
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           if (!has_q) {
             qr[e] = pt[2 * D + e];
           } else if (kStageQ) {
-            qr[e] = Qs[t * D + c16 * CPL + e];
+            qr[e] = Qs[(kXB > 1 ? bpar : 0) * (kSB * D) + t * D + c16 * CPL + e];
           } else {
             const int64_t qi = ((int64_t)b * N + pixc[t]) * Dt + (int64_t)h * D + c16 * CPL + e;
             qr[e] = p.queries_bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(vptr[2])[qi] << 16)
@@ -529,6 +535,13 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           if (kEarly) kinvs[t] = kinv;
         }
         __builtin_amdgcn_s_setprio(0);
+        if (kEarly && kStageQ && has_q && s1 < N) {
+          // the next block's given queries (this block's were read above), and the request
+          // for the block after it: chunks of at most 16 tokens, so they start at s1, s1 + C
+          stage_q(lid, qpf, bpar ^ 1);
+          const int tq2 = s1 + C;
+          qpf = fetch_q(lid, tq2, tq2 < N ? min(C, N - tq2) : 0, vptr[2]);
+        }
       } else if (kEarly) {
         // the solve waves meanwhile, each part on one wave and published in LDS in the
         // accumulator layout (lane (g, c16), entry i: t = 4g + i, j = c16) for the solve
@@ -588,7 +601,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           const int ntn = min(C, N - tn);
           const int ld_i = lid - kLoad0;
           const int ld_t = ld_i / (D / 8), ld_c8 = ld_i % (D / 8);
-          if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + ld_t * XLD + ld_c8 * 8) = pf;
+          if (ld_i >= 0) *reinterpret_cast<u32x4*>(Xs + (kXB > 1 ? bpar ^ 1 : 0) * (kSB * XLD) + ld_t * XLD + ld_c8 * 8) = pf;
           if (ld_i >= 0 && ld_i < kSB) pixs[bpar ^ 1][ld_i] = ld_i < ntn ? block_pixel(tn, ld_i) : 0;
           const int tn2 = tn + C;
           pf = fetch(lid, tn2, tn2 < N ? min(C, N - tn2) : 0);
@@ -964,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 4 : 1) void chain_mfma_kernel(Ch
           int lid2 = threadIdx.x;
           asm volatile("" : "+v"(lid2));
           stage_block(lid2, pf, tn, ntn);
-          stage_q(lid2, qpf);
+          stage_q(lid2, qpf, 0);
           int tn2, ntn2;
           next_block(tn, tn2, ntn2);
           pf = fetch(lid2, tn2, ntn2);
