@@ -102,6 +102,24 @@ def test_deterministic_bitwise():
     assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
 
 
+@pytest.mark.parametrize("extra", [{}, dict(route_scales=True, skip=True)], ids=["default", "scales_skip"])
+def test_stage3_image_independent_of_batch(extra):
+    # the d = 64 kernel (gate-phase staging, shared Gram and retention tiles): an image's
+    # outputs and final memories are bitwise the same alone and in a batch of six
+    import torch
+    w = wl.WORKLOADS[3].with_batch(6)
+    inp = wl.draw_workload(w, live=True)
+    one = dict(inp, x=inp["x"][:1], x_bits=inp["x_bits"][:1])
+    kw = {}
+    if extra:
+        rng = np.random.Generator(np.random.PCG64(11))
+        kw["route_scales"] = torch.from_numpy(rng.uniform(0.5, 1.5, (4, w.D)).astype(np.float32)).cuda()
+        kw["skip"] = torch.from_numpy((rng.standard_normal(w.D) * 0.3).astype(np.float32)).cuda()
+    o6, f6 = run_gpu(inp, w.n_heads, w.dtype, **kw)
+    o1, f1 = run_gpu(one, w.n_heads, w.dtype, **kw)
+    assert np.array_equal(o6[:1], o1) and np.array_equal(f6[:1], f1)
+
+
 # Full-size workloads: the GPU runs the whole map; the oracle checks sampled slices.
 SAMPLES = {1: ([0, 15], [0, 2]), 2: ([0, 63], [1, 5]), 3: ([0, 127], [0, 5]), 4: ([1], [2])}
 
